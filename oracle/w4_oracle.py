@@ -1,0 +1,345 @@
+"""Plain CPU oracle for the 4-bit weight-quantized matmul path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+product path (the HIP library and its Python binding) never does, and this
+module imports nothing from it: the two share no code, tables or constants.
+
+Everything here is slow and obviously correct: floating point is fp64, integer
+work is exact int64, and each function follows the step order of the passage
+it cites.  NumPy primitives (min/max, rint, matmul, einsum) are used as steps;
+there is no blocking or reordering beyond the definitions.
+
+Pages cited (title, section):
+
+* [MSD]    "Multi-Scale Dequant: Eliminating Dequantization Bottleneck via
+           Activation Decomposition for Efficient LLM Inference", Abstract.
+* [MixPE]  "MixPE: Quantization and Hardware Co-design for Efficient LLM
+           Inference", Abstract.
+* [NF4]    "Fast NF4 Dequantization Kernels for Large Language Model
+           Inference", Abstract.
+* [DecDEC] "DecDEC: A Systems Approach to Advancing Low-Bit LLM
+           Quantization", "Builds on" list (names QLoRA, the source of the
+           NormalFloat construction used for the NF4 codebook).
+
+Where the pages leave a step open, the reading taken is stated in the
+docstring of the function that implements it (marked READING).
+
+Pins: every function below is pinned by ``tests/test_oracle_pins.py`` against
+closed forms, brute force on tiny inputs, exact rational arithmetic or
+invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from statistics import NormalDist
+
+import numpy as np
+
+INT4_LEVELS = 15  # codes 0..15
+NF4_ZERO_INDEX = 7  # index of the exact-zero NF4 level
+INT8_QMAX = 127  # symmetric int8 range [-127, 127]
+
+FMT_INT4_ASYM = 0
+FMT_NF4 = 1
+
+
+# --------------------------------------------------------------------------
+# rounding helpers (IEEE round-to-nearest-even everywhere)
+# --------------------------------------------------------------------------
+def fp32_rne(v):
+    """Round fp64 value(s) to fp32 (nearest-even) and return them as fp64."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def fp16_from_fp32(v32):
+    """Round fp32 value(s) to fp16 (nearest-even)."""
+    return np.asarray(v32, dtype=np.float32).astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# NF4 codebook  ([NF4] Abstract: "NF4 (4-bit NormalFloat)"; construction per
+# QLoRA, listed in [DecDEC] "Builds on")
+# --------------------------------------------------------------------------
+def nf4_codebook_fp64() -> np.ndarray:
+    """The 16 NormalFloat levels in fp64, before rounding to fp32.
+
+    READING: the pages name NF4 but print no codebook.  The NormalFloat
+    construction of QLoRA is taken: with the offset
+    delta = 1/2 * ((1 - 1/30) + (1 - 1/32)), the 8 positive levels are the
+    standard-normal quantiles at the first 8 of 9 evenly spaced
+    probabilities from delta down to 1/2, the 7 negative levels are the
+    negated quantiles at the first 7 of 8 evenly spaced probabilities over the
+    same interval, an exact zero is added, and all 16 are divided by the
+    largest.  Quantiles come from ``statistics.NormalDist.inv_cdf``.
+    """
+    nd = NormalDist()
+    delta = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0))
+    pos_p = np.linspace(delta, 0.5, 9)[:-1]
+    neg_p = np.linspace(delta, 0.5, 8)[:-1]
+    pos = [nd.inv_cdf(float(p)) for p in pos_p]
+    neg = [-nd.inv_cdf(float(p)) for p in neg_p]
+    levels = sorted(pos + [0.0] + neg)
+    top = max(levels)
+    return np.array([v / top for v in levels], dtype=np.float64)
+
+
+def nf4_codebook() -> np.ndarray:
+    """NF4 levels rounded to fp32 (nearest-even); shape (16,), dtype float32."""
+    return nf4_codebook_fp64().astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# INT4 asymmetric quantization  ([MixPE] Abstract: scale and zero point are
+# shared within each quantization group)
+# --------------------------------------------------------------------------
+def quantize_int4_asym(wt: np.ndarray, G: int):
+    """Quantize W^T [N][K] (fp32) per (row n, group of G along K).
+
+    Steps for each group, all in fp64 (READING: the pages say only that a
+    scale and a zero point are shared within a group):
+
+    1. lo = min(0, min w), hi = max(0, max w)  (range widened to hold 0, so the
+       zero point is always a valid code);
+    2. s = fp16(fp32((hi - lo) / 15))  (rounding staged fp64 -> fp32 -> fp16);
+    3. z = clamp(rint(-lo / s), 0, 15)  (an integer, stored as fp16);
+    4. q = clamp(rint(w / s) + z, 0, 15);
+    5. if s == 0 the group is all zero: q = z = 0.
+
+    ``rint`` is round-half-to-even.  Returns (codes uint8 [N][K],
+    scale float16 [N][K/G], zero float16 [N][K/G]).
+    """
+    wt = np.asarray(wt, dtype=np.float32)
+    N, K = wt.shape
+    assert K % G == 0
+    w = wt.astype(np.float64).reshape(N, K // G, G)
+    lo = np.minimum(w.min(axis=2), 0.0)
+    hi = np.maximum(w.max(axis=2), 0.0)
+    s16 = fp16_from_fp32(fp32_rne((hi - lo) / float(INT4_LEVELS)))
+    s = s16.astype(np.float64)
+    nz = s != 0.0
+    safe = np.where(nz, s, 1.0)
+    z = np.clip(np.rint(-lo / safe), 0, INT4_LEVELS)
+    q = np.clip(np.rint(w / safe[..., None]) + z[..., None], 0, INT4_LEVELS)
+    z = np.where(nz, z, 0.0)
+    q = np.where(nz[..., None], q, 0.0)
+    return (q.reshape(N, K).astype(np.uint8), s16, z.astype(np.float16))
+
+
+def dequant_int4_asym(codes, scale, zero, G: int) -> np.ndarray:
+    """W' [N][K] in fp64: w' = s * (q - z), exact in fp64."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    q = codes.astype(np.float64).reshape(N, K // G, G)
+    s = np.asarray(scale, dtype=np.float16).astype(np.float64)[..., None]
+    z = np.asarray(zero, dtype=np.float16).astype(np.float64)[..., None]
+    return (s * (q - z)).reshape(N, K)
+
+
+# --------------------------------------------------------------------------
+# NF4 quantization  ([NF4] Abstract)
+# --------------------------------------------------------------------------
+def quantize_nf4(wt: np.ndarray, B: int = 64, row_chunk: int = 256):
+    """Quantize W^T [N][K] (fp32) to NF4 codes with a per-block absmax.
+
+    For each (row n, block of B along K):
+
+    1. a = fp16(max |w|)  (the absmax is exact in fp32, then rounded once);
+    2. idx = argmin_i |w - c_i * a| over the 16 fp32 levels c_i, evaluated in
+       fp64 (c_i * a is exact); READING: ties go to the lowest index;
+    3. if a == 0 every code is the exact-zero level, index 7.
+
+    Returns (codes uint8 [N][K], absmax float16 [N][K/B]).
+    """
+    wt = np.asarray(wt, dtype=np.float32)
+    N, K = wt.shape
+    assert K % B == 0
+    c = nf4_codebook().astype(np.float64)
+    codes = np.empty((N, K), dtype=np.uint8)
+    absmax = np.empty((N, K // B), dtype=np.float16)
+    for r0 in range(0, N, row_chunk):
+        r1 = min(N, r0 + row_chunk)
+        blk = wt[r0:r1].reshape(r1 - r0, K // B, B)
+        a16 = fp16_from_fp32(np.abs(blk).max(axis=2))
+        a = a16.astype(np.float64)
+        levels = c[None, None, :] * a[..., None]  # exact products
+        d = np.abs(blk.astype(np.float64)[..., :, None] - levels[..., None, :])
+        idx = np.argmin(d, axis=-1)  # first minimum = lowest index
+        idx = np.where((a == 0.0)[..., None], NF4_ZERO_INDEX, idx)
+        codes[r0:r1] = idx.reshape(r1 - r0, K).astype(np.uint8)
+        absmax[r0:r1] = a16
+    return codes, absmax
+
+
+def dequant_nf4(codes, absmax, B: int = 64) -> np.ndarray:
+    """W' [N][K] in fp64: w' = c[idx] * a, exact in fp64."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    c = nf4_codebook().astype(np.float64)
+    a = np.asarray(absmax, dtype=np.float16).astype(np.float64)
+    return (c[codes.astype(np.int64)].reshape(N, K // B, B) * a[..., None]).reshape(N, K)
+
+
+def dequant(fmt: int, codes, scale, zero, G: int) -> np.ndarray:
+    if fmt == FMT_INT4_ASYM:
+        return dequant_int4_asym(codes, scale, zero, G)
+    if fmt == FMT_NF4:
+        return dequant_nf4(codes, scale, G)
+    raise ValueError(fmt)
+
+
+# --------------------------------------------------------------------------
+# nibble packing
+# --------------------------------------------------------------------------
+def pack_nibbles(codes) -> np.ndarray:
+    """[N][K] codes (0..15) -> [N][K/2] bytes; byte j = q[2j] | q[2j+1] << 4.
+
+    READING: the pages fix no layout.  The low nibble holds the even K index
+    and rows stay K-contiguous (the PyTorch Linear weight layout, in keeping
+    with the [NF4] page's drop-in compatibility aim).
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    assert codes.shape[1] % 2 == 0
+    assert codes.max(initial=0) <= 15
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    N, H = packed.shape
+    out = np.empty((N, 2 * H), dtype=np.uint8)
+    out[:, 0::2] = packed & 0x0F
+    out[:, 1::2] = packed >> 4
+    return out
+
+
+# --------------------------------------------------------------------------
+# products
+# --------------------------------------------------------------------------
+def matmul_ref(x, w_deq) -> np.ndarray:
+    """y = x . W'  with x [M][K] (fp16), W' given as W'^T [N][K]; fp64 result [M][N].
+
+    The problem statement of mixed-precision GEMM ([MixPE] Abstract): low
+    precision weights times higher precision activations.
+    """
+    xd = np.asarray(x).astype(np.float64)
+    return xd @ np.asarray(w_deq, dtype=np.float64).T
+
+
+def postscale_ref(fmt: int, x, codes, scale, zero, G: int) -> np.ndarray:
+    """Per-group products scaled after accumulation ([MixPE] Abstract: because
+    scale and zero are shared inside a group, dequantization can follow the
+    per-group mpGEMM).
+
+    y[m, n] = sum_g s[n, g] * sum_{k in g} x[m, k] * v[n, k], where v = q - z for
+    INT4 and v = c[idx] for NF4.  Algebraically equal to ``matmul_ref`` of the
+    dequantized weights; the fp64 results agree to rounding.
+    """
+    xd = np.asarray(x).astype(np.float64)
+    M, K = xd.shape
+    codes = np.asarray(codes)
+    N = codes.shape[0]
+    ng = K // G
+    if fmt == FMT_INT4_ASYM:
+        z = np.asarray(zero, dtype=np.float16).astype(np.float64)
+        v = codes.astype(np.float64).reshape(N, ng, G) - z[..., None]
+    else:
+        c = nf4_codebook().astype(np.float64)
+        v = c[codes.astype(np.int64)].reshape(N, ng, G)
+    s = np.asarray(scale, dtype=np.float16).astype(np.float64)
+    part = np.einsum("mgk,ngk->mgn", xd.reshape(M, ng, G), v)  # per-group sums
+    return np.einsum("mgn,ng->mn", part, s)
+
+
+# --------------------------------------------------------------------------
+# Multi-Scale Dequant activation decomposition  ([MSD] Abstract)
+# --------------------------------------------------------------------------
+def decompose_activations(x, nslices: int = 2):
+    """Split fp16 activations [M][K] into ``nslices`` int8 slices with per-token
+    fp32 scales, so that x ~= sum_j s_j[m] * A_j[m, k].
+
+    READING of [MSD] ("decomposes high-precision activations into multiple
+    low-precision components ... two-pass INT8 decomposition"): a greedy
+    residual quantization.  With r = x (in fp64), for each pass j:
+
+    1. s_j = fp32(max_k |r[m, k]| / 127);
+    2. A_j = clamp(rint(r / s_j), -127, 127)  (round-half-to-even);
+    3. r <- r - s_j * A_j  (exact in fp64 for two passes);
+    4. a pass whose scale is 0 yields an all-zero slice.
+
+    Returns (A int8 [nslices][M][K], s float32 [nslices][M]).
+    """
+    r = np.asarray(x).astype(np.float64)
+    M, K = r.shape
+    A = np.zeros((nslices, M, K), dtype=np.int8)
+    S = np.zeros((nslices, M), dtype=np.float32)
+    for j in range(nslices):
+        amax = np.abs(r).max(axis=1) if K else np.zeros(M)
+        s = fp32_rne(amax / float(INT8_QMAX))
+        nz = s != 0.0
+        safe = np.where(nz, s, 1.0)
+        a = np.clip(np.rint(r / safe[:, None]), -INT8_QMAX, INT8_QMAX)
+        a = np.where(nz[:, None], a, 0.0)
+        A[j] = a.astype(np.int8)
+        S[j] = s.astype(np.float32)
+        r = r - s[:, None] * a
+    return A, S
+
+
+def msd_accumulators(slices, codes, zero, G: int) -> np.ndarray:
+    """Exact integer per-group products D_j[m, g, n] = sum_{k in g} A_j[m, k] *
+    (q[n, k] - z[n, g]), as int64 [nslices][M][K/G][N].
+
+    These are what the int8 matrix cores produce in [MSD]: slices multiplied
+    directly with the integer weights, with no conversion of the weights to a
+    floating type.
+    """
+    A = np.asarray(slices).astype(np.int64)
+    J, M, K = A.shape
+    codes = np.asarray(codes)
+    N = codes.shape[0]
+    ng = K // G
+    z = np.asarray(zero, dtype=np.float16).astype(np.int64)
+    qz = codes.astype(np.int64).reshape(N, ng, G) - z[..., None]
+    return np.einsum("jmgk,ngk->jmgn", A.reshape(J, M, ng, G), qz)
+
+
+def msd_result(tok_scale, acc, scale) -> np.ndarray:
+    """y[m, n] = sum_j s_j[m] * sum_g s[n, g] * D_j[m, g, n]  in fp64
+    (group scales applied after the integer accumulation, [MixPE] Abstract;
+    slices recombined by their scales, [MSD] Abstract)."""
+    S = np.asarray(tok_scale, dtype=np.float32).astype(np.float64)
+    D = np.asarray(acc).astype(np.float64)
+    s = np.asarray(scale, dtype=np.float16).astype(np.float64)  # [N][ng]
+    per_slice = np.einsum("jmgn,ng->jmn", D, s)
+    return np.einsum("jm,jmn->mn", S, per_slice)
+
+
+def msd_matmul(x, codes, scale, zero, G: int, nslices: int = 2):
+    """Full MSD product: decompose, integer per-group products, rescale."""
+    A, S = decompose_activations(x, nslices)
+    D = msd_accumulators(A, codes, zero, G)
+    return msd_result(S, D, scale), A, S, D
+
+
+# --------------------------------------------------------------------------
+# exact rational product for tiny shapes
+# --------------------------------------------------------------------------
+def matmul_exact(x, w_deq):
+    """Exact rational x . W' for tiny shapes (pure Python Fractions)."""
+    xf = [[Fraction(float(v)) for v in row] for row in np.asarray(x).astype(np.float64)]
+    wf = [[Fraction(float(v)) for v in row] for row in np.asarray(w_deq, dtype=np.float64)]
+    return [[sum((a * b for a, b in zip(xr, wr)), Fraction(0)) for wr in wf] for xr in xf]
+
+
+# --------------------------------------------------------------------------
+# parity metric
+# --------------------------------------------------------------------------
+def max_row_rel_l2(y, y_ref) -> float:
+    """max over rows m of ||y[m] - y_ref[m]||_2 / ||y_ref[m]||_2."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    num = np.linalg.norm(y - y_ref, axis=1)
+    den = np.linalg.norm(y_ref, axis=1)
+    den = np.where(den == 0.0, 1.0, den)
+    return float((num / den).max(initial=0.0))

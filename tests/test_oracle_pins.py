@@ -1,0 +1,395 @@
+"""Pins for the CPU oracle, independent of the oracle's own formulas.
+
+Each check below ties an oracle function to something other than itself:
+an inverse relation checked with a different library routine, exact rational
+arithmetic, brute force over every candidate code, hand-written bytes, closed
+form error bounds, or constructed inputs whose answer is known.  The
+``planted`` tests feed deliberately wrong variants of oracle steps to the same
+checks and assert that they are rejected, so a dropped term, a wrong sign or a
+transposed operand cannot pass unnoticed.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import ndtr  # standard normal CDF (not the quantile routine the oracle calls)
+
+import oracle as o
+import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- NF4 table
+def check_nf4_table(c64, c32):
+    """Construction-level checks of a 16-level NormalFloat table.
+
+    c64: levels before fp32 rounding, c32: the fp32 table.
+    """
+    assert c32.shape == (16,) and c32.dtype == np.float32
+    assert c32.nbytes == 64  # 16 entries x 4 bytes, the 64-byte table of the NF4 page
+    assert c32[0] == -1.0 and c32[7] == 0.0 and c32[15] == 1.0
+    assert np.all(np.diff(c32.astype(np.float64)) > 0)
+    assert (c32 < 0).sum() == 7 and (c32 > 0).sum() == 8
+    assert np.array_equal(c64.astype(np.float32), c32)
+    # Undo the normalisation with t = Phi^-1(delta), checked through the CDF.
+    delta = 0.5 * ((1 - 1 / 30) + (1 - 1 / 32))
+    lo, hi = 0.0, 10.0
+    for _ in range(200):  # bisection on the CDF for t with Phi(t) = delta
+        mid = 0.5 * (lo + hi)
+        lo, hi = (mid, hi) if ndtr(mid) < delta else (lo, mid)
+    t = 0.5 * (lo + hi)
+    pos = c64[8:] * t
+    neg = -c64[:7] * t
+    # positive levels sit at evenly spaced probabilities 1/2 + i*(delta-1/2)/8
+    p_pos = ndtr(pos)
+    want_pos = 0.5 + np.arange(1, 9) * (delta - 0.5) / 8
+    assert np.allclose(p_pos, want_pos, rtol=0, atol=1e-12)
+    # negative levels at 1/2 + i*(delta-1/2)/7 (mirrored), i = 1..7
+    p_neg = ndtr(neg)
+    want_neg = 0.5 + np.arange(7, 0, -1) * (delta - 0.5) / 7
+    assert np.allclose(p_neg, want_neg, rtol=0, atol=1e-12)
+
+
+def test_nf4_codebook_construction():
+    check_nf4_table(o.nf4_codebook_fp64(), o.nf4_codebook())
+
+
+def test_nf4_codebook_fp16_rounding_error_bound():
+    c32 = o.nf4_codebook().astype(np.float64)
+    c16 = o.nf4_codebook().astype(np.float16).astype(np.float64)
+    nz = c32 != 0
+    assert np.all(np.abs(c16 - c32)[nz] / np.abs(c32[nz]) <= 2.0 ** -11)
+
+
+def test_planted_nf4_mistakes_rejected():
+    good = o.nf4_codebook_fp64()
+    # wrong offset: 7 and 8 level halves built from the same spacing
+    bad1 = good.copy()
+    bad1[8:] = np.sort(good[8:]) * 0.999
+    bad1[15] = 1.0
+    # missing zero level / shifted table
+    bad2 = np.concatenate([good[:7], good[8:], [1.0]])
+    for bad in (bad1, bad2):
+        with pytest.raises(AssertionError):
+            check_nf4_table(bad, bad.astype(np.float32))
+
+
+# ---------------------------------------------------------- INT4 quantize
+def _grid_int4(rng, N, K, G, log2s=-6):
+    """Weights exactly on a 4-bit grid with power-of-two scale and integer
+    zero point; every group contains codes 0 and 15."""
+    ng = K // G
+    s = np.float64(2.0 ** log2s)
+    z = rng.integers(0, 16, size=(N, ng))
+    q = rng.integers(0, 16, size=(N, ng, G))
+    q[:, :, 0] = 0
+    q[:, :, 1] = 15
+    for n in range(N):
+        for g in range(ng):
+            rng.shuffle(q[n, g])
+    w = (s * (q - z[..., None])).reshape(N, K).astype(np.float32)
+    return w, q.reshape(N, K), s, z
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_int4_round_trip_on_grid(G):
+    rng = np.random.default_rng(7)
+    w, q, s, z = _grid_int4(rng, 6, 4 * G, G)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    assert np.all(scale.astype(np.float64) == s)
+    assert np.array_equal(zero.astype(np.int64), z)
+    assert np.array_equal(codes.astype(np.int64), q)
+    assert np.array_equal(o.dequant_int4_asym(codes, scale, zero, G), w.astype(np.float64))
+
+
+def _int4_codes_optimal(w, codes, scale, zero, G):
+    """Brute force: each code is a nearest grid point among q in [0, 15]
+    (exact rational comparison)."""
+    N, K = w.shape
+    for n in range(N):
+        for k in range(K):
+            g = k // G
+            s = Fraction(float(scale[n, g]))
+            z = Fraction(float(zero[n, g]))
+            wf = Fraction(float(w[n, k]))
+            errs = [abs(wf - s * (q - z)) for q in range(16)]
+            if errs[int(codes[n, k])] != min(errs):
+                return False
+    return True
+
+
+def test_int4_codes_are_nearest_grid_points():
+    w = wl.make_weight(99, 0, 4, 256)
+    codes, scale, zero = o.quantize_int4_asym(w, 64)
+    assert _int4_codes_optimal(w, codes, scale, zero, 64)
+
+
+def test_int4_grid_spans_group_range():
+    """The dequant grid reaches both group extremes: every weight is within one
+    step of its reconstruction, and the group's min and max within half a step
+    plus the fp16 rounding of the scale."""
+    w = wl.make_weight(98, 0, 32, 512)
+    G = 128
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    wd = o.dequant_int4_asym(codes, scale, zero, G).reshape(32, 4, G)
+    wg = w.astype(np.float64).reshape(32, 4, G)
+    s = scale.astype(np.float64)[..., None]
+    assert np.all(np.abs(wd - wg) <= 0.5 * s + 16 * s * 2.0 ** -11)
+    assert np.all(s > 0)
+
+
+def test_int4_special_cases():
+    w = np.zeros((2, 128), np.float32)
+    w[1, 64:] = np.linspace(0.01, 0.5, 64, dtype=np.float32)  # all-positive group
+    codes, scale, zero = o.quantize_int4_asym(w, 64)
+    assert scale[0, 0] == 0 and zero[0, 0] == 0 and np.all(codes[0] == 0)
+    assert scale[1, 0] == 0 and np.all(codes[1, :64] == 0)
+    assert zero[1, 1] == 0 and codes[1, 127] == 15 and codes[1, 64] >= 0
+
+
+def test_planted_int4_mistakes_rejected():
+    rng = np.random.default_rng(5)
+    w, q, s, z = _grid_int4(rng, 4, 256, 64)
+    # (a) zero point with the wrong sign, (b) code without the zero point
+    bad_a = np.clip(np.rint(w.astype(np.float64).reshape(4, 4, 64) / s) - z[..., None], 0, 15)
+    bad_b = np.clip(np.rint(w.astype(np.float64).reshape(4, 4, 64) / s), 0, 15)
+    for bad in (bad_a, bad_b):
+        assert not np.array_equal(bad.reshape(4, 256).astype(np.int64), q)
+
+
+# ----------------------------------------------------------- NF4 quantize
+def test_nf4_round_trip_on_levels():
+    rng = np.random.default_rng(11)
+    c = o.nf4_codebook()
+    N, K, B = 5, 256, 64
+    idx = rng.integers(0, 16, size=(N, K // B, B))
+    idx[:, :, 0] = 15
+    a = np.float32(2.0 ** rng.integers(-8, 2, size=(N, K // B)))
+    w = (c[idx] * a[..., None]).astype(np.float32).reshape(N, K)
+    codes, absmax = o.quantize_nf4(w, B)
+    assert np.array_equal(absmax.astype(np.float32), a)
+    assert np.array_equal(codes, idx.reshape(N, K).astype(np.uint8))
+    assert np.array_equal(o.dequant_nf4(codes, absmax, B), w.astype(np.float64))
+
+
+def test_nf4_codes_are_nearest_levels():
+    w = wl.make_weight(97, 0, 3, 128)
+    codes, absmax = o.quantize_nf4(w, 64)
+    c = [Fraction(float(v)) for v in o.nf4_codebook()]
+    for n in range(3):
+        for k in range(128):
+            a = Fraction(float(absmax[n, k // 64]))
+            wf = Fraction(float(w[n, k]))
+            errs = [abs(wf - ci * a) for ci in c]
+            i = int(codes[n, k])
+            assert errs[i] == min(errs)
+            assert i == errs.index(min(errs))  # lowest index on ties
+
+
+def test_nf4_zero_block():
+    w = np.zeros((1, 128), np.float32)
+    w[0, 64:] = 0.25
+    codes, absmax = o.quantize_nf4(w, 64)
+    assert absmax[0, 0] == 0 and np.all(codes[0, :64] == 7)
+    assert absmax[0, 1] == np.float16(0.25) and np.all(codes[0, 64:] == 15)
+
+
+# ----------------------------------------------------------------- packing
+def test_pack_hand_written_bytes():
+    codes = np.array([[1, 2, 3, 4, 5, 6, 7, 8], [15, 0, 0, 15, 9, 10, 11, 12]], np.uint8)
+    want = np.array([[0x21, 0x43, 0x65, 0x87], [0x0F, 0xF0, 0xA9, 0xCB]], np.uint8)
+    assert np.array_equal(o.pack_nibbles(codes), want)
+    assert np.array_equal(o.unpack_nibbles(want), codes)
+
+
+def test_pack_round_trip_and_size():
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, size=(16, 1024)).astype(np.uint8)
+    p = o.pack_nibbles(codes)
+    assert p.shape == (16, 512) and p.nbytes * 4 == codes.size * 2  # 4x smaller than fp16
+    assert np.array_equal(o.unpack_nibbles(p), codes)
+
+
+def test_planted_pack_mistake_rejected():
+    codes = np.array([[1, 2, 3, 4]], np.uint8)
+    swapped = (codes[:, 1::2] | (codes[:, 0::2] << 4)).astype(np.uint8)
+    assert not np.array_equal(swapped, np.array([[0x21, 0x43]], np.uint8))
+
+
+# -------------------------------------------------- activation decomposition
+def _decomp_rows_ok(x, A, S):
+    """Brute force + closed-form bound for a two-slice decomposition."""
+    xd = x.astype(np.float64)
+    M, K = xd.shape
+    cand = np.arange(-127, 128, dtype=np.float64)
+    r = xd.copy()
+    for j in range(A.shape[0]):
+        s = S[j].astype(np.float64)
+        for m in range(M):
+            if s[m] == 0:
+                if np.any(A[j, m] != 0):
+                    return False
+                continue
+            # each integer is a nearest point of the grid s * [-127, 127]
+            err = np.abs(r[m][:, None] - s[m] * cand[None, :])
+            chosen = np.abs(r[m] - s[m] * A[j, m].astype(np.float64))
+            if np.any(chosen > err.min(axis=1)):
+                return False
+        r = r - s[:, None] * A[j].astype(np.float64)
+    return True
+
+
+def test_decompose_nearest_integers_and_bound():
+    x = wl.make_activations(96, 0, 8, 512, outliers=True)
+    A, S = o.decompose_activations(x, 2)
+    assert A.dtype == np.int8 and S.dtype == np.float32
+    assert _decomp_rows_ok(x, A, S)
+    # exact reconstruction error (rational), bound amax / (127 * 508)
+    for m in range(8):
+        amax = Fraction(float(np.abs(x[m].astype(np.float64)).max()))
+        s1, s2 = Fraction(float(S[0, m])), Fraction(float(S[1, m]))
+        worst = max(abs(Fraction(float(xv)) - s1 * int(a1) - s2 * int(a2))
+                    for xv, a1, a2 in zip(x[m], A[0, m], A[1, m]))
+        assert worst <= s2 / 2
+        assert worst <= amax / 64516 * Fraction(1 + 2 ** -21)
+        # "near 16 effective bits" (MSD page, Abstract)
+        assert float(amax / worst if worst else 1e30) >= 2 ** 15.97
+
+
+def test_decompose_exact_first_slice():
+    rng = np.random.default_rng(2)
+    ints = rng.integers(-127, 128, size=(3, 64))
+    ints[:, 0] = 127
+    x = (ints * 2.0 ** -4).astype(np.float16)
+    A, S = o.decompose_activations(x, 2)
+    assert np.all(S[0] == np.float32(2.0 ** -4))
+    assert np.array_equal(A[0].astype(np.int64), ints)
+    assert np.all(S[1] == 0) and np.all(A[1] == 0)
+
+
+def test_decompose_zero_rows_and_one_slice():
+    x = np.zeros((2, 32), np.float16)
+    x[1, 5] = -3.0
+    A, S = o.decompose_activations(x, 1)
+    assert A.shape == (1, 2, 32)
+    assert S[0, 0] == 0 and np.all(A[0, 0] == 0)
+    assert A[0, 1, 5] == -127
+
+
+def test_planted_decompose_mistake_rejected():
+    x = wl.make_activations(95, 0, 4, 256)
+    A, S = o.decompose_activations(x, 2)
+    # second slice taken from x instead of the residual: fails the bound
+    A2 = np.clip(np.rint(x.astype(np.float64) / S[1].astype(np.float64)[:, None]), -127, 127)
+    bad = A.copy()
+    bad[1] = A2.astype(np.int8)
+    assert not _decomp_rows_ok(x, bad, S)
+
+
+# ------------------------------------------------------------------ products
+def _tiny_case(fmt, seed, M=3, N=4, K=256, G=64):
+    w = wl.make_weight(seed, 0, N, K)
+    x = wl.make_activations(seed, 0, M, K)
+    if fmt == o.FMT_INT4_ASYM:
+        codes, scale, zero = o.quantize_int4_asym(w, G)
+    else:
+        codes, scale = o.quantize_nf4(w, G)
+        zero = None
+    return x, codes, scale, zero
+
+
+@pytest.mark.parametrize("fmt", [o.FMT_INT4_ASYM, o.FMT_NF4])
+def test_matmul_matches_exact_rationals(fmt):
+    x, codes, scale, zero = _tiny_case(fmt, 90 + fmt)
+    wd = o.dequant(fmt, codes, scale, zero, 64)
+    y = o.matmul_ref(x, wd)
+    ex = o.matmul_exact(x, wd)
+    absxw = np.abs(x.astype(np.float64)) @ np.abs(wd).T
+    for m in range(y.shape[0]):
+        for n in range(y.shape[1]):
+            # standard dot-product rounding bound, K * 2^-53 * sum |x||w|
+            assert abs(Fraction(float(y[m, n])) - ex[m][n]) <= Fraction(256 * 2.0 ** -53) * Fraction(float(absxw[m, n])) * 2
+
+
+def test_planted_transpose_rejected():
+    x, codes, scale, zero = _tiny_case(o.FMT_INT4_ASYM, 89, M=2, N=4, K=256)
+    wd = o.dequant(o.FMT_INT4_ASYM, codes, scale, zero, 64)
+    ex = o.matmul_exact(x, wd)
+    # a plausible slip: using W' in the wrong orientation (reshape, not transpose)
+    bad = x.astype(np.float64) @ wd.reshape(256, 4)
+    assert not np.allclose(bad, np.array(ex, dtype=np.float64), rtol=1e-6)
+
+
+@pytest.mark.parametrize("fmt", [o.FMT_INT4_ASYM, o.FMT_NF4])
+def test_postscale_equals_dequant_first(fmt):
+    x, codes, scale, zero = _tiny_case(fmt, 80 + fmt, M=5, N=32, K=512, G=128 if fmt == 0 else 64)
+    G = 128 if fmt == 0 else 64
+    y_dq = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
+    y_ps = o.postscale_ref(fmt, x, codes, scale, zero, G)
+    assert np.allclose(y_ps, y_dq, rtol=1e-12, atol=1e-12 * np.abs(y_dq).max())
+
+
+def test_msd_accumulators_brute_force():
+    x, codes, scale, zero = _tiny_case(o.FMT_INT4_ASYM, 70, M=2, N=3, K=128, G=64)
+    A, S = o.decompose_activations(x, 2)
+    D = o.msd_accumulators(A, codes, zero, 64)
+    for j in range(2):
+        for m in range(2):
+            for g in range(2):
+                for n in range(3):
+                    want = 0
+                    for k in range(64 * g, 64 * g + 64):
+                        want += int(A[j, m, k]) * (int(codes[n, k]) - int(zero[n, g]))
+                    assert D[j, m, g, n] == want
+    # int32 never overflows: |D| <= 127 * 15 * G
+    assert np.abs(D).max() <= 127 * 15 * 64
+
+
+def test_msd_result_exact_and_bound():
+    G = 64
+    x, codes, scale, zero = _tiny_case(o.FMT_INT4_ASYM, 71, M=3, N=4, K=256, G=G)
+    y, A, S, D = o.msd_matmul(x, codes, scale, zero, G, 2)
+    # exact rational recombination
+    for m in range(3):
+        for n in range(4):
+            ex = sum(Fraction(float(S[j, m])) * Fraction(float(scale[n, g])) * int(D[j, m, g, n])
+                     for j in range(2) for g in range(4))
+            assert abs(Fraction(float(y[m, n])) - ex) <= abs(ex) * Fraction(2.0 ** -48) + Fraction(2.0 ** -80)
+    # closed-form bound against the exact product: |y_msd - y| <= amax/64516 * sum|w'|
+    wd = o.dequant_int4_asym(codes, scale, zero, G)
+    y_exact = o.matmul_ref(x, wd)
+    amax = np.abs(x.astype(np.float64)).max(axis=1)
+    bound = (amax / 64516)[:, None] * np.abs(wd).sum(axis=1)[None, :] * (1 + 2 ** -20)
+    assert np.all(np.abs(y - y_exact) <= bound + 1e-12)
+
+
+def test_max_row_rel_l2_hand_example():
+    y_ref = np.array([[3.0, 4.0], [1.0, 0.0]])
+    y = np.array([[3.0, 4.5], [1.0, 0.01]])
+    assert o.max_row_rel_l2(y, y_ref) == pytest.approx(max(0.5 / 5.0, 0.01))
+
+
+# ------------------------------------------------------- hand-worked fixtures
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
+def test_int4_hand_example():
+    g = _golden("int4_hand_example.json")
+    w = np.array([g["w"]], np.float32)
+    codes, scale, zero = o.quantize_int4_asym(w, g["G"])
+    assert codes[0].tolist() == g["codes"]
+    assert hex(int(scale.view(np.uint16)[0, 0])) == g["scale_fp16_bits"]
+    assert float(zero[0, 0]) == g["zero"]
+
+
+def test_nf4_hand_example():
+    g = _golden("nf4_hand_example.json")
+    w = np.array([g["w"]], np.float32)
+    codes, absmax = o.quantize_nf4(w, g["B"])
+    assert codes[0].tolist() == g["codes"]
+    assert float(absmax[0, 0]) == g["absmax"]
