@@ -1,0 +1,196 @@
+"""Python binding of libw4.so, the gfx950 4-bit weight-quantized matmul library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch provides device memory and the current HIP stream.  The
+functions take and return torch tensors on the GPU; fp16 data are
+``torch.float16`` tensors whose bits travel through the C ABI as uint16.
+
+Entry points mirror ``include/w4.h``: quantize, pack, gemv, gemm,
+gemm_decomp, workspace_bytes, nf4_levels.  If the library is not built,
+importing works but the first call raises ``W4LibraryMissing``; nothing
+falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
+    "lib", "lib_path", "quantize", "pack", "gemv", "gemm", "gemm_decomp",
+    "workspace_bytes", "nf4_levels", "version",
+]
+
+INT4_ASYM = 0
+NF4 = 1
+DQ_F16 = 0
+POSTSCALE = 1
+OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP = range(5)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libw4.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+class W4LibraryMissing(RuntimeError):
+    pass
+
+
+class W4Error(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load libw4.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise W4LibraryMissing(
+                f"{lib_path} is not built; run `python -m bit_weight_quantized_amd.build` "
+                "or __graft_entry__.build()")
+        L = ctypes.CDLL(lib_path)
+        L.w4_quantize.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p]
+        L.w4_pack.argtypes = [_p, _i, _i, _p, _p]
+        L.w4_gemv.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p]
+        L.w4_gemm.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
+        L.w4_gemm_decomp.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
+        L.w4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+        L.w4_workspace_bytes.restype = _sz
+        L.w4_nf4_levels.argtypes = [_p]
+        L.w4_status_str.argtypes = [_i]
+        L.w4_status_str.restype = ctypes.c_char_p
+        L.w4_last_error.argtypes = []
+        L.w4_last_error.restype = ctypes.c_char_p
+        L.w4_version.restype = ctypes.c_char_p
+        for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp", "w4_nf4_levels"):
+            getattr(L, fn).restype = _i
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise W4Error(fn, status, lib().w4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    return t
+
+
+def version() -> str:
+    return lib().w4_version().decode()
+
+
+def nf4_levels() -> "list[float]":
+    """The library's 16 fp32 NF4 levels (host copy)."""
+    buf = (ctypes.c_float * 16)()
+    _check("w4_nf4_levels", lib().w4_nf4_levels(ctypes.cast(buf, _p)))
+    return list(buf)
+
+
+def workspace_bytes(op: int, M: int, K: int, N: int, G: int, fmt_or_mode: int) -> int:
+    return int(lib().w4_workspace_bytes(op, M, K, N, G, fmt_or_mode))
+
+
+def quantize(wt, G: int, fmt: int, *, codes=None, scale=None, zero=None, stream=None):
+    """Quantize fp32 W^T [N][K] -> (codes uint8 [N][K], scale fp16 [N][K/G],
+    zero fp16 [N][K/G] or None for NF4)."""
+    _dev(wt, torch.float32, "wt")
+    N, K = wt.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=wt.device) if codes is None else codes
+    ng = K // G if G else 0
+    scale = torch.empty((N, ng), dtype=torch.float16, device=wt.device) if scale is None else scale
+    if fmt == INT4_ASYM and zero is None:
+        zero = torch.empty((N, ng), dtype=torch.float16, device=wt.device)
+    _check("w4_quantize", lib().w4_quantize(_ptr(wt), K, N, G, fmt, _ptr(codes), _ptr(scale),
+                                            _ptr(zero) if fmt == INT4_ASYM else None, _stream(stream)))
+    return codes, scale, (zero if fmt == INT4_ASYM else None)
+
+
+def pack(codes, *, out=None, stream=None):
+    """Pack codes [N][K] -> [N][K/2] bytes (low nibble = even k)."""
+    _dev(codes, torch.uint8, "codes")
+    N, K = codes.shape
+    out = torch.empty((N, K // 2), dtype=torch.uint8, device=codes.device) if out is None else out
+    _check("w4_pack", lib().w4_pack(_ptr(codes), K, N, _ptr(out), _stream(stream)))
+    return out
+
+
+def _weights(packed, scale, zero):
+    _dev(packed, torch.uint8, "packed")
+    _dev(scale, torch.float16, "scale")
+    if zero is not None:
+        _dev(zero, torch.float16, "zero")
+    N, half_k = packed.shape
+    return N, 2 * half_k
+
+
+def gemv(x, packed, scale, zero, G: int, fmt: int, *, out=None, workspace=None, stream=None):
+    """y[M][N] = x[M][K] . W' for 1 <= M <= 32 (fp16 in, fp16 out)."""
+    _dev(x, torch.float16, "x")
+    N, K = _weights(packed, scale, zero)
+    M = x.shape[0]
+    out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
+    ws_n = workspace_bytes(OP_GEMV, M, K, N, G, fmt)
+    if workspace is None and ws_n:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
+    _check("w4_gemv", lib().w4_gemv(_ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, fmt,
+                                    _ptr(out), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out
+
+
+def gemm(x, packed, scale, zero, G: int, fmt: int, mode: int, *, out=None, workspace=None, stream=None):
+    """y[M][N] = x[M][K] . W' on fp16 matrix cores, mode DQ_F16 or POSTSCALE."""
+    _dev(x, torch.float16, "x")
+    N, K = _weights(packed, scale, zero)
+    M = x.shape[0]
+    out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
+    ws_n = workspace_bytes(OP_GEMM, M, K, N, G, mode)
+    if workspace is None and ws_n:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
+    _check("w4_gemm", lib().w4_gemm(_ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, fmt,
+                                    mode, _ptr(out), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out
+
+
+def gemm_decomp(x, packed, scale, zero, G: int, nslices: int = 2, *, out=None, slices_out=None,
+                tok_scale_out=None, acc_out=None, workspace=None, stream=None):
+    """Multi-Scale Dequant product: x split into int8 slices, int8 matrix cores.
+
+    Returns y, or (y, slices, tok_scales, acc) when any optional output is
+    given (pass tensors to receive them)."""
+    _dev(x, torch.float16, "x")
+    N, K = _weights(packed, scale, zero)
+    M = x.shape[0]
+    out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
+    ws_n = workspace_bytes(OP_GEMM_DECOMP, M, K, N, G, nslices)
+    if workspace is None and ws_n and (slices_out is None or tok_scale_out is None):
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
+    _check("w4_gemm_decomp", lib().w4_gemm_decomp(
+        _ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, nslices, _ptr(out),
+        _ptr(slices_out), _ptr(tok_scale_out), _ptr(acc_out), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
+    if slices_out is None and tok_scale_out is None and acc_out is None:
+        return out
+    return out, slices_out, tok_scale_out, acc_out

@@ -1,0 +1,200 @@
+// Host side of the C ABI declared in include/w4.h: argument validation,
+// status codes, the thread-local error text and dispatch to the launchers.
+#include "../../include/w4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "w4_internal.h"
+
+namespace w4 {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_group(int G) { return G == 64 || G == 128; }
+
+// Shape rules shared by the matmul entry points.
+int check_matmul_shape(const char* fn, int M, int K, int N, int G) {
+  if (M < 1) return fail(W4_EINVAL, "%s: M must be >= 1 (got %d)", fn, M);
+  if (K < 1 || N < 1) return fail(W4_EINVAL, "%s: K and N must be >= 1 (got K=%d N=%d)", fn, K, N);
+  if (!valid_group(G)) return fail(W4_EINVAL, "%s: G must be 64 or 128 (got %d)", fn, G);
+  if (K % G != 0) return fail(W4_EINVAL, "%s: K=%d is not a multiple of G=%d", fn, K, G);
+  if (N % 16 != 0) return fail(W4_EINVAL, "%s: N=%d is not a multiple of 16", fn, N);
+  return W4_OK;
+}
+
+int check_weights(const char* fn, const uint8_t* packed, const uint16_t* scale,
+                  const uint16_t* zero, int fmt) {
+  if (fmt != W4_INT4_ASYM && fmt != W4_NF4) return fail(W4_EINVAL, "%s: unknown fmt %d", fn, fmt);
+  if (!packed || !scale) return fail(W4_EINVAL, "%s: packed and scale must be non-null", fn);
+  if (fmt == W4_INT4_ASYM && !zero) return fail(W4_EINVAL, "%s: INT4 weights need a zero-point array", fn);
+  if (fmt == W4_NF4 && zero) return fail(W4_EINVAL, "%s: NF4 weights take zero == NULL", fn);
+  if (!aligned16(packed) || !aligned16(scale) || (zero && !aligned16(zero)))
+    return fail(W4_EINVAL, "%s: weight pointers must be 16-byte aligned", fn);
+  return W4_OK;
+}
+
+int check_io(const char* fn, const void* x, const void* y) {
+  if (!x || !y) return fail(W4_EINVAL, "%s: x and y must be non-null", fn);
+  if (!aligned16(x) || !aligned16(y)) return fail(W4_EINVAL, "%s: x and y must be 16-byte aligned", fn);
+  return W4_OK;
+}
+}  // namespace
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(W4_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return W4_OK;
+}
+
+const uint32_t kNf4LevelBits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+}  // namespace w4
+
+using namespace w4;
+
+extern "C" {
+
+int w4_quantize(const float* wt, int K, int N, int G, int fmt, uint8_t* codes,
+                uint16_t* scale, uint16_t* zero, void* stream) {
+  g_last_error[0] = '\0';
+  if (K < 1 || N < 1) return fail(W4_EINVAL, "w4_quantize: K and N must be >= 1 (got K=%d N=%d)", K, N);
+  if (!valid_group(G)) return fail(W4_EINVAL, "w4_quantize: G must be 64 or 128 (got %d)", G);
+  if (K % G != 0) return fail(W4_EINVAL, "w4_quantize: K=%d is not a multiple of G=%d", K, G);
+  if (!wt || !codes || !scale) return fail(W4_EINVAL, "w4_quantize: wt, codes and scale must be non-null");
+  if (fmt == W4_INT4_ASYM) {
+    if (!zero) return fail(W4_EINVAL, "w4_quantize: INT4 needs a zero-point array");
+    return launch_quantize_int4(wt, K, N, G, codes, scale, zero, (hipStream_t)stream);
+  }
+  if (fmt == W4_NF4) {
+    if (zero) return fail(W4_EINVAL, "w4_quantize: NF4 takes zero == NULL");
+    return launch_quantize_nf4(wt, K, N, G, codes, scale, (hipStream_t)stream);
+  }
+  return fail(W4_EINVAL, "w4_quantize: unknown fmt %d", fmt);
+}
+
+int w4_pack(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream) {
+  g_last_error[0] = '\0';
+  if (K < 1 || N < 1) return fail(W4_EINVAL, "w4_pack: K and N must be >= 1 (got K=%d N=%d)", K, N);
+  if (K % 32 != 0) return fail(W4_EINVAL, "w4_pack: K=%d is not a multiple of 32", K);
+  if (!codes || !packed) return fail(W4_EINVAL, "w4_pack: codes and packed must be non-null");
+  if (!aligned16(codes) || !aligned16(packed)) return fail(W4_EINVAL, "w4_pack: pointers must be 16-byte aligned");
+  return launch_pack(codes, K, N, packed, (hipStream_t)stream);
+}
+
+int w4_gemv(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+            const uint16_t* scale, const uint16_t* zero, int G, int fmt, uint16_t* y,
+            void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  (void)ws;
+  (void)ws_bytes;
+  int st;
+  if ((st = check_matmul_shape("w4_gemv", M, K, N, G)) != W4_OK) return st;
+  if (M > 32) return fail(W4_EINVAL, "w4_gemv: M must be <= 32 (got %d); use w4_gemm", M);
+  if ((st = check_weights("w4_gemv", packed, scale, zero, fmt)) != W4_OK) return st;
+  if ((st = check_io("w4_gemv", x, y)) != W4_OK) return st;
+  return launch_gemv(x, M, K, N, packed, scale, zero, G, fmt, y, (hipStream_t)stream);
+}
+
+int w4_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+            const uint16_t* scale, const uint16_t* zero, int G, int fmt, int mode,
+            uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  (void)ws;
+  (void)ws_bytes;
+  int st;
+  if ((st = check_matmul_shape("w4_gemm", M, K, N, G)) != W4_OK) return st;
+  if (mode != W4_DQ_F16 && mode != W4_POSTSCALE) return fail(W4_EINVAL, "w4_gemm: unknown mode %d", mode);
+  if ((st = check_weights("w4_gemm", packed, scale, zero, fmt)) != W4_OK) return st;
+  if ((st = check_io("w4_gemm", x, y)) != W4_OK) return st;
+  return launch_gemm(x, M, K, N, packed, scale, zero, G, fmt, mode, y, (hipStream_t)stream);
+}
+
+int w4_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                   const uint16_t* scale, const uint16_t* zero, int G, int nslices,
+                   uint16_t* y, int8_t* slices_out, float* tok_scale_out, int32_t* acc_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  int st;
+  if ((st = check_matmul_shape("w4_gemm_decomp", M, K, N, G)) != W4_OK) return st;
+  if (nslices != 1 && nslices != 2)
+    return fail(W4_EINVAL, "w4_gemm_decomp: nslices must be 1 or 2 (got %d)", nslices);
+  if (packed && scale && !zero)
+    return fail(W4_EUNSUPPORTED, "w4_gemm_decomp: needs INT4 weights (zero != NULL); NF4 levels are not integers");
+  if ((st = check_weights("w4_gemm_decomp", packed, scale, zero, W4_INT4_ASYM)) != W4_OK) return st;
+  if ((st = check_io("w4_gemm_decomp", x, y)) != W4_OK) return st;
+  if ((slices_out && !aligned16(slices_out)) || (tok_scale_out && !aligned16(tok_scale_out)) ||
+      (acc_out && !aligned16(acc_out)))
+    return fail(W4_EINVAL, "w4_gemm_decomp: optional outputs must be 16-byte aligned");
+  const size_t need = decomp_workspace_bytes(M, K, nslices);
+  int8_t* sl = slices_out;
+  float* ts = tok_scale_out;
+  if (!sl || !ts) {
+    if (!ws || ws_bytes < need)
+      return fail(W4_EWORKSPACE, "w4_gemm_decomp: workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemm_decomp: workspace must be 16-byte aligned");
+    char* base = static_cast<char*>(ws);
+    const size_t slice_bytes = ((size_t)nslices * M * K + 255) & ~(size_t)255;
+    if (!sl) sl = reinterpret_cast<int8_t*>(base);
+    if (!ts) ts = reinterpret_cast<float*>(base + slice_bytes);
+  }
+  return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, y, sl, ts, acc_out,
+                            (hipStream_t)stream);
+}
+
+size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
+  (void)N;
+  (void)G;
+  switch (op) {
+    case W4_OP_QUANTIZE:
+    case W4_OP_PACK:
+    case W4_OP_GEMV:
+    case W4_OP_GEMM:
+      return 0;
+    case W4_OP_GEMM_DECOMP:
+      if (M < 1 || K < 1 || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
+      return decomp_workspace_bytes(M, K, fmt_or_mode);
+    default:
+      return (size_t)-1;
+  }
+}
+
+int w4_nf4_levels(float* out16) {
+  if (!out16) return fail(W4_EINVAL, "w4_nf4_levels: out16 must be non-null");
+  std::memcpy(out16, kNf4LevelBits, sizeof(kNf4LevelBits));
+  return W4_OK;
+}
+
+const char* w4_status_str(int status) {
+  switch (status) {
+    case W4_OK: return "W4_OK";
+    case W4_EINVAL: return "W4_EINVAL: invalid argument";
+    case W4_EUNSUPPORTED: return "W4_EUNSUPPORTED: unsupported request";
+    case W4_EWORKSPACE: return "W4_EWORKSPACE: workspace too small";
+    case W4_EHIP: return "W4_EHIP: HIP runtime error";
+    default: return "unknown w4 status";
+  }
+}
+
+const char* w4_last_error(void) { return g_last_error; }
+
+const char* w4_version(void) { return "w4 0.1.0 (gfx950)"; }
+
+}  // extern "C"

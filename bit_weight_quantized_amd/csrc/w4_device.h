@@ -1,0 +1,74 @@
+// Device-side helpers for gfx950 (CDNA4, wave64): vector types, matrix-core
+// wrappers, wave reductions, fp16 bit helpers and the NF4 level table.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// NormalFloat levels rounded to fp32 (QLoRA's construction, which the
+// "Fast NF4 Dequantization Kernels" page builds on), as bit patterns.
+#define W4_NF4_LEVEL_BITS                                                  \
+  0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu,          \
+      0xbe3d353du, 0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu,      \
+      0x3e7c04dau, 0x3ead0336u, 0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u,      \
+      0x3f800000u
+
+__device__ __forceinline__ float nf4_level(int i) {
+  constexpr uint32_t bits[16] = {W4_NF4_LEVEL_BITS};
+  return __uint_as_float(bits[i]);
+}
+
+// 16x16x32 fp16 matrix-core product, fp32 accumulate.
+// Lane l supplies A[m = l%16][k = 8*(l/16) + i] and B[k = 8*(l/16) + i][n = l%16]
+// for i = 0..7, and holds D[m = 4*(l/16) + r][n = l%16], r = 0..3.
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+// 16x16x64 int8 matrix-core product, int32 accumulate; same lane mapping with
+// 16 k values per lane (k = 16*(l/16) + i).
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+}  // namespace w4

@@ -1,0 +1,42 @@
+// Internal declarations shared by the library's translation units (not part
+// of the public ABI; see include/w4.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4 {
+
+// Records `msg` as this thread's last error and returns `status`.
+int fail(int status, const char* fmt, ...);
+
+// Maps the last HIP launch error to W4_EHIP (recording its text) or W4_OK.
+int check_launch(const char* what);
+
+// ---- launchers (host side); arguments are validated by the caller ----
+int launch_quantize_int4(const float* wt, int K, int N, int G, uint8_t* codes,
+                         uint16_t* scale, uint16_t* zero, hipStream_t s);
+int launch_quantize_nf4(const float* wt, int K, int N, int G, uint8_t* codes,
+                        uint16_t* absmax, hipStream_t s);
+int launch_pack(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t s);
+
+int launch_gemv(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                const uint16_t* scale, const uint16_t* zero, int G, int fmt,
+                uint16_t* y, hipStream_t s);
+
+int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                const uint16_t* scale, const uint16_t* zero, int G, int fmt,
+                int mode, uint16_t* y, hipStream_t s);
+
+size_t decomp_workspace_bytes(int M, int K, int nslices);
+int launch_gemm_decomp(const uint16_t* x, int M, int K, int N,
+                       const uint8_t* packed, const uint16_t* scale,
+                       const uint16_t* zero, int G, int nslices, uint16_t* y,
+                       int8_t* slices, float* tok_scale, int32_t* acc_out,
+                       hipStream_t s);
+
+// The 16 NF4 levels as fp32 bit patterns (host copy).
+extern const uint32_t kNf4LevelBits[16];
+
+}  // namespace w4

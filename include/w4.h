@@ -1,0 +1,183 @@
+/*
+ * w4.h -- C ABI of a 4-bit weight-quantized matmul library for AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * The library computes y = x . W' where x is fp16 activations [M][K] and W' is
+ * a 4-bit quantized weight matrix, either INT4 with a per-group scale and zero
+ * point or NF4 (16-level NormalFloat codebook) with a per-block absmax.  This
+ * is the mixed-precision GEMM (low-precision weights times higher-precision
+ * activations) of the page "MixPE: Quantization and Hardware Co-design for
+ * Efficient LLM Inference" (Abstract).
+ *
+ * Pages cited below by short name (title, section):
+ *   [MSD]   "Multi-Scale Dequant: Eliminating Dequantization Bottleneck via
+ *           Activation Decomposition for Efficient LLM Inference", Abstract.
+ *   [MixPE] "MixPE: Quantization and Hardware Co-design for Efficient LLM
+ *           Inference", Abstract.
+ *   [NF4]   "Fast NF4 Dequantization Kernels for Large Language Model
+ *           Inference", Abstract.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts.  The weight is stored transposed, W^T [N][K], K contiguous (the
+ *   PyTorch Linear weight layout).  Codes are one byte each, [N][K].  Packed
+ *   weights are [N][K/2] bytes: byte j of row n holds code 2j in its low
+ *   nibble and code 2j+1 in its high nibble.  Per-group scales, zero points
+ *   and NF4 absmax values are fp16 [N][K/G] (group g covers k in
+ *   [g*G, (g+1)*G)).  Zero points are integers 0..15 stored as fp16.
+ *   Activations x are fp16 [M][K]; outputs y are fp16 [M][N]; all row-major.
+ *   fp16 values travel as uint16_t bit patterns.
+ * Memory.  Every pointer argument except those marked "host" is a device
+ *   pointer on the current HIP device.  The caller owns every buffer; the
+ *   library allocates nothing and keeps no state besides a thread-local
+ *   error string.  Device pointers must be 16-byte aligned.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Calls only enqueue work and never synchronize; outputs are valid
+ *   once the stream reaches that point.  Calls that share a workspace must be
+ *   ordered on one stream.
+ * Errors.  Arguments are checked before anything is enqueued.  A failed check
+ *   returns a negative w4_status and enqueues nothing; w4_last_error() then
+ *   describes the failure.  A launch failure reported by HIP returns W4_EHIP.
+ *   No C++ exception crosses this boundary.
+ * Shape rules.  G (group or block size along K) is 64 or 128; K % G == 0;
+ *   N % 16 == 0; M >= 1.  NF4 takes zero == NULL; INT4 needs zero != NULL.
+ */
+#ifndef W4_H_
+#define W4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4_OK = 0,
+  W4_EINVAL = -1,        /* bad shape, null or misaligned pointer, bad enum */
+  W4_EUNSUPPORTED = -2,  /* valid request this entry point does not serve */
+  W4_EWORKSPACE = -3,    /* workspace missing or smaller than required */
+  W4_EHIP = -4           /* the HIP runtime reported an error */
+} w4_status;
+
+typedef enum { W4_INT4_ASYM = 0, W4_NF4 = 1 } w4_fmt;
+
+/* W4_DQ_F16: weights are dequantized to fp16 (s*(q-z), or c[idx]*a) before
+ *   the fp16 matrix-core product (the dequantization baseline of [MSD], [NF4]).
+ * W4_POSTSCALE: the integer codes (q-z), or the NF4 levels c[idx], enter the
+ *   fp16 product unscaled; each group's fp32 partial sum is multiplied by its
+ *   scale after accumulation ([MixPE]: dequantization after per-group
+ *   mpGEMM). */
+typedef enum { W4_DQ_F16 = 0, W4_POSTSCALE = 1 } w4_mode;
+
+typedef enum {
+  W4_OP_QUANTIZE = 0,
+  W4_OP_PACK = 1,
+  W4_OP_GEMV = 2,
+  W4_OP_GEMM = 3,
+  W4_OP_GEMM_DECOMP = 4
+} w4_op;
+
+/*
+ * w4_quantize -- quantize fp32 weights W^T [N][K] per group of G along K.
+ *
+ * fmt == W4_INT4_ASYM ([MixPE]: scale and zero shared within a group), per
+ * group, in fp64: lo = min(0, min w), hi = max(0, max w);
+ * s = fp16(fp32((hi - lo) / 15)); z = clamp(rint(-lo / s), 0, 15);
+ * q = clamp(rint(w / s) + z, 0, 15); a group with s == 0 gets q = z = 0.
+ * Writes codes [N][K], scale [N][K/G], zero [N][K/G].
+ *
+ * fmt == W4_NF4 ([NF4]): a = fp16(max |w|) per block of G; idx = the index i
+ * minimizing |w - c_i * a| in fp64 over the 16 fp32 NormalFloat levels c_i
+ * (lowest i on ties); a block with a == 0 gets idx = 7 (the zero level).
+ * Writes codes [N][K] and the absmax into `scale`; `zero` must be NULL.
+ *
+ * rint is round-half-to-even.  Results are bit-exact functions of the input;
+ * weights must be finite.  Codes are unpacked; see w4_pack.
+ */
+int w4_quantize(const float* wt, int K, int N, int G, int fmt,
+                uint8_t* codes, uint16_t* scale, uint16_t* zero, void* stream);
+
+/*
+ * w4_pack -- pack codes [N][K] (values 0..15) into [N][K/2] bytes, low nibble
+ * = even k.  Four-bit storage is the 4x reduction against fp16 noted on the
+ * [NF4] page.  Requires K % 32 == 0.  Codes above 15 are masked to 4 bits.
+ */
+int w4_pack(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream);
+
+/*
+ * w4_gemv -- decode-shaped product y[M][N] = x[M][K] . W', 1 <= M <= 32.
+ *
+ * Reads each packed weight once from HBM.  The group scale (and, for INT4, the
+ * zero point) is applied to each group's partial sum after accumulation
+ * ([MixPE]); NF4 levels come from a small on-chip table ([NF4]: codebook in
+ * shared memory).  `ws`/`ws_bytes`: workspace of at least
+ * w4_workspace_bytes(W4_OP_GEMV, ...) bytes (may be 0, then ws may be NULL).
+ * Output y is fp16, rounded to nearest-even from fp32 accumulation.
+ */
+int w4_gemv(const uint16_t* x, int M, int K, int N,
+            const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
+            int G, int fmt, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * w4_gemm -- prefill-shaped product y[M][N] = x[M][K] . W' for any M >= 1 on
+ * fp16 matrix cores, in `mode` W4_DQ_F16 or W4_POSTSCALE (see w4_mode), for
+ * either weight format.  Workspace as for w4_gemv with W4_OP_GEMM.
+ */
+int w4_gemm(const uint16_t* x, int M, int K, int N,
+            const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
+            int G, int fmt, int mode, uint16_t* y, void* ws, size_t ws_bytes,
+            void* stream);
+
+/*
+ * w4_gemm_decomp -- Multi-Scale Dequant product ([MSD]): the fp16 activations
+ * are split into `nslices` (1 or 2) int8 slices with per-token fp32 scales,
+ * and each slice is multiplied directly with the 4-bit integer weights on the
+ * int8 matrix cores, with no conversion of the weights to a floating type.
+ *
+ * Decomposition, per token m, in fp64 with r = x: s_j = fp32(max|r| / 127);
+ * A_j = clamp(rint(r / s_j), -127, 127); r -= s_j * A_j; a zero scale gives an
+ * all-zero slice.  Products: D_j[m,g,n] = sum_{k in g} A_j[m,k] * (q[n,k] -
+ * z[n,g]) exactly in int32; y[m,n] = sum_j s_j[m] * sum_g s[n,g] * D_j[m,g,n]
+ * accumulated in fp32 and rounded to fp16.
+ *
+ * INT4 weights only: NF4 levels are not integers, so fmt-free inputs with
+ * zero == NULL return W4_EUNSUPPORTED.
+ * Optional outputs (NULL to skip): slices_out int8 [nslices][M][K];
+ * tok_scale_out fp32 [nslices][M]; acc_out int32 [nslices][M][K/G][N], the
+ * per-group integer accumulators (a debugging aid for small shapes).
+ * Workspace: at least w4_workspace_bytes(W4_OP_GEMM_DECOMP, M, K, N, G,
+ * nslices) bytes; it holds the slices and scales when the optional outputs
+ * are NULL.
+ */
+int w4_gemm_decomp(const uint16_t* x, int M, int K, int N,
+                   const uint8_t* packed, const uint16_t* scale,
+                   const uint16_t* zero, int G, int nslices, uint16_t* y,
+                   int8_t* slices_out, float* tok_scale_out, int32_t* acc_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * w4_workspace_bytes -- bytes of workspace an entry point needs for the given
+ * shape.  `fmt_or_mode`: the w4_fmt for W4_OP_GEMV, the w4_mode for
+ * W4_OP_GEMM, nslices for W4_OP_GEMM_DECOMP.  Host-only; returns 0 for ops
+ * that need none and (size_t)-1 for an invalid op.
+ */
+size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode);
+
+/* Host-only: copies the library's 16 fp32 NF4 levels into out16 (host). */
+int w4_nf4_levels(float* out16);
+
+/* Host-only: static text for a w4_status value. */
+const char* w4_status_str(int status);
+
+/* Host-only: message of the last failed call on this thread ("" if none). */
+const char* w4_last_error(void);
+
+/* Host-only: library version string. */
+const char* w4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H_ */

@@ -102,7 +102,7 @@ def quantize_int4_asym(wt: np.ndarray, G: int):
     1. lo = min(0, min w), hi = max(0, max w)  (range widened to hold 0, so the
        zero point is always a valid code);
     2. s = fp16(fp32((hi - lo) / 15))  (rounding staged fp64 -> fp32 -> fp16);
-    3. z = clamp(rint(-lo / s), 0, 15)  (an integer, stored as fp16);
+    3. z = clamp(rint(-lo / s), 0, 15)  (an integer, stored as fp16, +0 for 0);
     4. q = clamp(rint(w / s) + z, 0, 15);
     5. if s == 0 the group is all zero: q = z = 0.
 
@@ -119,7 +119,9 @@ def quantize_int4_asym(wt: np.ndarray, G: int):
     s = s16.astype(np.float64)
     nz = s != 0.0
     safe = np.where(nz, s, 1.0)
-    z = np.clip(np.rint(-lo / safe), 0, INT4_LEVELS)
+    # "+ 0.0" turns a -0 (from lo == +0) into +0: the zero point is the
+    # integer 0, stored as the fp16 bit pattern 0x0000.
+    z = np.clip(np.rint(-lo / safe), 0, INT4_LEVELS) + 0.0
     q = np.clip(np.rint(w / safe[..., None]) + z[..., None], 0, INT4_LEVELS)
     z = np.where(nz, z, 0.0)
     q = np.where(nz[..., None], q, 0.0)

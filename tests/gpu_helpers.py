@@ -1,0 +1,49 @@
+"""Helpers for the GPU parity tests: device transfer, oracle-side weight prep,
+and the parity metrics.  The oracle side only ever sees seeded inputs and its
+own results; nothing computed by the HIP path is fed back into it."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+
+TOL_ROW_REL_L2 = 2e-3  # max over rows of ||y - y_ref||_2 / ||y_ref||_2
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU: deselect with -m 'not gpu'")
+
+
+def announce(*parts):
+    """Names the case before a GPU step (flushed, so a fault still leaves it)."""
+    print("[gpu case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def oracle_weights(fmt, w, G):
+    """Oracle quantization of W^T (numpy): codes, scale, zero (None for NF4)."""
+    if fmt == o.FMT_INT4_ASYM:
+        return o.quantize_int4_asym(w, G)
+    codes, absmax = o.quantize_nf4(w, G)
+    return codes, absmax, None
+
+
+def upload_weights(codes, scale, zero):
+    """Oracle-packed weights on the device."""
+    packed = dev(o.pack_nibbles(codes))
+    return packed, dev(scale), (None if zero is None else dev(zero))
+
+
+def row_rel_l2(y_gpu, y_ref):
+    return o.max_row_rel_l2(np.asarray(y_gpu, dtype=np.float64), y_ref)

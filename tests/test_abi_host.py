@@ -1,0 +1,118 @@
+"""Host-only checks of the C ABI (no GPU needed, no compute launched).
+
+* libw4.so loads and exports every function include/w4.h declares;
+* the library's NF4 level table is bit-equal to the oracle's derivation;
+* argument errors return their documented status before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+W4_OK, W4_EINVAL, W4_EUNSUPPORTED, W4_EWORKSPACE, W4_EHIP = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def L():
+    import bit_weight_quantized_amd as w4
+    if not os.path.exists(w4.lib_path):
+        import bit_weight_quantized_amd.build as b
+        b.build()
+    return w4.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for want in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp",
+                 "w4_workspace_bytes", "w4_status_str", "w4_last_error"):
+        assert want in fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [f for f in declared_functions() if not hasattr(L, f)]
+    assert not missing, missing
+
+
+def test_nf4_levels_bit_equal_to_oracle(L):
+    import bit_weight_quantized_amd as w4
+    lib_levels = np.array(w4.nf4_levels(), dtype=np.float32)
+    assert np.array_equal(lib_levels.view(np.uint32), o.nf4_codebook().view(np.uint32))
+
+
+def test_status_strings(L):
+    for st in (W4_OK, W4_EINVAL, W4_EUNSUPPORTED, W4_EWORKSPACE, W4_EHIP):
+        assert L.w4_status_str(st)
+    assert L.w4_version().startswith(b"w4")
+
+
+FAKE = ctypes.c_void_p(0x7F0000001000)  # never dereferenced: every call below fails validation first
+MISALIGNED = ctypes.c_void_p(0x7F0000001001)
+
+
+def _gemv(L, M=1, K=256, N=32, packed=FAKE, scale=FAKE, zero=FAKE, G=128, fmt=0, x=FAKE, y=FAKE):
+    return L.w4_gemv(x, M, K, N, packed, scale, zero, G, fmt, y, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), W4_EINVAL),
+    (dict(M=33), W4_EINVAL),
+    (dict(K=200), W4_EINVAL),          # K % G != 0
+    (dict(G=32, K=256), W4_EINVAL),    # G not in {64, 128}
+    (dict(N=40), W4_EINVAL),           # N % 16 != 0
+    (dict(fmt=7), W4_EINVAL),
+    (dict(zero=None), W4_EINVAL),      # INT4 without zero points
+    (dict(fmt=1), W4_EINVAL),          # NF4 with zero points
+    (dict(x=None), W4_EINVAL),
+    (dict(packed=MISALIGNED), W4_EINVAL),
+])
+def test_gemv_argument_errors(L, kw, status):
+    assert _gemv(L, **kw) == status
+    assert L.w4_last_error()  # a message was recorded
+
+
+def test_gemm_argument_errors(L):
+    args = [FAKE, 64, 256, 32, FAKE, FAKE, FAKE, 128, 0]
+    assert L.w4_gemm(*args, 5, FAKE, None, 0, None) == W4_EINVAL  # unknown mode
+    assert L.w4_gemm(FAKE, 64, 256, 30, FAKE, FAKE, FAKE, 128, 0, 0, FAKE, None, 0, None) == W4_EINVAL
+
+
+def test_decomp_argument_errors(L):
+    base = dict(x=FAKE, M=4, K=256, N=32, packed=FAKE, scale=FAKE, zero=FAKE, G=128, ns=2)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return L.w4_gemm_decomp(a["x"], a["M"], a["K"], a["N"], a["packed"], a["scale"], a["zero"],
+                                a["G"], a["ns"], FAKE, None, None, None, a.get("ws"),
+                                a.get("wsb", 0), None)
+    assert call(ns=3) == W4_EINVAL
+    assert call(zero=None) == W4_EUNSUPPORTED  # NF4 weights cannot feed int8 matrix cores
+    assert call() == W4_EWORKSPACE              # slices/scales need a workspace
+    need = L.w4_workspace_bytes(4, 4, 256, 32, 128, 2)
+    assert need >= 2 * 4 * 256 + 2 * 4 * 4
+    assert call(ws=FAKE, wsb=need - 1) == W4_EWORKSPACE
+
+
+def test_quantize_and_pack_argument_errors(L):
+    assert L.w4_quantize(FAKE, 100, 16, 64, 0, FAKE, FAKE, FAKE, None) == W4_EINVAL
+    assert L.w4_quantize(FAKE, 128, 16, 64, 1, FAKE, FAKE, FAKE, None) == W4_EINVAL  # NF4 + zero
+    assert L.w4_quantize(FAKE, 128, 16, 64, 0, FAKE, FAKE, None, None) == W4_EINVAL  # INT4 no zero
+    assert L.w4_pack(FAKE, 48, 16, FAKE, None) == W4_EINVAL
+    assert L.w4_pack(MISALIGNED, 64, 16, FAKE, None) == W4_EINVAL
+
+
+def test_workspace_bytes(L):
+    assert L.w4_workspace_bytes(2, 1, 8192, 8192, 128, 0) == 0
+    assert L.w4_workspace_bytes(99, 1, 1, 1, 1, 0) == ctypes.c_size_t(-1).value

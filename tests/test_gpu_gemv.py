@@ -1,0 +1,122 @@
+"""GPU parity: w4_gemv against the fp64 oracle.
+
+Small shapes use oracle-quantized, oracle-packed weights uploaded as is, and
+compare every output.  Full-size shapes (the decode and MLP layers) run the
+whole GPU pipeline and compare a sample of output columns whose weight rows
+the oracle quantizes itself from the same seeded weights."""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_quantized_amd as w4
+import oracle as o
+import workloads as wl
+from gpu_helpers import (TOL_ROW_REL_L2, announce, dev, host, oracle_weights, require_gpu,
+                         row_rel_l2, upload_weights)
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [(o.FMT_INT4_ASYM, 128), (o.FMT_INT4_ASYM, 64), (o.FMT_NF4, 64), (o.FMT_NF4, 128)]
+
+
+def run_small(fmt, G, M, K, N, seed, outliers=True):
+    w = wl.make_weight(seed, 0, N, K)
+    x = wl.make_activations(seed, 0, M, K, outliers=outliers)
+    codes, scale, zero = oracle_weights(fmt, w, G)
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    announce("gemv", dict(fmt=fmt, G=G, M=M, K=K, N=N, seed=seed))
+    y = w4.gemv(dev(x), packed, sc, zc, G, fmt)
+    torch.cuda.synchronize()
+    y_ref = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
+    return host(y), y_ref
+
+
+@pytest.mark.parametrize("fmt,G", FMTS)
+@pytest.mark.parametrize("M", [1, 2, 5, 16, 17, 32])
+@pytest.mark.parametrize("K,N", [(128, 16), (640, 48), (1024, 1040), (2048, 256)])
+def test_gemv_small(fmt, G, M, K, N):
+    if K % G:
+        pytest.skip("K not a multiple of G")
+    y, y_ref = run_small(fmt, G, M, K, N, seed=100 + M)
+    assert y.shape == (M, N)
+    err = row_rel_l2(y, y_ref)
+    assert err <= TOL_ROW_REL_L2, err
+
+
+@pytest.mark.parametrize("rt,nw", [(1, 1), (2, 3), (4, 8), (1, 8), (2, 2)])
+def test_gemv_launch_variants_agree(monkeypatch, rt, nw):
+    """Every work split gives results within tolerance of the oracle (split-K
+    and row-tiling races would show here)."""
+    monkeypatch.setenv("W4_GEMV_RT", str(rt))
+    monkeypatch.setenv("W4_GEMV_NW", str(nw))
+    for fmt, G in FMTS[:3]:
+        y, y_ref = run_small(fmt, G, 3, 1536, 208, seed=7)
+        assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
+
+
+def test_gemv_cfg1_both_formats():
+    """1024 x 1024, G = 64, M = 1, no outliers (the single-GEMV workload)."""
+    for fmt in (o.FMT_INT4_ASYM, o.FMT_NF4):
+        y, y_ref = run_small(fmt, 64, 1, 1024, 1024, seed=1, outliers=False)
+        assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
+
+
+def test_gemv_zero_activations_and_weights():
+    require_gpu()
+    K, N = 256, 32
+    w = np.zeros((N, K), np.float32)
+    w[: N // 2] = wl.make_weight(5, 0, N // 2, K)
+    for fmt, G in FMTS[:3]:
+        codes, scale, zero = oracle_weights(fmt, w, G)
+        packed, sc, zc = upload_weights(codes, scale, zero)
+        x = np.zeros((2, K), np.float16)
+        x[1] = wl.make_activations(5, 0, 1, K)[0]
+        announce("gemv zeros", fmt, G)
+        y = host(w4.gemv(dev(x), packed, sc, zc, G, fmt))
+        assert np.all(y[0] == 0)
+        assert np.all(y[1, N // 2:] == 0)
+        y_ref = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
+        assert o.max_row_rel_l2(y[1:], y_ref[1:]) <= TOL_ROW_REL_L2
+
+
+def test_gemv_repeatable():
+    """Two runs give bit-identical outputs (deterministic reduction order)."""
+    require_gpu()
+    w = wl.make_weight(9, 0, 512, 4096)
+    x = wl.make_activations(9, 0, 4, 4096)
+    codes, scale, zero = oracle_weights(o.FMT_INT4_ASYM, w, 128)
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    xd = dev(x)
+    announce("gemv repeat")
+    a = host(w4.gemv(xd, packed, sc, zc, 128, 0))
+    b = host(w4.gemv(xd, packed, sc, zc, 128, 0))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def full_size_case(fmt, G, M, K, N, cfg, mat, n_sample=160):
+    w = wl.make_weight(cfg, mat, N, K)
+    x = wl.make_activations(cfg, mat, M, K)
+    announce("gemv full", dict(fmt=fmt, G=G, M=M, K=K, N=N))
+    codes, scale, zero = w4.quantize(dev(w), G, fmt)
+    packed = w4.pack(codes)
+    y = host(w4.gemv(dev(x), packed, scale, zero, G, fmt))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(cfg).choice(N, n_sample, replace=False)]))
+    rc, rs, rz = oracle_weights(fmt, w[rows], G)
+    assert np.array_equal(host(codes[rows]), rc)  # the sampled weights are the oracle's
+    y_ref = o.matmul_ref(x, o.dequant(fmt, rc, rs, rz, G))
+    return y[:, rows], y_ref
+
+
+@pytest.mark.parametrize("fmt,G", [(o.FMT_INT4_ASYM, 128), (o.FMT_NF4, 64)])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemv_decode_layer_8192(fmt, G, M):
+    y, y_ref = full_size_case(fmt, G, M, 8192, 8192, cfg=2, mat=0)
+    assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
+
+
+@pytest.mark.parametrize("fmt,G", [(o.FMT_INT4_ASYM, 128), (o.FMT_NF4, 64)])
+@pytest.mark.parametrize("M,K,N", [(1, 8192, 28672), (32, 8192, 28672), (8, 28672, 8192)])
+def test_gemv_mlp_layers(fmt, G, M, K, N):
+    y, y_ref = full_size_case(fmt, G, M, K, N, cfg=3, mat=0 if N == 28672 else 1, n_sample=96)
+    assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
