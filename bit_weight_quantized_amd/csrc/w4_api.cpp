@@ -26,6 +26,8 @@ int check_matmul_shape(const char* fn, int M, int K, int N, int G) {
   if (!valid_group(G)) return fail(W4_EINVAL, "%s: G must be 64 or 128 (got %d)", fn, G);
   if (K % G != 0) return fail(W4_EINVAL, "%s: K=%d is not a multiple of G=%d", fn, K, G);
   if (N % 16 != 0) return fail(W4_EINVAL, "%s: N=%d is not a multiple of 16", fn, N);
+  if ((uint64_t)(N + 16) * (uint64_t)(K / 2) >= (1ull << 32))
+    return fail(W4_EINVAL, "%s: packed weights of %d x %d exceed the 4 GiB addressable per matrix", fn, N, K);
   return W4_OK;
 }
 
@@ -103,14 +105,18 @@ int w4_gemv(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
             const uint16_t* scale, const uint16_t* zero, int G, int fmt, uint16_t* y,
             void* ws, size_t ws_bytes, void* stream) {
   g_last_error[0] = '\0';
-  (void)ws;
-  (void)ws_bytes;
   int st;
   if ((st = check_matmul_shape("w4_gemv", M, K, N, G)) != W4_OK) return st;
   if (M > 32) return fail(W4_EINVAL, "w4_gemv: M must be <= 32 (got %d); use w4_gemm", M);
   if ((st = check_weights("w4_gemv", packed, scale, zero, fmt)) != W4_OK) return st;
   if ((st = check_io("w4_gemv", x, y)) != W4_OK) return st;
-  return launch_gemv(x, M, K, N, packed, scale, zero, G, fmt, y, (hipStream_t)stream);
+  const GemvPlan plan = plan_gemv(M, K, N, G);
+  if (plan.ws_bytes > 0) {
+    if (!ws || ws_bytes < plan.ws_bytes)
+      return fail(W4_EWORKSPACE, "w4_gemv: workspace of %zu bytes required (got %zu)", plan.ws_bytes, ws_bytes);
+    if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemv: workspace must be 16-byte aligned");
+  }
+  return launch_gemv(plan, x, M, K, N, packed, scale, zero, G, fmt, y, ws, (hipStream_t)stream);
 }
 
 int w4_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
@@ -160,14 +166,14 @@ int w4_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed
 }
 
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
-  (void)N;
-  (void)G;
   switch (op) {
     case W4_OP_QUANTIZE:
     case W4_OP_PACK:
-    case W4_OP_GEMV:
     case W4_OP_GEMM:
       return 0;
+    case W4_OP_GEMV:
+      if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G) return 0;
+      return plan_gemv(M, K, N, G).ws_bytes;
     case W4_OP_GEMM_DECOMP:
       if (M < 1 || K < 1 || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
       return decomp_workspace_bytes(M, K, fmt_or_mode);

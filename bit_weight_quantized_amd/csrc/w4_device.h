@@ -44,6 +44,18 @@ __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
                                                __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
 }
 
+// Raw buffer access.  The descriptor covers [base, base + bytes); loads at
+// offsets past `bytes` return zeros instead of touching memory.
+constexpr int kBufferFlags = 0x00020000;  // descriptor word 3 for gfx9 raw buffers
+constexpr int kNonTemporal = 2;           // cache-policy bit: streaming (nt)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
+}
+
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }

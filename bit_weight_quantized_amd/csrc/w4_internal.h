@@ -21,9 +21,17 @@ int launch_quantize_nf4(const float* wt, int K, int N, int G, uint8_t* codes,
                         uint16_t* absmax, hipStream_t s);
 int launch_pack(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t s);
 
-int launch_gemv(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
-                const uint16_t* scale, const uint16_t* zero, int G, int fmt,
-                uint16_t* y, hipStream_t s);
+// Launch shape of the GEMV: token tiles (mt), row waves and K waves per
+// workgroup (nwr, nwk), K slices over workgroups (s), grid rows, dynamic LDS
+// and workspace bytes (split-K partials + ticket counters).
+struct GemvPlan {
+  int mt, nwr, nwk, s, ring, row_blocks;
+  size_t lds_bytes, ws_partial_bytes, ws_bytes;
+};
+GemvPlan plan_gemv(int M, int K, int N, int G);
+int launch_gemv(const GemvPlan& plan, const uint16_t* x, int M, int K, int N,
+                const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
+                int G, int fmt, uint16_t* y, void* ws, hipStream_t s);
 
 int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
                 const uint16_t* scale, const uint16_t* zero, int G, int fmt,
