@@ -185,7 +185,7 @@ def gemm_decomp(x, packed, scale, zero, G: int, nslices: int = 2, *, out=None, s
     M = x.shape[0]
     out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
     ws_n = workspace_bytes(OP_GEMM_DECOMP, M, K, N, G, nslices)
-    if workspace is None and ws_n and (slices_out is None or tok_scale_out is None):
+    if workspace is None and ws_n:  # slices, scales (unless given) and per-group slice sums
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
     _check("w4_gemm_decomp", lib().w4_gemm_decomp(
         _ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, nslices, _ptr(out),

@@ -124,7 +124,7 @@ int w4_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
             uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
   g_last_error[0] = '\0';
   (void)ws;
-  (void)ws_bytes;
+  (void)ws_bytes;  // the tiled product needs no workspace
   int st;
   if ((st = check_matmul_shape("w4_gemm", M, K, N, G)) != W4_OK) return st;
   if (mode != W4_DQ_F16 && mode != W4_POSTSCALE) return fail(W4_EINVAL, "w4_gemm: unknown mode %d", mode);
@@ -149,19 +149,17 @@ int w4_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed
   if ((slices_out && !aligned16(slices_out)) || (tok_scale_out && !aligned16(tok_scale_out)) ||
       (acc_out && !aligned16(acc_out)))
     return fail(W4_EINVAL, "w4_gemm_decomp: optional outputs must be 16-byte aligned");
-  const size_t need = decomp_workspace_bytes(M, K, nslices);
-  int8_t* sl = slices_out;
-  float* ts = tok_scale_out;
-  if (!sl || !ts) {
-    if (!ws || ws_bytes < need)
-      return fail(W4_EWORKSPACE, "w4_gemm_decomp: workspace of %zu bytes required (got %zu)", need, ws_bytes);
-    if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemm_decomp: workspace must be 16-byte aligned");
-    char* base = static_cast<char*>(ws);
-    const size_t slice_bytes = ((size_t)nslices * M * K + 255) & ~(size_t)255;
-    if (!sl) sl = reinterpret_cast<int8_t*>(base);
-    if (!ts) ts = reinterpret_cast<float*>(base + slice_bytes);
-  }
-  return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, y, sl, ts, acc_out,
+  const size_t need = decomp_workspace_bytes(M, K, G, nslices);
+  if (!ws || ws_bytes < need)
+    return fail(W4_EWORKSPACE, "w4_gemm_decomp: workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemm_decomp: workspace must be 16-byte aligned");
+  char* base = static_cast<char*>(ws);
+  const size_t slice_bytes = ((size_t)nslices * M * K + 255) / 256 * 256;
+  const size_t scale_bytes = ((size_t)nslices * M * sizeof(float) + 255) / 256 * 256;
+  int8_t* sl = slices_out ? slices_out : reinterpret_cast<int8_t*>(base);
+  float* ts = tok_scale_out ? tok_scale_out : reinterpret_cast<float*>(base + slice_bytes);
+  int32_t* gsum = reinterpret_cast<int32_t*>(base + slice_bytes + scale_bytes);
+  return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, y, sl, ts, gsum, acc_out,
                             (hipStream_t)stream);
 }
 
@@ -175,8 +173,8 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
       if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G) return 0;
       return plan_gemv(M, K, N, G).ws_bytes;
     case W4_OP_GEMM_DECOMP:
-      if (M < 1 || K < 1 || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
-      return decomp_workspace_bytes(M, K, fmt_or_mode);
+      if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
+      return decomp_workspace_bytes(M, K, G, fmt_or_mode);
     default:
       return (size_t)-1;
   }

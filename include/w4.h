@@ -129,7 +129,7 @@ int w4_gemv(const uint16_t* x, int M, int K, int N,
 /*
  * w4_gemm -- prefill-shaped product y[M][N] = x[M][K] . W' for any M >= 1 on
  * fp16 matrix cores, in `mode` W4_DQ_F16 or W4_POSTSCALE (see w4_mode), for
- * either weight format.  Workspace as for w4_gemv with W4_OP_GEMM.
+ * either weight format.  Needs no workspace: ws may be NULL, ws_bytes 0.
  */
 int w4_gemm(const uint16_t* x, int M, int K, int N,
             const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
@@ -148,14 +148,15 @@ int w4_gemm(const uint16_t* x, int M, int K, int N,
  * z[n,g]) exactly in int32; y[m,n] = sum_j s_j[m] * sum_g s[n,g] * D_j[m,g,n]
  * accumulated in fp32 and rounded to fp16.
  *
- * INT4 weights only: NF4 levels are not integers, so fmt-free inputs with
- * zero == NULL return W4_EUNSUPPORTED.
+ * INT4 weights only: NF4 levels are not integers, so NF4 weights (zero ==
+ * NULL) return W4_EUNSUPPORTED.  K / G must not exceed 512.
  * Optional outputs (NULL to skip): slices_out int8 [nslices][M][K];
  * tok_scale_out fp32 [nslices][M]; acc_out int32 [nslices][M][K/G][N], the
  * per-group integer accumulators (a debugging aid for small shapes).
- * Workspace: at least w4_workspace_bytes(W4_OP_GEMM_DECOMP, M, K, N, G,
- * nslices) bytes; it holds the slices and scales when the optional outputs
- * are NULL.
+ * Workspace (required, 16-byte aligned, contents need not be initialised):
+ * at least w4_workspace_bytes(W4_OP_GEMM_DECOMP, M, K, N, G, nslices) bytes;
+ * it holds the per-group slice sums, and the slices and scales when the
+ * optional outputs are NULL.  Calls that overlap in time must not share it.
  */
 int w4_gemm_decomp(const uint16_t* x, int M, int K, int N,
                    const uint8_t* packed, const uint16_t* scale,

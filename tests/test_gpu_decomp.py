@@ -1,0 +1,132 @@
+"""GPU parity: w4_gemm_decomp (Multi-Scale Dequant) against the fp64 oracle.
+
+The int8 slices, the per-token scales and the per-group int32 accumulators are
+integer (or fp32 decision) results and must be bit-exact; the fp16 output is
+compared with the oracle's recombination of its own accumulators within the
+row-relative tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_quantized_amd as w4
+import oracle as o
+import workloads as wl
+from gpu_helpers import (TOL_ROW_REL_L2, announce, dev, host, oracle_weights, require_gpu,
+                         row_rel_l2, upload_weights)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decomp(x, codes, scale, zero, G, nslices, with_acc=True):
+    M, K = x.shape
+    N = codes.shape[0]
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    sl = torch.empty((nslices, M, K), dtype=torch.int8, device="cuda")
+    ts = torch.empty((nslices, M), dtype=torch.float32, device="cuda")
+    acc = torch.empty((nslices, M, K // G, N), dtype=torch.int32, device="cuda") if with_acc else None
+    y, _, _, _ = w4.gemm_decomp(dev(x), packed, sc, zc, G, nslices, slices_out=sl, tok_scale_out=ts,
+                                acc_out=acc)
+    return host(y), host(sl), host(ts), (host(acc) if with_acc else None)
+
+
+@pytest.mark.parametrize("G", [128, 64])
+@pytest.mark.parametrize("nslices", [2, 1])
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 640, 48), (130, 1024, 272), (257, 512, 144),
+                                   (64, 2048, 256)])
+def test_decomp_small(G, nslices, M, K, N):
+    if K % G:
+        pytest.skip("K not a multiple of G")
+    require_gpu()
+    w = wl.make_weight(300 + M, 0, N, K)
+    x = wl.make_activations(300 + M, 0, M, K)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    announce("decomp", dict(G=G, nslices=nslices, M=M, K=K, N=N))
+    y, sl, ts, acc = run_decomp(x, codes, scale, zero, G, nslices)
+    A, S = o.decompose_activations(x, nslices)
+    assert np.array_equal(sl, A)
+    assert np.array_equal(ts.view(np.uint32), S.view(np.uint32))
+    D = o.msd_accumulators(A, codes, zero, G)
+    assert np.array_equal(acc.astype(np.int64), D)
+    assert row_rel_l2(y, o.msd_result(S, D, scale)) <= TOL_ROW_REL_L2
+
+
+def test_decomp_degenerate_rows():
+    """A zero token row (both scales 0, output exactly 0); a row of integers
+    with max |x| = 127 (first scale exactly 1, residual 0, second slice all
+    zero); a row with one non-zero entry; a single huge outlier."""
+    require_gpu()
+    M, K, N, G = 6, 256, 64, 128
+    x = wl.make_activations(13, 0, M, K)
+    x[0] = 0
+    x[1] = np.float16(np.random.default_rng(13).integers(-127, 128, K))
+    x[1, 5] = 127
+    x[2] = 0
+    x[2, 77] = -3.5
+    x[3, 100] = 30000
+    w = wl.make_weight(13, 0, N, K)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    announce("decomp degenerate")
+    y, sl, ts, acc = run_decomp(x, codes, scale, zero, G, 2)
+    A, S = o.decompose_activations(x, 2)
+    assert S[0, 1] == 1.0 and S[1, 1] == 0.0 and S[0, 0] == 0.0
+    assert np.array_equal(sl, A)
+    assert np.array_equal(ts.view(np.uint32), S.view(np.uint32))
+    D = o.msd_accumulators(A, codes, zero, G)
+    assert np.array_equal(acc.astype(np.int64), D)
+    assert np.all(y[0] == 0)
+    ref = o.msd_result(S, D, scale)
+    assert row_rel_l2(y[1:], ref[1:]) <= TOL_ROW_REL_L2
+
+
+def test_decomp_repeatable_without_optional_outputs():
+    """The workspace-only call (no optional outputs) gives the same bits as
+    the call that returns slices and accumulators, twice."""
+    require_gpu()
+    M, K, N, G = 200, 1024, 192, 128
+    x = wl.make_activations(14, 0, M, K)
+    codes, scale, zero = o.quantize_int4_asym(wl.make_weight(14, 0, N, K), G)
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    xd = dev(x)
+    ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8, device="cuda")
+    announce("decomp repeat")
+    a = host(w4.gemm_decomp(xd, packed, sc, zc, G, 2, workspace=ws))
+    b = host(w4.gemm_decomp(xd, packed, sc, zc, G, 2, workspace=ws))
+    c, _, _, _ = run_decomp(x, codes, scale, zero, G, 2)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.array_equal(a.view(np.uint16), c.view(np.uint16))
+
+
+def test_decomp_rejects_nf4():
+    require_gpu()
+    K, N, G = 256, 32, 64
+    codes, absmax = o.quantize_nf4(wl.make_weight(15, 0, N, K), G)
+    packed, sc, _ = upload_weights(codes, absmax, None)
+    x = dev(wl.make_activations(15, 0, 2, K))
+    with pytest.raises(w4.W4Error) as e:
+        w4.gemm_decomp(x, packed, sc, None, G, 2)
+    assert e.value.status == -2
+
+
+@pytest.mark.parametrize("nslices", [2, 1])
+def test_decomp_prefill_m2048_k5120_n25600(nslices):
+    """Full prefill shape: slices and scales bit-exact over the whole input;
+    outputs compared on sampled columns."""
+    M, K, N, G = 2048, 5120, 25600, 128
+    w = wl.make_weight(4, 0, N, K)
+    x = wl.make_activations(4, 0, M, K)
+    announce("decomp full quantize")
+    codes, scale, zero = w4.quantize(dev(w), G, w4.INT4_ASYM)
+    packed = w4.pack(codes)
+    sl = torch.empty((nslices, M, K), dtype=torch.int8, device="cuda")
+    ts = torch.empty((nslices, M), dtype=torch.float32, device="cuda")
+    announce("decomp prefill", dict(nslices=nslices, M=M, K=K, N=N))
+    y, _, _, _ = w4.gemm_decomp(dev(x), packed, scale, zero, G, nslices, slices_out=sl, tok_scale_out=ts)
+    y = host(y)
+    A, S = o.decompose_activations(x, nslices)
+    assert np.array_equal(host(sl), A)
+    assert np.array_equal(host(ts).view(np.uint32), S.view(np.uint32))
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(41).choice(N, 64, replace=False)]))
+    rc, rs, rz = o.quantize_int4_asym(w[rows], G)
+    assert np.array_equal(host(codes[rows]), rc)
+    ref = o.msd_result(S, o.msd_accumulators(A, rc, rz, G), rs)
+    assert row_rel_l2(y[:, rows], ref) <= TOL_ROW_REL_L2
