@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=64,
                     help="eager launches per variant for the live per-kernel timing")
+    ap.add_argument("--gemm-reps", type=int, default=20,
+                    help="timed launches per prefill GEMM path (0 skips the GEMM section)")
     return ap.parse_args()
 
 
@@ -98,6 +100,55 @@ def cpu_baseline_decode(variants, K, N, n_rows, min_seconds=10.0):
             total_bytes += weight_stream_bytes(fmt, K, n_rows, G)
         reps += 1
     return total_bytes / total_s / 1e9, total_s, threads, reps
+
+
+def bench_gemm_prefill(w4, torch, reps):
+    """Prefill product M = 2048, K = 5120, N = 25600, INT4 g128, three ways:
+    dequantize-to-fp16 MFMA, post-scaled fp16 MFMA, and the two-slice
+    Multi-Scale Dequant int8 MFMA (its activation decomposition included).
+    Back-to-back launches between HIP events on the launch stream."""
+    import workloads as wl
+    M, K, N, G = 2048, 5120, 25600, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(40000)
+    w = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    codes, scale, zero = w4.quantize(w, G, w4.INT4_ASYM)
+    packed = w4.pack(codes)
+    del w, codes
+    x = torch.from_numpy(wl.make_activations(4, 0, M, K)).cuda()
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8, device="cuda")
+    flops = 2.0 * M * N * K
+    paths = {
+        "dq_f16": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.DQ_F16, out=y), 1, FP16_MFMA_PEAK_TFLOPS),
+        "postscale": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.POSTSCALE, out=y), 1,
+                      FP16_MFMA_PEAK_TFLOPS),
+        "msd2": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 2, out=y, workspace=ws), 2, INT8_MFMA_PEAK_TOPS),
+    }
+    res = {}
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for name, (fn, mfma_mult, peak) in paths.items():
+            for _ in range(3):
+                fn()
+            st.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for _ in range(reps):
+                fn()
+            b.record(st)
+            st.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            mfma_rate = flops * mfma_mult / (us * 1e-6) / 1e12
+            res[name] = {"us_per_call": round(us, 1), "tflops_useful": round(flops / (us * 1e-6) / 1e12, 1),
+                         "mfma_tops": round(mfma_rate, 1), "mfma_peak": peak,
+                         "frac": round(mfma_rate / peak, 4)}
+    return {"workload": "prefill_gemm_m2048_k5120_n25600", "M": M, "K": K, "N": N, "fmt": "int4_asym_g128",
+            "flops_per_call": flops, "calls_timed": reps,
+            "note": "fp16 paths against the dense fp16 MFMA peak; msd2 issues 2 int8 products per useful "
+                    "multiply-add and is measured against the dense int8 peak; msd2 time includes the "
+                    "activation decomposition",
+            "paths": res}
 
 
 def main():
@@ -187,6 +238,8 @@ def main():
     sum_us = sum(p["us_avg"] for p in per)
     achieved = sum_bytes / (sum_us * 1e-6) / 1e9
 
+    gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
+
     cpu = None
     if not args.no_cpu_baseline:
         gbs, secs, threads, reps = cpu_baseline_decode(variants, K, N, n_rows=2048)
@@ -216,6 +269,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": "packed N*K/2 + fp16 scales (+ zeros) = %d" % per_set},
         "per_launch": per,
+        "gemm_prefill": gemm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
