@@ -20,20 +20,30 @@
 //
 // Tiling.  A workgroup of 4 waves (2 x 2) owns a BM x BN output tile, BM = 128
 // rows of tokens, BN = 32 * NT columns; each wave owns 64 x 16*NT.  The K loop
-// steps one quantization group at a time: the group's activation tile, packed
-// weight tile, scales/zeros (and for MSD the slice sums) are staged in LDS,
-// while the next group's tiles are already loading into registers.
+// steps one weight-tile column (128 K positions: one or two quantization
+// groups) at a time: the step's activation tile, weight tiles, scales/zeros
+// (and for MSD the slice sums) are stored to LDS while the next step's tiles
+// are already loading into registers.
+//
+// Weight tiles.  The packed weights are stored as 1 KB tiles of 16 rows x 128
+// K positions in which lane l finds its B operands in bytes 16 l .. 16 l + 15
+// (word t: 8 codes of row l % 16 at K positions 32 t + 8 (l / 16) + 0..7).  A
+// tile is copied to LDS as is and read back with one 16-byte load per lane.
 //
 // Operand order.  INT4 codes are unpacked in the order the cheapest mask/shift
-// sequence produces them (for fp16: (k0,k4),(k1,k5),(k2,k6),(k3,k7) per 8
-// codes; for int8: even codes then odd codes per 8), and the activation tile
-// is permuted the same way once, when it is written to LDS.  A dot product is
+// sequence produces them (for fp16: (c0,c4),(c1,c5),(c2,c6),(c3,c7) per word;
+// for int8: even codes then odd codes per word), and the activation tile is
+// permuted the same way once, when it is written to LDS.  A dot product is
 // invariant under a common permutation of its terms.
 //
 // INT4 post-scaled operands are exact: the masked code q in the low bits of an
 // fp16 lane is the subnormal q * 2^-24, and q - z is formed by one packed
 // subtraction of subnormals (exact), so the group's fp32 partial is
 // 2^-24 * sum x (q - z) and is scaled by s * 2^24.
+//
+// Block order.  Workgroups are dealt to the 8 XCDs round-robin; the kernel
+// renumbers them so each XCD gets a contiguous run of output tiles, N fastest,
+// and the token rows it shares stay in that XCD's L2.
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -42,6 +52,8 @@ namespace {
 
 constexpr int kGemmThreads = 256;
 constexpr int kBM = 128;
+constexpr int kStepK = 128;  // one weight-tile column per K step
+constexpr int kXcds = 8;
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -54,38 +66,35 @@ __device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
 
-template <int PATH>
-struct PathTraits;
-
-// LDS tile geometry per path.  Row strides are padded by 16 bytes so the 16
-// rows one fragment read touches fall in different banks.
-template <int PATH, int LB, int NT, int NS>
+// LDS geometry per path.  Activation planes are padded by one 16-byte row so
+// the staging writes (16 planes per token row) fall in different banks.
+template <int PATH, int NT, int NS, int GPT>
 struct GemmGeom {
-  static constexpr int G = 8 * LB;
   static constexpr int BN = 32 * NT;
-  static constexpr int A_ELEM = PATH == 2 ? 1 : 2;                  // bytes per activation element
-  static constexpr int A_STRIDE = G * A_ELEM + 16;                  // bytes per tile row
-  static constexpr int A_BYTES = NS * kBM * A_STRIDE;
-  static constexpr int B_STRIDE = G / 2 + 16;
-  static constexpr int B_BYTES = BN * B_STRIDE;
+  static constexpr int A_PLANES = PATH == 2 ? 8 : 16;  // fp16: chunk c of 8; int8: (product u, k-block j)
+  static constexpr int A_PLANE = (kBM + 1) * 16;
+  static constexpr int A_BYTES = (PATH == 2 ? NS : 1) * A_PLANES * A_PLANE;
+  static constexpr int B_BYTES = (BN / 16) * 1024;
   static constexpr int OFF_B = A_BYTES;
-  static constexpr int OFF_S = OFF_B + B_BYTES;                     // scale, zero bits per column
-  static constexpr int OFF_T = OFF_S + BN * 4;                      // MSD: per-row fp32 T, int SA_j
-  static constexpr int LDS = OFF_T + (PATH == 2 ? kBM * 4 * (1 + NS) : 0);
-  static constexpr int A_CHUNKS = NS * kBM * G * A_ELEM / 16;       // 16-byte global chunks per group
-  static constexpr int B_CHUNKS = BN * (G / 2) / 16;
-  static constexpr int A_PER_T = A_CHUNKS / kGemmThreads;
-  static constexpr int B_PER_T = (B_CHUNKS + kGemmThreads - 1) / kGemmThreads;
+  static constexpr int OFF_S = OFF_B + B_BYTES;          // [GPT][scale, zero][BN] fp16 bits
+  static constexpr int OFF_T = OFF_S + GPT * 2 * BN * 2;  // MSD: T [GPT][BM] fp32, SA [GPT][NS][BM] int32
+  static constexpr int OFF_R = OFF_T + (PATH == 2 ? GPT * kBM * 4 * (1 + NS) : 0);  // MSD: s2/s1 per row
+  static constexpr int LDS = OFF_R + (PATH == 2 ? kBM * 4 : 0);
+  static constexpr int A_UNITS = PATH == 2 ? NS * kBM * 8 : kBM * 16;  // 16-byte global chunks per step
+  static constexpr int B_UNITS = (BN / 16) * 64;
+  static constexpr int A_PER_T = A_UNITS / kGemmThreads;
+  static constexpr int B_PER_T = (B_UNITS + kGemmThreads - 1) / kGemmThreads;
 };
 
-template <int PATH, int FMT, int LB, int NT, int NS>
+template <int PATH, int FMT, int GPT, int NT, int NS, bool DBG>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const void* __restrict__ a_src, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
     const float* __restrict__ tok_scale, const int32_t* __restrict__ gsum, int32_t* __restrict__ acc_out) {
-  using Geo = GemmGeom<PATH, LB, NT, NS>;
-  constexpr int G = Geo::G;
+  using Geo = GemmGeom<PATH, NT, NS, GPT>;
   constexpr int BN = Geo::BN;
+  constexpr int G = kStepK / GPT;
+  constexpr int WPG = 4 / GPT;  // fp16 products (tile words) per group
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
 
@@ -94,123 +103,130 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave % 2, wn = wave / 2;
   const int ln = lane % 16, kb = lane / 16;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * kBM;
+
+  // XCD-aware renumbering (a bijection of [0, tiles))
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles = gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, idx = b / kXcds;
+  const int per = tiles / kXcds, rem = tiles % kXcds;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int n0 = (logical % tiles_n) * BN;
+  const int m0 = (logical / tiles_n) * kBM;
+
   const int ng = K / G;
-  const size_t row_bytes = (size_t)K / 2;
+  const int KT = K / kStepK;
+  const int ntile_last = N / 16 - 1;
 
   if constexpr (FMT == 1) {
-    for (int b = tid; b < 256; b += kGemmThreads)
-      lut[b] = (uint32_t)float_to_half_bits(nf4_level(b & 15)) |
-               ((uint32_t)float_to_half_bits(nf4_level(b >> 4)) << 16);
+    for (int i = tid; i < 256; i += kGemmThreads)
+      lut[i] = (uint32_t)float_to_half_bits(nf4_level(i & 15)) |
+               ((uint32_t)float_to_half_bits(nf4_level(i >> 4)) << 16);
   }
 
-  // ---- global -> register prefetch of one group's tiles
+  // ---- global -> register prefetch of one K step
   u32x4 ra[Geo::A_PER_T];
   u32x4 rb[Geo::B_PER_T];
-  uint16_t rs = 0, rz = 0;   // thread t < BN: column n0 + t
-  int32_t rsa[NS];           // MSD, thread t < BM: slice sums of row m0 + t
-  auto prefetch = [&](int g) {
+  uint16_t rs = 0, rz = 0;  // thread t < GPT*BN: group t / BN, column n0 + t % BN
+  int32_t rsa[NS];          // MSD, thread t < GPT*BM: slice sums of group t / BM, row m0 + t % BM
+  auto prefetch = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < Geo::A_PER_T; ++i) {
-      const int c = tid + i * kGemmThreads;
+      const int u = tid + i * kGemmThreads;
       if constexpr (PATH == 2) {
-        constexpr int per_row = G / 16;
-        const int j = c / (kBM * per_row);
-        const int rem = c - j * kBM * per_row;
-        const int r = rem / per_row, cc = rem - r * per_row;
-        const int8_t* src = static_cast<const int8_t*>(a_src) + ((size_t)j * M + min(m0 + r, M - 1)) * K +
-                            (size_t)g * G + cc * 16;
+        const int js = u / (kBM * 8);
+        const int rem8 = u - js * kBM * 8;
+        const int m = rem8 / 8, c = rem8 % 8;
+        const int8_t* src = static_cast<const int8_t*>(a_src) + ((size_t)js * M + min(m0 + m, M - 1)) * K +
+                            (size_t)kt * kStepK + c * 16;
         ra[i] = *reinterpret_cast<const u32x4*>(src);
       } else {
-        constexpr int per_row = G / 8;
-        const int r = c / per_row, cc = c - r * per_row;
+        const int m = u / 16, c = u % 16;
         const uint16_t* src =
-            static_cast<const uint16_t*>(a_src) + (size_t)min(m0 + r, M - 1) * K + (size_t)g * G + cc * 8;
+            static_cast<const uint16_t*>(a_src) + (size_t)min(m0 + m, M - 1) * K + (size_t)kt * kStepK + c * 8;
         ra[i] = *reinterpret_cast<const u32x4*>(src);
       }
     }
 #pragma unroll
     for (int i = 0; i < Geo::B_PER_T; ++i) {
-      constexpr int per_row = G / 32;
-      const int c = min(tid + i * kGemmThreads, Geo::B_CHUNKS - 1);
-      const int r = c / per_row, cc = c - r * per_row;
-      rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          packed + (size_t)min(n0 + r, N - 1) * row_bytes + (size_t)g * (G / 2) + cc * 16));
+      const int u = min(tid + i * kGemmThreads, Geo::B_UNITS - 1);
+      const int t = u / 64, slot = u % 64;
+      const size_t tile = (size_t)min(n0 / 16 + t, ntile_last) * KT + kt;
+      rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + tile * 1024 + slot * 16));
     }
     {
-      const size_t o = (size_t)min(n0 + min(tid, BN - 1), N - 1) * ng + g;
+      const int t = min(tid, GPT * BN - 1);
+      const size_t o = (size_t)min(n0 + t % BN, N - 1) * ng + (size_t)kt * GPT + t / BN;
       rs = scale[o];
       if constexpr (FMT == 0) rz = zero[o];
     }
     if constexpr (PATH == 2) {
-      const int r = min(m0 + min(tid, kBM - 1), M - 1);
+      const int t = min(tid, GPT * kBM - 1);
+      const int r = min(m0 + t % kBM, M - 1);
 #pragma unroll
-      for (int j = 0; j < NS; ++j) rsa[j] = gsum[((size_t)j * M + r) * ng + g];
+      for (int j = 0; j < NS; ++j) rsa[j] = gsum[((size_t)j * M + r) * ng + (size_t)kt * GPT + t / kBM];
     }
   };
 
-  // per-token ratio s2/s1 (MSD): for the 16 rows this lane's accumulators hold
-  float rr[4][4];
+  // per-token ratio s2/s1 (MSD), one per tile row, in LDS (read after the
+  // first barrier of the K loop)
   if constexpr (PATH == 2) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = min(m0 + wm * 64 + mt * 16 + 4 * kb + i, M - 1);
-        const float s1 = tok_scale[m];
-        rr[mt][i] = (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
-      }
+    if (tid < kBM) {
+      const int m = min(m0 + tid, M - 1);
+      const float s1 = tok_scale[m];
+      reinterpret_cast<float*>(smem + Geo::OFF_R)[tid] =
+          (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
+    }
   }
 
   // ---- registers -> LDS (activation permutation applied here)
   auto stash = [&]() {
 #pragma unroll
     for (int i = 0; i < Geo::A_PER_T; ++i) {
-      const int c = tid + i * kGemmThreads;
-      u32x4 v = ra[i];
-      unsigned char* dst;
+      const int u = tid + i * kGemmThreads;
+      const u32x4 v = ra[i];
       if constexpr (PATH == 2) {
-        constexpr int per_row = G / 16;
-        const int j = c / (kBM * per_row);
-        const int rem = c - j * kBM * per_row;
-        const int r = rem / per_row, cc = rem - r * per_row;
-        dst = smem + (j * kBM + r) * Geo::A_STRIDE + cc * 16;
-        // bytes (0,2,4,6 | 1,3,5,7) of each 8: even codes, then odd codes
-        v = u32x4{perm_b32(v.y, v.x, 0x06040200u), perm_b32(v.y, v.x, 0x07050301u),
-                  perm_b32(v.w, v.z, 0x06040200u), perm_b32(v.w, v.z, 0x07050301u)};
+        const int js = u / (kBM * 8);
+        const int rem8 = u - js * kBM * 8;
+        const int m = rem8 / 8, c = rem8 % 8;
+        // K positions 16c .. 16c+15 of the step: product pu = c / 4, half h of
+        // its 32-blocks, k-blocks jj and jj + 1; bytes reordered even-then-odd
+        const int pu = c / 4, h = (c % 4) / 2, jj = 2 * (c % 2);
+        unsigned char* base = smem + js * Geo::A_PLANES * Geo::A_PLANE + m * 16 + 8 * h;
+        *reinterpret_cast<u32x2*>(base + (pu * 4 + jj) * Geo::A_PLANE) =
+            u32x2{perm_b32(v.y, v.x, 0x06040200u), perm_b32(v.y, v.x, 0x07050301u)};
+        *reinterpret_cast<u32x2*>(base + (pu * 4 + jj + 1) * Geo::A_PLANE) =
+            u32x2{perm_b32(v.w, v.z, 0x06040200u), perm_b32(v.w, v.z, 0x07050301u)};
       } else {
-        constexpr int per_row = G / 8;
-        const int r = c / per_row, cc = c - r * per_row;
-        dst = smem + r * Geo::A_STRIDE + cc * 16;
+        const int m = u / 16, c = u % 16;
+        u32x4 q = v;
         if constexpr (FMT == 0)  // (x0,x4),(x1,x5),(x2,x6),(x3,x7)
-          v = u32x4{pair_lo(v.x, v.z), pair_hi(v.x, v.z), pair_lo(v.y, v.w), pair_hi(v.y, v.w)};
+          q = u32x4{pair_lo(v.x, v.z), pair_hi(v.x, v.z), pair_lo(v.y, v.w), pair_hi(v.y, v.w)};
+        *reinterpret_cast<u32x4*>(smem + c * Geo::A_PLANE + m * 16) = q;
       }
-      *reinterpret_cast<u32x4*>(dst) = v;
     }
 #pragma unroll
     for (int i = 0; i < Geo::B_PER_T; ++i) {
-      constexpr int per_row = G / 32;
-      const int c = tid + i * kGemmThreads;
-      if (c < Geo::B_CHUNKS) {
-        const int r = c / per_row, cc = c - r * per_row;
-        *reinterpret_cast<u32x4*>(smem + Geo::OFF_B + r * Geo::B_STRIDE + cc * 16) = rb[i];
-      }
+      const int u = tid + i * kGemmThreads;
+      if (u < Geo::B_UNITS) *reinterpret_cast<u32x4*>(smem + Geo::OFF_B + u * 16) = rb[i];
     }
-    if (tid < BN) {
-      reinterpret_cast<uint16_t*>(smem + Geo::OFF_S)[tid] = rs;
-      reinterpret_cast<uint16_t*>(smem + Geo::OFF_S)[BN + tid] = rz;
+    if (tid < GPT * BN) {
+      const int gi = tid / BN, col = tid % BN;
+      reinterpret_cast<uint16_t*>(smem + Geo::OFF_S)[(gi * 2) * BN + col] = rs;
+      reinterpret_cast<uint16_t*>(smem + Geo::OFF_S)[(gi * 2 + 1) * BN + col] = rz;
     }
     if constexpr (PATH == 2) {
-      if (tid < kBM) {
-        const int m = min(m0 + tid, M - 1);
+      if (tid < GPT * kBM) {
+        const int gi = tid / kBM, row = tid % kBM;
+        const int m = min(m0 + row, M - 1);
         const float s1 = tok_scale[m];
         const float r = (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
         float t = (float)rsa[0];
         if constexpr (NS == 2) t = fmaf(r, (float)rsa[1], t);
-        reinterpret_cast<float*>(smem + Geo::OFF_T)[tid] = t;
+        reinterpret_cast<float*>(smem + Geo::OFF_T)[gi * kBM + row] = t;
 #pragma unroll
-        for (int j = 0; j < NS; ++j) reinterpret_cast<int32_t*>(smem + Geo::OFF_T)[kBM * (1 + j) + tid] = rsa[j];
+        for (int j = 0; j < NS; ++j)
+          reinterpret_cast<int32_t*>(smem + Geo::OFF_T)[GPT * kBM + (gi * NS + j) * kBM + row] = rsa[j];
       }
     }
   };
@@ -221,144 +237,155 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(smem + Geo::OFF_S);
   prefetch(0);
-  for (int g = 0; g < ng; ++g) {
-    __syncthreads();  // previous group's compute is done with LDS
+  for (int kt = 0; kt < KT; ++kt) {
+    __syncthreads();  // the previous step's products are done with LDS
     stash();
     __syncthreads();
-    prefetch(min(g + 1, ng - 1));  // unconditional: the last group is fetched twice
+    prefetch(min(kt + 1, KT - 1));  // unconditional: the last step is fetched twice
 
-    const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(smem + Geo::OFF_S);
+    // this lane's 16 bytes of each of the wave's weight tiles
+    u32x4 Bq[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      Bq[nt] = *reinterpret_cast<const u32x4*>(smem + Geo::OFF_B + (wn * NT + nt) * 1024 + lane * 16);
+
     if constexpr (PATH != 2) {
-      f32x4 acc[4][NT];
-      if constexpr (PATH == 1) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      // per-column (lane) constants of this group
-      uint32_t zz[NT], sp[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int col = wn * 16 * NT + nt * 16 + ln;
-        const uint32_t sb = s_lds[col];
-        sp[nt] = sb | (sb << 16);  // (s, s) fp16 pair
-        if constexpr (FMT == 0) {
-          const uint32_t z = (uint32_t)half_bits_to_float(s_lds[BN + col]);  // integer 0..15
-          // PS: (z, z) * 2^-24 as subnormal fp16; DQ: (1024 + z, 1024 + z)
-          zz[nt] = PATH == 1 ? (z | (z << 16)) : ((0x6400u | z) | ((0x6400u | z) << 16));
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < G / 32; ++ks) {
-        u32x4 A[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          A[mt] = *reinterpret_cast<const u32x4*>(smem + (wm * 64 + mt * 16 + ln) * Geo::A_STRIDE +
-                                                  (ks * 32 + 8 * kb) * 2);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = wn * 16 * NT + nt * 16 + ln;
-          const uint32_t v =
-              *reinterpret_cast<const uint32_t*>(smem + Geo::OFF_B + col * Geo::B_STRIDE + ks * 16 + 4 * kb);
-          u32x4 B;
-          if constexpr (FMT == 0) {
-            uint32_t w[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t q = (v >> (4 * j)) & 0x000F000Fu;
-              if constexpr (PATH == 1) {
-                w[j] = pk_sub_f16(q, zz[nt]);  // (q - z) * 2^-24, exact
-              } else {
-                w[j] = pk_mul_f16(pk_sub_f16(q | 0x64006400u, zz[nt]), sp[nt]);  // fp16(s * (q - z))
-              }
-            }
-            B = u32x4{w[0], w[1], w[2], w[3]};
-          } else {
-            B = u32x4{lut[v & 0xFFu], lut[(v >> 8) & 0xFFu], lut[(v >> 16) & 0xFFu], lut[v >> 24]};
-            if constexpr (PATH == 0) B = u32x4{pk_mul_f16(B.x, sp[nt]), pk_mul_f16(B.y, sp[nt]),
-                                               pk_mul_f16(B.z, sp[nt]), pk_mul_f16(B.w, sp[nt])};
-          }
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            if constexpr (PATH == 1) acc[mt][nt] = mfma_f16(A[mt], B, acc[mt][nt]);
-            else C[mt][nt] = mfma_f16(A[mt], B, C[mt][nt]);
-          }
-        }
-      }
-      if constexpr (PATH == 1) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = wn * 16 * NT + nt * 16 + ln;
-          float sf = half_bits_to_float(s_lds[col]);
-          if constexpr (FMT == 0) sf *= 16777216.0f;
+      for (int gi = 0; gi < GPT; ++gi) {
+        f32x4 acc[4][NT];
+        if constexpr (PATH == 1) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) C[mt][nt][i] = fmaf(sf, acc[mt][nt][i], C[mt][nt][i]);
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // per-column (lane) constants of this group
+        uint32_t zz[NT], sp[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int col = wn * 16 * NT + nt * 16 + ln;
+          const uint32_t sb = s_lds[(gi * 2) * BN + col];
+          sp[nt] = sb | (sb << 16);  // (s, s) fp16 pair
+          if constexpr (FMT == 0) {
+            const uint32_t z = (uint32_t)half_bits_to_float(s_lds[(gi * 2 + 1) * BN + col]);  // 0..15
+            // PS: (z, z) * 2^-24 as subnormal fp16; DQ: (1024 + z, 1024 + z)
+            zz[nt] = PATH == 1 ? (z | (z << 16)) : ((0x6400u | z) | ((0x6400u | z) << 16));
+          }
+        }
+#pragma unroll
+        for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) {
+          u32x4 A[4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            A[mt] = *reinterpret_cast<const u32x4*>(smem + (4 * w + kb) * Geo::A_PLANE + (wm * 64 + mt * 16 + ln) * 16);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const uint32_t v = Bq[nt][w];
+            u32x4 B;
+            if constexpr (FMT == 0) {
+              uint32_t d[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t q = (v >> (4 * j)) & 0x000F000Fu;
+                if constexpr (PATH == 1) {
+                  d[j] = pk_sub_f16(q, zz[nt]);  // (q - z) * 2^-24, exact
+                } else {
+                  d[j] = pk_mul_f16(pk_sub_f16(q | 0x64006400u, zz[nt]), sp[nt]);  // fp16(s * (q - z))
+                }
+              }
+              B = u32x4{d[0], d[1], d[2], d[3]};
+            } else {
+              B = u32x4{lut[v & 0xFFu], lut[(v >> 8) & 0xFFu], lut[(v >> 16) & 0xFFu], lut[v >> 24]};
+              if constexpr (PATH == 0) B = u32x4{pk_mul_f16(B.x, sp[nt]), pk_mul_f16(B.y, sp[nt]),
+                                                 pk_mul_f16(B.z, sp[nt]), pk_mul_f16(B.w, sp[nt])};
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+              if constexpr (PATH == 1) acc[mt][nt] = mfma_f16(A[mt], B, acc[mt][nt]);
+              else C[mt][nt] = mfma_f16(A[mt], B, C[mt][nt]);
+            }
+          }
+        }
+        if constexpr (PATH == 1) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int col = wn * 16 * NT + nt * 16 + ln;
+            float sf = half_bits_to_float(s_lds[(gi * 2) * BN + col]);
+            if constexpr (FMT == 0) sf *= 16777216.0f;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) C[mt][nt][i] = fmaf(sf, acc[mt][nt][i], C[mt][nt][i]);
+          }
         }
       }
     } else {
-      // ---- MSD: int8 slices x int8 codes, int32 per group
-      i32x4 D[NS][4][NT];
+      // ---- MSD: int8 slices x int8 codes, exact int32 per group
+      const float* t_lds = reinterpret_cast<const float*>(smem + Geo::OFF_T);
+      const int32_t* sa_lds = reinterpret_cast<const int32_t*>(smem + Geo::OFF_T) + GPT * kBM;
+      constexpr int UPG = 2 / GPT;  // int8 products (64 K positions each) per group
 #pragma unroll
-      for (int j = 0; j < NS; ++j)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) D[j][mt][nt] = i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < G / 64; ++ks) {
-        u32x4 A[NS][4];
+      for (int gi = 0; gi < GPT; ++gi) {
+        i32x4 D[NS][4][NT];
 #pragma unroll
         for (int j = 0; j < NS; ++j)
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            A[j][mt] = *reinterpret_cast<const u32x4*>(smem + (j * kBM + wm * 64 + mt * 16 + ln) * Geo::A_STRIDE +
-                                                       ks * 64 + 16 * kb);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = wn * 16 * NT + nt * 16 + ln;
-          const u32x2 v =
-              *reinterpret_cast<const u32x2*>(smem + Geo::OFF_B + col * Geo::B_STRIDE + ks * 32 + 8 * kb);
-          const u32x4 B{v.x & 0x0F0F0F0Fu, (v.x >> 4) & 0x0F0F0F0Fu, v.y & 0x0F0F0F0Fu, (v.y >> 4) & 0x0F0F0F0Fu};
+            for (int nt = 0; nt < NT; ++nt) D[j][mt][nt] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int pu = gi * UPG; pu < (gi + 1) * UPG; ++pu) {
+          u32x4 A[NS][4];
 #pragma unroll
           for (int j = 0; j < NS; ++j)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) D[j][mt][nt] = mfma_i8(A[j][mt], B, D[j][mt][nt]);
-        }
-      }
-      // group epilogue: C' += s * (D1 + r * D2) - s * z * (SA1 + r * SA2)
-      const float* t_lds = reinterpret_cast<const float*>(smem + Geo::OFF_T);
-      const int32_t* sa_lds = reinterpret_cast<const int32_t*>(smem + Geo::OFF_T);
+            for (int mt = 0; mt < 4; ++mt)
+              A[j][mt] = *reinterpret_cast<const u32x4*>(smem + j * Geo::A_PLANES * Geo::A_PLANE +
+                                                         (pu * 4 + kb) * Geo::A_PLANE +
+                                                         (wm * 64 + mt * 16 + ln) * 16);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int col = wn * 16 * NT + nt * 16 + ln;
-        const float sv = half_bits_to_float(s_lds[col]);
-        const float zv = half_bits_to_float(s_lds[BN + col]);
-        const float nsz = -sv * zv;
+          for (int nt = 0; nt < NT; ++nt) {
+            const uint32_t w0 = Bq[nt][2 * pu], w1 = Bq[nt][2 * pu + 1];
+            const u32x4 B{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int rloc = wm * 64 + mt * 16 + 4 * kb;
-          const f32x4 T = *reinterpret_cast<const f32x4*>(t_lds + rloc);
+            for (int j = 0; j < NS; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float e = (float)D[0][mt][nt][i];
-            if constexpr (NS == 2) e = fmaf(rr[mt][i], (float)D[1][mt][nt][i], e);
-            C[mt][nt][i] = fmaf(sv, e, fmaf(nsz, T[i], C[mt][nt][i]));
+              for (int mt = 0; mt < 4; ++mt) D[j][mt][nt] = mfma_i8(A[j][mt], B, D[j][mt][nt]);
           }
-          if (acc_out) {  // debug output: exact integer per-group products, zero point folded
-            const int n = n0 + col;
-            const int z = (int)zv;
+        }
+        // group epilogue: C' += s * (D1 + r * D2) - s * z * (SA1 + r * SA2)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int col = wn * 16 * NT + nt * 16 + ln;
+          const float sv = half_bits_to_float(s_lds[(gi * 2) * BN + col]);
+          const float zv = half_bits_to_float(s_lds[(gi * 2 + 1) * BN + col]);
+          const float nsz = -sv * zv;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const int rloc = wm * 64 + mt * 16 + 4 * kb;
+            const f32x4 T = *reinterpret_cast<const f32x4*>(t_lds + gi * kBM + rloc);
+            const f32x4 rr = *reinterpret_cast<const f32x4*>(smem + Geo::OFF_R + rloc * 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int m = m0 + rloc + i;
-              if (m < M && n < N) {
+              float e = (float)D[0][mt][nt][i];
+              if constexpr (NS == 2) e = fmaf(rr[i], (float)D[1][mt][nt][i], e);
+              C[mt][nt][i] = fmaf(sv, e, fmaf(nsz, T[i], C[mt][nt][i]));
+            }
+            if constexpr (DBG) {  // debug output: exact integer per-group products, zero point folded
+              const int n = n0 + col;
+              const int z = (int)zv;
+              const int g = kt * GPT + gi;
 #pragma unroll
-                for (int j = 0; j < NS; ++j)
-                  acc_out[(((size_t)j * M + m) * ng + g) * N + n] =
-                      D[j][mt][nt][i] - z * sa_lds[kBM * (1 + j) + rloc + i];
+              for (int i = 0; i < 4; ++i) {
+                const int m = m0 + rloc + i;
+                if (m < M && n < N) {
+#pragma unroll
+                  for (int j = 0; j < NS; ++j)
+                    acc_out[(((size_t)j * M + m) * ng + g) * N + n] =
+                        D[j][mt][nt][i] - z * sa_lds[(gi * NS + j) * kBM + rloc + i];
+                }
               }
             }
           }
@@ -384,15 +411,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
 }
 
-template <int PATH, int FMT, int LB, int NT, int NS>
+template <int PATH, int FMT, int GPT, int NT, int NS>
 int launch_one(const void* a, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
                const uint16_t* zero, uint16_t* y, const float* tok_scale, const int32_t* gsum, int32_t* acc_out,
                hipStream_t s) {
-  using Geo = GemmGeom<PATH, LB, NT, NS>;
-  static_assert(Geo::A_CHUNKS % kGemmThreads == 0, "activation tile must split evenly over the threads");
-  const dim3 grid((unsigned)((N + Geo::BN - 1) / Geo::BN), (unsigned)((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gemm_kernel<PATH, FMT, LB, NT, NS>), grid, dim3(kGemmThreads), Geo::LDS, s, a, M, K, N, packed,
-                     scale, zero, y, tok_scale, gsum, acc_out);
+  using Geo = GemmGeom<PATH, NT, NS, GPT>;
+  static_assert(Geo::A_UNITS % kGemmThreads == 0, "activation tile must split evenly over the threads");
+  static_assert(GPT * Geo::BN <= kGemmThreads && GPT * kBM <= kGemmThreads, "one scale / row sum per thread");
+  const long tiles = (long)((N + Geo::BN - 1) / Geo::BN) * ((M + kBM - 1) / kBM);
+  if (acc_out)
+    hipLaunchKernelGGL((gemm_kernel<PATH, FMT, GPT, NT, NS, true>), dim3((unsigned)tiles), dim3(kGemmThreads), Geo::LDS,
+                       s, a, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out);
+  else
+    hipLaunchKernelGGL((gemm_kernel<PATH, FMT, GPT, NT, NS, false>), dim3((unsigned)tiles), dim3(kGemmThreads),
+                       Geo::LDS, s, a, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out);
   return check_launch(PATH == 2 ? "gemm_msd" : "gemm");
 }
 
@@ -401,22 +433,22 @@ int launch_one(const void* a, int M, int K, int N, const uint8_t* packed, const 
 int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
                 const uint16_t* zero, int G, int fmt, int mode, uint16_t* y, hipStream_t s) {
   constexpr int NT = 4;
-#define W4_GEMM_CASE(PATH, FMT, LB)                                                                          \
-  return launch_one<PATH, FMT, LB, NT, 1>(x, M, K, N, packed, scale, zero, y, nullptr, nullptr, nullptr, s)
+#define W4_GEMM_CASE(PATH, FMT, GPT) \
+  return launch_one<PATH, FMT, GPT, NT, 1>(x, M, K, N, packed, scale, zero, y, nullptr, nullptr, nullptr, s)
   if (mode == 0) {
     if (fmt == 0) {
-      if (G == 64) W4_GEMM_CASE(0, 0, 8);
-      W4_GEMM_CASE(0, 0, 16);
+      if (G == 64) W4_GEMM_CASE(0, 0, 2);
+      W4_GEMM_CASE(0, 0, 1);
     }
-    if (G == 64) W4_GEMM_CASE(0, 1, 8);
-    W4_GEMM_CASE(0, 1, 16);
+    if (G == 64) W4_GEMM_CASE(0, 1, 2);
+    W4_GEMM_CASE(0, 1, 1);
   }
   if (fmt == 0) {
-    if (G == 64) W4_GEMM_CASE(1, 0, 8);
-    W4_GEMM_CASE(1, 0, 16);
+    if (G == 64) W4_GEMM_CASE(1, 0, 2);
+    W4_GEMM_CASE(1, 0, 1);
   }
-  if (G == 64) W4_GEMM_CASE(1, 1, 8);
-  W4_GEMM_CASE(1, 1, 16);
+  if (G == 64) W4_GEMM_CASE(1, 1, 2);
+  W4_GEMM_CASE(1, 1, 1);
 #undef W4_GEMM_CASE
 }
 
@@ -434,11 +466,11 @@ int launch_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* pa
   if (st != 0) return st;
   constexpr int NT = 2;
   if (nslices == 1) {
-    if (G == 64) return launch_one<2, 0, 8, NT, 1>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
-    return launch_one<2, 0, 16, NT, 1>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
+    if (G == 64) return launch_one<2, 0, 2, NT, 1>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
+    return launch_one<2, 0, 1, NT, 1>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
   }
-  if (G == 64) return launch_one<2, 0, 8, NT, 2>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
-  return launch_one<2, 0, 16, NT, 2>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
+  if (G == 64) return launch_one<2, 0, 2, NT, 2>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
+  return launch_one<2, 0, 1, NT, 2>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
 }
 
 }  // namespace w4

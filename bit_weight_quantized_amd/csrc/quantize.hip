@@ -106,28 +106,41 @@ __global__ __launch_bounds__(kWave * kQuantWavesPerBlock) void quantize_nf4_kern
   if (lane == 0) absmax[blk] = a16;
 }
 
-// Each thread packs 32 codes (two 16-byte loads) into 16 bytes.
-__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes,
-                                                   long n_chunks, uint8_t* __restrict__ packed) {
-  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_chunks) return;
-  const u32x4* src = reinterpret_cast<const u32x4*>(codes) + 2 * t;
-  const u32x4 c0 = src[0], c1 = src[1];
-  u32x4 out;
-  const unsigned in[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  unsigned half[8];
+// Tile layout of the packed weights: tile (nb, kb) = rows 16 nb .. 16 nb + 15
+// x K positions 128 kb .. 128 kb + 127, 1024 contiguous bytes at
+// (nb * K / 128 + kb) * 1024.  "Lane" l = 16 j + r of a tile owns bytes
+// 16 l .. 16 l + 15: word t holds the 8 codes of row r at K positions
+// 32 t + 8 j + 0..7, two per byte, low nibble first.  One 16-byte load per
+// lane of a wave therefore delivers a whole tile, already in the operand
+// order of the 16x16 matrix-core products.
+//
+// One thread per 16-byte lane slot: four 8-byte code loads, 16 bytes out.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int K,
+                                                   long n_slots, uint8_t* __restrict__ packed) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_slots) return;
+  const int kt = K / 128;
+  const long tile = idx / 64;
+  const int l = (int)(idx % 64);
+  const long nb = tile / kt;
+  const int kb = (int)(tile % kt);
+  const int r = l % 16, j = l / 16;
+  const uint8_t* row = codes + (nb * 16 + r) * (long)K + kb * 128 + 8 * j;
+  uint32_t out[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // bytes (c0, c1, c2, c3) -> c0 | c1 << 4 in bits 0-7, c2 | c3 << 4 in bits 16-23
-    const unsigned v = in[i] & 0x0F0F0F0Fu;
-    const unsigned p = (v | (v >> 4)) & 0x00FF00FFu;
-    half[i] = (p & 0xFFu) | ((p >> 8) & 0xFF00u);
+  for (int t = 0; t < 4; ++t) {
+    const u32x2 c = *reinterpret_cast<const u32x2*>(row + 32 * t);  // codes k .. k + 7, one per byte
+    uint32_t w = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // bytes (c0, c1, c2, c3) -> c0 | c1 << 4 in bits 0-7, c2 | c3 << 4 in bits 8-15
+      const uint32_t v = c[h] & 0x0F0F0F0Fu;
+      const uint32_t p = (v | (v >> 4)) & 0x00FF00FFu;
+      w |= ((p & 0xFFu) | ((p >> 8) & 0xFF00u)) << (16 * h);
+    }
+    out[t] = w;
   }
-  out.x = half[0] | (half[1] << 16);
-  out.y = half[2] | (half[3] << 16);
-  out.z = half[4] | (half[5] << 16);
-  out.w = half[6] | (half[7] << 16);
-  reinterpret_cast<u32x4*>(packed)[t] = out;
+  reinterpret_cast<u32x4*>(packed)[idx] = u32x4{out[0], out[1], out[2], out[3]};
 }
 
 }  // namespace
@@ -159,10 +172,9 @@ int launch_quantize_nf4(const float* wt, int K, int N, int G, uint8_t* codes,
 }
 
 int launch_pack(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t s) {
-  const long n_chunks = (long)N * (K / 32);
-  if (n_chunks == 0) return 0;
-  const dim3 grid((unsigned)((n_chunks + 255) / 256));
-  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, codes, n_chunks, packed);
+  const long n_slots = (long)N * K / 32;  // 16 bytes = 32 codes each
+  if (n_slots == 0) return 0;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((n_slots + 255) / 256)), dim3(256), 0, s, codes, K, n_slots, packed);
   return check_launch("pack");
 }
 

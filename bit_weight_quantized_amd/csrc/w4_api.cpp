@@ -25,6 +25,7 @@ int check_matmul_shape(const char* fn, int M, int K, int N, int G) {
   if (K < 1 || N < 1) return fail(W4_EINVAL, "%s: K and N must be >= 1 (got K=%d N=%d)", fn, K, N);
   if (!valid_group(G)) return fail(W4_EINVAL, "%s: G must be 64 or 128 (got %d)", fn, G);
   if (K % G != 0) return fail(W4_EINVAL, "%s: K=%d is not a multiple of G=%d", fn, K, G);
+  if (K % 128 != 0) return fail(W4_EINVAL, "%s: K=%d is not a multiple of 128 (the weight tile)", fn, K);
   if (N % 16 != 0) return fail(W4_EINVAL, "%s: N=%d is not a multiple of 16", fn, N);
   if ((uint64_t)(N + 16) * (uint64_t)(K / 2) >= (1ull << 32))
     return fail(W4_EINVAL, "%s: packed weights of %d x %d exceed the 4 GiB addressable per matrix", fn, N, K);
@@ -95,7 +96,8 @@ int w4_quantize(const float* wt, int K, int N, int G, int fmt, uint8_t* codes,
 int w4_pack(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream) {
   g_last_error[0] = '\0';
   if (K < 1 || N < 1) return fail(W4_EINVAL, "w4_pack: K and N must be >= 1 (got K=%d N=%d)", K, N);
-  if (K % 32 != 0) return fail(W4_EINVAL, "w4_pack: K=%d is not a multiple of 32", K);
+  if (K % 128 != 0) return fail(W4_EINVAL, "w4_pack: K=%d is not a multiple of 128 (the weight tile)", K);
+  if (N % 16 != 0) return fail(W4_EINVAL, "w4_pack: N=%d is not a multiple of 16 (the weight tile)", N);
   if (!codes || !packed) return fail(W4_EINVAL, "w4_pack: codes and packed must be non-null");
   if (!aligned16(codes) || !aligned16(packed)) return fail(W4_EINVAL, "w4_pack: pointers must be 16-byte aligned");
   return launch_pack(codes, K, N, packed, (hipStream_t)stream);
@@ -170,7 +172,7 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
     case W4_OP_GEMM:
       return 0;
     case W4_OP_GEMV:
-      if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G) return 0;
+      if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G || K % 128) return 0;
       return plan_gemv(M, K, N, G).ws_bytes;
     case W4_OP_GEMM_DECOMP:
       if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;

@@ -215,6 +215,57 @@ def unpack_nibbles(packed) -> np.ndarray:
     return out
 
 
+TILE_ROWS = 16   # weight rows (output columns) per tile
+TILE_K = 128     # K positions per tile; one tile is 16 * 128 / 2 = 1024 bytes
+
+
+def tile_offset(n: int, k: int, K: int):
+    """Byte offset and nibble (0 low, 1 high) of code (n, k) in the tile layout.
+
+    READING: the pages fix no storage order.  The stored form groups the
+    row-major bytes of ``pack_nibbles`` into tiles of 16 rows x 128 K
+    positions, tile (n // 16, k // 128) at byte (n // 16 * K // 128 + k // 128)
+    * 1024.  Inside a tile, "lane" l = 16 j + r owns 16 bytes at 16 l: four
+    4-byte words, word t holding the 8 codes of row r at K positions
+    32 t + 8 j + 0..7 of the tile, in the byte order of ``pack_nibbles``.
+    """
+    nb, r = divmod(n, TILE_ROWS)
+    kb, kk = divmod(k, TILE_K)
+    t, rest = divmod(kk, 32)
+    j, p = divmod(rest, 8)
+    lane = TILE_ROWS * j + r
+    off = (nb * (K // TILE_K) + kb) * 1024 + lane * 16 + 4 * t + p // 2
+    return off, p % 2
+
+
+def tile_packed(packed) -> np.ndarray:
+    """Row-major packed bytes [N][K/2] -> the tile layout (same [N][K/2]
+    shape; row tile nb occupies the bytes of rows 16 nb .. 16 nb + 15).
+    The word arrangement of ``tile_offset``, written as a reshape/transpose."""
+    p = np.asarray(packed, dtype=np.uint8)
+    N, H = p.shape
+    K = 2 * H
+    assert N % TILE_ROWS == 0 and K % TILE_K == 0
+    # row word w covers k = 8 w .. 8 w + 7, w = 16 kb + 4 t + j
+    w = p.reshape(N // TILE_ROWS, TILE_ROWS, K // TILE_K, 4, 4, 4)  # [nb][r][kb][t][j][byte]
+    tiles = w.transpose(0, 2, 4, 1, 3, 5)                            # [nb][kb][j][r][t][byte]
+    return np.ascontiguousarray(tiles).reshape(N, H)
+
+
+def untile_packed(tiled) -> np.ndarray:
+    """Inverse of ``tile_packed``."""
+    t = np.asarray(tiled, dtype=np.uint8)
+    N, H = t.shape
+    K = 2 * H
+    w = t.reshape(N // TILE_ROWS, K // TILE_K, 4, TILE_ROWS, 4, 4)  # [nb][kb][j][r][t][byte]
+    return np.ascontiguousarray(w.transpose(0, 3, 1, 4, 2, 5)).reshape(N, H)
+
+
+def pack_w4(codes) -> np.ndarray:
+    """The stored weight form: nibble packing, then the tile layout."""
+    return tile_packed(pack_nibbles(codes))
+
+
 # --------------------------------------------------------------------------
 # products
 # --------------------------------------------------------------------------

@@ -41,7 +41,7 @@ def oracle_weights(fmt, w, G):
 
 def upload_weights(codes, scale, zero):
     """Oracle-packed weights on the device."""
-    packed = dev(o.pack_nibbles(codes))
+    packed = dev(o.pack_w4(codes))
     return packed, dev(scale), (None if zero is None else dev(zero))
 
 

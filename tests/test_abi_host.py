@@ -70,6 +70,7 @@ def _gemv(L, M=1, K=256, N=32, packed=FAKE, scale=FAKE, zero=FAKE, G=128, fmt=0,
     (dict(M=0), W4_EINVAL),
     (dict(M=33), W4_EINVAL),
     (dict(K=200), W4_EINVAL),          # K % G != 0
+    (dict(K=192, G=64), W4_EINVAL),    # K % 128 != 0 (the weight tile)
     (dict(G=32, K=256), W4_EINVAL),    # G not in {64, 128}
     (dict(N=40), W4_EINVAL),           # N % 16 != 0
     (dict(fmt=7), W4_EINVAL),
@@ -110,7 +111,9 @@ def test_quantize_and_pack_argument_errors(L):
     assert L.w4_quantize(FAKE, 128, 16, 64, 1, FAKE, FAKE, FAKE, None) == W4_EINVAL  # NF4 + zero
     assert L.w4_quantize(FAKE, 128, 16, 64, 0, FAKE, FAKE, None, None) == W4_EINVAL  # INT4 no zero
     assert L.w4_pack(FAKE, 48, 16, FAKE, None) == W4_EINVAL
-    assert L.w4_pack(MISALIGNED, 64, 16, FAKE, None) == W4_EINVAL
+    assert L.w4_pack(MISALIGNED, 128, 16, FAKE, None) == W4_EINVAL
+    assert L.w4_pack(FAKE, 192, 16, FAKE, None) == W4_EINVAL   # K % 128 != 0 (the weight tile)
+    assert L.w4_pack(FAKE, 128, 24, FAKE, None) == W4_EINVAL   # N % 16 != 0
 
 
 def test_workspace_bytes(L):

@@ -53,14 +53,15 @@ def test_quantize_special_groups():
                 assert np.array_equal(host(zero).view(np.uint16), rz.view(np.uint16))
 
 
-@pytest.mark.parametrize("N,K", [(16, 32), (48, 96), (256, 8192)])
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (256, 8192), (32, 28672)])
 def test_pack_bit_exact(N, K):
+    """The packed bytes in the tile layout equal the oracle's, byte for byte."""
     require_gpu()
     codes = np.random.default_rng(N + K).integers(0, 16, size=(N, K)).astype(np.uint8)
     announce("pack", N, K)
     packed = w4.pack(dev(codes))
     torch.cuda.synchronize()
-    assert np.array_equal(host(packed), o.pack_nibbles(codes))
+    assert np.array_equal(host(packed), o.pack_w4(codes))
 
 
 @pytest.mark.parametrize("fmt,G", [(o.FMT_INT4_ASYM, 128), (o.FMT_NF4, 64)])
@@ -74,10 +75,12 @@ def test_quantize_full_size_sampled_rows(fmt, G):
     codes, scale, zero = w4.quantize(dev(w), G, fmt)
     packed = w4.pack(codes)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).choice(N, 96, replace=False)]))
+    # whole 16-row tiles, so the packed bytes can be compared tile for tile
+    tiles = np.unique(np.concatenate([[0, N // 16 - 1], np.random.default_rng(1).choice(N // 16, 6, replace=False)]))
+    rows = (tiles[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
     rc, rs, rz = oracle_weights(fmt, w[rows], G)
     assert np.array_equal(host(codes[rows]), rc)
     assert np.array_equal(host(scale[rows]).view(np.uint16), rs.view(np.uint16))
     if fmt == o.FMT_INT4_ASYM:
         assert np.array_equal(host(zero[rows]).view(np.uint16), rz.view(np.uint16))
-    assert np.array_equal(host(packed[rows]), o.pack_nibbles(rc))
+    assert np.array_equal(host(packed[rows]), o.pack_w4(rc))

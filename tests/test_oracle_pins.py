@@ -211,6 +211,52 @@ def test_pack_round_trip_and_size():
     assert np.array_equal(o.unpack_nibbles(p), codes)
 
 
+def test_tile_layout_matches_offset_formula():
+    """Every code of a random 32 x 256 matrix sits at the byte and nibble the
+    per-element formula names (brute force over all positions)."""
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, (32, 256)).astype(np.uint8)
+    flat = o.pack_w4(codes).reshape(-1)
+    for n in range(32):
+        for k in range(256):
+            off, nib = o.tile_offset(n, k, 256)
+            assert (flat[off] >> (4 * nib)) & 15 == codes[n, k], (n, k)
+
+
+def test_tile_layout_golden_and_round_trip():
+    g = _golden("tile_layout_example.json")
+    N, K = g["N"], g["K"]
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    codes = ((n + k // 8 + 1) % 16).astype(np.uint8)
+    t = o.pack_w4(codes).reshape(-1)
+    for off, val in g["bytes"].items():
+        assert t[int(off)] == val, off
+    rng = np.random.default_rng(4)
+    c2 = rng.integers(0, 16, (48, 384)).astype(np.uint8)
+    p = o.pack_nibbles(c2)
+    assert np.array_equal(o.untile_packed(o.tile_packed(p)), p)
+    # a tile is 1 KB of contiguous bytes: row tile nb holds only rows 16 nb .. 16 nb + 15
+    t2 = o.tile_packed(p)
+    for nb in range(3):
+        assert sorted(t2[16 * nb:16 * nb + 16].reshape(-1)) == sorted(p[16 * nb:16 * nb + 16].reshape(-1))
+
+
+def test_planted_tile_mistake_rejected():
+    """Swapping the lane's row and K-block roles (a transposed operand) is caught."""
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, (32, 256)).astype(np.uint8)
+    p = o.pack_nibbles(codes)
+    w = p.reshape(2, 16, 2, 4, 4, 4).transpose(0, 2, 1, 4, 3, 5)  # [nb][kb][r][j]... wrong order
+    wrong = np.ascontiguousarray(w).reshape(32, 128).reshape(-1)
+    bad = 0
+    for n in range(32):
+        for k in range(0, 256, 7):
+            off, nib = o.tile_offset(n, k, 256)
+            bad += int((wrong[off] >> (4 * nib)) & 15 != codes[n, k])
+    assert bad > 0
+
+
 def test_planted_pack_mistake_rejected():
     codes = np.array([[1, 2, 3, 4]], np.uint8)
     swapped = (codes[:, 1::2] | (codes[:, 0::2] << 4)).astype(np.uint8)
