@@ -30,11 +30,13 @@
 // (word t: 8 codes of row l % 16 at K positions 32 t + 8 (l / 16) + 0..7).  A
 // tile is copied to LDS as is and read back with one 16-byte load per lane.
 //
-// Operand order.  INT4 codes are unpacked in the order the cheapest mask/shift
-// sequence produces them (for fp16: (c0,c4),(c1,c5),(c2,c6),(c3,c7) per word;
-// for int8: even codes then odd codes per word), and the activation tile is
-// permuted the same way once, when it is written to LDS.  A dot product is
-// invariant under a common permutation of its terms.
+// Operand order.  With the stored nibble order (even K positions in nibbles
+// 0-3, odd in 4-7) the fp16 masks (w >> 4i) & 0x000F000F give the pairs
+// (c0,c1),(c2,c3),... in K order, so INT4 activations are staged as they are.
+// The int8 masks (bytes c0 c4 c1 c5 | c2 c6 c3 c7) and the NF4 byte table
+// ((c0,c2),(c4,c6),(c1,c3),(c5,c7)) need the activation tile permuted the
+// same way once, when it is written to LDS; a dot product is invariant under a
+// common permutation of its terms.
 //
 // INT4 post-scaled operands are exact: the masked code q in the low bits of an
 // fp16 lane is the subnormal q * 2^-24, and q - z is formed by one packed
@@ -190,18 +192,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         const int rem8 = u - js * kBM * 8;
         const int m = rem8 / 8, c = rem8 % 8;
         // K positions 16c .. 16c+15 of the step: product pu = c / 4, half h of
-        // its 32-blocks, k-blocks jj and jj + 1; bytes reordered even-then-odd
+        // its 32-blocks, k-blocks jj and jj + 1; bytes reordered to the int8
+        // masks' order x0 x4 x1 x5 x2 x6 x3 x7
         const int pu = c / 4, h = (c % 4) / 2, jj = 2 * (c % 2);
         unsigned char* base = smem + js * Geo::A_PLANES * Geo::A_PLANE + m * 16 + 8 * h;
         *reinterpret_cast<u32x2*>(base + (pu * 4 + jj) * Geo::A_PLANE) =
-            u32x2{perm_b32(v.y, v.x, 0x06040200u), perm_b32(v.y, v.x, 0x07050301u)};
+            u32x2{perm_b32(v.y, v.x, 0x05010400u), perm_b32(v.y, v.x, 0x07030602u)};
         *reinterpret_cast<u32x2*>(base + (pu * 4 + jj + 1) * Geo::A_PLANE) =
-            u32x2{perm_b32(v.w, v.z, 0x06040200u), perm_b32(v.w, v.z, 0x07050301u)};
+            u32x2{perm_b32(v.w, v.z, 0x05010400u), perm_b32(v.w, v.z, 0x07030602u)};
       } else {
         const int m = u / 16, c = u % 16;
-        u32x4 q = v;
-        if constexpr (FMT == 0)  // (x0,x4),(x1,x5),(x2,x6),(x3,x7)
-          q = u32x4{pair_lo(v.x, v.z), pair_hi(v.x, v.z), pair_lo(v.y, v.w), pair_hi(v.y, v.w)};
+        u32x4 q = v;  // INT4: the masks yield (c0,c1),(c2,c3),... -- K order, stored as is
+        if constexpr (FMT == 1)  // NF4 level pairs of bytes 0..3: (x0,x2),(x4,x6),(x1,x3),(x5,x7)
+          q = u32x4{pair_lo(v.x, v.y), pair_lo(v.z, v.w), pair_hi(v.x, v.y), pair_hi(v.z, v.w)};
         *reinterpret_cast<u32x4*>(smem + c * Geo::A_PLANE + m * 16) = q;
       }
     }

@@ -31,11 +31,11 @@
 // INT4 operands.  A code q in the low nibble of an fp16 lane is the subnormal
 // value q * 2^-24 exactly, and in bits 4..7 it is q * 2^-20; masking the packed
 // word therefore yields exact fp16 operands in 5 VALU ops per 8 codes, with no
-// offset to cancel.  The masks pair codes (c0, c4), (c1, c5), (c2, c6),
-// (c3, c7) of a word, the odd-position ones (2^-20) meeting activations
-// pre-scaled by 1/16, so every product is x*q*2^-24; the staged activations
-// are permuted the same way.  The zero point is applied with the group's
-// activation sum: y += s * (2^24 * sum x*q - z * sum x).
+// offset to cancel.  With the stored nibble order the masks yield the pairs
+// (c0, c1), (c2, c3) * 16, (c4, c5), (c6, c7) * 16; the activations of the
+// scaled pairs are staged pre-scaled by 1/16, so every product is
+// x*q*2^-24.  The zero point is applied with the group's activation sum:
+// y += s * (2^24 * sum x*q - z * sum x).
 //
 // Split K.  With S > 1 each workgroup leaves its fp32 partial in the workspace
 // and the last one to finish a row block (a ticket counter) adds the S
@@ -224,9 +224,11 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     int m, r;
     div_small(u, n_chunks, inv_nc, m, r);
     if constexpr (FMT == 0) {
-      // (x0,x4), (x1,x5)/16, (x2,x6), (x3,x7)/16: the order the INT4 masks produce
-      q = u32x4{pair_lo(q.x, q.z), pk_mul_f16(pair_hi(q.x, q.z), kHalfSixteenthPair), pair_lo(q.y, q.w),
-                pk_mul_f16(pair_hi(q.y, q.w), kHalfSixteenthPair)};
+      // (x0,x1), (x2,x3)/16, (x4,x5), (x6,x7)/16: the order and scale the INT4 masks produce
+      q = u32x4{q.x, pk_mul_f16(q.y, kHalfSixteenthPair), q.z, pk_mul_f16(q.w, kHalfSixteenthPair)};
+    } else {
+      // (x0,x2), (x4,x6), (x1,x3), (x5,x7): the level pairs of bytes 0..3 of a word
+      q = u32x4{pair_lo(q.x, q.y), pair_lo(q.z, q.w), pair_hi(q.x, q.y), pair_hi(q.z, q.w)};
     }
     xs[r * M + m] = q;
   };

@@ -106,13 +106,15 @@ __global__ __launch_bounds__(kWave * kQuantWavesPerBlock) void quantize_nf4_kern
   if (lane == 0) absmax[blk] = a16;
 }
 
-// Tile layout of the packed weights: tile (nb, kb) = rows 16 nb .. 16 nb + 15
-// x K positions 128 kb .. 128 kb + 127, 1024 contiguous bytes at
-// (nb * K / 128 + kb) * 1024.  "Lane" l = 16 j + r of a tile owns bytes
-// 16 l .. 16 l + 15: word t holds the 8 codes of row r at K positions
-// 32 t + 8 j + 0..7, two per byte, low nibble first.  One 16-byte load per
-// lane of a wave therefore delivers a whole tile, already in the operand
-// order of the 16x16 matrix-core products.
+// Stored form of the packed weights: tiles of 16 rows x 128 K positions,
+// tile (nb, kb) = rows 16 nb .. 16 nb + 15 x K positions 128 kb .. 128 kb + 127,
+// 1024 contiguous bytes at (nb * K / 128 + kb) * 1024.  "Lane" l = 16 j + r of
+// a tile owns bytes 16 l .. 16 l + 15: little-endian word t holds the 8 codes
+// of row r at K positions 32 t + 8 j + 0..7, the even positions in nibbles
+// 0-3 and the odd ones in nibbles 4-7 (nibble p: position 0,2,4,6,1,3,5,7).
+// One 16-byte load per lane of a wave therefore delivers a whole tile in the
+// operand order of the 16x16 matrix-core products, and the masks
+// (w >> 4 i) & 0x000F000F produce the fp16 pairs (c_2i, c_2i+1) in K order.
 //
 // One thread per 16-byte lane slot: four 8-byte code loads, 16 bytes out.
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int K,
@@ -127,18 +129,17 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ c
   const int r = l % 16, j = l / 16;
   const uint8_t* row = codes + (nb * 16 + r) * (long)K + kb * 128 + 8 * j;
   uint32_t out[4];
+  // four codes (one per byte, each < 16) -> four nibbles, first code lowest
+  auto nib4 = [](uint32_t v) {
+    const uint32_t p = (v | (v >> 4)) & 0x00FF00FFu;
+    return (p & 0xFFu) | ((p >> 8) & 0xFF00u);
+  };
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const u32x2 c = *reinterpret_cast<const u32x2*>(row + 32 * t);  // codes k .. k + 7, one per byte
-    uint32_t w = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // bytes (c0, c1, c2, c3) -> c0 | c1 << 4 in bits 0-7, c2 | c3 << 4 in bits 8-15
-      const uint32_t v = c[h] & 0x0F0F0F0Fu;
-      const uint32_t p = (v | (v >> 4)) & 0x00FF00FFu;
-      w |= ((p & 0xFFu) | ((p >> 8) & 0xFF00u)) << (16 * h);
-    }
-    out[t] = w;
+    const uint32_t even = perm_b32(c.y, c.x, 0x06040200u) & 0x0F0F0F0Fu;  // c0 c2 c4 c6
+    const uint32_t odd = perm_b32(c.y, c.x, 0x07050301u) & 0x0F0F0F0Fu;   // c1 c3 c5 c7
+    out[t] = nib4(even) | (nib4(odd) << 16);
   }
   reinterpret_cast<u32x4*>(packed)[idx] = u32x4{out[0], out[1], out[2], out[3]};
 }

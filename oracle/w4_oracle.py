@@ -217,53 +217,61 @@ def unpack_nibbles(packed) -> np.ndarray:
 
 TILE_ROWS = 16   # weight rows (output columns) per tile
 TILE_K = 128     # K positions per tile; one tile is 16 * 128 / 2 = 1024 bytes
+# nibble p (bits 4p .. 4p+3) of a 4-byte word holds the code at K offset
+# WORD_NIBBLE_K[p] of the word's 8 positions
+WORD_NIBBLE_K = (0, 2, 4, 6, 1, 3, 5, 7)
 
 
 def tile_offset(n: int, k: int, K: int):
-    """Byte offset and nibble (0 low, 1 high) of code (n, k) in the tile layout.
+    """Byte offset and nibble (0 low, 1 high) of code (n, k) in the stored form.
 
-    READING: the pages fix no storage order.  The stored form groups the
-    row-major bytes of ``pack_nibbles`` into tiles of 16 rows x 128 K
-    positions, tile (n // 16, k // 128) at byte (n // 16 * K // 128 + k // 128)
-    * 1024.  Inside a tile, "lane" l = 16 j + r owns 16 bytes at 16 l: four
-    4-byte words, word t holding the 8 codes of row r at K positions
-    32 t + 8 j + 0..7 of the tile, in the byte order of ``pack_nibbles``.
+    READING: the pages fix no storage order.  The stored form is tiles of 16
+    rows x 128 K positions, tile (n // 16, k // 128) at byte
+    (n // 16 * K // 128 + k // 128) * 1024.  Inside a tile, "lane" l = 16 j + r
+    owns 16 bytes at 16 l: four little-endian 4-byte words, word t holding the
+    8 codes of row r at K positions 32 t + 8 j + 0..7, the code at offset o in
+    nibble p where WORD_NIBBLE_K[p] = o (even offsets in nibbles 0-3, odd ones
+    in nibbles 4-7).
     """
     nb, r = divmod(n, TILE_ROWS)
     kb, kk = divmod(k, TILE_K)
     t, rest = divmod(kk, 32)
-    j, p = divmod(rest, 8)
+    j, o = divmod(rest, 8)
+    p = WORD_NIBBLE_K.index(o)
     lane = TILE_ROWS * j + r
     off = (nb * (K // TILE_K) + kb) * 1024 + lane * 16 + 4 * t + p // 2
     return off, p % 2
 
 
-def tile_packed(packed) -> np.ndarray:
-    """Row-major packed bytes [N][K/2] -> the tile layout (same [N][K/2]
-    shape; row tile nb occupies the bytes of rows 16 nb .. 16 nb + 15).
-    The word arrangement of ``tile_offset``, written as a reshape/transpose."""
-    p = np.asarray(packed, dtype=np.uint8)
-    N, H = p.shape
-    K = 2 * H
-    assert N % TILE_ROWS == 0 and K % TILE_K == 0
-    # row word w covers k = 8 w .. 8 w + 7, w = 16 kb + 4 t + j
-    w = p.reshape(N // TILE_ROWS, TILE_ROWS, K // TILE_K, 4, 4, 4)  # [nb][r][kb][t][j][byte]
-    tiles = w.transpose(0, 2, 4, 1, 3, 5)                            # [nb][kb][j][r][t][byte]
-    return np.ascontiguousarray(tiles).reshape(N, H)
-
-
-def untile_packed(tiled) -> np.ndarray:
-    """Inverse of ``tile_packed``."""
-    t = np.asarray(tiled, dtype=np.uint8)
-    N, H = t.shape
-    K = 2 * H
-    w = t.reshape(N // TILE_ROWS, K // TILE_K, 4, TILE_ROWS, 4, 4)  # [nb][kb][j][r][t][byte]
-    return np.ascontiguousarray(w.transpose(0, 3, 1, 4, 2, 5)).reshape(N, H)
-
-
 def pack_w4(codes) -> np.ndarray:
-    """The stored weight form: nibble packing, then the tile layout."""
-    return tile_packed(pack_nibbles(codes))
+    """[N][K] codes (0..15) -> the stored form, [N][K/2] bytes (row tile nb
+    occupies the bytes of rows 16 nb .. 16 nb + 15).  The arrangement of
+    ``tile_offset``, written as reshapes and a transpose."""
+    c = np.asarray(codes, dtype=np.uint32)
+    assert c.max(initial=0) <= 15
+    N, K = c.shape
+    assert N % TILE_ROWS == 0 and K % TILE_K == 0
+    c8 = c.reshape(N, K // 8, 8)  # 8-code words in K order
+    word = np.zeros((N, K // 8), dtype=np.uint32)
+    for p, o in enumerate(WORD_NIBBLE_K):
+        word |= c8[:, :, o] << (4 * p)
+    # row word w covers k = 8 w .. 8 w + 7, w = 16 kb + 4 t + j
+    w = word.reshape(N // TILE_ROWS, TILE_ROWS, K // TILE_K, 4, 4)  # [nb][r][kb][t][j]
+    tiles = np.ascontiguousarray(w.transpose(0, 2, 4, 1, 3))        # [nb][kb][j][r][t]
+    return tiles.astype("<u4").view(np.uint8).reshape(N, K // 2)
+
+
+def unpack_w4(stored) -> np.ndarray:
+    """Inverse of ``pack_w4``."""
+    b = np.ascontiguousarray(np.asarray(stored, dtype=np.uint8))
+    N, H = b.shape
+    K = 2 * H
+    words = b.reshape(-1).view("<u4").reshape(N // TILE_ROWS, K // TILE_K, 4, TILE_ROWS, 4)  # [nb][kb][j][r][t]
+    w = np.ascontiguousarray(words.transpose(0, 3, 1, 4, 2)).reshape(N, K // 8)           # [n][word]
+    out = np.zeros((N, K // 8, 8), dtype=np.uint8)
+    for p, o in enumerate(WORD_NIBBLE_K):
+        out[:, :, o] = (w >> (4 * p)) & 15
+    return out.reshape(N, K)
 
 
 # --------------------------------------------------------------------------

@@ -232,26 +232,30 @@ def test_tile_layout_golden_and_round_trip():
     t = o.pack_w4(codes).reshape(-1)
     for off, val in g["bytes"].items():
         assert t[int(off)] == val, off
+    tb = o.pack_w4(np.broadcast_to(k % 8, (N, K)).astype(np.uint8)).reshape(-1)
+    assert list(tb[:4]) == g["pattern_b_first_word"]
+    assert list(tb[1020:1024]) == g["pattern_b_first_word"]
     rng = np.random.default_rng(4)
     c2 = rng.integers(0, 16, (48, 384)).astype(np.uint8)
-    p = o.pack_nibbles(c2)
-    assert np.array_equal(o.untile_packed(o.tile_packed(p)), p)
-    # a tile is 1 KB of contiguous bytes: row tile nb holds only rows 16 nb .. 16 nb + 15
-    t2 = o.tile_packed(p)
+    t2 = o.pack_w4(c2)
+    assert t2.shape == (48, 192)
+    assert np.array_equal(o.unpack_w4(t2), c2)
+    # row tile nb holds only rows 16 nb .. 16 nb + 15
     for nb in range(3):
-        assert sorted(t2[16 * nb:16 * nb + 16].reshape(-1)) == sorted(p[16 * nb:16 * nb + 16].reshape(-1))
+        assert np.array_equal(o.unpack_w4(t2[16 * nb:16 * nb + 16]), c2[16 * nb:16 * nb + 16])
 
 
 def test_planted_tile_mistake_rejected():
-    """Swapping the lane's row and K-block roles (a transposed operand) is caught."""
+    """Codes packed low-nibble-first in K order (the plain nibble packing,
+    words placed as in the tile layout) are caught by the offset formula."""
     rng = np.random.default_rng(5)
     codes = rng.integers(0, 16, (32, 256)).astype(np.uint8)
     p = o.pack_nibbles(codes)
-    w = p.reshape(2, 16, 2, 4, 4, 4).transpose(0, 2, 1, 4, 3, 5)  # [nb][kb][r][j]... wrong order
-    wrong = np.ascontiguousarray(w).reshape(32, 128).reshape(-1)
+    w = p.reshape(2, 16, 2, 4, 4, 4).transpose(0, 2, 4, 1, 3, 5)  # [nb][kb][j][r][t][byte]
+    wrong = np.ascontiguousarray(w).reshape(-1)
     bad = 0
     for n in range(32):
-        for k in range(0, 256, 7):
+        for k in range(0, 256, 3):
             off, nib = o.tile_offset(n, k, 256)
             bad += int((wrong[off] >> (4 * nib)) & 15 != codes[n, k])
     assert bad > 0
