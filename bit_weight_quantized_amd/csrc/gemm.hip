@@ -414,6 +414,268 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// fp16 matrix-core paths (PATH_DQ, PATH_PS), large tile: a workgroup of 8
+// waves (2 x 4, two per SIMD: one wave alone cannot keep the matrix core
+// busy) owns 256 tokens x 128 weight rows; each wave owns 128 x 32 (8 x 2
+// products of 16 x 16), so every unpacked weight operand feeds 128 token
+// rows.  The K step is one weight-tile column.  Both operand tiles of a
+// step are copied global -> LDS by the load unit itself (16 bytes per lane,
+// lane l's bytes landing at the instruction's LDS base + 16 l), double
+// buffered: step k+1 is in flight while step k is computed, and one barrier
+// per step hands the buffers over.  The activation tile is row-major in LDS
+// (256 bytes per token row), 16-byte chunk c of row m at position c ^ (m % 16),
+// which keeps both the fill and the operand reads free of bank conflicts.
+// One workgroup per CU (its two buffers take most of the LDS).
+constexpr int kF16BM = 256;
+constexpr int kF16BN = 128;
+constexpr int kF16Threads = 512;  // 8 waves: 2 (M) x 4 (N), two per SIMD
+constexpr int kF16A = kF16BM * 256;            // activation tile bytes per stage
+constexpr int kF16B = (kF16BN / 16) * 1024;    // weight tiles
+constexpr int kF16S = 2 * 2 * kF16BN * 2;      // [group in step][scale, zero][BN] fp16 bits
+constexpr int kF16Stage = kF16A + kF16B + kF16S;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a raw buffer (offset = voff + soff) to lds_base +
+// 16 * lane (lds_base wave-uniform).  Lanes whose voff lies past the buffer
+// write zeros.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              unsigned char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+
+template <int PATH, int FMT, int GPT>
+__global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_f16_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y) {
+  constexpr int G = kStepK / GPT;
+  constexpr int WPG = 4 / GPT;  // products (tile words) per group
+  constexpr int MT = 8, NT = 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave % 2, wn = wave / 2;  // wn = 0..3
+  const int ln = lane % 16, kb = lane / 16;
+
+  // XCD-aware renumbering (a bijection of [0, tiles))
+  const int tiles_n = (N + kF16BN - 1) / kF16BN;
+  const int tiles = gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, idx = b / kXcds;
+  const int per = tiles / kXcds, rem = tiles % kXcds;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int n0 = (logical % tiles_n) * kF16BN;
+  const int m0 = (logical / tiles_n) * kF16BM;
+
+  const int ng = K / G;
+  const int KT = K / kStepK;
+  const int ntile_last = N / 16 - 1;
+
+  if constexpr (FMT == 1) {
+    for (int i = tid; i < 256; i += kF16Threads)
+      lut[i] = (uint32_t)float_to_half_bits(nf4_level(i & 15)) |
+               ((uint32_t)float_to_half_bits(nf4_level(i >> 4)) << 16);
+  }
+
+  // ---- per-lane copy offsets (fixed for the whole K loop; the step adds a
+  // scalar offset).  This wave fills token rows [32 wave, 32 wave + 32), 4 rows
+  // per instruction, and weight tile `wave`.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
+  // instruction i covers rows 32 wave + 4 i + lane / 16; its swizzle depends on
+  // i % 4 only, so four bases plus a row stride give every offset
+  uint32_t voff_a4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wave * 32 + 4 * i + lane / 16;
+    const int c = (lane % 16) ^ (row & 15);
+    voff_a4[i] = (uint32_t)(m0 + row) * (uint32_t)(K * 2) + (uint32_t)c * 16;  // rows past M read zeros
+  }
+  const uint32_t row16_bytes = (uint32_t)K * 32;  // 16 token rows
+  const uint32_t voff_b = (uint32_t)min(n0 / 16 + wave, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
+  auto issue_step = [&](int kt, unsigned char* st) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      copy16_to_lds(xr, voff_a4[i % 4] + (uint32_t)(i / 4) * row16_bytes, (uint32_t)kt * 256,
+                    st + (wave * 32 + 4 * i) * 256);
+    copy16_to_lds(wr, voff_b, (uint32_t)kt * 1024, st + kF16A + wave * 1024);
+  };
+  // scales / zeros of a step: thread t < GPT * BN holds group t / BN, column t % BN
+  auto load_scales = [&](int kt, uint16_t& rs, uint16_t& rz) {
+    const int t = min(tid, GPT * kF16BN - 1);
+    const size_t o = (size_t)min(n0 + t % kF16BN, N - 1) * ng + (size_t)kt * GPT + t / kF16BN;
+    rs = scale[o];
+    rz = FMT == 0 ? zero[o] : (uint16_t)0;
+  };
+  auto store_scales = [&](unsigned char* st, uint16_t rs, uint16_t rz) {
+    if (tid < GPT * kF16BN) {
+      const int gi = tid / kF16BN, col = tid % kF16BN;
+      reinterpret_cast<uint16_t*>(st + kF16A + kF16B)[(gi * 2) * kF16BN + col] = rs;
+      reinterpret_cast<uint16_t*>(st + kF16A + kF16B)[(gi * 2 + 1) * kF16BN + col] = rz;
+    }
+  };
+  // operand-read offsets within a stage: word w of token tile mt at
+  // a_off[w] + mt * 4096 (swizzled chunk 4w + kb of row wm*128 + mt*16 + ln)
+  uint32_t a_off[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) a_off[w] = (uint32_t)(wm * 128 + ln) * 256 + ((uint32_t)((4 * w + kb) ^ ln) << 4);
+
+  f32x4 C[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  {
+    uint16_t rs, rz;
+    issue_step(0, smem);
+    load_scales(0, rs, rz);
+    store_scales(smem, rs, rz);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    unsigned char* cur = smem + (kt & 1) * kF16Stage;
+    unsigned char* nxt = smem + ((kt + 1) & 1) * kF16Stage;
+    const bool more = kt + 1 < KT;
+    uint16_t rs = 0, rz = 0;
+    if (more) {
+      issue_step(kt + 1, nxt);
+      load_scales(kt + 1, rs, rz);
+    }
+
+    const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(cur + kF16A + kF16B);
+    u32x4 Bq[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kF16A + (wn * NT + nt) * 1024 + lane * 16);
+
+    // Word by word: the next word's weight operands are unpacked while this
+    // word's 16 products run; the second wave on the SIMD covers the LDS
+    // latency of the fragment reads.
+    float sfv[GPT][NT];      // PS: per-column scale (x 2^24 for INT4)
+    uint32_t zzv[GPT][NT];   // INT4: zero-point pair
+    uint32_t spv[GPT][NT];   // DQ: (s, s) pair
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = wn * 32 + nt * 16 + ln;
+        const uint32_t sb = s_lds[(gi * 2) * kF16BN + col];
+        spv[gi][nt] = sb | (sb << 16);
+        sfv[gi][nt] = half_bits_to_float((uint16_t)sb) * (FMT == 0 ? 16777216.0f : 1.0f);
+        zzv[gi][nt] = 0;
+        if constexpr (FMT == 0) {
+          const uint32_t z = (uint32_t)half_bits_to_float(s_lds[(gi * 2 + 1) * kF16BN + col]);  // 0..15
+          // PS: (z, z) * 2^-24 as subnormal fp16; DQ: (1024 + z, 1024 + z)
+          zzv[gi][nt] = PATH == 1 ? (z | (z << 16)) : ((0x6400u | z) | ((0x6400u | z) << 16));
+        }
+      }
+    auto unpack = [&](u32x4 (&Bu)[NT], int w) {
+      const int gi = w / WPG;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t v = Bq[nt][w];
+        if constexpr (FMT == 0) {
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t q = (v >> (4 * j)) & 0x000F000Fu;  // (c_2j, c_2j+1) * 2^-24
+            d[j] = PATH == 1 ? pk_sub_f16(q, zzv[gi][nt]) : pk_mul_f16(pk_sub_f16(q | 0x64006400u, zzv[gi][nt]), spv[gi][nt]);
+          }
+          Bu[nt] = u32x4{d[0], d[1], d[2], d[3]};
+        } else {
+          // table index (c_2j | c_2j+1 << 4) for the K-ordered pairs: even positions
+          // sit in nibbles 0-3 and odd ones in 4-7, so fold bytes 2,3 onto 0,1
+          const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+          const uint32_t il = lo | (lo >> 12), ih = hi | (hi >> 12);  // bytes 0,1: pairs (0,1),(4,5) / (2,3),(6,7)
+          u32x4 L{lut[il & 0xFFu], lut[ih & 0xFFu], lut[(il >> 8) & 0xFFu], lut[(ih >> 8) & 0xFFu]};
+          if constexpr (PATH == 0)
+            L = u32x4{pk_mul_f16(L.x, spv[gi][nt]), pk_mul_f16(L.y, spv[gi][nt]), pk_mul_f16(L.z, spv[gi][nt]),
+                      pk_mul_f16(L.w, spv[gi][nt])};
+          Bu[nt] = L;
+        }
+      }
+    };
+    auto load_a = [&](u32x4 (&A)[MT], int w) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) A[mt] = *reinterpret_cast<const u32x4*>(cur + a_off[w] + mt * 4096);
+    };
+
+    f32x4 acc[MT][NT];  // PS: the group's partial products
+    u32x4 B0[NT], B1[NT];
+    unpack(B0, 0);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      u32x4(&Bc)[NT] = (w % 2 == 0) ? B0 : B1;
+      u32x4(&Bn)[NT] = (w % 2 == 0) ? B1 : B0;
+      u32x4 A[MT];
+      load_a(A, w);
+      if (w + 1 < 4) unpack(Bn, w + 1);  // next word's operands while this word's products run
+      const bool first = (w % WPG) == 0;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (PATH == 1) acc[mt][nt] = mfma_f16(A[mt], Bc[nt], first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][nt]);
+          else C[mt][nt] = mfma_f16(A[mt], Bc[nt], C[mt][nt]);
+        }
+      if constexpr (PATH == 1) {
+        if ((w % WPG) == WPG - 1) {  // group complete: scale once
+          const int gi = w / WPG;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) C[mt][nt][i] = fmaf(sfv[gi][nt], acc[mt][nt][i], C[mt][nt][i]);
+        }
+      }
+    }
+
+    if (more) store_scales(nxt, rs, rz);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies for the next step have landed
+    __syncthreads();                // everyone's have, and nobody still reads this step's buffer
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 128 + mt * 16 + 4 * kb + i;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + wn * 32 + nt * 16 + ln;
+        if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
+      }
+    }
+}
+
+template <int PATH, int FMT, int GPT>
+int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
+               const uint16_t* zero, uint16_t* y, hipStream_t s) {
+  if ((size_t)M * K * 2 >= (1ull << 32))
+    return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm: activations of %d x %d exceed the 4 GiB one call addresses", M, K);
+  static bool attr_set = false;  // one-time opt-in to more than 64 KB of LDS
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kF16Stage);
+    if (e != hipSuccess) return fail(-4 /* W4_EHIP */, "w4_gemm: cannot reserve %d bytes of LDS: %s", 2 * kF16Stage,
+                                     hipGetErrorString(e));
+    attr_set = true;
+  }
+  const long tiles = (long)((N + kF16BN - 1) / kF16BN) * ((M + kF16BM - 1) / kF16BM);
+  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kF16Stage, s, x,
+                     M, K, N, packed, scale, zero, y);
+  return check_launch("gemm");
+}
+
 template <int PATH, int FMT, int GPT, int NT, int NS>
 int launch_one(const void* a, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
                const uint16_t* zero, uint16_t* y, const float* tok_scale, const int32_t* gsum, int32_t* acc_out,
@@ -435,9 +697,7 @@ int launch_one(const void* a, int M, int K, int N, const uint8_t* packed, const 
 
 int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
                 const uint16_t* zero, int G, int fmt, int mode, uint16_t* y, hipStream_t s) {
-  constexpr int NT = 4;
-#define W4_GEMM_CASE(PATH, FMT, GPT) \
-  return launch_one<PATH, FMT, GPT, NT, 1>(x, M, K, N, packed, scale, zero, y, nullptr, nullptr, nullptr, s)
+#define W4_GEMM_CASE(PATH, FMT, GPT) return launch_f16<PATH, FMT, GPT>(x, M, K, N, packed, scale, zero, y, s)
   if (mode == 0) {
     if (fmt == 0) {
       if (G == 64) W4_GEMM_CASE(0, 0, 2);
