@@ -8,9 +8,16 @@
 // exact, so contraction cannot change the result).  All decisions are IEEE
 // fp64 operations, bit-identical to any other correct fp64 evaluation.
 //
-// Besides the slices and scales, the kernel emits the per-group slice sums
-// SA_j[m, g] = sum_{k in g} A_j[m, k] (exact int32), which the integer product
-// kernel needs to apply each group's zero point after accumulation.
+// The slices are written in the byte order the int8 matrix-core product reads
+// them in (the operand layout below); the plain [slice][token][K] layout is
+// written as well when the caller asks for it.
+//
+// Operand layout of a token row: per 64 K positions, 64 bytes; K position
+// 64 b + 32 h + 8 kb + e is stored at byte 64 b + 16 kb + 8 h + p(e) with
+// p(0..7) = 0, 2, 4, 6, 1, 3, 5, 7 -- so lane kb's 16-byte A operand of a
+// 16x16x64 product is contiguous and its bytes pair with the weight bytes
+// the masks (w & 0x0F0F0F0F), ((w >> 4) & 0x0F0F0F0F) produce from the stored
+// nibble order (codes c0 c4 c1 c5 | c2 c6 c3 c7 of each 8).
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -20,7 +27,6 @@ namespace w4 {
 namespace {
 
 constexpr int kDecompThreads = 256;
-constexpr int kDecompMaxGroups = 512;  // K / G per row held in LDS
 
 __device__ __forceinline__ double block_max(double v, double* red) {
   v = wave_max_d(v);
@@ -37,12 +43,6 @@ __device__ __forceinline__ double quant127(double r, double s) {
   return s != 0.0 ? fmin(fmax(rint(r / s), -127.0), 127.0) : 0.0;
 }
 
-// Sum over the `seg` consecutive lanes (a power of two) that share one group.
-__device__ __forceinline__ int segment_sum(int v, int seg) {
-  for (int off = 1; off < seg; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
   return (uint32_t)(a0 & 0xFF) | ((uint32_t)(a1 & 0xFF) << 8) | ((uint32_t)(a2 & 0xFF) << 16) |
          ((uint32_t)(a3 & 0xFF) << 24);
@@ -51,22 +51,16 @@ __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
 // One workgroup per token row, passes over the (cache-resident) row: the
 // absmax, then slice 1 (with the residual's absmax), then slice 2, whose
 // residual is recomputed from x and slice 1 exactly as before.  Each thread
-// takes 8 consecutive elements per step (one 16-byte load); the G / 8 lanes
-// that share a group add their slice sums with register shuffles, and one of
-// them adds the result into the row's LDS group total.
+// takes 8 consecutive elements per step (one 16-byte load) and stores them as
+// one 8-byte piece of the operand layout (and of the plain layout if asked).
 template <int NS>
 __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
-    const uint16_t* __restrict__ x, int M, int K, int G, int8_t* __restrict__ slices,
-    float* __restrict__ tok_scale, int32_t* __restrict__ gsum) {
+    const uint16_t* __restrict__ x, int M, int K, int8_t* __restrict__ slices_op, int8_t* __restrict__ slices_out,
+    float* __restrict__ tok_scale) {
   __shared__ double red[kDecompThreads / kWave];
-  __shared__ int gs[NS][kDecompMaxGroups];
   constexpr int kStep = 8 * kDecompThreads;
   const int m = blockIdx.x;
-  const int ng = K / G;
-  const int seg = G / 8;
-  const int lane = threadIdx.x % kWave;
   const uint16_t* xr = x + (size_t)m * K;
-  for (int t = threadIdx.x; t < NS * ng; t += kDecompThreads) gs[t / ng][t % ng] = 0;
 
   auto load8 = [&](int k, double* v) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(xr + k);
@@ -76,6 +70,15 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
       v[2 * i + 1] = (double)half_bits_to_float((uint16_t)(w[i] >> 16));
     }
   };
+  // K positions k .. k + 7 of slice j: plain and operand layouts
+  auto store8 = [&](int j, int k, const int (&a)[8]) {
+    const size_t row = ((size_t)j * M + m) * K;
+    if (slices_out)
+      *reinterpret_cast<u32x2*>(slices_out + row + k) = u32x2{pack4(a[0], a[1], a[2], a[3]), pack4(a[4], a[5], a[6], a[7])};
+    const int kk = k % 64, h = kk / 32, kb = (kk % 32) / 8;
+    *reinterpret_cast<u32x2*>(slices_op + row + (k - kk) + 16 * kb + 8 * h) =
+        u32x2{pack4(a[0], a[4], a[1], a[5]), pack4(a[2], a[6], a[3], a[7])};
+  };
 
   double amax = 0.0;
   for (int k = 8 * threadIdx.x; k < K; k += kStep) {
@@ -84,25 +87,21 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(v[i]));
   }
-  amax = block_max(amax, red);  // also orders the gs clearing before the adds below
+  amax = block_max(amax, red);
   const double s1 = (double)(float)(amax / 127.0);
 
   double amax2 = 0.0;
   for (int k = 8 * threadIdx.x; k < K; k += kStep) {
     double v[8];
     load8(k, v);
-    int a[8], sum = 0;
+    int a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const double q = quant127(v[i], s1);
       a[i] = (int)q;
-      sum += a[i];
       amax2 = fmax(amax2, fabs(v[i] - s1 * q));
     }
-    *reinterpret_cast<u32x2*>(slices + (size_t)m * K + k) = u32x2{pack4(a[0], a[1], a[2], a[3]),
-                                                                   pack4(a[4], a[5], a[6], a[7])};
-    sum = segment_sum(sum, seg);  // whole segments are active together (K % G == 0)
-    if (lane % seg == 0) atomicAdd(&gs[0][k / G], sum);
+    store8(0, k, a);
   }
   if (threadIdx.x == 0) tok_scale[m] = (float)s1;
   if constexpr (NS == 2) {
@@ -111,39 +110,28 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
     for (int k = 8 * threadIdx.x; k < K; k += kStep) {
       double v[8];
       load8(k, v);
-      int a[8], sum = 0;
+      int a[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const double r1 = v[i] - s1 * quant127(v[i], s1);
         a[i] = (int)quant127(r1, s2);
-        sum += a[i];
       }
-      *reinterpret_cast<u32x2*>(slices + ((size_t)M + m) * K + k) =
-          u32x2{pack4(a[0], a[1], a[2], a[3]), pack4(a[4], a[5], a[6], a[7])};
-      sum = segment_sum(sum, seg);
-      if (lane % seg == 0) atomicAdd(&gs[1][k / G], sum);
+      store8(1, k, a);
     }
     if (threadIdx.x == 0) tok_scale[(size_t)M + m] = (float)s2;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < NS * ng; t += kDecompThreads) {
-    const int j = t / ng, g = t - j * ng;
-    gsum[((size_t)j * M + m) * ng + g] = gs[j][g];
   }
 }
 
 }  // namespace
 
-int launch_decompose(const uint16_t* x, int M, int K, int G, int nslices, int8_t* slices,
-                     float* tok_scale, int32_t* gsum, hipStream_t s) {
-  if (K / G > kDecompMaxGroups)
-    return fail(-2, "w4_gemm_decomp: K/G=%d exceeds the limit of %d groups per row", K / G, kDecompMaxGroups);
+int launch_decompose(const uint16_t* x, int M, int K, int nslices, int8_t* slices_op, int8_t* slices_out,
+                     float* tok_scale, hipStream_t s) {
   if (nslices == 1)
-    hipLaunchKernelGGL(decompose_kernel<1>, dim3(M), dim3(kDecompThreads), 0, s, x, M, K, G, slices, tok_scale,
-                       gsum);
+    hipLaunchKernelGGL(decompose_kernel<1>, dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, slices_out,
+                       tok_scale);
   else
-    hipLaunchKernelGGL(decompose_kernel<2>, dim3(M), dim3(kDecompThreads), 0, s, x, M, K, G, slices, tok_scale,
-                       gsum);
+    hipLaunchKernelGGL(decompose_kernel<2>, dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, slices_out,
+                       tok_scale);
   return check_launch("decompose");
 }
 

@@ -68,352 +68,6 @@ __device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
 
-// LDS geometry per path.  Activation planes are padded by one 16-byte row so
-// the staging writes (16 planes per token row) fall in different banks.
-template <int PATH, int NT, int NS, int GPT>
-struct GemmGeom {
-  static constexpr int BN = 32 * NT;
-  static constexpr int A_PLANES = PATH == 2 ? 8 : 16;  // fp16: chunk c of 8; int8: (product u, k-block j)
-  static constexpr int A_PLANE = (kBM + 1) * 16;
-  static constexpr int A_BYTES = (PATH == 2 ? NS : 1) * A_PLANES * A_PLANE;
-  static constexpr int B_BYTES = (BN / 16) * 1024;
-  static constexpr int OFF_B = A_BYTES;
-  static constexpr int OFF_S = OFF_B + B_BYTES;          // [GPT][scale, zero][BN] fp16 bits
-  static constexpr int OFF_T = OFF_S + GPT * 2 * BN * 2;  // MSD: T [GPT][BM] fp32, SA [GPT][NS][BM] int32
-  static constexpr int OFF_R = OFF_T + (PATH == 2 ? GPT * kBM * 4 * (1 + NS) : 0);  // MSD: s2/s1 per row
-  static constexpr int LDS = OFF_R + (PATH == 2 ? kBM * 4 : 0);
-  static constexpr int A_UNITS = PATH == 2 ? NS * kBM * 8 : kBM * 16;  // 16-byte global chunks per step
-  static constexpr int B_UNITS = (BN / 16) * 64;
-  static constexpr int A_PER_T = A_UNITS / kGemmThreads;
-  static constexpr int B_PER_T = (B_UNITS + kGemmThreads - 1) / kGemmThreads;
-};
-
-template <int PATH, int FMT, int GPT, int NT, int NS, bool DBG>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
-    const void* __restrict__ a_src, int M, int K, int N, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
-    const float* __restrict__ tok_scale, const int32_t* __restrict__ gsum, int32_t* __restrict__ acc_out) {
-  using Geo = GemmGeom<PATH, NT, NS, GPT>;
-  constexpr int BN = Geo::BN;
-  constexpr int G = kStepK / GPT;
-  constexpr int WPG = 4 / GPT;  // fp16 products (tile words) per group
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
-
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave % 2, wn = wave / 2;
-  const int ln = lane % 16, kb = lane / 16;
-
-  // XCD-aware renumbering (a bijection of [0, tiles))
-  const int tiles_n = (N + BN - 1) / BN;
-  const int tiles = gridDim.x;
-  const int b = blockIdx.x;
-  const int xcd = b % kXcds, idx = b / kXcds;
-  const int per = tiles / kXcds, rem = tiles % kXcds;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const int n0 = (logical % tiles_n) * BN;
-  const int m0 = (logical / tiles_n) * kBM;
-
-  const int ng = K / G;
-  const int KT = K / kStepK;
-  const int ntile_last = N / 16 - 1;
-
-  if constexpr (FMT == 1) {
-    for (int i = tid; i < 256; i += kGemmThreads)
-      lut[i] = (uint32_t)float_to_half_bits(nf4_level(i & 15)) |
-               ((uint32_t)float_to_half_bits(nf4_level(i >> 4)) << 16);
-  }
-
-  // ---- global -> register prefetch of one K step
-  u32x4 ra[Geo::A_PER_T];
-  u32x4 rb[Geo::B_PER_T];
-  uint16_t rs = 0, rz = 0;  // thread t < GPT*BN: group t / BN, column n0 + t % BN
-  int32_t rsa[NS];          // MSD, thread t < GPT*BM: slice sums of group t / BM, row m0 + t % BM
-  auto prefetch = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < Geo::A_PER_T; ++i) {
-      const int u = tid + i * kGemmThreads;
-      if constexpr (PATH == 2) {
-        const int js = u / (kBM * 8);
-        const int rem8 = u - js * kBM * 8;
-        const int m = rem8 / 8, c = rem8 % 8;
-        const int8_t* src = static_cast<const int8_t*>(a_src) + ((size_t)js * M + min(m0 + m, M - 1)) * K +
-                            (size_t)kt * kStepK + c * 16;
-        ra[i] = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        const int m = u / 16, c = u % 16;
-        const uint16_t* src =
-            static_cast<const uint16_t*>(a_src) + (size_t)min(m0 + m, M - 1) * K + (size_t)kt * kStepK + c * 8;
-        ra[i] = *reinterpret_cast<const u32x4*>(src);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < Geo::B_PER_T; ++i) {
-      const int u = min(tid + i * kGemmThreads, Geo::B_UNITS - 1);
-      const int t = u / 64, slot = u % 64;
-      const size_t tile = (size_t)min(n0 / 16 + t, ntile_last) * KT + kt;
-      rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + tile * 1024 + slot * 16));
-    }
-    {
-      const int t = min(tid, GPT * BN - 1);
-      const size_t o = (size_t)min(n0 + t % BN, N - 1) * ng + (size_t)kt * GPT + t / BN;
-      rs = scale[o];
-      if constexpr (FMT == 0) rz = zero[o];
-    }
-    if constexpr (PATH == 2) {
-      const int t = min(tid, GPT * kBM - 1);
-      const int r = min(m0 + t % kBM, M - 1);
-#pragma unroll
-      for (int j = 0; j < NS; ++j) rsa[j] = gsum[((size_t)j * M + r) * ng + (size_t)kt * GPT + t / kBM];
-    }
-  };
-
-  // per-token ratio s2/s1 (MSD), one per tile row, in LDS (read after the
-  // first barrier of the K loop)
-  if constexpr (PATH == 2) {
-    if (tid < kBM) {
-      const int m = min(m0 + tid, M - 1);
-      const float s1 = tok_scale[m];
-      reinterpret_cast<float*>(smem + Geo::OFF_R)[tid] =
-          (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
-    }
-  }
-
-  // ---- registers -> LDS (activation permutation applied here)
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < Geo::A_PER_T; ++i) {
-      const int u = tid + i * kGemmThreads;
-      const u32x4 v = ra[i];
-      if constexpr (PATH == 2) {
-        const int js = u / (kBM * 8);
-        const int rem8 = u - js * kBM * 8;
-        const int m = rem8 / 8, c = rem8 % 8;
-        // K positions 16c .. 16c+15 of the step: product pu = c / 4, half h of
-        // its 32-blocks, k-blocks jj and jj + 1; bytes reordered to the int8
-        // masks' order x0 x4 x1 x5 x2 x6 x3 x7
-        const int pu = c / 4, h = (c % 4) / 2, jj = 2 * (c % 2);
-        unsigned char* base = smem + js * Geo::A_PLANES * Geo::A_PLANE + m * 16 + 8 * h;
-        *reinterpret_cast<u32x2*>(base + (pu * 4 + jj) * Geo::A_PLANE) =
-            u32x2{perm_b32(v.y, v.x, 0x05010400u), perm_b32(v.y, v.x, 0x07030602u)};
-        *reinterpret_cast<u32x2*>(base + (pu * 4 + jj + 1) * Geo::A_PLANE) =
-            u32x2{perm_b32(v.w, v.z, 0x05010400u), perm_b32(v.w, v.z, 0x07030602u)};
-      } else {
-        const int m = u / 16, c = u % 16;
-        u32x4 q = v;  // INT4: the masks yield (c0,c1),(c2,c3),... -- K order, stored as is
-        if constexpr (FMT == 1)  // NF4 level pairs of bytes 0..3: (x0,x2),(x4,x6),(x1,x3),(x5,x7)
-          q = u32x4{pair_lo(v.x, v.y), pair_lo(v.z, v.w), pair_hi(v.x, v.y), pair_hi(v.z, v.w)};
-        *reinterpret_cast<u32x4*>(smem + c * Geo::A_PLANE + m * 16) = q;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < Geo::B_PER_T; ++i) {
-      const int u = tid + i * kGemmThreads;
-      if (u < Geo::B_UNITS) *reinterpret_cast<u32x4*>(smem + Geo::OFF_B + u * 16) = rb[i];
-    }
-    if (tid < GPT * BN) {
-      const int gi = tid / BN, col = tid % BN;
-      reinterpret_cast<uint16_t*>(smem + Geo::OFF_S)[(gi * 2) * BN + col] = rs;
-      reinterpret_cast<uint16_t*>(smem + Geo::OFF_S)[(gi * 2 + 1) * BN + col] = rz;
-    }
-    if constexpr (PATH == 2) {
-      if (tid < GPT * kBM) {
-        const int gi = tid / kBM, row = tid % kBM;
-        const int m = min(m0 + row, M - 1);
-        const float s1 = tok_scale[m];
-        const float r = (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
-        float t = (float)rsa[0];
-        if constexpr (NS == 2) t = fmaf(r, (float)rsa[1], t);
-        reinterpret_cast<float*>(smem + Geo::OFF_T)[gi * kBM + row] = t;
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-          reinterpret_cast<int32_t*>(smem + Geo::OFF_T)[GPT * kBM + (gi * NS + j) * kBM + row] = rsa[j];
-      }
-    }
-  };
-
-  f32x4 C[4][NT];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(smem + Geo::OFF_S);
-  prefetch(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    __syncthreads();  // the previous step's products are done with LDS
-    stash();
-    __syncthreads();
-    prefetch(min(kt + 1, KT - 1));  // unconditional: the last step is fetched twice
-
-    // this lane's 16 bytes of each of the wave's weight tiles
-    u32x4 Bq[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      Bq[nt] = *reinterpret_cast<const u32x4*>(smem + Geo::OFF_B + (wn * NT + nt) * 1024 + lane * 16);
-
-    if constexpr (PATH != 2) {
-#pragma unroll
-      for (int gi = 0; gi < GPT; ++gi) {
-        f32x4 acc[4][NT];
-        if constexpr (PATH == 1) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        // per-column (lane) constants of this group
-        uint32_t zz[NT], sp[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = wn * 16 * NT + nt * 16 + ln;
-          const uint32_t sb = s_lds[(gi * 2) * BN + col];
-          sp[nt] = sb | (sb << 16);  // (s, s) fp16 pair
-          if constexpr (FMT == 0) {
-            const uint32_t z = (uint32_t)half_bits_to_float(s_lds[(gi * 2 + 1) * BN + col]);  // 0..15
-            // PS: (z, z) * 2^-24 as subnormal fp16; DQ: (1024 + z, 1024 + z)
-            zz[nt] = PATH == 1 ? (z | (z << 16)) : ((0x6400u | z) | ((0x6400u | z) << 16));
-          }
-        }
-#pragma unroll
-        for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) {
-          u32x4 A[4];
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            A[mt] = *reinterpret_cast<const u32x4*>(smem + (4 * w + kb) * Geo::A_PLANE + (wm * 64 + mt * 16 + ln) * 16);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const uint32_t v = Bq[nt][w];
-            u32x4 B;
-            if constexpr (FMT == 0) {
-              uint32_t d[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint32_t q = (v >> (4 * j)) & 0x000F000Fu;
-                if constexpr (PATH == 1) {
-                  d[j] = pk_sub_f16(q, zz[nt]);  // (q - z) * 2^-24, exact
-                } else {
-                  d[j] = pk_mul_f16(pk_sub_f16(q | 0x64006400u, zz[nt]), sp[nt]);  // fp16(s * (q - z))
-                }
-              }
-              B = u32x4{d[0], d[1], d[2], d[3]};
-            } else {
-              B = u32x4{lut[v & 0xFFu], lut[(v >> 8) & 0xFFu], lut[(v >> 16) & 0xFFu], lut[v >> 24]};
-              if constexpr (PATH == 0) B = u32x4{pk_mul_f16(B.x, sp[nt]), pk_mul_f16(B.y, sp[nt]),
-                                                 pk_mul_f16(B.z, sp[nt]), pk_mul_f16(B.w, sp[nt])};
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-              if constexpr (PATH == 1) acc[mt][nt] = mfma_f16(A[mt], B, acc[mt][nt]);
-              else C[mt][nt] = mfma_f16(A[mt], B, C[mt][nt]);
-            }
-          }
-        }
-        if constexpr (PATH == 1) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int col = wn * 16 * NT + nt * 16 + ln;
-            float sf = half_bits_to_float(s_lds[(gi * 2) * BN + col]);
-            if constexpr (FMT == 0) sf *= 16777216.0f;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) C[mt][nt][i] = fmaf(sf, acc[mt][nt][i], C[mt][nt][i]);
-          }
-        }
-      }
-    } else {
-      // ---- MSD: int8 slices x int8 codes, exact int32 per group
-      const float* t_lds = reinterpret_cast<const float*>(smem + Geo::OFF_T);
-      const int32_t* sa_lds = reinterpret_cast<const int32_t*>(smem + Geo::OFF_T) + GPT * kBM;
-      constexpr int UPG = 2 / GPT;  // int8 products (64 K positions each) per group
-#pragma unroll
-      for (int gi = 0; gi < GPT; ++gi) {
-        i32x4 D[NS][4][NT];
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) D[j][mt][nt] = i32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int pu = gi * UPG; pu < (gi + 1) * UPG; ++pu) {
-          u32x4 A[NS][4];
-#pragma unroll
-          for (int j = 0; j < NS; ++j)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              A[j][mt] = *reinterpret_cast<const u32x4*>(smem + j * Geo::A_PLANES * Geo::A_PLANE +
-                                                         (pu * 4 + kb) * Geo::A_PLANE +
-                                                         (wm * 64 + mt * 16 + ln) * 16);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const uint32_t w0 = Bq[nt][2 * pu], w1 = Bq[nt][2 * pu + 1];
-            const u32x4 B{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
-#pragma unroll
-            for (int j = 0; j < NS; ++j)
-#pragma unroll
-              for (int mt = 0; mt < 4; ++mt) D[j][mt][nt] = mfma_i8(A[j][mt], B, D[j][mt][nt]);
-          }
-        }
-        // group epilogue: C' += s * (D1 + r * D2) - s * z * (SA1 + r * SA2)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = wn * 16 * NT + nt * 16 + ln;
-          const float sv = half_bits_to_float(s_lds[(gi * 2) * BN + col]);
-          const float zv = half_bits_to_float(s_lds[(gi * 2 + 1) * BN + col]);
-          const float nsz = -sv * zv;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const int rloc = wm * 64 + mt * 16 + 4 * kb;
-            const f32x4 T = *reinterpret_cast<const f32x4*>(t_lds + gi * kBM + rloc);
-            const f32x4 rr = *reinterpret_cast<const f32x4*>(smem + Geo::OFF_R + rloc * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float e = (float)D[0][mt][nt][i];
-              if constexpr (NS == 2) e = fmaf(rr[i], (float)D[1][mt][nt][i], e);
-              C[mt][nt][i] = fmaf(sv, e, fmaf(nsz, T[i], C[mt][nt][i]));
-            }
-            if constexpr (DBG) {  // debug output: exact integer per-group products, zero point folded
-              const int n = n0 + col;
-              const int z = (int)zv;
-              const int g = kt * GPT + gi;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int m = m0 + rloc + i;
-                if (m < M && n < N) {
-#pragma unroll
-                  for (int j = 0; j < NS; ++j)
-                    acc_out[(((size_t)j * M + m) * ng + g) * N + n] =
-                        D[j][mt][nt][i] - z * sa_lds[(gi * NS + j) * kBM + rloc + i];
-                }
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-
-  // ---- store: y = C (MSD: times the token's first-slice scale)
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 64 + mt * 16 + 4 * kb + i;
-      if (m >= M) continue;
-      float rs1 = 1.f;
-      if constexpr (PATH == 2) rs1 = tok_scale[m];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int n = n0 + wn * 16 * NT + nt * 16 + ln;
-        if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i] * rs1);
-      }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // fp16 matrix-core paths (PATH_DQ, PATH_PS), large tile: a workgroup of 8
 // waves (2 x 4, two per SIMD: one wave alone cannot keep the matrix core
@@ -676,21 +330,235 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
   return check_launch("gemm");
 }
 
-template <int PATH, int FMT, int GPT, int NT, int NS>
-int launch_one(const void* a, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
-               const uint16_t* zero, uint16_t* y, const float* tok_scale, const int32_t* gsum, int32_t* acc_out,
-               hipStream_t s) {
-  using Geo = GemmGeom<PATH, NT, NS, GPT>;
-  static_assert(Geo::A_UNITS % kGemmThreads == 0, "activation tile must split evenly over the threads");
-  static_assert(GPT * Geo::BN <= kGemmThreads && GPT * kBM <= kGemmThreads, "one scale / row sum per thread");
-  const long tiles = (long)((N + Geo::BN - 1) / Geo::BN) * ((M + kBM - 1) / kBM);
+// ---------------------------------------------------------------------------
+// Multi-Scale Dequant path, same frame as the fp16 kernel (8 waves, buffer ->
+// LDS copies, double buffered) with 128 tokens x 128 weight rows per
+// workgroup, each wave 64 x 32 (two slices of accumulators per tile).  The activation slices arrive from the decomposition kernel in
+// the operand layout (per 64 K positions, lane kb's 16 bytes contiguous), so
+// a token row of a step is 128 bytes = 8 chunks, stored at chunk c ^ (m % 8).
+// The zero point is folded into the weight operand exactly: per byte,
+// ((q | 0x80) - z) ^ 0x80 is q - z in two's complement (no byte borrows, since
+// 113 <= 128 + q - z <= 143), so each group's int32 product is
+// D_j = sum A_j * (q - z) and the epilogue is C += s * (D_1 + r * D_2) with
+// r = s_2 / s_1 per token; y = s_1 * C.
+constexpr int kMsdBM = 128;  // tokens per workgroup (each wave: 64 x 32)
+
+template <int GPT, int NS, bool DBG>
+__global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_msd_kernel(
+    const int8_t* __restrict__ slices, int M, int K, int N, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
+    const float* __restrict__ tok_scale, int32_t* __restrict__ acc_out) {
+  constexpr int G = kStepK / GPT;
+  constexpr int UPG = 2 / GPT;  // int8 products (64 K positions each) per group
+  constexpr int MT = 4, NT = 2;
+  constexpr int BM = kMsdBM;
+  constexpr int kSliceBytes = BM * 128;  // one slice's rows of a step
+  constexpr int kA = NS * kSliceBytes;
+  constexpr int kStage = kA + kF16B + kF16S;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float ratio[kMsdBM];  // s_2 / s_1 per tile row
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave % 2, wn = wave / 2;
+  const int ln = lane % 16, kb = lane / 16;
+
+  const int tiles_n = (N + kF16BN - 1) / kF16BN;
+  const int tiles = gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, idx = b / kXcds;
+  const int per = tiles / kXcds, rem = tiles % kXcds;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int n0 = (logical % tiles_n) * kF16BN;
+  const int m0 = (logical / tiles_n) * BM;
+
+  const int ng = K / G;
+  const int KT = K / kStepK;
+  const int ntile_last = N / 16 - 1;
+
+  if (tid < BM) {
+    const int m = min(m0 + tid, M - 1);
+    const float s1 = tok_scale[m];
+    ratio[tid] = (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
+  }
+
+  // copies: slice j = wave / (8 / NS); 8 rows (128 B each) per instruction
+  constexpr int kWavesPerSlice = 8 / NS;
+  constexpr int kInstr = (BM / 8) / kWavesPerSlice;  // instructions per wave per step
+  const int js = wave / kWavesPerSlice;
+  const int row_base = (wave % kWavesPerSlice) * (BM / kWavesPerSlice);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(slices + (size_t)js * M * K, (uint32_t)((size_t)M * K));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
+  const int arow = lane / 8, apos = lane % 8;
+  const uint32_t voff_a0 = (uint32_t)(m0 + row_base + arow) * (uint32_t)K;  // rows past M read zeros
+  const uint32_t voff_b = (uint32_t)min(n0 / 16 + wave, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
+  auto issue_step = [&](int kt, unsigned char* st) {
+#pragma unroll
+    for (int i = 0; i < kInstr; ++i) {
+      const int row = row_base + 8 * i + arow;
+      const int c = apos ^ (row & 7);
+      copy16_to_lds(ar, voff_a0 + (uint32_t)(8 * i) * (uint32_t)K + (uint32_t)c * 16, (uint32_t)kt * 128,
+                    st + js * kSliceBytes + (row_base + 8 * i) * 128);
+    }
+    copy16_to_lds(wr, voff_b, (uint32_t)kt * 1024, st + kA + wave * 1024);
+  };
+  auto load_scales = [&](int kt, uint16_t& rs, uint16_t& rz) {
+    const int t = min(tid, GPT * kF16BN - 1);
+    const size_t o = (size_t)min(n0 + t % kF16BN, N - 1) * ng + (size_t)kt * GPT + t / kF16BN;
+    rs = scale[o];
+    rz = zero[o];
+  };
+  auto store_scales = [&](unsigned char* st, uint16_t rs, uint16_t rz) {
+    if (tid < GPT * kF16BN) {
+      const int gi = tid / kF16BN, col = tid % kF16BN;
+      reinterpret_cast<uint16_t*>(st + kA + kF16B)[(gi * 2) * kF16BN + col] = rs;
+      reinterpret_cast<uint16_t*>(st + kA + kF16B)[(gi * 2 + 1) * kF16BN + col] = rz;
+    }
+  };
+
+  f32x4 C[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  {
+    uint16_t rs, rz;
+    issue_step(0, smem);
+    load_scales(0, rs, rz);
+    store_scales(smem, rs, rz);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    unsigned char* cur = smem + (kt & 1) * kStage;
+    unsigned char* nxt = smem + ((kt + 1) & 1) * kStage;
+    const bool more = kt + 1 < KT;
+    uint16_t rs = 0, rz = 0;
+    if (more) {
+      issue_step(kt + 1, nxt);
+      load_scales(kt + 1, rs, rz);
+    }
+    const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(cur + kA + kF16B);
+    u32x4 Bq[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kA + (wn * NT + nt) * 1024 + lane * 16);
+
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      u32x4 Bi[UPG][NT];
+      float sv[NT];
+      int zv[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = wn * 32 + nt * 16 + ln;
+        sv[nt] = half_bits_to_float(s_lds[(gi * 2) * kF16BN + col]);
+        zv[nt] = (int)half_bits_to_float(s_lds[(gi * 2 + 1) * kF16BN + col]);
+        const uint32_t zb = (uint32_t)zv[nt] * 0x01010101u;
+#pragma unroll
+        for (int u = 0; u < UPG; ++u) {
+          const int pu = gi * UPG + u;
+          const uint32_t w0 = Bq[nt][2 * pu], w1 = Bq[nt][2 * pu + 1];
+          auto qz = [&](uint32_t q) { return ((q | 0x80808080u) - zb) ^ 0x80808080u; };  // bytes q - z
+          Bi[u][nt] = u32x4{qz(w0 & 0x0F0F0F0Fu), qz((w0 >> 4) & 0x0F0F0F0Fu), qz(w1 & 0x0F0F0F0Fu),
+                            qz((w1 >> 4) & 0x0F0F0F0Fu)};
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * 64 + mt * 16 + ln;
+        i32x4 D[NS][NT];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          u32x4 A[UPG];
+#pragma unroll
+          for (int u = 0; u < UPG; ++u) {
+            const int c = 4 * (gi * UPG + u) + kb;
+            A[u] = *reinterpret_cast<const u32x4*>(cur + j * kSliceBytes + row * 128 + ((c ^ (ln & 7)) << 4));
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            i32x4 d = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < UPG; ++u) d = mfma_i8(A[u], Bi[u][nt], d);
+            D[j][nt] = d;
+          }
+        }
+        const int rloc = wm * 64 + mt * 16 + 4 * kb;
+        const f32x4 rr = *reinterpret_cast<const f32x4*>(&ratio[rloc]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e = (float)D[0][nt][i];
+            if constexpr (NS == 2) e = fmaf(rr[i], (float)D[1][nt][i], e);
+            C[mt][nt][i] = fmaf(sv[nt], e, C[mt][nt][i]);
+          }
+          if constexpr (DBG) {  // exact integer per-group products, zero point folded
+            const int n = n0 + wn * 32 + nt * 16 + ln;
+            const int g = kt * GPT + gi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = m0 + rloc + i;
+              if (m < M && n < N) {
+#pragma unroll
+                for (int j = 0; j < NS; ++j) acc_out[(((size_t)j * M + m) * ng + g) * N + n] = D[j][nt][i];
+              }
+            }
+          }
+        }
+        // keep each token tile's fragment loads with its own products (hoisting
+        // all eight tiles' loads would not fit the registers of two waves per SIMD)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    if (more) store_scales(nxt, rs, rz);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 64 + mt * 16 + 4 * kb + i;
+      if (m >= M) continue;
+      const float s1 = tok_scale[m];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + wn * 32 + nt * 16 + ln;
+        if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i] * s1);
+      }
+    }
+}
+
+template <int GPT, int NS>
+int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
+               const uint16_t* zero, uint16_t* y, const float* tok_scale, int32_t* acc_out, hipStream_t s) {
+  constexpr int kStage = NS * kMsdBM * 128 + kF16B + kF16S;
+  if ((size_t)M * K >= (1ull << 32))
+    return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm_decomp: slices of %d x %d exceed the 4 GiB one call addresses", M, K);
+  static bool attr_set[2] = {false, false};  // one-time opt-in to more than 64 KB of LDS
+  if (!attr_set[acc_out ? 1 : 0]) {
+    const void* fn = acc_out ? reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, true>)
+                             : reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, false>);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStage);
+    if (e != hipSuccess)
+      return fail(-4 /* W4_EHIP */, "w4_gemm_decomp: cannot reserve %d bytes of LDS: %s", 2 * kStage, hipGetErrorString(e));
+    attr_set[acc_out ? 1 : 0] = true;
+  }
+  const long tiles = (long)((N + kF16BN - 1) / kF16BN) * ((M + kMsdBM - 1) / kMsdBM);
   if (acc_out)
-    hipLaunchKernelGGL((gemm_kernel<PATH, FMT, GPT, NT, NS, true>), dim3((unsigned)tiles), dim3(kGemmThreads), Geo::LDS,
-                       s, a, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out);
+    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kStage, s,
+                       slices, M, K, N, packed, scale, zero, y, tok_scale, acc_out);
   else
-    hipLaunchKernelGGL((gemm_kernel<PATH, FMT, GPT, NT, NS, false>), dim3((unsigned)tiles), dim3(kGemmThreads),
-                       Geo::LDS, s, a, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out);
-  return check_launch(PATH == 2 ? "gemm_msd" : "gemm");
+    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kStage, s,
+                       slices, M, K, N, packed, scale, zero, y, tok_scale, acc_out);
+  return check_launch("gemm_msd");
 }
 
 }  // namespace
@@ -716,24 +584,23 @@ int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed, c
 }
 
 size_t decomp_workspace_bytes(int M, int K, int G, int nslices) {
-  const size_t slices = ((size_t)nslices * M * K + 255) / 256 * 256;
+  (void)G;
+  const size_t slices = ((size_t)nslices * M * K + 255) / 256 * 256;  // operand layout
   const size_t scales = ((size_t)nslices * M * sizeof(float) + 255) / 256 * 256;
-  const size_t sums = (size_t)nslices * M * (K / G) * sizeof(int32_t);
-  return slices + scales + sums;
+  return slices + scales;
 }
 
 int launch_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
-                       const uint16_t* zero, int G, int nslices, uint16_t* y, int8_t* slices, float* tok_scale,
-                       int32_t* gsum, int32_t* acc_out, hipStream_t s) {
-  int st = launch_decompose(x, M, K, G, nslices, slices, tok_scale, gsum, s);
+                       const uint16_t* zero, int G, int nslices, uint16_t* y, int8_t* slices_op, int8_t* slices_out,
+                       float* tok_scale, int32_t* acc_out, hipStream_t s) {
+  int st = launch_decompose(x, M, K, nslices, slices_op, slices_out, tok_scale, s);
   if (st != 0) return st;
-  constexpr int NT = 2;
   if (nslices == 1) {
-    if (G == 64) return launch_one<2, 0, 2, NT, 1>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
-    return launch_one<2, 0, 1, NT, 1>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
+    if (G == 64) return launch_msd<2, 1>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
+    return launch_msd<1, 1>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
   }
-  if (G == 64) return launch_one<2, 0, 2, NT, 2>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
-  return launch_one<2, 0, 1, NT, 2>(slices, M, K, N, packed, scale, zero, y, tok_scale, gsum, acc_out, s);
+  if (G == 64) return launch_msd<2, 2>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
+  return launch_msd<1, 2>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
 }
 
 }  // namespace w4

@@ -157,11 +157,9 @@ int w4_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed
   if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemm_decomp: workspace must be 16-byte aligned");
   char* base = static_cast<char*>(ws);
   const size_t slice_bytes = ((size_t)nslices * M * K + 255) / 256 * 256;
-  const size_t scale_bytes = ((size_t)nslices * M * sizeof(float) + 255) / 256 * 256;
-  int8_t* sl = slices_out ? slices_out : reinterpret_cast<int8_t*>(base);
+  int8_t* sl_op = reinterpret_cast<int8_t*>(base);
   float* ts = tok_scale_out ? tok_scale_out : reinterpret_cast<float*>(base + slice_bytes);
-  int32_t* gsum = reinterpret_cast<int32_t*>(base + slice_bytes + scale_bytes);
-  return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, y, sl, ts, gsum, acc_out,
+  return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, y, sl_op, slices_out, ts, acc_out,
                             (hipStream_t)stream);
 }
 

@@ -37,16 +37,18 @@ int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
                 const uint16_t* scale, const uint16_t* zero, int G, int fmt,
                 int mode, uint16_t* y, hipStream_t s);
 
-// Workspace of the decomposed product: int8 slices [nslices][M][K] (256-byte
-// aligned), fp32 token scales [nslices][M] (256-byte aligned), int32 per-group
-// slice sums [nslices][M][K/G].
+// Workspace of the decomposed product: int8 slices [nslices][M][K] in the
+// matrix-core operand layout (256-byte aligned), then fp32 token scales
+// [nslices][M].
 size_t decomp_workspace_bytes(int M, int K, int G, int nslices);
-int launch_decompose(const uint16_t* x, int M, int K, int G, int nslices,
-                     int8_t* slices, float* tok_scale, int32_t* gsum, hipStream_t s);
+// Decomposition: operand-layout slices, plus the plain layout when
+// slices_out is non-null.
+int launch_decompose(const uint16_t* x, int M, int K, int nslices, int8_t* slices_op, int8_t* slices_out,
+                     float* tok_scale, hipStream_t s);
 int launch_gemm_decomp(const uint16_t* x, int M, int K, int N,
                        const uint8_t* packed, const uint16_t* scale,
                        const uint16_t* zero, int G, int nslices, uint16_t* y,
-                       int8_t* slices, float* tok_scale, int32_t* gsum,
+                       int8_t* slices_op, int8_t* slices_out, float* tok_scale,
                        int32_t* acc_out, hipStream_t s);
 
 // The 16 NF4 levels as fp32 bit patterns (host copy).
