@@ -37,8 +37,21 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="decode_gemv", choices=["decode_gemv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=64,
-                    help="eager launches per variant for the live per-kernel timing")
+    ap.add_argument("--kernel-replays", type=int, default=4,
+                    help="graph replays per variant for the live per-launch timing (each replay launches "
+                         "the variant once on every weight set of the rotation)")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="instead of the bench: launch each GEMV variant --profile-launches times eagerly, "
+                         "then a plain device copy of a known size (the reference for rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE); prints what ran")
+    ap.add_argument("--profile-launches", type=int, default=16)
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: from the counter_collection CSVs of two --profile-pass runs (rocprofv3 "
+                         "--pmc FETCH_SIZE, then --pmc WRITE_SIZE) print the HBM traffic summary of the GEMV "
+                         "variants, calibrated on the plain copy")
+    ap.add_argument("--summarize", nargs="+", metavar="CSV",
+                    help="no GPU: print a markdown summary of rocprofv3 CSV output (kernel_stats or "
+                         "counter_collection files)")
     ap.add_argument("--gemm-reps", type=int, default=20,
                     help="timed launches per prefill GEMM path (0 skips the GEMM section)")
     return ap.parse_args()
@@ -151,8 +164,152 @@ def bench_gemm_prefill(w4, torch, reps):
             "paths": res}
 
 
+GEMV_SOURCE = os.path.join(ROOT, "bit_weight_quantized_amd", "csrc", "gemv.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_decode_k8192_n8192_hbm_traffic.md")
+COPY_BYTES = 256 * 2 ** 20  # the plain copy the --pmc counters are calibrated on
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic_profile():
+    """Per-launch HBM bytes of the GEMV variants from the committed --pmc
+    summary, or None when it is missing or was taken on another version of
+    the kernel source.  Rows: | variant | ... | traffic bytes per launch |."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    sha, rows = None, {}
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if line.startswith("kernel source sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 3 and cells[0].startswith(("int4", "nf4")):
+                try:
+                    rows[cells[0]] = float(cells[-1])
+                except ValueError:
+                    pass
+    if sha != source_sha256(GEMV_SOURCE) or not rows:
+        return None
+    return rows
+
+
+def variant_name(fmt, M):
+    return ("int4_g128" if fmt == 0 else "nf4_b64") + f"_m{M}"
+
+
+def graph_of(torch, stream, calls):
+    """Captures `calls` (a list of thunks) into one HIP graph on `stream`."""
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for c in calls[:2]:  # eager first launches (code objects load outside the capture)
+            c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, stream, graph, replays):
+    """Milliseconds of `replays` back-to-back replays, from HIP events
+    recorded on the stream the graph runs on."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def summarize(paths):
+    """Markdown tables from rocprofv3 CSV files: kernel statistics, or counter
+    values averaged per dispatch and grouped by kernel and launch geometry."""
+    import csv
+    import collections
+    for path in paths:
+        with open(path, newline="") as f:
+            rows = list(csv.DictReader(f))
+        if not rows:
+            continue
+        cols = {c.lower(): c for c in rows[0]}
+        print(f"\n`{os.path.basename(path)}`\n")
+        if "averagens" in cols:
+            print("| kernel | calls | average (us) | min (us) | max (us) |")
+            print("|---|---|---|---|---|")
+            for r in rows:
+                print(f"| `{short_kernel(r[cols['name']])}` | {r[cols['calls']]} | "
+                      f"{float(r[cols['averagens']]) / 1e3:.2f} | {float(r[cols['minns']]) / 1e3:.2f} | "
+                      f"{float(r[cols['maxns']]) / 1e3:.2f} |")
+        elif "counter_name" in cols:
+            agg = collections.defaultdict(list)
+            for r in rows:
+                key = (short_kernel(r[cols["kernel_name"]]), r[cols["grid_size"]], r[cols["workgroup_size"]],
+                       r[cols["counter_name"]])
+                agg[key].append(float(r[cols["counter_value"]]))
+            print("| kernel | grid | workgroup | counter | dispatches | mean per dispatch |")
+            print("|---|---|---|---|---|---|")
+            for (k, g, wg, c), v in agg.items():
+                print(f"| `{k}` | {g} | {wg} | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """Per-launch HBM bytes of each GEMV variant: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by what each counter reads for the plain copy
+    of COPY_BYTES, whose true reads and writes are COPY_BYTES each.  The
+    profile pass launches the variants in bench order, --profile-launches
+    each, so the i-th run of gemv dispatches is the i-th variant."""
+    import csv
+    def per_dispatch(path, counter):
+        with open(path, newline="") as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        gemv = [float(r["Counter_Value"]) for r in rows if "gemv_kernel" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
+        return gemv, copy
+    names = [variant_name(f, m) for f in (0, 1) for m in (1, 4, 16)]
+    fg, fc = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wg, wc = per_dispatch(write_csv, "WRITE_SIZE")
+    n = len(fg) // len(names)
+    assert n > 0 and len(fg) == n * len(names) == len(wg), (len(fg), len(wg))
+    fscale = COPY_BYTES / (sum(fc) / len(fc) * 1024)
+    wscale = COPY_BYTES / (sum(wc) / len(wc) * 1024)
+    print(f"kernel source sha256: {source_sha256(GEMV_SOURCE)}")
+    print(f"copy reference: {len(fc)} copies of {COPY_BYTES} bytes; FETCH_SIZE reads "
+          f"{sum(fc) / len(fc):.1f} KiB per copy (scale {fscale:.4f}), WRITE_SIZE {sum(wc) / len(wc):.1f} KiB "
+          f"(scale {wscale:.4f})\n")
+    print("| variant | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | algorithmic bytes | traffic / algorithmic "
+          "| traffic bytes per launch |")
+    print("|---|---|---|---|---|---|---|")
+    for i, name in enumerate(names):
+        f = sum(fg[i * n:(i + 1) * n]) / n
+        w = sum(wg[i * n:(i + 1) * n]) / n
+        t = f * 1024 * fscale + w * 1024 * wscale
+        alg = weight_stream_bytes(0 if name.startswith("int4") else 1, 8192, 8192, 128 if name.startswith("int4") else 64)
+        print(f"| {name} | {n} | {f:.1f} | {w:.1f} | {alg} | {t / alg:.3f} | {t:.0f} |")
+
+
+def short_kernel(name):
+    name = name.replace("w4::(anonymous namespace)::", "")
+    return name.split("(")[0] if "(" in name else name
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.traffic:
+        traffic_summary(*args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every box here has one GPU "
               "and this library has no multi-GPU path.", file=sys.stderr)
@@ -177,66 +334,67 @@ def main():
     wss = {(fmt, M): torch.zeros(max(16, w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)), dtype=torch.uint8,
                                  device="cuda") for fmt, M, G in variants}
 
-    def step(i):
-        for fmt, M, G in variants:
-            packed, scale, zero = sets[fmt][(i * len(Ms) + Ms.index(M)) % n_sets]
-            w4.gemv(xs[M], packed, scale, zero, G, fmt, out=ys[M], workspace=wss[(fmt, M)])
+    def launch(fmt, M, G, i):
+        packed, scale, zero = sets[fmt][i % n_sets]
+        w4.gemv(xs[M], packed, scale, zero, G, fmt, out=ys[M], workspace=wss[(fmt, M)])
 
-    # ---- capture one rotation of steps in a graph
     stream = torch.cuda.Stream()
-    steps_per_graph = n_sets
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for i in range(2):  # eager warm-up on the capture stream (also loads code objects)
-            step(i)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(steps_per_graph):
-            step(i)
-    torch.cuda.synchronize()
+    if args.profile_pass:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for fmt, M, G in variants:
+                for i in range(args.profile_launches):
+                    launch(fmt, M, G, i)
+                torch.cuda.synchronize()
+                print(f"profile pass: {args.profile_launches} launches of {variant_name(fmt, M)}", flush=True)
+            for _ in range(4):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(f"profile pass: 4 copies of {COPY_BYTES} bytes (reads {COPY_BYTES}, writes {COPY_BYTES})",
+              flush=True)
+        return
 
+    # ---- the timed region: HIP graph replays of whole steps
+    def step_calls(i):
+        return [lambda fmt=fmt, M=M, G=G: launch(fmt, M, G, i * len(Ms) + Ms.index(M)) for fmt, M, G in variants]
+
+    steps_per_graph = n_sets
+    graph = graph_of(torch, stream, [c for i in range(steps_per_graph) for c in step_calls(i)])
     replays_warm = max(1, -(-args.warmup // steps_per_graph))
     replays = max(1, -(-args.steps // steps_per_graph))
     steps_timed = replays * steps_per_graph
-    for _ in range(replays_warm):
-        graph.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(replays):
-        graph.replay()
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    time_replays(torch, stream, graph, replays_warm)
+    total_ms = time_replays(torch, stream, graph, replays)
     ms_per_step = total_ms / steps_timed
     step_bytes = sum(weight_stream_bytes(fmt, K, N, G) for fmt, M, G in variants)
     value = step_bytes * steps_timed / (total_ms * 1e-3) / 1e9
+    del graph
 
-    # ---- live per-kernel timing: HIP events around eager launches queued
-    # behind a spin kernel, on the stream the kernels run on
+    # ---- live per-launch timing of each variant: a graph of one launch per
+    # weight set, replayed back to back between events on its stream
     per = []
-    kstream = torch.cuda.Stream()
-    with torch.cuda.stream(kstream):
-        for fmt, M, G in variants:
-            reps = args.kernel_reps
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            torch.cuda._sleep(50_000_000)
-            for r in range(reps):
-                packed, scale, zero = sets[fmt][r % n_sets]
-                evs[r][0].record(kstream)
-                w4.gemv(xs[M], packed, scale, zero, G, fmt, out=ys[M], workspace=wss[(fmt, M)])
-                evs[r][1].record(kstream)
-            torch.cuda.synchronize()
-            durs = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[2:])  # us
-            avg = float(np.mean(durs))
-            b = weight_stream_bytes(fmt, K, N, G)
-            per.append({"fmt": "int4_g128" if fmt == 0 else "nf4_b64", "M": M, "us_avg": round(avg, 3),
-                        "us_median": round(durs[len(durs) // 2], 3), "weight_bytes": b,
-                        "GBps": round(b / (avg * 1e-6) / 1e9, 1)})
+    for fmt, M, G in variants:
+        g = graph_of(torch, stream, [lambda fmt=fmt, M=M, G=G, i=i: launch(fmt, M, G, i) for i in range(n_sets)])
+        time_replays(torch, stream, g, 1)
+        ms = time_replays(torch, stream, g, args.kernel_replays)
+        us = ms * 1e3 / (args.kernel_replays * n_sets)
+        b = weight_stream_bytes(fmt, K, N, G)
+        per.append({"variant": variant_name(fmt, M), "us_per_launch": round(us, 3), "weight_bytes": b,
+                    "GBps": round(b / (us * 1e-6) / 1e9, 1), "launches": args.kernel_replays * n_sets})
+        del g
     sum_bytes = sum(p["weight_bytes"] for p in per)
-    sum_us = sum(p["us_avg"] for p in per)
+    sum_us = sum(p["us_per_launch"] for p in per)
     achieved = sum_bytes / (sum_us * 1e-6) / 1e9
+    per_kernel = {}
+    for fmt, G in fmts:
+        us = [p["us_per_launch"] for p in per if p["variant"].startswith("int4" if fmt == 0 else "nf4")]
+        per_kernel["gemv_kernel<%d, %d, 1, 4>" % (fmt, G // 8)] = round(sum(us) / len(us), 3)
+
+    traffic_rows = read_traffic_profile()
+    traffic = None
+    if traffic_rows and all(p["variant"] in traffic_rows for p in per):
+        traffic = round(sum(traffic_rows[p["variant"]] for p in per) / len(per))
 
     gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
 
@@ -264,10 +422,11 @@ def main():
         "config": {"workload": "decode_gemv_k8192_n8192", "M": list(Ms), "K": K, "N": N,
                    "formats": ["int4_asym_g128", "nf4_b64"], "launches_per_step": len(variants),
                    "timed": "HIP graph replays, %d steps per graph" % steps_per_graph},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (all 6 launches of a step)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (the 6 launches of a step)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": "packed N*K/2 + fp16 scales (+ zeros) = %d" % per_set},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": "packed N*K/2 + fp16 scales (+ zeros) = %d" % per_set,
+                     "launch_average_us": round(sum_us / len(per), 3), "per_kernel_average_us": per_kernel},
         "per_launch": per,
         "gemm_prefill": gemm,
         "cpu_baseline": cpu,

@@ -21,12 +21,20 @@
  * ---------------------------------------
  * Layouts.  The weight is stored transposed, W^T [N][K], K contiguous (the
  *   PyTorch Linear weight layout).  Codes are one byte each, [N][K].  Packed
- *   weights are [N][K/2] bytes: byte j of row n holds code 2j in its low
- *   nibble and code 2j+1 in its high nibble.  Per-group scales, zero points
- *   and NF4 absmax values are fp16 [N][K/G] (group g covers k in
- *   [g*G, (g+1)*G)).  Zero points are integers 0..15 stored as fp16.
- *   Activations x are fp16 [M][K]; outputs y are fp16 [M][N]; all row-major.
- *   fp16 values travel as uint16_t bit patterns.
+ *   weights (this library's own encoding, N*K/2 bytes) are a sequence of
+ *   1024-byte tiles, each holding 16 weight rows x 128 K positions; tile
+ *   (nb, kb) covers rows 16nb..16nb+15 and K positions 128kb..128kb+127 and
+ *   sits at byte offset (nb * K/128 + kb) * 1024.  Within a tile, the 16
+ *   bytes at offset 16*(16j + r) hold row r (0..15), j = 0..3, as four
+ *   little-endian 32-bit words; word t (0..3) holds the codes of K positions
+ *   32t + 8j + e, e = 0..7, with offset e in nibble p where e = (0, 2, 4, 6,
+ *   1, 3, 5, 7)[p] (nibble p = bits 4p..4p+3).  This puts one 64-lane
+ *   wavefront's 16-byte loads on one contiguous kilobyte and lets the
+ *   masks 0x000F000F << 4i pick out the adjacent code pairs (8j+2i, 8j+2i+1).
+ *   Per-group scales, zero points and NF4 absmax values are fp16 [N][K/G]
+ *   (group g covers k in [g*G, (g+1)*G)).  Zero points are integers 0..15
+ *   stored as fp16.  Activations x are fp16 [M][K]; outputs y are fp16
+ *   [M][N]; all row-major.  fp16 values travel as uint16_t bit patterns.
  * Memory.  Every pointer argument except those marked "host" is a device
  *   pointer on the current HIP device.  The caller owns every buffer; the
  *   library allocates nothing and keeps no state besides a thread-local
@@ -40,7 +48,9 @@
  *   describes the failure.  A launch failure reported by HIP returns W4_EHIP.
  *   No C++ exception crosses this boundary.
  * Shape rules.  G (group or block size along K) is 64 or 128; K % G == 0;
- *   N % 16 == 0; M >= 1.  NF4 takes zero == NULL; INT4 needs zero != NULL.
+ *   entry points that take packed weights also need K % 128 == 0 and
+ *   N % 16 == 0 (whole tiles) and N * K / 2 < 4 GiB; M >= 1.  NF4 takes
+ *   zero == NULL; INT4 needs zero != NULL.
  */
 #ifndef W4_H_
 #define W4_H_
@@ -99,9 +109,10 @@ int w4_quantize(const float* wt, int K, int N, int G, int fmt,
                 uint8_t* codes, uint16_t* scale, uint16_t* zero, void* stream);
 
 /*
- * w4_pack -- pack codes [N][K] (values 0..15) into [N][K/2] bytes, low nibble
- * = even k.  Four-bit storage is the 4x reduction against fp16 noted on the
- * [NF4] page.  Requires K % 32 == 0.  Codes above 15 are masked to 4 bits.
+ * w4_pack -- pack codes [N][K] (values 0..15) into the tiled four-bit form
+ * described under Layouts (N*K/2 bytes).  Four-bit storage is the 4x
+ * reduction against fp16 noted on the [NF4] page.  Requires K % 128 == 0 and
+ * N % 16 == 0.  Codes above 15 are masked to 4 bits.
  */
 int w4_pack(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream);
 
@@ -149,14 +160,16 @@ int w4_gemm(const uint16_t* x, int M, int K, int N,
  * accumulated in fp32 and rounded to fp16.
  *
  * INT4 weights only: NF4 levels are not integers, so NF4 weights (zero ==
- * NULL) return W4_EUNSUPPORTED.  K / G must not exceed 512.
- * Optional outputs (NULL to skip): slices_out int8 [nslices][M][K];
- * tok_scale_out fp32 [nslices][M]; acc_out int32 [nslices][M][K/G][N], the
- * per-group integer accumulators (a debugging aid for small shapes).
+ * NULL) return W4_EUNSUPPORTED.  Also requires nslices * M * K < 4 GiB.
+ * Optional outputs (NULL to skip): slices_out int8 [nslices][M][K] (row-major,
+ * K contiguous); tok_scale_out fp32 [nslices][M]; acc_out int32
+ * [nslices][M][K/G][N], the per-group integer accumulators (a debugging aid
+ * for small shapes; it selects a slower kernel).
  * Workspace (required, 16-byte aligned, contents need not be initialised):
  * at least w4_workspace_bytes(W4_OP_GEMM_DECOMP, M, K, N, G, nslices) bytes;
- * it holds the per-group slice sums, and the slices and scales when the
- * optional outputs are NULL.  Calls that overlap in time must not share it.
+ * it holds the slices in the int8 matrix-core operand order and, when
+ * tok_scale_out is NULL, the per-token scales.  Calls that overlap in time
+ * must not share it.
  */
 int w4_gemm_decomp(const uint16_t* x, int M, int K, int N,
                    const uint8_t* packed, const uint16_t* scale,
