@@ -330,7 +330,7 @@ def main():
     sets = {fmt: make_weight_sets(w4, torch, fmt, K, N, G, n_sets, 20000 + 1000 * fmt) for fmt, G in fmts}
     xs = {M: torch.from_numpy(wl.make_activations(2, 0, M, K)).cuda() for M in Ms}
     ys = {M: torch.empty((M, N), dtype=torch.float16, device="cuda") for M in Ms}
-    # zero-filled once; every call leaves its workspace zero again (no memset in the graph)
+    # split-K partials (written before they are read: no initial contents needed)
     wss = {(fmt, M): torch.zeros(max(16, w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)), dtype=torch.uint8,
                                  device="cuda") for fmt, M, G in variants}
 

@@ -152,7 +152,7 @@ def gemv(x, packed, scale, zero, G: int, fmt: int, *, out=None, workspace=None, 
     out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
     ws_n = workspace_bytes(OP_GEMV, M, K, N, G, fmt)
     if workspace is None and ws_n:
-        workspace = torch.zeros(ws_n, dtype=torch.uint8, device=x.device)  # counters start at zero
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
     _check("w4_gemv", lib().w4_gemv(_ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, fmt,
                                     _ptr(out), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(stream)))

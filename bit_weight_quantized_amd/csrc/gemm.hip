@@ -316,14 +316,9 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
                const uint16_t* zero, uint16_t* y, hipStream_t s) {
   if ((size_t)M * K * 2 >= (1ull << 32))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm: activations of %d x %d exceed the 4 GiB one call addresses", M, K);
-  static bool attr_set = false;  // one-time opt-in to more than 64 KB of LDS
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kF16Stage);
-    if (e != hipSuccess) return fail(-4 /* W4_EHIP */, "w4_gemm: cannot reserve %d bytes of LDS: %s", 2 * kF16Stage,
-                                     hipGetErrorString(e));
-    attr_set = true;
-  }
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>), 2 * kF16Stage,
+                                   "w4_gemm");
+  if (st != 0) return st;
   const long tiles = (long)((N + kF16BN - 1) / kF16BN) * ((M + kF16BM - 1) / kF16BM);
   hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kF16Stage, s, x,
                      M, K, N, packed, scale, zero, y);
@@ -542,15 +537,10 @@ int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed,
   constexpr int kStage = NS * kMsdBM * 128 + kF16B + kF16S;
   if ((size_t)M * K >= (1ull << 32))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm_decomp: slices of %d x %d exceed the 4 GiB one call addresses", M, K);
-  static bool attr_set[2] = {false, false};  // one-time opt-in to more than 64 KB of LDS
-  if (!attr_set[acc_out ? 1 : 0]) {
-    const void* fn = acc_out ? reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, true>)
-                             : reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, false>);
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStage);
-    if (e != hipSuccess)
-      return fail(-4 /* W4_EHIP */, "w4_gemm_decomp: cannot reserve %d bytes of LDS: %s", 2 * kStage, hipGetErrorString(e));
-    attr_set[acc_out ? 1 : 0] = true;
-  }
+  const void* fn = acc_out ? reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, true>)
+                           : reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, false>);
+  const int st = allow_dynamic_lds(fn, 2 * kStage, "w4_gemm_decomp");
+  if (st != 0) return st;
   const long tiles = (long)((N + kF16BN - 1) / kF16BN) * ((M + kMsdBM - 1) / kMsdBM);
   if (acc_out)
     hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kStage, s,

@@ -37,10 +37,12 @@
 // x*q*2^-24.  The zero point is applied with the group's activation sum:
 // y += s * (2^24 * sum x*q - z * sum x).
 //
-// Split K.  With S > 1 each workgroup leaves its fp32 partial in the workspace
-// and the last one to finish a row block (a ticket counter) adds the S
-// partials in slice order, writes y, and zeroes what it used, so results are
-// deterministic and the workspace stays all-zero between calls.
+// Split K.  With S > 1 each workgroup stores its fp32 partial in the workspace
+// with plain stores, and a small second kernel on the same stream adds the S
+// partials in slice order and writes y.  Results are deterministic, the
+// workspace needs no initial contents, and no workgroup waits on another (a
+// last-arrival protocol through device-scope atomics costs several
+// microseconds of serial latency at the end of every launch).
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -50,6 +52,12 @@ namespace w4 {
 namespace {
 
 constexpr int kGemvMaxThreads = 512;
+constexpr int kRing = 4;       // weight tiles in flight per wave
+constexpr int kXUMax = 8;      // staged activation units (16 B) per thread, at most
+constexpr int kXUSmall = 4;    // the smaller staging batch (fewer redundant loads)
+constexpr int kSE = 8;         // scale entries per lane, at most: 16 rows x 32 tiles per wave
+constexpr int kMaxRun = kSE * kWave / 16;  // tiles per wave, at most
+constexpr int kLutCopies = 16;  // copies of the NF4 pair table (16 KB of LDS)
 constexpr int kTileK = 128;      // K positions per weight tile
 constexpr int kTileBytes = 1024;  // 16 rows x 128 codes
 
@@ -68,11 +76,6 @@ __device__ __forceinline__ float hi_half(uint32_t w) { return half_bits_to_float
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
 
-// Shared-memory bytes of a workgroup: the staged activation slice, [8-position
-// chunk of the slice][M] x 16 B (the same space later holds the cross-wave
-// reduction).
-__host__ __device__ inline int gemv_stage_bytes(int M, int slice_k) { return slice_k * 2 * M; }
-
 // u / d and u % d for 0 <= u < 2^22, 0 < d < 2^16, from a float reciprocal and
 // one correction step (the float estimate is off by at most one).
 __device__ __forceinline__ void div_small(int u, int d, float inv_d, int& q, int& r) {
@@ -89,11 +92,12 @@ __device__ __forceinline__ void div_small(int u, int d, float inv_d, int& q, int
 
 // Cross-wave reduction over the NWK waves of a workgroup (through `red`, NWR x
 // NWK x MT x 256 floats of LDS, free when called after a barrier), then the
-// fp16 store, or with S > 1 the split-K partial and ticket protocol.
+// fp16 store, or with S > 1 the fp32 partial of this K slice (summed over the
+// slices by gemv_reduce_kernel, launched right after on the same stream).
 template <int MT>
-__device__ __forceinline__ void gemv_finish(const f32x4 (&C)[MT], float* red, int* last_flag, int wave, int lane,
-                                            int nwr, int nwk, int row_wg0, int M, int N, uint16_t* __restrict__ y,
-                                            float* __restrict__ partial, uint32_t* __restrict__ tickets) {
+__device__ __forceinline__ void gemv_finish(const f32x4 (&C)[MT], float* red, int wave, int lane, int nwr, int nwk,
+                                            int row_wg0, int M, int N, uint16_t* __restrict__ y,
+                                            float* __restrict__ partial) {
   constexpr int kTile = MT * 256;
   const int S = gridDim.y;
   const int ks = blockIdx.y;
@@ -104,83 +108,65 @@ __device__ __forceinline__ void gemv_finish(const f32x4 (&C)[MT], float* red, in
   __syncthreads();
 
   // element e of the workgroup's output (nwr tiles of 16 rows x 16*MT tokens)
-  auto coords = [&](int e, int& n, int& m, int& w_r, int& el) {
-    w_r = e / kTile;
-    el = e - w_r * kTile;
+  const int total = nwr * kTile;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int w_r = e / kTile;
+    const int el = e - w_r * kTile;
     const int l = el % 64;
     const int i = (el / 64) % 4;
     const int t = el / 256;
-    n = row_wg0 + 16 * w_r + l % 16;
-    m = t * 16 + 4 * (l / 16) + i;
-  };
-  auto wg_sum = [&](int w_r, int el) {
+    const int n = row_wg0 + 16 * w_r + l % 16;
+    const int m = t * 16 + 4 * (l / 16) + i;
+    if (m >= M || n >= N) continue;
     float sum = 0.f;
     for (int k2 = 0; k2 < nwk; ++k2) sum += red[(k2 * nwr + w_r) * kTile + el];
-    return sum;
-  };
-
-  const int total = nwr * kTile;
-  if (S == 1) {
-    for (int e = threadIdx.x; e < total; e += blockDim.x) {
-      int n, m, w_r, el;
-      coords(e, n, m, w_r, el);
-      if (m < M && n < N) y[(size_t)m * N + n] = float_to_half_bits(wg_sum(w_r, el));
-    }
-    return;
-  }
-
-  // ---- split-K: publish this slice's partial; the last arrival finishes.
-  // Every access to the partials and tickets is an agent-scope atomic, which
-  // this hardware performs at the device coherence point (write-through, not
-  // left dirty in one XCD's L2).  Ordering comes from completion: each thread
-  // waits until its partial stores are acknowledged, the barrier collects the
-  // workgroup, and only then is the ticket incremented; the last arrival reads
-  // the partials after observing the final ticket value.  This avoids the
-  // whole-L2 write-back/invalidate an acquire-release fence costs per workgroup.
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    int n, m, w_r, el;
-    coords(e, n, m, w_r, el);
-    if (m < M && n < N)
-      __hip_atomic_store(partial + ((size_t)ks * M + m) * N + n, wg_sum(w_r, el), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // all counters to zero: the stores above are acknowledged
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(tickets + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *last_flag = (old == (uint32_t)(S - 1));
-  }
-  __syncthreads();
-  if (!*last_flag) return;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    int n, m, w_r, el;
-    coords(e, n, m, w_r, el);
-    if (m < M && n < N) {
-      float sum = 0.f;
-      for (int k2 = 0; k2 < S; ++k2) {
-        float* p = partial + ((size_t)k2 * M + m) * N + n;
-        sum += __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // leave the workspace all-zero for the next call, whatever its shape
-        __hip_atomic_store(p, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    if (S == 1)
       y[(size_t)m * N + n] = float_to_half_bits(sum);
-    }
+    else
+      partial[((size_t)ks * M + m) * N + n] = sum;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(tickets + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int FMT, int LB, int MT, int R>
+// y = the sum of the S fp32 partials, in slice order (deterministic), rounded
+// to fp16; 4 outputs per thread.
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ partial, int S, long MN,
+                                                          uint16_t* __restrict__ y) {
+  const long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= MN) return;
+  if (i + 4 <= MN) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(partial + i);
+    for (int k = 1; k < S; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(partial + (size_t)k * MN + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += v[j];
+    }
+    const uint32_t lo = (uint32_t)float_to_half_bits(acc[0]) | ((uint32_t)float_to_half_bits(acc[1]) << 16);
+    const uint32_t hi = (uint32_t)float_to_half_bits(acc[2]) | ((uint32_t)float_to_half_bits(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(y + i) = uint2{lo, hi};
+  } else {
+    for (long e = i; e < MN; ++e) {
+      float acc = partial[e];
+      for (int k = 1; k < S; ++k) acc += partial[(size_t)k * MN + e];
+      y[e] = float_to_half_bits(acc);
+    }
+  }
+}
+
+template <int FMT, int LB, int MT, int XU>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
-    float* __restrict__ partial, uint32_t* __restrict__ tickets, int nwr, int nwk) {
+    float* __restrict__ partial, int nwr, int nwk, int sc_pitch, int x_bytes) {
+  constexpr int R = kRing;         // weight tiles in flight per wave
   constexpr int G = 8 * LB;
   constexpr int GPT = kTileK / G;  // groups per tile: 1 (G=128) or 2 (G=64)
   constexpr int WPG = 4 / GPT;     // 4-byte words (one product each) per group
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ uint32_t lut[FMT == 1 ? 256 : 1];
-  __shared__ int last_flag;
+  // NF4 pair table, kLutCopies interleaved copies: entry e of copy c at word
+  // e * kLutCopies + c, and lane l reads copy l % kLutCopies, so random
+  // indices from the lanes of a copy group spread over the banks instead of
+  // colliding (one copy costs several conflict cycles per lookup).
+  __shared__ uint32_t lut[FMT == 1 ? 256 * kLutCopies : 1];
 
   const int lane = threadIdx.x % kWave;
   // wave-uniform by construction; readfirstlane lets the compiler keep it (and
@@ -196,6 +182,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   const int row_wg0 = blockIdx.x * rows_wg;
   const int S = gridDim.y;
   const int ks = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
 
   // tile ranges: the workgroup's slice [ts0, ts1), the wave's run [t0, t0 + cnt)
   const int ts0 = (int)((long)KT * ks / S), ts1 = (int)((long)KT * (ks + 1) / S);
@@ -207,22 +195,23 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   // row block) re-reads the last column and stores nothing
   const int colw = min(row_wg0 / 16 + wr, N / 16 - 1);
 
+  // Staging.  The whole slice's activations are staged once, as units of 8
+  // consecutive K positions of one token: unit u = r M + m is chunk r of the
+  // slice (K positions k0 + 8 r .. + 7) of token m, and u is also its 16-byte
+  // slot (consecutive threads store consecutive slots).  Unit r = 16 tl + kb +
+  // 4 w of tile tl is the A operand of lane (kb, m) for word w.  The plan keeps
+  // the slice within XU units per thread, so it is loaded in one batch of
+  // straight-line code whose waits count exactly the loads they need (a loop
+  // over batches would drain the weight ring too).
   u32x4* xs = reinterpret_cast<u32x4*>(smem);
-
-  // Staging.  One unit = 8 consecutive activations of token row m (chunk r of
-  // the slice: K positions k0 + 8 r .. + 7), r fastest so loads coalesce; it is
-  // the A operand of lane (kb = r % 4, m) for word (r / 4) % 4 of tile r / 16.
-  const int n_chunks = (ts1 - ts0) * (kTileK / 8);
-  const int n_xu = n_chunks * M;
-  const float inv_nc = 1.0f / (float)n_chunks;
+  const int n_xu = (ts1 - ts0) * (kTileK / 8) * M;
+  const float inv_m = 1.0f / (float)M;
   auto load_xunit = [&](int u) {
-    int m, r;
-    div_small(u, n_chunks, inv_nc, m, r);
+    int r, m;
+    div_small(u, M, inv_m, r, m);
     return *reinterpret_cast<const u32x4*>(x + (size_t)m * K + k0 + 8 * r);
   };
   auto store_xunit = [&](u32x4 q, int u) {
-    int m, r;
-    div_small(u, n_chunks, inv_nc, m, r);
     if constexpr (FMT == 0) {
       // (x0,x1), (x2,x3)/16, (x4,x5), (x6,x7)/16: the order and scale the INT4 masks produce
       q = u32x4{q.x, pk_mul_f16(q.y, kHalfSixteenthPair), q.z, pk_mul_f16(q.w, kHalfSixteenthPair)};
@@ -230,61 +219,92 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
       // (x0,x2), (x4,x6), (x1,x3), (x5,x7): the level pairs of bytes 0..3 of a word
       q = u32x4{pair_lo(q.x, q.y), pair_lo(q.z, q.w), pair_hi(q.x, q.y), pair_hi(q.z, q.w)};
     }
-    xs[r * M + m] = q;
+    xs[u] = q;
   };
 
-  // Ring slot: the lane's 16 bytes of a weight tile and the tile's scale and
-  // zero point for the lane's row (G = 64: both groups, low half first).
-  struct Slot {
-    u32x4 w;
-    uint32_t s, z;
+  // Scale block of this wave: entry (r, j) = the scale (and zero point) of row
+  // r of its tile column for tile t0 + j, fetched once with row-contiguous
+  // loads and kept in LDS at row pitch sc_pitch (odd, so the 16 rows a
+  // lane group reads fall in distinct banks).  GPT = 2 entries hold both
+  // groups of the tile, low half first.
+  constexpr int EW = (FMT == 0 && GPT == 2) ? 2 : 1;  // 32-bit words per entry
+  uint32_t* sc = reinterpret_cast<uint32_t*>(smem + (size_t)x_bytes) + (size_t)wave * 16 * sc_pitch * EW;
+  const int n_se = 16 * cnt;
+  const float inv_cnt = 1.0f / (float)max(cnt, 1);
+  const size_t srow0 = (size_t)colw * 16 * ng;
+  auto load_entry = [&](int e, uint32_t (&v)[EW]) {
+    int r, j;
+    div_small(e, max(cnt, 1), inv_cnt, r, j);
+    const size_t o = srow0 + (size_t)r * ng + (size_t)min(t0 + j, KT - 1) * GPT;  // a wave without tiles still loads
+    if constexpr (GPT == 1) {
+      v[0] = (uint32_t)scale[o] | (FMT == 0 ? (uint32_t)zero[o] << 16 : 0u);
+    } else {
+      v[0] = *reinterpret_cast<const uint32_t*>(scale + o);
+      if constexpr (EW == 2) v[1] = *reinterpret_cast<const uint32_t*>(zero + o);
+    }
   };
+  auto store_entry = [&](int e, const uint32_t (&v)[EW]) {
+    int r, j;
+    div_small(e, max(cnt, 1), inv_cnt, r, j);
+#pragma unroll
+    for (int w = 0; w < EW; ++w) sc[(r * sc_pitch + j) * EW + w] = v[w];
+  };
+
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
   const uint32_t voff = (uint32_t)lane * 16;
   const uint32_t col_base = (uint32_t)colw * (uint32_t)KT;
-  const size_t srow = (size_t)(colw * 16 + ln) * ng;
-  auto load_slot = [&](Slot& sl, int t) {
+  auto load_tile = [&](int t) {
     // a wave without tiles (more waves than tiles) still loads: keep it in bounds
     const int tt = __builtin_amdgcn_readfirstlane(min(min(t, t_last), KT - 1));
-    sl.w = buffer_load16(wrs, voff, (col_base + (uint32_t)tt) * (uint32_t)kTileBytes);
-    if constexpr (GPT == 1) {
-      sl.s = scale[srow + tt];
-      sl.z = FMT == 0 ? (uint32_t)zero[srow + tt] : 0u;
-    } else {
-      sl.s = *reinterpret_cast<const uint32_t*>(scale + srow + 2 * tt);
-      sl.z = FMT == 0 ? *reinterpret_cast<const uint32_t*>(zero + srow + 2 * tt) : 0u;
-    }
+    return buffer_load16(wrs, voff, (col_base + (uint32_t)tt) * (uint32_t)kTileBytes);
   };
 
-  // ---- 1. first staging batch (clamped index: every thread loads), then the
-  // weight ring, so the staging loads are the older ones and never wait
-  // behind weight traffic
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
-  constexpr int kXB = 4;  // x units per thread per batch
-  u32x4 xb[kXB];
+  // ---- 1. loads, oldest first: NF4 table entries, phase 0 activations,
+  // scales, then the weight ring (every count is static, so each wait below
+  // covers exactly the loads it needs)
+  constexpr int kLutPer = FMT == 1 ? 256 / kWave : 1;  // table entries per thread, at most (64 threads)
+  uint32_t lutv[kLutPer];
+  if constexpr (FMT == 1) {
 #pragma unroll
-  for (int i = 0; i < kXB; ++i) xb[i] = load_xunit(min(tid + i * nthr, n_xu - 1));
-  Slot ring[R];
-#pragma unroll
-  for (int d = 0; d < R; ++d) load_slot(ring[d], t0 + d);
-
-  // ---- 2. finish staging
-  for (int base = 0; base < n_xu; base += kXB * nthr) {
-    if (base > 0) {
-#pragma unroll
-      for (int i = 0; i < kXB; ++i) xb[i] = load_xunit(min(base + tid + i * nthr, n_xu - 1));
-    }
-#pragma unroll
-    for (int i = 0; i < kXB; ++i) {
-      const int u = base + tid + i * nthr;
-      if (u < n_xu) store_xunit(xb[i], u);
+    for (int i = 0; i < kLutPer; ++i) {
+      const int e = min(tid + i * nthr, 255);
+      lutv[i] = (uint32_t)float_to_half_bits(nf4_level(e & 15)) |
+                ((uint32_t)float_to_half_bits(nf4_level(e >> 4)) << 16);
     }
   }
+  // (indices past the end are clamped: the loads stay unconditional, only the
+  // stores are predicated)
+  u32x4 xb[XU];
+#pragma unroll
+  for (int i = 0; i < XU; ++i) xb[i] = load_xunit(min(tid + i * nthr, n_xu - 1));
+  uint32_t se[kSE][EW];
+#pragma unroll
+  for (int i = 0; i < kSE; ++i) load_entry(min(lane + i * kWave, max(n_se, 1) - 1), se[i]);
+  u32x4 ring[R];
+#pragma unroll
+  for (int d = 0; d < R; ++d) ring[d] = load_tile(t0 + d);
+
+  // ---- 2. LDS stores as the data arrive
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int u = tid + i * nthr;
+    if (u < n_xu) store_xunit(xb[i], u);
+  }
+#pragma unroll
+  for (int i = 0; i < kSE; ++i) {
+    const int e = lane + i * kWave;
+    if (e < n_se) store_entry(e, se[i]);
+  }
   if constexpr (FMT == 1) {
-    for (int i = tid; i < 256; i += nthr)
-      lut[i] = (uint32_t)float_to_half_bits(nf4_level(i & 15)) |
-               ((uint32_t)float_to_half_bits(nf4_level(i >> 4)) << 16);
+#pragma unroll
+    for (int i = 0; i < kLutPer; ++i) {
+      const int e = tid + i * nthr;
+      if (e < 256) {
+#pragma unroll
+        for (int c = 0; c < kLutCopies; c += 4)
+          *reinterpret_cast<u32x4*>(&lut[e * kLutCopies + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
+      }
+    }
   }
   __syncthreads();
 
@@ -297,24 +317,34 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   // INT4: the group's activation sum per token, as a product with constant B
   // (1 for the even pairs, 16 for the pre-scaled odd pairs)
   const u32x4 kSumB{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u};
+  const uint32_t* sc_row = sc + (size_t)ln * sc_pitch * EW;
+  const uint32_t* lut_c = lut + lane % kLutCopies;
 
-  // products of one tile (tl: tile index within the slice), group by group
-  auto compute_tile = [&](const Slot& sl, int tl) {
+  // products of tile ci of the wave's run
+  auto compute_tile = [&](const u32x4& wv, int ci) {
+    uint32_t sz[EW];
+#pragma unroll
+    for (int w = 0; w < EW; ++w) sz[w] = sc_row[ci * EW + w];
+    const uint32_t s_word = sz[0];
+    const uint32_t z_word = EW == 2 ? sz[EW - 1] : (sz[0] >> 16);
     u32x4 B[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t a = sl.w[w];
+      const uint32_t a = wv[w];
       if constexpr (FMT == 0) {
         const uint32_t as = a >> 8;
         B[w] = u32x4{a & 0x000F000Fu, a & 0x00F000F0u, as & 0x000F000Fu, as & 0x00F000F0u};
       } else {
-        B[w] = u32x4{lut[a & 0xFFu], lut[(a >> 8) & 0xFFu], lut[(a >> 16) & 0xFFu], lut[a >> 24]};
+        B[w] = u32x4{lut_c[(a & 0xFFu) * kLutCopies], lut_c[((a >> 8) & 0xFFu) * kLutCopies],
+                     lut_c[((a >> 16) & 0xFFu) * kLutCopies], lut_c[(a >> 24) * kLutCopies]};
       }
     }
+    const int tl = t0 - ts0 + ci;  // tile index within the slice
     const u32x4* xa = xs + (size_t)(tl * 16 + kb) * M;  // + (4 w) * M + m
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
-      const float sv = half_bits_to_float((uint16_t)(sl.s >> (16 * gi)));
+      const float sv = GPT == 1 ? half_bits_to_float((uint16_t)(s_word & 0xFFFFu))
+                                : half_bits_to_float((uint16_t)(s_word >> (16 * gi)));
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -324,7 +354,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
           f32x4 sx = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) sx = mfma_f16(xa[(4 * w) * M + mrow[t]], kSumB, sx);
-          const float zv = half_bits_to_float((uint16_t)(sl.z >> (16 * gi)));
+          const float zv = GPT == 1 ? half_bits_to_float((uint16_t)(z_word & 0xFFFFu))
+                                    : half_bits_to_float((uint16_t)(z_word >> (16 * gi)));
           const float ex = sv * 16777216.0f, ey = -sv * zv;  // codes enter as q * 2^-24
 #pragma unroll
           for (int i = 0; i < 4; ++i) C[t][i] = fmaf(ex, acc[i], fmaf(ey, sx[i], C[t][i]));
@@ -336,33 +367,30 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     }
   };
 
+  // ---- 3. the run.  A ring slot is consumed before its refill is issued, so
+  // the refill lands in the same registers (moving a register whose load is
+  // still in flight would make the wave wait for it, draining the ring).
   if (cnt > 0) {
     const int cnt_pad = (cnt + R - 1) / R * R;
     int base = 0;
-    // steady state: every block of R tiles but the last refills the ring.
-    // A slot is consumed before its refill is issued, so the refill lands in
-    // the same registers: moving a register whose load is still in flight
-    // would make the wave wait for it (draining the ring every R tiles).
     for (; base + R < cnt_pad; base += R) {
 #pragma unroll
       for (int d = 0; d < R; ++d) {
         const int ci = base + d;
-        if (ci < cnt) compute_tile(ring[d], t0 + ci - ts0);
-        load_slot(ring[d], t0 + ci + R);
+        if (ci < cnt) compute_tile(ring[d], ci);
+        ring[d] = load_tile(t0 + ci + R);
       }
     }
-    // last block: no refill
 #pragma unroll
-    for (int d = 0; d < R; ++d) {
+    for (int d = 0; d < R; ++d) {  // last block: no refill
       const int ci = base + d;
-      if (ci < cnt) compute_tile(ring[d], t0 + ci - ts0);
+      if (ci < cnt) compute_tile(ring[d], ci);
     }
   }
+  __syncthreads();
 
   // ---- cross-wave reduction (over wk) through LDS, reusing the staging area
-  __syncthreads();
-  gemv_finish<MT>(C, reinterpret_cast<float*>(smem), &last_flag, wave, lane, nwr, nwk, row_wg0, M, N, y, partial,
-                  tickets);
+  gemv_finish<MT>(C, reinterpret_cast<float*>(smem), wave, lane, nwr, nwk, row_wg0, M, N, y, partial);
 }
 
 int env_int(const char* name, int dflt) {
@@ -371,75 +399,104 @@ int env_int(const char* name, int dflt) {
   return std::atoi(v);
 }
 
-constexpr int kGemvLdsTarget = 76 * 1024;  // two workgroups per CU
+constexpr int kGemvLdsTarget = 78 * 1024;   // two workgroups per CU (160 KB of LDS)
+constexpr int kGemvLdsOne = 150 * 1024;     // one workgroup per CU (static LDS included)
+constexpr int kCUs = 256;
+constexpr int kLutBytes = 256 * kLutCopies * 4;
 
 }  // namespace
 
-GemvPlan plan_gemv(int M, int K, int N, int G) {
+GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
   GemvPlan c;
   const int KT = K / kTileK;  // tiles per 16-row column
+  const int gpt = kTileK / G;
+  const int max_waves = kGemvMaxThreads / kWave;
   c.mt = M <= 16 ? 1 : 2;
-  c.ring = 4;
-  // Measured on MI355X (K = N = 8192, M = 1..16, both formats): one 16-row
-  // tile column per workgroup for M <= 2, two beyond (the staged activations
-  // then serve twice the weight rows); four K waves per workgroup; K split
-  // over workgroups until the grid holds about 2048 waves.
-  c.nwr = M <= 2 ? 1 : 2;
-  c.nwk = 4;
-  const int want_waves = 2048;
-  c.row_blocks = (N + 16 * c.nwr - 1) / (16 * c.nwr);
-  c.s = 1;
-  while (c.row_blocks * c.s * c.nwr * c.nwk < want_waves && KT / (c.s * 2 * c.nwk) >= 8) c.s *= 2;
-  // long rows: more K waves (up to 8) keep at most about 32 tiles per wave
-  while (c.nwk < 8 && c.nwr * c.nwk * 2 <= kGemvMaxThreads / kWave && KT / (c.s * c.nwk) > 32) c.nwk *= 2;
-  const int ring = env_int("W4_GEMV_RING", 0);
+  // Measured on MI355X (K = N = 8192, both formats): one 16-row tile column
+  // per workgroup with four K waves for M <= 2; two columns for M <= 8 (the
+  // staged activations then serve twice the weight rows); beyond, eight
+  // columns with one K wave each, so that the activations, which outweigh the
+  // weights per K position from M = 8 on, are staged once per 128 rows.  K is
+  // split over workgroups (fp32 partials and a second kernel) while the grid
+  // holds fewer than about 2048 waves, or while the slice's activations would
+  // not fit one staging batch or the LDS.
+  c.nwr = M <= 2 ? 1 : M <= 8 ? 2 : 8;
+  c.nwk = M <= 8 ? 4 : 1;
   const int nwr = env_int("W4_GEMV_NWR", 0);
   const int nwk = env_int("W4_GEMV_NWK", 0);
   const int s = env_int("W4_GEMV_S", 0);
-  if (ring == 4 || ring == 8) c.ring = ring;
-  if (nwr >= 1 && nwr <= 8) c.nwr = nwr;
-  if (nwk >= 1 && nwk <= 8) c.nwk = nwk;
-  if (s >= 1 && s <= KT) c.s = s;
-  if (c.nwr * c.nwk > kGemvMaxThreads / kWave) c.nwk = kGemvMaxThreads / kWave / c.nwr;
-  // shrink the activation slice (more K splits) until the workgroup fits in LDS
+  if (nwr >= 1 && nwr <= max_waves) c.nwr = nwr;
+  if (nwk >= 1 && nwk <= max_waves) c.nwk = nwk;
+  if (c.nwr * c.nwk > max_waves) c.nwk = max(1, max_waves / c.nwr);
+  c.row_blocks = (N + 16 * c.nwr - 1) / (16 * c.nwr);
+  c.s = 1;
+  if (s >= 1 && s <= KT) {
+    c.s = s;
+  } else {
+    const int want_waves = 2048;
+    while (c.row_blocks * c.s * c.nwr * c.nwk < want_waves && KT / (c.s * 2 * c.nwk) >= 8) c.s *= 2;
+  }
+  const int ew = (fmt == 0 && gpt == 2) ? 2 : 1;  // 32-bit words per scale entry
   for (;;) {
-    const int slice_tiles = (KT + c.s - 1) / c.s;
-    const int stage = gemv_stage_bytes(M, slice_tiles * kTileK);
-    const int red = c.nwr * c.nwk * c.mt * 256 * 4;
-    c.lds_bytes = (size_t)(stage > red ? stage : red);
-    if ((int)c.lds_bytes <= kGemvLdsTarget || c.s >= KT) break;
+    const int slice_max = (KT + c.s - 1) / c.s;
+    const int nthr = c.nwr * c.nwk * kWave;
+    const int run = (slice_max + c.nwk - 1) / c.nwk;
+    const long n_xu = (long)slice_max * (kTileK / 8) * M;
+    if (n_xu > (long)kXUMax * nthr || run > kMaxRun) {
+      if (c.nwr * c.nwk * 2 <= max_waves) c.nwk *= 2;
+      else if (c.s < KT) ++c.s;
+      else break;  // not reached: one tile per slice always fits
+      continue;
+    }
+    c.sc_pitch = run | 1;
+    c.x_bytes = (int)(n_xu * 16);
+    c.xu = n_xu <= (long)kXUSmall * nthr ? kXUSmall : kXUMax;
+    const long sc_bytes = (long)c.nwr * c.nwk * 16 * c.sc_pitch * ew * 4;
+    const long red = (long)c.nwr * c.nwk * c.mt * 256 * 4;
+    const long need = c.x_bytes + sc_bytes;
+    c.lds_bytes = (size_t)(need > red ? need : red);
+    const long wgs = (long)((N + 16 * c.nwr - 1) / (16 * c.nwr)) * c.s;
+    const long target = (wgs > kCUs ? kGemvLdsTarget : kGemvLdsOne) - (fmt == 1 ? kLutBytes : 0);
+    if ((long)c.lds_bytes <= target || c.s >= KT) break;
     ++c.s;
   }
   c.row_blocks = (N + 16 * c.nwr - 1) / (16 * c.nwr);
-  c.ws_partial_bytes = c.s > 1 ? ((size_t)c.s * M * N * sizeof(float) + 255) / 256 * 256 : 0;
-  c.ws_bytes = c.s > 1 ? c.ws_partial_bytes + (size_t)c.row_blocks * sizeof(uint32_t) : 0;
+  c.ws_bytes = c.s > 1 ? (size_t)c.s * M * N * sizeof(float) : 0;
   return c;
 }
 
 namespace {
 
-template <int FMT, int LB, int MT>
+template <int FMT, int LB, int MT, int XU>
 int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
              const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   const dim3 block(c.nwr * c.nwk * kWave);
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
-  uint32_t* tickets =
-      c.s > 1 ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + c.ws_partial_bytes) : nullptr;
-  if (c.ring == 4)
-    hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, 4>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
-                       y, partial, tickets, c.nwr, c.nwk);
-  else
-    hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, 8>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
-                       y, partial, tickets, c.nwr, c.nwk);
+  // the plan's one-workgroup budget; the NF4 table is static LDS on top
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU>),
+                                   kGemvLdsOne - (FMT == 1 ? kLutBytes : 0), "w4_gemv");
+  if (st != 0) return st;
+  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
+                     y, partial, c.nwr, c.nwk, c.sc_pitch, c.x_bytes);
+  if (c.s > 1) {
+    const long mn = (long)M * N;
+    const long threads = (mn + 3) / 4;
+    hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, partial, c.s, mn,
+                       y);
+  }
   return check_launch("gemv");
 }
 
 template <int FMT, int LB>
 int launch_mt(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
               const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
-  if (c.mt == 1) return launch_t<FMT, LB, 1>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-  return launch_t<FMT, LB, 2>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  if (c.mt == 1) {
+    if (c.xu == kXUSmall) return launch_t<FMT, LB, 1, kXUSmall>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+    return launch_t<FMT, LB, 1, kXUMax>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  }
+  if (c.xu == kXUSmall) return launch_t<FMT, LB, 2, kXUSmall>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_t<FMT, LB, 2, kXUMax>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
 }  // namespace

@@ -7,6 +7,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <set>
+#include <tuple>
 
 #include "w4_internal.h"
 
@@ -64,6 +67,20 @@ int check_launch(const char* what) {
   return W4_OK;
 }
 
+int allow_dynamic_lds(const void* fn, int bytes, const char* what) {
+  static std::mutex mu;
+  static std::set<std::tuple<const void*, int, int>> done;  // (kernel, device, bytes)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W4_EHIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({fn, dev, bytes})) return W4_OK;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return fail(W4_EHIP, "%s: cannot reserve %d bytes of LDS: %s", what, bytes, hipGetErrorString(e));
+  done.insert({fn, dev, bytes});
+  return W4_OK;
+}
+
 const uint32_t kNf4LevelBits[16] = {
     0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
     0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
@@ -112,7 +129,7 @@ int w4_gemv(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
   if (M > 32) return fail(W4_EINVAL, "w4_gemv: M must be <= 32 (got %d); use w4_gemm", M);
   if ((st = check_weights("w4_gemv", packed, scale, zero, fmt)) != W4_OK) return st;
   if ((st = check_io("w4_gemv", x, y)) != W4_OK) return st;
-  const GemvPlan plan = plan_gemv(M, K, N, G);
+  const GemvPlan plan = plan_gemv(M, K, N, G, fmt);
   if (plan.ws_bytes > 0) {
     if (!ws || ws_bytes < plan.ws_bytes)
       return fail(W4_EWORKSPACE, "w4_gemv: workspace of %zu bytes required (got %zu)", plan.ws_bytes, ws_bytes);
@@ -171,7 +188,7 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
       return 0;
     case W4_OP_GEMV:
       if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G || K % 128) return 0;
-      return plan_gemv(M, K, N, G).ws_bytes;
+      return plan_gemv(M, K, N, G, fmt_or_mode == W4_NF4 ? W4_NF4 : W4_INT4_ASYM).ws_bytes;
     case W4_OP_GEMM_DECOMP:
       if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
       return decomp_workspace_bytes(M, K, G, fmt_or_mode);

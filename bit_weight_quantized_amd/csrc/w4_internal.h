@@ -14,6 +14,10 @@ int fail(int status, const char* fmt, ...);
 // Maps the last HIP launch error to W4_EHIP (recording its text) or W4_OK.
 int check_launch(const char* what);
 
+// Allows kernel `fn` up to `bytes` of dynamic LDS on the current device (once
+// per kernel and device); W4_OK, or W4_EHIP with the error text recorded.
+int allow_dynamic_lds(const void* fn, int bytes, const char* what);
+
 // ---- launchers (host side); arguments are validated by the caller ----
 int launch_quantize_int4(const float* wt, int K, int N, int G, uint8_t* codes,
                          uint16_t* scale, uint16_t* zero, hipStream_t s);
@@ -22,13 +26,15 @@ int launch_quantize_nf4(const float* wt, int K, int N, int G, uint8_t* codes,
 int launch_pack(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t s);
 
 // Launch shape of the GEMV: token tiles (mt), row waves and K waves per
-// workgroup (nwr, nwk), K slices over workgroups (s), grid rows, dynamic LDS
-// and workspace bytes (split-K partials + ticket counters).
+// workgroup (nwr, nwk), K slices over workgroups (s), staged activation units
+// per thread (xu), grid rows, the LDS row pitch of each wave's scale block,
+// the bytes of staged activations, dynamic LDS and workspace bytes (fp32
+// split-K partials).
 struct GemvPlan {
-  int mt, nwr, nwk, s, ring, row_blocks;
-  size_t lds_bytes, ws_partial_bytes, ws_bytes;
+  int mt, nwr, nwk, s, xu, row_blocks, sc_pitch, x_bytes;
+  size_t lds_bytes, ws_bytes;
 };
-GemvPlan plan_gemv(int M, int K, int N, int G);
+GemvPlan plan_gemv(int M, int K, int N, int G, int fmt);
 int launch_gemv(const GemvPlan& plan, const uint16_t* x, int M, int K, int N,
                 const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
                 int G, int fmt, uint16_t* y, void* ws, hipStream_t s);

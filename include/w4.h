@@ -125,13 +125,12 @@ int w4_pack(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream);
  * shared memory).  `ws`/`ws_bytes`: workspace of at least
  * w4_workspace_bytes(W4_OP_GEMV, M, K, N, G, fmt) bytes; when that is 0, ws may
  * be NULL.  Shapes whose activation slice does not fit on chip split K over
- * workgroups; the workspace then holds fp32 partial sums and per-row-block
- * ticket counters.  The workspace must be zero-filled before its first use
- * (e.g. hipMemsetAsync); every call leaves all the bytes it used zero again,
- * so one zero-fill serves any number of calls of any shape ordered on one
- * stream.  Calls that overlap in time must not share a workspace.  Partials
- * are added in a fixed order, so repeated calls give bit-identical results.
- * Output y is fp16, rounded to nearest-even from fp32 accumulation.
+ * workgroups; the workspace then holds their fp32 partial sums
+ * [S][M][N], which a second kernel on the same stream adds in slice order.
+ * The workspace needs no initial contents (it is written before it is read).
+ * Calls that overlap in time must not share a workspace.  Repeated calls give
+ * bit-identical results.  Output y is fp16, rounded to nearest-even from fp32
+ * accumulation.
  */
 int w4_gemv(const uint16_t* x, int M, int K, int N,
             const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,

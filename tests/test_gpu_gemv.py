@@ -43,21 +43,20 @@ def test_gemv_small(fmt, G, M, K, N):
     assert err <= TOL_ROW_REL_L2, err
 
 
-@pytest.mark.parametrize("ring", [4, 8])
 @pytest.mark.parametrize("nwr,nwk,s", [(1, 1, 1), (1, 4, 1), (2, 3, 1), (4, 2, 1), (1, 8, 1), (1, 2, 3),
-                                       (2, 2, 5), (1, 1, 12), (8, 1, 2), (4, 1, 4), (1, 5, 3)])
-def test_gemv_launch_variants_agree(monkeypatch, ring, nwr, nwk, s):
-    """Every work split (row waves, K waves, K slices over workgroups) and
-    ring depth stays within tolerance of the oracle, and two calls sharing one
-    workspace give bit-identical results (the split-K tickets are reset by each
-    call and the partials are added in a fixed order).  Split-K and ticket races
-    would show here.  K = 1536 is 12 weight tiles, so some splits leave waves
-    without tiles."""
+                                       (2, 2, 5), (1, 1, 12), (8, 1, 2), (4, 1, 4), (1, 5, 3), (2, 4, 2),
+                                       (1, 6, 1), (2, 1, 7)])
+def test_gemv_launch_variants_agree(monkeypatch, nwr, nwk, s):
+    """Every work split (row waves, K waves, K slices over workgroups) stays
+    within tolerance of the oracle, and two calls sharing one
+    workspace give bit-identical results (the split-K partials are added in a
+    fixed order).  The workspace starts as NaN bytes: a partial read before it
+    is written would show.  K = 1536 is 12 weight tiles, so some splits leave
+    waves without tiles."""
     require_gpu()
     monkeypatch.setenv("W4_GEMV_NWR", str(nwr))
     monkeypatch.setenv("W4_GEMV_NWK", str(nwk))
     monkeypatch.setenv("W4_GEMV_S", str(s))
-    monkeypatch.setenv("W4_GEMV_RING", str(ring))
     K, N = 1536, 208
     w = wl.make_weight(7, 0, N, K)
     for fmt, G in FMTS[:3]:
@@ -67,15 +66,13 @@ def test_gemv_launch_variants_agree(monkeypatch, ring, nwr, nwk, s):
             x = wl.make_activations(7, 0, M, K)
             xd = dev(x)
             ws_n = w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)
-            ws = torch.zeros(max(ws_n, 16), dtype=torch.uint8, device="cuda")
-            announce("gemv variant", dict(ring=ring, nwr=nwr, nwk=nwk, s=s, fmt=fmt, G=G, M=M, ws=ws_n))
+            ws = torch.full((max(ws_n, 16),), 0xFF, dtype=torch.uint8, device="cuda")  # fp32 NaNs
+            announce("gemv variant", dict(nwr=nwr, nwk=nwk, s=s, fmt=fmt, G=G, M=M, ws=ws_n))
             y1 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
             y2 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
             y_ref = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
             assert row_rel_l2(y1, y_ref) <= TOL_ROW_REL_L2, (fmt, G, M)
             assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
-            # the call left every workspace byte it used at zero
-            assert int(ws.count_nonzero().item()) == 0
 
 
 def test_gemv_cfg1_both_formats():
