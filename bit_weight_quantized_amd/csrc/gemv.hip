@@ -58,6 +58,8 @@ constexpr int kXUSmall = 4;    // the smaller staging batch (fewer redundant loa
 constexpr int kSE = 8;         // scale entries per lane, at most: 16 rows x 32 tiles per wave
 constexpr int kMaxRun = kSE * kWave / 16;  // tiles per wave, at most
 constexpr int kLutCopies = 16;  // copies of the NF4 pair table (16 KB of LDS)
+constexpr int kSEDirect = 8;    // scale entries per lane in the direct variant
+constexpr int kDirectFromM = 4; // the direct variant serves M > 4
 constexpr int kTileK = 128;      // K positions per weight tile
 constexpr int kTileBytes = 1024;  // 16 rows x 128 codes
 
@@ -393,6 +395,250 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   gemv_finish<MT>(C, reinterpret_cast<float*>(smem), wave, lane, nwr, nwk, row_wg0, M, N, y, partial);
 }
 
+// Direct variant.  Each wave owns C tile columns (16 C weight rows) and a run
+// of K tiles; the workgroup's waves split K between them and add their
+// results through LDS at the end.  The activations are read from memory (L2,
+// where all workgroups find them) straight into matrix-core A operands: no
+// staging and no barrier before the products.  One set of A operands serves C
+// weight tiles, and for INT4 the group's activation sum too, so the operand
+// traffic per weight byte falls with C.  The unpacked INT4 pairs all carry
+// the same 2^-24 (the odd pairs are shifted down rather than the
+// activations pre-scaled); for NF4 the activation pairs are permuted in
+// registers to the byte order of the level pairs.
+template <int FMT, int LB, int MT, int C, int R>
+__global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
+    float* __restrict__ partial, int sc_pitch) {
+  constexpr int G = 8 * LB;
+  constexpr int GPT = kTileK / G;
+  constexpr int WPG = 4 / GPT;
+  constexpr int EW = (FMT == 0 && GPT == 2) ? 2 : 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ uint32_t lut[FMT == 1 ? 256 * kLutCopies : 1];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // = the K wave
+  const int nwk = blockDim.x / kWave;
+  const int ln = lane % 16;
+  const int kb = lane / 16;
+  const int ng = K / G;
+  const int KT = K / kTileK;
+  const int ncol = N / 16;
+  const int col0 = blockIdx.x * C;
+  const int S = gridDim.y;
+  const int ks = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+
+  const int ts0 = (int)((long)KT * ks / S), ts1 = (int)((long)KT * (ks + 1) / S);
+  const int t0 = ts0 + (int)((long)(ts1 - ts0) * wave / nwk);
+  const int cnt = ts0 + (int)((long)(ts1 - ts0) * (wave + 1) / nwk) - t0;
+  const int t_last = t0 + max(cnt, 1) - 1;
+  int colc[C];  // a group past the last column re-reads it and stores nothing
+#pragma unroll
+  for (int c = 0; c < C; ++c) colc[c] = min(col0 + c, ncol - 1);
+
+  // scale block of this wave: entry (c, r, j) = column c, row r, tile t0 + j
+  uint32_t* sc = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * C * 16 * sc_pitch * EW;
+  const int n_se = C * 16 * cnt;
+  const float inv_cnt = 1.0f / (float)max(cnt, 1);
+  auto load_entry = [&](int e, uint32_t (&v)[EW]) {
+    int cr, j;
+    div_small(e, max(cnt, 1), inv_cnt, cr, j);
+    const int c = cr / 16, r = cr % 16;
+    const size_t o = (size_t)(min(col0 + c, ncol - 1) * 16 + r) * ng + (size_t)min(t0 + j, KT - 1) * GPT;
+    if constexpr (GPT == 1) {
+      v[0] = (uint32_t)scale[o] | (FMT == 0 ? (uint32_t)zero[o] << 16 : 0u);
+    } else {
+      v[0] = *reinterpret_cast<const uint32_t*>(scale + o);
+      if constexpr (EW == 2) v[1] = *reinterpret_cast<const uint32_t*>(zero + o);
+    }
+  };
+
+  // ring slot: the lane's 16 bytes of C weight tiles and its A operands
+  struct Slot {
+    u32x4 w[C];
+    u32x4 a[4][MT];
+  };
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
+  const uint32_t voff = (uint32_t)lane * 16;
+  const u32x4* xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    xrow[m] = reinterpret_cast<const u32x4*>(x + (size_t)min(m * 16 + ln, M - 1) * K) + kb;
+  auto load_slot = [&](Slot& sl, int t) {
+    const int tt = __builtin_amdgcn_readfirstlane(min(min(t, t_last), KT - 1));
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      sl.w[c] = buffer_load16(wrs, voff, ((uint32_t)colc[c] * (uint32_t)KT + (uint32_t)tt) * (uint32_t)kTileBytes);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) sl.a[w][m] = xrow[m][tt * 16 + 4 * w];
+  };
+
+  // ---- prologue: table entries, scale entries, then the ring
+  constexpr int kLutPer = FMT == 1 ? 256 / kWave : 1;
+  uint32_t lutv[kLutPer];
+  if constexpr (FMT == 1) {
+#pragma unroll
+    for (int i = 0; i < kLutPer; ++i) {
+      const int e = min(tid + i * nthr, 255);
+      lutv[i] = (uint32_t)float_to_half_bits(nf4_level(e & 15)) |
+                ((uint32_t)float_to_half_bits(nf4_level(e >> 4)) << 16);
+    }
+  }
+  uint32_t se[kSEDirect][EW];
+#pragma unroll
+  for (int i = 0; i < kSEDirect; ++i) load_entry(min(lane + i * kWave, max(n_se, 1) - 1), se[i]);
+  Slot ring[R];
+#pragma unroll
+  for (int d = 0; d < R; ++d) {
+    load_slot(ring[d], t0 + d);
+    // keep the slots' loads in slot order, as the refills issue them, so the
+    // waits in the loop count the same way on entry as in steady state
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < kSEDirect; ++i) {
+    const int e = lane + i * kWave;
+    if (e < n_se) {
+      int cr, j;
+      div_small(e, max(cnt, 1), inv_cnt, cr, j);
+#pragma unroll
+      for (int w = 0; w < EW; ++w) sc[(cr * sc_pitch + j) * EW + w] = se[i][w];
+    }
+  }
+  if constexpr (FMT == 1) {
+#pragma unroll
+    for (int i = 0; i < kLutPer; ++i) {
+      const int e = tid + i * nthr;
+      if (e < 256) {
+#pragma unroll
+        for (int c = 0; c < kLutCopies; c += 4)
+          *reinterpret_cast<u32x4*>(&lut[e * kLutCopies + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
+      }
+    }
+    __syncthreads();  // the table is shared; the scale block is the wave's own
+  }
+
+  f32x4 acc_c[C][MT];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc_c[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 kOnes{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  const uint32_t* lut_c = lut + lane % kLutCopies;
+
+  auto compute = [&](Slot& sl, int ci) {
+    if constexpr (FMT == 1) {
+      // activation pairs in the order of the level pairs of bytes 0..3: (x0,x2), (x4,x6), (x1,x3), (x5,x7)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4 q = sl.a[w][m];
+          sl.a[w][m] = u32x4{pair_lo(q.x, q.y), pair_lo(q.z, q.w), pair_hi(q.x, q.y), pair_hi(q.z, q.w)};
+        }
+    }
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      f32x4 sx[MT];
+      if constexpr (FMT == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          sx[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) sx[m] = mfma_f16(sl.a[w][m], kOnes, sx[m]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        uint32_t sz[EW];
+#pragma unroll
+        for (int w = 0; w < EW; ++w) sz[w] = sc[((c * 16 + ln) * sc_pitch + ci) * EW + w];
+        const float sv = GPT == 1 ? half_bits_to_float((uint16_t)(sz[0] & 0xFFFFu))
+                                  : half_bits_to_float((uint16_t)(sz[0] >> (16 * gi)));
+        u32x4 B[WPG];
+#pragma unroll
+        for (int wi = 0; wi < WPG; ++wi) {
+          const uint32_t a = sl.w[c][gi * WPG + wi];
+          if constexpr (FMT == 0) {
+            B[wi] = u32x4{a & 0x000F000Fu, (a >> 4) & 0x000F000Fu, (a >> 8) & 0x000F000Fu, (a >> 12) & 0x000F000Fu};
+          } else {
+            B[wi] = u32x4{lut_c[(a & 0xFFu) * kLutCopies], lut_c[((a >> 8) & 0xFFu) * kLutCopies],
+                          lut_c[((a >> 16) & 0xFFu) * kLutCopies], lut_c[(a >> 24) * kLutCopies]};
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int wi = 0; wi < WPG; ++wi) acc = mfma_f16(sl.a[gi * WPG + wi][m], B[wi], acc);
+          if constexpr (FMT == 0) {
+            const uint32_t zw = EW == 2 ? sz[EW - 1] : (sz[0] >> 16);
+            const float zv = GPT == 1 ? half_bits_to_float((uint16_t)(zw & 0xFFFFu))
+                                      : half_bits_to_float((uint16_t)(zw >> (16 * gi)));
+            const float ex = sv * 16777216.0f, ey = -sv * zv;  // codes enter as q * 2^-24
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc_c[c][m][i] = fmaf(ex, acc[i], fmaf(ey, sx[m][i], acc_c[c][m][i]));
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc_c[c][m][i] = fmaf(sv, acc[i], acc_c[c][m][i]);
+          }
+        }
+      }
+    }
+  };
+
+  if (cnt > 0) {
+    const int cnt_pad = (cnt + R - 1) / R * R;
+    int base = 0;
+    for (; base + R < cnt_pad; base += R) {
+#pragma unroll
+      for (int d = 0; d < R; ++d) {
+        const int ci = base + d;
+        if (ci < cnt) compute(ring[d], ci);
+        load_slot(ring[d], t0 + ci + R);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < R; ++d) {
+      const int ci = base + d;
+      if (ci < cnt) compute(ring[d], ci);
+    }
+  }
+
+  // ---- sum over the K waves through LDS (the scale blocks are dead by now)
+  __syncthreads();
+  constexpr int kT = MT * 256;  // one column's outputs
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(wave * C + c) * kT + (m * 4 + i) * 64 + lane] = acc_c[c][m][i];
+  __syncthreads();
+  for (int e = tid; e < C * kT; e += nthr) {
+    const int c = e / kT;
+    const int el = e - c * kT;
+    const int l = el % 64;
+    const int i = (el / 64) % 4;
+    const int t = el / 256;
+    const int m = t * 16 + 4 * (l / 16) + i;
+    if (m >= M || col0 + c >= ncol) continue;
+    const int n = (col0 + c) * 16 + l % 16;
+    float sum = 0.f;
+    for (int w2 = 0; w2 < nwk; ++w2) sum += red[(w2 * C + c) * kT + el];
+    if (S == 1)
+      y[(size_t)m * N + n] = float_to_half_bits(sum);
+    else
+      partial[((size_t)ks * M + m) * N + n] = sum;
+  }
+}
+
 int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
   if (!v || !*v) return dflt;
@@ -405,6 +651,44 @@ constexpr int kCUs = 256;
 constexpr int kLutBytes = 256 * kLutCopies * 4;
 
 }  // namespace
+
+// Direct variant: C columns per wave, nwk K waves per workgroup, K split
+// over workgroups only while the grid is short of about 2048 waves or a run
+// would exceed the scale block.
+void plan_direct(GemvPlan& c, int M, int K, int N, int G, int fmt) {
+  const int KT = K / kTileK;
+  const int gpt = kTileK / G;
+  const int max_waves = kGemvMaxThreads / kWave;
+  c.kind = 1;
+  c.mt = M <= 16 ? 1 : 2;
+  c.cols = 2;
+  c.nwr = 1;
+  c.nwk = 8;
+  const int cols = env_int("W4_GEMV_C", 0);
+  const int nwk = env_int("W4_GEMV_NWK", 0);
+  const int s = env_int("W4_GEMV_S", 0);
+  if (cols == 1 || cols == 2 || cols == 4) c.cols = cols;
+  if (nwk >= 1 && nwk <= max_waves) c.nwk = nwk;
+  const int groups = (N / 16 + c.cols - 1) / c.cols;
+  c.s = 1;
+  if (s >= 1 && s <= KT) {
+    c.s = s;
+  } else {
+    while ((long)groups * c.s * c.nwk < 2048 && KT / (c.s * 2 * c.nwk) >= 4) c.s *= 2;
+  }
+  const int max_run = kSEDirect * kWave / (16 * c.cols);
+  while (((KT + c.s - 1) / c.s + c.nwk - 1) / c.nwk > max_run) ++c.s;
+  const int run = ((KT + c.s - 1) / c.s + c.nwk - 1) / c.nwk;
+  const int ew = (fmt == 0 && gpt == 2) ? 2 : 1;
+  c.sc_pitch = run | 1;
+  c.x_bytes = 0;
+  c.xu = 0;
+  const long sc_bytes = (long)c.nwk * c.cols * 16 * c.sc_pitch * ew * 4;
+  const long red = (long)c.nwk * c.cols * c.mt * 256 * 4;
+  c.lds_bytes = (size_t)(sc_bytes > red ? sc_bytes : red);
+  c.row_blocks = groups;
+  (void)M;
+}
 
 GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
   GemvPlan c;
@@ -461,6 +745,13 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
     ++c.s;
   }
   c.row_blocks = (N + 16 * c.nwr - 1) / (16 * c.nwr);
+  c.kind = 0;
+  c.cols = 1;
+  // Measured on MI355X (K = N = 8192): the staged kernel is faster up to M =
+  // 4, the direct one (two columns per wave, eight K waves) beyond, where the
+  // staged activations would outweigh the weights a workgroup streams.
+  const int kind = env_int("W4_GEMV_KIND", -1);
+  if (kind == 1 || (kind != 0 && M > kDirectFromM)) plan_direct(c, M, K, N, G, fmt);
   c.ws_bytes = c.s > 1 ? (size_t)c.s * M * N * sizeof(float) : 0;
   return c;
 }
@@ -488,9 +779,39 @@ int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const ui
   return check_launch("gemv");
 }
 
+template <int FMT, int LB, int MT, int C>
+int launch_direct(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                  const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+  constexpr int R = MT == 1 ? 4 : 2;
+  const dim3 block(c.nwk * kWave);
+  const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
+  float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
+  hipLaunchKernelGGL((gemv_direct_kernel<FMT, LB, MT, C, R>), grid, block, c.lds_bytes, s, x, M, K, N, packed,
+                     scale, zero, y, partial, c.sc_pitch);
+  if (c.s > 1) {
+    const long mn = (long)M * N;
+    const long threads = (mn + 3) / 4;
+    hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, partial, c.s, mn,
+                       y);
+  }
+  return check_launch("gemv");
+}
+
+template <int FMT, int LB, int MT>
+int launch_direct_c(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                    const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+  if (c.cols == 1) return launch_direct<FMT, LB, MT, 1>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  if (c.cols == 4) return launch_direct<FMT, LB, MT, 4>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_direct<FMT, LB, MT, 2>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+}
+
 template <int FMT, int LB>
 int launch_mt(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
               const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+  if (c.kind == 1) {
+    if (c.mt == 1) return launch_direct_c<FMT, LB, 1>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+    return launch_direct_c<FMT, LB, 2>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  }
   if (c.mt == 1) {
     if (c.xu == kXUSmall) return launch_t<FMT, LB, 1, kXUSmall>(c, x, M, K, N, packed, scale, zero, y, ws, s);
     return launch_t<FMT, LB, 1, kXUMax>(c, x, M, K, N, packed, scale, zero, y, ws, s);

@@ -30,8 +30,9 @@ int launch_pack(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t
 // per thread (xu), grid rows, the LDS row pitch of each wave's scale block,
 // the bytes of staged activations, dynamic LDS and workspace bytes (fp32
 // split-K partials).
+// kind 1 is the direct variant: cols tile columns per wave, no staging.
 struct GemvPlan {
-  int mt, nwr, nwk, s, xu, row_blocks, sc_pitch, x_bytes;
+  int kind, cols, mt, nwr, nwk, s, xu, row_blocks, sc_pitch, x_bytes;
   size_t lds_bytes, ws_bytes;
 };
 GemvPlan plan_gemv(int M, int K, int N, int G, int fmt);

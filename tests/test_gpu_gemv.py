@@ -54,6 +54,7 @@ def test_gemv_launch_variants_agree(monkeypatch, nwr, nwk, s):
     is written would show.  K = 1536 is 12 weight tiles, so some splits leave
     waves without tiles."""
     require_gpu()
+    monkeypatch.setenv("W4_GEMV_KIND", "0")  # the staged variant, whatever M
     monkeypatch.setenv("W4_GEMV_NWR", str(nwr))
     monkeypatch.setenv("W4_GEMV_NWK", str(nwk))
     monkeypatch.setenv("W4_GEMV_S", str(s))
@@ -68,6 +69,36 @@ def test_gemv_launch_variants_agree(monkeypatch, nwr, nwk, s):
             ws_n = w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)
             ws = torch.full((max(ws_n, 16),), 0xFF, dtype=torch.uint8, device="cuda")  # fp32 NaNs
             announce("gemv variant", dict(nwr=nwr, nwk=nwk, s=s, fmt=fmt, G=G, M=M, ws=ws_n))
+            y1 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
+            y2 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
+            y_ref = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
+            assert row_rel_l2(y1, y_ref) <= TOL_ROW_REL_L2, (fmt, G, M)
+            assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+@pytest.mark.parametrize("cols,nwk,s", [(1, 8, 1), (2, 8, 1), (4, 8, 1), (2, 4, 1), (2, 3, 2), (4, 1, 3),
+                                        (2, 8, 5), (1, 2, 1)])
+def test_gemv_direct_variants_agree(monkeypatch, cols, nwk, s):
+    """The direct variant (activations read straight into matrix-core
+    operands, `cols` tile columns per wave) for each work split: within
+    tolerance of the oracle and repeatable.  N = 208 is 13 tile columns, so
+    the last column group is partial for cols = 2 and 4."""
+    require_gpu()
+    monkeypatch.setenv("W4_GEMV_KIND", "1")
+    monkeypatch.setenv("W4_GEMV_C", str(cols))
+    monkeypatch.setenv("W4_GEMV_NWK", str(nwk))
+    monkeypatch.setenv("W4_GEMV_S", str(s))
+    K, N = 1536, 208
+    w = wl.make_weight(8, 0, N, K)
+    for fmt, G in FMTS:
+        codes, scale, zero = oracle_weights(fmt, w, G)
+        packed, sc, zc = upload_weights(codes, scale, zero)
+        for M in (1, 5, 16, 17, 32):
+            x = wl.make_activations(8, 0, M, K)
+            xd = dev(x)
+            ws_n = w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)
+            ws = torch.full((max(ws_n, 16),), 0xFF, dtype=torch.uint8, device="cuda")  # fp32 NaNs
+            announce("gemv direct", dict(cols=cols, nwk=nwk, s=s, fmt=fmt, G=G, M=M, ws=ws_n))
             y1 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
             y2 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
             y_ref = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
