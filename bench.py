@@ -271,7 +271,8 @@ def traffic_summary(fetch_csv, write_csv):
         with open(path, newline="") as f:
             rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        gemv = [float(r["Counter_Value"]) for r in rows if "gemv_kernel" in r["Kernel_Name"]]
+        gemv = [float(r["Counter_Value"]) for r in rows
+                if "gemv_kernel" in r["Kernel_Name"] or "gemv_direct_kernel" in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows
                 if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
         return gemv, copy
@@ -386,10 +387,6 @@ def main():
     sum_bytes = sum(p["weight_bytes"] for p in per)
     sum_us = sum(p["us_per_launch"] for p in per)
     achieved = sum_bytes / (sum_us * 1e-6) / 1e9
-    per_kernel = {}
-    for fmt, G in fmts:
-        us = [p["us_per_launch"] for p in per if p["variant"].startswith("int4" if fmt == 0 else "nf4")]
-        per_kernel["gemv_kernel<%d, %d, 1, 4>" % (fmt, G // 8)] = round(sum(us) / len(us), 3)
 
     traffic_rows = read_traffic_profile()
     traffic = None
@@ -426,7 +423,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": "packed N*K/2 + fp16 scales (+ zeros) = %d" % per_set,
-                     "launch_average_us": round(sum_us / len(per), 3), "per_kernel_average_us": per_kernel},
+                     "launch_average_us": round(sum_us / len(per), 3)},
         "per_launch": per,
         "gemm_prefill": gemm,
         "cpu_baseline": cpu,
