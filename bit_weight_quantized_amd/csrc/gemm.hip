@@ -18,12 +18,12 @@
 //           scales, zero points and token scales are applied after the
 //           integer accumulation of each group.
 //
-// Tiling.  A workgroup of 4 waves (2 x 2) owns a BM x BN output tile, BM = 128
-// rows of tokens, BN = 32 * NT columns; each wave owns 64 x 16*NT.  The K loop
-// steps one weight-tile column (128 K positions: one or two quantization
-// groups) at a time: the step's activation tile, weight tiles, scales/zeros
-// (and for MSD the slice sums) are stored to LDS while the next step's tiles
-// are already loading into registers.
+// Tiling.  Workgroups of 8 waves (two per SIMD: one wave alone cannot keep a
+// matrix core busy) own 256 tokens x 128 weight rows (fp16 paths) or 128 x
+// 128 (MSD).  The K loop steps one weight-tile column (128 K positions: one
+// or two quantization groups) at a time.  Each step's activation tile,
+// weight tiles and scales are copied global -> LDS by the load unit itself,
+// double buffered, with one barrier per step.
 //
 // Weight tiles.  The packed weights are stored as 1 KB tiles of 16 rows x 128
 // K positions in which lane l finds its B operands in bytes 16 l .. 16 l + 15
@@ -52,8 +52,6 @@
 namespace w4 {
 namespace {
 
-constexpr int kGemmThreads = 256;
-constexpr int kBM = 128;
 constexpr int kStepK = 128;  // one weight-tile column per K step
 constexpr int kXcds = 8;
 
