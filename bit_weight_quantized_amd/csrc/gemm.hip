@@ -97,6 +97,28 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
 }
 
+// fp16 paths: 128 tokens x 256 weight rows per workgroup, the 8 waves side by
+// side along N (each 128 x 32: 8 x 2 products of 16 x 16), so every weight
+// operand is unpacked by exactly one wave and serves 128 token rows.  A K step
+// moves 32 KB of activations, 16 KB of weight tiles and the scales -- a third
+// fewer bytes per product than a 256 x 128 block -- and the 50 KB stage allows
+// three buffers: steps k+1 and k+2 are in flight while step k is computed.
+// The scales (and zero points) of a step travel the same way: a 2-byte copy
+// puts lane l's value, zero-extended, in the dword at base + 4 l, so a step's
+// scales land as [group][scale, zero][256] dwords; their load latency hides
+// behind two steps like the tiles' (a plain load consumed within its step
+// exposed one memory latency per step).
+constexpr int kHBM = 128;
+constexpr int kHBN = 256;
+constexpr int kHA = kHBM * 256;          // activation tile bytes per stage
+constexpr int kHB = (kHBN / 16) * 1024;  // weight tiles
+constexpr int kHS = 2 * 2 * kHBN * 4;    // [group in step][scale, zero][BN] dwords
+constexpr int kHStage = kHA + kHB + kHS;
+constexpr int kHStages = 3;
+constexpr int kHTileCopies = kHA / (kF16Threads * 16) + kHB / (kF16Threads * 16);  // per wave per step
+// scale copies per wave per step: GPT groups x (scale [, zero]) x 4 x 64 columns over 8 waves
+constexpr int h_scale_copies(int fmt, int gpt) { return (gpt * (fmt == 0 ? 2 : 1) * 4 + 7) / 8; }
+
 template <int PATH, int FMT, int GPT>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_f16_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
@@ -109,19 +131,18 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave % 2, wn = wave / 2;  // wn = 0..3
+  const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);  // the wave: columns 32 wn .. 32 wn + 31
   const int ln = lane % 16, kb = lane / 16;
 
   // XCD-aware renumbering (a bijection of [0, tiles))
-  const int tiles_n = (N + kF16BN - 1) / kF16BN;
+  const int tiles_n = (N + kHBN - 1) / kHBN;
   const int tiles = gridDim.x;
   const int b = blockIdx.x;
   const int xcd = b % kXcds, idx = b / kXcds;
   const int per = tiles / kXcds, rem = tiles % kXcds;
   const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const int n0 = (logical % tiles_n) * kF16BN;
-  const int m0 = (logical / tiles_n) * kF16BM;
+  const int n0 = (logical % tiles_n) * kHBN;
+  const int m0 = (logical / tiles_n) * kHBM;
 
   const int ng = K / G;
   const int KT = K / kStepK;
@@ -134,47 +155,67 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // ---- per-lane copy offsets (fixed for the whole K loop; the step adds a
-  // scalar offset).  This wave fills token rows [32 wave, 32 wave + 32), 4 rows
-  // per instruction, and weight tile `wave`.
+  // scalar offset).  Wave w fills token rows [16 w, 16 w + 16), 4 rows per
+  // instruction, and weight tiles 2 w and 2 w + 1.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
-  // instruction i covers rows 32 wave + 4 i + lane / 16; its swizzle depends on
-  // i % 4 only, so four bases plus a row stride give every offset
-  uint32_t voff_a4[4];
+  uint32_t voff_a[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = wave * 32 + 4 * i + lane / 16;
+    const int row = wn * 16 + 4 * i + lane / 16;
     const int c = (lane % 16) ^ (row & 15);
-    voff_a4[i] = (uint32_t)(m0 + row) * (uint32_t)(K * 2) + (uint32_t)c * 16;  // rows past M read zeros
+    voff_a[i] = (uint32_t)(m0 + row) * (uint32_t)(K * 2) + (uint32_t)c * 16;  // rows past M read zeros
   }
-  const uint32_t row16_bytes = (uint32_t)K * 32;  // 16 token rows
-  const uint32_t voff_b = (uint32_t)min(n0 / 16 + wave, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
-  auto issue_step = [&](int kt, unsigned char* st) {
+  uint32_t voff_b[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      copy16_to_lds(xr, voff_a4[i % 4] + (uint32_t)(i / 4) * row16_bytes, (uint32_t)kt * 256,
-                    st + (wave * 32 + 4 * i) * 256);
-    copy16_to_lds(wr, voff_b, (uint32_t)kt * 1024, st + kF16A + wave * 1024);
-  };
-  // scales / zeros of a step: thread t < GPT * BN holds group t / BN, column t % BN
-  auto load_scales = [&](int kt, uint16_t& rs, uint16_t& rz) {
-    const int t = min(tid, GPT * kF16BN - 1);
-    const size_t o = (size_t)min(n0 + t % kF16BN, N - 1) * ng + (size_t)kt * GPT + t / kF16BN;
-    rs = scale[o];
-    rz = FMT == 0 ? zero[o] : (uint16_t)0;
-  };
-  auto store_scales = [&](unsigned char* st, uint16_t rs, uint16_t rz) {
-    if (tid < GPT * kF16BN) {
-      const int gi = tid / kF16BN, col = tid % kF16BN;
-      reinterpret_cast<uint16_t*>(st + kF16A + kF16B)[(gi * 2) * kF16BN + col] = rs;
-      reinterpret_cast<uint16_t*>(st + kF16A + kF16B)[(gi * 2 + 1) * kF16BN + col] = rz;
+  for (int j = 0; j < 2; ++j)
+    voff_b[j] = (uint32_t)min(n0 / 16 + 2 * wn + j, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
+  // scale copies: instruction c (of GPT x arrays x 4) covers group c / (4 A),
+  // array (c / 4) % A (0 scale, 1 zero), columns 64 (c % 4) .. + 63; every
+  // wave issues kSC of them (the last ones repeat earlier ones when the count
+  // does not divide: identical bytes to identical places), so that every wave
+  // has the same number of copies in flight
+  constexpr int kArrays = FMT == 0 ? 2 : 1;
+  constexpr int kSCTotal = GPT * kArrays * 4;
+  constexpr int kSC = h_scale_copies(FMT, GPT);
+  constexpr int kCopies = kHTileCopies + kSC;
+  static_assert(kCopies < 16, "copy count must fit the low vmcnt field");
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scale, (uint32_t)((size_t)N * ng * 2));
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(FMT == 0 ? zero : scale, (uint32_t)((size_t)N * ng * 2));
+  uint32_t voff_s[kSC];
+  int sc_dst[kSC];
+#pragma unroll
+  for (int j = 0; j < kSC; ++j) {
+    const int c = (wn * kSC + j) % kSCTotal;
+    const int gi = c / (4 * kArrays), arr = (c / 4) % kArrays, quarter = c % 4;
+    const int col = quarter * 64 + lane;
+    // columns past N read zeros (the buffer's range check)
+    voff_s[j] = (uint32_t)(n0 + col) * (uint32_t)ng * 2u + (uint32_t)gi * 2u;
+    sc_dst[j] = kHA + kHB + ((gi * 2 + arr) * kHBN + quarter * 64) * 4;
+  }
+  auto stage = [&](int kt) { return smem + (kt % kHStages) * kHStage; };
+  auto issue_step = [&](int kt) {
+    unsigned char* st = stage(kt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy16_to_lds(xr, voff_a[i], (uint32_t)kt * 256, st + (wn * 16 + 4 * i) * 256);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) copy16_to_lds(wr, voff_b[j], (uint32_t)kt * 1024, st + kHA + (2 * wn + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < kSC; ++j) {
+      const int c = (wn * kSC + j) % kSCTotal;
+      const __amdgpu_buffer_rsrc_t rr = ((c / 4) % kArrays) == 1 ? zr : sr;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(st + sc_dst[j]), 2, voff_s[j], (uint32_t)kt * GPT * 2u,
+                                               0, 0);
     }
   };
+  // all but the newest step's copies have landed (vmcnt = kCopies in the low
+  // field, bits 15:14 zero; expcnt and lgkmcnt left at their maxima)
+  auto wait_all_but_one_step = [&]() { __builtin_amdgcn_s_waitcnt(kCopies | (0x7 << 4) | (0xF << 8)); };
   // operand-read offsets within a stage: word w of token tile mt at
-  // a_off[w] + mt * 4096 (swizzled chunk 4w + kb of row wm*128 + mt*16 + ln)
+  // a_off[w] + mt * 4096 (swizzled chunk 4w + kb of row mt*16 + ln)
   uint32_t a_off[4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) a_off[w] = (uint32_t)(wm * 128 + ln) * 256 + ((uint32_t)((4 * w + kb) ^ ln) << 4);
+  for (int w = 0; w < 4; ++w) a_off[w] = (uint32_t)ln * 256 + ((uint32_t)((4 * w + kb) ^ ln) << 4);
 
   f32x4 C[MT][NT];
 #pragma unroll
@@ -182,34 +223,26 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  {
-    uint16_t rs, rz;
-    issue_step(0, smem);
-    load_scales(0, rs, rz);
-    store_scales(smem, rs, rz);
+  // ---- prologue: steps 0 and 1 in flight, step 0 landed
+  issue_step(0);
+  if (KT > 1) {
+    issue_step(1);
+    wait_all_but_one_step();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
-    unsigned char* cur = smem + (kt & 1) * kF16Stage;
-    unsigned char* nxt = smem + ((kt + 1) & 1) * kF16Stage;
-    const bool more = kt + 1 < KT;
-    uint16_t rs = 0, rz = 0;
-    if (more) {
-      issue_step(kt + 1, nxt);
-      load_scales(kt + 1, rs, rz);
-    }
+    const unsigned char* cur = stage(kt);
+    const bool more2 = kt + 2 < KT;
+    if (more2) issue_step(kt + 2);
 
-    const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(cur + kF16A + kF16B);
+    const uint32_t* s_lds = reinterpret_cast<const uint32_t*>(cur + kHA + kHB);
     u32x4 Bq[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kF16A + (wn * NT + nt) * 1024 + lane * 16);
+    for (int nt = 0; nt < NT; ++nt) Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kHA + (2 * wn + nt) * 1024 + lane * 16);
 
-    // Word by word: the next word's weight operands are unpacked while this
-    // word's 16 products run; the second wave on the SIMD covers the LDS
-    // latency of the fragment reads.
     float sfv[GPT][NT];      // PS: per-column scale (x 2^24 for INT4)
     uint32_t zzv[GPT][NT];   // INT4: zero-point pair
     uint32_t spv[GPT][NT];   // DQ: (s, s) pair
@@ -218,12 +251,12 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int col = wn * 32 + nt * 16 + ln;
-        const uint32_t sb = s_lds[(gi * 2) * kF16BN + col];
+        const uint32_t sb = s_lds[(gi * 2) * kHBN + col];
         spv[gi][nt] = sb | (sb << 16);
         sfv[gi][nt] = half_bits_to_float((uint16_t)sb) * (FMT == 0 ? 16777216.0f : 1.0f);
         zzv[gi][nt] = 0;
         if constexpr (FMT == 0) {
-          const uint32_t z = (uint32_t)half_bits_to_float(s_lds[(gi * 2 + 1) * kF16BN + col]);  // 0..15
+          const uint32_t z = (uint32_t)half_bits_to_float(s_lds[(gi * 2 + 1) * kHBN + col]);  // 0..15
           // PS: (z, z) * 2^-24 as subnormal fp16; DQ: (1024 + z, 1024 + z)
           zzv[gi][nt] = PATH == 1 ? (z | (z << 16)) : ((0x6400u | z) | ((0x6400u | z) << 16));
         }
@@ -259,16 +292,23 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
       for (int mt = 0; mt < MT; ++mt) A[mt] = *reinterpret_cast<const u32x4*>(cur + a_off[w] + mt * 4096);
     };
 
+    // Word by word, the next word's operands are read and unpacked while this
+    // word's 16 products run.
     f32x4 acc[MT][NT];  // PS: the group's partial products
     u32x4 B0[NT], B1[NT];
+    u32x4 A0[MT], A1[MT];
+    load_a(A0, 0);
     unpack(B0, 0);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       u32x4(&Bc)[NT] = (w % 2 == 0) ? B0 : B1;
       u32x4(&Bn)[NT] = (w % 2 == 0) ? B1 : B0;
-      u32x4 A[MT];
-      load_a(A, w);
-      if (w + 1 < 4) unpack(Bn, w + 1);  // next word's operands while this word's products run
+      u32x4(&A)[MT] = (w % 2 == 0) ? A0 : A1;
+      u32x4(&An)[MT] = (w % 2 == 0) ? A1 : A0;
+      if (w + 1 < 4) {
+        load_a(An, w + 1);
+        unpack(Bn, w + 1);
+      }
       const bool first = (w % WPG) == 0;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -290,16 +330,18 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
 
-    if (more) store_scales(nxt, rs, rz);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies for the next step have landed
-    __syncthreads();                // everyone's have, and nobody still reads this step's buffer
+    if (more2)
+      wait_all_but_one_step();  // step kt+1's copies have landed
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // everyone's have, and nobody still reads this step's buffer
   }
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + mt * 16 + 4 * kb + i;
+      const int m = m0 + mt * 16 + 4 * kb + i;
       if (m >= M) continue;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -314,12 +356,12 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
                const uint16_t* zero, uint16_t* y, hipStream_t s) {
   if ((size_t)M * K * 2 >= (1ull << 32))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm: activations of %d x %d exceed the 4 GiB one call addresses", M, K);
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>), 2 * kF16Stage,
-                                   "w4_gemm");
+  constexpr int kLds = kHStages * kHStage;
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>), kLds, "w4_gemm");
   if (st != 0) return st;
-  const long tiles = (long)((N + kF16BN - 1) / kF16BN) * ((M + kF16BM - 1) / kF16BM);
-  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kF16Stage, s, x,
-                     M, K, N, packed, scale, zero, y);
+  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
+  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, x, M, K,
+                     N, packed, scale, zero, y);
   return check_launch("gemm");
 }
 
