@@ -49,6 +49,9 @@
 #include "w4_device.h"
 #include "w4_internal.h"
 
+#include <algorithm>
+#include <cstdlib>
+
 namespace w4 {
 namespace {
 
@@ -122,7 +125,8 @@ constexpr int h_scale_copies(int fmt, int gpt) { return (gpt * (fmt == 0 ? 2 : 1
 template <int PATH, int FMT, int GPT>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_f16_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y) {
+    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
+    float* __restrict__ partial) {
   constexpr int G = kStepK / GPT;
   constexpr int WPG = 4 / GPT;  // products (tile words) per group
   constexpr int MT = 8, NT = 2;
@@ -132,6 +136,8 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);  // the wave: columns 32 wn .. 32 wn + 31
+  const int S = gridDim.y;  // K slices (partials in `partial` when S > 1)
+  const int ks = blockIdx.y;
   const int ln = lane % 16, kb = lane / 16;
 
   // XCD-aware renumbering (a bijection of [0, tiles))
@@ -147,6 +153,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   const int ng = K / G;
   const int KT = K / kStepK;
   const int ntile_last = N / 16 - 1;
+  const int kt0 = (int)((long)KT * ks / S), kt1 = (int)((long)KT * (ks + 1) / S);  // this slice's steps
 
   if constexpr (FMT == 1) {
     for (int i = tid; i < 256; i += kF16Threads)
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     voff_s[j] = (uint32_t)(n0 + col) * (uint32_t)ng * 2u + (uint32_t)gi * 2u;
     sc_dst[j] = kHA + kHB + ((gi * 2 + arr) * kHBN + quarter * 64) * 4;
   }
-  auto stage = [&](int kt) { return smem + (kt % kHStages) * kHStage; };
+  auto stage = [&](int kt) { return smem + ((kt - kt0) % kHStages) * kHStage; };
   auto issue_step = [&](int kt) {
     unsigned char* st = stage(kt);
 #pragma unroll
@@ -223,19 +230,19 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: steps 0 and 1 in flight, step 0 landed
-  issue_step(0);
-  if (KT > 1) {
-    issue_step(1);
+  // ---- prologue: the slice's first two steps in flight, the first landed
+  issue_step(kt0);
+  if (kt1 - kt0 > 1) {
+    issue_step(kt0 + 1);
     wait_all_but_one_step();
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     const unsigned char* cur = stage(kt);
-    const bool more2 = kt + 2 < KT;
+    const bool more2 = kt + 2 < kt1;
     if (more2) issue_step(kt + 2);
 
     const uint32_t* s_lds = reinterpret_cast<const uint32_t*>(cur + kHA + kHB);
@@ -346,23 +353,29 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + wn * 32 + nt * 16 + ln;
-        if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
+        if (n >= N) continue;
+        if (S == 1)
+          y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
+        else
+          partial[((size_t)ks * M + m) * N + n] = C[mt][nt][i];
       }
     }
 }
 
 template <int PATH, int FMT, int GPT>
 int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
-               const uint16_t* zero, uint16_t* y, hipStream_t s) {
+               const uint16_t* zero, uint16_t* y, float* partial, int S, hipStream_t s) {
   if ((size_t)M * K * 2 >= (1ull << 32))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm: activations of %d x %d exceed the 4 GiB one call addresses", M, K);
   constexpr int kLds = kHStages * kHStage;
   const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>), kLds, "w4_gemm");
   if (st != 0) return st;
   const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
-  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, x, M, K,
-                     N, packed, scale, zero, y);
-  return check_launch("gemm");
+  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles, (unsigned)S), dim3(kF16Threads), kLds,
+                     s, x, M, K, N, packed, scale, zero, y, partial);
+  const int st2 = check_launch("gemm");
+  if (st2 != 0 || S == 1) return st2;
+  return launch_reduce_partials(partial, S, (long)M * N, y, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -593,9 +606,32 @@ int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed,
 
 }  // namespace
 
+// K slices for the fp16 GEMM: while the grid holds fewer than about 192
+// workgroups (256 CUs), double S as long as every slice keeps at least 4
+// steps.  M = 256 layers: N = 8192 has 64 tiles -> S = 4.
+int gemm_split(int M, int K, int N) {
+  const int KT = K / kStepK;
+  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
+  int S = 1;
+  const char* e = std::getenv("W4_GEMM_S");
+  if (e && *e && std::atoi(e) >= 1) return std::min(std::atoi(e), KT);
+  while (tiles * S < 192 && KT / (2 * S) >= 4) S *= 2;
+  return S;
+}
+
+size_t gemm_workspace_bytes(int M, int K, int N) {
+  const int S = gemm_split(M, K, N);
+  return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
+}
+
 int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
-                const uint16_t* zero, int G, int fmt, int mode, uint16_t* y, hipStream_t s) {
-#define W4_GEMM_CASE(PATH, FMT, GPT) return launch_f16<PATH, FMT, GPT>(x, M, K, N, packed, scale, zero, y, s)
+                const uint16_t* zero, int G, int fmt, int mode, uint16_t* y, void* ws, size_t ws_bytes,
+                hipStream_t s) {
+  int S = gemm_split(M, K, N);
+  if (S > 1 && (!ws || ws_bytes < (size_t)S * M * N * sizeof(float))) S = 1;  // no room for partials: unsplit
+  float* partial = S > 1 ? static_cast<float*>(ws) : nullptr;
+#define W4_GEMM_CASE(PATH, FMT, GPT) \
+  return launch_f16<PATH, FMT, GPT>(x, M, K, N, packed, scale, zero, y, partial, S, s)
   if (mode == 0) {
     if (fmt == 0) {
       if (G == 64) W4_GEMM_CASE(0, 0, 2);

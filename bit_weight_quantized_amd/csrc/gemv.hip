@@ -770,12 +770,7 @@ int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const ui
   if (st != 0) return st;
   hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
                      y, partial, c.nwr, c.nwk, c.sc_pitch, c.x_bytes);
-  if (c.s > 1) {
-    const long mn = (long)M * N;
-    const long threads = (mn + 3) / 4;
-    hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, partial, c.s, mn,
-                       y);
-  }
+  if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
 }
 
@@ -788,12 +783,7 @@ int launch_direct(const GemvPlan& c, const uint16_t* x, int M, int K, int N, con
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   hipLaunchKernelGGL((gemv_direct_kernel<FMT, LB, MT, C, R>), grid, block, c.lds_bytes, s, x, M, K, N, packed,
                      scale, zero, y, partial, c.sc_pitch);
-  if (c.s > 1) {
-    const long mn = (long)M * N;
-    const long threads = (mn + 3) / 4;
-    hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, partial, c.s, mn,
-                       y);
-  }
+  if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
 }
 
@@ -821,6 +811,12 @@ int launch_mt(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const u
 }
 
 }  // namespace
+
+int launch_reduce_partials(const float* partial, int S, long MN, uint16_t* y, hipStream_t s) {
+  const long threads = (MN + 3) / 4;
+  hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, partial, S, MN, y);
+  return check_launch("reduce partials");
+}
 
 int launch_gemv(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
                 const uint16_t* scale, const uint16_t* zero, int G, int fmt, uint16_t* y, void* ws,

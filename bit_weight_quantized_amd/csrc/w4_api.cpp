@@ -142,14 +142,14 @@ int w4_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
             const uint16_t* scale, const uint16_t* zero, int G, int fmt, int mode,
             uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
   g_last_error[0] = '\0';
-  (void)ws;
-  (void)ws_bytes;  // the tiled product needs no workspace
   int st;
   if ((st = check_matmul_shape("w4_gemm", M, K, N, G)) != W4_OK) return st;
   if (mode != W4_DQ_F16 && mode != W4_POSTSCALE) return fail(W4_EINVAL, "w4_gemm: unknown mode %d", mode);
   if ((st = check_weights("w4_gemm", packed, scale, zero, fmt)) != W4_OK) return st;
   if ((st = check_io("w4_gemm", x, y)) != W4_OK) return st;
-  return launch_gemm(x, M, K, N, packed, scale, zero, G, fmt, mode, y, (hipStream_t)stream);
+  if (ws && ws_bytes >= gemm_workspace_bytes(M, K, N) && !aligned16(ws))
+    return fail(W4_EINVAL, "w4_gemm: workspace must be 16-byte aligned");
+  return launch_gemm(x, M, K, N, packed, scale, zero, G, fmt, mode, y, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int w4_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
@@ -184,8 +184,10 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
   switch (op) {
     case W4_OP_QUANTIZE:
     case W4_OP_PACK:
-    case W4_OP_GEMM:
       return 0;
+    case W4_OP_GEMM:
+      if (M < 1 || K < 1 || N < 1 || K % 128) return 0;
+      return gemm_workspace_bytes(M, K, N);
     case W4_OP_GEMV:
       if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G || K % 128) return 0;
       return plan_gemv(M, K, N, G, fmt_or_mode == W4_NF4 ? W4_NF4 : W4_INT4_ASYM).ws_bytes;

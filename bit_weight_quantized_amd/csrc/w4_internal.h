@@ -40,9 +40,16 @@ int launch_gemv(const GemvPlan& plan, const uint16_t* x, int M, int K, int N,
                 const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
                 int G, int fmt, uint16_t* y, void* ws, hipStream_t s);
 
+// fp16 GEMM: K slices over workgroups (1 when the grid already fills the
+// chip) and the fp32 partial workspace that takes ([S][M][N], 0 when S = 1).
+int gemm_split(int M, int K, int N);
+size_t gemm_workspace_bytes(int M, int K, int N);
+// Launches the fp16 GEMM; with ws_bytes < gemm_workspace_bytes it runs unsplit.
 int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
                 const uint16_t* scale, const uint16_t* zero, int G, int fmt,
-                int mode, uint16_t* y, hipStream_t s);
+                int mode, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t s);
+// y[i] = fp16(sum over k < S of partial[k * MN + i]) in slice order.
+int launch_reduce_partials(const float* partial, int S, long MN, uint16_t* y, hipStream_t s);
 
 // Workspace of the decomposed product: int8 slices [nslices][M][K] in the
 // matrix-core operand layout (256-byte aligned), then fp32 token scales

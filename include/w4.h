@@ -139,7 +139,14 @@ int w4_gemv(const uint16_t* x, int M, int K, int N,
 /*
  * w4_gemm -- prefill-shaped product y[M][N] = x[M][K] . W' for any M >= 1 on
  * fp16 matrix cores, in `mode` W4_DQ_F16 or W4_POSTSCALE (see w4_mode), for
- * either weight format.  Needs no workspace: ws may be NULL, ws_bytes 0.
+ * either weight format.  Workspace is optional: when the output tiles alone
+ * would not fill the GPU (e.g. M = 256, N = 8192), K is split over
+ * workgroups if the caller passes at least
+ * w4_workspace_bytes(W4_OP_GEMM, M, K, N, G, mode) bytes (16-byte aligned,
+ * no initial contents needed: fp32 partials [S][M][N], added in slice order
+ * by a second kernel on the same stream); with less (or NULL) the product
+ * runs unsplit.  Results do not depend on the split beyond fp32 rounding of
+ * the partial sums.
  */
 int w4_gemm(const uint16_t* x, int M, int K, int N,
             const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,

@@ -47,6 +47,47 @@ def test_gemm_small(fmt, G, mode, M, K, N):
     assert err <= TOL_ROW_REL_L2, err
 
 
+@pytest.mark.parametrize("S", [2, 3, 5])
+@pytest.mark.parametrize("M,K,N", [(130, 1024, 272), (257, 768, 144)])
+def test_gemm_split_k(monkeypatch, S, M, K, N):
+    """K split over S workgroup slices (fp32 partials added by a second
+    kernel): within tolerance of the oracle for both modes and formats,
+    repeatable, and independent of the workspace's previous contents (NaN
+    bytes here)."""
+    require_gpu()
+    monkeypatch.setenv("W4_GEMM_S", str(S))
+    w = wl.make_weight(300 + S, 0, N, K)
+    x = wl.make_activations(300 + S, 0, M, K)
+    for fmt, G in FMTS[:3]:
+        codes, scale, zero = oracle_weights(fmt, w, G)
+        packed, sc, zc = upload_weights(codes, scale, zero)
+        for mode in MODES:
+            n_ws = w4.workspace_bytes(w4.OP_GEMM, M, K, N, G, mode)
+            assert n_ws == min(S, K // 128) * M * N * 4
+            ws = torch.full((n_ws,), 0xFF, dtype=torch.uint8, device="cuda")
+            announce("gemm split", dict(S=S, fmt=fmt, G=G, mode=mode, M=M, K=K, N=N))
+            y1 = host(w4.gemm(dev(x), packed, sc, zc, G, fmt, mode, workspace=ws))
+            y2 = host(w4.gemm(dev(x), packed, sc, zc, G, fmt, mode, workspace=ws))
+            assert row_rel_l2(y1, reference(mode, fmt, x, codes, scale, zero, G)) <= TOL_ROW_REL_L2
+            assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+def test_gemm_without_workspace_runs_unsplit():
+    """A shape that would split (M = 256, N = 1024: 8 output tiles) computes
+    the same product unsplit when the caller passes no room for partials."""
+    require_gpu()
+    M, K, N, G, fmt = 256, 2048, 1024, 128, o.FMT_INT4_ASYM
+    assert w4.workspace_bytes(w4.OP_GEMM, M, K, N, G, w4.POSTSCALE) > 0
+    w = wl.make_weight(13, 0, N, K)
+    x = wl.make_activations(13, 0, M, K)
+    codes, scale, zero = oracle_weights(fmt, w, G)
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    tiny = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    announce("gemm unsplit", dict(M=M, K=K, N=N))
+    y = host(w4.gemm(dev(x), packed, sc, zc, G, fmt, w4.POSTSCALE, workspace=tiny))
+    assert row_rel_l2(y, reference(w4.POSTSCALE, fmt, x, codes, scale, zero, G)) <= TOL_ROW_REL_L2
+
+
 def test_gemm_zero_rows_and_columns():
     """All-zero weight rows give exactly zero outputs; an all-zero token row
     gives an exactly zero output row."""
