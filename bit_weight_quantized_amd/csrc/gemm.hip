@@ -70,25 +70,14 @@ __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return per
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return perm_b32(b, a, 0x07060302u); }
 
 // ---------------------------------------------------------------------------
-// fp16 matrix-core paths (PATH_DQ, PATH_PS), large tile: a workgroup of 8
-// waves (2 x 4, two per SIMD: one wave alone cannot keep the matrix core
-// busy) owns 256 tokens x 128 weight rows; each wave owns 128 x 32 (8 x 2
-// products of 16 x 16), so every unpacked weight operand feeds 128 token
-// rows.  The K step is one weight-tile column.  Both operand tiles of a
-// step are copied global -> LDS by the load unit itself (16 bytes per lane,
-// lane l's bytes landing at the instruction's LDS base + 16 l), double
-// buffered: step k+1 is in flight while step k is computed, and one barrier
-// per step hands the buffers over.  The activation tile is row-major in LDS
-// (256 bytes per token row), 16-byte chunk c of row m at position c ^ (m % 16),
-// which keeps both the fill and the operand reads free of bank conflicts.
-// One workgroup per CU (its two buffers take most of the LDS).
-constexpr int kF16BM = 256;
-constexpr int kF16BN = 128;
-constexpr int kF16Threads = 512;  // 8 waves: 2 (M) x 4 (N), two per SIMD
-constexpr int kF16A = kF16BM * 256;            // activation tile bytes per stage
-constexpr int kF16B = (kF16BN / 16) * 1024;    // weight tiles
-constexpr int kF16S = 2 * 2 * kF16BN * 2;      // [group in step][scale, zero][BN] fp16 bits
-constexpr int kF16Stage = kF16A + kF16B + kF16S;
+// Both matrix-core kernels run 8 waves per workgroup, two per SIMD (one wave
+// alone cannot keep a matrix core busy), one workgroup per CU.  Operand tiles
+// are copied global -> LDS by the load unit itself (16 bytes per lane, lane
+// l's bytes landing at the instruction's LDS base + 16 l).  In LDS, a token
+// row's 16-byte chunk c sits at c ^ (row mod 16) (fp16) or c ^ (row mod 8)
+// (int8), which keeps both the fill and the operand reads free of bank
+// conflicts.
+constexpr int kF16Threads = 512;  // 8 waves
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -379,17 +368,22 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
 }
 
 // ---------------------------------------------------------------------------
-// Multi-Scale Dequant path, same frame as the fp16 kernel (8 waves, buffer ->
-// LDS copies, double buffered) with 128 tokens x 128 weight rows per
-// workgroup, each wave 64 x 32 (two slices of accumulators per tile).  The activation slices arrive from the decomposition kernel in
-// the operand layout (per 64 K positions, lane kb's 16 bytes contiguous), so
-// a token row of a step is 128 bytes = 8 chunks, stored at chunk c ^ (m % 8).
-// The zero point is folded into the weight operand exactly: per byte,
-// ((q | 0x80) - z) ^ 0x80 is q - z in two's complement (no byte borrows, since
-// 113 <= 128 + q - z <= 143), so each group's int32 product is
+// Multi-Scale Dequant path, on the fp16 kernel's frame: 128 tokens x 256
+// weight rows per workgroup, the 8 waves side by side along N (each 128 x 32,
+// so every widened weight operand serves 8 token tiles and both slices), and
+// three stages of global -> LDS copies (both slices' tiles, the weight tiles
+// and the scales).  The activation slices arrive from the decomposition kernel
+// in the operand layout (per 64 K positions, lane kb's 16 bytes contiguous),
+// so a token row of a step is 128 bytes = 8 chunks, stored at chunk
+// c ^ (m % 8).  The zero point is folded into the weight operand exactly: per
+// byte, ((q | 0x80) - z) ^ 0x80 is q - z in two's complement (no byte borrows,
+// since 113 <= 128 + q - z <= 143), so each group's int32 product is
 // D_j = sum A_j * (q - z) and the epilogue is C += s * (D_1 + r * D_2) with
 // r = s_2 / s_1 per token; y = s_1 * C.
-constexpr int kMsdBM = 128;  // tokens per workgroup (each wave: 64 x 32)
+// Token tiles per wave: 8 (128 tokens per workgroup) where the registers
+// allow, 4 for G = 64 with two slices and for the test variant that also
+// writes the integer products.
+constexpr int msd_mt(int gpt, int ns, bool dbg) { return (!dbg && (gpt == 1 || ns == 1)) ? 8 : 4; }
 
 template <int GPT, int NS, bool DBG>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_msd_kernel(
@@ -398,27 +392,27 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     const float* __restrict__ tok_scale, int32_t* __restrict__ acc_out) {
   constexpr int G = kStepK / GPT;
   constexpr int UPG = 2 / GPT;  // int8 products (64 K positions each) per group
-  constexpr int MT = 4, NT = 2;
-  constexpr int BM = kMsdBM;
-  constexpr int kSliceBytes = BM * 128;  // one slice's rows of a step
-  constexpr int kA = NS * kSliceBytes;
-  constexpr int kStage = kA + kF16B + kF16S;
+  constexpr int MT = msd_mt(GPT, NS, DBG), NT = 2;
+  constexpr int BM = 16 * MT;       // tokens per workgroup
+  constexpr int kRowCopies = BM / 64;  // 8-row copies per wave per slice
+  constexpr int kSlice = BM * 128;  // one slice's rows of a step
+  constexpr int kA = NS * kSlice;
+  constexpr int kStage = kA + kHB + kHS;
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float ratio[kMsdBM];  // s_2 / s_1 per tile row
+  __shared__ float ratio[BM];  // s_2 / s_1 per tile row
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave % 2, wn = wave / 2;
+  const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int ln = lane % 16, kb = lane / 16;
 
-  const int tiles_n = (N + kF16BN - 1) / kF16BN;
+  const int tiles_n = (N + kHBN - 1) / kHBN;
   const int tiles = gridDim.x;
   const int b = blockIdx.x;
   const int xcd = b % kXcds, idx = b / kXcds;
   const int per = tiles / kXcds, rem = tiles % kXcds;
   const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const int n0 = (logical % tiles_n) * kF16BN;
+  const int n0 = (logical % tiles_n) * kHBN;
   const int m0 = (logical / tiles_n) * BM;
 
   const int ng = K / G;
@@ -431,39 +425,58 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     ratio[tid] = (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
   }
 
-  // copies: slice j = wave / (8 / NS); 8 rows (128 B each) per instruction
-  constexpr int kWavesPerSlice = 8 / NS;
-  constexpr int kInstr = (BM / 8) / kWavesPerSlice;  // instructions per wave per step
-  const int js = wave / kWavesPerSlice;
-  const int row_base = (wave % kWavesPerSlice) * (BM / kWavesPerSlice);
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(slices + (size_t)js * M * K, (uint32_t)((size_t)M * K));
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
-  const int arow = lane / 8, apos = lane % 8;
-  const uint32_t voff_a0 = (uint32_t)(m0 + row_base + arow) * (uint32_t)K;  // rows past M read zeros
-  const uint32_t voff_b = (uint32_t)min(n0 / 16 + wave, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
-  auto issue_step = [&](int kt, unsigned char* st) {
+  // ---- copies.  Wave w fills rows [w BM/8, (w + 1) BM/8) of every slice (8
+  // rows of 128 bytes per instruction), weight tiles 2 w and 2 w + 1, and its
+  // share of the scale copies (as in the fp16 kernel).
+  __amdgpu_buffer_rsrc_t ar[NS];
 #pragma unroll
-    for (int i = 0; i < kInstr; ++i) {
-      const int row = row_base + 8 * i + arow;
-      const int c = apos ^ (row & 7);
-      copy16_to_lds(ar, voff_a0 + (uint32_t)(8 * i) * (uint32_t)K + (uint32_t)c * 16, (uint32_t)kt * 128,
-                    st + js * kSliceBytes + (row_base + 8 * i) * 128);
+  for (int j = 0; j < NS; ++j) ar[j] = make_rsrc(slices + (size_t)j * M * K, (uint32_t)((size_t)M * K));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
+  uint32_t voff_a[kRowCopies];
+#pragma unroll
+  for (int i = 0; i < kRowCopies; ++i) {
+    const int row = wn * (BM / 8) + 8 * i + lane / 8;
+    const int c = (lane % 8) ^ (row & 7);
+    voff_a[i] = (uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)c * 16;  // rows past M read zeros
+  }
+  uint32_t voff_b[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    voff_b[j] = (uint32_t)min(n0 / 16 + 2 * wn + j, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
+  constexpr int kSCTotal = GPT * 2 * 4;
+  constexpr int kSC = h_scale_copies(0, GPT);
+  constexpr int kCopies = NS * kRowCopies + 2 + kSC;
+  static_assert(kCopies < 16, "copy count must fit the low vmcnt field");
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scale, (uint32_t)((size_t)N * ng * 2));
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(zero, (uint32_t)((size_t)N * ng * 2));
+  uint32_t voff_s[kSC];
+  int sc_dst[kSC];
+#pragma unroll
+  for (int j = 0; j < kSC; ++j) {
+    const int c = (wn * kSC + j) % kSCTotal;
+    const int gi = c / 8, arr = (c / 4) % 2, quarter = c % 4;
+    const int col = quarter * 64 + lane;
+    voff_s[j] = (uint32_t)(n0 + col) * (uint32_t)ng * 2u + (uint32_t)gi * 2u;  // columns past N read zeros
+    sc_dst[j] = kA + kHB + ((gi * 2 + arr) * kHBN + quarter * 64) * 4;
+  }
+  auto stage = [&](int kt) { return smem + (kt % kHStages) * kStage; };
+  auto issue_step = [&](int kt) {
+    unsigned char* st = stage(kt);
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < kRowCopies; ++i)
+        copy16_to_lds(ar[j], voff_a[i], (uint32_t)kt * 128, st + j * kSlice + (wn * (BM / 8) + 8 * i) * 128);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) copy16_to_lds(wr, voff_b[j], (uint32_t)kt * 1024, st + kA + (2 * wn + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < kSC; ++j) {
+      const int c = (wn * kSC + j) % kSCTotal;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(((c / 4) % 2) == 1 ? zr : sr, (lds_void*)(st + sc_dst[j]), 2,
+                                               voff_s[j], (uint32_t)kt * GPT * 2u, 0, 0);
     }
-    copy16_to_lds(wr, voff_b, (uint32_t)kt * 1024, st + kA + wave * 1024);
   };
-  auto load_scales = [&](int kt, uint16_t& rs, uint16_t& rz) {
-    const int t = min(tid, GPT * kF16BN - 1);
-    const size_t o = (size_t)min(n0 + t % kF16BN, N - 1) * ng + (size_t)kt * GPT + t / kF16BN;
-    rs = scale[o];
-    rz = zero[o];
-  };
-  auto store_scales = [&](unsigned char* st, uint16_t rs, uint16_t rz) {
-    if (tid < GPT * kF16BN) {
-      const int gi = tid / kF16BN, col = tid % kF16BN;
-      reinterpret_cast<uint16_t*>(st + kA + kF16B)[(gi * 2) * kF16BN + col] = rs;
-      reinterpret_cast<uint16_t*>(st + kA + kF16B)[(gi * 2 + 1) * kF16BN + col] = rz;
-    }
-  };
+  auto wait_all_but_one_step = [&]() { __builtin_amdgcn_s_waitcnt(kCopies | (0x7 << 4) | (0xF << 8)); };
 
   f32x4 C[MT][NT];
 #pragma unroll
@@ -471,41 +484,35 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  {
-    uint16_t rs, rz;
-    issue_step(0, smem);
-    load_scales(0, rs, rz);
-    store_scales(smem, rs, rz);
+  issue_step(0);
+  if (KT > 1) {
+    issue_step(1);
+    wait_all_but_one_step();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
-    unsigned char* cur = smem + (kt & 1) * kStage;
-    unsigned char* nxt = smem + ((kt + 1) & 1) * kStage;
-    const bool more = kt + 1 < KT;
-    uint16_t rs = 0, rz = 0;
-    if (more) {
-      issue_step(kt + 1, nxt);
-      load_scales(kt + 1, rs, rz);
-    }
-    const uint16_t* s_lds = reinterpret_cast<const uint16_t*>(cur + kA + kF16B);
+    const unsigned char* cur = stage(kt);
+    const bool more2 = kt + 2 < KT;
+    if (more2) issue_step(kt + 2);
+
+    const uint32_t* s_lds = reinterpret_cast<const uint32_t*>(cur + kA + kHB);
     u32x4 Bq[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kA + (wn * NT + nt) * 1024 + lane * 16);
+    for (int nt = 0; nt < NT; ++nt) Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kA + (2 * wn + nt) * 1024 + lane * 16);
 
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
       u32x4 Bi[UPG][NT];
       float sv[NT];
-      int zv[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int col = wn * 32 + nt * 16 + ln;
-        sv[nt] = half_bits_to_float(s_lds[(gi * 2) * kF16BN + col]);
-        zv[nt] = (int)half_bits_to_float(s_lds[(gi * 2 + 1) * kF16BN + col]);
-        const uint32_t zb = (uint32_t)zv[nt] * 0x01010101u;
+        sv[nt] = half_bits_to_float((uint16_t)s_lds[(gi * 2) * kHBN + col]);
+        const int zv = (int)half_bits_to_float((uint16_t)s_lds[(gi * 2 + 1) * kHBN + col]);
+        const uint32_t zb = (uint32_t)zv * 0x01010101u;
 #pragma unroll
         for (int u = 0; u < UPG; ++u) {
           const int pu = gi * UPG + u;
@@ -517,7 +524,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * 64 + mt * 16 + ln;
+        const int row = mt * 16 + ln;
         i32x4 D[NS][NT];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
@@ -525,7 +532,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
           for (int u = 0; u < UPG; ++u) {
             const int c = 4 * (gi * UPG + u) + kb;
-            A[u] = *reinterpret_cast<const u32x4*>(cur + j * kSliceBytes + row * 128 + ((c ^ (ln & 7)) << 4));
+            A[u] = *reinterpret_cast<const u32x4*>(cur + j * kSlice + row * 128 + ((c ^ (ln & 7)) << 4));
           }
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
             D[j][nt] = d;
           }
         }
-        const int rloc = wm * 64 + mt * 16 + 4 * kb;
+        const int rloc = mt * 16 + 4 * kb;
         const f32x4 rr = *reinterpret_cast<const f32x4*>(&ratio[rloc]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -558,22 +565,23 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
             }
           }
         }
-        // keep each token tile's fragment loads with its own products (hoisting
-        // all eight tiles' loads would not fit the registers of two waves per SIMD)
+        // keep each token tile's fragment reads with its own products
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
-    if (more) store_scales(nxt, rs, rz);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (more2)
+      wait_all_but_one_step();  // step kt+1's copies have landed
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // everyone's have, and nobody still reads this step's buffer
   }
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 64 + mt * 16 + 4 * kb + i;
+      const int m = m0 + mt * 16 + 4 * kb + i;
       if (m >= M) continue;
       const float s1 = tok_scale[m];
 #pragma unroll
@@ -587,20 +595,22 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 template <int GPT, int NS>
 int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
                const uint16_t* zero, uint16_t* y, const float* tok_scale, int32_t* acc_out, hipStream_t s) {
-  constexpr int kStage = NS * kMsdBM * 128 + kF16B + kF16S;
-  if ((size_t)M * K >= (1ull << 32))
+  constexpr int kStage = NS * 16 * msd_mt(GPT, NS, false) * 128 + kHB + kHS;  // the larger of the two variants
+  constexpr int kLds = kHStages * kStage;
+  if ((size_t)NS * M * K >= (1ull << 32))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm_decomp: slices of %d x %d exceed the 4 GiB one call addresses", M, K);
   const void* fn = acc_out ? reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, true>)
                            : reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, false>);
-  const int st = allow_dynamic_lds(fn, 2 * kStage, "w4_gemm_decomp");
+  const int st = allow_dynamic_lds(fn, kLds, "w4_gemm_decomp");
   if (st != 0) return st;
-  const long tiles = (long)((N + kF16BN - 1) / kF16BN) * ((M + kMsdBM - 1) / kMsdBM);
+  const int bm = 16 * msd_mt(GPT, NS, acc_out != nullptr);
+  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + bm - 1) / bm);
   if (acc_out)
-    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kStage, s,
-                       slices, M, K, N, packed, scale, zero, y, tok_scale, acc_out);
+    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices, M,
+                       K, N, packed, scale, zero, y, tok_scale, acc_out);
   else
-    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false>), dim3((unsigned)tiles), dim3(kF16Threads), 2 * kStage, s,
-                       slices, M, K, N, packed, scale, zero, y, tok_scale, acc_out);
+    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices,
+                       M, K, N, packed, scale, zero, y, tok_scale, acc_out);
   return check_launch("gemm_msd");
 }
 
