@@ -325,8 +325,12 @@ def decompose_activations(x, nslices: int = 2):
 
     1. s_j = fp32(max_k |r[m, k]| / 127);
     2. A_j = clamp(rint(r / s_j), -127, 127)  (round-half-to-even);
-    3. r <- r - s_j * A_j  (exact in fp64 for two passes);
+    3. r <- r - s_j * A_j  (exact in fp64 for up to three passes: every
+       residual is a short sum of fp16 and fp32 x int8 terms);
     4. a pass whose scale is 0 yields an all-zero slice.
+
+    ``nslices`` = 1 is one int8 quantization of the activations; 3 adds a
+    third pass on the second residual.
 
     Returns (A int8 [nslices][M][K], s float32 [nslices][M]).
     """
@@ -344,6 +348,45 @@ def decompose_activations(x, nslices: int = 2):
         A[j] = a.astype(np.int8)
         S[j] = s.astype(np.float32)
         r = r - s[:, None] * a
+    return A, S
+
+
+FIXED_RATIO = 254  # s_2 = s_1 / 254 in the fixed-ratio decomposition
+
+
+def decompose_fixed_ratio(x):
+    """Two-slice decomposition with a fixed scale ratio, s_2 = s_1 / 254.
+
+    READING of [MSD] Abstract (the pages do not say how the second scale is
+    chosen): instead of the residual's own absmax, the second slice uses the
+    first slice's step divided by 254.  Since |r_1| <= s_1 / 2, the second
+    slice's codes then lie in [-127, 127] without clamping, and
+    x ~= (s_1 / 254) * (254 * A_1 + A_2): the two integer products combine
+    exactly as 254 * D_1 + D_2 before any conversion to floating point.
+
+    Per token m, in fp64:
+
+    1. s_1 = fp32(max_k |x[m, k]| / 127);
+    2. A_1 = clamp(rint(x / s_1), -127, 127);
+    3. r_1 = x - s_1 * A_1  (exact);
+    4. A_2 = clamp(rint((254 * r_1) / s_1), -127, 127)  (254 * r_1 is exact,
+       the division one correctly rounded fp64 operation);
+    5. s_1 = 0 gives all-zero slices.
+
+    Returns (A int8 [2][M][K], s float32 [2][M]); s[1] = fp32(s_1 / 254) is
+    reported for reference only -- results use the exact ratio.
+    """
+    xd = np.asarray(x).astype(np.float64)
+    M, K = xd.shape
+    amax = np.abs(xd).max(axis=1) if K else np.zeros(M)
+    s1 = fp32_rne(amax / float(INT8_QMAX))
+    nz = s1 != 0.0
+    safe = np.where(nz, s1, 1.0)
+    a1 = np.where(nz[:, None], np.clip(np.rint(xd / safe[:, None]), -INT8_QMAX, INT8_QMAX), 0.0)
+    r1 = xd - s1[:, None] * a1
+    a2 = np.where(nz[:, None], np.clip(np.rint((FIXED_RATIO * r1) / safe[:, None]), -INT8_QMAX, INT8_QMAX), 0.0)
+    A = np.stack([a1, a2]).astype(np.int8)
+    S = np.stack([s1, fp32_rne(s1 / FIXED_RATIO)]).astype(np.float32)
     return A, S
 
 
@@ -374,6 +417,24 @@ def msd_result(tok_scale, acc, scale) -> np.ndarray:
     s = np.asarray(scale, dtype=np.float16).astype(np.float64)  # [N][ng]
     per_slice = np.einsum("jmgn,ng->jmn", D, s)
     return np.einsum("jm,jmn->mn", S, per_slice)
+
+
+def msd_fixed_result(s1, acc, scale) -> np.ndarray:
+    """Fixed-ratio recombination: the integer combine E = 254 * D_1 + D_2 per
+    group (exact), then y[m, n] = (s_1[m] / 254) * sum_g s[n, g] * E[m, g, n]
+    in fp64."""
+    D = np.asarray(acc).astype(np.int64)
+    E = (FIXED_RATIO * D[0] + D[1]).astype(np.float64)
+    s = np.asarray(scale, dtype=np.float16).astype(np.float64)
+    t = np.asarray(s1, dtype=np.float32).astype(np.float64) / FIXED_RATIO
+    return t[:, None] * np.einsum("mgn,ng->mn", E, s)
+
+
+def msd_fixed_matmul(x, codes, scale, zero, G: int):
+    """Full fixed-ratio MSD product: decompose, integer products, combine."""
+    A, S = decompose_fixed_ratio(x)
+    D = msd_accumulators(A, codes, zero, G)
+    return msd_fixed_result(S[0], D, scale), A, S, D
 
 
 def msd_matmul(x, codes, scale, zero, G: int, nslices: int = 2):

@@ -337,6 +337,97 @@ def test_planted_decompose_mistake_rejected():
     assert not _decomp_rows_ok(x, bad, S)
 
 
+def test_three_slices_nearest_integers_exact_residual_and_bound():
+    x = wl.make_activations(97, 0, 6, 512, outliers=True)
+    A, S = o.decompose_activations(x, 3)
+    assert A.shape == (3, 6, 512)
+    assert _decomp_rows_ok(x, A, S)
+    for m in range(6):
+        r = [Fraction(float(v)) for v in x[m]]
+        rf = x[m].astype(np.float64)
+        for j in range(3):
+            sj = Fraction(float(S[j, m]))
+            r = [rv - sj * int(a) for rv, a in zip(r, A[j, m])]
+            rf = rf - np.float64(S[j, m]) * A[j, m].astype(np.float64)
+            # the fp64 residual the oracle carries is the exact one
+            assert all(Fraction(float(a)) == b for a, b in zip(rf, r))
+        worst = max(abs(v) for v in r)
+        assert worst <= Fraction(float(S[2, m])) / 2
+        # each pass shrinks the step by about 254: third step <= amax / 127^3 / 4
+        amax = Fraction(float(np.abs(x[m].astype(np.float64)).max()))
+        assert worst <= amax / (127 * 254 * 254) * Fraction(1 + 2 ** -20)
+
+
+def _fixed_rows_ok(x, A, S):
+    """Brute-force check of a fixed-ratio decomposition, exact rationals."""
+    cand = range(-127, 128)
+    for m in range(x.shape[0]):
+        s1 = Fraction(float(S[0, m]))
+        if s1 == 0:
+            if np.any(A[:, m] != 0):
+                return False
+            continue
+        if Fraction(float(S[1, m])) != Fraction(float(np.float32(float(s1 / 254)))):
+            return False
+        for xv, a1, a2 in zip(x[m], A[0, m], A[1, m]):
+            xv = Fraction(float(xv))
+            e1 = [abs(xv - s1 * c) for c in cand]
+            if abs(xv - s1 * int(a1)) != min(e1):
+                return False
+            r1 = xv - s1 * int(a1)
+            e2 = [abs(r1 - s1 / 254 * c) for c in cand]
+            best = min(e2)
+            if abs(r1 - s1 / 254 * int(a2)) != best:
+                return False
+            # on an exact tie the even code is taken (rint)
+            if e2.count(best) > 1 and int(a2) % 2:
+                return False
+    return True
+
+
+def test_fixed_ratio_nearest_codes_and_bound():
+    x = wl.make_activations(98, 0, 5, 256, outliers=True)
+    x[4, :] = 0
+    A, S = o.decompose_fixed_ratio(x)
+    assert A.dtype == np.int8 and S.dtype == np.float32 and A.shape == (2, 5, 256)
+    assert _fixed_rows_ok(x, A, S)
+    assert np.all(A[:, 4] == 0) and S[0, 4] == 0
+    for m in range(4):
+        s1 = Fraction(float(S[0, m]))
+        worst = max(abs(Fraction(float(xv)) - s1 * int(a1) - s1 / 254 * int(a2))
+                    for xv, a1, a2 in zip(x[m], A[0, m], A[1, m]))
+        assert worst <= s1 / 508
+        assert np.abs(A[1, m]).max() <= 127
+
+
+def test_fixed_ratio_exact_first_slice_and_ties():
+    # x on the first grid: the second slice is zero
+    ints = np.arange(-127, 128, dtype=np.int64)
+    x = (ints * 2.0 ** -6).astype(np.float16)[None, :]
+    A, S = o.decompose_fixed_ratio(x)
+    assert S[0, 0] == np.float32(2.0 ** -6)
+    assert np.array_equal(A[0, 0].astype(np.int64), ints) and np.all(A[1] == 0)
+    # residual of exactly half a second-grid step (s1 = 1, x = 1 + 0.5/254 is
+    # not an fp16; use s1 = 2^-6 * 127 / 127 and a residual of 2^-14): checks
+    # rounding of 254 * r / s1 = 254 * 2^-14 / 2^-6 = 0.9921875 -> 1
+    x2 = np.array([[127 * 2.0 ** -6, 2.0 ** -6 + 2.0 ** -14]], np.float16)
+    A2, S2 = o.decompose_fixed_ratio(x2)
+    assert A2[0, 0, 1] == 1 and A2[1, 0, 1] == 1
+
+
+def test_planted_fixed_ratio_mistakes_rejected():
+    x = wl.make_activations(99, 0, 3, 128, outliers=True)
+    A, S = o.decompose_fixed_ratio(x)
+    # the residual's own scale instead of the fixed ratio
+    Aa, Sa = o.decompose_activations(x, 2)
+    assert not _fixed_rows_ok(x, Aa, np.stack([Sa[0], S[1]]))
+    # ratio 256 instead of 254
+    r1 = x.astype(np.float64) - S[0].astype(np.float64)[:, None] * A[0]
+    bad = A.copy()
+    bad[1] = np.clip(np.rint(256 * r1 / S[0].astype(np.float64)[:, None]), -127, 127).astype(np.int8)
+    assert not _fixed_rows_ok(x, bad, S)
+
+
 # ------------------------------------------------------------------ products
 def _tiny_case(fmt, seed, M=3, N=4, K=256, G=64):
     w = wl.make_weight(seed, 0, N, K)
@@ -412,6 +503,44 @@ def test_msd_result_exact_and_bound():
     amax = np.abs(x.astype(np.float64)).max(axis=1)
     bound = (amax / 64516)[:, None] * np.abs(wd).sum(axis=1)[None, :] * (1 + 2 ** -20)
     assert np.all(np.abs(y - y_exact) <= bound + 1e-12)
+
+
+def test_msd_fixed_result_exact_and_bound():
+    G = 64
+    x, codes, scale, zero = _tiny_case(o.FMT_INT4_ASYM, 72, M=3, N=4, K=256, G=G)
+    y, A, S, D = o.msd_fixed_matmul(x, codes, scale, zero, G)
+    wd = o.dequant_int4_asym(codes, scale, zero, G)
+    # equals the exact rational product of the reconstructed activations
+    for m in range(3):
+        s1 = Fraction(float(S[0, m]))
+        xh = [s1 * int(a1) + s1 / 254 * int(a2) for a1, a2 in zip(A[0, m], A[1, m])]
+        for n in range(4):
+            ex = sum(xv * Fraction(float(wv)) for xv, wv in zip(xh, wd[n]))
+            assert abs(Fraction(float(y[m, n])) - ex) <= abs(ex) * Fraction(2.0 ** -46) + Fraction(2.0 ** -80)
+    # integer combine, brute force
+    for m in range(3):
+        for g in range(4):
+            for n in range(4):
+                want = sum((254 * int(A[0, m, k]) + int(A[1, m, k])) * (int(codes[n, k]) - int(zero[n, g]))
+                           for k in range(G * g, G * g + G))
+                assert 254 * int(D[0, m, g, n]) + int(D[1, m, g, n]) == want
+                assert abs(want) < 2 ** 31
+    # bound against the exact product: |y - y_exact| <= s1/508 * sum|w'|
+    y_exact = o.matmul_ref(x, wd)
+    bound = (S[0].astype(np.float64) / 508)[:, None] * np.abs(wd).sum(axis=1)[None, :] * (1 + 2 ** -20)
+    assert np.all(np.abs(y - y_exact) <= bound + 1e-12)
+
+
+def test_planted_fixed_combine_rejected():
+    G = 64
+    x, codes, scale, zero = _tiny_case(o.FMT_INT4_ASYM, 73, M=2, N=3, K=128, G=G)
+    y, A, S, D = o.msd_fixed_matmul(x, codes, scale, zero, G)
+    y_exact = o.matmul_ref(x, o.dequant_int4_asym(codes, scale, zero, G))
+    # dropping the second slice or weighting it twice moves the result by far
+    # more than the decomposition error (which the bound test above pins)
+    assert o.max_row_rel_l2(y, y_exact) < 1e-3
+    assert o.max_row_rel_l2(o.msd_fixed_result(S[0], np.stack([D[0], 0 * D[1]]), scale), y) > 5e-3
+    assert o.max_row_rel_l2(o.msd_fixed_result(S[0], np.stack([D[0], 2 * D[1]]), scale), y) > 5e-3
 
 
 def test_max_row_rel_l2_hand_example():
