@@ -116,9 +116,10 @@ def cpu_baseline_decode(variants, K, N, n_rows, min_seconds=10.0):
 
 
 def bench_gemm_prefill(w4, torch, reps):
-    """Prefill product M = 2048, K = 5120, N = 25600, INT4 g128, three ways:
-    dequantize-to-fp16 MFMA, post-scaled fp16 MFMA, and the two-slice
-    Multi-Scale Dequant int8 MFMA (its activation decomposition included).
+    """Prefill product M = 2048, K = 5120, N = 25600, INT4 g128: dequantize-to-
+    fp16 MFMA, post-scaled fp16 MFMA, and the Multi-Scale Dequant int8 MFMA
+    with two slices (adaptive and fixed-ratio scales), one and three slices
+    (each with its activation decomposition included).
     Back-to-back launches between HIP events on the launch stream."""
     import workloads as wl
     M, K, N, G = 2048, 5120, 25600, 128
@@ -130,13 +131,17 @@ def bench_gemm_prefill(w4, torch, reps):
     del w, codes
     x = torch.from_numpy(wl.make_activations(4, 0, M, K)).cuda()
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 3), dtype=torch.uint8, device="cuda")
     flops = 2.0 * M * N * K
     paths = {
         "dq_f16": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.DQ_F16, out=y), 1, FP16_MFMA_PEAK_TFLOPS),
         "postscale": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.POSTSCALE, out=y), 1,
                       FP16_MFMA_PEAK_TFLOPS),
         "msd2": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 2, out=y, workspace=ws), 2, INT8_MFMA_PEAK_TOPS),
+        "msd2_fixed": (lambda: w4.gemm_decomp_fixed(x, packed, scale, zero, G, out=y, workspace=ws), 2,
+                       INT8_MFMA_PEAK_TOPS),
+        "msd1": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 1, out=y, workspace=ws), 1, INT8_MFMA_PEAK_TOPS),
+        "msd3": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 3, out=y, workspace=ws), 3, INT8_MFMA_PEAK_TOPS),
     }
     res = {}
     st = torch.cuda.Stream()
@@ -158,9 +163,10 @@ def bench_gemm_prefill(w4, torch, reps):
                          "frac": round(mfma_rate / peak, 4)}
     return {"workload": "prefill_gemm_m2048_k5120_n25600", "M": M, "K": K, "N": N, "fmt": "int4_asym_g128",
             "flops_per_call": flops, "calls_timed": reps,
-            "note": "fp16 paths against the dense fp16 MFMA peak; msd2 issues 2 int8 products per useful "
-                    "multiply-add and is measured against the dense int8 peak; msd2 time includes the "
-                    "activation decomposition",
+            "note": "fp16 paths against the dense fp16 MFMA peak; msdJ issues J int8 products per useful "
+                    "multiply-add and is measured against the dense int8 peak; msd times include the "
+                    "activation decomposition; msd2_fixed uses s2 = s1/254 and combines the two int32 "
+                    "products in integers",
             "paths": res}
 
 

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
-    "lib", "lib_path", "quantize", "pack", "gemv", "gemm", "gemm_decomp",
+    "lib", "lib_path", "quantize", "pack", "gemv", "gemm", "gemm_decomp", "gemm_decomp_fixed",
     "workspace_bytes", "nf4_levels", "version",
 ]
 
@@ -62,6 +62,7 @@ def lib():
         L.w4_gemv.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p]
         L.w4_gemm.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
         L.w4_gemm_decomp.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
+        L.w4_gemm_decomp_fixed.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
         L.w4_workspace_bytes.restype = _sz
         L.w4_nf4_levels.argtypes = [_p]
@@ -70,7 +71,8 @@ def lib():
         L.w4_last_error.argtypes = []
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
-        for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp", "w4_nf4_levels"):
+        for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
+                   "w4_nf4_levels"):
             getattr(L, fn).restype = _i
         _lib = L
     return _lib
@@ -189,6 +191,26 @@ def gemm_decomp(x, packed, scale, zero, G: int, nslices: int = 2, *, out=None, s
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
     _check("w4_gemm_decomp", lib().w4_gemm_decomp(
         _ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, nslices, _ptr(out),
+        _ptr(slices_out), _ptr(tok_scale_out), _ptr(acc_out), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
+    if slices_out is None and tok_scale_out is None and acc_out is None:
+        return out
+    return out, slices_out, tok_scale_out, acc_out
+
+
+def gemm_decomp_fixed(x, packed, scale, zero, G: int, *, out=None, slices_out=None,
+                      tok_scale_out=None, acc_out=None, workspace=None, stream=None):
+    """Two-slice Multi-Scale Dequant product with s_2 = s_1 / 254: the two int8
+    products combine exactly in integers.  Returns as ``gemm_decomp``."""
+    _dev(x, torch.float16, "x")
+    N, K = _weights(packed, scale, zero)
+    M = x.shape[0]
+    out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
+    ws_n = workspace_bytes(OP_GEMM_DECOMP, M, K, N, G, 2)
+    if workspace is None and ws_n:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
+    _check("w4_gemm_decomp_fixed", lib().w4_gemm_decomp_fixed(
+        _ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, _ptr(out),
         _ptr(slices_out), _ptr(tok_scale_out), _ptr(acc_out), _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream(stream)))
     if slices_out is None and tok_scale_out is None and acc_out is None:

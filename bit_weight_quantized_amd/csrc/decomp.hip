@@ -4,9 +4,10 @@
 // slices with per-token scales, so that x ~= sum_j s_j[m] * A_j[m, k].
 //
 // Per token m, in fp64 with r = x: s_j = fp32(max_k |r| / 127);
-// A_j = clamp(rint(r / s_j), -127, 127); r <- r - s_j * A_j (the product is
-// exact, so contraction cannot change the result).  All decisions are IEEE
-// fp64 operations, bit-identical to any other correct fp64 evaluation.
+// A_j = clamp(rint(r / s_j), -127, 127); r <- r - s_j * A_j (the product and
+// the difference are exact for up to three slices, so contraction cannot
+// change the result).  All decisions are IEEE fp64 operations, bit-identical
+// to any other correct fp64 evaluation.
 //
 // The slices are written in the byte order the int8 matrix-core product reads
 // them in (the operand layout below); the plain [slice][token][K] layout is
@@ -49,14 +50,20 @@ __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
 }
 
 // One workgroup per token row, passes over the (cache-resident) row: the
-// absmax, then slice 1 (with the residual's absmax), then slice 2, whose
-// residual is recomputed from x and slice 1 exactly as before.  Each thread
-// takes 8 consecutive elements per step (one 16-byte load) and stores them as
-// one 8-byte piece of the operand layout (and of the plain layout if asked).
-template <int NS>
+// absmax, then one pass per slice.  Pass j recomputes the residual from x and
+// the earlier slices exactly as before and gathers the next residual's absmax
+// (adaptive scales).  With FIXED (two slices), the second slice uses the first
+// slice's step divided by 254: A_2 = clamp(rint((254 r_1) / s_1)), and its
+// reported scale is fp32(s_1 / 254).  Each thread takes 8 consecutive
+// elements per step (one 16-byte load) and stores them as one 8-byte piece of
+// the operand layout (and of the plain layout if asked).
+constexpr double kFixedRatio = 254.0;
+
+template <int NS, bool FIXED>
 __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
     const uint16_t* __restrict__ x, int M, int K, int8_t* __restrict__ slices_op, int8_t* __restrict__ slices_out,
     float* __restrict__ tok_scale) {
+  static_assert(!FIXED || NS == 2, "the fixed ratio defines a second slice");
   __shared__ double red[kDecompThreads / kWave];
   constexpr int kStep = 8 * kDecompThreads;
   const int m = blockIdx.x;
@@ -88,50 +95,56 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
     for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(v[i]));
   }
   amax = block_max(amax, red);
-  const double s1 = (double)(float)(amax / 127.0);
+  double s[NS];
+  s[0] = (double)(float)(amax / 127.0);
 
-  double amax2 = 0.0;
-  for (int k = 8 * threadIdx.x; k < K; k += kStep) {
-    double v[8];
-    load8(k, v);
-    int a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double q = quant127(v[i], s1);
-      a[i] = (int)q;
-      amax2 = fmax(amax2, fabs(v[i] - s1 * q));
-    }
-    store8(0, k, a);
-  }
-  if (threadIdx.x == 0) tok_scale[m] = (float)s1;
-  if constexpr (NS == 2) {
-    amax2 = block_max(amax2, red);
-    const double s2 = (double)(float)(amax2 / 127.0);
+  for (int j = 0; j < NS; ++j) {
+    double amax_next = 0.0;
     for (int k = 8 * threadIdx.x; k < K; k += kStep) {
       double v[8];
       load8(k, v);
       int a[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const double r1 = v[i] - s1 * quant127(v[i], s1);
-        a[i] = (int)quant127(r1, s2);
+        double r = v[i];
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) r = r - s[jj] * quant127(r, s[jj]);  // earlier slices' residual
+        double q;
+        if (FIXED && j == 1)
+          q = s[0] != 0.0 ? fmin(fmax(rint((kFixedRatio * r) / s[0]), -127.0), 127.0) : 0.0;
+        else
+          q = quant127(r, s[j]);
+        a[i] = (int)q;
+        if (!FIXED && j + 1 < NS) amax_next = fmax(amax_next, fabs(r - s[j] * q));
       }
-      store8(1, k, a);
+      store8(j, k, a);
     }
-    if (threadIdx.x == 0) tok_scale[(size_t)M + m] = (float)s2;
+    if (FIXED && j == 1) {
+      if (threadIdx.x == 0) tok_scale[(size_t)M + m] = (float)(s[0] / kFixedRatio);
+    } else {
+      if (threadIdx.x == 0) tok_scale[(size_t)j * M + m] = (float)s[j];
+      if (!FIXED && j + 1 < NS) s[j + 1] = (double)(float)(block_max(amax_next, red) / 127.0);
+    }
   }
 }
 
 }  // namespace
 
-int launch_decompose(const uint16_t* x, int M, int K, int nslices, int8_t* slices_op, int8_t* slices_out,
+int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, int8_t* slices_op, int8_t* slices_out,
                      float* tok_scale, hipStream_t s) {
-  if (nslices == 1)
-    hipLaunchKernelGGL(decompose_kernel<1>, dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, slices_out,
-                       tok_scale);
+#define W4_DECOMP(NS, FX)                                                                                   \
+  hipLaunchKernelGGL((decompose_kernel<NS, FX>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, \
+                     slices_out, tok_scale)
+  if (fixed)
+    W4_DECOMP(2, true);
+  else if (nslices == 1)
+    W4_DECOMP(1, false);
+  else if (nslices == 2)
+    W4_DECOMP(2, false);
   else
-    hipLaunchKernelGGL(decompose_kernel<2>, dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, slices_out,
-                       tok_scale);
+    W4_DECOMP(3, false);
+#undef W4_DECOMP
   return check_launch("decompose");
 }
 

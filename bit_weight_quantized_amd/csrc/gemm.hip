@@ -380,12 +380,16 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
 // since 113 <= 128 + q - z <= 143), so each group's int32 product is
 // D_j = sum A_j * (q - z) and the epilogue is C += s * (D_1 + r * D_2) with
 // r = s_2 / s_1 per token; y = s_1 * C.
-// Token tiles per wave: 8 (128 tokens per workgroup) where the registers
-// allow, 4 for G = 64 with two slices and for the test variant that also
-// writes the integer products.
-constexpr int msd_mt(int gpt, int ns, bool dbg) { return (!dbg && (gpt == 1 || ns == 1)) ? 8 : 4; }
+// With three slices, C += s * (D_1 + r_2 D_2 + r_3 D_3).  With the fixed
+// ratio (two slices, s_2 = s_1 / 254) the products combine exactly in int32
+// as E = 254 D_1 + D_2 (|E| < 2^26), one conversion per group: C += s * E,
+// and the store multiplies by s_1 / 254.
+// Token tiles per wave: 8 (128 tokens per workgroup) where the registers and
+// the LDS allow, 4 for G = 64 with two slices, for three slices and for the
+// test variant that also writes the integer products.
+constexpr int msd_mt(int gpt, int ns, bool dbg) { return (!dbg && ns < 3 && (gpt == 1 || ns == 1)) ? 8 : 4; }
 
-template <int GPT, int NS, bool DBG>
+template <int GPT, int NS, bool DBG, bool FIXED>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_msd_kernel(
     const int8_t* __restrict__ slices, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
@@ -398,8 +402,10 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int kSlice = BM * 128;  // one slice's rows of a step
   constexpr int kA = NS * kSlice;
   constexpr int kStage = kA + kHB + kHS;
+  static_assert(!FIXED || NS == 2, "the fixed ratio defines a second slice");
+  constexpr int NR = (NS > 1 && !FIXED) ? NS - 1 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float ratio[BM];  // s_2 / s_1 per tile row
+  __shared__ float ratio[NR][BM];  // s_j / s_1 per tile row, j >= 2
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -422,15 +428,19 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   if (tid < BM) {
     const int m = min(m0 + tid, M - 1);
     const float s1 = tok_scale[m];
-    ratio[tid] = (NS == 2 && s1 != 0.f) ? tok_scale[(size_t)M + m] / s1 : 0.f;
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+      ratio[j][tid] = (NS > 1 && !FIXED && s1 != 0.f) ? tok_scale[(size_t)(j + 1) * M + m] / s1 : 0.f;
   }
 
   // ---- copies.  Wave w fills rows [w BM/8, (w + 1) BM/8) of every slice (8
   // rows of 128 bytes per instruction), weight tiles 2 w and 2 w + 1, and its
   // share of the scale copies (as in the fp16 kernel).
-  __amdgpu_buffer_rsrc_t ar[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) ar[j] = make_rsrc(slices + (size_t)j * M * K, (uint32_t)((size_t)M * K));
+  // slice j's descriptor, from a slice size kept in a scalar register (the
+  // compiler otherwise may share the product with vector code and then has
+  // to loop over lanes to form the descriptor)
+  const uint32_t slice_bytes = __builtin_amdgcn_readfirstlane((uint32_t)M * (uint32_t)K);
+  auto ar = [&](int j) { return make_rsrc(slices + (size_t)j * slice_bytes, slice_bytes); };
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
   uint32_t voff_a[kRowCopies];
 #pragma unroll
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int j = 0; j < NS; ++j)
 #pragma unroll
       for (int i = 0; i < kRowCopies; ++i)
-        copy16_to_lds(ar[j], voff_a[i], (uint32_t)kt * 128, st + j * kSlice + (wn * (BM / 8) + 8 * i) * 128);
+        copy16_to_lds(ar(j), voff_a[i], (uint32_t)kt * 128, st + j * kSlice + (wn * (BM / 8) + 8 * i) * 128);
 #pragma unroll
     for (int j = 0; j < 2; ++j) copy16_to_lds(wr, voff_b[j], (uint32_t)kt * 1024, st + kA + (2 * wn + j) * 1024);
 #pragma unroll
@@ -543,13 +553,21 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
           }
         }
         const int rloc = mt * 16 + 4 * kb;
-        const f32x4 rr = *reinterpret_cast<const f32x4*>(&ratio[rloc]);
+        f32x4 rr[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) rr[j] = *reinterpret_cast<const f32x4*>(&ratio[j][rloc]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float e = (float)D[0][nt][i];
-            if constexpr (NS == 2) e = fmaf(rr[i], (float)D[1][nt][i], e);
+            float e;
+            if constexpr (FIXED) {
+              e = (float)(__mul24(D[0][nt][i], 254) + D[1][nt][i]);
+            } else {
+              e = (float)D[0][nt][i];
+#pragma unroll
+              for (int j = 1; j < NS; ++j) e = fmaf(rr[j - 1][i], (float)D[j][nt][i], e);
+            }
             C[mt][nt][i] = fmaf(sv[nt], e, C[mt][nt][i]);
           }
           if constexpr (DBG) {  // exact integer per-group products, zero point folded
@@ -583,7 +601,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + mt * 16 + 4 * kb + i;
       if (m >= M) continue;
-      const float s1 = tok_scale[m];
+      const float s1 = tok_scale[FIXED ? (size_t)M + m : (size_t)m];  // s_1, or s_1 / 254
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + wn * 32 + nt * 16 + ln;
@@ -592,24 +610,24 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     }
 }
 
-template <int GPT, int NS>
+template <int GPT, int NS, bool FIXED>
 int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
                const uint16_t* zero, uint16_t* y, const float* tok_scale, int32_t* acc_out, hipStream_t s) {
   constexpr int kStage = NS * 16 * msd_mt(GPT, NS, false) * 128 + kHB + kHS;  // the larger of the two variants
   constexpr int kLds = kHStages * kStage;
   if ((size_t)NS * M * K >= (1ull << 32))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm_decomp: slices of %d x %d exceed the 4 GiB one call addresses", M, K);
-  const void* fn = acc_out ? reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, true>)
-                           : reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, false>);
+  const void* fn = acc_out ? reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, true, FIXED>)
+                           : reinterpret_cast<const void*>(&gemm_msd_kernel<GPT, NS, false, FIXED>);
   const int st = allow_dynamic_lds(fn, kLds, "w4_gemm_decomp");
   if (st != 0) return st;
   const int bm = 16 * msd_mt(GPT, NS, acc_out != nullptr);
   const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + bm - 1) / bm);
   if (acc_out)
-    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices, M,
+    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true, FIXED>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices, M,
                        K, N, packed, scale, zero, y, tok_scale, acc_out);
   else
-    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices,
+    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false, FIXED>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices,
                        M, K, N, packed, scale, zero, y, tok_scale, acc_out);
   return check_launch("gemm_msd");
 }
@@ -667,16 +685,18 @@ size_t decomp_workspace_bytes(int M, int K, int G, int nslices) {
 }
 
 int launch_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
-                       const uint16_t* zero, int G, int nslices, uint16_t* y, int8_t* slices_op, int8_t* slices_out,
-                       float* tok_scale, int32_t* acc_out, hipStream_t s) {
-  int st = launch_decompose(x, M, K, nslices, slices_op, slices_out, tok_scale, s);
+                       const uint16_t* zero, int G, int nslices, bool fixed, uint16_t* y, int8_t* slices_op,
+                       int8_t* slices_out, float* tok_scale, int32_t* acc_out, hipStream_t s) {
+  int st = launch_decompose(x, M, K, nslices, fixed, slices_op, slices_out, tok_scale, s);
   if (st != 0) return st;
-  if (nslices == 1) {
-    if (G == 64) return launch_msd<2, 1>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
-    return launch_msd<1, 1>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
-  }
-  if (G == 64) return launch_msd<2, 2>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
-  return launch_msd<1, 2>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s);
+#define W4_MSD(NS, FX)                                                                                        \
+  return G == 64 ? launch_msd<2, NS, FX>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s) \
+                 : launch_msd<1, NS, FX>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s)
+  if (fixed) W4_MSD(2, true);
+  if (nslices == 1) W4_MSD(1, false);
+  if (nslices == 2) W4_MSD(2, false);
+  W4_MSD(3, false);
+#undef W4_MSD
 }
 
 }  // namespace w4

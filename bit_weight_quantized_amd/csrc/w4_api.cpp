@@ -86,6 +86,37 @@ const uint32_t kNf4LevelBits[16] = {
     0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
     0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
 
+namespace {
+
+int gemm_decomp_checked(const char* fn, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                        const uint16_t* scale, const uint16_t* zero, int G, int nslices, bool fixed, uint16_t* y,
+                        int8_t* slices_out, float* tok_scale_out, int32_t* acc_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  g_last_error[0] = '\0';
+  int st;
+  if ((st = check_matmul_shape(fn, M, K, N, G)) != W4_OK) return st;
+  if (nslices < 1 || nslices > 3) return fail(W4_EINVAL, "%s: nslices must be 1, 2 or 3 (got %d)", fn, nslices);
+  if (packed && scale && !zero)
+    return fail(W4_EUNSUPPORTED, "%s: needs INT4 weights (zero != NULL); NF4 levels are not integers", fn);
+  if ((st = check_weights(fn, packed, scale, zero, W4_INT4_ASYM)) != W4_OK) return st;
+  if ((st = check_io(fn, x, y)) != W4_OK) return st;
+  if ((slices_out && !aligned16(slices_out)) || (tok_scale_out && !aligned16(tok_scale_out)) ||
+      (acc_out && !aligned16(acc_out)))
+    return fail(W4_EINVAL, "%s: optional outputs must be 16-byte aligned", fn);
+  const size_t need = decomp_workspace_bytes(M, K, G, nslices);
+  if (!ws || ws_bytes < need)
+    return fail(W4_EWORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need, ws_bytes);
+  if (!aligned16(ws)) return fail(W4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  char* base = static_cast<char*>(ws);
+  const size_t slice_bytes = ((size_t)nslices * M * K + 255) / 256 * 256;
+  int8_t* sl_op = reinterpret_cast<int8_t*>(base);
+  float* ts = tok_scale_out ? tok_scale_out : reinterpret_cast<float*>(base + slice_bytes);
+  return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, fixed, y, sl_op, slices_out, ts, acc_out,
+                            (hipStream_t)stream);
+}
+
+}  // namespace
+
 }  // namespace w4
 
 using namespace w4;
@@ -156,28 +187,16 @@ int w4_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed
                    const uint16_t* scale, const uint16_t* zero, int G, int nslices,
                    uint16_t* y, int8_t* slices_out, float* tok_scale_out, int32_t* acc_out,
                    void* ws, size_t ws_bytes, void* stream) {
-  g_last_error[0] = '\0';
-  int st;
-  if ((st = check_matmul_shape("w4_gemm_decomp", M, K, N, G)) != W4_OK) return st;
-  if (nslices != 1 && nslices != 2)
-    return fail(W4_EINVAL, "w4_gemm_decomp: nslices must be 1 or 2 (got %d)", nslices);
-  if (packed && scale && !zero)
-    return fail(W4_EUNSUPPORTED, "w4_gemm_decomp: needs INT4 weights (zero != NULL); NF4 levels are not integers");
-  if ((st = check_weights("w4_gemm_decomp", packed, scale, zero, W4_INT4_ASYM)) != W4_OK) return st;
-  if ((st = check_io("w4_gemm_decomp", x, y)) != W4_OK) return st;
-  if ((slices_out && !aligned16(slices_out)) || (tok_scale_out && !aligned16(tok_scale_out)) ||
-      (acc_out && !aligned16(acc_out)))
-    return fail(W4_EINVAL, "w4_gemm_decomp: optional outputs must be 16-byte aligned");
-  const size_t need = decomp_workspace_bytes(M, K, G, nslices);
-  if (!ws || ws_bytes < need)
-    return fail(W4_EWORKSPACE, "w4_gemm_decomp: workspace of %zu bytes required (got %zu)", need, ws_bytes);
-  if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemm_decomp: workspace must be 16-byte aligned");
-  char* base = static_cast<char*>(ws);
-  const size_t slice_bytes = ((size_t)nslices * M * K + 255) / 256 * 256;
-  int8_t* sl_op = reinterpret_cast<int8_t*>(base);
-  float* ts = tok_scale_out ? tok_scale_out : reinterpret_cast<float*>(base + slice_bytes);
-  return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, y, sl_op, slices_out, ts, acc_out,
-                            (hipStream_t)stream);
+  return gemm_decomp_checked("w4_gemm_decomp", x, M, K, N, packed, scale, zero, G, nslices, false, y, slices_out,
+                             tok_scale_out, acc_out, ws, ws_bytes, stream);
+}
+
+int w4_gemm_decomp_fixed(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                         const uint16_t* scale, const uint16_t* zero, int G, uint16_t* y,
+                         int8_t* slices_out, float* tok_scale_out, int32_t* acc_out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return gemm_decomp_checked("w4_gemm_decomp_fixed", x, M, K, N, packed, scale, zero, G, 2, true, y, slices_out,
+                             tok_scale_out, acc_out, ws, ws_bytes, stream);
 }
 
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
@@ -192,7 +211,7 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
       if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G || K % 128) return 0;
       return plan_gemv(M, K, N, G, fmt_or_mode == W4_NF4 ? W4_NF4 : W4_INT4_ASYM).ws_bytes;
     case W4_OP_GEMM_DECOMP:
-      if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
+      if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || fmt_or_mode < 1 || fmt_or_mode > 3) return 0;
       return decomp_workspace_bytes(M, K, G, fmt_or_mode);
     default:
       return (size_t)-1;

@@ -56,12 +56,13 @@ int launch_reduce_partials(const float* partial, int S, long MN, uint16_t* y, hi
 // [nslices][M].
 size_t decomp_workspace_bytes(int M, int K, int G, int nslices);
 // Decomposition: operand-layout slices, plus the plain layout when
-// slices_out is non-null.
-int launch_decompose(const uint16_t* x, int M, int K, int nslices, int8_t* slices_op, int8_t* slices_out,
-                     float* tok_scale, hipStream_t s);
+// slices_out is non-null.  nslices 1..3 with adaptive scales, or (fixed) two
+// slices with s_2 = s_1 / 254.
+int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, int8_t* slices_op,
+                     int8_t* slices_out, float* tok_scale, hipStream_t s);
 int launch_gemm_decomp(const uint16_t* x, int M, int K, int N,
                        const uint8_t* packed, const uint16_t* scale,
-                       const uint16_t* zero, int G, int nslices, uint16_t* y,
+                       const uint16_t* zero, int G, int nslices, bool fixed, uint16_t* y,
                        int8_t* slices_op, int8_t* slices_out, float* tok_scale,
                        int32_t* acc_out, hipStream_t s);
 

@@ -155,7 +155,7 @@ int w4_gemm(const uint16_t* x, int M, int K, int N,
 
 /*
  * w4_gemm_decomp -- Multi-Scale Dequant product ([MSD]): the fp16 activations
- * are split into `nslices` (1 or 2) int8 slices with per-token fp32 scales,
+ * are split into `nslices` (1, 2 or 3) int8 slices with per-token fp32 scales,
  * and each slice is multiplied directly with the 4-bit integer weights on the
  * int8 matrix cores, with no conversion of the weights to a floating type.
  *
@@ -182,6 +182,31 @@ int w4_gemm_decomp(const uint16_t* x, int M, int K, int N,
                    const uint16_t* zero, int G, int nslices, uint16_t* y,
                    int8_t* slices_out, float* tok_scale_out, int32_t* acc_out,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * w4_gemm_decomp_fixed -- two-slice Multi-Scale Dequant product ([MSD]) with
+ * a fixed ratio between the slice scales, so that the two int8 products
+ * combine exactly in integers before any conversion.
+ *
+ * The MSD abstract does not fix how the second scale is chosen; here it is
+ * the first slice's step divided by 254.  Per token m, in fp64:
+ * s_1 = fp32(max|x| / 127); A_1 = clamp(rint(x / s_1), -127, 127);
+ * r_1 = x - s_1 A_1; A_2 = clamp(rint((254 r_1) / s_1), -127, 127).  Since
+ * |r_1| <= s_1 / 2 the second slice never clamps in practice, and
+ * |x - s_1 A_1 - (s_1 / 254) A_2| <= s_1 / 508.  Products: D_j as in
+ * w4_gemm_decomp; E[m,g,n] = 254 D_1 + D_2 exactly in int32;
+ * y[m,n] = (s_1[m] / 254) * sum_g s[n,g] * E[m,g,n], accumulated in fp32.
+ *
+ * Arguments, shapes, errors and workspace as for w4_gemm_decomp with
+ * nslices = 2 (workspace: w4_workspace_bytes(W4_OP_GEMM_DECOMP, ..., 2));
+ * tok_scale_out [2][M] receives s_1 and fp32(s_1 / 254); acc_out
+ * [2][M][K/G][N] receives D_1 and D_2.
+ */
+int w4_gemm_decomp_fixed(const uint16_t* x, int M, int K, int N,
+                         const uint8_t* packed, const uint16_t* scale,
+                         const uint16_t* zero, int G, uint16_t* y,
+                         int8_t* slices_out, float* tok_scale_out, int32_t* acc_out,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /*
  * w4_workspace_bytes -- bytes of workspace an entry point needs for the given

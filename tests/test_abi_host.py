@@ -37,7 +37,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for want in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp",
-                 "w4_workspace_bytes", "w4_status_str", "w4_last_error"):
+                 "w4_gemm_decomp_fixed", "w4_workspace_bytes", "w4_status_str", "w4_last_error"):
         assert want in fns
 
 
@@ -98,12 +98,31 @@ def test_decomp_argument_errors(L):
         return L.w4_gemm_decomp(a["x"], a["M"], a["K"], a["N"], a["packed"], a["scale"], a["zero"],
                                 a["G"], a["ns"], FAKE, None, None, None, a.get("ws"),
                                 a.get("wsb", 0), None)
-    assert call(ns=3) == W4_EINVAL
+    assert call(ns=4) == W4_EINVAL
+    assert call(ns=0) == W4_EINVAL
+    assert call(ns=3) == W4_EWORKSPACE  # three slices are valid; still no workspace
     assert call(zero=None) == W4_EUNSUPPORTED  # NF4 weights cannot feed int8 matrix cores
     assert call() == W4_EWORKSPACE              # slices/scales need a workspace
     need = L.w4_workspace_bytes(4, 4, 256, 32, 128, 2)
     assert need >= 2 * 4 * 256 + 2 * 4 * 4
     assert call(ws=FAKE, wsb=need - 1) == W4_EWORKSPACE
+
+
+def test_decomp_fixed_argument_errors(L):
+    base = dict(x=FAKE, M=4, K=256, N=32, packed=FAKE, scale=FAKE, zero=FAKE, G=128)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return L.w4_gemm_decomp_fixed(a["x"], a["M"], a["K"], a["N"], a["packed"], a["scale"], a["zero"],
+                                      a["G"], FAKE, None, None, None, a.get("ws"), a.get("wsb", 0), None)
+    assert call(zero=None) == W4_EUNSUPPORTED
+    assert call(G=32) == W4_EINVAL
+    assert call(N=40) == W4_EINVAL
+    assert call() == W4_EWORKSPACE
+    need = L.w4_workspace_bytes(4, 4, 256, 32, 128, 2)
+    assert call(ws=FAKE, wsb=need - 1) == W4_EWORKSPACE
+    assert call(ws=MISALIGNED, wsb=need) == W4_EINVAL
+    assert b"w4_gemm_decomp_fixed" in L.w4_last_error()
 
 
 def test_quantize_and_pack_argument_errors(L):
@@ -118,4 +137,9 @@ def test_quantize_and_pack_argument_errors(L):
 
 def test_workspace_bytes(L):
     assert L.w4_workspace_bytes(2, 1, 8192, 8192, 128, 0) == 0
+    # decomposition: slices [nslices][M][K] then fp32 scales [nslices][M], each 256-byte aligned
+    for ns in (1, 2, 3):
+        want = -(-ns * 100 * 1024 // 256) * 256 + -(-ns * 100 * 4 // 256) * 256
+        assert L.w4_workspace_bytes(4, 100, 1024, 64, 128, ns) == want
+    assert L.w4_workspace_bytes(4, 100, 1024, 64, 128, 4) == 0
     assert L.w4_workspace_bytes(99, 1, 1, 1, 1, 0) == ctypes.c_size_t(-1).value

@@ -30,7 +30,7 @@ def run_decomp(x, codes, scale, zero, G, nslices, with_acc=True):
 
 
 @pytest.mark.parametrize("G", [128, 64])
-@pytest.mark.parametrize("nslices", [2, 1])
+@pytest.mark.parametrize("nslices", [2, 1, 3])
 @pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 640, 48), (130, 1024, 272), (257, 512, 144),
                                    (64, 2048, 256)])
 def test_decomp_small(G, nslices, M, K, N):
@@ -107,7 +107,7 @@ def test_decomp_rejects_nf4():
     assert e.value.status == -2
 
 
-@pytest.mark.parametrize("nslices", [2, 1])
+@pytest.mark.parametrize("nslices", [2, 1, 3])
 def test_decomp_prefill_m2048_k5120_n25600(nslices):
     """Full prefill shape: slices and scales bit-exact over the whole input;
     outputs compared on sampled columns."""
@@ -130,3 +130,103 @@ def test_decomp_prefill_m2048_k5120_n25600(nslices):
     assert np.array_equal(host(codes[rows]), rc)
     ref = o.msd_result(S, o.msd_accumulators(A, rc, rz, G), rs)
     assert row_rel_l2(y[:, rows], ref) <= TOL_ROW_REL_L2
+
+
+# ------------------------------------------------------------ fixed ratio
+def run_fixed(x, codes, scale, zero, G, with_acc=True, workspace=None):
+    M, K = x.shape
+    N = codes.shape[0]
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    sl = torch.empty((2, M, K), dtype=torch.int8, device="cuda")
+    ts = torch.empty((2, M), dtype=torch.float32, device="cuda")
+    acc = torch.empty((2, M, K // G, N), dtype=torch.int32, device="cuda") if with_acc else None
+    y, _, _, _ = w4.gemm_decomp_fixed(dev(x), packed, sc, zc, G, slices_out=sl, tok_scale_out=ts, acc_out=acc,
+                                      workspace=workspace)
+    return host(y), host(sl), host(ts), (host(acc) if with_acc else None)
+
+
+@pytest.mark.parametrize("G", [128, 64])
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (5, 640, 48), (130, 1024, 272), (257, 512, 144),
+                                   (64, 2048, 256)])
+def test_decomp_fixed_small(G, M, K, N):
+    if K % G:
+        pytest.skip("K not a multiple of G")
+    require_gpu()
+    w = wl.make_weight(310 + M, 0, N, K)
+    x = wl.make_activations(310 + M, 0, M, K, outliers=True)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    announce("decomp fixed", dict(G=G, M=M, K=K, N=N))
+    y, sl, ts, acc = run_fixed(x, codes, scale, zero, G)
+    A, S = o.decompose_fixed_ratio(x)
+    assert np.array_equal(sl, A)
+    assert np.array_equal(ts.view(np.uint32), S.view(np.uint32))
+    D = o.msd_accumulators(A, codes, zero, G)
+    assert np.array_equal(acc.astype(np.int64), D)
+    assert row_rel_l2(y, o.msd_fixed_result(S[0], D, scale)) <= TOL_ROW_REL_L2
+
+
+def test_decomp_fixed_degenerate_rows_and_repeat():
+    """Zero row (output exactly 0), integer row on the first grid (second
+    slice zero), one non-zero entry, a huge outlier; the workspace-only call
+    gives the same bits as the call with every optional output."""
+    require_gpu()
+    M, K, N, G = 6, 512, 64, 64
+    x = wl.make_activations(16, 0, M, K)
+    x[0] = 0
+    x[1] = np.float16(np.random.default_rng(16).integers(-127, 128, K))
+    x[1, 5] = 127
+    x[2] = 0
+    x[2, 77] = -3.5
+    x[3, 100] = 30000
+    codes, scale, zero = o.quantize_int4_asym(wl.make_weight(16, 0, N, K), G)
+    announce("decomp fixed degenerate")
+    y, sl, ts, acc = run_fixed(x, codes, scale, zero, G)
+    A, S = o.decompose_fixed_ratio(x)
+    assert S[0, 1] == 1.0 and np.all(A[1, 1] == 0) and S[0, 0] == 0.0
+    assert np.array_equal(sl, A)
+    assert np.array_equal(ts.view(np.uint32), S.view(np.uint32))
+    D = o.msd_accumulators(A, codes, zero, G)
+    assert np.array_equal(acc.astype(np.int64), D)
+    assert np.all(y[0] == 0)
+    assert row_rel_l2(y[1:], o.msd_fixed_result(S[0], D, scale)[1:]) <= TOL_ROW_REL_L2
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8, device="cuda")
+    a = host(w4.gemm_decomp_fixed(dev(x), packed, sc, zc, G, workspace=ws))
+    b = host(w4.gemm_decomp_fixed(dev(x), packed, sc, zc, G, workspace=ws))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.array_equal(a.view(np.uint16), y.view(np.uint16))
+
+
+def test_decomp_fixed_rejects_nf4():
+    require_gpu()
+    K, N, G = 256, 32, 64
+    codes, absmax = o.quantize_nf4(wl.make_weight(17, 0, N, K), G)
+    packed, sc, _ = upload_weights(codes, absmax, None)
+    with pytest.raises(w4.W4Error) as e:
+        w4.gemm_decomp_fixed(dev(wl.make_activations(17, 0, 2, K)), packed, sc, None, G)
+    assert e.value.status == -2
+
+
+def test_decomp_fixed_prefill_m2048_k5120_n25600():
+    """Full prefill shape: slices and scales bit-exact over the whole input;
+    outputs compared on sampled columns."""
+    M, K, N, G = 2048, 5120, 25600, 128
+    w = wl.make_weight(4, 0, N, K)
+    x = wl.make_activations(4, 0, M, K)
+    announce("decomp fixed full quantize")
+    codes, scale, zero = w4.quantize(dev(w), G, w4.INT4_ASYM)
+    packed = w4.pack(codes)
+    sl = torch.empty((2, M, K), dtype=torch.int8, device="cuda")
+    ts = torch.empty((2, M), dtype=torch.float32, device="cuda")
+    announce("decomp fixed prefill", dict(M=M, K=K, N=N))
+    y, _, _, _ = w4.gemm_decomp_fixed(dev(x), packed, scale, zero, G, slices_out=sl, tok_scale_out=ts)
+    y = host(y)
+    A, S = o.decompose_fixed_ratio(x)
+    assert np.array_equal(host(sl), A)
+    assert np.array_equal(host(ts).view(np.uint32), S.view(np.uint32))
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(42).choice(N, 64, replace=False)]))
+    rc, rs, rz = o.quantize_int4_asym(w[rows], G)
+    assert np.array_equal(host(codes[rows]), rc)
+    ref = o.msd_fixed_result(S[0], o.msd_accumulators(A, rc, rz, G), rs)
+    assert row_rel_l2(y[:, rows], ref) <= TOL_ROW_REL_L2
+
