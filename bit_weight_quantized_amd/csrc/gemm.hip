@@ -81,6 +81,20 @@ constexpr int kF16Threads = 512;  // 8 waves
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Workgroup barrier for the copy pipelines: this wave's LDS reads have
+// completed (lgkmcnt(0)) and no memory access moves across it, but its
+// global -> LDS copies stay in flight (no vmcnt wait; every wave waits for its
+// own copies of a step explicitly before the barrier that publishes them).
+// __syncthreads() would also drain the copies of the steps ahead.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
 // 16 bytes per lane from a raw buffer (offset = voff + soff) to lds_base +
 // 16 * lane (lds_base wave-uniform).  Lanes whose voff lies past the buffer
 // write zeros.
@@ -229,19 +243,15 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   __syncthreads();
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const unsigned char* cur = stage(kt);
-    const bool more2 = kt + 2 < kt1;
-    if (more2) issue_step(kt + 2);
-
+  // per-step state: raw weight words, per-column scales / zero points
+  u32x4 Bq[NT];
+  float sfv[GPT][NT];      // PS: per-column scale (x 2^24 for INT4)
+  uint32_t zzv[GPT][NT];   // INT4: zero-point pair
+  uint32_t spv[GPT][NT];   // DQ: (s, s) pair
+  auto load_step = [&](const unsigned char* cur) {
     const uint32_t* s_lds = reinterpret_cast<const uint32_t*>(cur + kHA + kHB);
-    u32x4 Bq[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kHA + (2 * wn + nt) * 1024 + lane * 16);
-
-    float sfv[GPT][NT];      // PS: per-column scale (x 2^24 for INT4)
-    uint32_t zzv[GPT][NT];   // INT4: zero-point pair
-    uint32_t spv[GPT][NT];   // DQ: (s, s) pair
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi)
 #pragma unroll
@@ -257,43 +267,70 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
           zzv[gi][nt] = PATH == 1 ? (z | (z << 16)) : ((0x6400u | z) | ((0x6400u | z) << 16));
         }
       }
-    auto unpack = [&](u32x4 (&Bu)[NT], int w) {
-      const int gi = w / WPG;
+  };
+  auto unpack = [&](u32x4 (&Bu)[NT], int w) {
+    const int gi = w / WPG;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t v = Bq[nt][w];
+      if constexpr (FMT == 0) {
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t q = (v >> (4 * j)) & 0x000F000Fu;  // (c_2j, c_2j+1) * 2^-24
+          d[j] = PATH == 1 ? pk_sub_f16(q, zzv[gi][nt]) : pk_mul_f16(pk_sub_f16(q | 0x64006400u, zzv[gi][nt]), spv[gi][nt]);
+        }
+        Bu[nt] = u32x4{d[0], d[1], d[2], d[3]};
+      } else {
+        // table index (c_2j | c_2j+1 << 4) for the K-ordered pairs: even positions
+        // sit in nibbles 0-3 and odd ones in 4-7, so fold bytes 2,3 onto 0,1
+        const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+        const uint32_t il = lo | (lo >> 12), ih = hi | (hi >> 12);  // bytes 0,1: pairs (0,1),(4,5) / (2,3),(6,7)
+        u32x4 L{lut[il & 0xFFu], lut[ih & 0xFFu], lut[(il >> 8) & 0xFFu], lut[(ih >> 8) & 0xFFu]};
+        if constexpr (PATH == 0)
+          L = u32x4{pk_mul_f16(L.x, spv[gi][nt]), pk_mul_f16(L.y, spv[gi][nt]), pk_mul_f16(L.z, spv[gi][nt]),
+                    pk_mul_f16(L.w, spv[gi][nt])};
+        Bu[nt] = L;
+      }
+    }
+  };
+  auto load_a = [&](const unsigned char* cur, u32x4 (&A)[MT], int w) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) A[mt] = *reinterpret_cast<const u32x4*>(cur + a_off[w] + mt * 4096);
+  };
+  f32x4 acc[MT][NT];  // PS: the group's partial products
+  // one word's 16 products (PS: into the group's partial products)
+  auto products = [&](const u32x4 (&A)[MT], const u32x4 (&Bc)[NT], int w) {
+    const bool first = (w % WPG) == 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const uint32_t v = Bq[nt][w];
-        if constexpr (FMT == 0) {
-          uint32_t d[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t q = (v >> (4 * j)) & 0x000F000Fu;  // (c_2j, c_2j+1) * 2^-24
-            d[j] = PATH == 1 ? pk_sub_f16(q, zzv[gi][nt]) : pk_mul_f16(pk_sub_f16(q | 0x64006400u, zzv[gi][nt]), spv[gi][nt]);
-          }
-          Bu[nt] = u32x4{d[0], d[1], d[2], d[3]};
-        } else {
-          // table index (c_2j | c_2j+1 << 4) for the K-ordered pairs: even positions
-          // sit in nibbles 0-3 and odd ones in 4-7, so fold bytes 2,3 onto 0,1
-          const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
-          const uint32_t il = lo | (lo >> 12), ih = hi | (hi >> 12);  // bytes 0,1: pairs (0,1),(4,5) / (2,3),(6,7)
-          u32x4 L{lut[il & 0xFFu], lut[ih & 0xFFu], lut[(il >> 8) & 0xFFu], lut[(ih >> 8) & 0xFFu]};
-          if constexpr (PATH == 0)
-            L = u32x4{pk_mul_f16(L.x, spv[gi][nt]), pk_mul_f16(L.y, spv[gi][nt]), pk_mul_f16(L.z, spv[gi][nt]),
-                      pk_mul_f16(L.w, spv[gi][nt])};
-          Bu[nt] = L;
-        }
+        if constexpr (PATH == 1) acc[mt][nt] = mfma_f16(A[mt], Bc[nt], first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][nt]);
+        else C[mt][nt] = mfma_f16(A[mt], Bc[nt], C[mt][nt]);
       }
-    };
-    auto load_a = [&](u32x4 (&A)[MT], int w) {
+  };
+  // PS: a group is complete; scale its partial products once
+  auto scale_group = [&](int gi) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) A[mt] = *reinterpret_cast<const u32x4*>(cur + a_off[w] + mt * 4096);
-    };
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) C[mt][nt][i] = fmaf(sfv[gi][nt], acc[mt][nt][i], C[mt][nt][i]);
+  };
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const unsigned char* cur = stage(kt);
+    const bool more2 = kt + 2 < kt1;
+    if (more2) issue_step(kt + 2);
+    load_step(cur);
 
     // Word by word, the next word's operands are read and unpacked while this
     // word's 16 products run.
-    f32x4 acc[MT][NT];  // PS: the group's partial products
     u32x4 B0[NT], B1[NT];
     u32x4 A0[MT], A1[MT];
-    load_a(A0, 0);
+    load_a(cur, A0, 0);
     unpack(B0, 0);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -302,27 +339,12 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
       u32x4(&A)[MT] = (w % 2 == 0) ? A0 : A1;
       u32x4(&An)[MT] = (w % 2 == 0) ? A1 : A0;
       if (w + 1 < 4) {
-        load_a(An, w + 1);
+        load_a(cur, An, w + 1);
         unpack(Bn, w + 1);
       }
-      const bool first = (w % WPG) == 0;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if constexpr (PATH == 1) acc[mt][nt] = mfma_f16(A[mt], Bc[nt], first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][nt]);
-          else C[mt][nt] = mfma_f16(A[mt], Bc[nt], C[mt][nt]);
-        }
+      products(A, Bc, w);
       if constexpr (PATH == 1) {
-        if ((w % WPG) == WPG - 1) {  // group complete: scale once
-          const int gi = w / WPG;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) C[mt][nt][i] = fmaf(sfv[gi][nt], acc[mt][nt][i], C[mt][nt][i]);
-        }
+        if ((w % WPG) == WPG - 1) scale_group(w / WPG);
       }
     }
 
@@ -330,7 +352,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
       wait_all_but_one_step();  // step kt+1's copies have landed
     else
       __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // everyone's have, and nobody still reads this step's buffer
+    lds_barrier();  // everyone's have, and nobody still reads this step's buffer
   }
 
 #pragma unroll
@@ -360,12 +382,13 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
   const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>), kLds, "w4_gemm");
   if (st != 0) return st;
   const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
-  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles, (unsigned)S), dim3(kF16Threads), kLds,
-                     s, x, M, K, N, packed, scale, zero, y, partial);
+  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles, (unsigned)S), dim3(kF16Threads),
+                     kLds, s, x, M, K, N, packed, scale, zero, y, partial);
   const int st2 = check_launch("gemm");
   if (st2 != 0 || S == 1) return st2;
   return launch_reduce_partials(partial, S, (long)M * N, y, s);
 }
+
 
 // ---------------------------------------------------------------------------
 // Multi-Scale Dequant path, on the fp16 kernel's frame: 128 tokens x 256
@@ -592,7 +615,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
       wait_all_but_one_step();  // step kt+1's copies have landed
     else
       __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // everyone's have, and nobody still reads this step's buffer
+    lds_barrier();  // everyone's have, and nobody still reads this step's buffer
   }
 
 #pragma unroll
