@@ -19,7 +19,8 @@ Pages cited (title, section):
 * [NF4]    "Fast NF4 Dequantization Kernels for Large Language Model
            Inference", Abstract.
 * [DecDEC] "DecDEC: A Systems Approach to Advancing Low-Bit LLM
-           Quantization", "Builds on" list (names QLoRA, the source of the
+           Quantization", Abstract (residual compensation of salient
+           channels) and "Builds on" list (names QLoRA, the source of the
            NormalFloat construction used for the NF4 codebook).
 
 Where the pages leave a step open, the reading taken is stated in the
@@ -442,6 +443,44 @@ def msd_matmul(x, codes, scale, zero, G: int, nslices: int = 2):
     A, S = decompose_activations(x, nslices)
     D = msd_accumulators(A, codes, zero, G)
     return msd_result(S, D, scale), A, S, D
+
+
+# --------------------------------------------------------------------------
+# residual compensation of salient channels  ([DecDEC] Abstract)
+# --------------------------------------------------------------------------
+def residual_fp16(wt, w_deq) -> np.ndarray:
+    """The residual matrix R = W - W' that [DecDEC] keeps in host memory, as
+    fp16 [K][N] (row k: input channel k's residuals for every output n).
+
+    READING: the pages do not fix the residual's precision or layout; here it
+    is the exact fp64 difference rounded once to fp16, stored channel-major so
+    that fetching one salient channel reads one contiguous row.
+    """
+    wt64 = np.asarray(wt, dtype=np.float32).astype(np.float64)  # [N][K]
+    return (wt64 - np.asarray(w_deq, dtype=np.float64)).T.astype(np.float16)
+
+
+def salient_channels(x, k: int) -> np.ndarray:
+    """The k salient input channels of activations x [M][K], as int32 indices.
+
+    READING of [DecDEC] (salient channels are the ones where the current
+    step's activations have outliers, chosen anew at every decode step):
+    channel c scores max_m |x[m, c]|; the k highest scores are taken, ordered
+    by score (descending) and, among equal scores, by channel index
+    (ascending).
+    """
+    a = np.abs(np.asarray(x).astype(np.float64))
+    score = a.max(axis=0) if a.shape[0] else np.zeros(a.shape[1])
+    order = np.lexsort((np.arange(score.size), -score))  # primary key: -score
+    return order[:k].astype(np.int32)
+
+
+def residual_correction(x, resid16, idx) -> np.ndarray:
+    """corr[m, n] = sum over selected channels c of x[m, c] * R[c, n], fp64."""
+    xd = np.asarray(x).astype(np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    R = np.asarray(resid16, dtype=np.float16).astype(np.float64)
+    return xd[:, idx] @ R[idx, :]
 
 
 # --------------------------------------------------------------------------

@@ -543,6 +543,92 @@ def test_planted_fixed_combine_rejected():
     assert o.max_row_rel_l2(o.msd_fixed_result(S[0], np.stack([D[0], 2 * D[1]]), scale), y) > 5e-3
 
 
+# ------------------------------------------------------- residual compensation
+def test_salient_channels_hand_example():
+    x = np.array([[0.5, -3.0, 2.0, 3.0, 0.0, 1.0],
+                  [0.25, 1.0, -2.5, 0.0, 0.0, -1.0]], np.float16)
+    # scores max_m |x|: 0.5, 3, 2.5, 3, 0, 1 -> 1 and 3 tie (lower index first), then 2, 5, 0, 4
+    assert o.salient_channels(x, 4).tolist() == [1, 3, 2, 5]
+    assert o.salient_channels(x, 6).tolist() == [1, 3, 2, 5, 0, 4]
+    assert o.salient_channels(x, 0).size == 0
+
+
+def test_salient_channels_brute_force():
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        M, K = int(rng.integers(1, 5)), int(rng.integers(1, 40))
+        x = rng.integers(-4, 5, size=(M, K)).astype(np.float16)  # many ties
+        k = int(rng.integers(0, K + 1))
+        idx = o.salient_channels(x, k).tolist()
+        score = [max(abs(float(x[m, c])) for m in range(M)) for c in range(K)]
+        # selection sort by (score desc, index asc), written out
+        rest, want = list(range(K)), []
+        for _ in range(k):
+            best = rest[0]
+            for c in rest[1:]:
+                if score[c] > score[best] or (score[c] == score[best] and c < best):
+                    best = c
+            want.append(best)
+            rest.remove(best)
+        assert idx == want
+
+
+def test_residual_restores_weights_within_fp16_rounding():
+    G = 64
+    w = wl.make_weight(91, 0, 4, 256)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    wd = o.dequant_int4_asym(codes, scale, zero, G)
+    R = o.residual_fp16(w, wd)
+    assert R.shape == (256, 4) and R.dtype == np.float16
+    for n in range(4):
+        for k in range(0, 256, 7):
+            exact = Fraction(float(w[n, k])) - Fraction(float(wd[n, k]))
+            r = Fraction(float(R[k, n]))
+            # fp16 rounding of the exact residual: within half an fp16 step
+            step = Fraction(2) ** (int(np.floor(np.log2(abs(float(exact))))) - 10) if exact else Fraction(0)
+            assert abs(r - exact) <= max(step / 2, Fraction(2) ** -25)
+
+
+def test_full_correction_equals_product_with_restored_weights():
+    G = 64
+    x, codes, scale, zero = _tiny_case(o.FMT_INT4_ASYM, 92, M=3, N=5, K=256, G=G)
+    w = wl.make_weight(92, 0, 5, 256)
+    wd = o.dequant_int4_asym(codes, scale, zero, G)
+    R = o.residual_fp16(w, wd)
+    idx = o.salient_channels(x, 256)
+    y = o.matmul_ref(x, wd) + o.residual_correction(x, R, idx)
+    # the same thing as one product with W' + R (a different evaluation order)
+    w_restored = wd + R.T.astype(np.float64)
+    y2 = x.astype(np.float64) @ w_restored.T
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-14)
+    # and it is closer to the unquantized product than W' alone
+    y_full = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.abs(y - y_full).max() < 1e-3 * np.abs(o.matmul_ref(x, wd) - y_full).max()
+    # planted mistakes: residual with the wrong sign, or the transposed residual
+    assert not np.allclose(o.matmul_ref(x, wd) - o.residual_correction(x, R, idx), y2, rtol=1e-6)
+    assert not np.allclose(x.astype(np.float64)[:, idx] @ R.astype(np.float64)[::-1][idx, :] + o.matmul_ref(x, wd),
+                           y2, rtol=1e-6)
+
+
+def test_correction_of_outlier_channels_reduces_error():
+    G = 128
+    M, K, N = 2, 1024, 64
+    w = wl.make_weight(93, 0, N, K)
+    x = wl.make_activations(93, 0, M, K, outliers=True)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    wd = o.dequant_int4_asym(codes, scale, zero, G)
+    R = o.residual_fp16(w, wd)
+    y_full = x.astype(np.float64) @ w.astype(np.float64).T
+    y_q = o.matmul_ref(x, wd)
+    n_out = int(np.ceil(0.01 * K))
+    idx = o.salient_channels(x, n_out)
+    # the selected channels are exactly the workload's x20 outlier channels
+    assert sorted(idx.tolist()) == wl.outlier_channels(93, 0, K).tolist()
+    err_q = np.linalg.norm(y_q - y_full)
+    err_c = np.linalg.norm(y_q + o.residual_correction(x, R, idx) - y_full)
+    assert err_c < 0.9 * err_q
+
+
 def test_max_row_rel_l2_hand_example():
     y_ref = np.array([[3.0, 4.0], [1.0, 0.0]])
     y = np.array([[3.0, 4.5], [1.0, 0.01]])
