@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
     "lib", "lib_path", "quantize", "pack", "gemv", "gemm", "gemm_decomp", "gemm_decomp_fixed",
+    "salient_select", "residual_correct",
     "workspace_bytes", "nf4_levels", "version",
 ]
 
@@ -63,6 +64,8 @@ def lib():
         L.w4_gemm.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
         L.w4_gemm_decomp.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_gemm_decomp_fixed.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]
+        L.w4_salient_select.argtypes = [_p, _i, _i, _i, _p, _p]
+        L.w4_residual_correct.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p]
         L.w4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
         L.w4_workspace_bytes.restype = _sz
         L.w4_nf4_levels.argtypes = [_p]
@@ -72,7 +75,7 @@ def lib():
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
         for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
-                   "w4_nf4_levels"):
+                   "w4_salient_select", "w4_residual_correct", "w4_nf4_levels"):
             getattr(L, fn).restype = _i
         _lib = L
     return _lib
@@ -216,3 +219,30 @@ def gemm_decomp_fixed(x, packed, scale, zero, G: int, *, out=None, slices_out=No
     if slices_out is None and tok_scale_out is None and acc_out is None:
         return out
     return out, slices_out, tok_scale_out, acc_out
+
+
+def salient_select(x, k: int, *, out=None, stream=None):
+    """The k salient channels of x [M][K] (int32 indices on x's device)."""
+    _dev(x, torch.float16, "x")
+    M, K = x.shape
+    out = torch.empty((k,), dtype=torch.int32, device=x.device) if out is None else out
+    _check("w4_salient_select", lib().w4_salient_select(_ptr(x), M, K, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def residual_correct(x, resid, idx, y, *, stream=None):
+    """y += x[:, idx] . resid[idx, :] in place; resid fp16 [K][N], pinned host
+    memory (``pin_memory=True``) or a device tensor."""
+    _dev(x, torch.float16, "x")
+    _dev(y, torch.float16, "y")
+    if resid.dtype != torch.float16 or resid.dim() != 2 or not resid.is_contiguous():
+        raise ValueError("resid must be a contiguous fp16 [K][N] tensor")
+    if resid.device.type == "cpu" and not resid.is_pinned():
+        raise ValueError("a host-resident resid must be pinned (pin_memory=True)")
+    M, K = x.shape
+    N = y.shape[1]
+    k = idx.numel()
+    _check("w4_residual_correct", lib().w4_residual_correct(_ptr(x), M, K, N, _ptr(resid), _ptr(idx), k, _ptr(y),
+                                                            _stream(stream)))
+    return y
+

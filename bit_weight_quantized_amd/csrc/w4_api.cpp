@@ -199,6 +199,50 @@ int w4_gemm_decomp_fixed(const uint16_t* x, int M, int K, int N, const uint8_t* 
                              tok_scale_out, acc_out, ws, ws_bytes, stream);
 }
 
+int w4_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, void* stream) {
+  g_last_error[0] = '\0';
+  if (M < 1 || K < 1 || K > kSelMaxK)
+    return fail(W4_EINVAL, "w4_salient_select: need M >= 1 and 1 <= K <= %d (got M=%d K=%d)", kSelMaxK, M, K);
+  if (k < 0 || k > K || k > kSelMaxTop)
+    return fail(W4_EINVAL, "w4_salient_select: k must be in [0, min(K, %d)] (got %d)", kSelMaxTop, k);
+  if (!x || (k > 0 && !idx)) return fail(W4_EINVAL, "w4_salient_select: x and idx must be non-null");
+  if ((reinterpret_cast<uintptr_t>(x) & 1u) || (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return fail(W4_EINVAL, "w4_salient_select: x must be 2-byte and idx 4-byte aligned");
+  if (k == 0) return W4_OK;
+  return launch_salient_select(x, M, K, k, idx, (hipStream_t)stream);
+}
+
+int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx, int k,
+                        uint16_t* y, void* stream) {
+  g_last_error[0] = '\0';
+  if (M < 1 || M > 32 || K < 1 || N < 1 || N % 8)
+    return fail(W4_EINVAL, "w4_residual_correct: need 1 <= M <= 32, K >= 1, N >= 1 with N %% 8 == 0 (got M=%d K=%d N=%d)",
+                M, K, N);
+  if (k < 0) return fail(W4_EINVAL, "w4_residual_correct: k must be >= 0 (got %d)", k);
+  if (!x || !y || !resid || (k > 0 && !idx)) return fail(W4_EINVAL, "w4_residual_correct: null operand");
+  if (!aligned16(resid) || !aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
+      (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return fail(W4_EINVAL, "w4_residual_correct: resid and y must be 16-byte aligned, x 2-byte, idx 4-byte");
+  // The residual lives in pinned host memory (the device reads it over the
+  // host link) or, for comparison, in device memory.
+  hipPointerAttribute_t attr;
+  const void* dev = nullptr;
+  if (hipPointerGetAttributes(&attr, resid) == hipSuccess) {
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+      dev = resid;
+    } else if (attr.type == hipMemoryTypeHost) {
+      void* d = nullptr;
+      if (hipHostGetDevicePointer(&d, const_cast<uint16_t*>(resid), 0) == hipSuccess) dev = d;
+    }
+  }
+  if (!dev) {
+    (void)hipGetLastError();  // clear the query's error
+    return fail(W4_EINVAL, "w4_residual_correct: resid must be pinned host memory (hipHostMalloc) or device memory");
+  }
+  if (k == 0) return W4_OK;
+  return launch_residual_correct(x, M, K, N, static_cast<const uint16_t*>(dev), idx, k, y, (hipStream_t)stream);
+}
+
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
   switch (op) {
     case W4_OP_QUANTIZE:

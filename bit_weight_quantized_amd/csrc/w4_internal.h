@@ -66,6 +66,15 @@ int launch_gemm_decomp(const uint16_t* x, int M, int K, int N,
                        int8_t* slices_op, int8_t* slices_out, float* tok_scale,
                        int32_t* acc_out, hipStream_t s);
 
+// Residual compensation: the k salient channels of x (k <= kSelMaxTop,
+// K <= kSelMaxK), and y += x[:, idx] . R[idx, :] with R fp16 [K][N] in memory
+// the device can read (M <= 32).
+constexpr int kSelMaxK = 32768;
+constexpr int kSelMaxTop = 1024;
+int launch_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, hipStream_t s);
+int launch_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
+                            int k, uint16_t* y, hipStream_t s);
+
 // The 16 NF4 levels as fp32 bit patterns (host copy).
 extern const uint32_t kNf4LevelBits[16];
 

@@ -209,6 +209,39 @@ int w4_gemm_decomp_fixed(const uint16_t* x, int M, int K, int N,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * w4_salient_select -- the k salient input channels of a decode step, for
+ * residual compensation ([DecDEC] Abstract: salient channels are those where
+ * the current activations have outliers, chosen anew at every step).
+ *
+ * x: fp16 [M][K] device, 2-byte aligned.  Channel c scores max_m |x[m,c]|
+ * (NaN inputs give an unspecified choice).  idx: int32 [k] device, receives
+ * the k highest-scoring channels ordered by score (descending) and, among
+ * equal scores, by channel (ascending) -- a unique order.  Requires
+ * 1 <= K <= 32768 and 0 <= k <= min(K, 1024); k = 0 enqueues nothing.
+ */
+int w4_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, void* stream);
+
+/*
+ * w4_residual_correct -- adds the residual of the picked channels to a
+ * quantized product ([DecDEC] Abstract: the residual matrix, full-precision
+ * minus quantized weights, is kept in host memory and fetched only for the
+ * salient channels):  y[m,n] = fp16(y[m,n] + sum_j x[m,idx[j]] * R[idx[j],n]),
+ * the sum in fp32.
+ *
+ * x: fp16 [M][K] device (the step's activations), 1 <= M <= 32.
+ * resid: fp16 [K][N] (row c = channel c's residuals for every output),
+ *   16-byte aligned, in pinned host memory (hipHostMalloc; read by the device
+ *   over the host link, nothing is copied ahead) or in device memory;
+ *   pageable host memory returns W4_EINVAL.  Caller-owned.
+ * idx: int32 [k] device (e.g. from w4_salient_select); entries outside
+ *   [0, K) are skipped.  y: fp16 [M][N] device, updated in place, 16-byte
+ *   aligned.  Requires N % 8 == 0.  k = 0 enqueues nothing.
+ */
+int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid,
+                        const int32_t* idx, int k, uint16_t* y, void* stream);
+
+/*
+ * w4_workspace_bytes/*
  * w4_workspace_bytes -- bytes of workspace an entry point needs for the given
  * shape.  `fmt_or_mode`: the w4_fmt for W4_OP_GEMV, the w4_mode for
  * W4_OP_GEMM, nslices for W4_OP_GEMM_DECOMP.  Host-only; returns 0 for ops

@@ -125,6 +125,29 @@ def test_decomp_fixed_argument_errors(L):
     assert b"w4_gemm_decomp_fixed" in L.w4_last_error()
 
 
+def test_residual_argument_errors(L):
+    # selection: K beyond the LDS-resident key array, k beyond K or 1024, nulls
+    assert L.w4_salient_select(FAKE, 1, 32769, 4, FAKE, None) == W4_EINVAL
+    assert L.w4_salient_select(FAKE, 1, 100, 101, FAKE, None) == W4_EINVAL
+    assert L.w4_salient_select(FAKE, 1, 4096, 1025, FAKE, None) == W4_EINVAL
+    assert L.w4_salient_select(FAKE, 0, 100, 4, FAKE, None) == W4_EINVAL
+    assert L.w4_salient_select(None, 1, 100, 4, FAKE, None) == W4_EINVAL
+    assert L.w4_salient_select(FAKE, 1, 100, 0, None, None) == W4_OK  # k = 0: nothing to do
+    # correction: M in 1..32, N % 8, operands, alignment
+    args = dict(x=FAKE, M=1, K=64, N=64, r=FAKE, idx=FAKE, k=4, y=FAKE)
+
+    def corr(**kw):
+        a = {**args, **kw}
+        return L.w4_residual_correct(a["x"], a["M"], a["K"], a["N"], a["r"], a["idx"], a["k"], a["y"], None)
+    assert corr(M=33) == W4_EINVAL
+    assert corr(N=12) == W4_EINVAL
+    assert corr(k=-1) == W4_EINVAL
+    assert corr(r=None) == W4_EINVAL
+    assert corr(idx=None) == W4_EINVAL
+    assert corr(r=MISALIGNED) == W4_EINVAL
+    assert b"w4_residual_correct" in L.w4_last_error()
+
+
 def test_quantize_and_pack_argument_errors(L):
     assert L.w4_quantize(FAKE, 100, 16, 64, 0, FAKE, FAKE, FAKE, None) == W4_EINVAL
     assert L.w4_quantize(FAKE, 128, 16, 64, 1, FAKE, FAKE, FAKE, None) == W4_EINVAL  # NF4 + zero
