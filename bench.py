@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="no GPU: print a markdown summary of rocprofv3 CSV output (kernel_stats or "
                          "counter_collection files)")
+    ap.add_argument("--no-residual", dest="residual", action="store_false",
+                    help="skip the residual-compensation timing")
     ap.add_argument("--gemm-reps", type=int, default=20,
                     help="timed launches per prefill GEMM path (0 skips the GEMM section)")
     return ap.parse_args()
@@ -168,6 +170,55 @@ def bench_gemm_prefill(w4, torch, reps):
                     "activation decomposition; msd2_fixed uses s2 = s1/254 and combines the two int32 "
                     "products in integers",
             "paths": res}
+
+
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, reps=64):
+    """Residual compensation on the decode layer (K = N = 8192, M = 1, INT4
+    g128): salient-channel selection and the correction that reads the picked
+    residual rows from pinned host memory (device memory for comparison), each
+    timed as HIP-graph replays on the launch stream, and the whole step (GEMV,
+    selection, correction) against the GEMV alone.  The residual is seeded
+    noise of the residual's size and place: the kernels' time does not depend
+    on its values (their parity is tested elsewhere)."""
+    import workloads as wl
+    x = torch.from_numpy(wl.make_activations(2, 0, 1, K)).cuda()
+    y = torch.zeros((1, N), dtype=torch.float16, device="cuda")
+    gen = torch.Generator().manual_seed(50000)
+    r_host = torch.empty((K, N), dtype=torch.float16, pin_memory=True)
+    r_host.copy_((torch.randn((K, N), generator=gen) * 1e-3).half())
+    r_dev = r_host.cuda()
+    res = []
+    for k in ks:
+        idx = torch.empty((k,), dtype=torch.int32, device="cuda")
+        timed = {}
+        for name, call, count in (
+                ("select_us", lambda: w4.salient_select(x, k, out=idx), reps),
+                ("correct_host_us", lambda: w4.residual_correct(x, r_host, idx, y), reps),
+                ("correct_device_us", lambda: w4.residual_correct(x, r_dev, idx, y), reps)):
+            g = graph_of(torch, stream, [call] * count)
+            time_replays(torch, stream, g, 1)
+            timed[name] = round(time_replays(torch, stream, g, 4) * 1e3 / (4 * count), 2)
+            del g
+
+        def chain(i):
+            gemv_launch(i)
+            w4.salient_select(x, k, out=idx)
+            w4.residual_correct(x, r_host, idx, y)
+        g = graph_of(torch, stream, [lambda i=i: chain(i) for i in range(n_sets)])
+        time_replays(torch, stream, g, 1)
+        step_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
+        del g
+        link = k * N * 2 / (timed["correct_host_us"] * 1e-6) / 1e9
+        res.append({"k": k, **timed, "gemv_us": round(gemv_us, 2), "step_us": round(step_us, 2),
+                    "overhead_frac": round((step_us - gemv_us) / gemv_us, 3),
+                    "residual_bytes": k * N * 2, "host_link_GBps": round(link, 2),
+                    "host_link_frac": round(link / HOST_LINK_PEAK_GBS, 3)})
+    return {"workload": "decode_gemv_k8192_n8192_m1_int4_g128 + residual of k salient channels",
+            "residual": "fp16 [K][N] in pinned host memory, read by the kernel over the host link",
+            "host_link_peak_GBps": HOST_LINK_PEAK_GBS, "per_k": res}
 
 
 GEMV_SOURCE = os.path.join(ROOT, "bit_weight_quantized_amd", "csrc", "gemv.hip")
@@ -400,6 +451,14 @@ def main():
         traffic = round(sum(traffic_rows[p["variant"]] for p in per) / len(per))
 
     gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
+    resid = None
+    if args.residual:
+        m1 = next(p for p in per if p["variant"] == variant_name(w4.INT4_ASYM, 1))
+        try:
+            resid = bench_residual(w4, torch, stream, lambda i: launch(w4.INT4_ASYM, 1, 128, i), n_sets,
+                                   m1["us_per_launch"], K, N, ks=(16, 82, 256))
+        except Exception as e:  # reported, never fatal to the headline line
+            resid = {"error": f"{type(e).__name__}: {e}"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -432,6 +491,7 @@ def main():
                      "launch_average_us": round(sum_us / len(per), 3)},
         "per_launch": per,
         "gemm_prefill": gemm,
+        "residual_compensation": resid,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -54,13 +54,29 @@ __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint1
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      // the digit whose bucket holds the remaining-th largest candidate
-      uint32_t rem = s_remaining;
-      int d = 255;
-      while (d > 0 && hist[d] < rem) rem -= hist[d--];
-      s_remaining = rem;
-      s_prefix = prefix | ((uint32_t)d << shift);
+    if (tid < kWave) {
+      // the digit whose bucket holds the remaining-th largest candidate: lane
+      // l owns buckets 4l .. 4l + 3; a suffix scan over the lanes gives the
+      // count above each lane's buckets, and exactly one lane's range holds
+      // the rank (counts over all buckets cover it)
+      const uint32_t rem = s_remaining;
+      uint32_t h[4], own = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) own += (h[b] = hist[4 * tid + b]);
+      uint32_t incl = own;  // sum over lanes >= tid
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t t = __shfl_down(incl, off);
+        if (tid + off < kWave) incl += t;
+      }
+      const uint32_t above = incl - own;
+      if (above < rem && rem <= incl) {
+        uint32_t r = rem - above;
+        int b = 3;
+        while (b > 0 && h[b] < r) r -= h[b--];
+        s_remaining = r;
+        s_prefix = prefix | ((uint32_t)(4 * tid + b) << shift);
+      }
     }
     mask |= 255u << shift;
     __syncthreads();
