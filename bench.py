@@ -226,10 +226,17 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_decode_k8192_n8192_hbm_tr
 COPY_BYTES = 256 * 2 ** 20  # the plain copy the --pmc counters are calibrated on
 
 
-def source_sha256(path):
+def source_sha256(path=None, text=None):
+    """SHA-256 of a C++ source's code: comments removed and whitespace runs
+    collapsed, so that a comment edit does not count as a kernel change."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    if text is None:
+        with open(path) as f:
+            text = f.read()
+    code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", text, flags=re.S)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def read_traffic_profile():
@@ -241,7 +248,7 @@ def read_traffic_profile():
     sha, rows = None, {}
     with open(TRAFFIC_PROFILE) as f:
         for line in f:
-            if line.startswith("kernel source sha256:"):
+            if line.startswith("kernel code sha256:"):
                 sha = line.split(":", 1)[1].strip()
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
             if len(cells) >= 3 and cells[0].startswith(("int4", "nf4")):
@@ -340,7 +347,7 @@ def traffic_summary(fetch_csv, write_csv):
     assert n > 0 and len(fg) == n * len(names) == len(wg), (len(fg), len(wg))
     fscale = COPY_BYTES / (sum(fc) / len(fc) * 1024)
     wscale = COPY_BYTES / (sum(wc) / len(wc) * 1024)
-    print(f"kernel source sha256: {source_sha256(GEMV_SOURCE)}")
+    print(f"kernel code sha256: {source_sha256(GEMV_SOURCE)}")
     print(f"copy reference: {len(fc)} copies of {COPY_BYTES} bytes; FETCH_SIZE reads "
           f"{sum(fc) / len(fc):.1f} KiB per copy (scale {fscale:.4f}), WRITE_SIZE {sum(wc) / len(wc):.1f} KiB "
           f"(scale {wscale:.4f})\n")

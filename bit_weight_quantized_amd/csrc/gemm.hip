@@ -9,8 +9,8 @@
 //  PATH_PS  post-scaled: the integer codes (q-z), or the NF4 levels c[idx],
 //           enter fp16 MFMA unscaled; each group's fp32 partial tile is
 //           multiplied by the group scale once ("MixPE: Quantization and
-//           Hardware Co-design for Efficient LLM Inference", Abstract:
-//           dequantization after per-group mpGEMM).
+//           Hardware Co-design for Efficient LLM Inference", Abstract: the
+//           dequantization moves after the per-group product).
 //  PATH_MSD Multi-Scale Dequant: the activations arrive as int8 slices; the
 //           4-bit codes are widened to int8 with mask/shift only (no
 //           conversion to a floating type) and meet every slice on the int8

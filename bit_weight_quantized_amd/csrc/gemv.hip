@@ -1,8 +1,8 @@
 // Decode-shaped W4 product y[M][N] = x[M][K] . W' for 1 <= M <= 32.
 //
 // The weight stream dominates: every packed byte is read once from HBM and
-// turned into matrix-core operands on chip.  Dequantization is "after
-// per-group mpGEMM" ("MixPE: Quantization and Hardware Co-design for Efficient
+// turned into matrix-core operands on chip.  Dequantization follows the
+// per-group product ("MixPE: Quantization and Hardware Co-design for Efficient
 // LLM Inference", Abstract): each group's partial product is formed from the
 // raw codes and multiplied by the group scale once.  NF4 levels come from a
 // small table in LDS, as the "Fast NF4 Dequantization Kernels for Large

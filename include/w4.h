@@ -76,8 +76,8 @@ typedef enum { W4_INT4_ASYM = 0, W4_NF4 = 1 } w4_fmt;
  *   the fp16 matrix-core product (the dequantization baseline of [MSD], [NF4]).
  * W4_POSTSCALE: the integer codes (q-z), or the NF4 levels c[idx], enter the
  *   fp16 product unscaled; each group's fp32 partial sum is multiplied by its
- *   scale after accumulation ([MixPE]: dequantization after per-group
- *   mpGEMM). */
+ *   scale after accumulation ([MixPE]: the dequantization moves after the
+ *   per-group product). */
 typedef enum { W4_DQ_F16 = 0, W4_POSTSCALE = 1 } w4_mode;
 
 typedef enum {

@@ -59,7 +59,7 @@ def fp16_from_fp32(v32):
 
 
 # --------------------------------------------------------------------------
-# NF4 codebook  ([NF4] Abstract: "NF4 (4-bit NormalFloat)"; construction per
+# NF4 codebook  ([NF4] Abstract: the 4-bit NormalFloat format; construction per
 # QLoRA, listed in [DecDEC] "Builds on")
 # --------------------------------------------------------------------------
 def nf4_codebook_fp64() -> np.ndarray:
@@ -289,9 +289,9 @@ def matmul_ref(x, w_deq) -> np.ndarray:
 
 
 def postscale_ref(fmt: int, x, codes, scale, zero, G: int) -> np.ndarray:
-    """Per-group products scaled after accumulation ([MixPE] Abstract: because
-    scale and zero are shared inside a group, dequantization can follow the
-    per-group mpGEMM).
+    """Per-group products scaled after accumulation ([MixPE] Abstract: scale and
+    zero are shared inside a group, so the dequantization can come after the
+    per-group product).
 
     y[m, n] = sum_g s[n, g] * sum_{k in g} x[m, k] * v[n, k], where v = q - z for
     INT4 and v = c[idx] for NF4.  Algebraically equal to ``matmul_ref`` of the
@@ -320,9 +320,9 @@ def decompose_activations(x, nslices: int = 2):
     """Split fp16 activations [M][K] into ``nslices`` int8 slices with per-token
     fp32 scales, so that x ~= sum_j s_j[m] * A_j[m, k].
 
-    READING of [MSD] ("decomposes high-precision activations into multiple
-    low-precision components ... two-pass INT8 decomposition"): a greedy
-    residual quantization.  With r = x (in fp64), for each pass j:
+    READING of [MSD] (the activations are split into several low-precision
+    parts, two int8 passes for integer weights): a greedy residual
+    quantization.  With r = x (in fp64), for each pass j:
 
     1. s_j = fp32(max_k |r[m, k]| / 127);
     2. A_j = clamp(rint(r / s_j), -127, 127)  (round-half-to-even);

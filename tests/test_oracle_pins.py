@@ -303,7 +303,7 @@ def test_decompose_nearest_integers_and_bound():
                     for xv, a1, a2 in zip(x[m], A[0, m], A[1, m]))
         assert worst <= s2 / 2
         assert worst <= amax / 64516 * Fraction(1 + 2 ** -21)
-        # "near 16 effective bits" (MSD page, Abstract)
+        # close to 16 effective bits (MSD page, Abstract)
         assert float(amax / worst if worst else 1e30) >= 2 ** 15.97
 
 
