@@ -18,6 +18,8 @@ Pages cited (title, section):
            Inference", Abstract.
 * [NF4]    "Fast NF4 Dequantization Kernels for Large Language Model
            Inference", Abstract.
+* OCP Microscaling (MX) format definition: the E2M1 element and E8M0 scale
+           encodings of MXFP4 (a published format the [MSD] page names).
 * [DecDEC] "DecDEC: A Systems Approach to Advancing Low-Bit LLM
            Quantization", Abstract (residual compensation of salient
            channels) and "Builds on" list (names QLoRA, the source of the
@@ -443,6 +445,136 @@ def msd_matmul(x, codes, scale, zero, G: int, nslices: int = 2):
     A, S = decompose_activations(x, nslices)
     D = msd_accumulators(A, codes, zero, G)
     return msd_result(S, D, scale), A, S, D
+
+
+# --------------------------------------------------------------------------
+# MXFP4: 4-bit E2M1 elements with one E8M0 (power-of-two) scale per 32
+# consecutive K positions  ([MSD] Abstract: MXFP4 weights, two-pass MXFP4
+# decomposition of the activations).  Element and scale encodings follow the
+# published OCP Microscaling (MX) format definition.
+# --------------------------------------------------------------------------
+MX_BLOCK = 32
+E2M1_MAX = 6.0
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 code: bit 3 sign, bits 2..1 exponent (bias 1),
+    bit 0 mantissa; exponent 0 is subnormal (0 or 0.5)."""
+    sign = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+    return sign * mag
+
+
+def mx_scale_exponent(amax):
+    """READING of the scale rule (the pages do not give one): the smallest
+    integer e with amax <= 6 * 2^e, so no element exceeds the largest E2M1
+    magnitude (no saturation); e is clamped to the E8M0 range [-127, 127] and
+    an all-zero block takes e = -127.  This rule reproduces the single-pass
+    MXFP8 figure of the MSD abstract (see the pins)."""
+    a = np.asarray(amax, dtype=np.float64)
+    e = np.zeros(a.shape, dtype=np.int64)
+    nz = a > 0
+    # start from ceil(log2(a / 6)) and correct it against exact comparisons
+    guess = np.ceil(np.log2(np.where(nz, a, 1.0) / E2M1_MAX)).astype(np.int64)
+    guess = np.where(E2M1_MAX * np.ldexp(1.0, guess) < a, guess + 1, guess)
+    guess = np.where(E2M1_MAX * np.ldexp(1.0, guess - 1) >= a, guess - 1, guess)
+    e = np.where(nz, guess, -127)
+    return np.clip(e, -127, 127)
+
+
+def e2m1_round(t) -> np.ndarray:
+    """E2M1 code nearest to t (|t| <= 6 expected; clamped), ties to the even
+    code (mantissa bit 0); a result of magnitude zero carries no sign."""
+    t = np.asarray(t, dtype=np.float64)
+    mags = np.array([e2m1_value(c) for c in range(8)])
+    a = np.minimum(np.abs(t), E2M1_MAX)
+    d = np.abs(a[..., None] - mags)
+    best = d.min(axis=-1, keepdims=True)
+    tie = (d == best)
+    even = tie & (np.arange(8) % 2 == 0)
+    code = np.where(tie.sum(axis=-1) > 1, np.argmax(even, axis=-1), np.argmax(tie, axis=-1))
+    neg = (t < 0) & (code != 0)
+    return (code + 8 * neg).astype(np.uint8)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    table = np.array([e2m1_value(c) for c in range(16)])
+    return table[np.asarray(codes, dtype=np.int64)]
+
+
+def mx_quantize(v):
+    """MXFP4 of v [..., K] (K a multiple of 32): codes uint8 [..., K] and
+    scale exponents int [..., K/32]; value = e2m1(code) * 2^e of its block."""
+    v = np.asarray(v, dtype=np.float64)
+    shp = v.shape
+    b = v.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK))
+    e = mx_scale_exponent(np.abs(b).max(axis=-1))
+    codes = e2m1_round(b / np.ldexp(1.0, e)[..., None])  # exact: a power-of-two scaling
+    return codes.reshape(shp), e
+
+
+def mx_dequant(codes, e) -> np.ndarray:
+    c = e2m1_decode(codes)
+    shp = c.shape
+    b = c.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK))
+    return (b * np.ldexp(1.0, np.asarray(e, dtype=np.int64))[..., None]).reshape(shp)
+
+
+def quantize_mxfp4(wt):
+    """MXFP4 weights from W^T fp32 [N][K]: codes [N][K], exponents [N][K/32]
+    (stored as E8M0 bytes e + 127)."""
+    return mx_quantize(np.asarray(wt, dtype=np.float32))
+
+
+def decompose_mxfp4(x, nslices: int = 2):
+    """[MSD] two-pass MXFP4 decomposition of fp16 activations [M][K]: slice 1
+    is MXFP4(x), slice j + 1 is MXFP4 of the residual left by slices 1..j, all
+    in fp64 (the residuals are exact: each is a short sum of fp16 and
+    power-of-two-scaled E2M1 values).  Returns codes [nslices][M][K] and
+    exponents [nslices][M][K/32].
+
+    Bound: pass 1 leaves |r| <= 2^e1 (half the widest E2M1 gap, 2, at the
+    top binade); pass 2 then has e2 <= e1 - 2 and leaves |r| <= 2^e2 <=
+    2^e1 / 4 < amax / 12 per block (amax > 3 * 2^e1 by the scale rule)."""
+    r = np.asarray(x).astype(np.float64)
+    M, K = r.shape
+    C = np.zeros((nslices, M, K), dtype=np.uint8)
+    E = np.zeros((nslices, M, K // MX_BLOCK), dtype=np.int64)
+    for j in range(nslices):
+        C[j], E[j] = mx_quantize(r)
+        r = r - mx_dequant(C[j], E[j])
+    return C, E
+
+
+def mx_matmul(x_codes, x_exp, w_codes, w_exp) -> np.ndarray:
+    """y[m, n] = sum_j sum_k xhat_j[m, k] * what[n, k] in fp64 (every operand is
+    an exact power-of-two multiple of an E2M1 value)."""
+    W = mx_dequant(w_codes, w_exp)
+    y = 0.0
+    for j in range(np.asarray(x_codes).shape[0]):
+        y = y + mx_dequant(x_codes[j], x_exp[j]) @ W.T
+    return y
+
+
+def pack_mx(codes) -> np.ndarray:
+    """MXFP4 weight codes [N][K] (N % 16 == 0, K % 128 == 0) -> packed bytes in
+    1 KB tiles of 16 rows x 128 K positions, tile (nb, kb) at byte offset
+    (nb * K/128 + kb) * 1024 (the INT4 tile order).  Inside a tile, the 16
+    bytes at 16 * (16 j + r) hold row r's K positions 128 kb + 32 j + e,
+    e = 0..31, position e in byte e / 2, low nibble first: one 16-byte load
+    per lane is the B operand of a 16x16x128 block-scaled fp4 product."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    t = codes.reshape(N // 16, 16, K // 128, 4, 16, 2)  # nb, r, kb, j, byte, nibble
+    bytes_ = (t[..., 0] | (t[..., 1] << 4)).astype(np.uint8)  # nb, r, kb, j, byte
+    return np.ascontiguousarray(bytes_.transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
+def unpack_mx(packed, N: int, K: int) -> np.ndarray:
+    b = np.asarray(packed, dtype=np.uint8).reshape(N // 16, K // 128, 4, 16, 16)  # nb, kb, j, r, byte
+    codes = np.stack([b & 15, b >> 4], axis=-1)  # nb, kb, j, r, byte, nibble
+    return np.ascontiguousarray(codes.transpose(0, 3, 1, 2, 4, 5)).reshape(N, K)
 
 
 # --------------------------------------------------------------------------
