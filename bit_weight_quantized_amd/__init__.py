@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
     "lib", "lib_path", "quantize", "pack", "gemv", "gemm", "gemm_decomp", "gemm_decomp_fixed",
-    "salient_select", "residual_correct",
+    "salient_select", "residual_correct", "quantize_mx", "pack_mx", "gemm_mx",
     "workspace_bytes", "nf4_levels", "version",
 ]
 
@@ -28,7 +28,7 @@ INT4_ASYM = 0
 NF4 = 1
 DQ_F16 = 0
 POSTSCALE = 1
-OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP = range(5)
+OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP, OP_GEMM_MX = range(6)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libw4.so")
@@ -65,6 +65,9 @@ def lib():
         L.w4_gemm_decomp.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_gemm_decomp_fixed.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_salient_select.argtypes = [_p, _i, _i, _i, _p, _p]
+        L.w4_quantize_mx.argtypes = [_p, _i, _i, _p, _p, _p]
+        L.w4_pack_mx.argtypes = [_p, _i, _i, _p, _p]
+        L.w4_gemm_mx.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _sz, _p]
         L.w4_residual_correct.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p]
         L.w4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
         L.w4_workspace_bytes.restype = _sz
@@ -75,7 +78,8 @@ def lib():
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
         for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
-                   "w4_salient_select", "w4_residual_correct", "w4_nf4_levels"):
+                   "w4_salient_select", "w4_residual_correct", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
+                   "w4_nf4_levels"):
             getattr(L, fn).restype = _i
         _lib = L
     return _lib
@@ -245,4 +249,44 @@ def residual_correct(x, resid, idx, y, *, stream=None):
     _check("w4_residual_correct", lib().w4_residual_correct(_ptr(x), M, K, N, _ptr(resid), _ptr(idx), k, _ptr(y),
                                                             _stream(stream)))
     return y
+
+
+def quantize_mx(wt, *, codes=None, scale=None, stream=None):
+    """MXFP4 of W^T fp32 [N][K]: (codes u8 [N][K], E8M0 scales u8 [N][K/32])."""
+    _dev(wt, torch.float32, "wt")
+    N, K = wt.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=wt.device) if codes is None else codes
+    scale = torch.empty((N, K // 32), dtype=torch.uint8, device=wt.device) if scale is None else scale
+    _check("w4_quantize_mx", lib().w4_quantize_mx(_ptr(wt), K, N, _ptr(codes), _ptr(scale), _stream(stream)))
+    return codes, scale
+
+
+def pack_mx(codes, *, out=None, stream=None):
+    """MXFP4 codes [N][K] -> packed tiles (N*K/2 bytes)."""
+    _dev(codes, torch.uint8, "codes")
+    N, K = codes.shape
+    out = torch.empty((N * K // 2,), dtype=torch.uint8, device=codes.device) if out is None else out
+    _check("w4_pack_mx", lib().w4_pack_mx(_ptr(codes), K, N, _ptr(out), _stream(stream)))
+    return out
+
+
+def gemm_mx(x, packed, scale, nslices: int = 2, *, out=None, slices_out=None, scales_out=None, workspace=None,
+            stream=None):
+    """y = x . W' with MXFP4 weights and x split into MXFP4 slices.  Returns y,
+    or (y, slices, scales) when an optional output is given."""
+    _dev(x, torch.float16, "x")
+    _dev(packed, torch.uint8, "packed")
+    _dev(scale, torch.uint8, "scale")
+    M, K = x.shape
+    N = scale.shape[0]
+    out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(OP_GEMM_MX, M, K, N, 32, nslices), dtype=torch.uint8,
+                                device=x.device)
+    _check("w4_gemm_mx", lib().w4_gemm_mx(
+        _ptr(x), M, K, N, _ptr(packed), _ptr(scale), nslices, _ptr(out), _ptr(slices_out), _ptr(scales_out),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    if slices_out is None and scales_out is None:
+        return out
+    return out, slices_out, scales_out
 

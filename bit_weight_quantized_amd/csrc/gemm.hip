@@ -79,29 +79,6 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return per
 // conflicts.
 constexpr int kF16Threads = 512;  // 8 waves
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Workgroup barrier for the copy pipelines: this wave's LDS reads have
-// completed (lgkmcnt(0)) and no memory access moves across it, but its
-// global -> LDS copies stay in flight (no vmcnt wait; every wave waits for its
-// own copies of a step explicitly before the barrier that publishes them).
-// __syncthreads() would also drain the copies of the steps ahead.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-// 16 bytes per lane from a raw buffer (offset = voff + soff) to lds_base +
-// 16 * lane (lds_base wave-uniform).  Lanes whose voff lies past the buffer
-// write zeros.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                              unsigned char* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
-}
 
 // fp16 paths: 128 tokens x 256 weight rows per workgroup, the 8 waves side by
 // side along N (each 128 x 32: 8 x 2 products of 16 x 16), so every weight

@@ -1,0 +1,371 @@
+// MXFP4 weights and the two-pass MXFP4 decomposition of the activations on
+// the block-scaled fp4 matrix cores ("Multi-Scale Dequant: Eliminating
+// Dequantization Bottleneck via Activation Decomposition for Efficient LLM
+// Inference", Abstract: MXFP4 weights, activations split into two MXFP4
+// parts, each multiplied with the weights directly).
+//
+// MXFP4 (the published OCP Microscaling format): 4-bit E2M1 elements (sign,
+// 2-bit exponent with bias 1, 1-bit mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3,
+// 4, 6) and one E8M0 scale 2^(s - 127) per 32 consecutive K positions.  Scale
+// rule (a reading; the pages give none): the smallest e with amax <= 6 * 2^e,
+// so no element saturates.  Rounding to E2M1 is to nearest, ties to the even
+// mantissa; a zero result carries no sign.  Every decision is taken in fp64,
+// where the scaled values and the residuals are exact.
+//
+// gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 operands takes, per
+// lane l, 16 bytes of A (row l % 16, K positions 32 (l / 16) .. + 31, two per
+// byte, low nibble first), the same for B (column l % 16), and one E8M0 byte
+// per operand for that lane's 32 positions; it applies both scales itself.
+// So a slice row stored as plain packed nibbles is already in operand order,
+// and the product needs no per-group epilogue: both slices accumulate into
+// the same fp32 tile.
+#include "w4_device.h"
+#include "w4_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace w4 {
+namespace {
+
+constexpr int kMxBlock = 32;
+constexpr int kMxStepK = 128;
+constexpr int kMxXcds = 8;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- encoding
+__device__ __forceinline__ int mx_exponent(double amax) {
+  if (!(amax > 0.0)) return -127;
+  int g = (int)ceil(log2(amax / 6.0));
+  if (6.0 * ldexp(1.0, g) < amax) ++g;        // the guess is within one of the
+  if (6.0 * ldexp(1.0, g - 1) >= amax) --g;   // answer; fix it with exact tests
+  return min(max(g, -127), 127);
+}
+
+__device__ __forceinline__ int e2m1_code(double t) {
+  const double a = fmin(fabs(t), 6.0);
+  const int c = a <= 0.25 ? 0 : a < 0.75 ? 1 : a <= 1.25 ? 2 : a < 1.75 ? 3
+              : a <= 2.5 ? 4 : a < 3.5 ? 5 : a <= 5.0 ? 6 : 7;
+  return (t < 0.0 && c != 0) ? (c | 8) : c;
+}
+
+__device__ __forceinline__ double e2m1_mag(int c) {
+  const int e = (c >> 1) & 3, m = c & 1;
+  return e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+}
+
+// one 32-element block: codes and exponent of v (v is left as the residual)
+__device__ __forceinline__ int mx_block(double (&v)[kMxBlock], uint8_t (&code)[kMxBlock]) {
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < kMxBlock; ++i) amax = fmax(amax, fabs(v[i]));
+  const int e = mx_exponent(amax);
+#pragma unroll
+  for (int i = 0; i < kMxBlock; ++i) {
+    const int c = e2m1_code(ldexp(v[i], -e));
+    code[i] = (uint8_t)c;
+    const double q = ldexp(e2m1_mag(c & 7), e);
+    v[i] = v[i] - ((c & 8) ? -q : q);
+  }
+  return e;
+}
+
+__device__ __forceinline__ u32x4 pack_nibbles(const uint8_t (&code)[kMxBlock]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x |= (uint32_t)code[8 * q + i] << (4 * i);
+    w[q] = x;
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// ------------------------------------------------------- weight quantizer
+// One thread per (row, block of 32): codes (one per byte) and E8M0 scales.
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const float* __restrict__ wt, int K, int N,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scale) {
+  const int nb = K / kMxBlock;
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (long)N * nb) return;
+  const long n = t / nb, b = t % nb;
+  const float* src = wt + n * K + b * kMxBlock;
+  double v[kMxBlock];
+#pragma unroll
+  for (int i = 0; i < kMxBlock; ++i) v[i] = (double)src[i];
+  uint8_t c[kMxBlock];
+  const int e = mx_block(v, c);
+  uint8_t* dst = codes + n * K + b * kMxBlock;
+#pragma unroll
+  for (int i = 0; i < kMxBlock; ++i) dst[i] = c[i];
+  scale[n * nb + b] = (uint8_t)(e + 127);
+}
+
+// codes [N][K] -> 1 KB tiles (16 rows x 128 K positions); lane l = 16 j + r of
+// a tile holds row r's positions 32 j .. 32 j + 31, two per byte, low first.
+__global__ __launch_bounds__(256) void pack_mx_kernel(const uint8_t* __restrict__ codes, int K, int N,
+                                                      uint8_t* __restrict__ packed) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte piece
+  const long KT = K / kMxStepK;
+  if (t >= (long)(N / 16) * KT * 64) return;
+  const long tile = t / 64;
+  const int l = (int)(t % 64), j = l / 16, r = l % 16;
+  const long nb = tile / KT, kb = tile % KT;
+  const uint8_t* src = codes + (nb * 16 + r) * K + kb * kMxStepK + 32 * j;
+  uint8_t c[kMxBlock];
+#pragma unroll
+  for (int i = 0; i < kMxBlock; ++i) c[i] = src[i];
+  *reinterpret_cast<u32x4*>(packed + t * 16) = pack_nibbles(c);
+}
+
+// ------------------------------------------------- activation decomposition
+// One thread per (token, block of 32): NS passes, each the MXFP4 of the
+// residual the earlier passes left.  Slices [NS][M][K/2] (packed nibbles,
+// low first) and E8M0 scales [NS][M][K/32].
+template <int NS>
+__global__ __launch_bounds__(256) void decompose_mx_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                           uint8_t* __restrict__ slices, uint8_t* __restrict__ scales,
+                                                           uint8_t* __restrict__ slices_out,
+                                                           uint8_t* __restrict__ scales_out) {
+  const int nb = K / kMxBlock;
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (long)M * nb) return;
+  const long m = t / nb, b = t % nb;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + m * K + b * kMxBlock);
+  double v[kMxBlock];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 w = src[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * q + 2 * i] = (double)half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
+      v[8 * q + 2 * i + 1] = (double)half_bits_to_float((uint16_t)(w[i] >> 16));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    uint8_t c[kMxBlock];
+    const int e = mx_block(v, c);
+    const u32x4 p = pack_nibbles(c);
+    const size_t row = (size_t)j * M + m;
+    *reinterpret_cast<u32x4*>(slices + row * (K / 2) + b * 16) = p;
+    scales[row * nb + b] = (uint8_t)(e + 127);
+    if (slices_out) *reinterpret_cast<u32x4*>(slices_out + row * (K / 2) + b * 16) = p;
+    if (scales_out) scales_out[row * nb + b] = (uint8_t)(e + 127);
+  }
+}
+
+// ------------------------------------------------------------------ product
+// 128 tokens x 256 weight rows per workgroup, 8 waves side by side along N
+// (each 128 x 32: 8 x 2 products of 16 x 16 per slice), K step 128 (one
+// block-scaled product per tile pair), three stages of global -> LDS copies:
+//  * slice j's step tile: 128 rows x 64 bytes; 16-byte chunk c of row m sits
+//    at chunk c ^ ((m >> 2) & 3), so the 16 lanes reading one chunk column of
+//    16 rows hit 16 different bank groups;
+//  * the 16 weight tiles of the step (1 KB each, lane l's operand at 16 l);
+//  * the step's E8M0 bytes as 4-byte words: [slice][row] and [column], each
+//    word the row's (column's) four blocks of the step; a lane extracts its
+//    own block's byte.
+constexpr int kMxThreads = 512;
+constexpr int kMxBM = 128;
+constexpr int kMxBN = 256;
+constexpr int kMxA = kMxBM * 64;
+constexpr int kMxB = (kMxBN / 16) * 1024;
+constexpr int kMxSA = kMxBM * 4;
+constexpr int kMxSB = kMxBN * 4;
+constexpr int kMxStages = 3;
+template <int NS>
+constexpr int mx_stage_bytes() { return NS * kMxA + kMxB + NS * kMxSA + kMxSB; }
+
+__device__ __forceinline__ f32x4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, f32x4 c) {
+  const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const v8i bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+template <int NS>
+__global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_mx_kernel(
+    const uint8_t* __restrict__ slices, const uint8_t* __restrict__ xscale, int M, int K, int N,
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ wscale, uint16_t* __restrict__ y) {
+  constexpr int MT = 8, NT = 2;
+  constexpr int kStage = mx_stage_bytes<NS>();
+  constexpr int kOffB = NS * kMxA, kOffSA = kOffB + kMxB, kOffSB = kOffSA + NS * kMxSA;
+  constexpr int kScaleCopies = 2 * NS + 4;  // 64 rows or columns each
+  constexpr int kCopies = NS + 2 + 1;       // per wave per step
+  static_assert(kScaleCopies <= 8, "one scale copy per wave");
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ln = lane % 16, jb = lane / 16;
+
+  const int tiles_n = (N + kMxBN - 1) / kMxBN;
+  const int tiles = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xcd = bid % kMxXcds, idx = bid / kMxXcds;
+  const int per = tiles / kMxXcds, rem = tiles % kMxXcds;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int n0 = (logical % tiles_n) * kMxBN;
+  const int m0 = (logical / tiles_n) * kMxBM;
+
+  const int KT = K / kMxStepK;
+  const int nbk = K / kMxBlock;  // scale bytes per row
+  const int ntile_last = N / 16 - 1;
+
+  // descriptors from scalar sizes (each slice and its scales on their own,
+  // so rows past M read zeros)
+  const uint32_t slice_bytes = __builtin_amdgcn_readfirstlane((uint32_t)M * (uint32_t)(K / 2));
+  const uint32_t xs_bytes = __builtin_amdgcn_readfirstlane((uint32_t)M * (uint32_t)nbk);
+  auto ar = [&](int j) { return make_rsrc(slices + (size_t)j * slice_bytes, slice_bytes); };
+  auto sr = [&](int j) { return make_rsrc(xscale + (size_t)j * xs_bytes, xs_bytes); };
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
+  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(wscale, (uint32_t)((size_t)N * nbk));
+
+  // wave wn copies rows 16 wn .. 16 wn + 15 of each slice: lane l -> row
+  // 16 wn + l / 4, LDS chunk l % 4, which holds global chunk (l % 4) ^ ((l / 16) & 3)
+  const int arow = 16 * wn + lane / 4;
+  const uint32_t voff_a = (uint32_t)(m0 + arow) * (uint32_t)(K / 2) + (uint32_t)(((lane % 4) ^ ((lane / 16) & 3)) * 16);
+  uint32_t voff_b[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    voff_b[j] = (uint32_t)min(n0 / 16 + 2 * wn + j, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
+  // this wave's scale copy: c < 2 NS: slice c / 2, rows 64 (c % 2) + lane;
+  // otherwise columns 64 (c - 2 NS) + lane
+  const int sc = wn % kScaleCopies;
+  const bool sc_x = sc < 2 * NS;
+  const int sc_j = sc_x ? sc / 2 : 0;
+  const uint32_t voff_s = sc_x ? (uint32_t)(m0 + 64 * (sc % 2) + lane) * (uint32_t)nbk
+                               : (uint32_t)(n0 + 64 * (sc - 2 * NS) + lane) * (uint32_t)nbk;
+  const int sc_dst = sc_x ? kOffSA + sc_j * kMxSA + 64 * (sc % 2) * 4 : kOffSB + 64 * (sc - 2 * NS) * 4;
+
+  auto stage = [&](int kt) { return smem + (kt % kMxStages) * kStage; };
+  auto issue_step = [&](int kt) {
+    unsigned char* st = stage(kt);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) copy16_to_lds(ar(j), voff_a, (uint32_t)kt * 64, st + j * kMxA + 16 * wn * 64);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) copy16_to_lds(wr, voff_b[j], (uint32_t)kt * 1024, st + kOffB + (2 * wn + j) * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_x ? sr(sc_j) : wsr, (lds_void*)(st + sc_dst), 4, voff_s,
+                                             (uint32_t)kt * 4, 0, 0);
+  };
+  auto wait_all_but_one_step = [&]() { __builtin_amdgcn_s_waitcnt(kCopies | (0x7 << 4) | (0xF << 8)); };
+
+  f32x4 C[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t a_chunk = (uint32_t)((jb ^ ((ln >> 2) & 3)) * 16);
+  const uint32_t shift = 8u * (uint32_t)jb;
+
+  issue_step(0);
+  if (KT > 1) {
+    issue_step(1);
+    wait_all_but_one_step();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const unsigned char* cur = stage(kt);
+    const bool more2 = kt + 2 < KT;
+    if (more2) issue_step(kt + 2);
+
+    u32x4 Bv[NT];
+    uint32_t sb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      Bv[nt] = *reinterpret_cast<const u32x4*>(cur + kOffB + (2 * wn + nt) * 1024 + lane * 16);
+      sb[nt] = __builtin_amdgcn_ubfe(*reinterpret_cast<const uint32_t*>(cur + kOffSB + (wn * 32 + nt * 16 + ln) * 4),
+                                     shift, 8);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const u32x4 A = *reinterpret_cast<const u32x4*>(cur + j * kMxA + (mt * 16 + ln) * 64 + a_chunk);
+        const uint32_t sa =
+            __builtin_amdgcn_ubfe(*reinterpret_cast<const uint32_t*>(cur + kOffSA + j * kMxSA + (mt * 16 + ln) * 4),
+                                  shift, 8);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) C[mt][nt] = mfma_fp4(A, sa, Bv[nt], sb[nt], C[mt][nt]);
+      }
+    }
+
+    if (more2)
+      wait_all_but_one_step();  // step kt+1's copies have landed
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();  // everyone's have, and nobody still reads this step's buffer
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + mt * 16 + 4 * jb + i;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + wn * 32 + nt * 16 + ln;
+        if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
+      }
+    }
+}
+
+template <int NS>
+int launch_gemm_mx_t(const uint8_t* slices, const uint8_t* xscale, int M, int K, int N, const uint8_t* packed,
+                     const uint8_t* wscale, uint16_t* y, hipStream_t s) {
+  constexpr int kLds = kMxStages * mx_stage_bytes<NS>();
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_mx_kernel<NS>), kLds, "w4_gemm_mx");
+  if (st != 0) return st;
+  const long tiles = (long)((N + kMxBN - 1) / kMxBN) * ((M + kMxBM - 1) / kMxBM);
+  hipLaunchKernelGGL((gemm_mx_kernel<NS>), dim3((unsigned)tiles), dim3(kMxThreads), kLds, s, slices, xscale, M, K, N,
+                     packed, wscale, y);
+  return check_launch("gemm_mx");
+}
+
+inline unsigned blocks_for(long threads) { return (unsigned)((threads + 255) / 256); }
+
+}  // namespace
+
+int launch_quantize_mx(const float* wt, int K, int N, uint8_t* codes, uint8_t* scale, hipStream_t s) {
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3(blocks_for((long)N * (K / kMxBlock))), dim3(256), 0, s, wt, K, N,
+                     codes, scale);
+  return check_launch("quantize_mx");
+}
+
+int launch_pack_mx(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t s) {
+  hipLaunchKernelGGL(pack_mx_kernel, dim3(blocks_for((long)(N / 16) * (K / kMxStepK) * 64)), dim3(256), 0, s, codes,
+                     K, N, packed);
+  return check_launch("pack_mx");
+}
+
+size_t mx_workspace_bytes(int M, int K, int nslices) {
+  const size_t sl = ((size_t)nslices * M * (K / 2) + 255) / 256 * 256;
+  const size_t sc = ((size_t)nslices * M * (K / kMxBlock) + 255) / 256 * 256;
+  return sl + sc;
+}
+
+int launch_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint8_t* wscale, int nslices,
+                   uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, hipStream_t s) {
+  uint8_t* sl = static_cast<uint8_t*>(ws);
+  uint8_t* sc = sl + ((size_t)nslices * M * (K / 2) + 255) / 256 * 256;
+  const unsigned blocks = blocks_for((long)M * (K / kMxBlock));
+  if (nslices == 1)
+    hipLaunchKernelGGL(decompose_mx_kernel<1>, dim3(blocks), dim3(256), 0, s, x, M, K, sl, sc, slices_out,
+                       scales_out);
+  else
+    hipLaunchKernelGGL(decompose_mx_kernel<2>, dim3(blocks), dim3(256), 0, s, x, M, K, sl, sc, slices_out,
+                       scales_out);
+  const int st = check_launch("decompose_mx");
+  if (st != 0) return st;
+  if (nslices == 1) return launch_gemm_mx_t<1>(sl, sc, M, K, N, packed, wscale, y, s);
+  return launch_gemm_mx_t<2>(sl, sc, M, K, N, packed, wscale, y, s);
+}
+
+}  // namespace w4

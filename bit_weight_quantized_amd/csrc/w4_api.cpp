@@ -243,6 +243,44 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
   return launch_residual_correct(x, M, K, N, static_cast<const uint16_t*>(dev), idx, k, y, (hipStream_t)stream);
 }
 
+int w4_quantize_mx(const float* wt, int K, int N, uint8_t* codes, uint8_t* scale, void* stream) {
+  g_last_error[0] = '\0';
+  if (K < 1 || N < 1 || K % 32)
+    return fail(W4_EINVAL, "w4_quantize_mx: need K, N >= 1 and K %% 32 == 0 (got K=%d N=%d)", K, N);
+  if (!wt || !codes || !scale) return fail(W4_EINVAL, "w4_quantize_mx: null operand");
+  if (reinterpret_cast<uintptr_t>(wt) & 3u) return fail(W4_EINVAL, "w4_quantize_mx: wt must be 4-byte aligned");
+  return launch_quantize_mx(wt, K, N, codes, scale, (hipStream_t)stream);
+}
+
+int w4_pack_mx(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream) {
+  g_last_error[0] = '\0';
+  if (K < 128 || N < 16 || K % 128 || N % 16)
+    return fail(W4_EINVAL, "w4_pack_mx: need K %% 128 == 0 and N %% 16 == 0 (got K=%d N=%d)", K, N);
+  if (!codes || !packed) return fail(W4_EINVAL, "w4_pack_mx: null operand");
+  if (!aligned16(packed)) return fail(W4_EINVAL, "w4_pack_mx: packed must be 16-byte aligned");
+  return launch_pack_mx(codes, K, N, packed, (hipStream_t)stream);
+}
+
+int w4_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint8_t* scale, int nslices,
+               uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (M < 1 || K < 128 || N < 16 || K % 128 || N % 16)
+    return fail(W4_EINVAL, "w4_gemm_mx: need M >= 1, K %% 128 == 0, N %% 16 == 0 (got M=%d K=%d N=%d)", M, K, N);
+  if (nslices != 1 && nslices != 2) return fail(W4_EINVAL, "w4_gemm_mx: nslices must be 1 or 2 (got %d)", nslices);
+  if (!packed || !scale) return fail(W4_EINVAL, "w4_gemm_mx: null weights");
+  if (!aligned16(packed)) return fail(W4_EINVAL, "w4_gemm_mx: packed must be 16-byte aligned");
+  int st;
+  if ((st = check_io("w4_gemm_mx", x, y)) != W4_OK) return st;
+  if (slices_out && !aligned16(slices_out)) return fail(W4_EINVAL, "w4_gemm_mx: slices_out must be 16-byte aligned");
+  if ((size_t)M * (K / 2) >= (1ull << 32) || (size_t)N * (K / 2) >= (1ull << 32))
+    return fail(W4_EUNSUPPORTED, "w4_gemm_mx: operands beyond the 4 GiB one call addresses");
+  const size_t need = mx_workspace_bytes(M, K, nslices);
+  if (!ws || ws_bytes < need)
+    return fail(W4_EWORKSPACE, "w4_gemm_mx: workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemm_mx: workspace must be 16-byte aligned");
+  return launch_gemm_mx(x, M, K, N, packed, scale, nslices, y, slices_out, scales_out, ws, (hipStream_t)stream);
+}
+
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
   switch (op) {
     case W4_OP_QUANTIZE:
@@ -254,6 +292,9 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
     case W4_OP_GEMV:
       if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G || K % 128) return 0;
       return plan_gemv(M, K, N, G, fmt_or_mode == W4_NF4 ? W4_NF4 : W4_INT4_ASYM).ws_bytes;
+    case W4_OP_GEMM_MX:
+      if (M < 1 || K < 128 || K % 128 || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
+      return mx_workspace_bytes(M, K, fmt_or_mode);
     case W4_OP_GEMM_DECOMP:
       if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || fmt_or_mode < 1 || fmt_or_mode > 3) return 0;
       return decomp_workspace_bytes(M, K, G, fmt_or_mode);

@@ -56,6 +56,30 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier for the copy pipelines: this wave's LDS reads have
+// completed (lgkmcnt(0)) and no memory access moves across it, but its
+// global -> LDS copies stay in flight (no vmcnt wait; every wave waits for its
+// own copies of a step explicitly before the barrier that publishes them).
+// __syncthreads() would also drain the copies of the steps ahead.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from a raw buffer (offset = voff + soff) to lds_base +
+// 16 * lane (lds_base wave-uniform).  Lanes whose voff lies past the buffer
+// write zeros.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              unsigned char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }

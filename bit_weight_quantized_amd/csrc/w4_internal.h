@@ -75,6 +75,16 @@ int launch_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, 
 int launch_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
                             int k, uint16_t* y, hipStream_t s);
 
+// MXFP4 weights (codes one per byte, E8M0 scales [N][K/32]), their packing
+// into 1 KB tiles, and the MXFP4 product with the activations split into
+// nslices (1 or 2) MXFP4 slices; workspace: slices [ns][M][K/2], then scales
+// [ns][M][K/32], each 256-byte aligned.
+int launch_quantize_mx(const float* wt, int K, int N, uint8_t* codes, uint8_t* scale, hipStream_t s);
+int launch_pack_mx(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t s);
+size_t mx_workspace_bytes(int M, int K, int nslices);
+int launch_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint8_t* wscale, int nslices,
+                   uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, hipStream_t s);
+
 // The 16 NF4 levels as fp32 bit patterns (host copy).
 extern const uint32_t kNf4LevelBits[16];
 

@@ -85,7 +85,8 @@ typedef enum {
   W4_OP_PACK = 1,
   W4_OP_GEMV = 2,
   W4_OP_GEMM = 3,
-  W4_OP_GEMM_DECOMP = 4
+  W4_OP_GEMM_DECOMP = 4,
+  W4_OP_GEMM_MX = 5
 } w4_op;
 
 /*
@@ -209,6 +210,55 @@ int w4_gemm_decomp_fixed(const uint16_t* x, int M, int K, int N,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * MXFP4 path ([MSD] Abstract: MXFP4 weights; the activations split into two
+ * MXFP4 parts, each multiplied with the weights directly on the matrix cores).
+ *
+ * MXFP4 is the published OCP Microscaling element format E2M1 (sign, 2-bit
+ * exponent with bias 1, 1-bit mantissa; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ * codes 0..15 with bit 3 the sign) with one E8M0 scale byte s per 32
+ * consecutive K positions (value 2^(s - 127)).  Scale rule (a reading: the
+ * pages give none): the smallest e with max|v| <= 6 * 2^e over the block
+ * (no element saturates), clamped to [-127, 127]; an all-zero block gets
+ * e = -127.  Elements round to nearest, ties to the even mantissa; a zero
+ * result has code 0.  All decisions are exact (fp64).
+ */
+
+/*
+ * w4_quantize_mx -- W^T fp32 [N][K] (device, 4-byte aligned, K % 32 == 0) ->
+ * codes u8 [N][K] (one E2M1 code per byte) and scales u8 [N][K/32] (E8M0).
+ */
+int w4_quantize_mx(const float* wt, int K, int N, uint8_t* codes, uint8_t* scale, void* stream);
+
+/*
+ * w4_pack_mx -- codes [N][K] -> packed [N*K/2] in 1 KB tiles of 16 rows x 128
+ * K positions, tile (nb, kb) at byte (nb*K/128 + kb)*1024; in a tile, the 16
+ * bytes at 16*(16j + r) hold row r's positions 128kb + 32j .. + 31, two per
+ * byte, low nibble first (the operand order of the block-scaled fp4 product).
+ * Requires K % 128 == 0, N % 16 == 0; packed 16-byte aligned.
+ */
+int w4_pack_mx(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream);
+
+/*
+ * w4_gemm_mx -- y[M][N] fp16 = x . W' with MXFP4 weights (packed by
+ * w4_pack_mx, scales [N][K/32]) and the activations split into `nslices`
+ * (1 or 2) MXFP4 slices: slice 1 = MXFP4(x), slice 2 = MXFP4(x - slice 1),
+ * per token and block of 32, in fp64.  Each slice meets the weights on the
+ * block-scaled fp4 matrix cores, which apply both E8M0 scales; the products
+ * accumulate in fp32.  Two slices: at most 2^(e1 - 2) < amax/12 error per
+ * element of a block (e1 the first slice's exponent, amax the block's max).
+ *
+ * Requires K % 128 == 0, N % 16 == 0, x and y 16-byte aligned, operands below
+ * 4 GiB.  Optional outputs (NULL to skip): slices_out u8 [nslices][M][K/2]
+ * (packed, low nibble first), scales_out u8 [nslices][M][K/32].  Workspace
+ * (required, 16-byte aligned, no initial contents):
+ * w4_workspace_bytes(W4_OP_GEMM_MX, M, K, N, 32, nslices) bytes.
+ */
+int w4_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+               const uint8_t* scale, int nslices, uint16_t* y, uint8_t* slices_out,
+               uint8_t* scales_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * w4_salient_select/*
  * w4_salient_select -- the k salient input channels of a decode step, for
  * residual compensation ([DecDEC] Abstract: salient channels are those where
  * the current activations have outliers, chosen anew at every step).
@@ -244,7 +294,7 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
  * w4_workspace_bytes/*
  * w4_workspace_bytes -- bytes of workspace an entry point needs for the given
  * shape.  `fmt_or_mode`: the w4_fmt for W4_OP_GEMV, the w4_mode for
- * W4_OP_GEMM, nslices for W4_OP_GEMM_DECOMP.  Host-only; returns 0 for ops
+ * W4_OP_GEMM, nslices for W4_OP_GEMM_DECOMP and W4_OP_GEMM_MX.  Host-only; returns 0 for ops
  * that need none and (size_t)-1 for an invalid op.
  */
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode);

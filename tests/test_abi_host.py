@@ -148,6 +148,27 @@ def test_residual_argument_errors(L):
     assert b"w4_residual_correct" in L.w4_last_error()
 
 
+def test_mx_argument_errors(L):
+    assert L.w4_quantize_mx(FAKE, 100, 16, FAKE, FAKE, None) == W4_EINVAL   # K % 32
+    assert L.w4_quantize_mx(None, 128, 16, FAKE, FAKE, None) == W4_EINVAL
+    assert L.w4_pack_mx(FAKE, 96, 16, FAKE, None) == W4_EINVAL             # K % 128
+    assert L.w4_pack_mx(FAKE, 128, 24, FAKE, None) == W4_EINVAL            # N % 16
+    assert L.w4_pack_mx(FAKE, 128, 16, MISALIGNED, None) == W4_EINVAL
+
+    def g(M=4, K=256, N=32, ns=2, ws=None, wsb=0, x=FAKE):
+        return L.w4_gemm_mx(x, M, K, N, FAKE, FAKE, ns, FAKE, None, None, ws, wsb, None)
+    assert g(ns=3) == W4_EINVAL
+    assert g(K=192) == W4_EINVAL
+    assert g(N=24) == W4_EINVAL
+    assert g(M=0) == W4_EINVAL
+    assert g(x=MISALIGNED) == W4_EINVAL
+    assert g() == W4_EWORKSPACE
+    need = L.w4_workspace_bytes(5, 4, 256, 32, 32, 2)
+    assert need == 1024 + 256  # slices 2*4*128 bytes, scales 2*4*8 bytes rounded up to 256
+    assert g(ws=FAKE, wsb=need - 1) == W4_EWORKSPACE
+    assert L.w4_workspace_bytes(5, 4, 256, 32, 32, 3) == 0
+
+
 def test_quantize_and_pack_argument_errors(L):
     assert L.w4_quantize(FAKE, 100, 16, 64, 0, FAKE, FAKE, FAKE, None) == W4_EINVAL
     assert L.w4_quantize(FAKE, 128, 16, 64, 1, FAKE, FAKE, FAKE, None) == W4_EINVAL  # NF4 + zero
