@@ -56,7 +56,6 @@ namespace w4 {
 namespace {
 
 constexpr int kStepK = 128;  // one weight-tile column per K step
-constexpr int kXcds = 8;
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -106,7 +105,7 @@ template <int PATH, int FMT, int GPT>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_f16_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
-    float* __restrict__ partial) {
+    float* __restrict__ partial, int gm) {
   constexpr int G = kStepK / GPT;
   constexpr int WPG = 4 / GPT;  // products (tile words) per group
   constexpr int MT = 8, NT = 2;
@@ -120,15 +119,12 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   const int ks = blockIdx.y;
   const int ln = lane % 16, kb = lane / 16;
 
-  // XCD-aware renumbering (a bijection of [0, tiles))
+  // XCD-aware, row-block-grouped renumbering (a bijection of [0, tiles))
   const int tiles_n = (N + kHBN - 1) / kHBN;
-  const int tiles = gridDim.x;
-  const int b = blockIdx.x;
-  const int xcd = b % kXcds, idx = b / kXcds;
-  const int per = tiles / kXcds, rem = tiles % kXcds;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const int n0 = (logical % tiles_n) * kHBN;
-  const int m0 = (logical / tiles_n) * kHBM;
+  int mb, nb;
+  tile_of(blockIdx.x, gridDim.x, (M + kHBM - 1) / kHBM, tiles_n, gm, mb, nb);
+  const int n0 = nb * kHBN;
+  const int m0 = mb * kHBM;
 
   const int ng = K / G;
   const int KT = K / kStepK;
@@ -360,7 +356,7 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
   if (st != 0) return st;
   const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
   hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles, (unsigned)S), dim3(kF16Threads),
-                     kLds, s, x, M, K, N, packed, scale, zero, y, partial);
+                     kLds, s, x, M, K, N, packed, scale, zero, y, partial, gemm_group_rows());
   const int st2 = check_launch("gemm");
   if (st2 != 0 || S == 1) return st2;
   return launch_reduce_partials(partial, S, (long)M * N, y, s);
@@ -393,7 +389,7 @@ template <int GPT, int NS, bool DBG, bool FIXED>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_msd_kernel(
     const int8_t* __restrict__ slices, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
-    const float* __restrict__ tok_scale, int32_t* __restrict__ acc_out) {
+    const float* __restrict__ tok_scale, int32_t* __restrict__ acc_out, int gm) {
   constexpr int G = kStepK / GPT;
   constexpr int UPG = 2 / GPT;  // int8 products (64 K positions each) per group
   constexpr int MT = msd_mt(GPT, NS, DBG), NT = 2;
@@ -413,13 +409,10 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   const int ln = lane % 16, kb = lane / 16;
 
   const int tiles_n = (N + kHBN - 1) / kHBN;
-  const int tiles = gridDim.x;
-  const int b = blockIdx.x;
-  const int xcd = b % kXcds, idx = b / kXcds;
-  const int per = tiles / kXcds, rem = tiles % kXcds;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const int n0 = (logical % tiles_n) * kHBN;
-  const int m0 = (logical / tiles_n) * BM;
+  int mb, nb;
+  tile_of(blockIdx.x, gridDim.x, (M + BM - 1) / BM, tiles_n, gm, mb, nb);
+  const int n0 = nb * kHBN;
+  const int m0 = mb * BM;
 
   const int ng = K / G;
   const int KT = K / kStepK;
@@ -625,10 +618,10 @@ int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed,
   const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + bm - 1) / bm);
   if (acc_out)
     hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true, FIXED>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices, M,
-                       K, N, packed, scale, zero, y, tok_scale, acc_out);
+                       K, N, packed, scale, zero, y, tok_scale, acc_out, gemm_group_rows());
   else
     hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false, FIXED>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices,
-                       M, K, N, packed, scale, zero, y, tok_scale, acc_out);
+                       M, K, N, packed, scale, zero, y, tok_scale, acc_out, gemm_group_rows());
   return check_launch("gemm_msd");
 }
 

@@ -29,7 +29,6 @@ namespace {
 
 constexpr int kMxBlock = 32;
 constexpr int kMxStepK = 128;
-constexpr int kMxXcds = 8;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
@@ -187,7 +186,7 @@ __device__ __forceinline__ f32x4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_
 template <int NS>
 __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_mx_kernel(
     const uint8_t* __restrict__ slices, const uint8_t* __restrict__ xscale, int M, int K, int N,
-    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ wscale, uint16_t* __restrict__ y) {
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ wscale, uint16_t* __restrict__ y, int gm) {
   constexpr int MT = 8, NT = 2;
   constexpr int kStage = mx_stage_bytes<NS>();
   constexpr int kOffB = NS * kMxA, kOffSA = kOffB + kMxB, kOffSB = kOffSA + NS * kMxSA;
@@ -202,13 +201,10 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int ln = lane % 16, jb = lane / 16;
 
   const int tiles_n = (N + kMxBN - 1) / kMxBN;
-  const int tiles = gridDim.x;
-  const int bid = blockIdx.x;
-  const int xcd = bid % kMxXcds, idx = bid / kMxXcds;
-  const int per = tiles / kMxXcds, rem = tiles % kMxXcds;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-  const int n0 = (logical % tiles_n) * kMxBN;
-  const int m0 = (logical / tiles_n) * kMxBM;
+  int mb, nb;
+  tile_of(blockIdx.x, gridDim.x, (M + kMxBM - 1) / kMxBM, tiles_n, gm, mb, nb);
+  const int n0 = nb * kMxBN;
+  const int m0 = mb * kMxBM;
 
   const int KT = K / kMxStepK;
   const int nbk = K / kMxBlock;  // scale bytes per row
@@ -325,7 +321,7 @@ int launch_gemm_mx_t(const uint8_t* slices, const uint8_t* xscale, int M, int K,
   if (st != 0) return st;
   const long tiles = (long)((N + kMxBN - 1) / kMxBN) * ((M + kMxBM - 1) / kMxBM);
   hipLaunchKernelGGL((gemm_mx_kernel<NS>), dim3((unsigned)tiles), dim3(kMxThreads), kLds, s, slices, xscale, M, K, N,
-                     packed, wscale, y);
+                     packed, wscale, y, gemm_group_rows());
   return check_launch("gemm_mx");
 }
 

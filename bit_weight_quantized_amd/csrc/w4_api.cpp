@@ -13,6 +13,8 @@
 
 #include "w4_internal.h"
 
+#include <cstdlib>
+
 namespace w4 {
 
 namespace {
@@ -79,6 +81,15 @@ int allow_dynamic_lds(const void* fn, int bytes, const char* what) {
   if (e != hipSuccess) return fail(W4_EHIP, "%s: cannot reserve %d bytes of LDS: %s", what, bytes, hipGetErrorString(e));
   done.insert({fn, dev, bytes});
   return W4_OK;
+}
+
+int gemm_group_rows() {
+  static const int gm = [] {
+    const char* e = std::getenv("W4_GEMM_GM");
+    const int v = e && *e ? std::atoi(e) : 4;
+    return v >= 1 && v <= 64 ? v : 4;
+  }();
+  return gm;
 }
 
 const uint32_t kNf4LevelBits[16] = {

@@ -80,6 +80,25 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
 }
 
+// Output tile (row block mb, column block nb) of workgroup b among tiles =
+// tiles_m x tiles_n.  Workgroups are dealt to the 8 XCDs round-robin; they are
+// renumbered so each XCD gets a contiguous run of tiles, and the run walks
+// groups of gm row blocks column block by column block: the workgroups that
+// run at once on one XCD share gm row blocks of activations and about
+// 32 / gm column blocks of weights in that XCD's L2 (gm = 1: one row block,
+// every weight block read once per tile).
+__device__ __forceinline__ void tile_of(int b, int tiles, int tiles_m, int tiles_n, int gm, int& mb, int& nb) {
+  const int xcd = b % 8, idx = b / 8;
+  const int per = tiles / 8, rem = tiles % 8;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int group = logical / (gm * tiles_n);
+  const int first = group * gm;
+  const int g = min(tiles_m - first, gm);
+  const int in = logical - group * gm * tiles_n;
+  mb = first + in % g;
+  nb = in / g;
+}
+
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }

@@ -40,6 +40,10 @@ int launch_gemv(const GemvPlan& plan, const uint16_t* x, int M, int K, int N,
                 const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
                 int G, int fmt, uint16_t* y, void* ws, hipStream_t s);
 
+// Row blocks per group in the matrix-core kernels' tile order (see tile_of;
+// W4_GEMM_GM overrides the default for sweeps).
+int gemm_group_rows();
+
 // fp16 GEMM: K slices over workgroups (1 when the grid already fills the
 // chip) and the fp32 partial workspace that takes ([S][M][N], 0 when S = 1).
 int gemm_split(int M, int K, int N);
