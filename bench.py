@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 matrix cores, published
 INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 matrix cores, published
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense fp4 matrix cores, published
 
 
 def parse():
@@ -133,6 +134,12 @@ def bench_gemm_prefill(w4, torch, reps):
     del w, codes
     x = torch.from_numpy(wl.make_activations(4, 0, M, K)).cuda()
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    # the same layer in MXFP4 (its own weights, quantized on the GPU)
+    wmx = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    mx_codes, mx_scale = w4.quantize_mx(wmx)
+    mx_packed = w4.pack_mx(mx_codes)
+    del wmx, mx_codes
+    ws_mx = torch.empty(w4.workspace_bytes(w4.OP_GEMM_MX, M, K, N, 32, 2), dtype=torch.uint8, device="cuda")
     ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 3), dtype=torch.uint8, device="cuda")
     flops = 2.0 * M * N * K
     paths = {
@@ -144,6 +151,8 @@ def bench_gemm_prefill(w4, torch, reps):
                        INT8_MFMA_PEAK_TOPS),
         "msd1": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 1, out=y, workspace=ws), 1, INT8_MFMA_PEAK_TOPS),
         "msd3": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 3, out=y, workspace=ws), 3, INT8_MFMA_PEAK_TOPS),
+        "mxfp4_2": (lambda: w4.gemm_mx(x, mx_packed, mx_scale, 2, out=y, workspace=ws_mx), 2, FP4_MFMA_PEAK_TFLOPS),
+        "mxfp4_1": (lambda: w4.gemm_mx(x, mx_packed, mx_scale, 1, out=y, workspace=ws_mx), 1, FP4_MFMA_PEAK_TFLOPS),
     }
     res = {}
     st = torch.cuda.Stream()
@@ -168,7 +177,9 @@ def bench_gemm_prefill(w4, torch, reps):
             "note": "fp16 paths against the dense fp16 MFMA peak; msdJ issues J int8 products per useful "
                     "multiply-add and is measured against the dense int8 peak; msd times include the "
                     "activation decomposition; msd2_fixed uses s2 = s1/254 and combines the two int32 "
-                    "products in integers",
+                    "products in integers; mxfp4_J: MXFP4 weights (the same distribution, own draw), the "
+                    "activations split into J MXFP4 slices, J block-scaled fp4 products per useful "
+                    "multiply-add against the dense fp4 peak, decomposition included",
             "paths": res}
 
 
