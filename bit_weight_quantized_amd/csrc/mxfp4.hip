@@ -22,6 +22,8 @@
 #include "w4_device.h"
 #include "w4_internal.h"
 
+#include <cstdlib>
+
 #pragma clang fp contract(off)
 
 namespace w4 {
@@ -156,26 +158,32 @@ __global__ __launch_bounds__(256) void decompose_mx_kernel(const uint16_t* __res
 }
 
 // ------------------------------------------------------------------ product
-// 128 tokens x 256 weight rows per workgroup, 8 waves side by side along N
-// (each 128 x 32: 8 x 2 products of 16 x 16 per slice), K step 128 (one
-// block-scaled product per tile pair), three stages of global -> LDS copies:
-//  * slice j's step tile: 128 rows x 64 bytes; 16-byte chunk c of row m sits
-//    at chunk c ^ ((m >> 2) & 3), so the 16 lanes reading one chunk column of
-//    16 rows hit 16 different bank groups;
+// Workgroups of 8 waves own (128 WM) tokens x 256 weight rows; the waves form
+// a WM x (8 / WM) grid, each 128 x (32 WM) (8 x 2 WM products of 16 x 16 per
+// slice), so each activation operand read from LDS serves 2 WM products.
+// WM = 2 halves the activation reads per product; WM = 1 makes twice as many,
+// smaller tiles (more even filling of the GPU).  K step 128 (one block-scaled product per tile pair),
+// three stages of global -> LDS copies:
+//  * slice j's step tile: 128 WM rows x 64 bytes; 16-byte chunk c of row m
+//    sits at chunk c ^ ((m >> 2) & 3), so the 16 lanes reading one chunk
+//    column of 16 rows hit 16 different bank groups;
 //  * the 16 weight tiles of the step (1 KB each, lane l's operand at 16 l);
 //  * the step's E8M0 bytes as 4-byte words: [slice][row] and [column], each
 //    word the row's (column's) four blocks of the step; a lane extracts its
 //    own block's byte.
 constexpr int kMxThreads = 512;
-constexpr int kMxBM = 128;
 constexpr int kMxBN = 256;
-constexpr int kMxA = kMxBM * 64;
 constexpr int kMxB = (kMxBN / 16) * 1024;
-constexpr int kMxSA = kMxBM * 4;
 constexpr int kMxSB = kMxBN * 4;
 constexpr int kMxStages = 3;
+template <int WM>
+constexpr int mx_bm() { return 128 * WM; }
+template <int NS, int WM>
+constexpr int mx_stage_bytes() { return NS * mx_bm<WM>() * 64 + kMxB + NS * mx_bm<WM>() * 4 + kMxSB; }
+// waves along M (measured at M = 2048, K = 5120, N = 25600: WM = 2 is faster
+// for one slice, 226 vs 286 us, and for two, 437 vs 450 us)
 template <int NS>
-constexpr int mx_stage_bytes() { return NS * kMxA + kMxB + NS * kMxSA + kMxSB; }
+constexpr int mx_wm() { return 2; }
 
 __device__ __forceinline__ f32x4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, f32x4 c) {
   const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
@@ -183,28 +191,33 @@ __device__ __forceinline__ f32x4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
-template <int NS>
+template <int NS, int WM>
 __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_mx_kernel(
     const uint8_t* __restrict__ slices, const uint8_t* __restrict__ xscale, int M, int K, int N,
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ wscale, uint16_t* __restrict__ y, int gm) {
-  constexpr int MT = 8, NT = 2;
-  constexpr int kStage = mx_stage_bytes<NS>();
-  constexpr int kOffB = NS * kMxA, kOffSA = kOffB + kMxB, kOffSB = kOffSA + NS * kMxSA;
-  constexpr int kScaleCopies = 2 * NS + 4;  // 64 rows or columns each
-  constexpr int kCopies = NS + 2 + 1;       // per wave per step
-  static_assert(kScaleCopies <= 8, "one scale copy per wave");
+  constexpr int BM = mx_bm<WM>();
+  constexpr int WN = 8 / WM;                // waves along N
+  constexpr int MT = 8, NT = 2 * WM;
+  constexpr int kA = BM * 64, kSA = BM * 4;
+  constexpr int kStage = mx_stage_bytes<NS, WM>();
+  constexpr int kOffB = NS * kA, kOffSA = kOffB + kMxB, kOffSB = kOffSA + NS * kSA;
+  constexpr int kScaleCopies = NS * (BM / 64) + 4;  // 64 rows or columns each
+  constexpr int kScW = (kScaleCopies + 7) / 8;      // per wave (the last repeat earlier ones)
+  constexpr int kCopies = NS * WM + 2 + kScW;       // per wave per step
+  static_assert(kCopies < 16, "copy count must fit the low vmcnt field");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wn / WN, wc = wn % WN;  // this wave: rows 128 wm .., columns 16 NT wc ..
   const int ln = lane % 16, jb = lane / 16;
 
   const int tiles_n = (N + kMxBN - 1) / kMxBN;
   int mb, nb;
-  tile_of(blockIdx.x, gridDim.x, (M + kMxBM - 1) / kMxBM, tiles_n, gm, mb, nb);
+  tile_of(blockIdx.x, gridDim.x, (M + BM - 1) / BM, tiles_n, gm, mb, nb);
   const int n0 = nb * kMxBN;
-  const int m0 = mb * kMxBM;
+  const int m0 = mb * BM;
 
   const int KT = K / kMxStepK;
   const int nbk = K / kMxBlock;  // scale bytes per row
@@ -219,32 +232,48 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
   const __amdgpu_buffer_rsrc_t wsr = make_rsrc(wscale, (uint32_t)((size_t)N * nbk));
 
-  // wave wn copies rows 16 wn .. 16 wn + 15 of each slice: lane l -> row
-  // 16 wn + l / 4, LDS chunk l % 4, which holds global chunk (l % 4) ^ ((l / 16) & 3)
-  const int arow = 16 * wn + lane / 4;
-  const uint32_t voff_a = (uint32_t)(m0 + arow) * (uint32_t)(K / 2) + (uint32_t)(((lane % 4) ^ ((lane / 16) & 3)) * 16);
+  // wave wn copies rows 16 WM wn + 16 i .. + 15 (i < WM) of each slice: lane l
+  // -> row + l / 4, LDS chunk l % 4, which holds global chunk (l % 4) ^ ((l / 16) & 3)
+  uint32_t voff_a[WM];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+    voff_a[i] = (uint32_t)(m0 + 16 * WM * wn + 16 * i + lane / 4) * (uint32_t)(K / 2) +
+                (uint32_t)(((lane % 4) ^ ((lane / 16) & 3)) * 16);
   uint32_t voff_b[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     voff_b[j] = (uint32_t)min(n0 / 16 + 2 * wn + j, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
-  // this wave's scale copy: c < 2 NS: slice c / 2, rows 64 (c % 2) + lane;
-  // otherwise columns 64 (c - 2 NS) + lane
-  const int sc = wn % kScaleCopies;
-  const bool sc_x = sc < 2 * NS;
-  const int sc_j = sc_x ? sc / 2 : 0;
-  const uint32_t voff_s = sc_x ? (uint32_t)(m0 + 64 * (sc % 2) + lane) * (uint32_t)nbk
-                               : (uint32_t)(n0 + 64 * (sc - 2 * NS) + lane) * (uint32_t)nbk;
-  const int sc_dst = sc_x ? kOffSA + sc_j * kMxSA + 64 * (sc % 2) * 4 : kOffSB + 64 * (sc - 2 * NS) * 4;
+  // scale copies: c < NS BM/64: slice c / (BM/64), rows 64 (c % (BM/64)) +
+  // lane; otherwise columns 64 (c - NS BM/64) + lane
+  constexpr int kRowSc = BM / 64;
+  uint32_t voff_s[kScW];
+  int sc_dst[kScW];
+  bool sc_x[kScW];
+  int sc_j[kScW];
+#pragma unroll
+  for (int i = 0; i < kScW; ++i) {
+    const int c = (wn * kScW + i) % kScaleCopies;
+    sc_x[i] = c < NS * kRowSc;
+    sc_j[i] = sc_x[i] ? c / kRowSc : 0;
+    voff_s[i] = sc_x[i] ? (uint32_t)(m0 + 64 * (c % kRowSc) + lane) * (uint32_t)nbk
+                        : (uint32_t)(n0 + 64 * (c - NS * kRowSc) + lane) * (uint32_t)nbk;
+    sc_dst[i] = sc_x[i] ? kOffSA + sc_j[i] * kSA + 64 * (c % kRowSc) * 4 : kOffSB + 64 * (c - NS * kRowSc) * 4;
+  }
 
   auto stage = [&](int kt) { return smem + (kt % kMxStages) * kStage; };
   auto issue_step = [&](int kt) {
     unsigned char* st = stage(kt);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) copy16_to_lds(ar(j), voff_a, (uint32_t)kt * 64, st + j * kMxA + 16 * wn * 64);
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        copy16_to_lds(ar(j), voff_a[i], (uint32_t)kt * 64, st + j * kA + (16 * WM * wn + 16 * i) * 64);
 #pragma unroll
     for (int j = 0; j < 2; ++j) copy16_to_lds(wr, voff_b[j], (uint32_t)kt * 1024, st + kOffB + (2 * wn + j) * 1024);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_x ? sr(sc_j) : wsr, (lds_void*)(st + sc_dst), 4, voff_s,
-                                             (uint32_t)kt * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kScW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_x[i] ? sr(sc_j[i]) : wsr, (lds_void*)(st + sc_dst[i]), 4, voff_s[i],
+                                               (uint32_t)kt * 4, 0, 0);
   };
   auto wait_all_but_one_step = [&]() { __builtin_amdgcn_s_waitcnt(kCopies | (0x7 << 4) | (0xF << 8)); };
 
@@ -275,18 +304,18 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     uint32_t sb[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      Bv[nt] = *reinterpret_cast<const u32x4*>(cur + kOffB + (2 * wn + nt) * 1024 + lane * 16);
-      sb[nt] = __builtin_amdgcn_ubfe(*reinterpret_cast<const uint32_t*>(cur + kOffSB + (wn * 32 + nt * 16 + ln) * 4),
-                                     shift, 8);
+      Bv[nt] = *reinterpret_cast<const u32x4*>(cur + kOffB + (NT * wc + nt) * 1024 + lane * 16);
+      sb[nt] = __builtin_amdgcn_ubfe(
+          *reinterpret_cast<const uint32_t*>(cur + kOffSB + (wc * 16 * NT + nt * 16 + ln) * 4), shift, 8);
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      const int row = wm * 128 + mt * 16 + ln;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const u32x4 A = *reinterpret_cast<const u32x4*>(cur + j * kMxA + (mt * 16 + ln) * 64 + a_chunk);
+        const u32x4 A = *reinterpret_cast<const u32x4*>(cur + j * kA + row * 64 + a_chunk);
         const uint32_t sa =
-            __builtin_amdgcn_ubfe(*reinterpret_cast<const uint32_t*>(cur + kOffSA + j * kMxSA + (mt * 16 + ln) * 4),
-                                  shift, 8);
+            __builtin_amdgcn_ubfe(*reinterpret_cast<const uint32_t*>(cur + kOffSA + j * kSA + row * 4), shift, 8);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) C[mt][nt] = mfma_fp4(A, sa, Bv[nt], sb[nt], C[mt][nt]);
       }
@@ -303,26 +332,40 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + mt * 16 + 4 * jb + i;
+      const int m = m0 + wm * 128 + mt * 16 + 4 * jb + i;
       if (m >= M) continue;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int n = n0 + wn * 32 + nt * 16 + ln;
+        const int n = n0 + wc * 16 * NT + nt * 16 + ln;
         if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
       }
     }
 }
 
+template <int NS, int WM>
+int launch_gemm_mx_w(const uint8_t* slices, const uint8_t* xscale, int M, int K, int N, const uint8_t* packed,
+                     const uint8_t* wscale, uint16_t* y, hipStream_t s) {
+  constexpr int kLds = kMxStages * mx_stage_bytes<NS, WM>();
+  static_assert(kLds <= 160 * 1024, "LDS");
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_mx_kernel<NS, WM>), kLds, "w4_gemm_mx");
+  if (st != 0) return st;
+  const long tiles = (long)((N + kMxBN - 1) / kMxBN) * ((M + mx_bm<WM>() - 1) / mx_bm<WM>());
+  hipLaunchKernelGGL((gemm_mx_kernel<NS, WM>), dim3((unsigned)tiles), dim3(kMxThreads), kLds, s, slices, xscale, M, K,
+                     N, packed, wscale, y, gemm_group_rows());
+  return check_launch("gemm_mx");
+}
+
+// W4_MX_WM (1 or 2) overrides the waves along M for sweeps
 template <int NS>
 int launch_gemm_mx_t(const uint8_t* slices, const uint8_t* xscale, int M, int K, int N, const uint8_t* packed,
                      const uint8_t* wscale, uint16_t* y, hipStream_t s) {
-  constexpr int kLds = kMxStages * mx_stage_bytes<NS>();
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_mx_kernel<NS>), kLds, "w4_gemm_mx");
-  if (st != 0) return st;
-  const long tiles = (long)((N + kMxBN - 1) / kMxBN) * ((M + kMxBM - 1) / kMxBM);
-  hipLaunchKernelGGL((gemm_mx_kernel<NS>), dim3((unsigned)tiles), dim3(kMxThreads), kLds, s, slices, xscale, M, K, N,
-                     packed, wscale, y, gemm_group_rows());
-  return check_launch("gemm_mx");
+  static const int wm = [] {
+    const char* e = std::getenv("W4_MX_WM");
+    return e && (*e == '1' || *e == '2') ? *e - '0' : 0;
+  }();
+  if (wm == 1 || (wm == 0 && mx_wm<NS>() == 1))
+    return launch_gemm_mx_w<NS, 1>(slices, xscale, M, K, N, packed, wscale, y, s);
+  return launch_gemm_mx_w<NS, 2>(slices, xscale, M, K, N, packed, wscale, y, s);
 }
 
 inline unsigned blocks_for(long threads) { return (unsigned)((threads + 255) / 256); }
