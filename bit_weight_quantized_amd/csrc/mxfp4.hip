@@ -9,8 +9,8 @@
 // 4, 6) and one E8M0 scale 2^(s - 127) per 32 consecutive K positions.  Scale
 // rule (a reading; the pages give none): the smallest e with amax <= 6 * 2^e,
 // so no element saturates.  Rounding to E2M1 is to nearest, ties to the even
-// mantissa; a zero result carries no sign.  Every decision is taken in fp64,
-// where the scaled values and the residuals are exact.
+// mantissa; a zero result carries no sign.  The scaled values and residuals
+// are exact (see below), so every decision is the exact one.
 //
 // gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 with fp4 operands takes, per
 // lane l, 16 bytes of A (row l % 16, K positions 32 (l / 16) .. + 31, two per
@@ -35,37 +35,46 @@ constexpr int kMxStepK = 128;
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- encoding
-__device__ __forceinline__ int mx_exponent(double amax) {
-  if (!(amax > 0.0)) return -127;
-  int g = (int)ceil(log2(amax / 6.0));
-  if (6.0 * ldexp(1.0, g) < amax) ++g;        // the guess is within one of the
-  if (6.0 * ldexp(1.0, g - 1) >= amax) --g;   // answer; fix it with exact tests
-  return min(max(g, -127), 127);
+// All arithmetic below is exact in fp32 for fp16 or fp32 inputs and up to two
+// passes: scaling by a power of two is exact (no overflow: |v| / 2^e <= 6;
+// no underflow for the values that occur), and a first-pass residual
+// v - q 2^e needs at most 13 significant bits (|v| >= 2^(e-2) when q != 0,
+// so v's last bit is at least 2^(e-12), and |v - q 2^e| <= 2^e).  The
+// decisions therefore match an fp64 evaluation bit for bit.
+
+// smallest e with amax <= 6 * 2^e: with amax = f 2^p, f in [0.5, 1), it is
+// p - 3 when f <= 0.75 and p - 2 otherwise
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int p;
+  const float f = frexpf(amax, &p);
+  const int e = f <= 0.75f ? p - 3 : p - 2;
+  return min(max(e, -127), 127);
 }
 
-__device__ __forceinline__ int e2m1_code(double t) {
-  const double a = fmin(fabs(t), 6.0);
-  const int c = a <= 0.25 ? 0 : a < 0.75 ? 1 : a <= 1.25 ? 2 : a < 1.75 ? 3
-              : a <= 2.5 ? 4 : a < 3.5 ? 5 : a <= 5.0 ? 6 : 7;
-  return (t < 0.0 && c != 0) ? (c | 8) : c;
+__device__ __forceinline__ int e2m1_code(float t) {
+  const float a = fminf(fabsf(t), 6.f);
+  const int c = a <= 0.25f ? 0 : a < 0.75f ? 1 : a <= 1.25f ? 2 : a < 1.75f ? 3
+              : a <= 2.5f ? 4 : a < 3.5f ? 5 : a <= 5.f ? 6 : 7;
+  return (t < 0.f && c != 0) ? (c | 8) : c;
 }
 
-__device__ __forceinline__ double e2m1_mag(int c) {
+__device__ __forceinline__ float e2m1_mag(int c) {
   const int e = (c >> 1) & 3, m = c & 1;
-  return e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return e == 0 ? 0.5f * m : ldexpf(1.f + 0.5f * m, e - 1);
 }
 
 // one 32-element block: codes and exponent of v (v is left as the residual)
-__device__ __forceinline__ int mx_block(double (&v)[kMxBlock], uint8_t (&code)[kMxBlock]) {
-  double amax = 0.0;
+__device__ __forceinline__ int mx_block(float (&v)[kMxBlock], uint8_t (&code)[kMxBlock]) {
+  float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMxBlock; ++i) amax = fmax(amax, fabs(v[i]));
+  for (int i = 0; i < kMxBlock; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int e = mx_exponent(amax);
 #pragma unroll
   for (int i = 0; i < kMxBlock; ++i) {
-    const int c = e2m1_code(ldexp(v[i], -e));
+    const int c = e2m1_code(ldexpf(v[i], -e));
     code[i] = (uint8_t)c;
-    const double q = ldexp(e2m1_mag(c & 7), e);
+    const float q = ldexpf(e2m1_mag(c & 7), e);
     v[i] = v[i] - ((c & 8) ? -q : q);
   }
   return e;
@@ -92,9 +101,9 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const float* __restric
   if (t >= (long)N * nb) return;
   const long n = t / nb, b = t % nb;
   const float* src = wt + n * K + b * kMxBlock;
-  double v[kMxBlock];
+  float v[kMxBlock];
 #pragma unroll
-  for (int i = 0; i < kMxBlock; ++i) v[i] = (double)src[i];
+  for (int i = 0; i < kMxBlock; ++i) v[i] = src[i];
   uint8_t c[kMxBlock];
   const int e = mx_block(v, c);
   uint8_t* dst = codes + n * K + b * kMxBlock;
@@ -134,14 +143,14 @@ __global__ __launch_bounds__(256) void decompose_mx_kernel(const uint16_t* __res
   if (t >= (long)M * nb) return;
   const long m = t / nb, b = t % nb;
   const u32x4* src = reinterpret_cast<const u32x4*>(x + m * K + b * kMxBlock);
-  double v[kMxBlock];
+  float v[kMxBlock];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const u32x4 w = src[q];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[8 * q + 2 * i] = (double)half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
-      v[8 * q + 2 * i + 1] = (double)half_bits_to_float((uint16_t)(w[i] >> 16));
+      v[8 * q + 2 * i] = half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
+      v[8 * q + 2 * i + 1] = half_bits_to_float((uint16_t)(w[i] >> 16));
     }
   }
 #pragma unroll
