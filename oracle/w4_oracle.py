@@ -578,6 +578,81 @@ def unpack_mx(packed, N: int, K: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Multi-Scale Dequant for the KV cache in decode attention  ([MSD] Abstract:
+# the KV cache is quantized and the activations on the other side of each
+# product -- the queries for the scores, the attention weights for the values
+# -- are decomposed instead of dequantizing the cache)
+# --------------------------------------------------------------------------
+ATTN_CHUNK = 256  # tokens per block of attention weights decomposed together
+
+
+def attention_ref(q, k_deq, v_deq, n_kv: int) -> np.ndarray:
+    """Plain decode attention in fp64 (one query token per head).
+
+    q [Hq][d]; k_deq, v_deq [Hkv][L][d]; query head g attends with key/value
+    head g // (Hq / Hkv) (grouped-query attention); scores scaled by 1/sqrt(d),
+    softmax over the L positions."""
+    q = np.asarray(q).astype(np.float64)
+    Hq, d = q.shape
+    G = Hq // n_kv
+    out = np.zeros((Hq, d))
+    for g in range(Hq):
+        h = g // G
+        s = np.asarray(k_deq[h], dtype=np.float64) @ q[g] / np.sqrt(d)
+        p = np.exp(s - s.max())
+        out[g] = (p / p.sum()) @ np.asarray(v_deq[h], dtype=np.float64)
+    return out
+
+
+def msd_attention(q, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, n_kv: int, chunk: int = ATTN_CHUNK):
+    """Decode attention with an INT4 KV cache and Multi-Scale Dequant on both
+    products, in fp64 with exact integer products.
+
+    READING (the page names the idea and its traffic benefit, not the steps):
+    * K and V are INT4 asymmetric with one scale and zero point per token and
+      head (a group spans the head dimension d): k[t] = sK[t] (qK[t] - zK[t]).
+    * Scores: the queries of each key/value head are split into two int8
+      slices per query head (``decompose_activations``);
+      D_j[g, t] = sum_d A_j[g, d] (qK[t, d] - zK[t]) exactly, and
+      score[g, t] = sK[t] sum_j s_j[g] D_j[g, t] / sqrt(d).
+    * Softmax: p = exp(score - max_t score), l = sum_t p.
+    * Values: the per-token value scale is folded into the weights,
+      w[g, t] = p[g, t] sV[t]; each block of ``chunk`` positions of w is split
+      into two int8 slices per query head (same decomposition), and
+      E_j[g, n] = sum_t B_j[g, t] (qV[t, n] - zV[t]) exactly;
+      o[g, n] = sum_blocks sum_j r_j[g] E_j[g, n] / l[g].
+
+    k_codes, v_codes [Hkv][L][d] uint8; scales, zeros [Hkv][L] fp16.
+    Returns o [Hq][d] fp64."""
+    q = np.asarray(q)
+    Hq, d = q.shape
+    G = Hq // n_kv
+    L = np.asarray(k_codes).shape[1]
+    out = np.zeros((Hq, d))
+    for h in range(n_kv):
+        rows = slice(h * G, (h + 1) * G)
+        A, S = decompose_activations(q[rows], 2)                      # [2][G][d], [2][G]
+        kz = np.asarray(k_zero[h], dtype=np.float16).astype(np.int64)
+        qk = np.asarray(k_codes[h]).astype(np.int64) - kz[:, None]    # [L][d]
+        D = np.einsum("jgd,td->jgt", A.astype(np.int64), qk)          # exact
+        sK = np.asarray(k_scale[h], dtype=np.float16).astype(np.float64)
+        score = sK[None, :] * np.einsum("jg,jgt->gt", S.astype(np.float64), D.astype(np.float64)) / np.sqrt(d)
+        p = np.exp(score - score.max(axis=1, keepdims=True))
+        l = p.sum(axis=1)
+        sV = np.asarray(v_scale[h], dtype=np.float16).astype(np.float64)
+        w = p * sV[None, :]
+        vz = np.asarray(v_zero[h], dtype=np.float16).astype(np.int64)
+        qv = np.asarray(v_codes[h]).astype(np.int64) - vz[:, None]    # [L][d]
+        o = np.zeros((G, d))
+        for c0 in range(0, L, chunk):
+            Bc, R = decompose_activations(w[:, c0:c0 + chunk], 2)     # [2][G][chunk], [2][G]
+            E = np.einsum("jgt,tn->jgn", Bc.astype(np.int64), qv[c0:c0 + chunk])
+            o += np.einsum("jg,jgn->gn", R.astype(np.float64), E.astype(np.float64))
+        out[rows] = o / l[:, None]
+    return out
+
+
+# --------------------------------------------------------------------------
 # residual compensation of salient channels  ([DecDEC] Abstract)
 # --------------------------------------------------------------------------
 def residual_fp16(wt, w_deq) -> np.ndarray:

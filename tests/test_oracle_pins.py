@@ -675,6 +675,62 @@ def test_mx_matmul_exact_and_pack_layout():
     assert np.array_equal(o.unpack_mx(p, 16, 128), wc)
 
 
+# ------------------------------------------------------------- KV-cache MSD
+def _kv_case(seed, Hq, Hkv, L, d=128):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((Hq, d)).astype(np.float16)
+    k = rng.standard_normal((Hkv, L, d)).astype(np.float32)
+    v = rng.standard_normal((Hkv, L, d)).astype(np.float32)
+    kq = [o.quantize_int4_asym(k[h], d) for h in range(Hkv)]
+    vq = [o.quantize_int4_asym(v[h], d) for h in range(Hkv)]
+    kc = np.stack([a[0] for a in kq]); ks = np.stack([a[1][:, 0] for a in kq]); kz = np.stack([a[2][:, 0] for a in kq])
+    vc = np.stack([a[0] for a in vq]); vs = np.stack([a[1][:, 0] for a in vq]); vz = np.stack([a[2][:, 0] for a in vq])
+    kd = np.stack([o.dequant_int4_asym(kc[h], ks[h][:, None], kz[h][:, None], d) for h in range(Hkv)])
+    vd = np.stack([o.dequant_int4_asym(vc[h], vs[h][:, None], vz[h][:, None], d) for h in range(Hkv)])
+    return q, (kc, ks, kz), (vc, vs, vz), kd, vd
+
+
+def test_attention_ref_brute_force_and_special_cases():
+    q, _, _, kd, vd = _kv_case(21, 4, 2, 5, d=128)
+    y = o.attention_ref(q, kd, vd, 2)
+    for g in range(4):
+        h = g // 2  # query heads 0, 1 -> kv head 0; 2, 3 -> kv head 1
+        sc = [sum(float(q[g, i]) * kd[h, t, i] for i in range(128)) / 128 ** 0.5 for t in range(5)]
+        mx = max(sc)
+        e = [np.exp(x - mx) for x in sc]
+        want = [sum(e[t] * vd[h, t, n] for t in range(5)) / sum(e) for n in range(128)]
+        assert np.allclose(y[g], want, rtol=1e-12, atol=1e-12)
+    # one position: the output is that value; equal keys: the mean of the values
+    y1 = o.attention_ref(q, kd[:, :1], vd[:, :1], 2)
+    assert np.allclose(y1[0], vd[0, 0]) and np.allclose(y1[3], vd[1, 0])
+    k2 = np.repeat(kd[:, :1], 2, axis=1)
+    y2 = o.attention_ref(q, k2, vd[:, :2], 2)
+    assert np.allclose(y2[1], vd[0, :2].mean(axis=0))
+    # planted: the wrong head grouping (g mod Hkv) changes the result
+    bad = np.stack([o.attention_ref(q[g:g + 1], kd[g % 2:g % 2 + 1], vd[g % 2:g % 2 + 1], 1)[0] for g in range(4)])
+    assert not np.allclose(bad, y, rtol=1e-6)
+
+
+def test_msd_attention_integer_scores_and_error():
+    q, K, V, kd, vd = _kv_case(22, 8, 2, 512)
+    y = o.msd_attention(q, *K, *V, 2)
+    y_ref = o.attention_ref(q, kd, vd, 2)
+    # two int8 slices on both sides: ~16 effective bits each
+    assert o.max_row_rel_l2(y, y_ref) < 5e-4
+    # the score products are exact integers (brute force on a few entries)
+    A, S = o.decompose_activations(q[:4], 2)
+    kc, ks, kz = K
+    for j in range(2):
+        for g in (0, 3):
+            for t in (0, 77, 511):
+                want = sum(int(A[j, g, i]) * (int(kc[0, t, i]) - int(kz[0, t])) for i in range(128))
+                got = int(np.einsum("d,d->", A[j, g].astype(np.int64), kc[0, t].astype(np.int64) - int(kz[0, t])))
+                assert got == want
+    # planted: dropping the value zero points is far off
+    y_bad = o.msd_attention(q, *K, V[0], V[1], np.zeros_like(V[2]), 2)
+    assert o.max_row_rel_l2(y_bad, y_ref) > 1e-2
+
+
 # ------------------------------------------------------- residual compensation
 def test_salient_channels_hand_example():
     x = np.array([[0.5, -3.0, 2.0, 3.0, 0.0, 1.0],
