@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
     "lib", "lib_path", "quantize", "pack", "gemv", "gemm", "gemm_decomp", "gemm_decomp_fixed",
-    "salient_select", "residual_correct", "quantize_mx", "pack_mx", "gemm_mx",
+    "salient_select", "residual_correct", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
     "workspace_bytes", "nf4_levels", "version",
 ]
 
@@ -28,7 +28,7 @@ INT4_ASYM = 0
 NF4 = 1
 DQ_F16 = 0
 POSTSCALE = 1
-OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP, OP_GEMM_MX = range(6)
+OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP, OP_GEMM_MX, OP_ATTN_MSD = range(7)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libw4.so")
@@ -68,6 +68,7 @@ def lib():
         L.w4_quantize_mx.argtypes = [_p, _i, _i, _p, _p, _p]
         L.w4_pack_mx.argtypes = [_p, _i, _i, _p, _p]
         L.w4_gemm_mx.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _sz, _p]
+        L.w4_attn_decode_msd.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_residual_correct.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p]
         L.w4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
         L.w4_workspace_bytes.restype = _sz
@@ -79,6 +80,7 @@ def lib():
         L.w4_version.restype = ctypes.c_char_p
         for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
                    "w4_salient_select", "w4_residual_correct", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
+                   "w4_attn_decode_msd",
                    "w4_nf4_levels"):
             getattr(L, fn).restype = _i
         _lib = L
@@ -289,4 +291,21 @@ def gemm_mx(x, packed, scale, nslices: int = 2, *, out=None, slices_out=None, sc
     if slices_out is None and scales_out is None:
         return out
     return out, slices_out, scales_out
+
+
+def attn_decode_msd(q, k_packed, k_scale, k_zero, vt_packed, v_scale, v_zero, n_kv: int, *, out=None,
+                    workspace=None, stream=None):
+    """Decode attention over an INT4 KV cache with MSD on both products.
+    q fp16 [B][Hq][128]; caches as documented for w4_attn_decode_msd
+    (k_scale [B][Hkv][L] etc.).  Returns out fp16 [B][Hq][128]."""
+    _dev(q, torch.float16, "q")
+    B, Hq, d = q.shape
+    L = k_scale.shape[-1]
+    out = torch.empty_like(q) if out is None else out
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(OP_ATTN_MSD, B, Hq, L, 0, 0), dtype=torch.uint8, device=q.device)
+    _check("w4_attn_decode_msd", lib().w4_attn_decode_msd(
+        _ptr(q), B, Hq, n_kv, L, d, _ptr(k_packed), _ptr(k_scale), _ptr(k_zero), _ptr(vt_packed), _ptr(v_scale),
+        _ptr(v_zero), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
 

@@ -292,6 +292,30 @@ int w4_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
   return launch_gemm_mx(x, M, K, N, packed, scale, nslices, y, slices_out, scales_out, ws, (hipStream_t)stream);
 }
 
+int w4_attn_decode_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, int d, const uint8_t* k_packed,
+                       const uint16_t* k_scale, const uint16_t* k_zero, const uint8_t* vt_packed,
+                       const uint16_t* v_scale, const uint16_t* v_zero, uint16_t* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_last_error[0] = '\0';
+  if (d != 128) return fail(W4_EUNSUPPORTED, "w4_attn_decode_msd: head dimension must be 128 (got %d)", d);
+  if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || Hq / Hkv > 16)
+    return fail(W4_EINVAL, "w4_attn_decode_msd: need B >= 1 and Hq a multiple of Hkv with Hq/Hkv <= 16 (got B=%d Hq=%d Hkv=%d)",
+                B, Hq, Hkv);
+  if (L < 256 || L % 256) return fail(W4_EINVAL, "w4_attn_decode_msd: L must be a positive multiple of 256 (got %d)", L);
+  if (!q || !k_packed || !k_scale || !k_zero || !vt_packed || !v_scale || !v_zero || !out)
+    return fail(W4_EINVAL, "w4_attn_decode_msd: null operand");
+  if (!aligned16(q) || !aligned16(k_packed) || !aligned16(vt_packed) || (reinterpret_cast<uintptr_t>(k_scale) & 1u) ||
+      (reinterpret_cast<uintptr_t>(k_zero) & 1u) || (reinterpret_cast<uintptr_t>(v_scale) & 1u) ||
+      (reinterpret_cast<uintptr_t>(v_zero) & 1u) || (reinterpret_cast<uintptr_t>(out) & 1u))
+    return fail(W4_EINVAL, "w4_attn_decode_msd: q and the packed caches must be 16-byte aligned, fp16 arrays 2-byte");
+  const size_t need = attn_workspace_bytes(B, Hq, L);
+  if (!ws || ws_bytes < need)
+    return fail(W4_EWORKSPACE, "w4_attn_decode_msd: workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  if (!aligned16(ws)) return fail(W4_EINVAL, "w4_attn_decode_msd: workspace must be 16-byte aligned");
+  return launch_attn_msd(q, B, Hq, Hkv, L, k_packed, k_scale, k_zero, vt_packed, v_scale, v_zero, out, ws,
+                         (hipStream_t)stream);
+}
+
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
   switch (op) {
     case W4_OP_QUANTIZE:
@@ -303,6 +327,9 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
     case W4_OP_GEMV:
       if (M < 1 || M > 32 || K < 1 || N < 1 || (G != 64 && G != 128) || K % G || K % 128) return 0;
       return plan_gemv(M, K, N, G, fmt_or_mode == W4_NF4 ? W4_NF4 : W4_INT4_ASYM).ws_bytes;
+    case W4_OP_ATTN_MSD:  // M = batch, K = query heads, N = positions
+      if (M < 1 || K < 1 || N < 256 || N % 256) return 0;
+      return attn_workspace_bytes(M, K, N);
     case W4_OP_GEMM_MX:
       if (M < 1 || K < 128 || K % 128 || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
       return mx_workspace_bytes(M, K, fmt_or_mode);

@@ -89,6 +89,14 @@ size_t mx_workspace_bytes(int M, int K, int nslices);
 int launch_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint8_t* wscale, int nslices,
                    uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, hipStream_t s);
 
+// Decode attention over an INT4 KV cache with MSD on both products (head
+// dimension 128, L % 256 == 0, Hq / Hkv <= 16); workspace: query slices and
+// scales, then per-chunk partial outputs and (max, sum).
+size_t attn_workspace_bytes(int B, int Hq, int L);
+int launch_attn_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, const uint8_t* kp, const uint16_t* ks,
+                    const uint16_t* kz, const uint8_t* vtp, const uint16_t* vs, const uint16_t* vz, uint16_t* out,
+                    void* ws, hipStream_t s);
+
 // The 16 NF4 levels as fp32 bit patterns (host copy).
 extern const uint32_t kNf4LevelBits[16];
 

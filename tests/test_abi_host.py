@@ -169,6 +169,20 @@ def test_mx_argument_errors(L):
     assert L.w4_workspace_bytes(5, 4, 256, 32, 32, 3) == 0
 
 
+def test_attn_argument_errors(L):
+    def a(B=1, Hq=8, Hkv=1, Lp=256, d=128, ws=None, wsb=0, q=FAKE):
+        return L.w4_attn_decode_msd(q, B, Hq, Hkv, Lp, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert a(d=64) == W4_EUNSUPPORTED
+    assert a(Hq=8, Hkv=3) == W4_EINVAL
+    assert a(Hq=34, Hkv=2) == W4_EINVAL   # 17 query heads per kv head
+    assert a(Lp=300) == W4_EINVAL
+    assert a(q=None) == W4_EINVAL
+    assert a() == W4_EWORKSPACE
+    need = L.w4_workspace_bytes(6, 1, 8, 256, 0, 0)
+    assert need > 8 * 128 * 4  # at least the partial outputs
+    assert a(ws=FAKE, wsb=need - 1) == W4_EWORKSPACE
+
+
 def test_quantize_and_pack_argument_errors(L):
     assert L.w4_quantize(FAKE, 100, 16, 64, 0, FAKE, FAKE, FAKE, None) == W4_EINVAL
     assert L.w4_quantize(FAKE, 128, 16, 64, 1, FAKE, FAKE, FAKE, None) == W4_EINVAL  # NF4 + zero
