@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="no GPU: print a markdown summary of rocprofv3 CSV output (kernel_stats or "
                          "counter_collection files)")
+    ap.add_argument("--no-attention", dest="attention", action="store_false",
+                    help="skip the KV-cache attention timing")
     ap.add_argument("--no-residual", dest="residual", action="store_false",
                     help="skip the residual-compensation timing")
     ap.add_argument("--gemm-reps", type=int, default=20,
@@ -230,6 +232,48 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
     return {"workload": "decode_gemv_k8192_n8192_m1_int4_g128 + residual of k salient channels",
             "residual": "fp16 [K][N] in pinned host memory, read by the kernel over the host link",
             "host_link_peak_GBps": HOST_LINK_PEAK_GBS, "per_k": res}
+
+
+def bench_attention(w4, torch, stream, reps=20):
+    """Decode attention over an INT4 KV cache with Multi-Scale Dequant on both
+    products, for a 70B-shaped layer: batch 8, 64 query heads over 8 key/value
+    heads of dimension 128, 8192 cached positions.  The caches are seeded
+    normal values quantized on the GPU (w4_quantize per token, w4_pack; V
+    transposed first).  Timed as HIP-graph replays on the launch stream;
+    rate = cache bytes read (packed K and V plus their fp16 scales and zero
+    points) per second, against the 8 TB/s HBM peak; the fp16 cache of the
+    same layer would be the bytes of `fp16_cache_bytes`."""
+    B, Hq, Hkv, L, D = 8, 64, 8, 8192, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(60000)
+    rows = B * Hkv * L
+    k = torch.randn((rows, D), generator=gen, device="cuda")
+    kc, ks, kz = w4.quantize(k, D, w4.INT4_ASYM)
+    kp = w4.pack(kc)
+    del k, kc
+    v = torch.randn((rows, D), generator=gen, device="cuda")
+    vc, vs, vz = w4.quantize(v, D, w4.INT4_ASYM)
+    del v
+    vt = vc.view(B * Hkv, L, D).transpose(1, 2).contiguous().view(B * Hkv * D, L)
+    vp = w4.pack(vt)
+    del vc, vt
+    q = torch.randn((B, Hq, D), generator=gen, device="cuda").half()
+    out = torch.empty_like(q)
+    ws = torch.empty(w4.workspace_bytes(w4.OP_ATTN_MSD, B, Hq, L, 0, 0), dtype=torch.uint8, device="cuda")
+    ks, kz, vs, vz = (t.view(B, Hkv, L) for t in (ks, kz, vs, vz))
+    call = lambda: w4.attn_decode_msd(q, kp, ks, kz, vp, vs, vz, Hkv, out=out, workspace=ws)
+    g = graph_of(torch, stream, [call] * reps)
+    time_replays(torch, stream, g, 1)
+    us = time_replays(torch, stream, g, 4) * 1e3 / (4 * reps)
+    del g
+    cache = B * Hkv * L * (D // 2 * 2 + 4 * 2)  # packed K and V, fp16 scale and zero of each
+    fp16 = B * Hkv * L * D * 2 * 2
+    rate = cache / (us * 1e-6) / 1e9
+    return {"workload": "decode_attention_b8_hq64_hkv8_d128_l8192_int4_kv",
+            "us_per_call": round(us, 2), "cache_bytes": cache, "fp16_cache_bytes": fp16,
+            "traffic_ratio_vs_fp16": round(fp16 / cache, 2), "GBps": round(rate, 1),
+            "hbm_frac": round(rate / HBM_PEAK_GBS, 4),
+            "note": "time includes the query decomposition and the chunk combination"}
 
 
 GEMV_SOURCE = os.path.join(ROOT, "bit_weight_quantized_amd", "csrc", "gemv.hip")
@@ -469,6 +513,12 @@ def main():
         traffic = round(sum(traffic_rows[p["variant"]] for p in per) / len(per))
 
     gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
+    attn = None
+    if args.attention:
+        try:
+            attn = bench_attention(w4, torch, stream)
+        except Exception as e:  # reported, never fatal to the headline line
+            attn = {"error": f"{type(e).__name__}: {e}"}
     resid = None
     if args.residual:
         m1 = next(p for p in per if p["variant"] == variant_name(w4.INT4_ASYM, 1))
@@ -510,6 +560,7 @@ def main():
         "per_launch": per,
         "gemm_prefill": gemm,
         "residual_compensation": resid,
+        "attention_kv_msd": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
