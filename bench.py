@@ -50,6 +50,8 @@ def parse():
                     help="no GPU: from the counter_collection CSVs of two --profile-pass runs (rocprofv3 "
                          "--pmc FETCH_SIZE, then --pmc WRITE_SIZE) print the HBM traffic summary of the GEMV "
                          "variants, calibrated on the plain copy")
+    ap.add_argument("--kernels", metavar="REGEX", default=None,
+                    help="with --summarize: only kernels whose name matches")
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="no GPU: print a markdown summary of rocprofv3 CSV output (kernel_stats or "
                          "counter_collection files)")
@@ -348,11 +350,14 @@ def time_replays(torch, stream, graph, replays):
     return start.elapsed_time(end)
 
 
-def summarize(paths):
+def summarize(paths, pattern=None):
     """Markdown tables from rocprofv3 CSV files: kernel statistics, or counter
-    values averaged per dispatch and grouped by kernel and launch geometry."""
+    values averaged per dispatch and grouped by kernel and launch geometry;
+    with `pattern`, only kernels whose name matches that regular expression."""
     import csv
     import collections
+    import re
+    keep = (lambda name: re.search(pattern, name) is not None) if pattern else (lambda name: True)
     for path in paths:
         with open(path, newline="") as f:
             rows = list(csv.DictReader(f))
@@ -364,12 +369,16 @@ def summarize(paths):
             print("| kernel | calls | average (us) | min (us) | max (us) |")
             print("|---|---|---|---|---|")
             for r in rows:
+                if not keep(r[cols["name"]]):
+                    continue
                 print(f"| `{short_kernel(r[cols['name']])}` | {r[cols['calls']]} | "
                       f"{float(r[cols['averagens']]) / 1e3:.2f} | {float(r[cols['minns']]) / 1e3:.2f} | "
                       f"{float(r[cols['maxns']]) / 1e3:.2f} |")
         elif "counter_name" in cols:
             agg = collections.defaultdict(list)
             for r in rows:
+                if not keep(r[cols["kernel_name"]]):
+                    continue
                 key = (short_kernel(r[cols["kernel_name"]]), r[cols["grid_size"]], r[cols["workgroup_size"]],
                        r[cols["counter_name"]])
                 agg[key].append(float(r[cols["counter_value"]]))
@@ -425,7 +434,7 @@ def short_kernel(name):
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize)
+        summarize(args.summarize, args.kernels)
         return
     if args.traffic:
         traffic_summary(*args.traffic)
