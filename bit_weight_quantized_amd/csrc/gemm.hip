@@ -315,6 +315,9 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
         load_a(cur, An, w + 1);
         unpack(Bn, w + 1);
       }
+      // keep the next word's reads ahead of this word's products (the
+      // scheduler would otherwise sink each read to just before its use)
+      __builtin_amdgcn_sched_barrier(0);
       products(A, Bc, w);
       if constexpr (PATH == 1) {
         if ((w % WPG) == WPG - 1) scale_group(w / WPG);
@@ -525,23 +528,32 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
                             qz((w1 >> 4) & 0x0F0F0F0Fu)};
         }
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      // slice fragments of token tile mt (both buffers: tile mt + 1's reads
+      // are issued before tile mt's products)
+      u32x4 Af[2][NS][UPG];
+      auto load_frag = [&](u32x4 (&A)[NS][UPG], int mt) {
         const int row = mt * 16 + ln;
-        i32x4 D[NS][NT];
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          u32x4 A[UPG];
+        for (int j = 0; j < NS; ++j)
 #pragma unroll
           for (int u = 0; u < UPG; ++u) {
             const int c = 4 * (gi * UPG + u) + kb;
-            A[u] = *reinterpret_cast<const u32x4*>(cur + j * kSlice + row * 128 + ((c ^ (ln & 7)) << 4));
+            A[j][u] = *reinterpret_cast<const u32x4*>(cur + j * kSlice + row * 128 + ((c ^ (ln & 7)) << 4));
           }
+      };
+      load_frag(Af[0], 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt + 1 < MT) load_frag(Af[(mt + 1) % 2], mt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        i32x4 D[NS][NT];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             i32x4 d = i32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int u = 0; u < UPG; ++u) d = mfma_i8(A[u], Bi[u][nt], d);
+            for (int u = 0; u < UPG; ++u) d = mfma_i8(Af[mt % 2][j][u], Bi[u][nt], d);
             D[j][nt] = d;
           }
         }
@@ -576,7 +588,6 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
             }
           }
         }
-        // keep each token tile's fragment reads with its own products
         __builtin_amdgcn_sched_barrier(0);
       }
     }
