@@ -50,6 +50,7 @@
 #include "w4_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 
 namespace w4 {
@@ -105,7 +106,7 @@ template <int PATH, int FMT, int GPT>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_f16_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
-    float* __restrict__ partial, int gm) {
+    float* __restrict__ partial, float* __restrict__ tpart, int tile0, int gm) {
   constexpr int G = kStepK / GPT;
   constexpr int WPG = 4 / GPT;  // products (tile words) per group
   constexpr int MT = 8, NT = 2;
@@ -115,14 +116,16 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);  // the wave: columns 32 wn .. 32 wn + 31
-  const int S = gridDim.y;  // K slices (partials in `partial` when S > 1)
+  const int S = gridDim.y;  // K slices (partials in `partial`, or `tpart` for a tail launch, when S > 1)
   const int ks = blockIdx.y;
   const int ln = lane % 16, kb = lane / 16;
 
-  // XCD-aware, row-block-grouped renumbering (a bijection of [0, tiles))
+  // XCD-aware, row-block-grouped renumbering (a bijection of the launch's
+  // places [tile0, tile0 + gridDim.x) of the walk)
   const int tiles_n = (N + kHBN - 1) / kHBN;
+  const int place = tile0 + xcd_run(blockIdx.x, gridDim.x);
   int mb, nb;
-  tile_of(blockIdx.x, gridDim.x, (M + kHBM - 1) / kHBM, tiles_n, gm, mb, nb);
+  tile_mn(place, (M + kHBM - 1) / kHBM, tiles_n, gm, mb, nb);
   const int n0 = nb * kHBN;
   const int m0 = mb * kHBM;
 
@@ -341,7 +344,9 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
       for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + wn * 32 + nt * 16 + ln;
         if (n >= N) continue;
-        if (S == 1)
+        if (tpart)
+          tpart[(((size_t)ks * gridDim.x + (place - tile0)) * kHBM + (m - m0)) * kHBN + (n - n0)] = C[mt][nt][i];
+        else if (S == 1)
           y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
         else
           partial[((size_t)ks * M + m) * N + n] = C[mt][nt][i];
@@ -349,19 +354,33 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     }
 }
 
+// S > 1: every tile split over S K slices into `partial` [S][M][N]; else the
+// tail plan `tp` (tp.S > 1: the left-over tiles split into `tpart`).
 template <int PATH, int FMT, int GPT>
 int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
-               const uint16_t* zero, uint16_t* y, float* partial, int S, hipStream_t s) {
+               const uint16_t* zero, uint16_t* y, float* partial, int S, const TailPlan& tp, float* tpart,
+               hipStream_t s) {
   if ((size_t)M * K * 2 >= (1ull << 32))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm: activations of %d x %d exceed the 4 GiB one call addresses", M, K);
   constexpr int kLds = kHStages * kHStage;
   const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_f16_kernel<PATH, FMT, GPT>), kLds, "w4_gemm");
   if (st != 0) return st;
-  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
-  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tiles, (unsigned)S), dim3(kF16Threads),
-                     kLds, s, x, M, K, N, packed, scale, zero, y, partial, gemm_group_rows());
-  const int st2 = check_launch("gemm");
-  if (st2 != 0 || S == 1) return st2;
+  const int tiles_m = (M + kHBM - 1) / kHBM, tiles_n = (N + kHBN - 1) / kHBN;
+  const long tiles = (long)tiles_n * tiles_m;
+  const int gm = gemm_group_rows();
+  const bool tail = S == 1 && tp.S > 1 && tpart;
+  const long main_tiles = tail ? tp.main : tiles;
+  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)main_tiles, (unsigned)S), dim3(kF16Threads),
+                     kLds, s, x, M, K, N, packed, scale, zero, y, partial, nullptr, 0, gm);
+  int st2 = check_launch("gemm");
+  if (st2 != 0) return st2;
+  if (tail) {
+    hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tp.r, (unsigned)tp.S), dim3(kF16Threads),
+                       kLds, s, x, M, K, N, packed, scale, zero, y, nullptr, tpart, (int)tp.main, gm);
+    if ((st2 = check_launch("gemm tail")) != 0) return st2;
+    return launch_tail_reduce(tpart, tp, kHBM, kHBN, tiles_m, tiles_n, gm, M, N, y, s);
+  }
+  if (S == 1) return 0;
   return launch_reduce_partials(partial, S, (long)M * N, y, s);
 }
 
@@ -392,7 +411,8 @@ template <int GPT, int NS, bool DBG, bool FIXED>
 __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_msd_kernel(
     const int8_t* __restrict__ slices, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
-    const float* __restrict__ tok_scale, int32_t* __restrict__ acc_out, int gm) {
+    const float* __restrict__ tok_scale, int32_t* __restrict__ acc_out, float* __restrict__ tpart, int tile0,
+    int gm) {
   constexpr int G = kStepK / GPT;
   constexpr int UPG = 2 / GPT;  // int8 products (64 K positions each) per group
   constexpr int MT = msd_mt(GPT, NS, DBG), NT = 2;
@@ -412,14 +432,19 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   const int ln = lane % 16, kb = lane / 16;
 
   const int tiles_n = (N + kHBN - 1) / kHBN;
+  const int place = tile0 + xcd_run(blockIdx.x, gridDim.x);
   int mb, nb;
-  tile_of(blockIdx.x, gridDim.x, (M + BM - 1) / BM, tiles_n, gm, mb, nb);
+  tile_mn(place, (M + BM - 1) / BM, tiles_n, gm, mb, nb);
   const int n0 = nb * kHBN;
   const int m0 = mb * BM;
 
   const int ng = K / G;
   const int KT = K / kStepK;
   const int ntile_last = N / 16 - 1;
+  // K slice of this workgroup (gridDim.y > 1 only for a tail launch, whose
+  // partials go to tpart)
+  const int S = gridDim.y, ks = blockIdx.y;
+  const int kt0 = (int)((long)KT * ks / S), kt1 = (int)((long)KT * (ks + 1) / S);
 
   if (tid < BM) {
     const int m = min(m0 + tid, M - 1);
@@ -465,7 +490,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
     voff_s[j] = (uint32_t)(n0 + col) * (uint32_t)ng * 2u + (uint32_t)gi * 2u;  // columns past N read zeros
     sc_dst[j] = kA + kHB + ((gi * 2 + arr) * kHBN + quarter * 64) * 4;
   }
-  auto stage = [&](int kt) { return smem + (kt % kHStages) * kStage; };
+  auto stage = [&](int kt) { return smem + ((kt - kt0) % kHStages) * kStage; };
   auto issue_step = [&](int kt) {
     unsigned char* st = stage(kt);
 #pragma unroll
@@ -490,18 +515,18 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue_step(0);
-  if (KT > 1) {
-    issue_step(1);
+  issue_step(kt0);
+  if (kt1 - kt0 > 1) {
+    issue_step(kt0 + 1);
     wait_all_but_one_step();
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     const unsigned char* cur = stage(kt);
-    const bool more2 = kt + 2 < KT;
+    const bool more2 = kt + 2 < kt1;
     if (more2) issue_step(kt + 2);
 
     const uint32_t* s_lds = reinterpret_cast<const uint32_t*>(cur + kA + kHB);
@@ -609,14 +634,19 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + wn * 32 + nt * 16 + ln;
-        if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i] * s1);
+        if (n >= N) continue;
+        if (tpart)
+          tpart[(((size_t)ks * gridDim.x + (place - tile0)) * BM + (m - m0)) * kHBN + (n - n0)] = C[mt][nt][i] * s1;
+        else
+          y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i] * s1);
       }
     }
 }
 
 template <int GPT, int NS, bool FIXED>
 int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
-               const uint16_t* zero, uint16_t* y, const float* tok_scale, int32_t* acc_out, hipStream_t s) {
+               const uint16_t* zero, uint16_t* y, const float* tok_scale, int32_t* acc_out, float* tpart,
+               size_t tpart_bytes, hipStream_t s) {
   constexpr int kStage = NS * 16 * msd_mt(GPT, NS, false) * 128 + kHB + kHS;  // the larger of the two variants
   constexpr int kLds = kHStages * kStage;
   if ((size_t)NS * M * K >= (1ull << 32))
@@ -626,14 +656,29 @@ int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed,
   const int st = allow_dynamic_lds(fn, kLds, "w4_gemm_decomp");
   if (st != 0) return st;
   const int bm = 16 * msd_mt(GPT, NS, acc_out != nullptr);
-  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + bm - 1) / bm);
-  if (acc_out)
-    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true, FIXED>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices, M,
-                       K, N, packed, scale, zero, y, tok_scale, acc_out, gemm_group_rows());
-  else
-    hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false, FIXED>), dim3((unsigned)tiles), dim3(kF16Threads), kLds, s, slices,
-                       M, K, N, packed, scale, zero, y, tok_scale, acc_out, gemm_group_rows());
-  return check_launch("gemm_msd");
+  const int tiles_m = (M + bm - 1) / bm, tiles_n = (N + kHBN - 1) / kHBN;
+  const long tiles = (long)tiles_n * tiles_m;
+  const int gm = gemm_group_rows();
+  const TailPlan tp = plan_tail(tiles, K / kStepK, bm, kHBN);
+  const bool tail = tp.S > 1 && tpart && tpart_bytes >= tp.bytes;
+  const long main_tiles = tail ? tp.main : tiles;
+  auto go = [&](dim3 grid, float* part, int tile0) {
+    if (acc_out)
+      hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, true, FIXED>), grid, dim3(kF16Threads), kLds, s, slices, M, K, N,
+                         packed, scale, zero, y, tok_scale, acc_out, part, tile0, gm);
+    else
+      hipLaunchKernelGGL((gemm_msd_kernel<GPT, NS, false, FIXED>), grid, dim3(kF16Threads), kLds, s, slices, M, K, N,
+                         packed, scale, zero, y, tok_scale, acc_out, part, tile0, gm);
+  };
+  int st2;
+  if (main_tiles > 0) {
+    go(dim3((unsigned)main_tiles), nullptr, 0);
+    if ((st2 = check_launch("gemm_msd")) != 0) return st2;
+  }
+  if (!tail) return 0;
+  go(dim3((unsigned)tp.r, (unsigned)tp.S), tpart, (int)tp.main);
+  if ((st2 = check_launch("gemm_msd tail")) != 0) return st2;
+  return launch_tail_reduce(tpart, tp, bm, kHBN, tiles_m, tiles_n, gm, M, N, y, s);
 }
 
 }  // namespace
@@ -641,6 +686,71 @@ int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed,
 // K slices for the fp16 GEMM: while the grid holds fewer than about 192
 // workgroups (256 CUs), double S as long as every slice keeps at least 4
 // steps.  M = 256 layers: N = 8192 has 64 tiles -> S = 4.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) {
+      (void)hipGetLastError();
+      v = -1;
+    }
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
+}
+
+TailPlan plan_tail(long tiles, int KT, int bm, int bn) {
+  TailPlan p{tiles, 0, 1, 0};
+  const char* e = std::getenv("W4_GEMM_TAIL");
+  if (e && *e == '0') return p;
+  const int C = device_cus();
+  if (C <= 0 || tiles < 1) return p;
+  const int r = (int)(tiles % C == 0 ? 0 : tiles % C);
+  if (r == 0) return p;
+  int S = 1;
+  while ((long)r * S * 2 <= C && KT / (S * 2) >= 4) S *= 2;
+  if (S == 1) return p;
+  p.main = tiles - r;
+  p.r = r;
+  p.S = S;
+  p.bytes = (size_t)S * r * bm * bn * sizeof(float);
+  return p;
+}
+
+namespace {
+// y at the tail tiles' outputs = fp16 of the sum over the S slices' partials,
+// in slice order; thread i takes element i of the tail's [r][bm][bn].
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ tpart, int S, int r, int tile0,
+                                                          int bm, int bn, int tiles_m, int tiles_n, int gm, int M,
+                                                          int N, uint16_t* __restrict__ y) {
+  const long per = (long)bm * bn;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)r * per) return;
+  const int t = (int)(i / per);
+  const int e = (int)(i - (long)t * per);
+  int mb, nb;
+  tile_mn(tile0 + t, tiles_m, tiles_n, gm, mb, nb);
+  const int m = mb * bm + e / bn, n = nb * bn + e % bn;
+  if (m >= M || n >= N) return;
+  float acc = 0.f;
+  for (int k = 0; k < S; ++k) acc += tpart[(size_t)k * r * per + i];
+  y[(size_t)m * N + n] = float_to_half_bits(acc);
+}
+}  // namespace
+
+int launch_tail_reduce(const float* tpart, const TailPlan& tp, int bm, int bn, int tiles_m, int tiles_n, int gm,
+                       int M, int N, uint16_t* y, hipStream_t s) {
+  const long n = (long)tp.r * bm * bn;
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tpart, tp.S, tp.r,
+                     (int)tp.main, bm, bn, tiles_m, tiles_n, gm, M, N, y);
+  return check_launch("gemm tail reduce");
+}
+
 int gemm_split(int M, int K, int N) {
   const int KT = K / kStepK;
   const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
@@ -653,7 +763,9 @@ int gemm_split(int M, int K, int N) {
 
 size_t gemm_workspace_bytes(int M, int K, int N) {
   const int S = gemm_split(M, K, N);
-  return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
+  if (S > 1) return (size_t)S * M * N * sizeof(float);
+  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
+  return plan_tail(tiles, K / kStepK, kHBM, kHBN).bytes;
 }
 
 int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
@@ -662,8 +774,12 @@ int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed, c
   int S = gemm_split(M, K, N);
   if (S > 1 && (!ws || ws_bytes < (size_t)S * M * N * sizeof(float))) S = 1;  // no room for partials: unsplit
   float* partial = S > 1 ? static_cast<float*>(ws) : nullptr;
+  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + kHBM - 1) / kHBM);
+  TailPlan tp = plan_tail(tiles, K / kStepK, kHBM, kHBN);
+  if (S > 1 || !ws || ws_bytes < tp.bytes) tp = TailPlan{tiles, 0, 1, 0};  // no room for the tail: one launch
+  float* tpart = tp.S > 1 ? static_cast<float*>(ws) : nullptr;
 #define W4_GEMM_CASE(PATH, FMT, GPT) \
-  return launch_f16<PATH, FMT, GPT>(x, M, K, N, packed, scale, zero, y, partial, S, s)
+  return launch_f16<PATH, FMT, GPT>(x, M, K, N, packed, scale, zero, y, partial, S, tp, tpart, s)
   if (mode == 0) {
     if (fmt == 0) {
       if (G == 64) W4_GEMM_CASE(0, 0, 2);
@@ -688,14 +804,23 @@ size_t decomp_workspace_bytes(int M, int K, int G, int nslices) {
   return slices + scales;
 }
 
+size_t decomp_tail_bytes(int M, int K, int N, int G, int nslices) {
+  const int bm = 16 * msd_mt(G == 64 ? 2 : 1, nslices, false);
+  const long tiles = (long)((N + kHBN - 1) / kHBN) * ((M + bm - 1) / bm);
+  return plan_tail(tiles, K / kStepK, bm, kHBN).bytes;
+}
+
 int launch_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
                        const uint16_t* zero, int G, int nslices, bool fixed, uint16_t* y, int8_t* slices_op,
-                       int8_t* slices_out, float* tok_scale, int32_t* acc_out, hipStream_t s) {
+                       int8_t* slices_out, float* tok_scale, int32_t* acc_out, float* tpart, size_t tpart_bytes,
+                       hipStream_t s) {
   int st = launch_decompose(x, M, K, nslices, fixed, slices_op, slices_out, tok_scale, s);
   if (st != 0) return st;
-#define W4_MSD(NS, FX)                                                                                        \
-  return G == 64 ? launch_msd<2, NS, FX>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s) \
-                 : launch_msd<1, NS, FX>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, s)
+#define W4_MSD(NS, FX)                                                                                             \
+  return G == 64 ? launch_msd<2, NS, FX>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, tpart,   \
+                                         tpart_bytes, s)                                                          \
+                 : launch_msd<1, NS, FX>(slices_op, M, K, N, packed, scale, zero, y, tok_scale, acc_out, tpart,   \
+                                         tpart_bytes, s)
   if (fixed) W4_MSD(2, true);
   if (nslices == 1) W4_MSD(1, false);
   if (nslices == 2) W4_MSD(2, false);

@@ -203,7 +203,8 @@ __device__ __forceinline__ f32x4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_
 template <int NS, int WM>
 __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_mx_kernel(
     const uint8_t* __restrict__ slices, const uint8_t* __restrict__ xscale, int M, int K, int N,
-    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ wscale, uint16_t* __restrict__ y, int gm) {
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ wscale, uint16_t* __restrict__ y,
+    float* __restrict__ tpart, int tile0, int gm) {
   constexpr int BM = mx_bm<WM>();
   constexpr int WN = 8 / WM;                // waves along N
   constexpr int MT = 8, NT = 2 * WM;
@@ -223,12 +224,16 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int ln = lane % 16, jb = lane / 16;
 
   const int tiles_n = (N + kMxBN - 1) / kMxBN;
+  const int place = tile0 + xcd_run(blockIdx.x, gridDim.x);
   int mb, nb;
-  tile_of(blockIdx.x, gridDim.x, (M + BM - 1) / BM, tiles_n, gm, mb, nb);
+  tile_mn(place, (M + BM - 1) / BM, tiles_n, gm, mb, nb);
   const int n0 = nb * kMxBN;
   const int m0 = mb * BM;
 
   const int KT = K / kMxStepK;
+  // K slice (gridDim.y > 1 only for a tail launch, whose partials go to tpart)
+  const int S = gridDim.y, ks = blockIdx.y;
+  const int kt0 = (int)((long)KT * ks / S), kt1 = (int)((long)KT * (ks + 1) / S);
   const int nbk = K / kMxBlock;  // scale bytes per row
   const int ntile_last = N / 16 - 1;
 
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     sc_dst[i] = sc_x[i] ? kOffSA + sc_j[i] * kSA + 64 * (c % kRowSc) * 4 : kOffSB + 64 * (c - NS * kRowSc) * 4;
   }
 
-  auto stage = [&](int kt) { return smem + (kt % kMxStages) * kStage; };
+  auto stage = [&](int kt) { return smem + ((kt - kt0) % kMxStages) * kStage; };
   auto issue_step = [&](int kt) {
     unsigned char* st = stage(kt);
 #pragma unroll
@@ -295,18 +300,18 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const uint32_t a_chunk = (uint32_t)((jb ^ ((ln >> 2) & 3)) * 16);
   const uint32_t shift = 8u * (uint32_t)jb;
 
-  issue_step(0);
-  if (KT > 1) {
-    issue_step(1);
+  issue_step(kt0);
+  if (kt1 - kt0 > 1) {
+    issue_step(kt0 + 1);
     wait_all_but_one_step();
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     const unsigned char* cur = stage(kt);
-    const bool more2 = kt + 2 < KT;
+    const bool more2 = kt + 2 < kt1;
     if (more2) issue_step(kt + 2);
 
     u32x4 Bv[NT];
@@ -317,16 +322,28 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
       sb[nt] = __builtin_amdgcn_ubfe(
           *reinterpret_cast<const uint32_t*>(cur + kOffSB + (wc * 16 * NT + nt * 16 + ln) * 4), shift, 8);
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    // slice fragments and scales of token tile mt; tile mt + 1's are read
+    // before tile mt's products run
+    u32x4 Af[2][NS];
+    uint32_t saf[2][NS];
+    auto load_frag = [&](int b, int mt) {
       const int row = wm * 128 + mt * 16 + ln;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const u32x4 A = *reinterpret_cast<const u32x4*>(cur + j * kA + row * 64 + a_chunk);
-        const uint32_t sa =
-            __builtin_amdgcn_ubfe(*reinterpret_cast<const uint32_t*>(cur + kOffSA + j * kSA + row * 4), shift, 8);
+        Af[b][j] = *reinterpret_cast<const u32x4*>(cur + j * kA + row * 64 + a_chunk);
+        saf[b][j] = *reinterpret_cast<const uint32_t*>(cur + kOffSA + j * kSA + row * 4);
+      }
+    };
+    load_frag(0, 0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) C[mt][nt] = mfma_fp4(A, sa, Bv[nt], sb[nt], C[mt][nt]);
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt + 1 < MT) load_frag((mt + 1) % 2, mt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const uint32_t sa = __builtin_amdgcn_ubfe(saf[mt % 2][j], shift, 8);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) C[mt][nt] = mfma_fp4(Af[mt % 2][j], sa, Bv[nt], sb[nt], C[mt][nt]);
       }
     }
 
@@ -346,35 +363,59 @@ __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + wc * 16 * NT + nt * 16 + ln;
-        if (n < N) y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
+        if (n >= N) continue;
+        if (tpart)
+          tpart[(((size_t)ks * gridDim.x + (place - tile0)) * BM + (m - m0)) * kMxBN + (n - n0)] = C[mt][nt][i];
+        else
+          y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i]);
       }
     }
 }
 
 template <int NS, int WM>
 int launch_gemm_mx_w(const uint8_t* slices, const uint8_t* xscale, int M, int K, int N, const uint8_t* packed,
-                     const uint8_t* wscale, uint16_t* y, hipStream_t s) {
+                     const uint8_t* wscale, uint16_t* y, float* tpart, size_t tpart_bytes, hipStream_t s) {
   constexpr int kLds = kMxStages * mx_stage_bytes<NS, WM>();
+  constexpr int BM = mx_bm<WM>();
   static_assert(kLds <= 160 * 1024, "LDS");
   const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemm_mx_kernel<NS, WM>), kLds, "w4_gemm_mx");
   if (st != 0) return st;
-  const long tiles = (long)((N + kMxBN - 1) / kMxBN) * ((M + mx_bm<WM>() - 1) / mx_bm<WM>());
-  hipLaunchKernelGGL((gemm_mx_kernel<NS, WM>), dim3((unsigned)tiles), dim3(kMxThreads), kLds, s, slices, xscale, M, K,
-                     N, packed, wscale, y, gemm_group_rows());
-  return check_launch("gemm_mx");
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + kMxBN - 1) / kMxBN;
+  const long tiles = (long)tiles_n * tiles_m;
+  const int gm = gemm_group_rows();
+  const TailPlan tp = plan_tail(tiles, K / kMxStepK, BM, kMxBN);
+  const bool tail = tp.S > 1 && tpart && tpart_bytes >= tp.bytes;
+  const long main_tiles = tail ? tp.main : tiles;
+  int st2;
+  if (main_tiles > 0) {
+    hipLaunchKernelGGL((gemm_mx_kernel<NS, WM>), dim3((unsigned)main_tiles), dim3(kMxThreads), kLds, s, slices,
+                       xscale, M, K, N, packed, wscale, y, nullptr, 0, gm);
+    if ((st2 = check_launch("gemm_mx")) != 0) return st2;
+  }
+  if (!tail) return 0;
+  hipLaunchKernelGGL((gemm_mx_kernel<NS, WM>), dim3((unsigned)tp.r, (unsigned)tp.S), dim3(kMxThreads), kLds, s,
+                     slices, xscale, M, K, N, packed, wscale, y, tpart, (int)tp.main, gm);
+  if ((st2 = check_launch("gemm_mx tail")) != 0) return st2;
+  return launch_tail_reduce(tpart, tp, BM, kMxBN, tiles_m, tiles_n, gm, M, N, y, s);
 }
 
-// W4_MX_WM (1 or 2) overrides the waves along M for sweeps
-template <int NS>
-int launch_gemm_mx_t(const uint8_t* slices, const uint8_t* xscale, int M, int K, int N, const uint8_t* packed,
-                     const uint8_t* wscale, uint16_t* y, hipStream_t s) {
+// waves along M of the MXFP4 product with ns slices (W4_MX_WM = 1 or 2
+// overrides it for sweeps)
+int mx_wm_for(int ns) {
   static const int wm = [] {
     const char* e = std::getenv("W4_MX_WM");
     return e && (*e == '1' || *e == '2') ? *e - '0' : 0;
   }();
-  if (wm == 1 || (wm == 0 && mx_wm<NS>() == 1))
-    return launch_gemm_mx_w<NS, 1>(slices, xscale, M, K, N, packed, wscale, y, s);
-  return launch_gemm_mx_w<NS, 2>(slices, xscale, M, K, N, packed, wscale, y, s);
+  if (wm) return wm;
+  return ns == 1 ? mx_wm<1>() : mx_wm<2>();
+}
+
+template <int NS>
+int launch_gemm_mx_t(const uint8_t* slices, const uint8_t* xscale, int M, int K, int N, const uint8_t* packed,
+                     const uint8_t* wscale, uint16_t* y, float* tpart, size_t tpart_bytes, hipStream_t s) {
+  if (mx_wm_for(NS) == 1)
+    return launch_gemm_mx_w<NS, 1>(slices, xscale, M, K, N, packed, wscale, y, tpart, tpart_bytes, s);
+  return launch_gemm_mx_w<NS, 2>(slices, xscale, M, K, N, packed, wscale, y, tpart, tpart_bytes, s);
 }
 
 inline unsigned blocks_for(long threads) { return (unsigned)((threads + 255) / 256); }
@@ -399,8 +440,14 @@ size_t mx_workspace_bytes(int M, int K, int nslices) {
   return sl + sc;
 }
 
+size_t mx_tail_bytes(int M, int K, int N, int nslices) {
+  const int bm = 128 * mx_wm_for(nslices);
+  const long tiles = (long)((N + kMxBN - 1) / kMxBN) * ((M + bm - 1) / bm);
+  return plan_tail(tiles, K / kMxStepK, bm, kMxBN).bytes;
+}
+
 int launch_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint8_t* wscale, int nslices,
-                   uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, hipStream_t s) {
+                   uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, size_t ws_bytes, hipStream_t s) {
   uint8_t* sl = static_cast<uint8_t*>(ws);
   uint8_t* sc = sl + ((size_t)nslices * M * (K / 2) + 255) / 256 * 256;
   const unsigned blocks = blocks_for((long)M * (K / kMxBlock));
@@ -412,8 +459,12 @@ int launch_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed
                        scales_out);
   const int st = check_launch("decompose_mx");
   if (st != 0) return st;
-  if (nslices == 1) return launch_gemm_mx_t<1>(sl, sc, M, K, N, packed, wscale, y, s);
-  return launch_gemm_mx_t<2>(sl, sc, M, K, N, packed, wscale, y, s);
+  // the tail's partials, when the workspace holds them after the slices and scales
+  const size_t base = mx_workspace_bytes(M, K, nslices);
+  float* tpart = ws_bytes > base ? reinterpret_cast<float*>(static_cast<char*>(ws) + base) : nullptr;
+  const size_t tbytes = ws_bytes > base ? ws_bytes - base : 0;
+  if (nslices == 1) return launch_gemm_mx_t<1>(sl, sc, M, K, N, packed, wscale, y, tpart, tbytes, s);
+  return launch_gemm_mx_t<2>(sl, sc, M, K, N, packed, wscale, y, tpart, tbytes, s);
 }
 
 }  // namespace w4

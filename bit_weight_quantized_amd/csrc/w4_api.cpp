@@ -122,8 +122,10 @@ int gemm_decomp_checked(const char* fn, const uint16_t* x, int M, int K, int N, 
   const size_t slice_bytes = ((size_t)nslices * M * K + 255) / 256 * 256;
   int8_t* sl_op = reinterpret_cast<int8_t*>(base);
   float* ts = tok_scale_out ? tok_scale_out : reinterpret_cast<float*>(base + slice_bytes);
+  // the tail's partials, when the workspace holds them after the slices and scales
+  float* tpart = ws_bytes > need ? reinterpret_cast<float*>(base + need) : nullptr;
   return launch_gemm_decomp(x, M, K, N, packed, scale, zero, G, nslices, fixed, y, sl_op, slices_out, ts, acc_out,
-                            (hipStream_t)stream);
+                            tpart, ws_bytes - need, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -289,7 +291,8 @@ int w4_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
   if (!ws || ws_bytes < need)
     return fail(W4_EWORKSPACE, "w4_gemm_mx: workspace of %zu bytes required (got %zu)", need, ws_bytes);
   if (!aligned16(ws)) return fail(W4_EINVAL, "w4_gemm_mx: workspace must be 16-byte aligned");
-  return launch_gemm_mx(x, M, K, N, packed, scale, nslices, y, slices_out, scales_out, ws, (hipStream_t)stream);
+  return launch_gemm_mx(x, M, K, N, packed, scale, nslices, y, slices_out, scales_out, ws, ws_bytes,
+                        (hipStream_t)stream);
 }
 
 int w4_attn_decode_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, int d, const uint8_t* k_packed,
@@ -332,10 +335,11 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
       return attn_workspace_bytes(M, K, N);
     case W4_OP_GEMM_MX:
       if (M < 1 || K < 128 || K % 128 || (fmt_or_mode != 1 && fmt_or_mode != 2)) return 0;
-      return mx_workspace_bytes(M, K, fmt_or_mode);
+      return mx_workspace_bytes(M, K, fmt_or_mode) + (N >= 16 ? mx_tail_bytes(M, K, N, fmt_or_mode) : 0);
     case W4_OP_GEMM_DECOMP:
       if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || fmt_or_mode < 1 || fmt_or_mode > 3) return 0;
-      return decomp_workspace_bytes(M, K, G, fmt_or_mode);
+      return decomp_workspace_bytes(M, K, G, fmt_or_mode) +
+             (N >= 16 && K % 128 == 0 ? decomp_tail_bytes(M, K, N, G, fmt_or_mode) : 0);
     default:
       return (size_t)-1;
   }

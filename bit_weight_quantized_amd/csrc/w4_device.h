@@ -87,16 +87,25 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
 // run at once on one XCD share gm row blocks of activations and about
 // 32 / gm column blocks of weights in that XCD's L2 (gm = 1: one row block,
 // every weight block read once per tile).
-__device__ __forceinline__ void tile_of(int b, int tiles, int tiles_m, int tiles_n, int gm, int& mb, int& nb) {
+// The two halves: xcd_run gives workgroup b's place in the launch's
+// XCD-contiguous order, tile_mn the tile at a place of the grouped walk.  A
+// launch that covers places [p0, p0 + tiles) of a larger walk (the split-K
+// tail of a GEMM) maps workgroup b to tile_mn(p0 + xcd_run(b, tiles)).
+__device__ __forceinline__ int xcd_run(int b, int tiles) {
   const int xcd = b % 8, idx = b / 8;
   const int per = tiles / 8, rem = tiles % 8;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+}
+__device__ __forceinline__ void tile_mn(int logical, int tiles_m, int tiles_n, int gm, int& mb, int& nb) {
   const int group = logical / (gm * tiles_n);
   const int first = group * gm;
   const int g = min(tiles_m - first, gm);
   const int in = logical - group * gm * tiles_n;
   mb = first + in % g;
   nb = in / g;
+}
+__device__ __forceinline__ void tile_of(int b, int tiles, int tiles_m, int tiles_n, int gm, int& mb, int& nb) {
+  tile_mn(xcd_run(b, tiles), tiles_m, tiles_n, gm, mb, nb);
 }
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {

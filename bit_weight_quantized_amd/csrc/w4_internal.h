@@ -44,11 +44,28 @@ int launch_gemv(const GemvPlan& plan, const uint16_t* x, int M, int K, int N,
 // W4_GEMM_GM overrides the default for sweeps).
 int gemm_group_rows();
 
+// Matrix-core GEMMs run one workgroup per CU.  With tiles = q C + r (C CUs,
+// 0 < r <= C / 2), the q C tiles run as one launch and the r left over as a
+// second launch with each tile's K steps split over S workgroups: fp32
+// partials [S][r][bm][bn] (`bytes`), then tail_reduce writes those tiles of
+// y.  S = 1: no tail launch.  W4_GEMM_TAIL=0 turns it off.
+struct TailPlan {
+  long main;  // tiles of the first launch (places [0, main) of the walk)
+  int r, S;
+  size_t bytes;
+};
+int device_cus();  // compute units of the current device, 0 when unknown
+TailPlan plan_tail(long tiles, int KT, int bm, int bn);
+int launch_tail_reduce(const float* tpart, const TailPlan& tp, int bm, int bn, int tiles_m, int tiles_n, int gm,
+                       int M, int N, uint16_t* y, hipStream_t s);
+
 // fp16 GEMM: K slices over workgroups (1 when the grid already fills the
-// chip) and the fp32 partial workspace that takes ([S][M][N], 0 when S = 1).
+// chip) and the fp32 partial workspace that takes ([S][M][N] when S > 1,
+// else the tail's partials).
 int gemm_split(int M, int K, int N);
 size_t gemm_workspace_bytes(int M, int K, int N);
-// Launches the fp16 GEMM; with ws_bytes < gemm_workspace_bytes it runs unsplit.
+// Launches the fp16 GEMM; with ws_bytes < gemm_workspace_bytes it runs unsplit
+// (and without a tail launch).
 int launch_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
                 const uint16_t* scale, const uint16_t* zero, int G, int fmt,
                 int mode, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t s);
@@ -59,6 +76,9 @@ int launch_reduce_partials(const float* partial, int S, long MN, uint16_t* y, hi
 // matrix-core operand layout (256-byte aligned), then fp32 token scales
 // [nslices][M].
 size_t decomp_workspace_bytes(int M, int K, int G, int nslices);
+// Optional room for the tail's partials after that (the product runs without
+// a tail launch when the workspace does not hold it).
+size_t decomp_tail_bytes(int M, int K, int N, int G, int nslices);
 // Decomposition: operand-layout slices, plus the plain layout when
 // slices_out is non-null.  nslices 1..3 with adaptive scales, or (fixed) two
 // slices with s_2 = s_1 / 254.
@@ -68,7 +88,7 @@ int launch_gemm_decomp(const uint16_t* x, int M, int K, int N,
                        const uint8_t* packed, const uint16_t* scale,
                        const uint16_t* zero, int G, int nslices, bool fixed, uint16_t* y,
                        int8_t* slices_op, int8_t* slices_out, float* tok_scale,
-                       int32_t* acc_out, hipStream_t s);
+                       int32_t* acc_out, float* tpart, size_t tpart_bytes, hipStream_t s);
 
 // Residual compensation: the k salient channels of x (k <= kSelMaxTop,
 // K <= kSelMaxK), and y += x[:, idx] . R[idx, :] with R fp16 [K][N] in memory
@@ -86,8 +106,9 @@ int launch_residual_correct(const uint16_t* x, int M, int K, int N, const uint16
 int launch_quantize_mx(const float* wt, int K, int N, uint8_t* codes, uint8_t* scale, hipStream_t s);
 int launch_pack_mx(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t s);
 size_t mx_workspace_bytes(int M, int K, int nslices);
+size_t mx_tail_bytes(int M, int K, int N, int nslices);  // optional, after the above
 int launch_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint8_t* wscale, int nslices,
-                   uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, hipStream_t s);
+                   uint16_t* y, uint8_t* slices_out, uint8_t* scales_out, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Decode attention over an INT4 KV cache with MSD on both products (head
 // dimension 128, L % 256 == 0, Hq / Hkv <= 16); workspace: query slices and
