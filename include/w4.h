@@ -146,9 +146,13 @@ int w4_gemv(const uint16_t* x, int M, int K, int N,
  * workgroups if the caller passes at least
  * w4_workspace_bytes(W4_OP_GEMM, M, K, N, G, mode) bytes (16-byte aligned,
  * no initial contents needed: fp32 partials [S][M][N], added in slice order
- * by a second kernel on the same stream); with less (or NULL) the product
- * runs unsplit.  Results do not depend on the split beyond fp32 rounding of
- * the partial sums.
+ * by a second kernel on the same stream).  When the tiles fill the GPU but
+ * leave a partial last round (tiles = q * CUs + r, 0 < r <= CUs / 2), the r
+ * left-over tiles run as a second launch with K split over S workgroups each,
+ * their fp32 partials [S][r][128][256] in the workspace, and a reduction
+ * kernel writes their part of y.  With less workspace (or NULL) the product
+ * runs as one launch.  Results do not depend on the split beyond fp32
+ * rounding of the partial sums.
  */
 int w4_gemm(const uint16_t* x, int M, int K, int N,
             const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
@@ -174,9 +178,12 @@ int w4_gemm(const uint16_t* x, int M, int K, int N,
  * [nslices][M][K/G][N], the per-group integer accumulators (a debugging aid
  * for small shapes; it selects a slower kernel).
  * Workspace (required, 16-byte aligned, contents need not be initialised):
- * at least w4_workspace_bytes(W4_OP_GEMM_DECOMP, M, K, N, G, nslices) bytes;
- * it holds the slices in the int8 matrix-core operand order and, when
- * tok_scale_out is NULL, the per-token scales.  Calls that overlap in time
+ * at least w4_workspace_bytes(W4_OP_GEMM_DECOMP, M, K, 0, G, nslices) bytes,
+ * which hold the slices in the int8 matrix-core operand order and, when
+ * tok_scale_out is NULL, the per-token scales.  w4_workspace_bytes with the
+ * real N adds room for the fp32 partials of the tiles left over from the last
+ * full round on the CUs, which then run with K split over workgroups (as in
+ * w4_gemm; without that room they run unsplit).  Calls that overlap in time
  * must not share it.
  */
 int w4_gemm_decomp(const uint16_t* x, int M, int K, int N,
@@ -251,8 +258,10 @@ int w4_pack_mx(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream
  * Requires K % 128 == 0, N % 16 == 0, x and y 16-byte aligned, operands below
  * 4 GiB.  Optional outputs (NULL to skip): slices_out u8 [nslices][M][K/2]
  * (packed, low nibble first), scales_out u8 [nslices][M][K/32].  Workspace
- * (required, 16-byte aligned, no initial contents):
- * w4_workspace_bytes(W4_OP_GEMM_MX, M, K, N, 32, nslices) bytes.
+ * (required, 16-byte aligned, no initial contents): at least
+ * w4_workspace_bytes(W4_OP_GEMM_MX, M, K, 0, 32, nslices) bytes for the
+ * slices and their scales; w4_workspace_bytes with the real N adds room for
+ * the split-K partials of the left-over tiles, as for w4_gemm_decomp.
  */
 int w4_gemm_mx(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
                const uint8_t* scale, int nslices, uint16_t* y, uint8_t* slices_out,
@@ -356,11 +365,13 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
                         const int32_t* idx, int k, uint16_t* y, void* stream);
 
 /*
- * w4_workspace_bytes/*
  * w4_workspace_bytes -- bytes of workspace an entry point needs for the given
  * shape.  `fmt_or_mode`: the w4_fmt for W4_OP_GEMV, the w4_mode for
- * W4_OP_GEMM, nslices for W4_OP_GEMM_DECOMP and W4_OP_GEMM_MX.  Host-only; returns 0 for ops
- * that need none and (size_t)-1 for an invalid op.
+ * W4_OP_GEMM, nslices for W4_OP_GEMM_DECOMP and W4_OP_GEMM_MX.  Host-only;
+ * returns 0 for ops that need none and (size_t)-1 for an invalid op.  The
+ * split-K room of the matrix-core products depends on the current device's
+ * CU count (none when no device is visible); N < 16 gives the minimum for
+ * W4_OP_GEMM_DECOMP and W4_OP_GEMM_MX.
  */
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode);
 
