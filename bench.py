@@ -59,6 +59,8 @@ def parse():
                     help="skip the KV-cache attention timing")
     ap.add_argument("--no-residual", dest="residual", action="store_false",
                     help="skip the residual-compensation timing")
+    ap.add_argument("--no-layers", dest="layers", action="store_false",
+                    help="skip the MLP-shaped GEMV and decoder-layer timings")
     ap.add_argument("--gemm-reps", type=int, default=20,
                     help="timed launches per prefill GEMM path (0 skips the GEMM section)")
     return ap.parse_args()
@@ -185,6 +187,114 @@ def bench_gemm_prefill(w4, torch, reps):
                     "activations split into J MXFP4 slices, J block-scaled fp4 products per useful "
                     "multiply-add against the dense fp4 peak, decomposition included",
             "paths": res}
+
+
+def rotation_sets(per_set_bytes):
+    """Weight sets per rotation: more than 512 MB, twice the Infinity Cache."""
+    return max(2, -(-(2 * 256 * 2 ** 20) // per_set_bytes) + 1)
+
+
+def bench_mlp_gemv(w4, torch, stream, replays=4):
+    """MLP-shaped decode products, M = 1, 8 and 32: up/gate (K = 8192,
+    N = 28672) and down (K = 28672, N = 8192), INT4 g128 and NF4 b64.  Per
+    launch: a HIP graph of one launch per weight set of a > 512 MB rotation,
+    replayed back to back between events on its stream."""
+    import workloads as wl
+    shapes = (("up_gate", 8192, 28672), ("down", 28672, 8192))
+    res = []
+    for si, (name, K, N) in enumerate(shapes):
+        for fmt, G in ((w4.INT4_ASYM, 128), (w4.NF4, 64)):
+            b = weight_stream_bytes(fmt, K, N, G)
+            n_sets = rotation_sets(b)
+            sets = make_weight_sets(w4, torch, fmt, K, N, G, n_sets, 50000 + 1000 * si + 100 * fmt)
+            for M in (1, 8, 32):
+                x = torch.from_numpy(wl.make_activations(3, si, M, K)).cuda()
+                y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                ws = torch.zeros(max(16, w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)), dtype=torch.uint8,
+                                 device="cuda")
+                calls = [lambda p=p: w4.gemv(x, p[0], p[1], p[2], G, fmt, out=y, workspace=ws) for p in sets]
+                g = graph_of(torch, stream, calls)
+                time_replays(torch, stream, g, 1)
+                us = time_replays(torch, stream, g, replays) * 1e3 / (replays * n_sets)
+                res.append({"matrix": name, "K": K, "N": N, "variant": variant_name(fmt, M),
+                            "us_per_launch": round(us, 3), "weight_bytes": b,
+                            "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                            "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+                del g
+            del sets
+            torch.cuda.empty_cache()
+    return {"workload": "mlp_gemv_up_gate_k8192_n28672_down_k28672_n8192", "rotation": "> 512 MB per variant",
+            "per_launch": res}
+
+
+DECODER_LAYER = (("q", 8192, 8192), ("k", 8192, 1024), ("v", 8192, 1024), ("o", 8192, 8192),
+                 ("gate", 8192, 28672), ("up", 8192, 28672), ("down", 28672, 8192))
+
+
+def bench_decoder_layer(w4, torch, stream, replays=4):
+    """A 70B-style decoder layer's seven products (q, k, v, o, gate, up,
+    down) back to back, at M = 1 (GEMV) and M = 256 (the matrix-core paths),
+    INT4 g128 and NF4 b64; two weight sets per format (> 512 MB).  Timed as
+    HIP graphs of whole layers replayed between events on their stream."""
+    import workloads as wl
+    out = []
+    flops_256 = sum(2.0 * 256 * K * N for _, K, N in DECODER_LAYER)
+    for fmt, G in ((w4.INT4_ASYM, 128), (w4.NF4, 64)):
+        layer_bytes = sum(weight_stream_bytes(fmt, K, N, G) for _, K, N in DECODER_LAYER)
+        n_sets = rotation_sets(layer_bytes)
+        sets = [{name: make_weight_sets(w4, torch, fmt, K, N, G, 1, 60000 + 1000 * s + 10 * i + 100 * fmt)[0]
+                 for i, (name, K, N) in enumerate(DECODER_LAYER)} for s in range(n_sets)]
+        paths = [("gemv", 1)]
+        paths += [("dq_f16", 256), ("postscale", 256)]
+        if fmt == w4.INT4_ASYM:
+            paths += [("msd2", 256), ("msd2_fixed", 256)]
+        for path, M in paths:
+            xs = {K: torch.from_numpy(wl.make_activations(5, 0 if K == 8192 else 6, M, K)).cuda()
+                  for K in {K for _, K, _ in DECODER_LAYER}}
+            ys = {name: torch.empty((M, N), dtype=torch.float16, device="cuda") for name, _, N in DECODER_LAYER}
+            calls = []
+            for s in range(n_sets):
+                for name, K, N in DECODER_LAYER:
+                    p, sc, z = sets[s][name]
+                    x, y = xs[K], ys[name]
+                    if path == "gemv":
+                        ws = torch.zeros(max(16, w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)), dtype=torch.uint8,
+                                         device="cuda")
+                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, K=K: w4.gemv(x, p, sc, z, G, fmt, out=y,
+                                                                                         workspace=ws))
+                    elif path in ("dq_f16", "postscale"):
+                        mode = w4.DQ_F16 if path == "dq_f16" else w4.POSTSCALE
+                        ws = torch.empty(max(16, w4.workspace_bytes(w4.OP_GEMM, M, K, N, G, mode)), dtype=torch.uint8,
+                                         device="cuda")
+                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, mode=mode: w4.gemm(
+                            x, p, sc, z, G, fmt, mode, out=y, workspace=ws))
+                    else:
+                        ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8,
+                                         device="cuda")
+                        fn = w4.gemm_decomp_fixed if path == "msd2_fixed" else (
+                            lambda *a, **k: w4.gemm_decomp(*a[:5], 2, **k))
+                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, fn=fn: fn(x, p, sc, z, G, out=y,
+                                                                                         workspace=ws))
+            g = graph_of(torch, stream, calls)
+            time_replays(torch, stream, g, 1)
+            us = time_replays(torch, stream, g, replays) * 1e3 / (replays * n_sets)
+            row = {"format": "int4_asym_g128" if fmt == w4.INT4_ASYM else "nf4_b64", "path": path, "M": M,
+                   "us_per_layer": round(us, 1), "weight_bytes": layer_bytes}
+            if M == 1:
+                gbs = layer_bytes / (us * 1e-6) / 1e9
+                row.update({"GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+            else:
+                tf = flops_256 / (us * 1e-6) / 1e12
+                mult, peak = (2, INT8_MFMA_PEAK_TOPS) if path.startswith("msd") else (1, FP16_MFMA_PEAK_TFLOPS)
+                row.update({"tflops_useful": round(tf, 1), "mfma_frac": round(tf * mult / peak, 4)})
+            out.append(row)
+            del g, calls
+        del sets
+        torch.cuda.empty_cache()
+    return {"workload": "decoder_layer_hidden8192_inter28672_q64_kv8", "matrices": [list(m) for m in DECODER_LAYER],
+            "note": "M=256 msd paths include the activation decomposition of every product and are measured "
+                    "against the dense int8 peak with two int8 products per useful multiply-add",
+            "rows": out}
 
 
 HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
@@ -522,6 +632,13 @@ def main():
         traffic = round(sum(traffic_rows[p["variant"]] for p in per) / len(per))
 
     gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
+    mlp = layer = None
+    if args.layers:
+        try:
+            mlp = bench_mlp_gemv(w4, torch, stream)
+            layer = bench_decoder_layer(w4, torch, stream)
+        except Exception as e:  # reported, never fatal to the headline line
+            layer = {"error": f"{type(e).__name__}: {e}"}
     attn = None
     if args.attention:
         try:
@@ -568,6 +685,8 @@ def main():
                      "launch_average_us": round(sum_us / len(per), 3)},
         "per_launch": per,
         "gemm_prefill": gemm,
+        "mlp_gemv": mlp,
+        "decoder_layer": layer,
         "residual_compensation": resid,
         "attention_kv_msd": attn,
         "cpu_baseline": cpu,

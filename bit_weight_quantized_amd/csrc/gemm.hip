@@ -319,8 +319,10 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
         unpack(Bn, w + 1);
       }
       // keep the next word's reads ahead of this word's products (the
-      // scheduler would otherwise sink each read to just before its use)
-      __builtin_amdgcn_sched_barrier(0);
+      // scheduler would otherwise sink each read to just before its use);
+      // post-scaled, only for INT4 G = 128: with two groups per step, or the
+      // NF4 table, the accumulators leave no registers for both buffers
+      if constexpr (PATH == 0 || (FMT == 0 && GPT == 1)) __builtin_amdgcn_sched_barrier(0);
       products(A, Bc, w);
       if constexpr (PATH == 1) {
         if ((w % WPG) == WPG - 1) scale_group(w / WPG);
