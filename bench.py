@@ -145,8 +145,11 @@ def bench_gemm_prefill(w4, torch, reps):
     mx_codes, mx_scale = w4.quantize_mx(wmx)
     mx_packed = w4.pack_mx(mx_codes)
     del wmx, mx_codes
-    ws_mx = torch.empty(w4.workspace_bytes(w4.OP_GEMM_MX, M, K, N, 32, 2), dtype=torch.uint8, device="cuda")
-    ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 3), dtype=torch.uint8, device="cuda")
+    ws_mx = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_MX, M, K, N, 32, ns) for ns in (1, 2)), dtype=torch.uint8,
+                        device="cuda")
+    # one workspace for every slice count: the largest need (slices, scales, split-K tail partials)
+    ws = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, ns) for ns in (1, 2, 3)),
+                     dtype=torch.uint8, device="cuda")
     flops = 2.0 * M * N * K
     paths = {
         "dq_f16": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.DQ_F16, out=y), 1, FP16_MFMA_PEAK_TFLOPS),
@@ -484,6 +487,19 @@ def summarize(paths, pattern=None):
                 print(f"| `{short_kernel(r[cols['name']])}` | {r[cols['calls']]} | "
                       f"{float(r[cols['averagens']]) / 1e3:.2f} | {float(r[cols['minns']]) / 1e3:.2f} | "
                       f"{float(r[cols['maxns']]) / 1e3:.2f} |")
+        elif "start_timestamp" in cols and "grid_size_x" in cols:  # kernel trace: per launch geometry
+            agg = collections.defaultdict(list)
+            for r in rows:
+                if not keep(r[cols["kernel_name"]]):
+                    continue
+                grid = "x".join(str(int(r[cols[f"grid_size_{a}"]]) // int(r[cols[f"workgroup_size_{a}"]]))
+                                for a in "xy")
+                key = (short_kernel(r[cols["kernel_name"]]), grid, r[cols["workgroup_size_x"]])
+                agg[key].append((int(r[cols["end_timestamp"]]) - int(r[cols["start_timestamp"]])) / 1e3)
+            print("| kernel | workgroups (x by y) | workgroup size | dispatches | average (us) | min (us) | max (us) |")
+            print("|---|---|---|---|---|---|---|")
+            for (k, g, wg), v in agg.items():
+                print(f"| `{k}` | {g} | {wg} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
         elif "counter_name" in cols:
             agg = collections.defaultdict(list)
             for r in rows:
