@@ -661,9 +661,19 @@ void plan_direct(GemvPlan& c, int M, int K, int N, int G, int fmt) {
   const int max_waves = kGemvMaxThreads / kWave;
   c.kind = 1;
   c.mt = M <= 16 ? 1 : 2;
-  c.cols = 2;
   c.nwr = 1;
+  // Measured on MI355X (K x N = 8192 x 8192, 8192 x 28672, 28672 x 8192):
+  // two tile columns and eight K waves per workgroup, except four columns
+  // (each activation operand serving twice the weight rows) from M = 9 on for
+  // layers of 2^27 weights or more, and four K waves at M <= 8 once the grid
+  // has 512 or more column pairs.
+  c.cols = 2;
   c.nwk = 8;
+  if (M > 8 && (long)N * K >= (1L << 27)) {
+    c.cols = 4;
+  } else if (M <= 8 && N / 32 >= 512) {
+    c.nwk = 4;
+  }
   const int cols = env_int("W4_GEMV_C", 0);
   const int nwk = env_int("W4_GEMV_NWK", 0);
   const int s = env_int("W4_GEMV_S", 0);
@@ -781,6 +791,17 @@ int launch_direct(const GemvPlan& c, const uint16_t* x, int M, int K, int N, con
   const dim3 block(c.nwk * kWave);
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
+  // the one-workgroup budget (the NF4 table is static LDS on top), reserved
+  // once per instantiation: beyond 64 KB of dynamic LDS a launch needs it
+  const int budget = kGemvLdsOne - (FMT == 1 ? kLutBytes : 0);
+  if (c.nwk * kWave > kGemvMaxThreads)  // the kernel is built for at most this many threads
+    return fail(-1 /* W4_EINVAL */, "w4_gemv: plan with %d K waves exceeds the kernel's %d threads", c.nwk,
+                kGemvMaxThreads);
+  if ((long)c.lds_bytes > budget)
+    return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemv: plan needs %zu bytes of LDS (at most %d)", c.lds_bytes, budget);
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_direct_kernel<FMT, LB, MT, C, R>), budget,
+                                   "w4_gemv");
+  if (st != 0) return st;
   hipLaunchKernelGGL((gemv_direct_kernel<FMT, LB, MT, C, R>), grid, block, c.lds_bytes, s, x, M, K, N, packed,
                      scale, zero, y, partial, c.sc_pitch);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
