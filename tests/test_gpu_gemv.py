@@ -172,7 +172,8 @@ def test_gemv_decode_layer_8192(fmt, G, M):
 
 
 @pytest.mark.parametrize("fmt,G", [(o.FMT_INT4_ASYM, 128), (o.FMT_NF4, 64)])
-@pytest.mark.parametrize("M,K,N", [(1, 8192, 28672), (32, 8192, 28672), (8, 28672, 8192)])
+@pytest.mark.parametrize("M,K,N", [(1, 8192, 28672), (4, 8192, 28672), (32, 8192, 28672), (8, 28672, 8192),
+                                   (4, 28672, 8192)])
 def test_gemv_mlp_layers(fmt, G, M, K, N):
     y, y_ref = full_size_case(fmt, G, M, K, N, cfg=3, mat=0 if N == 28672 else 1, n_sample=96)
     assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
