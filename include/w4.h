@@ -299,40 +299,6 @@ int w4_attn_decode_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, int d,
                        uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * w4_salient_select/*
- * w4_salient_select/*
- * w4_attn_decode_msd -- decode attention (one query token per head) over an
- * INT4 KV cache with Multi-Scale Dequant on both products ([MSD] Abstract:
- * the cache stays quantized and the other operand of each product is
- * decomposed, which cuts the cache's HBM traffic).
- *
- * q: fp16 [B][Hq][d] device, d = 128.  Query head g of a batch row uses
- *   key/value head g / (Hq/Hkv) (grouped-query attention, Hq/Hkv <= 16).
- * K cache, per (b, h): the [L][d] matrix quantized per token (w4_quantize
- *   with G = 128 on it as W^T [N=L][K=d]) and packed by w4_pack;
- *   k_packed [B][Hkv][L*d/2], k_scale and k_zero fp16 [B][Hkv][L].
- * V cache, per (b, h): quantized per token the same way, its codes
- *   transposed to [d][L] and packed by w4_pack (as W^T [N=d][K=L]);
- *   vt_packed [B][Hkv][d*L/2], v_scale and v_zero fp16 [B][Hkv][L].
- * out: fp16 [B][Hq][d].  L must be a multiple of 256.
- *
- * Computation: the queries are split into two int8 slices per head
- * (w4_gemm_decomp's decomposition); scores = sK[t] sum_j s_j (A_j . (qK[t] -
- * zK[t])) / sqrt(d) with exact int32 products; softmax per block of 256
- * positions (max m_c, sum l_c of exp(score - m_c)); w = exp(score - m_c) *
- * sV[t] is split per head and block into two int8 slices (B_j, r_j, same
- * rule), o_c = sum_j r_j sum_t B_j (qV[t] - zV[t]) exactly in int32; the
- * blocks are combined as sum_c e^(m_c - m) o_c / sum_c e^(m_c - m) l_c.
- * Workspace (required, 16-byte aligned, no initial contents):
- * w4_workspace_bytes(W4_OP_ATTN_MSD, B, Hq, L, 0, 0) bytes.
- */
-int w4_attn_decode_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, int d,
-                       const uint8_t* k_packed, const uint16_t* k_scale, const uint16_t* k_zero,
-                       const uint8_t* vt_packed, const uint16_t* v_scale, const uint16_t* v_zero,
-                       uint16_t* out, void* ws, size_t ws_bytes, void* stream);
-
-/*
- * w4_salient_select/*
  * w4_salient_select -- the k salient input channels of a decode step, for
  * residual compensation ([DecDEC] Abstract: salient channels are those where
  * the current activations have outliers, chosen anew at every step).
