@@ -149,3 +149,36 @@ def test_tail_gemm_mx(monkeypatch, group_rows, nslices):
     y_off = call(torch.empty(full, dtype=torch.uint8, device="cuda"))
     assert np.array_equal(y_small.view(np.uint16), y_off.view(np.uint16))
     assert row_rel_l2(y_tail, y_off.astype(np.float64)) <= TOL_ROW_REL_L2
+
+
+@pytest.mark.parametrize("variant", ["msd1", "msd2", "msd3", "fixed"])
+def test_tail_only_small_m_decomp(monkeypatch, group_rows, variant):
+    """M = 256: the 16 output tiles fill a sixteenth of the CUs, so every tile
+    runs with K split over workgroups (no full-round launch).  Every output
+    against the oracle, and against the unsplit product (W4_GEMM_TAIL=0)."""
+    M, K, N, G = 256, 2048, 2048, 128
+    ns = {"msd1": 1, "msd2": 2, "msd3": 3, "fixed": 2}[variant]
+    w = wl.make_weight(73, 0, N, K)
+    x = wl.make_activations(73, 0, M, K)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    full = w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, ns)
+    assert full > w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, 0, G, ns)
+    if variant == "fixed":
+        A, S = o.decompose_fixed_ratio(x)
+        ref = o.msd_fixed_result(S[0], o.msd_accumulators(A, codes, zero, G), scale)
+        call = lambda: w4.gemm_decomp_fixed(dev(x), packed, sc, zc, G,
+                                            workspace=torch.empty(full, dtype=torch.uint8, device="cuda"))
+    else:
+        A, S = o.decompose_activations(x, ns)
+        ref = o.msd_result(S, o.msd_accumulators(A, codes, zero, G), scale)
+        call = lambda: w4.gemm_decomp(dev(x), packed, sc, zc, G, ns,
+                                      workspace=torch.empty(full, dtype=torch.uint8, device="cuda"))
+    announce("decomp tail only", dict(variant=variant, M=M, K=K, N=N))
+    y_tail = host(call())
+    assert row_rel_l2(y_tail, ref) <= TOL_ROW_REL_L2
+    monkeypatch.setenv("W4_GEMM_TAIL", "0")
+    announce("decomp unsplit", dict(variant=variant))
+    y_off = host(call())
+    assert row_rel_l2(y_off, ref) <= TOL_ROW_REL_L2
+    assert row_rel_l2(y_tail, y_off.astype(np.float64)) <= TOL_ROW_REL_L2
