@@ -68,15 +68,18 @@ __device__ __forceinline__ float row16(float v) {
 }
 
 // reduces NV arrays of 4 row values (rows 4 kb + i of the lane) over the 16
-// lanes of a row group and then over the waves through LDS; integer sums go
-// through float (exact below 2^24)
-template <bool MAX, int NV>
+// lanes of a row group and then over the waves through the LDS buffer red;
+// array a is a max when bit a of MAXMASK is set, else a sum (integer sums go
+// through float, exact below 2^24).  One barrier: the caller alternates
+// between two buffers, so the barrier of the previous reduction, which every
+// wave reaches only after reading that reduction's buffer, already ordered
+// the reads of the buffer written here.
+template <int MAXMASK, int NV>
 __device__ __forceinline__ void reduce_rows(float (&v)[NV][4], float* red, int w, int lane) {
 #pragma unroll
   for (int a = 0; a < NV; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[a][i] = row16<MAX>(v[a][i]);
-  __syncthreads();  // red is free
+    for (int i = 0; i < 4; ++i) v[a][i] = ((MAXMASK >> a) & 1) ? row16<true>(v[a][i]) : row16<false>(v[a][i]);
   if (lane % 16 == 0)
 #pragma unroll
     for (int a = 0; a < NV; ++a)
@@ -92,7 +95,7 @@ __device__ __forceinline__ void reduce_rows(float (&v)[NV][4], float* red, int w
 #pragma unroll
       for (int ww = 1; ww < kAttnWaves; ++ww) {
         const float o = red[(a * kAttnWaves + ww) * 16 + row];
-        acc = MAX ? fmaxf(acc, o) : acc + o;
+        acc = ((MAXMASK >> a) & 1) ? fmaxf(acc, o) : acc + o;
       }
       v[a][i] = acc;
     }
@@ -123,7 +126,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
     const uint8_t* __restrict__ vtp, const uint16_t* __restrict__ vs, const uint16_t* __restrict__ vz,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __align__(16) int8_t psl[2][16][kChunk];  // weight slices in the int8 operand order
-  __shared__ float red[2 * kAttnWaves * 16];
+  // two reduction buffers, used alternately: four reductions per chunk
+  // (max; sum and max; max; sums), so every chunk starts on buffer 0
+  __shared__ float red[2][2 * kAttnWaves * 16];
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nsplit = gridDim.x;
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
     float m[1][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) m[0][i] = fmaxf(fmaxf(sc[0][i], sc[1][i]), fmaxf(sc[2][i], sc[3][i]));
-    reduce_rows<true, 1>(m, red, w, lane);
+    reduce_rows<1, 1>(m, red[0], w, lane);
     float sv[4];
     int zv[4];
 #pragma unroll
@@ -239,28 +244,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
       sv[tt] = half_bits_to_float(cur.vs[tt]);
       zv[tt] = (int)half_bits_to_float(cur.vz[tt]);
     }
-    float p[4][4], l[1][4], amax[1][4];
+    float p[4][4], la[2][4];  // la[0]: row sum of exp, la[1]: row max of the weights
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      l[0][i] = 0.f;
-      amax[0][i] = 0.f;
+      la[0][i] = 0.f;
+      la[1][i] = 0.f;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const float e = __expf(sc[tt][i] - m[0][i]);
-        l[0][i] += e;
+        la[0][i] += e;
         p[tt][i] = e * sv[tt];
-        amax[0][i] = fmaxf(amax[0][i], p[tt][i]);
+        la[1][i] = fmaxf(la[1][i], p[tt][i]);
       }
     }
-    reduce_rows<false, 1>(l, red, w, lane);
-    reduce_rows<true, 1>(amax, red, w, lane);
+    reduce_rows<2, 2>(la, red[1], w, lane);
+    float(&l)[4] = la[0];
+    float(&amax)[4] = la[1];
 
     // ---- the weights split into two int8 slices per row
     float r1[4], r2[4], amax2[1][4];
     int A1[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r1[i] = amax[0][i] * (1.f / 127.f);
+      r1[i] = amax[i] * (1.f / 127.f);
       const float inv = r1[i] > 0.f ? 1.f / r1[i] : 0.f;
       amax2[0][i] = 0.f;
 #pragma unroll
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
         amax2[0][i] = fmaxf(amax2[0][i], fabsf(p[tt][i]));
       }
     }
-    reduce_rows<true, 1>(amax2, red, w, lane);
+    reduce_rows<1, 1>(amax2, red[0], w, lane);
     float zt[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
       zt[0][i] = (float)z0;  // |sum| <= 256 * 127 * 15 < 2^24: exact
       zt[1][i] = (float)z1;
     }
-    reduce_rows<false, 2>(zt, red, w, lane);  // also publishes psl (barriers inside)
+    reduce_rows<0, 2>(zt, red[1], w, lane);  // its barrier also publishes psl
 
     // ---- values: this wave's 2 tiles of 16 head dimensions, merged into the
     // running output (the next chunk writes psl only after its first barrier,
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
       const float mn = fmaxf(Mrun[i], m[0][i]);
       fa[i] = __expf(Mrun[i] - mn);
       fb[i] = __expf(m[0][i] - mn);
-      Lrun[i] = fmaf(fa[i], Lrun[i], fb[i] * l[0][i]);
+      Lrun[i] = fmaf(fa[i], Lrun[i], fb[i] * l[i]);
       Mrun[i] = mn;
     }
 #pragma unroll
