@@ -706,19 +706,21 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
   const int gpt = kTileK / G;
   const int max_waves = kGemvMaxThreads / kWave;
   c.mt = M <= 16 ? 1 : 2;
-  // Measured on MI355X (K = N = 8192, both formats): one 16-row tile column
-  // per workgroup with four K waves for M <= 2; two columns for M <= 8 (the
-  // staged activations then serve twice the weight rows); beyond, eight
+  // Measured on MI355X (K = N = 8192, 8192 x 28672, 28672 x 8192, both
+  // formats): two 16-row tile columns per workgroup with four K waves up to
+  // M = 8 (the staged activations serve twice the weight rows); beyond, eight
   // columns with one K wave each, so that the activations, which outweigh the
-  // weights per K position from M = 8 on, are staged once per 128 rows.  K is
-  // split over workgroups (fp32 partials and a second kernel) while the grid
-  // holds fewer than about 2048 waves, or while the slice's activations would
-  // not fit one staging batch or the LDS.
-  c.nwr = M <= 2 ? 1 : M <= 8 ? 2 : 8;
+  // weights per K position from M = 8 on, are staged once per 128 rows.  On
+  // layers of 2^27 weights or more (the MLP matrices): one column at M <= 2,
+  // eight columns and one K wave from M = 3 on.  K is split over workgroups
+  // (fp32 partials and a second kernel) while the grid holds fewer than about
+  // 2048 waves, or while the slice's activations would not fit one staging
+  // batch or the LDS.
+  const bool large = (long)N * K >= (1L << 27);
+  c.nwr = M <= 8 ? 2 : 8;
   c.nwk = M <= 8 ? 4 : 1;
-  // layers of 2^27 weights or more (the MLP matrices) from M = 3 on: eight
-  // columns and one K wave, 7-19 % faster there at M = 4
-  if (M > 2 && (long)N * K >= (1L << 27)) {
+  if (large && M <= 2) c.nwr = 1;
+  if (large && M > 2) {
     c.nwr = 8;
     c.nwk = 1;
   }
