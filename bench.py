@@ -694,7 +694,7 @@ def main():
         "config": {"workload": "decode_gemv_k8192_n8192", "M": list(Ms), "K": K, "N": N,
                    "formats": ["int4_asym_g128", "nf4_b64"], "launches_per_step": len(variants),
                    "timed": "HIP graph replays, %d steps per graph" % steps_per_graph},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (the 6 launches of a step)",
+        "roofline": {"bound": "hbm", "kernel": "the 6 GEMV launches of a step (gemv_kernel at M = 1 and 4, gemv_direct_kernel at M = 16)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": "packed N*K/2 + fp16 scales (+ zeros) = %d" % per_set,
