@@ -59,7 +59,10 @@ __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
 // the operand layout (and of the plain layout if asked).
 constexpr double kFixedRatio = 254.0;
 
-template <int NS, bool FIXED>
+// CH > 0: the row's K <= CH * 8 * kDecompThreads positions are read once into
+// registers (CH 16-byte chunks per thread) and every pass reuses them; CH = 0
+// re-reads the row in each pass.
+template <int NS, bool FIXED, int CH>
 __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
     const uint16_t* __restrict__ x, int M, int K, int8_t* __restrict__ slices_op, int8_t* __restrict__ slices_out,
     float* __restrict__ tok_scale) {
@@ -69,8 +72,27 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
   const int m = blockIdx.x;
   const uint16_t* xr = x + (size_t)m * K;
 
-  auto load8 = [&](int k, double* v) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(xr + k);
+  u32x4 xc[CH > 0 ? CH : 1];
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int k = 8 * threadIdx.x + c * kStep;
+      if (k < K) xc[c] = *reinterpret_cast<const u32x4*>(xr + k);
+    }
+  }
+  // f(k, w) for each of this thread's 16-byte chunks w (K positions k .. k + 7)
+  auto for_chunks = [&](auto&& f) {
+    if constexpr (CH > 0) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int k = 8 * threadIdx.x + c * kStep;
+        if (k < K) f(k, xc[c]);
+      }
+    } else {
+      for (int k = 8 * threadIdx.x; k < K; k += kStep) f(k, *reinterpret_cast<const u32x4*>(xr + k));
+    }
+  };
+  auto load8 = [&](const u32x4& w, double* v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = (double)half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
@@ -88,12 +110,12 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
   };
 
   double amax = 0.0;
-  for (int k = 8 * threadIdx.x; k < K; k += kStep) {
+  for_chunks([&](int, const u32x4& w) {
     double v[8];
-    load8(k, v);
+    load8(w, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(v[i]));
-  }
+  });
   amax = block_max(amax, red);
   double s[NS];
   s[0] = (double)(float)(amax / 127.0);
@@ -101,9 +123,9 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     double amax_next = 0.0;
-    for (int k = 8 * threadIdx.x; k < K; k += kStep) {
+    for_chunks([&](int k, const u32x4& w) {
       double v[8];
-      load8(k, v);
+      load8(w, v);
       int a[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -119,7 +141,7 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
         if (!FIXED && j + 1 < NS) amax_next = fmax(amax_next, fabs(r - s[j] * q));
       }
       store8(j, k, a);
-    }
+    });
     if (FIXED && j == 1) {
       if (threadIdx.x == 0) tok_scale[(size_t)M + m] = (float)(s[0] / kFixedRatio);
     } else {
@@ -133,9 +155,15 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
 
 int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, int8_t* slices_op, int8_t* slices_out,
                      float* tok_scale, hipStream_t s) {
-#define W4_DECOMP(NS, FX)                                                                                   \
-  hipLaunchKernelGGL((decompose_kernel<NS, FX>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, \
-                     slices_out, tok_scale)
+#define W4_DECOMP(NS, FX)                                                                                        \
+  do {                                                                                                           \
+    if (K <= 4 * 8 * kDecompThreads)                                                                             \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, \
+                         slices_out, tok_scale);                                                                 \
+    else                                                                                                         \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 0>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, \
+                         slices_out, tok_scale);                                                                 \
+  } while (0)
   if (fixed)
     W4_DECOMP(2, true);
   else if (nslices == 1)
