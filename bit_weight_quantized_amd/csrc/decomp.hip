@@ -59,24 +59,33 @@ __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
 // the operand layout (and of the plain layout if asked).
 constexpr double kFixedRatio = 254.0;
 
-// CH > 0: the row's K <= CH * 8 * kDecompThreads positions are read once into
+// CH > 0: the row's K <= CH * 8 * (row threads) positions are read once into
 // registers (CH 16-byte chunks per thread) and every pass reuses them; CH = 0
-// re-reads the row in each pass.
-template <int NS, bool FIXED, int CH>
+// re-reads the row in each pass.  WR: one wave per row (K <= 512, four rows
+// per workgroup, wave-level maxima); otherwise the workgroup takes one row.
+template <int NS, bool FIXED, int CH, bool WR>
 __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
     const uint16_t* __restrict__ x, int M, int K, int8_t* __restrict__ slices_op, int8_t* __restrict__ slices_out,
     float* __restrict__ tok_scale) {
   static_assert(!FIXED || NS == 2, "the fixed ratio defines a second slice");
+  static_assert(!WR || CH == 1, "a wave's row is one chunk per lane");
   __shared__ double red[kDecompThreads / kWave];
-  constexpr int kStep = 8 * kDecompThreads;
-  const int m = blockIdx.x;
+  constexpr int kRowThreads = WR ? kWave : kDecompThreads;
+  constexpr int kStep = 8 * kRowThreads;
+  const int rt = WR ? (int)threadIdx.x % kWave : (int)threadIdx.x;  // thread within the row
+  const int m = WR ? (int)blockIdx.x * (kDecompThreads / kWave) + (int)threadIdx.x / kWave : (int)blockIdx.x;
+  if (WR && m >= M) return;  // whole waves leave; no workgroup barrier follows in this variant
   const uint16_t* xr = x + (size_t)m * K;
+  auto row_max = [&](double v) {  // the WR variant has no workgroup barrier
+    if constexpr (WR) return wave_max_d(v);
+    else return block_max(v, red);
+  };
 
   u32x4 xc[CH > 0 ? CH : 1];
   if constexpr (CH > 0) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int k = 8 * threadIdx.x + c * kStep;
+      const int k = 8 * rt + c * kStep;
       if (k < K) xc[c] = *reinterpret_cast<const u32x4*>(xr + k);
     }
   }
@@ -85,11 +94,11 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
     if constexpr (CH > 0) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const int k = 8 * threadIdx.x + c * kStep;
+        const int k = 8 * rt + c * kStep;
         if (k < K) f(k, xc[c]);
       }
     } else {
-      for (int k = 8 * threadIdx.x; k < K; k += kStep) f(k, *reinterpret_cast<const u32x4*>(xr + k));
+      for (int k = 8 * rt; k < K; k += kStep) f(k, *reinterpret_cast<const u32x4*>(xr + k));
     }
   };
   auto load8 = [&](const u32x4& w, double* v) {
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(v[i]));
   });
-  amax = block_max(amax, red);
+  amax = row_max(amax);
   double s[NS];
   s[0] = (double)(float)(amax / 127.0);
 
@@ -143,10 +152,10 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
       store8(j, k, a);
     });
     if (FIXED && j == 1) {
-      if (threadIdx.x == 0) tok_scale[(size_t)M + m] = (float)(s[0] / kFixedRatio);
+      if (rt == 0) tok_scale[(size_t)M + m] = (float)(s[0] / kFixedRatio);
     } else {
-      if (threadIdx.x == 0) tok_scale[(size_t)j * M + m] = (float)s[j];
-      if (!FIXED && j + 1 < NS) s[j + 1] = (double)(float)(block_max(amax_next, red) / 127.0);
+      if (rt == 0) tok_scale[(size_t)j * M + m] = (float)s[j];
+      if (!FIXED && j + 1 < NS) s[j + 1] = (double)(float)(row_max(amax_next) / 127.0);
     }
   }
 }
@@ -156,13 +165,17 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
 int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, int8_t* slices_op, int8_t* slices_out,
                      float* tok_scale, hipStream_t s) {
 #define W4_DECOMP(NS, FX)                                                                                        \
-  do {                                                                                                           \
-    if (K <= 4 * 8 * kDecompThreads)                                                                             \
-      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, \
-                         slices_out, tok_scale);                                                                 \
-    else                                                                                                         \
-      hipLaunchKernelGGL((decompose_kernel<NS, FX, 0>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K, slices_op, \
-                         slices_out, tok_scale);                                                                 \
+  do {                                                                                                            \
+    constexpr int kRows = kDecompThreads / kWave;                                                                 \
+    if (K <= 8 * kWave)                                                                                           \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 1, true>), dim3((M + kRows - 1) / kRows), dim3(kDecompThreads), \
+                         0, s, x, M, K, slices_op, slices_out, tok_scale);                                        \
+    else if (K <= 4 * 8 * kDecompThreads)                                                                         \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4, false>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K,      \
+                         slices_op, slices_out, tok_scale);                                                       \
+    else                                                                                                          \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 0, false>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K,      \
+                         slices_op, slices_out, tok_scale);                                                       \
   } while (0)
   if (fixed)
     W4_DECOMP(2, true);
