@@ -372,10 +372,12 @@ int launch_f16(const uint16_t* x, int M, int K, int N, const uint8_t* packed, co
   const int gm = gemm_group_rows();
   const bool tail = S == 1 && tp.S > 1 && tpart;
   const long main_tiles = tail ? tp.main : tiles;
-  hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)main_tiles, (unsigned)S), dim3(kF16Threads),
-                     kLds, s, x, M, K, N, packed, scale, zero, y, partial, nullptr, 0, gm);
-  int st2 = check_launch("gemm");
-  if (st2 != 0) return st2;
+  int st2;
+  if (main_tiles > 0) {  // a tail-only plan has no full rounds
+    hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)main_tiles, (unsigned)S),
+                       dim3(kF16Threads), kLds, s, x, M, K, N, packed, scale, zero, y, partial, nullptr, 0, gm);
+    if ((st2 = check_launch("gemm")) != 0) return st2;
+  }
   if (tail) {
     hipLaunchKernelGGL((gemm_f16_kernel<PATH, FMT, GPT>), dim3((unsigned)tp.r, (unsigned)tp.S), dim3(kF16Threads),
                        kLds, s, x, M, K, N, packed, scale, zero, y, nullptr, tpart, (int)tp.main, gm);
