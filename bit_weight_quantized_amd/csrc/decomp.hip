@@ -28,7 +28,12 @@ namespace w4 {
 namespace {
 
 constexpr int kDecompThreads = 256;
+// few rows (M <= kFewRows): one 1024-thread workgroup per row, so that the
+// grid still fills the CUs and each thread walks a quarter of the row
+constexpr int kDecompWide = 1024;
+constexpr int kFewRows = 512;
 
+template <int T>
 __device__ __forceinline__ double block_max(double v, double* red) {
   v = wave_max_d(v);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -36,7 +41,7 @@ __device__ __forceinline__ double block_max(double v, double* red) {
   if (lane == 0) red[wave] = v;
   __syncthreads();
   double r = red[0];
-  for (int w = 1; w < kDecompThreads / kWave; ++w) r = fmax(r, red[w]);
+  for (int w = 1; w < T / kWave; ++w) r = fmax(r, red[w]);
   return r;
 }
 
@@ -59,26 +64,27 @@ __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
 // the operand layout (and of the plain layout if asked).
 constexpr double kFixedRatio = 254.0;
 
-// CH > 0: the row's K <= CH * 8 * (row threads) positions are read once into
-// registers (CH 16-byte chunks per thread) and every pass reuses them; CH = 0
-// re-reads the row in each pass.  WR: one wave per row (K <= 512, four rows
-// per workgroup, wave-level maxima); otherwise the workgroup takes one row.
-template <int NS, bool FIXED, int CH, bool WR>
-__global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
+// T threads per workgroup.  CH > 0: the row's K <= CH * 8 * (row threads)
+// positions are read once into registers (CH 16-byte chunks per thread) and
+// every pass reuses them; CH = 0 re-reads the row in each pass.  WR: one wave
+// per row (K <= 512, T / 64 rows per workgroup, wave-level maxima);
+// otherwise the workgroup takes one row.
+template <int NS, bool FIXED, int CH, bool WR, int T>
+__global__ __launch_bounds__(T) void decompose_kernel(
     const uint16_t* __restrict__ x, int M, int K, int8_t* __restrict__ slices_op, int8_t* __restrict__ slices_out,
     float* __restrict__ tok_scale) {
   static_assert(!FIXED || NS == 2, "the fixed ratio defines a second slice");
   static_assert(!WR || CH == 1, "a wave's row is one chunk per lane");
-  __shared__ double red[kDecompThreads / kWave];
-  constexpr int kRowThreads = WR ? kWave : kDecompThreads;
+  __shared__ double red[T / kWave];
+  constexpr int kRowThreads = WR ? kWave : T;
   constexpr int kStep = 8 * kRowThreads;
   const int rt = WR ? (int)threadIdx.x % kWave : (int)threadIdx.x;  // thread within the row
-  const int m = WR ? (int)blockIdx.x * (kDecompThreads / kWave) + (int)threadIdx.x / kWave : (int)blockIdx.x;
+  const int m = WR ? (int)blockIdx.x * (T / kWave) + (int)threadIdx.x / kWave : (int)blockIdx.x;
   if (WR && m >= M) return;  // whole waves leave; no workgroup barrier follows in this variant
   const uint16_t* xr = x + (size_t)m * K;
   auto row_max = [&](double v) {  // the WR variant has no workgroup barrier
     if constexpr (WR) return wave_max_d(v);
-    else return block_max(v, red);
+    else return block_max<T>(v, red);
   };
 
   u32x4 xc[CH > 0 ? CH : 1];
@@ -165,17 +171,20 @@ __global__ __launch_bounds__(kDecompThreads) void decompose_kernel(
 int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, int8_t* slices_op, int8_t* slices_out,
                      float* tok_scale, hipStream_t s) {
 #define W4_DECOMP(NS, FX)                                                                                        \
-  do {                                                                                                            \
-    constexpr int kRows = kDecompThreads / kWave;                                                                 \
-    if (K <= 8 * kWave)                                                                                           \
-      hipLaunchKernelGGL((decompose_kernel<NS, FX, 1, true>), dim3((M + kRows - 1) / kRows), dim3(kDecompThreads), \
-                         0, s, x, M, K, slices_op, slices_out, tok_scale);                                        \
-    else if (K <= 4 * 8 * kDecompThreads)                                                                         \
-      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4, false>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K,      \
-                         slices_op, slices_out, tok_scale);                                                       \
-    else                                                                                                          \
-      hipLaunchKernelGGL((decompose_kernel<NS, FX, 0, false>), dim3(M), dim3(kDecompThreads), 0, s, x, M, K,      \
-                         slices_op, slices_out, tok_scale);                                                       \
+  do {                                                                                                          \
+    constexpr int kRows = kDecompThreads / kWave;                                                               \
+    if (K <= 8 * kWave)                                                                                         \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 1, true, kDecompThreads>), dim3((M + kRows - 1) / kRows),    \
+                         dim3(kDecompThreads), 0, s, x, M, K, slices_op, slices_out, tok_scale);                \
+    else if (M <= kFewRows && K <= 4 * 8 * kDecompWide)                                                         \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4, false, kDecompWide>), dim3(M), dim3(kDecompWide), 0, s, x, \
+                         M, K, slices_op, slices_out, tok_scale);                                               \
+    else if (K <= 4 * 8 * kDecompThreads)                                                                       \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4, false, kDecompThreads>), dim3(M), dim3(kDecompThreads), 0, \
+                         s, x, M, K, slices_op, slices_out, tok_scale);                                         \
+    else                                                                                                        \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 0, false, kDecompThreads>), dim3(M), dim3(kDecompThreads), 0, \
+                         s, x, M, K, slices_op, slices_out, tok_scale);                                         \
   } while (0)
   if (fixed)
     W4_DECOMP(2, true);
