@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
-    "lib", "lib_path", "quantize", "pack", "gemv", "gemm", "gemm_decomp", "gemm_decomp_fixed",
+    "lib", "lib_path", "quantize", "pack", "gemv", "gemv_plan", "gemm", "gemm_decomp", "gemm_decomp_fixed",
     "salient_select", "residual_correct", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
     "workspace_bytes", "nf4_levels", "version",
 ]
@@ -61,6 +61,7 @@ def lib():
         L.w4_quantize.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p]
         L.w4_pack.argtypes = [_p, _i, _i, _p, _p]
         L.w4_gemv.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p]
+        L.w4_gemv_plan.argtypes = [_i, _i, _i, _i, _i, _p, _i]
         L.w4_gemm.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
         L.w4_gemm_decomp.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_gemm_decomp_fixed.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]
@@ -78,7 +79,7 @@ def lib():
         L.w4_last_error.argtypes = []
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
-        for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
+        for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemv_plan", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
                    "w4_salient_select", "w4_residual_correct", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
                    "w4_attn_decode_msd",
                    "w4_nf4_levels"):
@@ -168,6 +169,18 @@ def gemv(x, packed, scale, zero, G: int, fmt: int, *, out=None, workspace=None, 
                                     _ptr(out), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(stream)))
     return out
+
+
+GEMV_PLAN_FIELDS = ("kernel", "cols", "token_tiles", "row_waves", "k_waves", "k_slices", "staged_units",
+                    "workgroups", "threads", "lds_bytes", "lds_budget", "static_lds", "workspace_bytes", "ok")
+
+
+def gemv_plan(M: int, K: int, N: int, G: int, fmt: int) -> dict:
+    """The launch plan w4_gemv would use for this shape (host only; the
+    W4_GEMV_* environment overrides of this process apply)."""
+    buf = (ctypes.c_int64 * len(GEMV_PLAN_FIELDS))()
+    _check("w4_gemv_plan", lib().w4_gemv_plan(M, K, N, G, fmt, ctypes.cast(buf, _p), len(GEMV_PLAN_FIELDS)))
+    return dict(zip(GEMV_PLAN_FIELDS, (int(v) for v in buf)))
 
 
 def gemm(x, packed, scale, zero, G: int, fmt: int, mode: int, *, out=None, workspace=None, stream=None):

@@ -774,14 +774,26 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
   return c;
 }
 
+size_t gemv_lds_budget(int fmt) { return (size_t)(kGemvLdsOne - (fmt == 1 ? kLutBytes : 0)); }
+size_t gemv_static_lds(int fmt) { return fmt == 1 ? (size_t)kLutBytes : 4; }
+int gemv_plan_threads(const GemvPlan& c) { return (c.kind == 1 ? 1 : c.nwr) * c.nwk * kWave; }
+
+int check_gemv_plan(const GemvPlan& c, int fmt) {
+  if (gemv_plan_threads(c) > kGemvMaxThreads)  // the kernels are built for at most this many threads
+    return fail(-1 /* W4_EINVAL */, "w4_gemv: plan with %d x %d waves exceeds the kernel's %d threads",
+                c.kind == 1 ? 1 : c.nwr, c.nwk, kGemvMaxThreads);
+  if (c.lds_bytes > gemv_lds_budget(fmt))
+    return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemv: plan needs %zu bytes of LDS (at most %zu)", c.lds_bytes,
+                gemv_lds_budget(fmt));
+  return 0;
+}
+
 namespace {
 
 template <int FMT, int LB, int MT, int XU>
 int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
              const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
-  if (c.nwr * c.nwk * kWave > kGemvMaxThreads)  // the kernel is built for at most this many threads
-    return fail(-1 /* W4_EINVAL */, "w4_gemv: plan with %d x %d waves exceeds the kernel's %d threads", c.nwr, c.nwk,
-                kGemvMaxThreads);
+  if (const int bad = check_gemv_plan(c, FMT)) return bad;
   const dim3 block(c.nwr * c.nwk * kWave);
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
@@ -804,12 +816,8 @@ int launch_direct(const GemvPlan& c, const uint16_t* x, int M, int K, int N, con
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   // the one-workgroup budget (the NF4 table is static LDS on top), reserved
   // once per instantiation: beyond 64 KB of dynamic LDS a launch needs it
-  const int budget = kGemvLdsOne - (FMT == 1 ? kLutBytes : 0);
-  if (c.nwk * kWave > kGemvMaxThreads)  // the kernel is built for at most this many threads
-    return fail(-1 /* W4_EINVAL */, "w4_gemv: plan with %d K waves exceeds the kernel's %d threads", c.nwk,
-                kGemvMaxThreads);
-  if ((long)c.lds_bytes > budget)
-    return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemv: plan needs %zu bytes of LDS (at most %d)", c.lds_bytes, budget);
+  const int budget = (int)gemv_lds_budget(FMT);
+  if (const int bad = check_gemv_plan(c, FMT)) return bad;
   const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_direct_kernel<FMT, LB, MT, C, R>), budget,
                                    "w4_gemv");
   if (st != 0) return st;
@@ -860,5 +868,6 @@ int launch_gemv(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const
   if (G == 64) return launch_mt<1, 8>(c, x, M, K, N, packed, scale, zero, y, ws, s);
   return launch_mt<1, 16>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
+
 
 }  // namespace w4

@@ -3,7 +3,7 @@
 // IEEE operations (no contraction), and the fp64 -> fp32 -> fp16 roundings are
 // explicit round-to-nearest-even conversions.
 //
-// INT4 asymmetric: scale and zero point shared within a group ("MixPE:
+// INT4 asymmetric: one scale and one zero point per group ("MixPE:
 // Quantization and Hardware Co-design for Efficient LLM Inference", Abstract).
 // NF4: 16-level NormalFloat codebook with a per-block absmax ("Fast NF4
 // Dequantization Kernels for Large Language Model Inference", Abstract).

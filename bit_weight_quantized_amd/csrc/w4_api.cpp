@@ -182,6 +182,33 @@ int w4_gemv(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
   return launch_gemv(plan, x, M, K, N, packed, scale, zero, G, fmt, y, ws, (hipStream_t)stream);
 }
 
+int w4_gemv_plan(int M, int K, int N, int G, int fmt, int64_t* out, int n_out) {
+  g_last_error[0] = '\0';
+  int st;
+  if ((st = check_matmul_shape("w4_gemv_plan", M, K, N, G)) != W4_OK) return st;
+  if (M > 32) return fail(W4_EINVAL, "w4_gemv_plan: M must be <= 32 (got %d)", M);
+  if (fmt != W4_INT4_ASYM && fmt != W4_NF4) return fail(W4_EINVAL, "w4_gemv_plan: unknown fmt %d", fmt);
+  if (!out || n_out < 0) return fail(W4_EINVAL, "w4_gemv_plan: out must be non-null");
+  const GemvPlan c = plan_gemv(M, K, N, G, fmt);
+  const int64_t v[W4_GEMV_PLAN_FIELDS] = {c.kind,
+                                          c.cols,
+                                          c.mt,
+                                          c.kind == 1 ? 1 : c.nwr,
+                                          c.nwk,
+                                          c.s,
+                                          c.xu,
+                                          c.row_blocks,
+                                          gemv_plan_threads(c),
+                                          (int64_t)c.lds_bytes,
+                                          (int64_t)gemv_lds_budget(fmt),
+                                          (int64_t)gemv_static_lds(fmt),
+                                          (int64_t)c.ws_bytes,
+                                          check_gemv_plan(c, fmt) == 0 ? 1 : 0};
+  for (int i = 0; i < n_out && i < W4_GEMV_PLAN_FIELDS; ++i) out[i] = v[i];
+  g_last_error[0] = '\0';
+  return W4_OK;
+}
+
 int w4_gemm(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
             const uint16_t* scale, const uint16_t* zero, int G, int fmt, int mode,
             uint16_t* y, void* ws, size_t ws_bytes, void* stream) {

@@ -36,6 +36,14 @@ struct GemvPlan {
   size_t lds_bytes, ws_bytes;
 };
 GemvPlan plan_gemv(int M, int K, int N, int G, int fmt);
+// Bounds every GEMV plan must meet: at most 512 threads per workgroup (the
+// kernels' launch bound) and dynamic LDS within gemv_lds_budget (the static
+// LDS, gemv_static_lds, comes on top).  check_gemv_plan returns 0 or a
+// negative w4_status with the error text recorded.
+size_t gemv_lds_budget(int fmt);
+size_t gemv_static_lds(int fmt);
+int gemv_plan_threads(const GemvPlan& c);
+int check_gemv_plan(const GemvPlan& c, int fmt);
 int launch_gemv(const GemvPlan& plan, const uint16_t* x, int M, int K, int N,
                 const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
                 int G, int fmt, uint16_t* y, void* ws, hipStream_t s);

@@ -93,7 +93,7 @@ typedef enum {
 /*
  * w4_quantize -- quantize fp32 weights W^T [N][K] per group of G along K.
  *
- * fmt == W4_INT4_ASYM ([MixPE]: scale and zero shared within a group), per
+ * fmt == W4_INT4_ASYM ([MixPE]: one scale and one zero point per group), per
  * group, in fp64: lo = min(0, min w), hi = max(0, max w);
  * s = fp16(fp32((hi - lo) / 15)); z = clamp(rint(-lo / s), 0, 15);
  * q = clamp(rint(w / s) + z, 0, 15); a group with s == 0 gets q = z = 0.
@@ -137,6 +137,23 @@ int w4_pack(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream);
 int w4_gemv(const uint16_t* x, int M, int K, int N,
             const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
             int G, int fmt, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * w4_gemv_plan -- host-only introspection: the launch plan w4_gemv would use
+ * for this shape and format on this thread right now (the W4_GEMV_*
+ * environment overrides included).  Writes min(n_out, W4_GEMV_PLAN_FIELDS)
+ * int64 values to out (host memory), in this order:
+ *   0 kernel (0 = staged activations, 1 = direct operand loads),
+ *   1 tile columns per wave, 2 token tiles of 16, 3 row waves,
+ *   4 K waves, 5 K slices over workgroups, 6 staged units per thread,
+ *   7 workgroups along N, 8 threads per workgroup, 9 dynamic LDS bytes,
+ *   10 dynamic LDS budget, 11 static LDS bytes, 12 workspace bytes,
+ *   13 1 when the plan meets the kernels' bounds (threads <= 512, dynamic
+ *      LDS within budget), else 0 -- w4_gemv refuses such a plan.
+ * Shape rules and errors as for w4_gemv; nothing touches a device.
+ */
+#define W4_GEMV_PLAN_FIELDS 14
+int w4_gemv_plan(int M, int K, int N, int G, int fmt, int64_t* out, int n_out);
 
 /*
  * w4_gemm -- prefill-shaped product y[M][N] = x[M][K] . W' for any M >= 1 on
@@ -252,8 +269,10 @@ int w4_pack_mx(const uint8_t* codes, int K, int N, uint8_t* packed, void* stream
  * (1 or 2) MXFP4 slices: slice 1 = MXFP4(x), slice 2 = MXFP4(x - slice 1),
  * per token and block of 32, in fp64.  Each slice meets the weights on the
  * block-scaled fp4 matrix cores, which apply both E8M0 scales; the products
- * accumulate in fp32.  Two slices: at most 2^(e1 - 2) < amax/12 error per
- * element of a block (e1 the first slice's exponent, amax the block's max).
+ * accumulate in fp32.  Two slices: at most 2^(e1 - 3) error per element of a
+ * block, which is 1/64 of 2^(e1 + 3), the power of two above the first
+ * slice's largest value 6 * 2^e1 ([MSD]'s 1/64 per block), and below
+ * amax/24 (e1 the first slice's exponent, amax the block's max).
  *
  * Requires K % 128 == 0, N % 16 == 0, x and y 16-byte aligned, operands below
  * 4 GiB.  Optional outputs (NULL to skip): slices_out u8 [nslices][M][K/2]

@@ -93,14 +93,14 @@ def nf4_codebook() -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# INT4 asymmetric quantization  ([MixPE] Abstract: scale and zero point are
-# shared within each quantization group)
+# INT4 asymmetric quantization  ([MixPE] Abstract: one scale and one zero
+# point per quantization group)
 # --------------------------------------------------------------------------
 def quantize_int4_asym(wt: np.ndarray, G: int):
     """Quantize W^T [N][K] (fp32) per (row n, group of G along K).
 
-    Steps for each group, all in fp64 (READING: the pages say only that a
-    scale and a zero point are shared within a group):
+    Steps for each group, all in fp64 (READING: the pages give only one
+    scale and one zero point per group):
 
     1. lo = min(0, min w), hi = max(0, max w)  (range widened to hold 0, so the
        zero point is always a valid code);
@@ -535,8 +535,14 @@ def decompose_mxfp4(x, nslices: int = 2):
     exponents [nslices][M][K/32].
 
     Bound: pass 1 leaves |r| <= 2^e1 (half the widest E2M1 gap, 2, at the
-    top binade); pass 2 then has e2 <= e1 - 2 and leaves |r| <= 2^e2 <=
-    2^e1 / 4 < amax / 12 per block (amax > 3 * 2^e1 by the scale rule)."""
+    top binade).  Pass 2 then has e2 <= e1 - 2.  With e2 = e1 - 2 the
+    residual lies within 4 * 2^e2, below the top binade, so it is left within
+    half the gap of [2, 4]: 2^(e2 - 1) = 2^(e1 - 3); with e2 <= e1 - 3 it is
+    left within 2^e2 <= 2^(e1 - 3).  So |x - slice 1 - slice 2| <= 2^(e1 - 3)
+    = 2^(e1 + 3) / 64 per block, where 2^(e1 + 3) is the power of two just
+    above the first slice's largest value 6 * 2^e1: the 1/64 per block of the
+    MSD abstract (the bound is attained).  Against the block's maximum,
+    2^(e1 - 3) < amax / 24 (amax > 3 * 2^e1 by the scale rule)."""
     r = np.asarray(x).astype(np.float64)
     M, K = r.shape
     C = np.zeros((nslices, M, K), dtype=np.uint8)

@@ -47,3 +47,22 @@ def upload_weights(codes, scale, zero):
 
 def row_rel_l2(y_gpu, y_ref):
     return o.max_row_rel_l2(np.asarray(y_gpu, dtype=np.float64), y_ref)
+
+
+def assert_elementwise(y_gpu, y_ref, rel=2.0 ** -10):
+    """Per-element guard under the row gate: |y - y_ref| <= rel * (|y_ref| +
+    rms of y_ref's row).  A correct kernel's error is the fp16 rounding of
+    the output (2^-11 relative) plus fp32 accumulation and, for fp16 weight
+    operands, their rounding (about 2^-12 of the row's rms); one wrong zero
+    point or scale in a group moves its outputs by a few percent of the
+    row's rms, which the row-relative L2 norm over thousands of columns
+    would hide."""
+    y = np.asarray(y_gpu, dtype=np.float64)
+    ref = np.asarray(y_ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    bound = rel * (np.abs(ref) + rms)
+    bad = np.abs(y - ref) > bound
+    if bad.any():
+        m, n = np.argwhere(bad)[0]
+        raise AssertionError(f"{int(bad.sum())} outputs beyond the per-element bound; first at [{m},{n}]: "
+                             f"{y[m, n]} vs {ref[m, n]} (bound {bound[m, n]:.3g})")

@@ -11,8 +11,8 @@ import torch
 import bit_weight_quantized_amd as w4
 import oracle as o
 import workloads as wl
-from gpu_helpers import (TOL_ROW_REL_L2, announce, dev, host, oracle_weights, require_gpu,
-                         row_rel_l2, upload_weights)
+from gpu_helpers import (TOL_ROW_REL_L2, announce, assert_elementwise, dev, host, oracle_weights,
+                         require_gpu, row_rel_l2, upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -230,3 +230,63 @@ def test_decomp_fixed_prefill_m2048_k5120_n25600():
     ref = o.msd_fixed_result(S[0], o.msd_accumulators(A, rc, rz, G), rs)
     assert row_rel_l2(y[:, rows], ref) <= TOL_ROW_REL_L2
 
+
+
+# ------------------------------------------------- decoder layer at M = 256
+# The 70B-style layer's products (hidden 8192, intermediate 28672, 8 KV heads
+# of 128): index in the layer order q, k, v, o, gate, up, down.
+LAYER_INDEX = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6}
+
+
+@pytest.mark.parametrize("fixed", [False, True], ids=["adaptive", "fixed"])
+@pytest.mark.parametrize("name,K,N", [("q", 8192, 8192), ("k", 8192, 1024), ("gate", 8192, 28672),
+                                      ("down", 28672, 8192)])
+def test_decomp_decoder_layer_m256(name, K, N, fixed):
+    """Two-slice MSD (adaptive and fixed-ratio scales) on decoder-layer
+    products at M = 256: the slices and token scales bit-exact over the whole
+    input (these shapes take the 1024-thread decomposition, which holds rows
+    of up to 32768 positions in registers), the output on sampled columns
+    (including the split-K tail's, when the plan has one)."""
+    M, G = 256, 128
+    w = wl.make_weight(5, LAYER_INDEX[name], N, K)
+    x = wl.make_activations(5, 0 if K == 8192 else 6, M, K)
+    announce("decomp layer quantize", dict(name=name, K=K, N=N))
+    codes, scale, zero = w4.quantize(dev(w), G, w4.INT4_ASYM)
+    packed = w4.pack(codes)
+    sl = torch.empty((2, M, K), dtype=torch.int8, device="cuda")
+    ts = torch.empty((2, M), dtype=torch.float32, device="cuda")
+    announce("decomp layer", dict(name=name, M=M, K=K, N=N, fixed=fixed))
+    if fixed:
+        y, _, _, _ = w4.gemm_decomp_fixed(dev(x), packed, scale, zero, G, slices_out=sl, tok_scale_out=ts)
+        A, S = o.decompose_fixed_ratio(x)
+    else:
+        y, _, _, _ = w4.gemm_decomp(dev(x), packed, scale, zero, G, 2, slices_out=sl, tok_scale_out=ts)
+        A, S = o.decompose_activations(x, 2)
+    y = host(y)
+    assert np.array_equal(host(sl), A)
+    assert np.array_equal(host(ts).view(np.uint32), S.view(np.uint32))
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(43).choice(N, 48, replace=False)]))
+    rc, rs, rz = o.quantize_int4_asym(w[rows], G)
+    assert np.array_equal(host(codes[rows]), rc)
+    D = o.msd_accumulators(A, rc, rz, G)
+    ref = o.msd_fixed_result(S[0], D, rs) if fixed else o.msd_result(S, D, rs)
+    assert row_rel_l2(y[:, rows], ref) <= TOL_ROW_REL_L2
+    assert_elementwise(y[:, rows], ref)
+
+
+@pytest.mark.parametrize("nslices", [1, 3])
+@pytest.mark.parametrize("K", [8192, 28672])
+def test_decomp_slices_m256_long_rows(nslices, K):
+    """One and three slices at M = 256 on the decoder layer's row lengths:
+    slices and scales bit-exact, every output within tolerance."""
+    M, N, G = 256, 256, 128
+    x = wl.make_activations(5, 0 if K == 8192 else 6, M, K)
+    codes, scale, zero = o.quantize_int4_asym(wl.make_weight(320, 0, N, K), G)
+    announce("decomp long rows", dict(nslices=nslices, M=M, K=K, N=N))
+    y, sl, ts, _ = run_decomp(x, codes, scale, zero, G, nslices, with_acc=False)
+    A, S = o.decompose_activations(x, nslices)
+    assert np.array_equal(sl, A)
+    assert np.array_equal(ts.view(np.uint32), S.view(np.uint32))
+    ref = o.msd_result(S, o.msd_accumulators(A, codes, zero, G), scale)
+    assert row_rel_l2(y, ref) <= TOL_ROW_REL_L2
+    assert_elementwise(y, ref)

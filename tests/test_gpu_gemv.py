@@ -11,7 +11,7 @@ import torch
 import bit_weight_quantized_amd as w4
 import oracle as o
 import workloads as wl
-from gpu_helpers import (TOL_ROW_REL_L2, announce, dev, host, oracle_weights, require_gpu,
+from gpu_helpers import (TOL_ROW_REL_L2, announce, assert_elementwise, dev, host, oracle_weights, require_gpu,
                          row_rel_l2, upload_weights)
 
 pytestmark = pytest.mark.gpu
@@ -37,14 +37,11 @@ def run_small(fmt, G, M, K, N, seed, outliers=True):
 def test_gemv_small(fmt, G, M, K, N):
     if K % G:
         pytest.skip("K not a multiple of G")
-    if (M, K, N) == (17, 128, 16):
-        pytest.skip("this case faulted under a launch plan (1024-thread direct workgroups, beyond the kernel's "
-                    "512-thread bound) that has since been removed and is now refused on the host; the case stays "
-                    "skipped until that fix has been reviewed")
     y, y_ref = run_small(fmt, G, M, K, N, seed=100 + M)
     assert y.shape == (M, N)
     err = row_rel_l2(y, y_ref)
     assert err <= TOL_ROW_REL_L2, err
+    assert_elementwise(y, y_ref)
 
 
 @pytest.mark.parametrize("nwr,nwk,s", [(1, 1, 1), (1, 4, 1), (2, 3, 1), (4, 2, 1), (1, 8, 1), (1, 2, 3),
@@ -169,11 +166,26 @@ def full_size_case(fmt, G, M, K, N, cfg, mat, n_sample=160):
 def test_gemv_decode_layer_8192(fmt, G, M):
     y, y_ref = full_size_case(fmt, G, M, 8192, 8192, cfg=2, mat=0)
     assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
+    assert_elementwise(y, y_ref)
 
 
+# Every (M, matrix) point of the MLP-shaped workload: up/gate K=8192, N=28672
+# and down K=28672, N=8192 at M = 1, 8, 32 (plus M = 4, a staged-kernel plan).
 @pytest.mark.parametrize("fmt,G", [(o.FMT_INT4_ASYM, 128), (o.FMT_NF4, 64)])
-@pytest.mark.parametrize("M,K,N", [(1, 8192, 28672), (4, 8192, 28672), (32, 8192, 28672), (8, 28672, 8192),
-                                   (4, 28672, 8192)])
+@pytest.mark.parametrize("M,K,N", [(1, 8192, 28672), (4, 8192, 28672), (8, 8192, 28672), (32, 8192, 28672),
+                                   (1, 28672, 8192), (4, 28672, 8192), (8, 28672, 8192), (32, 28672, 8192)])
 def test_gemv_mlp_layers(fmt, G, M, K, N):
     y, y_ref = full_size_case(fmt, G, M, K, N, cfg=3, mat=0 if N == 28672 else 1, n_sample=96)
     assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
+    assert_elementwise(y, y_ref)
+
+
+# The decoder layer's products at M = 1 not covered above: k and v
+# (K = 8192, N = 1024, which split K over workgroups).
+@pytest.mark.parametrize("fmt,G", [(o.FMT_INT4_ASYM, 128), (o.FMT_NF4, 64)])
+def test_gemv_decoder_layer_kv_m1(fmt, G):
+    p = w4.gemv_plan(1, 8192, 1024, G, fmt)
+    assert p["k_slices"] > 1, p  # the case exercises the split-K reduction
+    y, y_ref = full_size_case(fmt, G, 1, 8192, 1024, cfg=5, mat=1, n_sample=128)
+    assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
+    assert_elementwise(y, y_ref)
