@@ -19,6 +19,9 @@ namespace w4 {
 
 namespace {
 thread_local char g_last_error[512] = "";
+}  // namespace
+
+void clear_error() { g_last_error[0] = '\0'; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -53,7 +56,15 @@ int check_io(const char* fn, const void* x, const void* y) {
   if (!aligned16(x) || !aligned16(y)) return fail(W4_EINVAL, "%s: x and y must be 16-byte aligned", fn);
   return W4_OK;
 }
-}  // namespace
+
+int check_gemv_args(const char* fn, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                    const uint16_t* scale, const uint16_t* zero, int G, int fmt, const uint16_t* y) {
+  int st;
+  if ((st = check_matmul_shape(fn, M, K, N, G)) != W4_OK) return st;
+  if (M > 32) return fail(W4_EINVAL, "%s: M must be <= 32 (got %d); use w4_gemm", fn, M);
+  if ((st = check_weights(fn, packed, scale, zero, fmt)) != W4_OK) return st;
+  return check_io(fn, x, y);
+}
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -169,10 +180,7 @@ int w4_gemv(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
             void* ws, size_t ws_bytes, void* stream) {
   g_last_error[0] = '\0';
   int st;
-  if ((st = check_matmul_shape("w4_gemv", M, K, N, G)) != W4_OK) return st;
-  if (M > 32) return fail(W4_EINVAL, "w4_gemv: M must be <= 32 (got %d); use w4_gemm", M);
-  if ((st = check_weights("w4_gemv", packed, scale, zero, fmt)) != W4_OK) return st;
-  if ((st = check_io("w4_gemv", x, y)) != W4_OK) return st;
+  if ((st = check_gemv_args("w4_gemv", x, M, K, N, packed, scale, zero, G, fmt, y)) != W4_OK) return st;
   const GemvPlan plan = plan_gemv(M, K, N, G, fmt);
   if (plan.ws_bytes > 0) {
     if (!ws || ws_bytes < plan.ws_bytes)

@@ -11,6 +11,19 @@ namespace w4 {
 // Records `msg` as this thread's last error and returns `status`.
 int fail(int status, const char* fmt, ...);
 
+// Clears this thread's last error (every entry point starts with it).
+void clear_error();
+
+// Argument checks shared by the entry points: each returns W4_OK or a
+// negative w4_status with the error text recorded.
+bool aligned16(const void* p);
+int check_matmul_shape(const char* fn, int M, int K, int N, int G);
+int check_weights(const char* fn, const uint8_t* packed, const uint16_t* scale, const uint16_t* zero, int fmt);
+int check_io(const char* fn, const void* x, const void* y);
+// w4_gemv's rules: the above plus 1 <= M <= 32.
+int check_gemv_args(const char* fn, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                    const uint16_t* scale, const uint16_t* zero, int G, int fmt, const uint16_t* y);
+
 // Maps the last HIP launch error to W4_EHIP (recording its text) or W4_OK.
 int check_launch(const char* what);
 
