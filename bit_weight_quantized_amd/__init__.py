@@ -172,7 +172,8 @@ def gemv(x, packed, scale, zero, G: int, fmt: int, *, out=None, workspace=None, 
 
 
 GEMV_PLAN_FIELDS = ("kernel", "cols", "token_tiles", "row_waves", "k_waves", "k_slices", "staged_units",
-                    "workgroups", "threads", "lds_bytes", "lds_budget", "static_lds", "workspace_bytes", "ok")
+                    "workgroups", "threads", "lds_bytes", "lds_budget", "static_lds", "workspace_bytes", "ok",
+                    "ring")
 
 
 def gemv_plan(M: int, K: int, N: int, G: int, fmt: int) -> dict:

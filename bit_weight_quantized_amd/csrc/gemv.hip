@@ -52,7 +52,7 @@ namespace w4 {
 namespace {
 
 constexpr int kGemvMaxThreads = 512;
-constexpr int kRing = 4;       // weight tiles in flight per wave
+constexpr int kRing = 4;       // weight tiles in flight per wave (default depth of the staged kernel's ring)
 constexpr int kXUMax = 8;      // staged activation units (16 B) per thread, at most
 constexpr int kXUSmall = 4;    // the smaller staging batch (fewer redundant loads)
 constexpr int kSE = 8;         // scale entries per lane, at most: 16 rows x 32 tiles per wave
@@ -154,12 +154,11 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
   }
 }
 
-template <int FMT, int LB, int MT, int XU>
+template <int FMT, int LB, int MT, int XU, int R>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
     float* __restrict__ partial, int nwr, int nwk, int sc_pitch, int x_bytes) {
-  constexpr int R = kRing;         // weight tiles in flight per wave
   constexpr int G = 8 * LB;
   constexpr int GPT = kTileK / G;  // groups per tile: 1 (G=128) or 2 (G=64)
   constexpr int WPG = 4 / GPT;     // 4-byte words (one product each) per group
@@ -660,6 +659,7 @@ void plan_direct(GemvPlan& c, int M, int K, int N, int G, int fmt) {
   const int gpt = kTileK / G;
   const int max_waves = kGemvMaxThreads / kWave;
   c.kind = 1;
+  c.ring = M <= 16 ? 4 : 2;
   c.mt = M <= 16 ? 1 : 2;
   c.nwr = 1;
   // Measured on MI355X (K x N = 8192 x 8192, 8192 x 28672, 28672 x 8192):
@@ -765,6 +765,9 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
   c.row_blocks = (N + 16 * c.nwr - 1) / (16 * c.nwr);
   c.kind = 0;
   c.cols = 1;
+  c.ring = kRing;
+  const int ring = env_int("W4_GEMV_RING", 0);
+  if (c.mt == 1 && (ring == 4 || ring == 8 || ring == 16)) c.ring = ring;
   // Measured on MI355X (K = N = 8192): the staged kernel is faster up to M =
   // 4, the direct one (two columns per wave, eight K waves) beyond, where the
   // staged activations would outweigh the weights a workgroup streams.
@@ -790,7 +793,7 @@ int check_gemv_plan(const GemvPlan& c, int fmt) {
 
 namespace {
 
-template <int FMT, int LB, int MT, int XU>
+template <int FMT, int LB, int MT, int XU, int R>
 int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
              const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   if (const int bad = check_gemv_plan(c, FMT)) return bad;
@@ -798,10 +801,10 @@ int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const ui
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   // the plan's one-workgroup budget; the NF4 table is static LDS on top
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU>),
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R>),
                                    kGemvLdsOne - (FMT == 1 ? kLutBytes : 0), "w4_gemv");
   if (st != 0) return st;
-  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
+  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
                      y, partial, c.nwr, c.nwk, c.sc_pitch, c.x_bytes);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
@@ -843,11 +846,18 @@ int launch_mt(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const u
     return launch_direct_c<FMT, LB, 2>(c, x, M, K, N, packed, scale, zero, y, ws, s);
   }
   if (c.mt == 1) {
-    if (c.xu == kXUSmall) return launch_t<FMT, LB, 1, kXUSmall>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-    return launch_t<FMT, LB, 1, kXUMax>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+#define W4_GEMV_STAGED_R(XU)                                                                        \
+  switch (c.ring) {                                                                                 \
+    case 16: return launch_t<FMT, LB, 1, XU, 16>(c, x, M, K, N, packed, scale, zero, y, ws, s);    \
+    case 8: return launch_t<FMT, LB, 1, XU, 8>(c, x, M, K, N, packed, scale, zero, y, ws, s);      \
+    default: return launch_t<FMT, LB, 1, XU, kRing>(c, x, M, K, N, packed, scale, zero, y, ws, s); \
   }
-  if (c.xu == kXUSmall) return launch_t<FMT, LB, 2, kXUSmall>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-  return launch_t<FMT, LB, 2, kXUMax>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+    if (c.xu == kXUSmall) W4_GEMV_STAGED_R(kXUSmall)
+    W4_GEMV_STAGED_R(kXUMax)
+#undef W4_GEMV_STAGED_R
+  }
+  if (c.xu == kXUSmall) return launch_t<FMT, LB, 2, kXUSmall, kRing>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_t<FMT, LB, 2, kXUMax, kRing>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
 }  // namespace

@@ -211,7 +211,8 @@ int w4_gemv_plan(int M, int K, int N, int G, int fmt, int64_t* out, int n_out) {
                                           (int64_t)gemv_lds_budget(fmt),
                                           (int64_t)gemv_static_lds(fmt),
                                           (int64_t)c.ws_bytes,
-                                          check_gemv_plan(c, fmt) == 0 ? 1 : 0};
+                                          check_gemv_plan(c, fmt) == 0 ? 1 : 0,
+                                          c.ring};
   for (int i = 0; i < n_out && i < W4_GEMV_PLAN_FIELDS; ++i) out[i] = v[i];
   g_last_error[0] = '\0';
   return W4_OK;

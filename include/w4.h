@@ -149,10 +149,12 @@ int w4_gemv(const uint16_t* x, int M, int K, int N,
  *   7 workgroups along N, 8 threads per workgroup, 9 dynamic LDS bytes,
  *   10 dynamic LDS budget, 11 static LDS bytes, 12 workspace bytes,
  *   13 1 when the plan meets the kernels' bounds (threads <= 512, dynamic
- *      LDS within budget), else 0 -- w4_gemv refuses such a plan.
+ *      LDS within budget), else 0 -- w4_gemv refuses such a plan,
+ *   14 weight tiles (staged kernel) or operand slots (direct kernel) each
+ *      wave keeps in flight.
  * Shape rules and errors as for w4_gemv; nothing touches a device.
  */
-#define W4_GEMV_PLAN_FIELDS 14
+#define W4_GEMV_PLAN_FIELDS 15
 int w4_gemv_plan(int M, int K, int N, int G, int fmt, int64_t* out, int n_out);
 
 /*

@@ -15,7 +15,7 @@ import bit_weight_quantized_amd as w4
 LDS_PER_CU = 160 * 1024
 MAX_THREADS = 512
 FMTS = [(0, 128), (0, 64), (1, 64), (1, 128)]
-OVERRIDES = ("W4_GEMV_KIND", "W4_GEMV_NWR", "W4_GEMV_NWK", "W4_GEMV_C", "W4_GEMV_S")
+OVERRIDES = ("W4_GEMV_KIND", "W4_GEMV_NWR", "W4_GEMV_NWK", "W4_GEMV_C", "W4_GEMV_S", "W4_GEMV_RING")
 
 
 @pytest.fixture(autouse=True)
@@ -42,10 +42,12 @@ def check(p, M, K, N):
     else:
         assert p["workspace_bytes"] == 0, where
     if p["kernel"] == 1:
+        assert p["ring"] == (4 if M <= 16 else 2), where
         assert p["row_waves"] == 1 and p["cols"] in (1, 2, 4), where
         assert p["workgroups"] == -(-(N // 16) // p["cols"]), where
     else:
         assert p["kernel"] == 0 and p["cols"] == 1, where
+        assert p["ring"] in ((4, 8, 16) if M <= 16 else (4,)), where
         assert p["workgroups"] == -(-N // (16 * p["row_waves"])), where
 
 
@@ -88,7 +90,8 @@ def test_forced_plans_fit_the_kernels(monkeypatch, kind):
         combos = itertools.product(waves, waves, (0,), slices)
     else:
         combos = itertools.product((0,), waves, (0, 1, 2, 3, 4, 8), slices)
-    for nwr, nwk, c, s in combos:
+    for n, (nwr, nwk, c, s) in enumerate(combos):
+        monkeypatch.setenv("W4_GEMV_RING", str((0, 4, 8, 16, 5)[n % 5]))
         monkeypatch.setenv("W4_GEMV_NWR", str(nwr))
         monkeypatch.setenv("W4_GEMV_NWK", str(nwk))
         monkeypatch.setenv("W4_GEMV_C", str(c))

@@ -77,6 +77,43 @@ def test_gemv_launch_variants_agree(monkeypatch, nwr, nwk, s):
             assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
 
 
+@pytest.mark.parametrize("ring", [8, 16])
+@pytest.mark.parametrize("nwr,nwk,s,K", [(1, 4, 1, 1536), (2, 4, 1, 1536), (1, 1, 1, 1536), (1, 8, 2, 1536),
+                                         (2, 4, 1, 8192), (1, 4, 1, 8192), (1, 2, 1, 8192)])
+def test_gemv_ring_depths_agree(monkeypatch, ring, nwr, nwk, s, K):
+    """The staged kernel with 8 or 16 weight tiles in flight per wave: runs
+    shorter than, equal to and longer than the ring (K = 1536 is 12 tiles
+    per column, K = 8192 64), within tolerance of the oracle, bit-identical
+    to the default 4-deep ring (same products, same order) and repeatable."""
+    require_gpu()
+    monkeypatch.setenv("W4_GEMV_KIND", "0")
+    monkeypatch.setenv("W4_GEMV_NWR", str(nwr))
+    monkeypatch.setenv("W4_GEMV_NWK", str(nwk))
+    monkeypatch.setenv("W4_GEMV_S", str(s))
+    N = 208
+    w = wl.make_weight(9, 1, N, K)
+    for fmt, G in FMTS[:3]:
+        codes, scale, zero = oracle_weights(fmt, w, G)
+        packed, sc, zc = upload_weights(codes, scale, zero)
+        for M in (1, 3):
+            x = wl.make_activations(9, 1, M, K)
+            xd = dev(x)
+            ws_n = w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)
+            ws = torch.full((max(ws_n, 16),), 0xFF, dtype=torch.uint8, device="cuda")  # fp32 NaNs
+            monkeypatch.setenv("W4_GEMV_RING", str(ring))
+            assert w4.gemv_plan(M, K, N, G, fmt)["ring"] == ring
+            announce("gemv ring", dict(ring=ring, nwr=nwr, nwk=nwk, s=s, K=K, fmt=fmt, G=G, M=M))
+            y1 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
+            y2 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
+            monkeypatch.setenv("W4_GEMV_RING", "4")
+            y4 = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
+            y_ref = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
+            assert row_rel_l2(y1, y_ref) <= TOL_ROW_REL_L2, (fmt, G, M)
+            assert_elementwise(y1, y_ref)
+            assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+            assert np.array_equal(y1.view(np.uint16), y4.view(np.uint16))
+
+
 @pytest.mark.parametrize("cols,nwk,s", [(1, 8, 1), (2, 8, 1), (4, 8, 1), (2, 4, 1), (2, 3, 2), (4, 1, 3),
                                         (2, 8, 5), (1, 2, 1)])
 def test_gemv_direct_variants_agree(monkeypatch, cols, nwk, s):
