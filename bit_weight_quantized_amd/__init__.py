@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
-    "lib", "lib_path", "quantize", "pack", "gemv", "gemv_plan", "gemm", "gemm_decomp", "gemm_decomp_fixed",
+    "lib", "lib_path", "quantize", "pack", "gemv", "gemv_noalloc", "gemv_plan", "gemm", "gemm_decomp", "gemm_decomp_fixed",
     "salient_select", "residual_correct", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
     "workspace_bytes", "nf4_levels", "version",
 ]
@@ -62,6 +62,7 @@ def lib():
         L.w4_pack.argtypes = [_p, _i, _i, _p, _p]
         L.w4_gemv.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _sz, _p]
         L.w4_gemv_plan.argtypes = [_i, _i, _i, _i, _i, _p, _i]
+        L.w4_gemv_noalloc.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p]
         L.w4_gemm.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
         L.w4_gemm_decomp.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_gemm_decomp_fixed.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]
@@ -79,7 +80,7 @@ def lib():
         L.w4_last_error.argtypes = []
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
-        for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemv_plan", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
+        for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemv_noalloc", "w4_gemv_plan", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
                    "w4_salient_select", "w4_residual_correct", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
                    "w4_attn_decode_msd",
                    "w4_nf4_levels"):
@@ -168,6 +169,18 @@ def gemv(x, packed, scale, zero, G: int, fmt: int, *, out=None, workspace=None, 
     _check("w4_gemv", lib().w4_gemv(_ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, fmt,
                                     _ptr(out), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out
+
+
+def gemv_noalloc(x, packed, scale, zero, G: int, fmt: int, *, out=None, stream=None):
+    """w4_gemv without a workspace: split-K partials in the library's fixed
+    per-device scratch (calls on one device must not overlap in time)."""
+    _dev(x, torch.float16, "x")
+    N, K = _weights(packed, scale, zero)
+    M = x.shape[0]
+    out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
+    _check("w4_gemv_noalloc", lib().w4_gemv_noalloc(_ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G,
+                                                    fmt, _ptr(out), _stream(stream)))
     return out
 
 

@@ -139,6 +139,23 @@ int w4_gemv(const uint16_t* x, int M, int K, int N,
             int G, int fmt, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * w4_gemv_noalloc -- w4_gemv for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, plan and results (bit-identical to w4_gemv),
+ * with no workspace argument.  Split-K partials go to a fixed 4 MiB device
+ * array inside the library, one per device, held until the process ends; a
+ * shape whose partials need more (w4_workspace_bytes(W4_OP_GEMV, ...) >
+ * 4 MiB) returns W4_EWORKSPACE and enqueues nothing.  The array's address is
+ * looked up on the first call on each device (no allocation).  Calls on one
+ * device share that array: calls that overlap in time on one device (other
+ * streams, other threads) race and must be ordered by the caller.  Arguments
+ * and errors otherwise as for w4_gemv.
+ */
+int w4_gemv_noalloc(const uint16_t* x, int M, int K, int N,
+                    const uint8_t* packed, const uint16_t* scale, const uint16_t* zero,
+                    int G, int fmt, uint16_t* y, void* stream);
+
+/*
  * w4_gemv_plan -- host-only introspection: the launch plan w4_gemv would use
  * for this shape and format on this thread right now (the W4_GEMV_*
  * environment overrides included).  Writes min(n_out, W4_GEMV_PLAN_FIELDS)
