@@ -46,6 +46,13 @@ def parse():
                          "then a plain device copy of a known size (the reference for rocprofv3 --pmc "
                          "FETCH_SIZE / WRITE_SIZE); prints what ran")
     ap.add_argument("--profile-launches", type=int, default=16)
+    ap.add_argument("--profile-gemm", action="store_true",
+                    help="instead of the bench: launch each prefill path (M=2048, K=5120, N=25600) "
+                         "--profile-launches times eagerly, for rocprofv3 --pmc counter passes over the "
+                         "matrix-core kernels; prints what ran")
+    ap.add_argument("--profile-attention", action="store_true",
+                    help="instead of the bench: launch the KV-cache attention call --profile-launches times "
+                         "eagerly and the plain copy, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: from the counter_collection CSVs of two --profile-pass runs (rocprofv3 "
                          "--pmc FETCH_SIZE, then --pmc WRITE_SIZE) print the HBM traffic summary of the GEMV "
@@ -128,41 +135,11 @@ def bench_gemm_prefill(w4, torch, reps):
     """Prefill product M = 2048, K = 5120, N = 25600, INT4 g128: dequantize-to-
     fp16 MFMA, post-scaled fp16 MFMA, and the Multi-Scale Dequant int8 MFMA
     with two slices (adaptive and fixed-ratio scales), one and three slices
-    (each with its activation decomposition included).
-    Back-to-back launches between HIP events on the launch stream."""
-    import workloads as wl
-    M, K, N, G = 2048, 5120, 25600, 128
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(40000)
-    w = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
-    codes, scale, zero = w4.quantize(w, G, w4.INT4_ASYM)
-    packed = w4.pack(codes)
-    del w, codes
-    x = torch.from_numpy(wl.make_activations(4, 0, M, K)).cuda()
-    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    # the same layer in MXFP4 (its own weights, quantized on the GPU)
-    wmx = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
-    mx_codes, mx_scale = w4.quantize_mx(wmx)
-    mx_packed = w4.pack_mx(mx_codes)
-    del wmx, mx_codes
-    ws_mx = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_MX, M, K, N, 32, ns) for ns in (1, 2)), dtype=torch.uint8,
-                        device="cuda")
-    # one workspace for every slice count: the largest need (slices, scales, split-K tail partials)
-    ws = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, ns) for ns in (1, 2, 3)),
-                     dtype=torch.uint8, device="cuda")
+    (each with its activation decomposition included), and MXFP4 weights with
+    one and two MXFP4 slices.  Back-to-back launches between HIP events on the
+    launch stream."""
+    (M, K, N), paths = prefill_paths(w4, torch)
     flops = 2.0 * M * N * K
-    paths = {
-        "dq_f16": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.DQ_F16, out=y), 1, FP16_MFMA_PEAK_TFLOPS),
-        "postscale": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.POSTSCALE, out=y), 1,
-                      FP16_MFMA_PEAK_TFLOPS),
-        "msd2": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 2, out=y, workspace=ws), 2, INT8_MFMA_PEAK_TOPS),
-        "msd2_fixed": (lambda: w4.gemm_decomp_fixed(x, packed, scale, zero, G, out=y, workspace=ws), 2,
-                       INT8_MFMA_PEAK_TOPS),
-        "msd1": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 1, out=y, workspace=ws), 1, INT8_MFMA_PEAK_TOPS),
-        "msd3": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 3, out=y, workspace=ws), 3, INT8_MFMA_PEAK_TOPS),
-        "mxfp4_2": (lambda: w4.gemm_mx(x, mx_packed, mx_scale, 2, out=y, workspace=ws_mx), 2, FP4_MFMA_PEAK_TFLOPS),
-        "mxfp4_1": (lambda: w4.gemm_mx(x, mx_packed, mx_scale, 1, out=y, workspace=ws_mx), 1, FP4_MFMA_PEAK_TFLOPS),
-    }
     res = {}
     st = torch.cuda.Stream()
     with torch.cuda.stream(st):
@@ -192,9 +169,79 @@ def bench_gemm_prefill(w4, torch, reps):
             "paths": res}
 
 
+def prefill_paths(w4, torch):
+    """The prefill product M = 2048, K = 5120, N = 25600 (INT4 g128; MXFP4 for
+    the mxfp4 paths): a dict of name -> (thunk, MFMA products per useful
+    multiply-add, dense peak of that product's type)."""
+    import workloads as wl
+    M, K, N, G = 2048, 5120, 25600, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(40000)
+    w = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    codes, scale, zero = w4.quantize(w, G, w4.INT4_ASYM)
+    packed = w4.pack(codes)
+    del w, codes
+    x = torch.from_numpy(wl.make_activations(4, 0, M, K)).cuda()
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wmx = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    mx_codes, mx_scale = w4.quantize_mx(wmx)
+    mx_packed = w4.pack_mx(mx_codes)
+    del wmx, mx_codes
+    ws_mx = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_MX, M, K, N, 32, ns) for ns in (1, 2)), dtype=torch.uint8,
+                        device="cuda")
+    ws = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, ns) for ns in (1, 2, 3)),
+                     dtype=torch.uint8, device="cuda")
+    ws_f16 = torch.empty(max(16, w4.workspace_bytes(w4.OP_GEMM, M, K, N, G, w4.DQ_F16)), dtype=torch.uint8,
+                         device="cuda")
+    return (M, K, N), {
+        "dq_f16": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.DQ_F16, out=y, workspace=ws_f16), 1,
+                   FP16_MFMA_PEAK_TFLOPS),
+        "postscale": (lambda: w4.gemm(x, packed, scale, zero, G, w4.INT4_ASYM, w4.POSTSCALE, out=y,
+                                      workspace=ws_f16), 1, FP16_MFMA_PEAK_TFLOPS),
+        "msd2": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 2, out=y, workspace=ws), 2, INT8_MFMA_PEAK_TOPS),
+        "msd2_fixed": (lambda: w4.gemm_decomp_fixed(x, packed, scale, zero, G, out=y, workspace=ws), 2,
+                       INT8_MFMA_PEAK_TOPS),
+        "msd1": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 1, out=y, workspace=ws), 1, INT8_MFMA_PEAK_TOPS),
+        "msd3": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 3, out=y, workspace=ws), 3, INT8_MFMA_PEAK_TOPS),
+        "mxfp4_2": (lambda: w4.gemm_mx(x, mx_packed, mx_scale, 2, out=y, workspace=ws_mx), 2, FP4_MFMA_PEAK_TFLOPS),
+        "mxfp4_1": (lambda: w4.gemm_mx(x, mx_packed, mx_scale, 1, out=y, workspace=ws_mx), 1, FP4_MFMA_PEAK_TFLOPS),
+    }
+
+
 def rotation_sets(per_set_bytes):
     """Weight sets per rotation: more than 512 MB, twice the Infinity Cache."""
     return max(2, -(-(2 * 256 * 2 ** 20) // per_set_bytes) + 1)
+
+
+def bench_single_gemv(w4, torch, stream, replays=4):
+    """The single small GEMV: M = 1, K = N = 1024, G = 64, INT4 (scale +
+    zero) and NF4 (absmax), activations without outliers.  Per launch: a
+    HIP graph of one launch per weight set of a > 512 MB rotation (about
+    900 sets of 0.59 MB), replayed back to back.  At 0.59 MB per launch the
+    HBM time at peak is about 74 ns, so the launch itself bounds it."""
+    import workloads as wl
+    K = N = 1024
+    G = 64
+    res = []
+    for fmt in (w4.INT4_ASYM, w4.NF4):
+        b = weight_stream_bytes(fmt, K, N, G)
+        n_sets = rotation_sets(b)
+        sets = make_weight_sets(w4, torch, fmt, K, N, G, n_sets, 45000 + 5000 * fmt)
+        x = torch.from_numpy(wl.make_activations(1, 0, 1, K, outliers=False)).cuda()
+        y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+        ws = torch.zeros(max(16, w4.workspace_bytes(w4.OP_GEMV, 1, K, N, G, fmt)), dtype=torch.uint8, device="cuda")
+        calls = [lambda p=p: w4.gemv(x, p[0], p[1], p[2], G, fmt, out=y, workspace=ws) for p in sets]
+        g = graph_of(torch, stream, calls)
+        time_replays(torch, stream, g, 1)
+        us = time_replays(torch, stream, g, replays) * 1e3 / (replays * n_sets)
+        del g, sets
+        torch.cuda.empty_cache()
+        gbs = b / (us * 1e-6) / 1e9
+        res.append({"variant": ("int4_g64" if fmt == w4.INT4_ASYM else "nf4_b64") + "_m1", "us_per_launch": round(us, 3),
+                    "weight_bytes": b, "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "rotation_sets": n_sets})
+    return {"workload": "single_gemv_m1_k1024_n1024_g64", "note": "launch-bound: 0.59 MB is about 74 ns of HBM "
+            "time at peak", "per_launch": res}
 
 
 def bench_mlp_gemv(w4, torch, stream, replays=4):
@@ -335,29 +382,45 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
             gemv_launch(i)
             w4.salient_select(x, k, out=idx)
             w4.residual_correct(x, r_host, idx, y)
+
+        # the selection depends only on x: it runs on a second stream (same
+        # priority) beside the GEMV, and the correction waits for both
+        side = torch.cuda.Stream()
+
+        def forked(i):
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                w4.salient_select(x, k, out=idx)
+            gemv_launch(i)
+            cur.wait_stream(side)
+            w4.residual_correct(x, r_host, idx, y)
         g = graph_of(torch, stream, [lambda i=i: chain(i) for i in range(n_sets)])
+        time_replays(torch, stream, g, 1)
+        serial_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
+        del g
+        g = graph_of(torch, stream, [lambda i=i: forked(i) for i in range(n_sets)])
         time_replays(torch, stream, g, 1)
         step_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
         del g
         link = k * N * 2 / (timed["correct_host_us"] * 1e-6) / 1e9
-        res.append({"k": k, **timed, "gemv_us": round(gemv_us, 2), "step_us": round(step_us, 2),
+        res.append({"k": k, **timed, "gemv_us": round(gemv_us, 2), "step_serial_us": round(serial_us, 2),
+                    "step_us": round(step_us, 2),
                     "overhead_frac": round((step_us - gemv_us) / gemv_us, 3),
                     "residual_bytes": k * N * 2, "host_link_GBps": round(link, 2),
                     "host_link_frac": round(link / HOST_LINK_PEAK_GBS, 3)})
     return {"workload": "decode_gemv_k8192_n8192_m1_int4_g128 + residual of k salient channels",
             "residual": "fp16 [K][N] in pinned host memory, read by the kernel over the host link",
+            "step": "step_us: the selection on a second stream beside the GEMV, the correction after both; "
+                    "step_serial_us: the three calls one after the other",
             "host_link_peak_GBps": HOST_LINK_PEAK_GBS, "per_k": res}
 
 
-def bench_attention(w4, torch, stream, reps=20):
-    """Decode attention over an INT4 KV cache with Multi-Scale Dequant on both
-    products, for a 70B-shaped layer: batch 8, 64 query heads over 8 key/value
-    heads of dimension 128, 8192 cached positions.  The caches are seeded
-    normal values quantized on the GPU (w4_quantize per token, w4_pack; V
-    transposed first).  Timed as HIP-graph replays on the launch stream;
-    rate = cache bytes read (packed K and V plus their fp16 scales and zero
-    points) per second, against the 8 TB/s HBM peak; the fp16 cache of the
-    same layer would be the bytes of `fp16_cache_bytes`."""
+def attention_call(w4, torch):
+    """The decode-attention workload: batch 8, 64 query heads over 8 key/value
+    heads of dimension 128, 8192 cached positions, INT4 caches quantized on the
+    GPU (w4_quantize per token, w4_pack; V transposed first).  Returns (thunk,
+    shape)."""
     B, Hq, Hkv, L, D = 8, 64, 8, 8192, 128
     gen = torch.Generator(device="cuda")
     gen.manual_seed(60000)
@@ -376,7 +439,17 @@ def bench_attention(w4, torch, stream, reps=20):
     out = torch.empty_like(q)
     ws = torch.empty(w4.workspace_bytes(w4.OP_ATTN_MSD, B, Hq, L, 0, 0), dtype=torch.uint8, device="cuda")
     ks, kz, vs, vz = (t.view(B, Hkv, L) for t in (ks, kz, vs, vz))
-    call = lambda: w4.attn_decode_msd(q, kp, ks, kz, vp, vs, vz, Hkv, out=out, workspace=ws)
+    return (lambda: w4.attn_decode_msd(q, kp, ks, kz, vp, vs, vz, Hkv, out=out, workspace=ws)), (B, Hq, Hkv, L, D)
+
+
+def bench_attention(w4, torch, stream, reps=20):
+    """Decode attention over an INT4 KV cache with Multi-Scale Dequant on both
+    products, for a 70B-shaped layer (see attention_call).  Timed as HIP-graph
+    replays on the launch stream; rate = cache bytes read (packed K and V plus
+    their fp16 scales and zero points) per second, against the 8 TB/s HBM
+    peak; the fp16 cache of the same layer would be the bytes of
+    `fp16_cache_bytes`."""
+    call, (B, Hq, Hkv, L, D) = attention_call(w4, torch)
     g = graph_of(torch, stream, [call] * reps)
     time_replays(torch, stream, g, 1)
     us = time_replays(torch, stream, g, 4) * 1e3 / (4 * reps)
@@ -565,6 +638,9 @@ def main():
     if args.traffic:
         traffic_summary(*args.traffic)
         return
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every box here has one GPU "
               "and this library has no multi-GPU path.", file=sys.stderr)
@@ -594,6 +670,30 @@ def main():
         w4.gemv(xs[M], packed, scale, zero, G, fmt, out=ys[M], workspace=wss[(fmt, M)])
 
     stream = torch.cuda.Stream()
+    if args.profile_gemm:
+        _, paths = prefill_paths(w4, torch)
+        with torch.cuda.stream(stream):
+            for name, (fn, _, _) in paths.items():
+                for _ in range(args.profile_launches):
+                    fn()
+                torch.cuda.synchronize()
+                print(f"profile gemm: {args.profile_launches} calls of {name}", flush=True)
+        return
+    if args.profile_attention:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        call, _ = attention_call(w4, torch)
+        with torch.cuda.stream(stream):
+            for _ in range(args.profile_launches):
+                call()
+            torch.cuda.synchronize()
+            print(f"profile attention: {args.profile_launches} calls", flush=True)
+            for _ in range(4):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(f"profile attention: 4 copies of {COPY_BYTES} bytes (reads {COPY_BYTES}, writes {COPY_BYTES})",
+              flush=True)
+        return
     if args.profile_pass:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -610,21 +710,46 @@ def main():
               flush=True)
         return
 
-    # ---- the timed region: HIP graph replays of whole steps
+    # ---- the timed region: exactly --steps steps after exactly --warmup
+    # steps, as HIP graph replays: a graph of n_sets whole steps (one pass
+    # over the weight rotation) replayed as often as it fits, then a graph of
+    # the remaining steps
     def step_calls(i):
         return [lambda fmt=fmt, M=M, G=G: launch(fmt, M, G, i * len(Ms) + Ms.index(M)) for fmt, M, G in variants]
 
     steps_per_graph = n_sets
-    graph = graph_of(torch, stream, [c for i in range(steps_per_graph) for c in step_calls(i)])
-    replays_warm = max(1, -(-args.warmup // steps_per_graph))
-    replays = max(1, -(-args.steps // steps_per_graph))
-    steps_timed = replays * steps_per_graph
-    time_replays(torch, stream, graph, replays_warm)
-    total_ms = time_replays(torch, stream, graph, replays)
+    graphs = {}
+
+    def steps_graph(n):
+        if n not in graphs:
+            graphs[n] = graph_of(torch, stream, [c for i in range(n) for c in step_calls(i)])
+        return graphs[n]
+
+    def run_steps(n):
+        """Replays of exactly n steps on `stream` (no synchronization)."""
+        for _ in range(n // steps_per_graph):
+            steps_graph(steps_per_graph).replay()
+        if n % steps_per_graph:
+            steps_graph(n % steps_per_graph).replay()
+
+    for n in {steps_per_graph, args.steps % steps_per_graph, args.warmup % steps_per_graph} - {0}:
+        steps_graph(n)  # captured before the timed region
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        run_steps(args.warmup)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        run_steps(args.steps)
+        end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    steps_timed = args.steps
     ms_per_step = total_ms / steps_timed
     step_bytes = sum(weight_stream_bytes(fmt, K, N, G) for fmt, M, G in variants)
     value = step_bytes * steps_timed / (total_ms * 1e-3) / 1e9
-    del graph
+    graphs.clear()
 
     # ---- live per-launch timing of each variant: a graph of one launch per
     # weight set, replayed back to back between events on its stream
@@ -648,6 +773,11 @@ def main():
         traffic = round(sum(traffic_rows[p["variant"]] for p in per) / len(per))
 
     gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
+    single = None
+    try:
+        single = bench_single_gemv(w4, torch, stream)
+    except Exception as e:  # reported, never fatal to the headline line
+        single = {"error": f"{type(e).__name__}: {e}"}
     mlp = layer = None
     if args.layers:
         try:
@@ -683,7 +813,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps_timed,
-        "warmup": replays_warm * steps_per_graph,
+        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -693,7 +823,8 @@ def main():
                 "outlier channels; weights rotate over %d sets per format (%.0f MB)" % (n_sets, n_sets * per_set / 1e6),
         "config": {"workload": "decode_gemv_k8192_n8192", "M": list(Ms), "K": K, "N": N,
                    "formats": ["int4_asym_g128", "nf4_b64"], "launches_per_step": len(variants),
-                   "timed": "HIP graph replays, %d steps per graph" % steps_per_graph},
+                   "timed": "HIP graph replays (graphs of %d steps and of the remainder), exactly the "
+                            "requested steps after exactly the requested warmup" % steps_per_graph},
         "roofline": {"bound": "hbm", "kernel": "the 6 GEMV launches of a step (gemv_kernel at M = 1 and 4, gemv_direct_kernel at M = 16)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -701,6 +832,7 @@ def main():
                      "launch_average_us": round(sum_us / len(per), 3)},
         "per_launch": per,
         "gemm_prefill": gemm,
+        "single_gemv": single,
         "mlp_gemv": mlp,
         "decoder_layer": layer,
         "residual_compensation": resid,

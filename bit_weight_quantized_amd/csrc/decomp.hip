@@ -45,8 +45,23 @@ __device__ __forceinline__ double block_max(double v, double* red) {
   return r;
 }
 
-__device__ __forceinline__ double quant127(double r, double s) {
-  return s != 0.0 ? fmin(fmax(rint(r / s), -127.0), 127.0) : 0.0;
+// clamp(rint(fl64(n / s)), -127, 127) without a division per element.  inv is
+// 1 / s correctly rounded; every quotient here has |n / s| < 2^8 (n is a
+// residual bounded by the row maximum, or 254 times a first residual).  Then
+// t = fl64(n * inv) and the correctly rounded quotient are both within 2^-44
+// of n / s, so they round to the same integer unless n / s lies within 2^-44
+// of a half-integer; a quotient t within 2^-30 of one takes the division
+// itself.  The result is the division's decision in every case.
+__device__ __forceinline__ double quant127_inv(double n, double s, double inv) {
+  if (s == 0.0) return 0.0;
+  const double t = n * inv;
+  double q = rint(t);
+  if (fabs(fabs(t - q) - 0.5) < 0x1p-30) q = rint(n / s);
+  return fmin(fmax(q, -127.0), 127.0);
+}
+
+__device__ __forceinline__ int code_byte(const uint32_t (&w)[2], int i) {
+  return (int)(int8_t)(uint8_t)(w[i / 4] >> (8 * (i % 4)));
 }
 
 __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
@@ -55,8 +70,9 @@ __device__ __forceinline__ uint32_t pack4(int a0, int a1, int a2, int a3) {
 }
 
 // One workgroup per token row, passes over the (cache-resident) row: the
-// absmax, then one pass per slice.  Pass j recomputes the residual from x and
-// the earlier slices exactly as before and gathers the next residual's absmax
+// absmax, then one pass per slice.  Pass j rebuilds the residual from x and
+// the earlier slices' codes (kept in registers when the row is; decided again,
+// identically, when it is re-read) and gathers the next residual's absmax
 // (adaptive scales).  With FIXED (two slices), the second slice uses the first
 // slice's step divided by 254: A_2 = clamp(rint((254 r_1) / s_1)), and its
 // reported scale is fp32(s_1 / 254).  Each thread takes 8 consecutive
@@ -95,16 +111,17 @@ __global__ __launch_bounds__(T) void decompose_kernel(
       if (k < K) xc[c] = *reinterpret_cast<const u32x4*>(xr + k);
     }
   }
-  // f(k, w) for each of this thread's 16-byte chunks w (K positions k .. k + 7)
+  // f(c, k, w) for each of this thread's 16-byte chunks w (K positions k ..
+  // k + 7; c its register slot when the row is cached, else 0)
   auto for_chunks = [&](auto&& f) {
     if constexpr (CH > 0) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int k = 8 * rt + c * kStep;
-        if (k < K) f(k, xc[c]);
+        if (k < K) f(c, k, xc[c]);
       }
     } else {
-      for (int k = 8 * rt; k < K; k += kStep) f(k, *reinterpret_cast<const u32x4*>(xr + k));
+      for (int k = 8 * rt; k < K; k += kStep) f(0, k, *reinterpret_cast<const u32x4*>(xr + k));
     }
   };
   auto load8 = [&](const u32x4& w, double* v) {
@@ -125,20 +142,24 @@ __global__ __launch_bounds__(T) void decompose_kernel(
   };
 
   double amax = 0.0;
-  for_chunks([&](int, const u32x4& w) {
+  for_chunks([&](int, int, const u32x4& w) {
     double v[8];
     load8(w, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(v[i]));
   });
   amax = row_max(amax);
-  double s[NS];
+  double s[NS], inv[NS];
   s[0] = (double)(float)(amax / 127.0);
+  inv[0] = s[0] != 0.0 ? 1.0 / s[0] : 0.0;
+  // the earlier slices' codes of the cached chunks (plain order), so a pass
+  // rebuilds its residual without deciding those codes again
+  uint32_t codes[NS > 1 ? NS - 1 : 1][CH > 0 ? CH : 1][2];
 
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     double amax_next = 0.0;
-    for_chunks([&](int k, const u32x4& w) {
+    for_chunks([&](int c, int k, const u32x4& w) {
       double v[8];
       load8(w, v);
       int a[8];
@@ -146,22 +167,34 @@ __global__ __launch_bounds__(T) void decompose_kernel(
       for (int i = 0; i < 8; ++i) {
         double r = v[i];
 #pragma unroll
-        for (int jj = 0; jj < j; ++jj) r = r - s[jj] * quant127(r, s[jj]);  // earlier slices' residual
+        for (int jj = 0; jj < j; ++jj) {  // earlier slices' residual
+          const double qq = CH > 0 ? (double)code_byte(codes[jj][c], i) : quant127_inv(r, s[jj], inv[jj]);
+          r = r - s[jj] * qq;
+        }
         double q;
         if (FIXED && j == 1)
-          q = s[0] != 0.0 ? fmin(fmax(rint((kFixedRatio * r) / s[0]), -127.0), 127.0) : 0.0;
+          q = quant127_inv(kFixedRatio * r, s[0], inv[0]);
         else
-          q = quant127(r, s[j]);
+          q = quant127_inv(r, s[j], inv[j]);
         a[i] = (int)q;
         if (!FIXED && j + 1 < NS) amax_next = fmax(amax_next, fabs(r - s[j] * q));
       }
       store8(j, k, a);
+      if constexpr (CH > 0) {
+        if (j + 1 < NS) {
+          codes[j][c][0] = pack4(a[0], a[1], a[2], a[3]);
+          codes[j][c][1] = pack4(a[4], a[5], a[6], a[7]);
+        }
+      }
     });
     if (FIXED && j == 1) {
       if (rt == 0) tok_scale[(size_t)M + m] = (float)(s[0] / kFixedRatio);
     } else {
       if (rt == 0) tok_scale[(size_t)j * M + m] = (float)s[j];
-      if (!FIXED && j + 1 < NS) s[j + 1] = (double)(float)(row_max(amax_next) / 127.0);
+      if (!FIXED && j + 1 < NS) {
+        s[j + 1] = (double)(float)(row_max(amax_next) / 127.0);
+        inv[j + 1] = s[j + 1] != 0.0 ? 1.0 / s[j + 1] : 0.0;
+      }
     }
   }
 }

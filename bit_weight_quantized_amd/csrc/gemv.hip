@@ -154,7 +154,8 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
   }
 }
 
-template <int FMT, int LB, int MT, int XU, int R>
+// Staged kernel.  ONE: M == 1 (only the accumulator of token 0 is updated).
+template <int FMT, int LB, int MT, int XU, int R, bool ONE>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
@@ -162,6 +163,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   constexpr int G = 8 * LB;
   constexpr int GPT = kTileK / G;  // groups per tile: 1 (G=128) or 2 (G=64)
   constexpr int WPG = 4 / GPT;     // 4-byte words (one product each) per group
+  constexpr int RG = G / 8;        // 8-position activation units per group
+  static_assert(!ONE || MT == 1, "M == 1 has one token tile");
   extern __shared__ __align__(16) unsigned char smem[];
   // NF4 pair table, kLutCopies interleaved copies: entry e of copy c at word
   // e * kLutCopies + c, and lane l reads copy l % kLutCopies, so random
@@ -223,32 +226,45 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     xs[u] = q;
   };
 
-  // Scale block of this wave: entry (r, j) = the scale (and zero point) of row
-  // r of its tile column for tile t0 + j, fetched once with row-contiguous
-  // loads and kept in LDS at row pitch sc_pitch (odd, so the 16 rows a
-  // lane group reads fall in distinct banks).  GPT = 2 entries hold both
-  // groups of the tile, low half first.
-  constexpr int EW = (FMT == 0 && GPT == 2) ? 2 : 1;  // 32-bit words per entry
-  uint32_t* sc = reinterpret_cast<uint32_t*>(smem + (size_t)x_bytes) + (size_t)wave * 16 * sc_pitch * EW;
+  // Scale block of this wave: entry (r, j) = the scale factors of row r of
+  // its tile column for tile t0 + j, fetched once with row-contiguous loads
+  // and kept in LDS, already as fp32 products, at row pitch sc_pitch (odd,
+  // so the 16 rows a lane group reads fall in distinct banks): INT4, per
+  // group, s * 2^24 and -s * z (codes enter the products as q * 2^-24); NF4,
+  // per group, s.
+  constexpr int EPG = FMT == 0 ? 2 : 1;  // fp32 words per group
+  constexpr int EW = EPG * GPT;          // fp32 words per entry
+  float* sc = reinterpret_cast<float*>(smem + (size_t)x_bytes) + (size_t)wave * 16 * sc_pitch * EW;
   const int n_se = 16 * cnt;
   const float inv_cnt = 1.0f / (float)max(cnt, 1);
   const size_t srow0 = (size_t)colw * 16 * ng;
-  auto load_entry = [&](int e, uint32_t (&v)[EW]) {
+  auto load_entry = [&](int e, uint32_t (&v)[2]) {
     int r, j;
     div_small(e, max(cnt, 1), inv_cnt, r, j);
     const size_t o = srow0 + (size_t)r * ng + (size_t)min(t0 + j, KT - 1) * GPT;  // a wave without tiles still loads
     if constexpr (GPT == 1) {
-      v[0] = (uint32_t)scale[o] | (FMT == 0 ? (uint32_t)zero[o] << 16 : 0u);
+      v[0] = (uint32_t)scale[o];
+      v[1] = FMT == 0 ? (uint32_t)zero[o] : 0u;
     } else {
       v[0] = *reinterpret_cast<const uint32_t*>(scale + o);
-      if constexpr (EW == 2) v[1] = *reinterpret_cast<const uint32_t*>(zero + o);
+      v[1] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(zero + o) : 0u;
     }
   };
-  auto store_entry = [&](int e, const uint32_t (&v)[EW]) {
+  auto store_entry = [&](int e, const uint32_t (&v)[2]) {
     int r, j;
     div_small(e, max(cnt, 1), inv_cnt, r, j);
+    float* dst = sc + (r * sc_pitch + j) * EW;
 #pragma unroll
-    for (int w = 0; w < EW; ++w) sc[(r * sc_pitch + j) * EW + w] = v[w];
+    for (int gi = 0; gi < GPT; ++gi) {
+      const float sv = half_bits_to_float((uint16_t)(v[0] >> (16 * gi)));
+      if constexpr (FMT == 0) {
+        const float zv = half_bits_to_float((uint16_t)(v[1] >> (16 * gi)));
+        dst[gi * 2] = sv * 16777216.0f;
+        dst[gi * 2 + 1] = -sv * zv;
+      } else {
+        dst[gi] = sv;
+      }
+    }
   };
 
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
@@ -278,7 +294,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   u32x4 xb[XU];
 #pragma unroll
   for (int i = 0; i < XU; ++i) xb[i] = load_xunit(min(tid + i * nthr, n_xu - 1));
-  uint32_t se[kSE][EW];
+  uint32_t se[kSE][2];
 #pragma unroll
   for (int i = 0; i < kSE; ++i) load_entry(min(lane + i * kWave, max(n_se, 1) - 1), se[i]);
   u32x4 ring[R];
@@ -314,20 +330,19 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   for (int t = 0; t < MT; ++t) C[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   int mrow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) mrow[t] = min(t * 16 + ln, M - 1);
+  for (int t = 0; t < MT; ++t) mrow[t] = ONE ? 0 : min(t * 16 + ln, M - 1);
   // INT4: the group's activation sum per token, as a product with constant B
   // (1 for the even pairs, 16 for the pre-scaled odd pairs)
   const u32x4 kSumB{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u};
-  const uint32_t* sc_row = sc + (size_t)ln * sc_pitch * EW;
+  const float* sc_row = sc + (size_t)ln * sc_pitch * EW;
   const uint32_t* lut_c = lut + lane % kLutCopies;
+  const int xstride = ONE ? 1 : M;
 
   // products of tile ci of the wave's run
   auto compute_tile = [&](const u32x4& wv, int ci) {
-    uint32_t sz[EW];
+    float sf[EW];
 #pragma unroll
-    for (int w = 0; w < EW; ++w) sz[w] = sc_row[ci * EW + w];
-    const uint32_t s_word = sz[0];
-    const uint32_t z_word = EW == 2 ? sz[EW - 1] : (sz[0] >> 16);
+    for (int w = 0; w < EW; ++w) sf[w] = sc_row[ci * EW + w];
     u32x4 B[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -341,28 +356,26 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
       }
     }
     const int tl = t0 - ts0 + ci;  // tile index within the slice
-    const u32x4* xa = xs + (size_t)(tl * 16 + kb) * M;  // + (4 w) * M + m
+    const u32x4* xa = xs + (size_t)(tl * 16 + kb) * xstride;  // + (4 w) * M + m
 #pragma unroll
     for (int gi = 0; gi < GPT; ++gi) {
-      const float sv = GPT == 1 ? half_bits_to_float((uint16_t)(s_word & 0xFFFFu))
-                                : half_bits_to_float((uint16_t)(s_word >> (16 * gi)));
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) acc = mfma_f16(xa[(4 * w) * M + mrow[t]], B[w], acc);
+        for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) acc = mfma_f16(xa[(4 * w) * xstride + mrow[t]], B[w], acc);
+        constexpr int NI = ONE ? 1 : 4;  // accumulators that hold tokens
         if constexpr (FMT == 0) {
+          // y += (s 2^24) sum x q 2^-24 - (s z) sum x
           f32x4 sx = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) sx = mfma_f16(xa[(4 * w) * M + mrow[t]], kSumB, sx);
-          const float zv = GPT == 1 ? half_bits_to_float((uint16_t)(z_word & 0xFFFFu))
-                                    : half_bits_to_float((uint16_t)(z_word >> (16 * gi)));
-          const float ex = sv * 16777216.0f, ey = -sv * zv;  // codes enter as q * 2^-24
+          for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) sx = mfma_f16(xa[(4 * w) * xstride + mrow[t]], kSumB, sx);
+          const float ex = sf[gi * 2], ey = sf[gi * 2 + 1];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) C[t][i] = fmaf(ex, acc[i], fmaf(ey, sx[i], C[t][i]));
+          for (int i = 0; i < NI; ++i) C[t][i] = fmaf(ex, acc[i], fmaf(ey, sx[i], C[t][i]));
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) C[t][i] = fmaf(sv, acc[i], C[t][i]);
+          for (int i = 0; i < NI; ++i) C[t][i] = fmaf(sf[gi], acc[i], C[t][i]);
         }
       }
     }
@@ -738,7 +751,7 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
     const int want_waves = 2048;
     while (c.row_blocks * c.s * c.nwr * c.nwk < want_waves && KT / (c.s * 2 * c.nwk) >= 8) c.s *= 2;
   }
-  const int ew = (fmt == 0 && gpt == 2) ? 2 : 1;  // 32-bit words per scale entry
+  const int ew = (fmt == 0 ? 2 : 1) * gpt;  // fp32 words per scale entry
   for (;;) {
     const int slice_max = (KT + c.s - 1) / c.s;
     const int nthr = c.nwr * c.nwk * kWave;
@@ -793,21 +806,29 @@ int check_gemv_plan(const GemvPlan& c, int fmt) {
 
 namespace {
 
-template <int FMT, int LB, int MT, int XU, int R>
-int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
-             const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+template <int FMT, int LB, int MT, int XU, int R, bool ONE>
+int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+              const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   if (const int bad = check_gemv_plan(c, FMT)) return bad;
   const dim3 block(c.nwr * c.nwk * kWave);
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   // the plan's one-workgroup budget; the NF4 table is static LDS on top
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R>),
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R, ONE>),
                                    kGemvLdsOne - (FMT == 1 ? kLutBytes : 0), "w4_gemv");
   if (st != 0) return st;
-  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
+  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R, ONE>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
                      y, partial, c.nwr, c.nwk, c.sc_pitch, c.x_bytes);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
+}
+
+template <int FMT, int LB, int MT, int XU, int R>
+int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+             const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+  if constexpr (MT == 1)
+    if (M == 1) return launch_t1<FMT, LB, 1, XU, R, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_t1<FMT, LB, MT, XU, R, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
 template <int FMT, int LB, int MT, int C>

@@ -290,3 +290,38 @@ def test_decomp_slices_m256_long_rows(nslices, K):
     ref = o.msd_result(S, o.msd_accumulators(A, codes, zero, G), scale)
     assert row_rel_l2(y, ref) <= TOL_ROW_REL_L2
     assert_elementwise(y, ref)
+
+
+@pytest.mark.parametrize("fixed", [False, True], ids=["adaptive", "fixed"])
+def test_decomp_exact_half_integer_quotients(fixed):
+    """Quotients x / s that are exact half-integers take the division itself
+    (round half to even); quotients a few ulps from one do not round
+    differently.  Rows: s = 1 (max |x| = 127) with x = k + 1/2; s = 2^-3 with
+    x = (k + 1/2) / 8; s = 2^5 with x = 32 (k + 1/2); and rows whose values
+    sit one fp16 ulp beside those ties.  Slices and scales bit-exact against
+    the oracle's fp64 division."""
+    require_gpu()
+    K, N, G = 512, 64, 128
+    ks = np.arange(-127, 127, dtype=np.float64)
+    rows = []
+    for scale_ in (1.0, 0.125, 32.0):
+        base = np.resize((ks + 0.5) * scale_, K)
+        base[0] = 127 * scale_  # the row maximum fixes s = scale_
+        rows.append(base)
+        near = base.astype(np.float16)
+        rows.append(np.nextafter(near, np.float16(np.inf)).astype(np.float64))
+        rows.append(np.nextafter(near, np.float16(-np.inf)).astype(np.float64))
+    x = np.array(rows, dtype=np.float16)
+    M = x.shape[0]
+    w = wl.make_weight(340, 0, N, K)
+    codes, scale, zero = o.quantize_int4_asym(w, G)
+    announce("decomp ties", dict(fixed=fixed, M=M, K=K))
+    if fixed:
+        y, sl, ts, _ = run_fixed(x, codes, scale, zero, G, with_acc=False)
+        A, S = o.decompose_fixed_ratio(x)
+    else:
+        y, sl, ts, _ = run_decomp(x, codes, scale, zero, G, 2, with_acc=False)
+        A, S = o.decompose_activations(x, 2)
+    assert np.array_equal(sl, A)
+    assert np.array_equal(ts.view(np.uint32), S.view(np.uint32))
+    assert S[0, 0] == 1.0 and S[0, 3] == 0.125 and S[0, 6] == 32.0
