@@ -155,7 +155,10 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
 }
 
 // Staged kernel.  ONE: M == 1 (only the accumulator of token 0 is updated).
-template <int FMT, int LB, int MT, int XU, int R, bool ONE>
+// VS: the workgroup stages its rows' scale block for all of K with 16-byte
+// loads (K not split, K / G a multiple of 8); otherwise each wave stages the
+// block of its own run.
+template <int FMT, int LB, int MT, int XU, int R, bool ONE, bool VS>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
@@ -226,44 +229,67 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     xs[u] = q;
   };
 
-  // Scale block of this wave: entry (r, j) = the scale factors of row r of
-  // its tile column for tile t0 + j, fetched once with row-contiguous loads
-  // and kept in LDS, already as fp32 products, at row pitch sc_pitch (odd,
-  // so the 16 rows a lane group reads fall in distinct banks): INT4, per
-  // group, s * 2^24 and -s * z (codes enter the products as q * 2^-24); NF4,
-  // per group, s.
-  constexpr int EPG = FMT == 0 ? 2 : 1;  // fp32 words per group
-  constexpr int EW = EPG * GPT;          // fp32 words per entry
-  float* sc = reinterpret_cast<float*>(smem + (size_t)x_bytes) + (size_t)wave * 16 * sc_pitch * EW;
+  // Scale block.  Entry (r, j) = the scale (and zero point) words of row r
+  // for tile j: GPT = 1, s | z << 16 (NF4: s); GPT = 2, the two groups' s
+  // pair, then (INT4) their z pair.  Per-wave blocks (16 rows x the wave's
+  // run, rows at pitch sc_pitch, odd, so the 16 rows a lane group reads fall
+  // in distinct banks), fetched with row-contiguous loads; or (VS) one block
+  // for the workgroup's 16 nwr rows x all KT tiles at row pitch sc_pitch
+  // (= 4 mod 32 words), fetched as 16-byte units of 8 groups, each unit of a
+  // row one piece of one cache line.
+  constexpr int EW = (FMT == 0 && GPT == 2) ? 2 : 1;  // 32-bit words per entry
+  uint32_t* sc = reinterpret_cast<uint32_t*>(smem + (size_t)x_bytes) +
+                 (VS ? 0 : (size_t)wave * 16 * sc_pitch * EW);
   const int n_se = 16 * cnt;
   const float inv_cnt = 1.0f / (float)max(cnt, 1);
   const size_t srow0 = (size_t)colw * 16 * ng;
-  auto load_entry = [&](int e, uint32_t (&v)[2]) {
+  auto load_entry = [&](int e, uint32_t (&v)[EW]) {
     int r, j;
     div_small(e, max(cnt, 1), inv_cnt, r, j);
     const size_t o = srow0 + (size_t)r * ng + (size_t)min(t0 + j, KT - 1) * GPT;  // a wave without tiles still loads
     if constexpr (GPT == 1) {
-      v[0] = (uint32_t)scale[o];
-      v[1] = FMT == 0 ? (uint32_t)zero[o] : 0u;
+      v[0] = (uint32_t)scale[o] | (FMT == 0 ? (uint32_t)zero[o] << 16 : 0u);
     } else {
       v[0] = *reinterpret_cast<const uint32_t*>(scale + o);
-      v[1] = FMT == 0 ? *reinterpret_cast<const uint32_t*>(zero + o) : 0u;
+      if constexpr (EW == 2) v[1] = *reinterpret_cast<const uint32_t*>(zero + o);
     }
   };
-  auto store_entry = [&](int e, const uint32_t (&v)[2]) {
+  auto store_entry = [&](int e, const uint32_t (&v)[EW]) {
     int r, j;
     div_small(e, max(cnt, 1), inv_cnt, r, j);
-    float* dst = sc + (r * sc_pitch + j) * EW;
 #pragma unroll
-    for (int gi = 0; gi < GPT; ++gi) {
-      const float sv = half_bits_to_float((uint16_t)(v[0] >> (16 * gi)));
-      if constexpr (FMT == 0) {
-        const float zv = half_bits_to_float((uint16_t)(v[1] >> (16 * gi)));
-        dst[gi * 2] = sv * 16777216.0f;
-        dst[gi * 2 + 1] = -sv * zv;
-      } else {
-        dst[gi] = sv;
+    for (int w = 0; w < EW; ++w) sc[(r * sc_pitch + j) * EW + w] = v[w];
+  };
+  // VS: unit u = r * upr + c holds groups 8c .. 8c + 7 of workgroup row r
+  constexpr int kVU = 2;  // units per thread (the plan guarantees 16 nwr upr <= kVU threads)
+  const int upr = ng / 8;
+  const float inv_upr = 1.0f / (float)max(upr, 1);
+  auto load_vunit = [&](int u, u32x4& vs, u32x4& vz) {
+    int r, c;
+    div_small(u, upr, inv_upr, r, c);
+    const size_t o = (size_t)min(row_wg0 + r, N - 1) * ng + (size_t)c * 8;
+    vs = *reinterpret_cast<const u32x4*>(scale + o);
+    if constexpr (FMT == 0) vz = *reinterpret_cast<const u32x4*>(zero + o);
+  };
+  auto store_vunit = [&](int u, const u32x4& vs, const u32x4& vz) {
+    int r, c;
+    div_small(u, upr, inv_upr, r, c);
+    uint32_t* dst = sc + (size_t)r * sc_pitch;
+    if constexpr (GPT == 1) {  // tiles 8c .. 8c + 7: s | z << 16
+      uint32_t e[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t zw = FMT == 0 ? vz[i] : 0u;
+        e[2 * i] = (vs[i] & 0xFFFFu) | (zw << 16);
+        e[2 * i + 1] = (vs[i] >> 16) | (zw & 0xFFFF0000u);
       }
+      *reinterpret_cast<u32x4*>(dst + 8 * c) = u32x4{e[0], e[1], e[2], e[3]};
+      *reinterpret_cast<u32x4*>(dst + 8 * c + 4) = u32x4{e[4], e[5], e[6], e[7]};
+    } else if constexpr (EW == 2) {  // tiles 4c .. 4c + 3: s pair, z pair
+      *reinterpret_cast<u32x4*>(dst + 8 * c) = u32x4{vs[0], vz[0], vs[1], vz[1]};
+      *reinterpret_cast<u32x4*>(dst + 8 * c + 4) = u32x4{vs[2], vz[2], vs[3], vz[3]};
+    } else {  // NF4, tiles 4c .. 4c + 3: s pair
+      *reinterpret_cast<u32x4*>(dst + 4 * c) = vs;
     }
   };
 
@@ -294,9 +320,17 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   u32x4 xb[XU];
 #pragma unroll
   for (int i = 0; i < XU; ++i) xb[i] = load_xunit(min(tid + i * nthr, n_xu - 1));
-  uint32_t se[kSE][2];
+  constexpr int kSEw = VS ? 1 : kSE;
+  uint32_t se[kSEw][EW];
+  u32x4 vsv[VS ? kVU : 1], vzv[VS ? kVU : 1];
+  if constexpr (VS) {
+    const int n_vu = 16 * nwr * upr;
 #pragma unroll
-  for (int i = 0; i < kSE; ++i) load_entry(min(lane + i * kWave, max(n_se, 1) - 1), se[i]);
+    for (int i = 0; i < kVU; ++i) load_vunit(min(tid + i * nthr, n_vu - 1), vsv[i], vzv[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSE; ++i) load_entry(min(lane + i * kWave, max(n_se, 1) - 1), se[i]);
+  }
   u32x4 ring[R];
 #pragma unroll
   for (int d = 0; d < R; ++d) ring[d] = load_tile(t0 + d);
@@ -307,10 +341,19 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     const int u = tid + i * nthr;
     if (u < n_xu) store_xunit(xb[i], u);
   }
+  if constexpr (VS) {
+    const int n_vu = 16 * nwr * upr;
 #pragma unroll
-  for (int i = 0; i < kSE; ++i) {
-    const int e = lane + i * kWave;
-    if (e < n_se) store_entry(e, se[i]);
+    for (int i = 0; i < kVU; ++i) {
+      const int u = tid + i * nthr;
+      if (u < n_vu) store_vunit(u, vsv[i], vzv[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSE; ++i) {
+      const int e = lane + i * kWave;
+      if (e < n_se) store_entry(e, se[i]);
+    }
   }
   if constexpr (FMT == 1) {
 #pragma unroll
@@ -334,15 +377,19 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   // INT4: the group's activation sum per token, as a product with constant B
   // (1 for the even pairs, 16 for the pre-scaled odd pairs)
   const u32x4 kSumB{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u};
-  const float* sc_row = sc + (size_t)ln * sc_pitch * EW;
+  // the lane's row of the scale block, at the wave's first tile
+  const uint32_t* sc_row = VS ? sc + (size_t)(wr * 16 + ln) * sc_pitch + (size_t)t0 * EW
+                              : sc + (size_t)ln * sc_pitch * EW;
   const uint32_t* lut_c = lut + lane % kLutCopies;
   const int xstride = ONE ? 1 : M;
 
   // products of tile ci of the wave's run
   auto compute_tile = [&](const u32x4& wv, int ci) {
-    float sf[EW];
+    uint32_t sz[EW];
 #pragma unroll
-    for (int w = 0; w < EW; ++w) sf[w] = sc_row[ci * EW + w];
+    for (int w = 0; w < EW; ++w) sz[w] = sc_row[ci * EW + w];
+    const uint32_t s_word = sz[0];
+    const uint32_t z_word = EW == 2 ? sz[EW - 1] : (sz[0] >> 16);
     u32x4 B[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -370,12 +417,15 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
           f32x4 sx = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) sx = mfma_f16(xa[(4 * w) * xstride + mrow[t]], kSumB, sx);
-          const float ex = sf[gi * 2], ey = sf[gi * 2 + 1];
+          const float sv = half_bits_to_float((uint16_t)(GPT == 1 ? s_word : s_word >> (16 * gi)));
+          const float zv = half_bits_to_float((uint16_t)(GPT == 1 ? z_word : z_word >> (16 * gi)));
+          const float ex = sv * 16777216.0f, ey = -sv * zv;  // codes enter as q * 2^-24
 #pragma unroll
           for (int i = 0; i < NI; ++i) C[t][i] = fmaf(ex, acc[i], fmaf(ey, sx[i], C[t][i]));
         } else {
+          const float sv = half_bits_to_float((uint16_t)(GPT == 1 ? s_word : s_word >> (16 * gi)));
 #pragma unroll
-          for (int i = 0; i < NI; ++i) C[t][i] = fmaf(sf[gi], acc[i], C[t][i]);
+          for (int i = 0; i < NI; ++i) C[t][i] = fmaf(sv, acc[i], C[t][i]);
         }
       }
     }
@@ -751,7 +801,7 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
     const int want_waves = 2048;
     while (c.row_blocks * c.s * c.nwr * c.nwk < want_waves && KT / (c.s * 2 * c.nwk) >= 8) c.s *= 2;
   }
-  const int ew = (fmt == 0 ? 2 : 1) * gpt;  // fp32 words per scale entry
+  const int ew = (fmt == 0 && gpt == 2) ? 2 : 1;  // 32-bit words per scale entry
   for (;;) {
     const int slice_max = (KT + c.s - 1) / c.s;
     const int nthr = c.nwr * c.nwk * kWave;
@@ -776,6 +826,23 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
     ++c.s;
   }
   c.row_blocks = (N + 16 * c.nwr - 1) / (16 * c.nwr);
+  // the workgroup's scale block with 16-byte loads: K not split, K / G a
+  // multiple of 8 (whole units per row), at most kVU units per thread, and
+  // no more LDS than the per-wave blocks
+  const int ng = K / G;
+  c.vs = 0;
+  if (c.s == 1 && ng % 8 == 0 && 16L * c.nwr * (ng / 8) <= 2L * c.nwr * c.nwk * kWave) {
+    const int pitch = (KT * ew + 31) / 32 * 32 + 4;  // 16-byte rows, 4 mod 32 words
+    const long vs_bytes = 16L * c.nwr * pitch * 4;
+    const long ws_bytes = (long)c.nwr * c.nwk * 16 * c.sc_pitch * ew * 4;
+    if (vs_bytes <= ws_bytes + 8 * 1024) {
+      c.vs = 1;
+      c.sc_pitch = pitch;
+      const long red = (long)c.nwr * c.nwk * c.mt * 256 * 4;
+      const long need = c.x_bytes + vs_bytes;
+      c.lds_bytes = (size_t)(need > red ? need : red);
+    }
+  }
   c.kind = 0;
   c.cols = 1;
   c.ring = kRing;
@@ -806,7 +873,7 @@ int check_gemv_plan(const GemvPlan& c, int fmt) {
 
 namespace {
 
-template <int FMT, int LB, int MT, int XU, int R, bool ONE>
+template <int FMT, int LB, int MT, int XU, int R, bool ONE, bool VS>
 int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
               const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   if (const int bad = check_gemv_plan(c, FMT)) return bad;
@@ -814,10 +881,10 @@ int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const u
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   // the plan's one-workgroup budget; the NF4 table is static LDS on top
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R, ONE>),
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R, ONE, VS>),
                                    kGemvLdsOne - (FMT == 1 ? kLutBytes : 0), "w4_gemv");
   if (st != 0) return st;
-  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R, ONE>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
+  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R, ONE, VS>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
                      y, partial, c.nwr, c.nwk, c.sc_pitch, c.x_bytes);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
@@ -826,9 +893,14 @@ int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const u
 template <int FMT, int LB, int MT, int XU, int R>
 int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
              const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
-  if constexpr (MT == 1)
-    if (M == 1) return launch_t1<FMT, LB, 1, XU, R, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-  return launch_t1<FMT, LB, MT, XU, R, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  if constexpr (MT == 1) {
+    if (M == 1) {
+      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, true, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+      return launch_t1<FMT, LB, 1, XU, R, true, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+    }
+  }
+  if (c.vs) return launch_t1<FMT, LB, MT, XU, R, false, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_t1<FMT, LB, MT, XU, R, false, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
 template <int FMT, int LB, int MT, int C>
