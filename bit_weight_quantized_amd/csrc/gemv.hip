@@ -467,7 +467,9 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
 // the same 2^-24 (the odd pairs are shifted down rather than the
 // activations pre-scaled); for NF4 the activation pairs are permuted in
 // registers to the byte order of the level pairs.
-template <int FMT, int LB, int MT, int C, int R>
+// VS: as in the staged kernel, one scale block for the workgroup's 16 C rows
+// and all of K, fetched with 16-byte loads.
+template <int FMT, int LB, int MT, int C, int R, bool VS>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
@@ -501,8 +503,9 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
 #pragma unroll
   for (int c = 0; c < C; ++c) colc[c] = min(col0 + c, ncol - 1);
 
-  // scale block of this wave: entry (c, r, j) = column c, row r, tile t0 + j
-  uint32_t* sc = reinterpret_cast<uint32_t*>(smem) + (size_t)wave * C * 16 * sc_pitch * EW;
+  // scale block of this wave: entry (c, r, j) = column c, row r, tile t0 + j;
+  // VS: of the workgroup, entry (c, r, tile) at row 16 c + r, pitch sc_pitch
+  uint32_t* sc = reinterpret_cast<uint32_t*>(smem) + (VS ? 0 : (size_t)wave * C * 16 * sc_pitch * EW);
   const int n_se = C * 16 * cnt;
   const float inv_cnt = 1.0f / (float)max(cnt, 1);
   auto load_entry = [&](int e, uint32_t (&v)[EW]) {
@@ -515,6 +518,38 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
     } else {
       v[0] = *reinterpret_cast<const uint32_t*>(scale + o);
       if constexpr (EW == 2) v[1] = *reinterpret_cast<const uint32_t*>(zero + o);
+    }
+  };
+
+  constexpr int kVU = 2;  // VS units per thread (the plan guarantees 16 C upr <= kVU threads)
+  const int upr = ng / 8;
+  const float inv_upr = 1.0f / (float)max(upr, 1);
+  auto load_vunit = [&](int u, u32x4& vs, u32x4& vz) {
+    int r, cg;
+    div_small(u, upr, inv_upr, r, cg);
+    const size_t o = (size_t)(min(col0 + r / 16, ncol - 1) * 16 + r % 16) * ng + (size_t)cg * 8;
+    vs = *reinterpret_cast<const u32x4*>(scale + o);
+    if constexpr (FMT == 0) vz = *reinterpret_cast<const u32x4*>(zero + o);
+  };
+  auto store_vunit = [&](int u, const u32x4& vs, const u32x4& vz) {
+    int r, cg;
+    div_small(u, upr, inv_upr, r, cg);
+    uint32_t* dst = sc + (size_t)r * sc_pitch;
+    if constexpr (GPT == 1) {  // tiles 8 cg .. 8 cg + 7: s | z << 16
+      uint32_t e[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t zw = FMT == 0 ? vz[i] : 0u;
+        e[2 * i] = (vs[i] & 0xFFFFu) | (zw << 16);
+        e[2 * i + 1] = (vs[i] >> 16) | (zw & 0xFFFF0000u);
+      }
+      *reinterpret_cast<u32x4*>(dst + 8 * cg) = u32x4{e[0], e[1], e[2], e[3]};
+      *reinterpret_cast<u32x4*>(dst + 8 * cg + 4) = u32x4{e[4], e[5], e[6], e[7]};
+    } else if constexpr (EW == 2) {  // tiles 4 cg .. 4 cg + 3: s pair, z pair
+      *reinterpret_cast<u32x4*>(dst + 8 * cg) = u32x4{vs[0], vz[0], vs[1], vz[1]};
+      *reinterpret_cast<u32x4*>(dst + 8 * cg + 4) = u32x4{vs[2], vz[2], vs[3], vz[3]};
+    } else {  // NF4, tiles 4 cg .. 4 cg + 3: s pair
+      *reinterpret_cast<u32x4*>(dst + 4 * cg) = vs;
     }
   };
 
@@ -551,9 +586,17 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
                 ((uint32_t)float_to_half_bits(nf4_level(e >> 4)) << 16);
     }
   }
-  uint32_t se[kSEDirect][EW];
+  constexpr int kSEw = VS ? 1 : kSEDirect;
+  uint32_t se[kSEw][EW];
+  u32x4 vsv[VS ? kVU : 1], vzv[VS ? kVU : 1];
+  if constexpr (VS) {
+    const int n_vu = C * 16 * upr;
 #pragma unroll
-  for (int i = 0; i < kSEDirect; ++i) load_entry(min(lane + i * kWave, max(n_se, 1) - 1), se[i]);
+    for (int i = 0; i < kVU; ++i) load_vunit(min(tid + i * nthr, n_vu - 1), vsv[i], vzv[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSEDirect; ++i) load_entry(min(lane + i * kWave, max(n_se, 1) - 1), se[i]);
+  }
   Slot ring[R];
 #pragma unroll
   for (int d = 0; d < R; ++d) {
@@ -562,14 +605,23 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
     // waits in the loop count the same way on entry as in steady state
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (VS) {
+    const int n_vu = C * 16 * upr;
 #pragma unroll
-  for (int i = 0; i < kSEDirect; ++i) {
-    const int e = lane + i * kWave;
-    if (e < n_se) {
-      int cr, j;
-      div_small(e, max(cnt, 1), inv_cnt, cr, j);
+    for (int i = 0; i < kVU; ++i) {
+      const int u = tid + i * nthr;
+      if (u < n_vu) store_vunit(u, vsv[i], vzv[i]);
+    }
+  } else {
 #pragma unroll
-      for (int w = 0; w < EW; ++w) sc[(cr * sc_pitch + j) * EW + w] = se[i][w];
+    for (int i = 0; i < kSEDirect; ++i) {
+      const int e = lane + i * kWave;
+      if (e < n_se) {
+        int cr, j;
+        div_small(e, max(cnt, 1), inv_cnt, cr, j);
+#pragma unroll
+        for (int w = 0; w < EW; ++w) sc[(cr * sc_pitch + j) * EW + w] = se[i][w];
+      }
     }
   }
   if constexpr (FMT == 1) {
@@ -582,8 +634,9 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
           *reinterpret_cast<u32x4*>(&lut[e * kLutCopies + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
       }
     }
-    __syncthreads();  // the table is shared; the scale block is the wave's own
+    if constexpr (!VS) __syncthreads();  // the table is shared; the scale block is the wave's own
   }
+  if constexpr (VS) __syncthreads();  // the workgroup's scale block (and the NF4 table) are shared
 
   f32x4 acc_c[C][MT];
 #pragma unroll
@@ -619,7 +672,9 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
       for (int c = 0; c < C; ++c) {
         uint32_t sz[EW];
 #pragma unroll
-        for (int w = 0; w < EW; ++w) sz[w] = sc[((c * 16 + ln) * sc_pitch + ci) * EW + w];
+        for (int w = 0; w < EW; ++w)
+          sz[w] = VS ? sc[(size_t)(c * 16 + ln) * sc_pitch + (size_t)(t0 + ci) * EW + w]
+                     : sc[((c * 16 + ln) * sc_pitch + ci) * EW + w];
         const float sv = GPT == 1 ? half_bits_to_float((uint16_t)(sz[0] & 0xFFFFu))
                                   : half_bits_to_float((uint16_t)(sz[0] >> (16 * gi)));
         u32x4 B[WPG];
@@ -760,6 +815,19 @@ void plan_direct(GemvPlan& c, int M, int K, int N, int G, int fmt) {
   const long red = (long)c.nwk * c.cols * c.mt * 256 * 4;
   c.lds_bytes = (size_t)(sc_bytes > red ? sc_bytes : red);
   c.row_blocks = groups;
+  // the workgroup's scale block with 16-byte loads (as in the staged kernel);
+  // it and the reduction area are never live together
+  const int ng = K / G;
+  c.vs = 0;
+  if (c.s == 1 && ng % 8 == 0 && 16L * c.cols * (ng / 8) <= 2L * c.nwk * kWave) {
+    const int pitch = (KT * ew + 31) / 32 * 32 + 4;
+    const long vs_bytes = 16L * c.cols * pitch * 4;
+    if (vs_bytes <= sc_bytes + 8 * 1024) {
+      c.vs = 1;
+      c.sc_pitch = pitch;
+      c.lds_bytes = (size_t)(vs_bytes > red ? vs_bytes : red);
+    }
+  }
   (void)M;
 }
 
@@ -903,9 +971,9 @@ int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const ui
   return launch_t1<FMT, LB, MT, XU, R, false, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
-template <int FMT, int LB, int MT, int C>
-int launch_direct(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
-                  const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+template <int FMT, int LB, int MT, int C, bool VS>
+int launch_direct1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                   const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   constexpr int R = MT == 1 ? 4 : 2;
   const dim3 block(c.nwk * kWave);
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
@@ -914,13 +982,20 @@ int launch_direct(const GemvPlan& c, const uint16_t* x, int M, int K, int N, con
   // once per instantiation: beyond 64 KB of dynamic LDS a launch needs it
   const int budget = (int)gemv_lds_budget(FMT);
   if (const int bad = check_gemv_plan(c, FMT)) return bad;
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_direct_kernel<FMT, LB, MT, C, R>), budget,
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_direct_kernel<FMT, LB, MT, C, R, VS>), budget,
                                    "w4_gemv");
   if (st != 0) return st;
-  hipLaunchKernelGGL((gemv_direct_kernel<FMT, LB, MT, C, R>), grid, block, c.lds_bytes, s, x, M, K, N, packed,
+  hipLaunchKernelGGL((gemv_direct_kernel<FMT, LB, MT, C, R, VS>), grid, block, c.lds_bytes, s, x, M, K, N, packed,
                      scale, zero, y, partial, c.sc_pitch);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
+}
+
+template <int FMT, int LB, int MT, int C>
+int launch_direct(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                  const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+  if (c.vs) return launch_direct1<FMT, LB, MT, C, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_direct1<FMT, LB, MT, C, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
 template <int FMT, int LB, int MT>
