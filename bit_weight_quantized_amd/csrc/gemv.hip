@@ -96,13 +96,31 @@ __device__ __forceinline__ void div_small(int u, int d, float inv_d, int& q, int
 // NWK x MT x 256 floats of LDS, free when called after a barrier), then the
 // fp16 store, or with S > 1 the fp32 partial of this K slice (summed over the
 // slices by gemv_reduce_kernel, launched right after on the same stream).
-template <int MT>
+template <int MT, bool ONE = false>
 __device__ __forceinline__ void gemv_finish(const f32x4 (&C)[MT], float* red, int wave, int lane, int nwr, int nwk,
                                             int row_wg0, int M, int N, uint16_t* __restrict__ y,
                                             float* __restrict__ partial) {
   constexpr int kTile = MT * 256;
   const int S = gridDim.y;
   const int ks = blockIdx.y;
+  if constexpr (ONE) {
+    // M = 1: only token 0 is live, in lanes 0..15 (row l) of each wave
+    if (lane < 16) red[wave * 16 + lane] = C[0][0];
+    __syncthreads();
+    const int e = threadIdx.x;
+    if (e < 16 * nwr) {
+      const int w_r = e / 16, n = row_wg0 + e;
+      if (n < N) {
+        float sum = 0.f;
+        for (int k2 = 0; k2 < nwk; ++k2) sum += red[(k2 * nwr + w_r) * 16 + e % 16];
+        if (S == 1)
+          y[n] = float_to_half_bits(sum);
+        else
+          partial[(size_t)ks * N + n] = sum;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -454,7 +472,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   __syncthreads();
 
   // ---- cross-wave reduction (over wk) through LDS, reusing the staging area
-  gemv_finish<MT>(C, reinterpret_cast<float*>(smem), wave, lane, nwr, nwk, row_wg0, M, N, y, partial);
+  gemv_finish<MT, ONE>(C, reinterpret_cast<float*>(smem), wave, lane, nwr, nwk, row_wg0, M, N, y, partial);
 }
 
 // Direct variant.  Each wave owns C tile columns (16 C weight rows) and a run
