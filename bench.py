@@ -59,6 +59,10 @@ def parse():
                          "variants, calibrated on the plain copy")
     ap.add_argument("--kernels", metavar="REGEX", default=None,
                     help="with --summarize: only kernels whose name matches")
+    ap.add_argument("--counters", nargs="+", metavar="CSV",
+                    help="no GPU: per-kernel table of the counter_collection CSVs of several rocprofv3 --pmc "
+                         "passes over the same command (--profile-gemm or --profile-attention), with the "
+                         "derived matrix-core, clock, instruction-mix, LDS and HBM-traffic figures")
     ap.add_argument("--summarize", nargs="+", metavar="CSV",
                     help="no GPU: print a markdown summary of rocprofv3 CSV output (kernel_stats or "
                          "counter_collection files)")
@@ -163,7 +167,8 @@ def bench_gemm_prefill(w4, torch, reps):
             "note": "fp16 paths against the dense fp16 MFMA peak; msdJ issues J int8 products per useful "
                     "multiply-add and is measured against the dense int8 peak; msd times include the "
                     "activation decomposition; msd2_fixed uses s2 = s1/254 and combines the two int32 "
-                    "products in integers; mxfp4_J: MXFP4 weights (the same distribution, own draw), the "
+                    "products in integers; msd2_fixed_fused computes only s1 in a pre-pass and forms both "
+                    "slices inside the product's K loop (same y bits); mxfp4_J: MXFP4 weights (the same distribution, own draw), the "
                     "activations split into J MXFP4 slices, J block-scaled fp4 products per useful "
                     "multiply-add against the dense fp4 peak, decomposition included",
             "paths": res}
@@ -189,7 +194,8 @@ def prefill_paths(w4, torch):
     del wmx, mx_codes
     ws_mx = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_MX, M, K, N, 32, ns) for ns in (1, 2)), dtype=torch.uint8,
                         device="cuda")
-    ws = torch.empty(max(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, ns) for ns in (1, 2, 3)),
+    ws = torch.empty(max([w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, ns) for ns in (1, 2, 3)] +
+                         [w4.workspace_bytes(w4.OP_GEMM_DECOMP_FUSED, M, K, N, G, 0)]),
                      dtype=torch.uint8, device="cuda")
     ws_f16 = torch.empty(max(16, w4.workspace_bytes(w4.OP_GEMM, M, K, N, G, w4.DQ_F16)), dtype=torch.uint8,
                          device="cuda")
@@ -201,6 +207,8 @@ def prefill_paths(w4, torch):
         "msd2": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 2, out=y, workspace=ws), 2, INT8_MFMA_PEAK_TOPS),
         "msd2_fixed": (lambda: w4.gemm_decomp_fixed(x, packed, scale, zero, G, out=y, workspace=ws), 2,
                        INT8_MFMA_PEAK_TOPS),
+        "msd2_fixed_fused": (lambda: w4.gemm_decomp_fixed_fused(x, packed, scale, zero, G, out=y, workspace=ws), 2,
+                             INT8_MFMA_PEAK_TOPS),
         "msd1": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 1, out=y, workspace=ws), 1, INT8_MFMA_PEAK_TOPS),
         "msd3": (lambda: w4.gemm_decomp(x, packed, scale, zero, G, 3, out=y, workspace=ws), 3, INT8_MFMA_PEAK_TOPS),
         "mxfp4_2": (lambda: w4.gemm_mx(x, mx_packed, mx_scale, 2, out=y, workspace=ws_mx), 2, FP4_MFMA_PEAK_TFLOPS),
@@ -242,6 +250,24 @@ def bench_single_gemv(w4, torch, stream, replays=4):
                     "rotation_sets": n_sets})
     return {"workload": "single_gemv_m1_k1024_n1024_g64", "note": "launch-bound: 0.59 MB is about 74 ns of HBM "
             "time at peak", "per_launch": res}
+
+
+def bench_plain_read(w4, torch, stream, nbytes, replays=4):
+    """The HBM read ceiling for one decode-layer weight stream: w4_stream_read
+    (16-byte non-temporal loads, every byte once) over buffers of the GEMV's
+    35.65 MB, rotating over > 512 MB like the GEMV's weight sets; one launch
+    per buffer in a HIP graph replayed back to back."""
+    n_sets = rotation_sets(nbytes)
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(n_sets)]
+    acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = graph_of(torch, stream, [lambda b=b: w4.stream_read(b, acc) for b in bufs])
+    time_replays(torch, stream, g, 1)
+    us = time_replays(torch, stream, g, replays) * 1e3 / (replays * n_sets)
+    del g, bufs
+    torch.cuda.empty_cache()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "plain_read_35651584_bytes", "us_per_launch": round(us, 3), "bytes": nbytes,
+            "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "rotation_sets": n_sets}
 
 
 def bench_mlp_gemv(w4, torch, stream, replays=4):
@@ -297,7 +323,7 @@ def bench_decoder_layer(w4, torch, stream, replays=4):
         paths = [("gemv", 1)]
         paths += [("dq_f16", 256), ("postscale", 256)]
         if fmt == w4.INT4_ASYM:
-            paths += [("msd2", 256), ("msd2_fixed", 256)]
+            paths += [("msd2", 256), ("msd2_fixed", 256), ("msd2_fixed_fused", 256)]
         for path, M in paths:
             xs = {K: torch.from_numpy(wl.make_activations(5, 0 if K == 8192 else 6, M, K)).cuda()
                   for K in {K for _, K, _ in DECODER_LAYER}}
@@ -318,6 +344,11 @@ def bench_decoder_layer(w4, torch, stream, replays=4):
                                          device="cuda")
                         calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, mode=mode: w4.gemm(
                             x, p, sc, z, G, fmt, mode, out=y, workspace=ws))
+                    elif path == "msd2_fixed_fused":
+                        ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP_FUSED, M, K, N, G, 0),
+                                         dtype=torch.uint8, device="cuda")
+                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws: w4.gemm_decomp_fixed_fused(
+                            x, p, sc, z, G, out=y, workspace=ws))
                     else:
                         ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8,
                                          device="cuda")
@@ -625,6 +656,72 @@ def traffic_summary(fetch_csv, write_csv):
         print(f"| {name} | {n} | {f:.1f} | {w:.1f} | {alg} | {t / alg:.3f} | {t:.0f} |")
 
 
+def counter_summary(paths, pattern=None):
+    """One row per kernel (and launch geometry) over several --pmc passes:
+    each counter's mean per dispatch, then derived figures.
+    * MfmaUtil: rocprofv3's derived matrix-core busy percentage
+      (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the SIMD count);
+    * clock: GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 over the dispatch
+      duration of the same pass;
+    * VALU / MFMA: SQ_INSTS_VALU over SQ_INSTS_MFMA (issued instructions);
+    * MFMA co-exec: SQ_VALU_MFMA_COEXEC_CYCLES over SQ_VALU_MFMA_BUSY_CYCLES
+      is not derivable from one pass, so the raw counts are listed;
+    * LDS conflict: SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE;
+    * HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB) scaled by what they read for
+      the plain copies of COPY_BYTES at the end of the profiled command."""
+    import csv
+    import collections
+    import re
+    keep = (lambda name: re.search(pattern, name) is not None) if pattern else (lambda name: True)
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(lambda: collections.defaultdict(list))
+    copies = collections.defaultdict(list)
+    order = []
+    for path in paths:
+        with open(path, newline="") as f:
+            rows = list(csv.DictReader(f))
+        for r in rows:
+            name = r["Kernel_Name"]
+            counter = r["Counter_Name"]
+            if "copyBuffer" in name and int(r["Grid_Size"]) >= 65536:
+                copies[counter].append(float(r["Counter_Value"]))
+                continue
+            if not keep(name):
+                continue
+            key = (short_kernel(name), r["Grid_Size"], r["Workgroup_Size"])
+            if key not in vals:
+                order.append(key)
+            vals[key][counter].append(float(r["Counter_Value"]))
+            if "Start_Timestamp" in r and r["Start_Timestamp"]:
+                durs[key][counter].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    scale = {c: COPY_BYTES / (sum(v) / len(v) * 1024) for c, v in copies.items()
+             if c in ("FETCH_SIZE", "WRITE_SIZE") and v and sum(v) > 0}
+    if scale:
+        print("copy reference: " + ", ".join(
+            f"{c} reads {sum(copies[c]) / len(copies[c]):.1f} KiB per {COPY_BYTES}-byte copy (scale {scale[c]:.4f})"
+            for c in sorted(scale)) + "\n")
+    counters = sorted({c for k in order for c in vals[k]})
+    print("| kernel | grid | workgroup | " + " | ".join(counters) + " | derived |")
+    print("|---|---|---|" + "---|" * len(counters) + "---|")
+    for key in order:
+        v = {c: sum(x) / len(x) for c, x in vals[key].items()}
+        cells = [f"{v[c]:.4g}" if c in v else "" for c in counters]
+        d = []
+        if "MfmaUtil" in v:
+            d.append(f"MFMA busy {v['MfmaUtil']:.1f} %")
+        if "GRBM_GUI_ACTIVE" in v and durs[key].get("GRBM_GUI_ACTIVE"):
+            us = sum(durs[key]["GRBM_GUI_ACTIVE"]) / len(durs[key]["GRBM_GUI_ACTIVE"])
+            d.append(f"{us:.1f} us, clock {v['GRBM_GUI_ACTIVE'] / 8 / (us * 1e3):.2f} GHz")
+        if "SQ_INSTS_VALU" in v and v.get("SQ_INSTS_MFMA"):
+            d.append(f"VALU/MFMA {v['SQ_INSTS_VALU'] / v['SQ_INSTS_MFMA']:.2f}")
+        if "SQ_LDS_BANK_CONFLICT" in v and v.get("SQ_LDS_IDX_ACTIVE"):
+            d.append(f"LDS conflict {100 * v['SQ_LDS_BANK_CONFLICT'] / v['SQ_LDS_IDX_ACTIVE']:.1f} %")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in v and c in scale:
+                d.append(f"{c.split('_')[0].lower()} {v[c] * 1024 * scale[c] / 1e6:.1f} MB")
+        print(f"| `{key[0]}` | {key[1]} | {key[2]} | " + " | ".join(cells) + " | " + "; ".join(d) + " |")
+
+
 def short_kernel(name):
     name = name.replace("w4::(anonymous namespace)::", "")
     return name.split("(")[0] if "(" in name else name
@@ -637,6 +734,9 @@ def main():
         return
     if args.traffic:
         traffic_summary(*args.traffic)
+        return
+    if args.counters:
+        counter_summary(args.counters, args.kernels)
         return
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
@@ -678,6 +778,12 @@ def main():
                     fn()
                 torch.cuda.synchronize()
                 print(f"profile gemm: {args.profile_launches} calls of {name}", flush=True)
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(4):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(f"profile gemm: 4 copies of {COPY_BYTES} bytes (reads {COPY_BYTES}, writes {COPY_BYTES})", flush=True)
         return
     if args.profile_attention:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -772,6 +878,11 @@ def main():
     if traffic_rows and all(p["variant"] in traffic_rows for p in per):
         traffic = round(sum(traffic_rows[p["variant"]] for p in per) / len(per))
 
+    plain = None
+    try:
+        plain = bench_plain_read(w4, torch, stream, per_set)
+    except Exception as e:  # reported, never fatal to the headline line
+        plain = {"error": f"{type(e).__name__}: {e}"}
     gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
     single = None
     try:
@@ -829,8 +940,10 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": "packed N*K/2 + fp16 scales (+ zeros) = %d" % per_set,
-                     "launch_average_us": round(sum_us / len(per), 3)},
+                     "launch_average_us": round(sum_us / len(per), 3),
+                     "plain_read_frac": plain.get("hbm_frac") if isinstance(plain, dict) else None},
         "per_launch": per,
+        "plain_read": plain,
         "gemm_prefill": gemm,
         "single_gemv": single,
         "mlp_gemv": mlp,

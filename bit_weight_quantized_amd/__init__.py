@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
     "lib", "lib_path", "quantize", "pack", "gemv", "gemv_noalloc", "gemv_plan", "gemm", "gemm_decomp", "gemm_decomp_fixed",
+    "gemm_decomp_fixed_fused", "stream_read",
     "salient_select", "residual_correct", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
     "workspace_bytes", "nf4_levels", "version",
 ]
@@ -28,7 +29,7 @@ INT4_ASYM = 0
 NF4 = 1
 DQ_F16 = 0
 POSTSCALE = 1
-OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP, OP_GEMM_MX, OP_ATTN_MSD = range(7)
+OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP, OP_GEMM_MX, OP_ATTN_MSD, OP_GEMM_DECOMP_FUSED = range(8)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libw4.so")
@@ -66,6 +67,8 @@ def lib():
         L.w4_gemm.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _p, _p, _sz, _p]
         L.w4_gemm_decomp.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_gemm_decomp_fixed.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]
+        L.w4_gemm_decomp_fixed_fused.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _sz, _p]
+        L.w4_stream_read.argtypes = [_p, _sz, _p, _p]
         L.w4_salient_select.argtypes = [_p, _i, _i, _i, _p, _p]
         L.w4_quantize_mx.argtypes = [_p, _i, _i, _p, _p, _p]
         L.w4_pack_mx.argtypes = [_p, _i, _i, _p, _p]
@@ -81,7 +84,7 @@ def lib():
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
         for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemv_noalloc", "w4_gemv_plan", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
-                   "w4_salient_select", "w4_residual_correct", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
+                   "w4_gemm_decomp_fixed_fused", "w4_stream_read", "w4_salient_select", "w4_residual_correct", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
                    "w4_attn_decode_msd",
                    "w4_nf4_levels"):
             getattr(L, fn).restype = _i
@@ -252,6 +255,36 @@ def gemm_decomp_fixed(x, packed, scale, zero, G: int, *, out=None, slices_out=No
     if slices_out is None and tok_scale_out is None and acc_out is None:
         return out
     return out, slices_out, tok_scale_out, acc_out
+
+
+def gemm_decomp_fixed_fused(x, packed, scale, zero, G: int, *, out=None, tok_scale_out=None, workspace=None,
+                            stream=None):
+    """The fixed-ratio Multi-Scale Dequant product with the decomposition
+    inside the product's K loop (only the token scales are computed first);
+    y equals ``gemm_decomp_fixed``'s bit for bit.  Returns y, or
+    (y, tok_scale_out) when tok_scale_out is given."""
+    _dev(x, torch.float16, "x")
+    N, K = _weights(packed, scale, zero)
+    M = x.shape[0]
+    out = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else out
+    ws_n = workspace_bytes(OP_GEMM_DECOMP_FUSED, M, K, N, G, 0)
+    if workspace is None and ws_n:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=x.device)
+    _check("w4_gemm_decomp_fixed_fused", lib().w4_gemm_decomp_fixed_fused(
+        _ptr(x), M, K, N, _ptr(packed), _ptr(scale), _ptr(zero), G, _ptr(out), _ptr(tok_scale_out),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out if tok_scale_out is None else (out, tok_scale_out)
+
+
+def stream_read(buf, xor_acc, *, stream=None):
+    """A plain read of the device tensor buf (16-byte multiple): XORs its
+    32-bit words into the int32 device scalar xor_acc."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous CUDA tensor")
+    _dev(xor_acc, torch.int32, "xor_acc")
+    nbytes = buf.numel() * buf.element_size()
+    _check("w4_stream_read", lib().w4_stream_read(_ptr(buf), nbytes, _ptr(xor_acc), _stream(stream)))
+    return xor_acc
 
 
 def salient_select(x, k: int, *, out=None, stream=None):

@@ -685,6 +685,359 @@ int launch_msd(const int8_t* slices, int M, int K, int N, const uint8_t* packed,
   return launch_tail_reduce(tpart, tp, bm, kHBN, tiles_m, tiles_n, gm, M, N, y, s);
 }
 
+// ---------------------------------------------------------------------------
+// Fixed-ratio Multi-Scale Dequant with the decomposition moved into the
+// product's K loop.  A pre-pass computes only s_1 per token (the row absmax
+// over 127); every K step copies the fp16 activation tile to LDS with the
+// weight tiles and scales, and the workgroup turns it into the two int8 slices
+// (the operand layout gemm_msd_kernel reads) before that step's products.  The
+// slices never reach HBM; in exchange each workgroup column decides its rows
+// again, N / 256 times per element.
+//
+// The decisions are taken in fp32 and equal the fp64 ones of the separate
+// decomposition.  With inv = fp32(1 / s_1) (relative error <= 2^-24 plus the
+// fp64 step's 2^-53), t_1 = fl32(x * inv) is within 127.0001 * 2^-23 <
+// 2^-16 of x / s_1, and with r_1 = fl32(x - s_1 A_1) (one fused rounding) and
+// t_2 = fl32(fl32(254 r_1) * inv), t_2 is within 127.0001 * 2^-22 < 2^-15
+// of 254 r_1 / s_1 (|x| <= amax <= 127.00002 s_1, |r_1| <= s_1 / 2).  The fp64
+// quotients are within 2^-46 of the exact ones.  So wherever t is at least
+// 2^-14 away from every half-integer, rint(t) is the fp64 decision; elements
+// closer than that (about 1 in 8000 per slice) are decided again exactly
+// (exact_rint_f32).  rint and the byte come from one fp32 addition:
+// for |t| < 2^22, fl32(t + 1.5 * 2^23) = 1.5 * 2^23 + rint(t) (ties to even),
+// whose low byte is rint(t) in two's complement.
+constexpr float kRintMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kNearHalf = 0x1p-14f;
+
+// s_1 = fp32(max_k |x[m,k]| / 127) (the quotient in fp64) and its fixed-ratio
+// partner fp32(s_1 / 254) per token row; one wave per row.
+__global__ __launch_bounds__(256) void row_scale_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                        float* __restrict__ tok_scale) {
+  const int lane = threadIdx.x % kWave;
+  const int m = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (m >= M) return;
+  const uint16_t* xr = x + (size_t)m * K;
+  float amax = 0.f;
+  constexpr int kU = 4;
+  for (int k0 = 8 * lane; k0 < K; k0 += kU * 8 * kWave) {
+    u32x4 w[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int k = k0 + u * 8 * kWave;
+      w[u] = k < K ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        amax = fmaxf(amax, fabsf(half_bits_to_float((uint16_t)(w[u][i] & 0xFFFFu))));
+        amax = fmaxf(amax, fabsf(half_bits_to_float((uint16_t)(w[u][i] >> 16))));
+      }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) {
+    const double s1 = (double)(float)((double)amax / 127.0);
+    tok_scale[m] = (float)s1;
+    tok_scale[(size_t)M + m] = (float)(s1 / 254.0);
+  }
+}
+
+// The two codes of one element (fp32 path; `near` is set when either quotient
+// lies within kNearHalf of a half-integer).  Returns the bits of the clamped
+// magic sums, whose low bytes are A_1 and A_2.
+__device__ __forceinline__ void fixed_codes_f32(float xf, float s1, float inv, uint32_t& b1, uint32_t& b2,
+                                                bool& near) {
+#pragma clang fp contract(off)
+  const float t1 = xf * inv;
+  const float y1 = t1 + kRintMagic;
+  const float e1 = t1 - (y1 - kRintMagic);
+  near |= fabsf(fabsf(e1) - 0.5f) < kNearHalf;
+  const float y1c = fminf(fmaxf(y1, kRintMagic - 127.f), kRintMagic + 127.f);
+  const float r1 = fmaf(-s1, y1c - kRintMagic, xf);
+  const float t2 = (254.f * r1) * inv;
+  const float y2 = t2 + kRintMagic;
+  const float e2 = t2 - (y2 - kRintMagic);
+  near |= fabsf(fabsf(e2) - 0.5f) < kNearHalf;
+  const float y2c = fminf(fmaxf(y2, kRintMagic - 127.f), kRintMagic + 127.f);
+  b1 = __float_as_uint(y1c);
+  b2 = __float_as_uint(y2c);
+}
+
+// rint((v - c s_1) / s_1) decided exactly from an estimate t within 1/4 of
+// the quotient: the half-integer next to rint(t) on t's side is the only
+// boundary that can lie between them, and the sign of v - (c + boundary) s_1,
+// computed exactly and rounded once, tells on which side the quotient lies
+// (on the boundary: to even).  v and c + boundary are exact in fp32 here.
+// The fp64 decomposition decides rint(fl64(quotient)); the two agree because
+// no quotient here lies within 2^-25 of a half-integer without being one (its
+// distance is a multiple of the finer of the grids of x and s_1 / 2, divided
+// by s_1), while fl64 moves it by at most 2^-46.
+__device__ __forceinline__ float exact_rint_f32(float v, float c, float s1, float t) {
+#pragma clang fp contract(off)
+  const float q = (t + kRintMagic) - kRintMagic;
+  const float sg = t >= q ? 1.f : -1.f;
+  const float hb = q + 0.5f * sg;
+  const float d = fmaf(-(c + hb), s1, v);
+  const bool odd = ((int)q & 1) != 0;
+  return (d * sg > 0.f || (d == 0.f && odd)) ? q + sg : q;
+}
+
+template <int GPT>
+__global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_msd_fused_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
+    const float* __restrict__ tok_scale, float* __restrict__ tpart, int tile0, int gm) {
+  constexpr int G = kStepK / GPT;
+  constexpr int UPG = 2 / GPT;
+  constexpr int MT = msd_mt(GPT, 2, false), NT = 2;
+  constexpr int BM = 16 * MT;
+  constexpr int kX = BM * 256;             // fp16 activation tile of a step
+  constexpr int kXCopies = BM / 32;        // 4 rows of 256 bytes per copy, BM / 8 rows per wave
+  constexpr int kSlice = BM * 128;         // one slice's rows of a step
+  constexpr int kStage = kX + kHB + kHS;   // two stages, then the two slices
+  constexpr int kTPR = kF16Threads / BM;   // threads per row in the conversion
+  constexpr int kCPT = 8 / kTPR;           // 16-byte operand chunks per thread per slice
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* const slices = smem + 2 * kStage;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ln = lane % 16, kb = lane / 16;
+
+  const int tiles_n = (N + kHBN - 1) / kHBN;
+  const int place = tile0 + xcd_run(blockIdx.x, gridDim.x);
+  int mb, nb;
+  tile_mn(place, (M + BM - 1) / BM, tiles_n, gm, mb, nb);
+  const int n0 = nb * kHBN;
+  const int m0 = mb * BM;
+  const int ng = K / G;
+  const int KT = K / kStepK;
+  const int ntile_last = N / 16 - 1;
+  const int S = gridDim.y, ks = blockIdx.y;
+  const int kt0 = (int)((long)KT * ks / S), kt1 = (int)((long)KT * (ks + 1) / S);
+
+  // this thread's conversion row and its scale (rows past M: zeros)
+  const int crow = tid / kTPR, cq = tid % kTPR;
+  const float s1r = m0 + crow < M ? tok_scale[m0 + crow] : 0.f;
+  const float invr = s1r != 0.f ? (float)(1.0 / (double)s1r) : 0.f;
+
+  // ---- copies: wave w fills activation rows [w BM/8, (w + 1) BM/8) (4 rows
+  // of 256 bytes per copy; row r's 16-byte chunk c lands at slot
+  // c ^ 4 (r mod 4), which keeps the conversion's reads free of bank
+  // conflicts), weight tiles 2 w and 2 w + 1, and its share of the scales.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
+  uint32_t voff_x[kXCopies];
+#pragma unroll
+  for (int i = 0; i < kXCopies; ++i) {
+    const int row = wn * (BM / 8) + 4 * i + lane / 16;
+    const int c = (lane % 16) ^ ((row & 3) << 2);
+    voff_x[i] = (uint32_t)(m0 + row) * (uint32_t)K * 2u + (uint32_t)c * 16u;  // rows past M read zeros
+  }
+  uint32_t voff_b[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    voff_b[j] = (uint32_t)min(n0 / 16 + 2 * wn + j, ntile_last) * (uint32_t)KT * 1024 + (uint32_t)lane * 16;
+  constexpr int kSCTotal = GPT * 2 * 4;
+  constexpr int kSC = h_scale_copies(0, GPT);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scale, (uint32_t)((size_t)N * ng * 2));
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(zero, (uint32_t)((size_t)N * ng * 2));
+  uint32_t voff_s[kSC];
+  int sc_dst[kSC];
+#pragma unroll
+  for (int j = 0; j < kSC; ++j) {
+    const int c = (wn * kSC + j) % kSCTotal;
+    const int gi = c / 8, quarter = c % 4;
+    const int col = quarter * 64 + lane;
+    voff_s[j] = (uint32_t)(n0 + col) * (uint32_t)ng * 2u + (uint32_t)gi * 2u;
+    sc_dst[j] = kX + kHB + ((gi * 2 + (c / 4) % 2) * kHBN + quarter * 64) * 4;
+  }
+  auto stage = [&](int kt) { return smem + ((kt - kt0) % 2) * kStage; };
+  auto issue_step = [&](int kt) {
+    unsigned char* st = stage(kt);
+#pragma unroll
+    for (int i = 0; i < kXCopies; ++i)
+      copy16_to_lds(xr, voff_x[i], (uint32_t)kt * 256, st + (wn * (BM / 8) + 4 * i) * 256);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) copy16_to_lds(wr, voff_b[j], (uint32_t)kt * 1024, st + kX + (2 * wn + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < kSC; ++j) {
+      const int c = (wn * kSC + j) % kSCTotal;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(((c / 4) % 2) == 1 ? zr : sr, (lds_void*)(st + sc_dst[j]), 2,
+                                               voff_s[j], (uint32_t)kt * GPT * 2u, 0, 0);
+    }
+  };
+  // the step's activation tile -> both slices in operand order: thread
+  // (row, q) writes operand chunks c = q + kTPR i of its row (K positions
+  // 64 b + 8 kb + 0..7 and 64 b + 32 + 8 kb + 0..7, c = 4 b + kb)
+  auto convert = [&](const unsigned char* xs) {
+#pragma unroll
+    for (int i = 0; i < kCPT; ++i) {
+      const int c = cq + kTPR * i;
+      const int b = c / 4, kq = c % 4;
+      uint32_t d1[4], d2[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int xc = 8 * b + 4 * h + kq;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(xs + crow * 256 + ((xc ^ ((crow & 3) << 2)) << 4));
+        uint32_t b1[8], b2[8];
+        bool near = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          fixed_codes_f32(half_bits_to_float((uint16_t)(w[e / 2] >> (16 * (e % 2)))), s1r, invr, b1[e], b2[e],
+                          near);
+        if (near) {  // rare: decide this piece's codes exactly
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xf = half_bits_to_float((uint16_t)(w[e / 2] >> (16 * (e % 2))));
+            const float a1 = fminf(fmaxf(exact_rint_f32(xf, 0.f, s1r, xf * invr), -127.f), 127.f);
+            const float r1 = fmaf(-s1r, a1, xf);
+            const float a2 =
+                fminf(fmaxf(exact_rint_f32(254.f * xf, 254.f * a1, s1r, (254.f * r1) * invr), -127.f), 127.f);
+            b1[e] = (uint32_t)(int)a1;
+            b2[e] = (uint32_t)(int)a2;
+          }
+        }
+        // operand byte order e0 e4 e1 e5 | e2 e6 e3 e7 (low bytes of the codes)
+        auto pack = [](uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
+          return perm_b32(perm_b32(p3, p2, 0x0c0c0400u), perm_b32(p1, p0, 0x0c0c0400u), 0x05040100u);
+        };
+        d1[2 * h] = pack(b1[0], b1[4], b1[1], b1[5]);
+        d1[2 * h + 1] = pack(b1[2], b1[6], b1[3], b1[7]);
+        d2[2 * h] = pack(b2[0], b2[4], b2[1], b2[5]);
+        d2[2 * h + 1] = pack(b2[2], b2[6], b2[3], b2[7]);
+      }
+      const int off = crow * 128 + ((c ^ (crow & 7)) << 4);
+      *reinterpret_cast<u32x4*>(slices + off) = u32x4{d1[0], d1[1], d1[2], d1[3]};
+      *reinterpret_cast<u32x4*>(slices + kSlice + off) = u32x4{d2[0], d2[1], d2[2], d2[3]};
+    }
+  };
+
+  f32x4 C[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) C[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue_step(kt0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const unsigned char* cur = stage(kt);
+    if (kt + 1 < kt1) issue_step(kt + 1);  // into the stage step kt - 1 used, read by everyone before the barrier
+    convert(cur);
+    lds_barrier();  // the slices are written
+
+    const uint32_t* s_lds = reinterpret_cast<const uint32_t*>(cur + kX + kHB);
+    u32x4 Bq[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) Bq[nt] = *reinterpret_cast<const u32x4*>(cur + kX + (2 * wn + nt) * 1024 + lane * 16);
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      u32x4 Bi[UPG][NT];
+      float sv[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = wn * 32 + nt * 16 + ln;
+        sv[nt] = half_bits_to_float((uint16_t)s_lds[(gi * 2) * kHBN + col]);
+        const int zv = (int)half_bits_to_float((uint16_t)s_lds[(gi * 2 + 1) * kHBN + col]);
+        const uint32_t zb = (uint32_t)zv * 0x01010101u;
+#pragma unroll
+        for (int u = 0; u < UPG; ++u) {
+          const int pu = gi * UPG + u;
+          const uint32_t w0 = Bq[nt][2 * pu], w1 = Bq[nt][2 * pu + 1];
+          auto qz = [&](uint32_t q) { return ((q | 0x80808080u) - zb) ^ 0x80808080u; };
+          Bi[u][nt] = u32x4{qz(w0 & 0x0F0F0F0Fu), qz((w0 >> 4) & 0x0F0F0F0Fu), qz(w1 & 0x0F0F0F0Fu),
+                            qz((w1 >> 4) & 0x0F0F0F0Fu)};
+        }
+      }
+      u32x4 Af[2][2][UPG];
+      auto load_frag = [&](u32x4 (&A)[2][UPG], int mt) {
+        const int row = mt * 16 + ln;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int u = 0; u < UPG; ++u) {
+            const int c = 4 * (gi * UPG + u) + kb;
+            A[j][u] = *reinterpret_cast<const u32x4*>(slices + j * kSlice + row * 128 + ((c ^ (ln & 7)) << 4));
+          }
+      };
+      load_frag(Af[0], 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt + 1 < MT) load_frag(Af[(mt + 1) % 2], mt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        i32x4 D[2][NT];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            i32x4 d = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < UPG; ++u) d = mfma_i8(Af[mt % 2][j][u], Bi[u][nt], d);
+            D[j][nt] = d;
+          }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            C[mt][nt][i] = fmaf(sv[nt], (float)(__mul24(D[0][nt][i], 254) + D[1][nt][i]), C[mt][nt][i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of step kt + 1 have landed
+    lds_barrier();                  // everyone's have; the slices and this stage are free again
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + mt * 16 + 4 * kb + i;
+      if (m >= M) continue;
+      const float s1 = tok_scale[(size_t)M + m];  // s_1 / 254
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + wn * 32 + nt * 16 + ln;
+        if (n >= N) continue;
+        if (tpart)
+          tpart[(((size_t)ks * gridDim.x + (place - tile0)) * BM + (m - m0)) * kHBN + (n - n0)] = C[mt][nt][i] * s1;
+        else
+          y[(size_t)m * N + n] = float_to_half_bits(C[mt][nt][i] * s1);
+      }
+    }
+}
+
+template <int GPT>
+int launch_msd_fused(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
+                     const uint16_t* zero, uint16_t* y, const float* tok_scale, float* tpart, size_t tpart_bytes,
+                     hipStream_t s) {
+  constexpr int BM = 16 * msd_mt(GPT, 2, false);
+  constexpr int kLds = 2 * (BM * 256 + kHB + kHS) + 2 * BM * 128;
+  const void* fn = reinterpret_cast<const void*>(&gemm_msd_fused_kernel<GPT>);
+  const int st = allow_dynamic_lds(fn, kLds, "w4_gemm_decomp_fixed_fused");
+  if (st != 0) return st;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + kHBN - 1) / kHBN;
+  const long tiles = (long)tiles_n * tiles_m;
+  const int gm = gemm_group_rows();
+  const TailPlan tp = plan_tail(tiles, K / kStepK, BM, kHBN);
+  const bool tail = tp.S > 1 && tpart && tpart_bytes >= tp.bytes;
+  const long main_tiles = tail ? tp.main : tiles;
+  int st2;
+  if (main_tiles > 0) {
+    hipLaunchKernelGGL((gemm_msd_fused_kernel<GPT>), dim3((unsigned)main_tiles), dim3(kF16Threads), kLds, s, x, M, K,
+                       N, packed, scale, zero, y, tok_scale, nullptr, 0, gm);
+    if ((st2 = check_launch("gemm_msd_fused")) != 0) return st2;
+  }
+  if (!tail) return 0;
+  hipLaunchKernelGGL((gemm_msd_fused_kernel<GPT>), dim3((unsigned)tp.r, (unsigned)tp.S), dim3(kF16Threads), kLds, s,
+                     x, M, K, N, packed, scale, zero, y, tok_scale, tpart, (int)tp.main, gm);
+  if ((st2 = check_launch("gemm_msd_fused tail")) != 0) return st2;
+  return launch_tail_reduce(tpart, tp, BM, kHBN, tiles_m, tiles_n, gm, M, N, y, s);
+}
+
 }  // namespace
 
 // K slices for the fp16 GEMM: while the grid holds fewer than about 192
@@ -830,6 +1183,21 @@ int launch_gemm_decomp(const uint16_t* x, int M, int K, int N, const uint8_t* pa
   if (nslices == 2) W4_MSD(2, false);
   W4_MSD(3, false);
 #undef W4_MSD
+}
+
+size_t decomp_fused_workspace_bytes(int M) { return ((size_t)2 * M * sizeof(float) + 255) / 256 * 256; }
+
+int launch_gemm_decomp_fused(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
+                             const uint16_t* zero, int G, uint16_t* y, float* tok_scale, float* tpart,
+                             size_t tpart_bytes, hipStream_t s) {
+  if ((size_t)M * K * 2 >= (1ull << 32))
+    return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemm_decomp_fixed_fused: x of %d x %d exceeds the 4 GiB one call addresses",
+                M, K);
+  hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, x, M, K, tok_scale);
+  int st = check_launch("row_scale");
+  if (st != 0) return st;
+  return G == 64 ? launch_msd_fused<2>(x, M, K, N, packed, scale, zero, y, tok_scale, tpart, tpart_bytes, s)
+                 : launch_msd_fused<1>(x, M, K, N, packed, scale, zero, y, tok_scale, tpart, tpart_bytes, s);
 }
 
 }  // namespace w4

@@ -248,6 +248,30 @@ int w4_gemm_decomp_fixed(const uint16_t* x, int M, int K, int N, const uint8_t* 
                              tok_scale_out, acc_out, ws, ws_bytes, stream);
 }
 
+int w4_gemm_decomp_fixed_fused(const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                               const uint16_t* scale, const uint16_t* zero, int G, uint16_t* y,
+                               float* tok_scale_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "w4_gemm_decomp_fixed_fused";
+  g_last_error[0] = '\0';
+  int st;
+  if ((st = check_matmul_shape(fn, M, K, N, G)) != W4_OK) return st;
+  if (packed && scale && !zero)
+    return fail(W4_EUNSUPPORTED, "%s: needs INT4 weights (zero != NULL); NF4 levels are not integers", fn);
+  if ((st = check_weights(fn, packed, scale, zero, W4_INT4_ASYM)) != W4_OK) return st;
+  if ((st = check_io(fn, x, y)) != W4_OK) return st;
+  if (tok_scale_out && !aligned16(tok_scale_out))
+    return fail(W4_EINVAL, "%s: tok_scale_out must be 16-byte aligned", fn);
+  const size_t need = decomp_fused_workspace_bytes(M);
+  if (!ws || ws_bytes < need)
+    return fail(W4_EWORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need, ws_bytes);
+  if (!aligned16(ws)) return fail(W4_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  char* base = static_cast<char*>(ws);
+  float* ts = tok_scale_out ? tok_scale_out : reinterpret_cast<float*>(base);
+  float* tpart = ws_bytes > need ? reinterpret_cast<float*>(base + need) : nullptr;
+  return launch_gemm_decomp_fused(x, M, K, N, packed, scale, zero, G, y, ts, tpart, ws_bytes - need,
+                                  (hipStream_t)stream);
+}
+
 int w4_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, void* stream) {
   g_last_error[0] = '\0';
   if (M < 1 || K < 1 || K > kSelMaxK)
@@ -376,9 +400,22 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode) {
       if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G || fmt_or_mode < 1 || fmt_or_mode > 3) return 0;
       return decomp_workspace_bytes(M, K, G, fmt_or_mode) +
              (N >= 16 && K % 128 == 0 ? decomp_tail_bytes(M, K, N, G, fmt_or_mode) : 0);
+    case W4_OP_GEMM_DECOMP_FUSED:
+      if (M < 1 || K < 1 || (G != 64 && G != 128) || K % G) return 0;
+      return decomp_fused_workspace_bytes(M) + (N >= 16 && K % 128 == 0 ? decomp_tail_bytes(M, K, N, G, 2) : 0);
     default:
       return (size_t)-1;
   }
+}
+
+int w4_stream_read(const void* buf, size_t bytes, uint32_t* xor_acc, void* stream) {
+  g_last_error[0] = '\0';
+  if (bytes % 16) return fail(W4_EINVAL, "w4_stream_read: bytes must be a multiple of 16 (got %zu)", bytes);
+  if (bytes == 0) return W4_OK;
+  if (!buf || !xor_acc) return fail(W4_EINVAL, "w4_stream_read: buf and xor_acc must be non-null");
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(xor_acc) & 3u))
+    return fail(W4_EINVAL, "w4_stream_read: buf must be 16-byte and xor_acc 4-byte aligned");
+  return launch_stream_read(buf, bytes, xor_acc, (hipStream_t)stream);
 }
 
 int w4_nf4_levels(float* out16) {

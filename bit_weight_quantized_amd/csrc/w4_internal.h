@@ -112,6 +112,14 @@ int launch_gemm_decomp(const uint16_t* x, int M, int K, int N,
                        const uint16_t* zero, int G, int nslices, bool fixed, uint16_t* y,
                        int8_t* slices_op, int8_t* slices_out, float* tok_scale,
                        int32_t* acc_out, float* tpart, size_t tpart_bytes, hipStream_t s);
+// Fixed-ratio product with the decomposition inside the product's K loop:
+// fp32 token scales [2][M] (s_1, s_1 / 254) from a row-absmax pre-pass, then
+// one product launch (plus the tail, as for launch_gemm_decomp; its partials
+// need decomp_tail_bytes(M, K, N, G, 2)).
+size_t decomp_fused_workspace_bytes(int M);
+int launch_gemm_decomp_fused(const uint16_t* x, int M, int K, int N, const uint8_t* packed, const uint16_t* scale,
+                             const uint16_t* zero, int G, uint16_t* y, float* tok_scale, float* tpart,
+                             size_t tpart_bytes, hipStream_t s);
 
 // Residual compensation: the k salient channels of x (k <= kSelMaxTop,
 // K <= kSelMaxK), and y += x[:, idx] . R[idx, :] with R fp16 [K][N] in memory
@@ -143,5 +151,8 @@ int launch_attn_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, const uint
 
 // The 16 NF4 levels as fp32 bit patterns (host copy).
 extern const uint32_t kNf4LevelBits[16];
+
+// Plain read of bytes / 16 16-byte pieces, XOR-folded into *acc.
+int launch_stream_read(const void* buf, size_t bytes, uint32_t* acc, hipStream_t s);
 
 }  // namespace w4

@@ -87,7 +87,8 @@ typedef enum {
   W4_OP_GEMM = 3,
   W4_OP_GEMM_DECOMP = 4,
   W4_OP_GEMM_MX = 5,
-  W4_OP_ATTN_MSD = 6
+  W4_OP_ATTN_MSD = 6,
+  W4_OP_GEMM_DECOMP_FUSED = 7
 } w4_op;
 
 /*
@@ -254,6 +255,31 @@ int w4_gemm_decomp_fixed(const uint16_t* x, int M, int K, int N,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * w4_gemm_decomp_fixed_fused -- the fixed-ratio Multi-Scale Dequant product
+ * with the decomposition folded into the product's K loop ([MSD] Abstract:
+ * the decomposition replaces the weight conversion on the product's critical
+ * path).  A pre-pass over x computes only s_1 per token; each workgroup turns
+ * every step's fp16 activation tile into the two int8 slices in LDS, so the
+ * slices never reach HBM.  Codes, products and y are those of
+ * w4_gemm_decomp_fixed, bit for bit (the slices are decided in fp32 by a
+ * procedure proven to reproduce the fp64 decisions).
+ *
+ * Arguments, shapes and errors as for w4_gemm_decomp_fixed, without the
+ * slices and integer-product outputs; requires M * K * 2 < 4 GiB.
+ * tok_scale_out (optional, 16-byte aligned) fp32 [2][M] receives s_1 and
+ * fp32(s_1 / 254).  Workspace (required, 16-byte aligned, contents need not
+ * be initialised): at least w4_workspace_bytes(W4_OP_GEMM_DECOMP_FUSED, M, K,
+ * 0, G, 0) bytes for the token scales; with the real N it adds room for the
+ * fp32 partials of the left-over tiles, as for w4_gemm_decomp.  Calls that
+ * overlap in time must not share it.
+ */
+int w4_gemm_decomp_fixed_fused(const uint16_t* x, int M, int K, int N,
+                               const uint8_t* packed, const uint16_t* scale,
+                               const uint16_t* zero, int G, uint16_t* y,
+                               float* tok_scale_out, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
  * MXFP4 path ([MSD] Abstract: MXFP4 weights; the activations split into two
  * MXFP4 parts, each multiplied with the weights directly on the matrix cores).
  *
@@ -378,6 +404,18 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
  * W4_OP_GEMM_DECOMP and W4_OP_GEMM_MX.
  */
 size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode);
+
+/*
+ * w4_stream_read -- a plain read of a device buffer, the measured HBM read
+ * ceiling the weight-streaming kernels are compared with (not part of the
+ * method).  Every 16-byte piece of buf is loaded once with a non-temporal
+ * load, as the GEMV loads its weight tiles, and every 32-bit word is XORed
+ * into *xor_acc (a device word; zero it first to obtain the buffer's XOR).
+ * buf 16-byte aligned device memory, bytes a multiple of 16 (0: nothing
+ * happens); xor_acc 4-byte aligned device memory.  Errors: W4_EINVAL for a
+ * null or misaligned pointer or a byte count that is not a multiple of 16.
+ */
+int w4_stream_read(const void* buf, size_t bytes, uint32_t* xor_acc, void* stream);
 
 /* Host-only: copies the library's 16 fp32 NF4 levels into out16 (host). */
 int w4_nf4_levels(float* out16);

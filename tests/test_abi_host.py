@@ -125,6 +125,39 @@ def test_decomp_fixed_argument_errors(L):
     assert b"w4_gemm_decomp_fixed" in L.w4_last_error()
 
 
+def test_decomp_fixed_fused_argument_errors(L):
+    base = dict(x=FAKE, M=4, K=256, N=32, packed=FAKE, scale=FAKE, zero=FAKE, G=128)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return L.w4_gemm_decomp_fixed_fused(a["x"], a["M"], a["K"], a["N"], a["packed"], a["scale"], a["zero"],
+                                            a["G"], FAKE, a.get("ts"), a.get("ws"), a.get("wsb", 0), None)
+    assert call(zero=None) == W4_EUNSUPPORTED
+    assert call(G=32) == W4_EINVAL
+    assert call(K=192, G=64) == W4_EINVAL  # not a multiple of the 128-position tile
+    assert call(N=40) == W4_EINVAL
+    assert call(M=0) == W4_EINVAL
+    assert call() == W4_EWORKSPACE
+    need = L.w4_workspace_bytes(7, 4, 256, 0, 128, 0)
+    assert need == 256  # fp32 token scales [2][4], 256-byte aligned
+    assert call(ws=FAKE, wsb=need - 1) == W4_EWORKSPACE
+    assert call(ws=MISALIGNED, wsb=need) == W4_EINVAL
+    assert call(ts=MISALIGNED, ws=FAKE, wsb=need) == W4_EINVAL
+    assert b"w4_gemm_decomp_fixed_fused" in L.w4_last_error()
+    # with the real N the workspace adds the tail partials of the fixed-ratio product's plan
+    assert L.w4_workspace_bytes(7, 300, 1024, 4096, 128, 0) >= need
+    assert L.w4_workspace_bytes(7, 4, 192, 32, 64, 0) == 256 and L.w4_workspace_bytes(7, 4, 200, 32, 64, 0) == 0
+
+
+def test_stream_read_argument_errors(L):
+    assert L.w4_stream_read(FAKE, 24, FAKE, None) == W4_EINVAL  # not whole 16-byte pieces
+    assert L.w4_stream_read(None, 32, FAKE, None) == W4_EINVAL
+    assert L.w4_stream_read(FAKE, 32, None, None) == W4_EINVAL
+    assert L.w4_stream_read(MISALIGNED, 32, FAKE, None) == W4_EINVAL
+    assert b"w4_stream_read" in L.w4_last_error()
+    assert L.w4_stream_read(None, 0, None, None) == W4_OK  # nothing to read
+
+
 def test_residual_argument_errors(L):
     # selection: K beyond the LDS-resident key array, k beyond K or 1024, nulls
     assert L.w4_salient_select(FAKE, 1, 32769, 4, FAKE, None) == W4_EINVAL
