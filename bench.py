@@ -259,7 +259,7 @@ def bench_plain_read(w4, torch, stream, nbytes, replays=4):
     per buffer in a HIP graph replayed back to back."""
     n_sets = rotation_sets(nbytes)
     bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(n_sets)]
-    acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc = torch.zeros(w4.STREAM_READ_ACC_WORDS, dtype=torch.int32, device="cuda")
     g = graph_of(torch, stream, [lambda b=b: w4.stream_read(b, acc) for b in bufs])
     time_replays(torch, stream, g, 1)
     us = time_replays(torch, stream, g, replays) * 1e3 / (replays * n_sets)

@@ -29,6 +29,7 @@ INT4_ASYM = 0
 NF4 = 1
 DQ_F16 = 0
 POSTSCALE = 1
+STREAM_READ_ACC_WORDS = 449  # W4_STREAM_READ_ACC_WORDS
 OP_QUANTIZE, OP_PACK, OP_GEMV, OP_GEMM, OP_GEMM_DECOMP, OP_GEMM_MX, OP_ATTN_MSD, OP_GEMM_DECOMP_FUSED = range(8)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -278,10 +279,13 @@ def gemm_decomp_fixed_fused(x, packed, scale, zero, G: int, *, out=None, tok_sca
 
 def stream_read(buf, xor_acc, *, stream=None):
     """A plain read of the device tensor buf (16-byte multiple): XORs its
-    32-bit words into the int32 device scalar xor_acc."""
+    32-bit words into xor_acc[0], xor_acc[64], ..., xor_acc[448] (an int32
+    device tensor of at least STREAM_READ_ACC_WORDS elements)."""
     if not (buf.is_cuda and buf.is_contiguous()):
         raise ValueError("buf must be a contiguous CUDA tensor")
     _dev(xor_acc, torch.int32, "xor_acc")
+    if xor_acc.numel() < STREAM_READ_ACC_WORDS:
+        raise ValueError(f"xor_acc needs {STREAM_READ_ACC_WORDS} int32 elements")
     nbytes = buf.numel() * buf.element_size()
     _check("w4_stream_read", lib().w4_stream_read(_ptr(buf), nbytes, _ptr(xor_acc), _stream(stream)))
     return xor_acc

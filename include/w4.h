@@ -410,11 +410,15 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode);
  * ceiling the weight-streaming kernels are compared with (not part of the
  * method).  Every 16-byte piece of buf is loaded once with a non-temporal
  * load, as the GEMV loads its weight tiles, and every 32-bit word is XORed
- * into *xor_acc (a device word; zero it first to obtain the buffer's XOR).
- * buf 16-byte aligned device memory, bytes a multiple of 16 (0: nothing
- * happens); xor_acc 4-byte aligned device memory.  Errors: W4_EINVAL for a
- * null or misaligned pointer or a byte count that is not a multiple of 16.
+ * into one of the eight device words xor_acc[0], xor_acc[64], ...,
+ * xor_acc[448] (spread so that the folds do not serialize on one address;
+ * zero them first: their XOR is then the buffer's XOR).  buf 16-byte aligned
+ * device memory, bytes a multiple of 16 (0: nothing happens); xor_acc 4-byte
+ * aligned device memory of at least W4_STREAM_READ_ACC_WORDS words.  Errors:
+ * W4_EINVAL for a null or misaligned pointer or a byte count that is not a
+ * multiple of 16.
  */
+#define W4_STREAM_READ_ACC_WORDS 449
 int w4_stream_read(const void* buf, size_t bytes, uint32_t* xor_acc, void* stream);
 
 /* Host-only: copies the library's 16 fp32 NF4 levels into out16 (host). */
