@@ -356,6 +356,277 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// One wave per chunk (G <= 8 query heads per key/value head).  With at most 8
+// heads, the 16 rows of a product hold both slices at once: rows 0-7 the
+// first slice of heads 0-7, rows 8-15 the second, so one pair of products
+// gives both D_1 and D_2 of a key tile.  The results of two tiles A and B are
+// then exchanged between the lane halves (v_permlane32_swap: lanes 32-63 of
+// the first with lanes 0-31 of the second), after which lane l holds, for
+// heads 4 hq + i (hq = (l / 16) mod 2), D_1 and D_2 of token l mod 16 of tile
+// A (l < 32) or B (l >= 32): every lane carries useful values, and the
+// softmax and slicing work per lane is half that of a 16-head layout.  The
+// value product stacks the weight slices the same way.  A wave's row
+// reductions stay inside the wave (DPP within 16 lanes, then the two halves),
+// so no workgroup barrier is needed per chunk; the 4 waves of a workgroup
+// (4 consecutive chunks) merge their (max, sum, output) once at the end.
+__device__ __forceinline__ void swap_halves(int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)a, (unsigned)b, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+
+// reduction over the 32 lanes that hold the same heads: the 16 lanes of a
+// row group, then lane l with lane l ^ 32
+template <bool MAX>
+__device__ __forceinline__ float row32(float v) {
+  v = row16<MAX>(v);
+  int a = __builtin_bit_cast(int, v), b = a;
+  swap_halves(a, b);  // a: lanes 0-31 of v on both halves, b: lanes 32-63
+  const float x = __builtin_bit_cast(float, a), y = __builtin_bit_cast(float, b);
+  return MAX ? fmaxf(x, y) : x + y;
+}
+
+// byte offset of chunk position t in the int8 operand order: per 64
+// positions, 64 b + 32 hh + 8 k + e sits at byte 64 b + 16 k + 8 hh + p(e),
+// p(0..7) = 0, 2, 4, 6, 1, 3, 5, 7
+__device__ __forceinline__ int operand_byte(int t) {
+  const int bb = t / 64, pos = t % 64, hh = pos / 32, kk = (pos % 32) / 8, e = pos % 8;
+  return 64 * bb + 16 * kk + 8 * hh + (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+}
+
+__global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
+    const int8_t* __restrict__ qsl, const float* __restrict__ qsc, int MQ, int Hq, int Hkv, int L,
+    const uint8_t* __restrict__ kp, const uint16_t* __restrict__ ks, const uint16_t* __restrict__ kz,
+    const uint8_t* __restrict__ vtp, const uint16_t* __restrict__ vs, const uint16_t* __restrict__ vz,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __align__(16) int8_t psl[kAttnWaves][16][kChunk];  // each wave's stacked weight slices
+  __shared__ float mo[kAttnWaves][8][kHeadDim];                  // each wave's chunk output
+  __shared__ float mml[kAttnWaves][8][2];                        // and its (max, sum) per head
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nsplit = gridDim.x;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ln = lane % 16, kb = lane / 16;
+  const int hi = lane / 32, hq = kb % 2;  // after the swaps: tile half, head quad
+  const size_t bh = (size_t)b * Hkv + h;
+  const int qrow0 = b * Hq + h * G;
+  const int chunk = split * kAttnWaves + w;
+  const int ltiles = L / 128;
+
+  float Mw[4], Lw[4], O[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Mw[i] = -INFINITY;
+    Lw[i] = 0.f;
+#pragma unroll
+    for (int np = 0; np < 4; ++np) O[np][i] = 0.f;
+  }
+
+  if (chunk < L / kChunk) {  // wave-uniform
+    const size_t tok0 = bh * L + (size_t)chunk * kChunk;
+    // ---- this chunk's 16 key tiles, their zero points (token ln of every
+    // tile: the B operand's rows) and the scales of the tokens the lane holds
+    // after the swaps (token ln of tile 2 p + hi)
+    u32x4 T[16];
+    const uint8_t* kbase = kp + (bh * (size_t)(L / 16) + (size_t)chunk * 16) * 1024 + 16 * lane;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) T[t] = *reinterpret_cast<const u32x4*>(kbase + (size_t)t * 1024);
+    uint16_t zk[16], sk[8];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) zk[t] = kz[tok0 + 16 * t + ln];
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) sk[pp] = ks[tok0 + 16 * (2 * pp + hi) + ln];
+    // ---- and its 16 value tiles (V^T: 8 tiles of 16 dimensions by 2 of 128
+    // positions) with their scales and zero points, all in flight at once:
+    // a wave computes one chunk, so nothing later would hide their latency
+    u32x4 V[16];
+    const uint8_t* vbase = vtp + bh * (size_t)L * (kHeadDim / 2) + 16 * lane;
+#pragma unroll
+    for (int nd = 0; nd < 8; ++nd)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        V[2 * nd + q] = *reinterpret_cast<const u32x4*>(vbase + ((size_t)nd * ltiles + chunk * 2 + q) * 1024);
+    uint16_t sv16[8], zv16[8];
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      sv16[pp] = vs[tok0 + 16 * (2 * pp + hi) + ln];
+      zv16[pp] = vz[tok0 + 16 * (2 * pp + hi) + ln];
+    }
+
+    // ---- stacked query operands: row ln = slice ln / 8 of head ln % 8
+    u32x4 Aq[2];
+    {
+      const int j = ln / 8, g = ln % 8;
+#pragma unroll
+      for (int pu = 0; pu < 2; ++pu)
+        Aq[pu] = g < G ? *reinterpret_cast<const u32x4*>(qsl + ((size_t)j * MQ + qrow0 + g) * kHeadDim + 64 * pu + 16 * kb)
+                       : u32x4{0, 0, 0, 0};
+    }
+    float s1q[4], s2q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * hq + i;
+      s1q[i] = g < G ? qsc[qrow0 + g] : 0.f;
+      s2q[i] = g < G ? qsc[(size_t)MQ + qrow0 + g] : 0.f;
+    }
+
+    // ---- scores: tile pairs (2 p, 2 p + 1)
+    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
+    float sc[8][4];
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      i32x4 D[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const u32x4& kt = T[2 * pp + hh];
+        const uint32_t zb = (uint32_t)half_bits_to_float(zk[2 * pp + hh]) * 0x01010101u;
+        auto qz = [&](uint32_t q) { return ((q | 0x80808080u) - zb) ^ 0x80808080u; };  // bytes q - z
+        u32x4 Bk[2];
+#pragma unroll
+        for (int pu = 0; pu < 2; ++pu) {
+          const uint32_t w0 = kt[2 * pu], w1 = kt[2 * pu + 1];
+          Bk[pu] = u32x4{qz(w0 & 0x0F0F0F0Fu), qz((w0 >> 4) & 0x0F0F0F0Fu), qz(w1 & 0x0F0F0F0Fu),
+                         qz((w1 >> 4) & 0x0F0F0F0Fu)};
+        }
+        D[hh] = mfma_i8_16x16x64(Aq[0], Bk[0], i32x4{0, 0, 0, 0});
+        D[hh] = mfma_i8_16x16x64(Aq[1], Bk[1], D[hh]);
+      }
+      const float skf = half_bits_to_float(sk[pp]) * inv_sqrt_d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int x = D[0][i], y = D[1][i];
+        swap_halves(x, y);  // x: D_1, y: D_2 of token ln of tile 2 pp + hi, head 4 hq + i
+        sc[pp][i] = skf * fmaf(s1q[i], (float)x, s2q[i] * (float)y);
+      }
+    }
+
+    // ---- softmax over the chunk, weights w = p sV, their two int8 slices
+    float m[4], l[4], am[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[i] = sc[0][i];
+#pragma unroll
+      for (int pp = 1; pp < 8; ++pp) m[i] = fmaxf(m[i], sc[pp][i]);
+      m[i] = row32<true>(m[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l[i] = 0.f;
+      am[i] = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < 8; ++pp) {
+        const float e = __expf(sc[pp][i] - m[i]);
+        l[i] += e;
+        sc[pp][i] = e * half_bits_to_float(sv16[pp]);
+        am[i] = fmaxf(am[i], sc[pp][i]);
+      }
+      l[i] = row32<false>(l[i]);
+      am[i] = row32<true>(am[i]);
+    }
+    float r1[4], r2[4], zt1[4], zt2[4];
+    int8_t* my = &psl[w][0][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r1[i] = am[i] * (1.f / 127.f);
+      const float inv1 = r1[i] > 0.f ? 1.f / r1[i] : 0.f;
+      float am2 = 0.f;
+      int z1 = 0;
+#pragma unroll
+      for (int pp = 0; pp < 8; ++pp) {
+        const float a = quant_i8(sc[pp][i], inv1);
+        const int t = 16 * (2 * pp + hi) + ln;
+        my[(4 * hq + i) * kChunk + operand_byte(t)] = (int8_t)(int)a;
+        z1 += (int)a * (int)half_bits_to_float(zv16[pp]);
+        sc[pp][i] = sc[pp][i] - r1[i] * a;
+        am2 = fmaxf(am2, fabsf(sc[pp][i]));
+      }
+      r2[i] = row32<true>(am2) * (1.f / 127.f);
+      const float inv2 = r2[i] > 0.f ? 1.f / r2[i] : 0.f;
+      int z2 = 0;
+#pragma unroll
+      for (int pp = 0; pp < 8; ++pp) {
+        const float a = quant_i8(sc[pp][i], inv2);
+        const int t = 16 * (2 * pp + hi) + ln;
+        my[(8 + 4 * hq + i) * kChunk + operand_byte(t)] = (int8_t)(int)a;
+        z2 += (int)a * (int)half_bits_to_float(zv16[pp]);
+      }
+      zt1[i] = row32<false>((float)z1);  // |sum| <= 256 * 127 * 15 < 2^24: exact
+      zt2[i] = row32<false>((float)z2);
+    }
+
+    // ---- values: E (rows 0-7 slice 1, 8-15 slice 2) per dim tile, pairs of
+    // dim tiles exchanged between the halves like the scores.  The slices
+    // were written by this wave; its LDS accesses complete in order.
+    u32x4 Av[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Av[u] = *reinterpret_cast<const u32x4*>(my + ln * kChunk + 64 * u + 16 * kb);
+#pragma unroll
+    for (int np = 0; np < 4; ++np) {
+      i32x4 E[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int nd = 2 * np + hh;
+        E[hh] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const u32x4& vt = V[2 * nd + u / 2];
+          const uint32_t w0 = vt[2 * (u % 2)], w1 = vt[2 * (u % 2) + 1];
+          const u32x4 Bv{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
+          E[hh] = mfma_i8_16x16x64(Av[u], Bv, E[hh]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int x = E[0][i], y = E[1][i];
+        swap_halves(x, y);  // dim 16 (2 np + hi) + ln, head 4 hq + i
+        O[np][i] = fmaf(r1[i], (float)x - zt1[i], r2[i] * ((float)y - zt2[i]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      Mw[i] = m[i];
+      Lw[i] = l[i];
+    }
+  }
+
+  // ---- merge the workgroup's chunks: (max, sum) and the unnormalised output
+  // relative to the merged max, as one partial of this split
+  if (ln == 0 && hi == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mml[w][4 * hq + i][0] = Mw[i];
+      mml[w][4 * hq + i][1] = Lw[i];
+    }
+#pragma unroll
+  for (int np = 0; np < 4; ++np)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mo[w][4 * hq + i][16 * (2 * np + hi) + ln] = O[np][i];
+  __syncthreads();
+  for (int e = tid; e < 8 * kHeadDim; e += kAttnThreads) {
+    const int g = e / kHeadDim, n = e % kHeadDim;
+    if (g >= G) break;  // e grows with g
+    float mx = mml[0][g][0];
+#pragma unroll
+    for (int ww = 1; ww < kAttnWaves; ++ww) mx = fmaxf(mx, mml[ww][g][0]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kAttnWaves; ++ww) {
+      const float f = __expf(mml[ww][g][0] - mx);  // 0 for a wave without a chunk
+      num = fmaf(f, mo[ww][g][n], num);
+      den = fmaf(f, mml[ww][g][1], den);
+    }
+    const size_t row = (size_t)(qrow0 + g) * nsplit + split;
+    part_o[row * kHeadDim + n] = num;
+    if (n == 0) {
+      part_ml[row * 2] = mx;
+      part_ml[row * 2 + 1] = den;
+    }
+  }
+}
+
 // one workgroup of 128 threads per query row: o[n] = sum_s e^(m_s - m) o_s[n]
 // / sum_s e^(m_s - m) l_s over the splits, in order (every thread reads the
 // splits' maxima and sums; the outputs eight splits at a time)
@@ -403,6 +674,12 @@ int attn_chunks_per_split(int B, int Hkv, int L) {
   return cpw;
 }
 
+// W4_ATTN_WAVE=0 selects the chunk-split kernel for every G (comparison runs).
+bool attn_wave_kernel_enabled() {
+  const char* e = std::getenv("W4_ATTN_WAVE");
+  return !(e && *e == '0');
+}
+
 size_t attn_workspace_bytes(int B, int Hq, int L) {
   const size_t MQ = (size_t)B * Hq;
   const size_t nchunk = (size_t)L / kChunk;
@@ -428,11 +705,19 @@ int launch_attn_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, const uint
   float* pm = reinterpret_cast<float*>(base);
   int st = launch_decompose(q, MQ, kHeadDim, 2, false, qsl, nullptr, qsc, s);
   if (st != 0) return st;
-  const int cpw = attn_chunks_per_split(B, Hkv, L);
-  const int nsplit = nchunk / cpw;
-  hipLaunchKernelGGL(attn_msd_chunk_kernel, dim3(nsplit, Hkv, B), dim3(kAttnThreads), 0, s, qsl, qsc, MQ, Hq, Hkv, L,
-                     cpw, kp, ks, kz, vtp, vs, vz, po, pm);
-  st = check_launch("attn_msd_chunk");
+  int nsplit;
+  if (Hq / Hkv <= 8 && attn_wave_kernel_enabled()) {
+    nsplit = (nchunk + kAttnWaves - 1) / kAttnWaves;
+    hipLaunchKernelGGL(attn_msd_wave_kernel, dim3(nsplit, Hkv, B), dim3(kAttnThreads), 0, s, qsl, qsc, MQ, Hq, Hkv, L,
+                       kp, ks, kz, vtp, vs, vz, po, pm);
+    st = check_launch("attn_msd_wave");
+  } else {
+    const int cpw = attn_chunks_per_split(B, Hkv, L);
+    nsplit = nchunk / cpw;
+    hipLaunchKernelGGL(attn_msd_chunk_kernel, dim3(nsplit, Hkv, B), dim3(kAttnThreads), 0, s, qsl, qsc, MQ, Hq, Hkv,
+                       L, cpw, kp, ks, kz, vtp, vs, vz, po, pm);
+    st = check_launch("attn_msd_chunk");
+  }
   if (st != 0) return st;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(MQ), dim3(kHeadDim), 0, s, po, pm, nsplit, out);
   return check_launch("attn_combine");

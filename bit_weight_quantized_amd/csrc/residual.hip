@@ -22,15 +22,24 @@ constexpr int kIdxBits = 17;  // channel field of a selection key
 // << 17 | (2^17 - 1 - c); for finite inputs the bit pattern of |x| orders like
 // its value, so larger keys are higher scores and, among equal scores, lower
 // channels, and keys are distinct (and nonzero, since K < 2^17).  A radix
-// select (four 8-bit digits, most significant first) finds the k-th largest
-// key T; the k keys >= T are gathered and sorted (bitonic, descending).
+// select (8-bit digits, most significant first) narrows down the prefix of
+// the k-th largest key; it stops as soon as the bucket holding that key holds
+// exactly the keys still needed, so every key whose prefix is at least the
+// final prefix is picked (usually after two digits).  The k picked keys are
+// gathered (one atomic per wave) and each is written to the place its rank
+// among them gives (the number of larger keys), which is the sorted order.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                      int k, int32_t* __restrict__ idx) {
   extern __shared__ uint32_t keys[];  // [K]
   __shared__ uint32_t hist[256];
   __shared__ uint32_t top[kSelMaxTop];
-  __shared__ uint32_t s_prefix, s_remaining, s_count;
+  __shared__ uint32_t s_prefix, s_remaining, s_count, s_done;
   const int tid = threadIdx.x;
+  const int lane = tid % kWave;
 
   for (int c = tid; c < K; c += kSelThreads) {
     uint32_t s = 0;
@@ -41,6 +50,7 @@ __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint1
     s_prefix = 0;
     s_remaining = (uint32_t)k;
     s_count = 0;
+    s_done = 0;
   }
   __syncthreads();
 
@@ -76,36 +86,36 @@ __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint1
         while (b > 0 && h[b] < r) r -= h[b--];
         s_remaining = r;
         s_prefix = prefix | ((uint32_t)(4 * tid + b) << shift);
+        if (h[b] == r) s_done = 1;  // the whole bucket is needed: its keys and every larger one
       }
     }
     mask |= 255u << shift;
     __syncthreads();
+    if (s_done) break;
   }
 
-  const uint32_t T = s_prefix;  // the k-th largest key
-  for (int c = tid; c < K; c += kSelThreads) {
-    const uint32_t key = keys[c];
-    if (key >= T) top[atomicAdd(&s_count, 1u)] = key;
-  }
-  int P = 1;
-  while (P < k) P <<= 1;
-  for (int i = k + tid; i < P; i += kSelThreads) top[i] = 0;  // padding sorts last
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P / 2; i += kSelThreads) {
-        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
-        const bool desc = (lo & size) == 0;  // the final merge (size = P) is descending
-        const uint32_t a = top[lo], b = top[hi];
-        if ((a < b) == desc) {
-          top[lo] = b;
-          top[hi] = a;
-        }
-      }
-      __syncthreads();
+  // gather the k keys whose masked prefix is at least the final prefix
+  const uint32_t T = s_prefix;
+  for (int c0 = 0; c0 < K; c0 += kSelThreads) {  // wave-uniform trip count
+    const int c = c0 + tid;
+    const uint32_t key = c < K ? keys[c] : 0u;
+    const bool sel = c < K && (key & mask) >= T;
+    const uint64_t b = __ballot(sel);
+    if (b) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s_count, (uint32_t)__popcll(b));
+      base = (uint32_t)__shfl((int)base, 0);
+      if (sel) top[base + lanes_below(b)] = key;
     }
-  for (int j = tid; j < k; j += kSelThreads)
-    idx[j] = (1 << kIdxBits) - 1 - (int)(top[j] & ((1u << kIdxBits) - 1));
+  }
+  __syncthreads();
+  // rank of each gathered key = number of larger ones (keys are distinct)
+  for (int i = tid; i < k; i += kSelThreads) {
+    const uint32_t key = top[i];
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += top[j] > key ? 1 : 0;
+    idx[r] = (1 << kIdxBits) - 1 - (int)(key & ((1u << kIdxBits) - 1));
+  }
 }
 
 // ---------------------------------------------------------------------------
