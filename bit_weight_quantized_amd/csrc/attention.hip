@@ -395,8 +395,20 @@ __device__ __forceinline__ int operand_byte(int t) {
   return 64 * bb + 16 * kk + 8 * hh + (e < 4 ? 2 * e : 2 * (e - 4) + 1);
 }
 
+// clamp(rint(fl64(n / s)), -127, 127) as the decomposition kernel decides
+// it: inv = 1 / s correctly rounded, |n / s| < 2^8, so fl64(n * inv) and the
+// quotient round alike unless the quotient lies within 2^-44 of a
+// half-integer; a product within 2^-30 of one takes the division itself.
+__device__ __forceinline__ double quant127_q(double n, double s, double inv) {
+  if (s == 0.0) return 0.0;
+  const double t = n * inv;
+  double q = rint(t);
+  if (fabs(fabs(t - q) - 0.5) < 0x1p-30) q = rint(n / s);
+  return fmin(fmax(q, -127.0), 127.0);
+}
+
 __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
-    const int8_t* __restrict__ qsl, const float* __restrict__ qsc, int MQ, int Hq, int Hkv, int L,
+    const uint16_t* __restrict__ qh, int MQ, int Hq, int Hkv, int L,
     const uint8_t* __restrict__ kp, const uint16_t* __restrict__ ks, const uint16_t* __restrict__ kz,
     const uint8_t* __restrict__ vtp, const uint16_t* __restrict__ vs, const uint16_t* __restrict__ vz,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
@@ -427,21 +439,76 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
 
   if (chunk < L / kChunk) {  // wave-uniform
     const size_t tok0 = bh * L + (size_t)chunk * kChunk;
-    // ---- this chunk's 16 key tiles, their zero points (token ln of every
-    // tile: the B operand's rows) and the scales of the tokens the lane holds
-    // after the swaps (token ln of tile 2 p + hi)
+    // ---- this chunk's 16 key tiles, and the scales and zero points of the
+    // tokens the lane holds after the swaps (token ln of tile 2 p + hi)
     u32x4 T[16];
     const uint8_t* kbase = kp + (bh * (size_t)(L / 16) + (size_t)chunk * 16) * 1024 + 16 * lane;
 #pragma unroll
     for (int t = 0; t < 16; ++t) T[t] = *reinterpret_cast<const u32x4*>(kbase + (size_t)t * 1024);
-    uint16_t zk[16], sk[8];
+    uint16_t zk[8], sk[8];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) zk[t] = kz[tok0 + 16 * t + ln];
+    for (int pp = 0; pp < 8; ++pp) {
+      zk[pp] = kz[tok0 + 16 * (2 * pp + hi) + ln];
+      sk[pp] = ks[tok0 + 16 * (2 * pp + hi) + ln];
+    }
+    // ---- the group's queries split into two int8 slices, in fp64 with the
+    // decisions of the decomposition kernel (per head: s_1 = fp32(max|q| /
+    // 127), A_1 = rint(q / s_1), r = q - s_1 A_1, s_2 = fp32(max|r| / 127),
+    // A_2 = rint(r / s_2)), while the cache loads are in flight.  Lane l takes
+    // head l / 8, dimensions 16 (l mod 8) .. + 15; the codes go to this wave's
+    // LDS rows (slice 1 of head g in row g, slice 2 in row 8 + g, operand
+    // order), from which the stacked A operands are read: row ln = slice
+    // ln / 8 of head ln mod 8.
+    __shared__ float qscale[kAttnWaves][2][8];
+    int8_t* my = &psl[w][0][0];
+    {
+      const int gq = lane / 8, p8 = lane % 8;
+      u32x4 xq[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+      if (gq < G) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(qh + (size_t)(qrow0 + gq) * kHeadDim + 16 * p8);
+        xq[0] = src[0];
+        xq[1] = src[1];
+      }
+      auto xval = [&](int e) {  // dimension 16 p8 + e
+        return (double)half_bits_to_float((uint16_t)(xq[e / 8][(e % 8) / 2] >> (16 * (e % 2))));
+      };
+      auto max8 = [](double v) {  // over the 8 lanes of a head
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) sk[pp] = ks[tok0 + 16 * (2 * pp + hi) + ln];
-    // ---- and its 16 value tiles (V^T: 8 tiles of 16 dimensions by 2 of 128
-    // positions) with their scales and zero points, all in flight at once:
-    // a wave computes one chunk, so nothing later would hide their latency
+        for (int off = 1; off < 8; off <<= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+        return v;
+      };
+      double amax = 0.0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax = fmax(amax, fabs(xval(e)));
+      amax = max8(amax);
+      const double s1 = (double)(float)(amax / 127.0);
+      const double inv1 = s1 != 0.0 ? 1.0 / s1 : 0.0;
+      double amax2 = 0.0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const double x = xval(e);
+        const double a = quant127_q(x, s1, inv1);
+        my[gq * kChunk + operand_byte(16 * p8 + e)] = (int8_t)(int)a;
+        amax2 = fmax(amax2, fabs(x - s1 * a));
+      }
+      amax2 = max8(amax2);
+      const double s2 = (double)(float)(amax2 / 127.0);
+      const double inv2 = s2 != 0.0 ? 1.0 / s2 : 0.0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const double x = xval(e);
+        const double r = x - s1 * quant127_q(x, s1, inv1);
+        my[(8 + gq) * kChunk + operand_byte(16 * p8 + e)] = (int8_t)(int)quant127_q(r, s2, inv2);
+      }
+      if (p8 == 0) {
+        qscale[w][0][gq] = (float)s1;
+        qscale[w][1][gq] = (float)s2;
+      }
+    }
+    // ---- the chunk's 16 value tiles (V^T: 8 tiles of 16 dimensions by 2 of
+    // 128 positions) with their scales and zero points, issued once the
+    // decomposition's registers are free; they fly during the scores and the
+    // softmax
     u32x4 V[16];
     const uint8_t* vbase = vtp + bh * (size_t)L * (kHeadDim / 2) + 16 * lane;
 #pragma unroll
@@ -456,21 +523,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
       zv16[pp] = vz[tok0 + 16 * (2 * pp + hi) + ln];
     }
 
-    // ---- stacked query operands: row ln = slice ln / 8 of head ln % 8
     u32x4 Aq[2];
-    {
-      const int j = ln / 8, g = ln % 8;
 #pragma unroll
-      for (int pu = 0; pu < 2; ++pu)
-        Aq[pu] = g < G ? *reinterpret_cast<const u32x4*>(qsl + ((size_t)j * MQ + qrow0 + g) * kHeadDim + 64 * pu + 16 * kb)
-                       : u32x4{0, 0, 0, 0};
-    }
+    for (int pu = 0; pu < 2; ++pu) Aq[pu] = *reinterpret_cast<const u32x4*>(my + ln * kChunk + 64 * pu + 16 * kb);
     float s1q[4], s2q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int g = 4 * hq + i;
-      s1q[i] = g < G ? qsc[qrow0 + g] : 0.f;
-      s2q[i] = g < G ? qsc[(size_t)MQ + qrow0 + g] : 0.f;
+      s1q[i] = qscale[w][0][4 * hq + i];
+      s2q[i] = qscale[w][1][4 * hq + i];
+    }
+    // the key zero point enters after the product: D_j = sum_d A_j q - zK
+    // sum_d A_j, with the row sums of the query slices from one product
+    // against ones (exact: every term is an integer below 2^24)
+    float sA1[4], sA2[4];
+    {
+      const u32x4 ones{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+      i32x4 S = mfma_i8_16x16x64(Aq[0], ones, i32x4{0, 0, 0, 0});
+      S = mfma_i8_16x16x64(Aq[1], ones, S);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int x = S[i], y = S[i];
+        swap_halves(x, y);
+        sA1[i] = (float)x;
+        sA2[i] = (float)y;
+      }
     }
 
     // ---- scores: tile pairs (2 p, 2 p + 1)
@@ -482,24 +558,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const u32x4& kt = T[2 * pp + hh];
-        const uint32_t zb = (uint32_t)half_bits_to_float(zk[2 * pp + hh]) * 0x01010101u;
-        auto qz = [&](uint32_t q) { return ((q | 0x80808080u) - zb) ^ 0x80808080u; };  // bytes q - z
         u32x4 Bk[2];
 #pragma unroll
         for (int pu = 0; pu < 2; ++pu) {
           const uint32_t w0 = kt[2 * pu], w1 = kt[2 * pu + 1];
-          Bk[pu] = u32x4{qz(w0 & 0x0F0F0F0Fu), qz((w0 >> 4) & 0x0F0F0F0Fu), qz(w1 & 0x0F0F0F0Fu),
-                         qz((w1 >> 4) & 0x0F0F0F0Fu)};
+          Bk[pu] = u32x4{w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
         }
         D[hh] = mfma_i8_16x16x64(Aq[0], Bk[0], i32x4{0, 0, 0, 0});
         D[hh] = mfma_i8_16x16x64(Aq[1], Bk[1], D[hh]);
       }
       const float skf = half_bits_to_float(sk[pp]) * inv_sqrt_d;
+      const float zkf = half_bits_to_float(zk[pp]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int x = D[0][i], y = D[1][i];
-        swap_halves(x, y);  // x: D_1, y: D_2 of token ln of tile 2 pp + hi, head 4 hq + i
-        sc[pp][i] = skf * fmaf(s1q[i], (float)x, s2q[i] * (float)y);
+        swap_halves(x, y);  // x: D_1, y: D_2 of token ln of tile 2 pp + hi, head 4 hq + i (before zK)
+        const float d1 = fmaf(-zkf, sA1[i], (float)x), d2 = fmaf(-zkf, sA2[i], (float)y);
+        sc[pp][i] = skf * fmaf(s1q[i], d1, s2q[i] * d2);
       }
     }
 
@@ -526,35 +601,33 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
       l[i] = row32<false>(l[i]);
       am[i] = row32<true>(am[i]);
     }
-    float r1[4], r2[4], zt1[4], zt2[4];
-    int8_t* my = &psl[w][0][0];
+    float r1[4], r2[4], zt1[4], zt2[4];  // the weight slices go to the same LDS rows (Aq is in registers)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       r1[i] = am[i] * (1.f / 127.f);
       const float inv1 = r1[i] > 0.f ? 1.f / r1[i] : 0.f;
-      float am2 = 0.f;
-      int z1 = 0;
+      float am2 = 0.f, z1 = 0.f;  // integer sums below 2^24: exact in fp32
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
         const float a = quant_i8(sc[pp][i], inv1);
         const int t = 16 * (2 * pp + hi) + ln;
         my[(4 * hq + i) * kChunk + operand_byte(t)] = (int8_t)(int)a;
-        z1 += (int)a * (int)half_bits_to_float(zv16[pp]);
+        z1 = fmaf(a, half_bits_to_float(zv16[pp]), z1);
         sc[pp][i] = sc[pp][i] - r1[i] * a;
         am2 = fmaxf(am2, fabsf(sc[pp][i]));
       }
       r2[i] = row32<true>(am2) * (1.f / 127.f);
       const float inv2 = r2[i] > 0.f ? 1.f / r2[i] : 0.f;
-      int z2 = 0;
+      float z2 = 0.f;
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
         const float a = quant_i8(sc[pp][i], inv2);
         const int t = 16 * (2 * pp + hi) + ln;
         my[(8 + 4 * hq + i) * kChunk + operand_byte(t)] = (int8_t)(int)a;
-        z2 += (int)a * (int)half_bits_to_float(zv16[pp]);
+        z2 = fmaf(a, half_bits_to_float(zv16[pp]), z2);
       }
-      zt1[i] = row32<false>((float)z1);  // |sum| <= 256 * 127 * 15 < 2^24: exact
-      zt2[i] = row32<false>((float)z2);
+      zt1[i] = row32<false>(z1);  // |sum| <= 256 * 127 * 15 < 2^24: exact
+      zt2[i] = row32<false>(z2);
     }
 
     // ---- values: E (rows 0-7 slice 1, 8-15 slice 2) per dim tile, pairs of
@@ -628,29 +701,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
 }
 
 // one workgroup of 128 threads per query row: o[n] = sum_s e^(m_s - m) o_s[n]
-// / sum_s e^(m_s - m) l_s over the splits, in order (every thread reads the
-// splits' maxima and sums; the outputs eight splits at a time)
+// / sum_s e^(m_s - m) l_s over the splits, in order.  Every thread loads the
+// splits' (max, sum) pairs and its outputs eight splits at a time, all of a
+// batch's loads issued before any is used (one memory round trip per eight
+// splits).
 __global__ __launch_bounds__(kHeadDim) void attn_combine_kernel(const float* __restrict__ part_o,
                                                                 const float* __restrict__ part_ml, int nsplit,
                                                                 uint16_t* __restrict__ out) {
   const size_t row = blockIdx.x;
   const int n = threadIdx.x;
-  const float* ml = part_ml + row * nsplit * 2;
-  float m = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) m = fmaxf(m, ml[2 * c]);
-  float num = 0.f, den = 0.f;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + row * nsplit;
   const float* po = part_o + row * nsplit * kHeadDim + n;
+  float m = -INFINITY, num = 0.f, den = 0.f;
   for (int c0 = 0; c0 < nsplit; c0 += 8) {
-    float v[8];
+    float2 v[8];
+    float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = c0 + i < nsplit ? po[(size_t)(c0 + i) * kHeadDim] : 0.f;
+    for (int i = 0; i < 8; ++i) {
+      v[i] = c0 + i < nsplit ? ml[c0 + i] : make_float2(-INFINITY, 0.f);
+      o[i] = c0 + i < nsplit ? po[(size_t)(c0 + i) * kHeadDim] : 0.f;
+    }
+    float mb = m;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (c0 + i < nsplit) {
-        const float f = expf(ml[2 * (c0 + i)] - m);
-        num = fmaf(f, v[i], num);
-        den = fmaf(f, ml[2 * (c0 + i) + 1], den);
-      }
+    for (int i = 0; i < 8; ++i) mb = fmaxf(mb, v[i].x);
+    const float f0 = m == -INFINITY ? 0.f : expf(m - mb);  // rescale what came before
+    num *= f0;
+    den *= f0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float f = v[i].x == -INFINITY ? 0.f : expf(v[i].x - mb);
+      num = fmaf(f, o[i], num);
+      den = fmaf(f, v[i].y, den);
+    }
+    m = mb;
   }
   out[row * kHeadDim + n] = float_to_half_bits(num / den);
 }
@@ -703,15 +786,15 @@ int launch_attn_msd(const uint16_t* q, int B, int Hq, int Hkv, int L, const uint
   float* po = reinterpret_cast<float*>(base);
   base += ((size_t)MQ * nchunk * kHeadDim * sizeof(float) + 255) / 256 * 256;
   float* pm = reinterpret_cast<float*>(base);
-  int st = launch_decompose(q, MQ, kHeadDim, 2, false, qsl, nullptr, qsc, s);
-  if (st != 0) return st;
-  int nsplit;
+  int nsplit, st;
   if (Hq / Hkv <= 8 && attn_wave_kernel_enabled()) {
     nsplit = (nchunk + kAttnWaves - 1) / kAttnWaves;
-    hipLaunchKernelGGL(attn_msd_wave_kernel, dim3(nsplit, Hkv, B), dim3(kAttnThreads), 0, s, qsl, qsc, MQ, Hq, Hkv, L,
-                       kp, ks, kz, vtp, vs, vz, po, pm);
+    hipLaunchKernelGGL(attn_msd_wave_kernel, dim3(nsplit, Hkv, B), dim3(kAttnThreads), 0, s, q, MQ, Hq, Hkv, L, kp,
+                       ks, kz, vtp, vs, vz, po, pm);
     st = check_launch("attn_msd_wave");
   } else {
+    st = launch_decompose(q, MQ, kHeadDim, 2, false, qsl, nullptr, qsc, s);
+    if (st != 0) return st;
     const int cpw = attn_chunks_per_split(B, Hkv, L);
     nsplit = nchunk / cpw;
     hipLaunchKernelGGL(attn_msd_chunk_kernel, dim3(nsplit, Hkv, B), dim3(kAttnThreads), 0, s, qsl, qsc, MQ, Hq, Hkv,
