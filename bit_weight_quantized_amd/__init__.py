@@ -190,7 +190,7 @@ def gemv_noalloc(x, packed, scale, zero, G: int, fmt: int, *, out=None, stream=N
 
 GEMV_PLAN_FIELDS = ("kernel", "cols", "token_tiles", "row_waves", "k_waves", "k_slices", "staged_units",
                     "workgroups", "threads", "lds_bytes", "lds_budget", "static_lds", "workspace_bytes", "ok",
-                    "ring")
+                    "ring", "act_lds")
 
 
 def gemv_plan(M: int, K: int, N: int, G: int, fmt: int) -> dict:

@@ -212,7 +212,8 @@ int w4_gemv_plan(int M, int K, int N, int G, int fmt, int64_t* out, int n_out) {
                                           (int64_t)gemv_static_lds(fmt),
                                           (int64_t)c.ws_bytes,
                                           check_gemv_plan(c, fmt) == 0 ? 1 : 0,
-                                          c.ring};
+                                          c.ring,
+                                          c.kind == 1 ? c.xl : 0};
   for (int i = 0; i < n_out && i < W4_GEMV_PLAN_FIELDS; ++i) out[i] = v[i];
   g_last_error[0] = '\0';
   return W4_OK;

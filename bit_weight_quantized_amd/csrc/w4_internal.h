@@ -47,7 +47,7 @@ int launch_pack(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t
 // ring: weight tiles (staged) or operand slots (direct) in flight per wave.
 // vs: the staged kernel fetches its workgroup's scale block with 16-byte loads.
 struct GemvPlan {
-  int kind, cols, mt, nwr, nwk, s, xu, row_blocks, sc_pitch, x_bytes, ring, vs;
+  int kind, cols, mt, nwr, nwk, s, xu, row_blocks, sc_pitch, x_bytes, ring, vs, xl, xl_off;
   size_t lds_bytes, ws_bytes;
 };
 GemvPlan plan_gemv(int M, int K, int N, int G, int fmt);

@@ -169,10 +169,12 @@ int w4_gemv_noalloc(const uint16_t* x, int M, int K, int N,
  *   13 1 when the plan meets the kernels' bounds (threads <= 512, dynamic
  *      LDS within budget), else 0 -- w4_gemv refuses such a plan,
  *   14 weight tiles (staged kernel) or operand slots (direct kernel) each
- *      wave keeps in flight.
+ *      wave keeps in flight,
+ *   15 1 when the direct kernel loads the activations whole rows at a time
+ *      and reorders them through LDS, else 0.
  * Shape rules and errors as for w4_gemv; nothing touches a device.
  */
-#define W4_GEMV_PLAN_FIELDS 15
+#define W4_GEMV_PLAN_FIELDS 16
 int w4_gemv_plan(int M, int K, int N, int G, int fmt, int64_t* out, int n_out);
 
 /*

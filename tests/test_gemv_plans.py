@@ -15,7 +15,7 @@ import bit_weight_quantized_amd as w4
 LDS_PER_CU = 160 * 1024
 MAX_THREADS = 512
 FMTS = [(0, 128), (0, 64), (1, 64), (1, 128)]
-OVERRIDES = ("W4_GEMV_KIND", "W4_GEMV_NWR", "W4_GEMV_NWK", "W4_GEMV_C", "W4_GEMV_S", "W4_GEMV_RING")
+OVERRIDES = ("W4_GEMV_KIND", "W4_GEMV_NWR", "W4_GEMV_NWK", "W4_GEMV_C", "W4_GEMV_S", "W4_GEMV_RING", "W4_GEMV_XL")
 
 
 @pytest.fixture(autouse=True)
@@ -45,8 +45,11 @@ def check(p, M, K, N):
         assert p["ring"] == (4 if M <= 16 else 2), where
         assert p["row_waves"] == 1 and p["cols"] in (1, 2, 4), where
         assert p["workgroups"] == -(-(N // 16) // p["cols"]), where
+        assert p["act_lds"] in (0, 1), where
+        if p["act_lds"]:  # the per-wave activation areas fit after the scale block or reduction area
+            assert p["lds_bytes"] >= p["k_waves"] * p["token_tiles"] * 4096, where
     else:
-        assert p["kernel"] == 0 and p["cols"] == 1, where
+        assert p["kernel"] == 0 and p["cols"] == 1 and p["act_lds"] == 0, where
         assert p["ring"] in ((4, 8, 16) if M <= 16 else (4,)), where
         assert p["workgroups"] == -(-N // (16 * p["row_waves"])), where
 
@@ -92,6 +95,7 @@ def test_forced_plans_fit_the_kernels(monkeypatch, kind):
         combos = itertools.product((0,), waves, (0, 1, 2, 3, 4, 8), slices)
     for n, (nwr, nwk, c, s) in enumerate(combos):
         monkeypatch.setenv("W4_GEMV_RING", str((0, 4, 8, 16, 5)[n % 5]))
+        monkeypatch.setenv("W4_GEMV_XL", str(n % 2))
         monkeypatch.setenv("W4_GEMV_NWR", str(nwr))
         monkeypatch.setenv("W4_GEMV_NWK", str(nwk))
         monkeypatch.setenv("W4_GEMV_C", str(c))

@@ -77,6 +77,39 @@ def test_gemv_launch_variants_agree(monkeypatch, nwr, nwk, s):
             assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
 
 
+@pytest.mark.parametrize("M", [5, 8, 16, 17, 32])
+@pytest.mark.parametrize("cols,nwk,K", [(2, 8, 1536), (4, 8, 8192), (1, 4, 8192), (2, 2, 1536)])
+def test_direct_activation_paths_agree(monkeypatch, M, cols, nwk, K):
+    """The direct kernel's two activation paths (operand-order loads, and
+    whole rows reordered through LDS): within tolerance of the oracle and
+    bit-identical to each other (same products, same order), for one and two
+    token tiles, ragged M, runs shorter and longer than the operand ring."""
+    require_gpu()
+    monkeypatch.setenv("W4_GEMV_KIND", "1")
+    monkeypatch.setenv("W4_GEMV_C", str(cols))
+    monkeypatch.setenv("W4_GEMV_NWK", str(nwk))
+    N = 208
+    w = wl.make_weight(10, 1, N, K)
+    x = wl.make_activations(10, 1, M, K)
+    xd = dev(x)
+    for fmt, G in FMTS[:3]:
+        codes, scale, zero = oracle_weights(fmt, w, G)
+        packed, sc, zc = upload_weights(codes, scale, zero)
+        ws_n = w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)
+        ws = torch.full((max(ws_n, 16),), 0xFF, dtype=torch.uint8, device="cuda")  # fp32 NaNs
+        ys = {}
+        for xl in ("0", "1"):
+            monkeypatch.setenv("W4_GEMV_XL", xl)
+            plan = w4.gemv_plan(M, K, N, G, fmt)
+            assert plan["kernel"] == 1 and plan["act_lds"] == int(xl), plan
+            announce("gemv direct activations", dict(xl=xl, cols=cols, nwk=nwk, K=K, fmt=fmt, G=G, M=M))
+            ys[xl] = host(w4.gemv(xd, packed, sc, zc, G, fmt, workspace=ws))
+        y_ref = o.matmul_ref(x, o.dequant(fmt, codes, scale, zero, G))
+        assert row_rel_l2(ys["1"], y_ref) <= TOL_ROW_REL_L2, (fmt, G, M)
+        assert_elementwise(ys["1"], y_ref)
+        assert np.array_equal(ys["0"].view(np.uint16), ys["1"].view(np.uint16)), (fmt, G, M)
+
+
 @pytest.mark.parametrize("ring", [8, 16])
 @pytest.mark.parametrize("nwr,nwk,s,K", [(1, 4, 1, 1536), (2, 4, 1, 1536), (1, 1, 1, 1536), (1, 8, 2, 1536),
                                          (2, 4, 1, 8192), (1, 4, 1, 8192), (1, 2, 1, 8192)])
