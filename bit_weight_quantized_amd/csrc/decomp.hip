@@ -6,8 +6,10 @@
 // Per token m, in fp64 with r = x: s_j = fp32(max_k |r| / 127);
 // A_j = clamp(rint(r / s_j), -127, 127); r <- r - s_j * A_j (the product and
 // the difference are exact for up to three slices, so contraction cannot
-// change the result).  All decisions are IEEE fp64 operations, bit-identical
-// to any other correct fp64 evaluation.
+// change the result).  The residuals and maxima are exact fp64 values; each
+// rint is decided from an fp32 estimate, with an exact fp64 sign test where
+// the estimate is near a half-integer (decide127), which gives the same
+// integers as the fp64 division.
 //
 // The slices are written in the byte order the int8 matrix-core product reads
 // them in (the operand layout below); the plain [slice][token][K] layout is
@@ -45,19 +47,35 @@ __device__ __forceinline__ double block_max(double v, double* red) {
   return r;
 }
 
-// clamp(rint(fl64(n / s)), -127, 127) without a division per element.  inv is
-// 1 / s correctly rounded; every quotient here has |n / s| < 2^8 (n is a
-// residual bounded by the row maximum, or 254 times a first residual).  Then
-// t = fl64(n * inv) and the correctly rounded quotient are both within 2^-44
-// of n / s, so they round to the same integer unless n / s lies within 2^-44
-// of a half-integer; a quotient t within 2^-30 of one takes the division
-// itself.  The result is the division's decision in every case.
-__device__ __forceinline__ double quant127_inv(double n, double s, double inv) {
-  if (s == 0.0) return 0.0;
-  const double t = n * inv;
-  double q = rint(t);
-  if (fabs(fabs(t - q) - 0.5) < 0x1p-30) q = rint(n / s);
-  return fmin(fmax(q, -127.0), 127.0);
+// clamp(rint(fl64(n / s)), -127, 127) for an exactly known fp64 numerator n
+// (x itself, a residual, or 254 times one) and a scale s that is an fp32
+// value, decided in fp32.  inv = fl32(1 / s) (the quotient in fp64, so its
+// relative error is at most 2^-24 + 2^-53); with nf = fl32(n) the estimate
+// t = fl32(nf * inv) is within 3 * 2^-24 * 127.0001 < 2^-15.4 of n / s, since
+// every quotient here has |n / s| <= 127.0001.  Where t is at least 2^-14 from
+// every half-integer, rint(t) is the decision.  Nearer (about 1 in 8000), the
+// sign of n - h s (h the half-integer next to rint(t) on t's side, the only
+// one that can lie between t and the quotient), from one fp64 fma of exact
+// operands rounded once, says which side the quotient lies on (on h: to
+// even).  That decides rint of the exact quotient; rint(fl64(n / s)) is the
+// same integer because no quotient here comes within 2^-25 of a half-integer
+// without being one (n - h s is a multiple of the finer of the grids of n and
+// s / 2, and that grid is at least 2^-25 s wherever the quotient is near a
+// half-integer of magnitude 1/2 or more), while fl64 moves a quotient by at
+// most 2^-46.  rint is the fp32 addition of 1.5 * 2^23 (ties to even).
+constexpr float kRintMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kNearHalf = 0x1p-14f;
+
+__device__ __forceinline__ float decide127(double n, double s, float inv) {
+#pragma clang fp contract(off)
+  const float t = (float)n * inv;
+  float q = (t + kRintMagic) - kRintMagic;
+  if (fabsf(fabsf(t - q) - 0.5f) < kNearHalf) {
+    const float sg = t >= q ? 1.f : -1.f;
+    const double d = fma(-(double)(q + 0.5f * sg), s, n);
+    if (d * (double)sg > 0.0 || (d == 0.0 && ((int)q & 1) != 0)) q += sg;
+  }
+  return fminf(fmaxf(q, -127.f), 127.f);
 }
 
 __device__ __forceinline__ int code_byte(const uint32_t (&w)[2], int i) {
@@ -149,9 +167,10 @@ __global__ __launch_bounds__(T) void decompose_kernel(
     for (int i = 0; i < 8; ++i) amax = fmax(amax, fabs(v[i]));
   });
   amax = row_max(amax);
-  double s[NS], inv[NS];
+  double s[NS];
+  float inv[NS];
   s[0] = (double)(float)(amax / 127.0);
-  inv[0] = s[0] != 0.0 ? 1.0 / s[0] : 0.0;
+  inv[0] = s[0] != 0.0 ? (float)(1.0 / s[0]) : 0.f;
   // the earlier slices' codes of the cached chunks (plain order), so a pass
   // rebuilds its residual without deciding those codes again
   uint32_t codes[NS > 1 ? NS - 1 : 1][CH > 0 ? CH : 1][2];
@@ -167,17 +186,17 @@ __global__ __launch_bounds__(T) void decompose_kernel(
       for (int i = 0; i < 8; ++i) {
         double r = v[i];
 #pragma unroll
-        for (int jj = 0; jj < j; ++jj) {  // earlier slices' residual
-          const double qq = CH > 0 ? (double)code_byte(codes[jj][c], i) : quant127_inv(r, s[jj], inv[jj]);
+        for (int jj = 0; jj < j; ++jj) {  // earlier slices' residual (exact in fp64)
+          const double qq = CH > 0 ? (double)code_byte(codes[jj][c], i) : (double)decide127(r, s[jj], inv[jj]);
           r = r - s[jj] * qq;
         }
-        double q;
+        float q;
         if (FIXED && j == 1)
-          q = quant127_inv(kFixedRatio * r, s[0], inv[0]);
+          q = decide127(kFixedRatio * r, s[0], inv[0]);
         else
-          q = quant127_inv(r, s[j], inv[j]);
+          q = decide127(r, s[j], inv[j]);
         a[i] = (int)q;
-        if (!FIXED && j + 1 < NS) amax_next = fmax(amax_next, fabs(r - s[j] * q));
+        if (!FIXED && j + 1 < NS) amax_next = fmax(amax_next, fabs(r - s[j] * (double)q));
       }
       store8(j, k, a);
       if constexpr (CH > 0) {
@@ -193,7 +212,7 @@ __global__ __launch_bounds__(T) void decompose_kernel(
       if (rt == 0) tok_scale[(size_t)j * M + m] = (float)s[j];
       if (!FIXED && j + 1 < NS) {
         s[j + 1] = (double)(float)(row_max(amax_next) / 127.0);
-        inv[j + 1] = s[j + 1] != 0.0 ? 1.0 / s[j + 1] : 0.0;
+        inv[j + 1] = s[j + 1] != 0.0 ? (float)(1.0 / s[j + 1]) : 0.f;
       }
     }
   }
