@@ -403,7 +403,8 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
         for name, call, count in (
                 ("select_us", lambda: w4.salient_select(x, k, out=idx), reps),
                 ("correct_host_us", lambda: w4.residual_correct(x, r_host, idx, y), reps),
-                ("correct_device_us", lambda: w4.residual_correct(x, r_dev, idx, y), reps)):
+                ("correct_device_us", lambda: w4.residual_correct(x, r_dev, idx, y), reps),
+                ("select_correct_host_us", lambda: w4.salient_correct(x, r_host, k, y, idx=idx), reps)):
             g = graph_of(torch, stream, [call] * count)
             time_replays(torch, stream, g, 1)
             timed[name] = round(time_replays(torch, stream, g, 4) * 1e3 / (4 * count), 2)
@@ -413,6 +414,10 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
             gemv_launch(i)
             w4.salient_select(x, k, out=idx)
             w4.residual_correct(x, r_host, idx, y)
+
+        def fused(i):  # selection and correction in one launch
+            gemv_launch(i)
+            w4.salient_correct(x, r_host, k, y, idx=idx)
 
         # the selection depends only on x: it runs on a second stream (same
         # priority) beside the GEMV, and the correction waits for both
@@ -434,11 +439,17 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
         time_replays(torch, stream, g, 1)
         forked_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
         del g
-        step_us = min(serial_us, forked_us)
+        g = graph_of(torch, stream, [lambda i=i: fused(i) for i in range(n_sets)])
+        time_replays(torch, stream, g, 1)
+        fused_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
+        del g
+        steps = {"serial": serial_us, "forked": forked_us, "fused": fused_us}
+        schedule = min(steps, key=steps.get)
+        step_us = steps[schedule]
         link = k * N * 2 / (timed["correct_host_us"] * 1e-6) / 1e9
         res.append({"k": k, **timed, "gemv_us": round(gemv_us, 2), "step_serial_us": round(serial_us, 2),
-                    "step_forked_us": round(forked_us, 2), "step_us": round(step_us, 2),
-                    "schedule": "serial" if serial_us <= forked_us else "forked",
+                    "step_forked_us": round(forked_us, 2), "step_fused_us": round(fused_us, 2),
+                    "step_us": round(step_us, 2), "schedule": schedule,
                     "overhead_frac": round((step_us - gemv_us) / gemv_us, 3),
                     "residual_bytes": k * N * 2, "host_link_GBps": round(link, 2),
                     "host_link_frac": round(link / HOST_LINK_PEAK_GBS, 3)})
@@ -446,7 +457,8 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
             "residual": "fp16 [K][N] in pinned host memory, read by the kernel over the host link",
             "step": "step_serial_us: GEMV, selection and correction one after the other on one stream; "
                     "step_forked_us: the selection on a second stream beside the GEMV, the correction after "
-                    "both; step_us: the faster of the two (schedule names it)",
+                    "both; step_fused_us: GEMV, then selection and correction in one launch "
+                    "(w4_salient_correct); step_us: the fastest (schedule names it)",
             "host_link_peak_GBps": HOST_LINK_PEAK_GBS, "per_k": res}
 
 

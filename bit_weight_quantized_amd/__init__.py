@@ -21,7 +21,7 @@ __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
     "lib", "lib_path", "quantize", "pack", "gemv", "gemv_noalloc", "gemv_plan", "gemm", "gemm_decomp", "gemm_decomp_fixed",
     "gemm_decomp_fixed_fused", "stream_read",
-    "salient_select", "residual_correct", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
+    "salient_select", "residual_correct", "salient_correct", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
     "workspace_bytes", "nf4_levels", "version",
 ]
 
@@ -76,6 +76,7 @@ def lib():
         L.w4_gemm_mx.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _sz, _p]
         L.w4_attn_decode_msd.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_residual_correct.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p]
+        L.w4_salient_correct.argtypes = [_p, _i, _i, _i, _p, _i, _p, _p, _p]
         L.w4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
         L.w4_workspace_bytes.restype = _sz
         L.w4_nf4_levels.argtypes = [_p]
@@ -315,6 +316,23 @@ def residual_correct(x, resid, idx, y, *, stream=None):
     _check("w4_residual_correct", lib().w4_residual_correct(_ptr(x), M, K, N, _ptr(resid), _ptr(idx), k, _ptr(y),
                                                             _stream(stream)))
     return y
+
+
+def salient_correct(x, resid, k, y, *, idx=None, stream=None):
+    """salient_select then residual_correct in one launch: y += x[:, idx] .
+    resid[idx, :] for the k salient channels; returns idx (int32 [k])."""
+    _dev(x, torch.float16, "x")
+    _dev(y, torch.float16, "y")
+    if resid.dtype != torch.float16 or resid.dim() != 2 or not resid.is_contiguous():
+        raise ValueError("resid must be a contiguous fp16 [K][N] tensor")
+    if resid.device.type == "cpu" and not resid.is_pinned():
+        raise ValueError("a host-resident resid must be pinned (pin_memory=True)")
+    M, K = x.shape
+    N = y.shape[1]
+    idx = torch.empty((k,), dtype=torch.int32, device=x.device) if idx is None else idx
+    _check("w4_salient_correct", lib().w4_salient_correct(_ptr(x), M, K, N, _ptr(resid), k, _ptr(idx), _ptr(y),
+                                                          _stream(stream)))
+    return idx
 
 
 def quantize_mx(wt, *, codes=None, scale=None, stream=None):

@@ -32,16 +32,27 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint16_t* __restrict__ x, int M, int K,
-                                                                     int k, int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t keys[];  // [K]
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t top[kSelMaxTop];
-  __shared__ uint32_t s_prefix, s_remaining, s_count, s_done;
+// LDS of one selection: keys[K] (caller-sized), hist[256], top[kSelMaxTop]
+// and four scalars; idx (LDS or device memory) receives the k channels.
+struct SelLds {
+  uint32_t hist[256];
+  uint32_t top[kSelMaxTop];
+  uint32_t prefix, remaining, count, done;
+};
+
+template <int NT>
+__device__ void select_salient(const uint16_t* __restrict__ x, int M, int K, int k, uint32_t* keys, SelLds& sl,
+                               int32_t* idx) {
+  uint32_t* hist = sl.hist;
+  uint32_t* top = sl.top;
+  uint32_t& s_prefix = sl.prefix;
+  uint32_t& s_remaining = sl.remaining;
+  uint32_t& s_count = sl.count;
+  uint32_t& s_done = sl.done;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
 
-  for (int c = tid; c < K; c += kSelThreads) {
+  for (int c = tid; c < K; c += NT) {
     uint32_t s = 0;
     for (int m = 0; m < M; ++m) s = max(s, (uint32_t)(x[(size_t)m * K + c] & 0x7FFFu));
     keys[c] = (s << kIdxBits) | (uint32_t)((1 << kIdxBits) - 1 - c);
@@ -59,7 +70,7 @@ __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint1
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix;
-    for (int c = tid; c < K; c += kSelThreads) {
+    for (int c = tid; c < K; c += NT) {
       const uint32_t key = keys[c];
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint1
 
   // gather the k keys whose masked prefix is at least the final prefix
   const uint32_t T = s_prefix;
-  for (int c0 = 0; c0 < K; c0 += kSelThreads) {  // wave-uniform trip count
+  for (int c0 = 0; c0 < K; c0 += NT) {  // wave-uniform trip count
     const int c = c0 + tid;
     const uint32_t key = c < K ? keys[c] : 0u;
     const bool sel = c < K && (key & mask) >= T;
@@ -110,12 +121,19 @@ __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint1
   }
   __syncthreads();
   // rank of each gathered key = number of larger ones (keys are distinct)
-  for (int i = tid; i < k; i += kSelThreads) {
+  for (int i = tid; i < k; i += NT) {
     const uint32_t key = top[i];
     int r = 0;
     for (int j = 0; j < k; ++j) r += top[j] > key ? 1 : 0;
     idx[r] = (1 << kIdxBits) - 1 - (int)(key & ((1u << kIdxBits) - 1));
   }
+}
+
+__global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                                     int k, int32_t* __restrict__ idx) {
+  extern __shared__ uint32_t keys[];  // [K]
+  __shared__ SelLds sl;
+  select_salient<kSelThreads>(x, M, K, k, keys, sl, idx);
 }
 
 // ---------------------------------------------------------------------------
@@ -129,10 +147,9 @@ constexpr int kCorrWaves = 8;
 constexpr int kCorrBatch = 4;
 
 template <int CPT, int MMAX>
-__global__ __launch_bounds__(kCorrWaves * kWave) void residual_correct_kernel(
-    const uint16_t* __restrict__ x, int M, int K, int N, const uint16_t* __restrict__ resid,
-    const int32_t* __restrict__ idx, int k, uint16_t* __restrict__ y) {
-  extern __shared__ float part[];  // [kCorrWaves][MMAX][64 * CPT]
+__device__ void correct_columns(const uint16_t* __restrict__ x, int M, int K, int N, const uint16_t* __restrict__ resid,
+                                const int32_t* idx, int k, uint16_t* __restrict__ y, float* part) {
+  // part: LDS [kCorrWaves][MMAX][64 * CPT]
   constexpr int kCols = 64 * CPT;
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -197,6 +214,32 @@ __global__ __launch_bounds__(kCorrWaves * kWave) void residual_correct_kernel(
 }
 
 template <int CPT, int MMAX>
+__global__ __launch_bounds__(kCorrWaves * kWave) void residual_correct_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int N, const uint16_t* __restrict__ resid,
+    const int32_t* __restrict__ idx, int k, uint16_t* __restrict__ y) {
+  extern __shared__ float part[];  // [kCorrWaves][MMAX][64 * CPT]
+  correct_columns<CPT, MMAX>(x, M, K, N, resid, idx, k, y, part);
+}
+
+// Selection and correction in one launch: every workgroup picks the channels
+// itself (the same ones: the selection is deterministic) into LDS, workgroup 0
+// also writes them to idx, and each then corrects its columns.  The dynamic
+// LDS holds the selection keys first and the correction's partial sums after.
+template <int CPT, int MMAX>
+__global__ __launch_bounds__(kCorrWaves * kWave) void salient_correct_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int N, const uint16_t* __restrict__ resid, int k,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ y) {
+  extern __shared__ uint32_t dyn[];  // keys[K], then part[kCorrWaves][MMAX][64 * CPT]
+  __shared__ SelLds sl;
+  __shared__ int32_t picked[kSelMaxTop];
+  select_salient<kCorrWaves * kWave>(x, M, K, k, dyn, sl, picked);
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < k; i += kCorrWaves * kWave) idx[i] = picked[i];
+  correct_columns<CPT, MMAX>(x, M, K, N, resid, picked, k, y, reinterpret_cast<float*>(dyn));
+}
+
+template <int CPT, int MMAX>
 int launch_correct_t(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx, int k,
                      uint16_t* y, hipStream_t s) {
   const int lds = kCorrWaves * MMAX * 64 * CPT * (int)sizeof(float);
@@ -224,6 +267,25 @@ int launch_residual_correct(const uint16_t* x, int M, int K, int N, const uint16
                             int k, uint16_t* y, hipStream_t s) {
   if (M <= 8) return launch_correct_t<8, 8>(x, M, K, N, resid, idx, k, y, s);
   return launch_correct_t<2, 32>(x, M, K, N, resid, idx, k, y, s);
+}
+
+template <int CPT, int MMAX>
+int launch_salient_correct_t(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
+                             uint16_t* y, hipStream_t s) {
+  const int lds = std::max(K * (int)sizeof(uint32_t), kCorrWaves * MMAX * 64 * CPT * (int)sizeof(float));
+  const void* fn = reinterpret_cast<const void*>(&salient_correct_kernel<CPT, MMAX>);
+  const int st = allow_dynamic_lds(fn, lds, "w4_salient_correct");
+  if (st != 0) return st;
+  const int blocks = (N + 64 * CPT - 1) / (64 * CPT);
+  hipLaunchKernelGGL((salient_correct_kernel<CPT, MMAX>), dim3(blocks), dim3(kCorrWaves * kWave), lds, s, x, M, K, N,
+                     resid, k, idx, y);
+  return check_launch("salient_correct");
+}
+
+int launch_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
+                           uint16_t* y, hipStream_t s) {
+  if (M <= 8) return launch_salient_correct_t<8, 8>(x, M, K, N, resid, k, idx, y, s);
+  return launch_salient_correct_t<2, 32>(x, M, K, N, resid, k, idx, y, s);
 }
 
 }  // namespace w4

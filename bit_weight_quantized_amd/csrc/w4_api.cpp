@@ -273,6 +273,23 @@ int w4_gemm_decomp_fixed_fused(const uint16_t* x, int M, int K, int N, const uin
                                   (hipStream_t)stream);
 }
 
+// The device address of a residual in pinned host memory (read over the host
+// link) or in device memory; null for anything else (pageable memory).
+static const void* residual_device_address(const uint16_t* resid) {
+  hipPointerAttribute_t attr;
+  const void* dev = nullptr;
+  if (hipPointerGetAttributes(&attr, resid) == hipSuccess) {
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+      dev = resid;
+    } else if (attr.type == hipMemoryTypeHost) {
+      void* d = nullptr;
+      if (hipHostGetDevicePointer(&d, const_cast<uint16_t*>(resid), 0) == hipSuccess) dev = d;
+    }
+  }
+  if (!dev) (void)hipGetLastError();  // clear the query's error
+  return dev;
+}
+
 int w4_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, void* stream) {
   g_last_error[0] = '\0';
   if (M < 1 || K < 1 || K > kSelMaxK)
@@ -297,24 +314,31 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
   if (!aligned16(resid) || !aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
       (reinterpret_cast<uintptr_t>(idx) & 3u))
     return fail(W4_EINVAL, "w4_residual_correct: resid and y must be 16-byte aligned, x 2-byte, idx 4-byte");
-  // The residual lives in pinned host memory (the device reads it over the
-  // host link) or, for comparison, in device memory.
-  hipPointerAttribute_t attr;
-  const void* dev = nullptr;
-  if (hipPointerGetAttributes(&attr, resid) == hipSuccess) {
-    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
-      dev = resid;
-    } else if (attr.type == hipMemoryTypeHost) {
-      void* d = nullptr;
-      if (hipHostGetDevicePointer(&d, const_cast<uint16_t*>(resid), 0) == hipSuccess) dev = d;
-    }
-  }
-  if (!dev) {
-    (void)hipGetLastError();  // clear the query's error
+  const void* dev = residual_device_address(resid);
+  if (!dev)
     return fail(W4_EINVAL, "w4_residual_correct: resid must be pinned host memory (hipHostMalloc) or device memory");
-  }
   if (k == 0) return W4_OK;
   return launch_residual_correct(x, M, K, N, static_cast<const uint16_t*>(dev), idx, k, y, (hipStream_t)stream);
+}
+
+int w4_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
+                       uint16_t* y, void* stream) {
+  g_last_error[0] = '\0';
+  if (M < 1 || M > 32 || K < 1 || K > kSelMaxK || N < 1 || N % 8)
+    return fail(W4_EINVAL,
+                "w4_salient_correct: need 1 <= M <= 32, 1 <= K <= %d, N >= 1 with N %% 8 == 0 (got M=%d K=%d N=%d)",
+                kSelMaxK, M, K, N);
+  if (k < 0 || k > K || k > kSelMaxTop)
+    return fail(W4_EINVAL, "w4_salient_correct: k must be in [0, min(K, %d)] (got %d)", kSelMaxTop, k);
+  if (!x || !y || !resid || (k > 0 && !idx)) return fail(W4_EINVAL, "w4_salient_correct: null operand");
+  if (!aligned16(resid) || !aligned16(y) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
+      (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return fail(W4_EINVAL, "w4_salient_correct: resid and y must be 16-byte aligned, x 2-byte, idx 4-byte");
+  const void* dev = residual_device_address(resid);
+  if (!dev)
+    return fail(W4_EINVAL, "w4_salient_correct: resid must be pinned host memory (hipHostMalloc) or device memory");
+  if (k == 0) return W4_OK;
+  return launch_salient_correct(x, M, K, N, static_cast<const uint16_t*>(dev), k, idx, y, (hipStream_t)stream);
 }
 
 int w4_quantize_mx(const float* wt, int K, int N, uint8_t* codes, uint8_t* scale, void* stream) {

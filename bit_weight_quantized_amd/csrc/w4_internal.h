@@ -129,6 +129,8 @@ constexpr int kSelMaxTop = 1024;
 int launch_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, hipStream_t s);
 int launch_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
                             int k, uint16_t* y, hipStream_t s);
+int launch_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
+                           uint16_t* y, hipStream_t s);
 
 // MXFP4 weights (codes one per byte, E8M0 scales [N][K/32]), their packing
 // into 1 KB tiles, and the MXFP4 product with the activations split into

@@ -397,6 +397,22 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
                         const int32_t* idx, int k, uint16_t* y, void* stream);
 
 /*
+ * w4_salient_correct -- w4_salient_select followed by w4_residual_correct in
+ * one launch ([DecDEC] Abstract: salient channels chosen anew at every step,
+ * their residual rows fetched from host memory).  The picks and y are
+ * exactly those of the two calls; idx receives the picks as
+ * w4_salient_select writes them.
+ *
+ * x: fp16 [M][K] device, 1 <= M <= 32, 1 <= K <= 32768.  resid, y: as for
+ * w4_residual_correct (N % 8 == 0).  idx: int32 [k] device, written.
+ * Requires 0 <= k <= min(K, 1024); k = 0 enqueues nothing.  Every workgroup
+ * of the launch makes the (deterministic) selection itself, so the call
+ * needs no workspace.
+ */
+int w4_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k,
+                       int32_t* idx, uint16_t* y, void* stream);
+
+/*
  * w4_workspace_bytes -- bytes of workspace an entry point needs for the given
  * shape.  `fmt_or_mode`: the w4_fmt for W4_OP_GEMV, the w4_mode for
  * W4_OP_GEMM, nslices for W4_OP_GEMM_DECOMP and W4_OP_GEMM_MX.  Host-only;

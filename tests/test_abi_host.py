@@ -179,6 +179,21 @@ def test_residual_argument_errors(L):
     assert corr(idx=None) == W4_EINVAL
     assert corr(r=MISALIGNED) == W4_EINVAL
     assert b"w4_residual_correct" in L.w4_last_error()
+    # selection and correction in one launch: both sets of bounds
+
+    def sc(**kw):
+        a = {**args, **kw}
+        return L.w4_salient_correct(a["x"], a["M"], a["K"], a["N"], a["r"], a["k"], a["idx"], a["y"], None)
+    assert sc(M=33) == W4_EINVAL
+    assert sc(K=32769) == W4_EINVAL
+    assert sc(N=12) == W4_EINVAL
+    assert sc(k=65) == W4_EINVAL  # k > K
+    assert sc(K=4096, k=1025) == W4_EINVAL
+    assert sc(k=-1) == W4_EINVAL
+    assert sc(r=None) == W4_EINVAL
+    assert sc(idx=None) == W4_EINVAL
+    assert sc(y=MISALIGNED) == W4_EINVAL
+    assert b"w4_salient_correct" in L.w4_last_error()
 
 
 def test_mx_argument_errors(L):

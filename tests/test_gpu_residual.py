@@ -55,6 +55,12 @@ def test_salient_select_ties_and_zeros():
     for k in (1, 7, 513, 1024):
         got = host(w4.salient_select(dev(x), k))
         assert np.array_equal(got, o.salient_channels(x, k)), k
+    # one score shared by every channel of the widest row: the ties fill
+    # all 32 channel chunks and the picks are the lowest channels
+    x = np.where(rng.integers(0, 2, size=(2, 32768)) == 1, 0.5, -0.5).astype(np.float16)
+    for k in (1, 1000, 1024):
+        got = host(w4.salient_select(dev(x), k))
+        assert np.array_equal(got, o.salient_channels(x, k)), k
 
 
 @pytest.mark.parametrize("where", ["pinned", "device"])
@@ -141,3 +147,30 @@ def test_gemv_then_correction_decode_layer(M, K, N, k):
     y_full = x.astype(np.float64) @ w[cols].astype(np.float64).T
     y_q = o.matmul_ref(x, wd)
     assert np.linalg.norm(host(y)[:, cols] - y_full) < np.linalg.norm(y_q - y_full)
+
+
+@pytest.mark.parametrize("where", ["pinned", "device"])
+@pytest.mark.parametrize("M,K,N,k", [(1, 1024, 256, 11), (5, 2048, 1040, 40), (8, 512, 8, 512),
+                                     (9, 1024, 520, 33), (32, 2048, 2048, 100), (1, 8192, 8192, 82),
+                                     (2, 32768, 1024, 1024), (3, 128, 8, 1), (4, 128, 64, 0)])
+def test_salient_correct_equals_select_then_correct(where, M, K, N, k):
+    """The one-launch step picks the same channels (in the same order) and
+    leaves the same y bits as the two calls; y also matches the oracle."""
+    require_gpu()
+    x, _, _, _, _, R = residual_case(640 + M, M, K, N)
+    r = pinned(R) if where == "pinned" else dev(R)
+    xd = dev(x)
+    y0 = torch.randn((M, N), device="cuda").half()
+    y_two, y_one = y0.clone(), y0.clone()
+    announce("salient correct", dict(where=where, M=M, K=K, N=N, k=k))
+    idx_two = w4.salient_select(xd, k)
+    w4.residual_correct(xd, r, idx_two, y_two)
+    idx_one = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+    w4.salient_correct(xd, r, k, y_one, idx=idx_one)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_one, idx_two)
+    assert torch.equal(y_one, y_two)
+    idx_ref = o.salient_channels(x, k)
+    assert np.array_equal(host(idx_one), idx_ref)
+    ref = host(y0).astype(np.float64) + o.residual_correction(x, R, idx_ref)
+    assert row_rel_l2(host(y_one), ref) <= TOL_ROW_REL_L2
