@@ -772,6 +772,86 @@ def test_msd_attention_integer_scores_and_error():
     assert o.max_row_rel_l2(y_bad, y_ref) > 1e-2
 
 
+def _int_query_case(seed, Hq, Hkv, L, d=128):
+    """Integer queries in [-127, 127] (each head reaching 127): their own first
+    int8 slice with s_1 = 1 and no residual, so the score products are exact.
+    Keys ~ N(0, 0.02^2) keep the softmax spread out; values ~ N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-127, 128, size=(Hq, d)).astype(np.float16)
+    q[:, 0] = 127
+    k = (rng.standard_normal((Hkv, L, d)) * 0.02).astype(np.float32)
+    v = rng.standard_normal((Hkv, L, d)).astype(np.float32)
+    kq = [o.quantize_int4_asym(k[h], d) for h in range(Hkv)]
+    vq = [o.quantize_int4_asym(v[h], d) for h in range(Hkv)]
+    K = tuple(np.stack([a[i] if i == 0 else a[i][:, 0] for a in kq]) for i in range(3))
+    V = tuple(np.stack([a[i] if i == 0 else a[i][:, 0] for a in vq]) for i in range(3))
+    kd = np.stack([o.dequant_int4_asym(K[0][h], K[1][h][:, None], K[2][h][:, None], d) for h in range(Hkv)])
+    vd = np.stack([o.dequant_int4_asym(V[0][h], V[1][h][:, None], V[2][h][:, None], d) for h in range(Hkv)])
+    return q, K, V, kd, vd
+
+
+def test_msd_attention_exact_when_its_slices_are():
+    """Exact score slices (integer queries) and one position per weight block:
+    each weight w is +-127 s_1 plus a second slice that takes the fp32 rounding
+    of s_1, so the split is exact to about 2^-48 and the output equals plain
+    attention over the dequantized cache to fp64 rounding."""
+    Hq, Hkv, L = 8, 2, 40
+    q, K, V, kd, vd = _int_query_case(23, Hq, Hkv, L)
+    A, S = o.decompose_activations(q, 2)
+    assert np.all(S[0] == 1.0) and np.all(S[1] == 0.0) and np.array_equal(A[0], q.astype(np.int8))
+    y = o.msd_attention(q, *K, *V, Hkv, chunk=1)
+    y_ref = o.attention_ref(q, kd, vd, Hkv)
+    assert o.max_row_rel_l2(y, y_ref) < 1e-10
+    # the softmax is not one-hot here: the check covers the whole weighting
+    h0 = q[:2].astype(np.float64) @ kd[0].T / np.sqrt(128)
+    p = np.exp(h0 - h0.max(axis=1, keepdims=True))
+    assert (p / p.sum(axis=1, keepdims=True)).max() < 0.5
+
+
+def test_msd_attention_value_error_within_slice_bound(monkeypatch):
+    """With exact scores only the weights' two-slice split errs, and the
+    decomposition leaves each weight within s_2 / 2 of its slices; so, per
+    query head g and dimension n, |o - o_ref| <= sum over blocks b of
+    s_2[b, g] / 2 * sum_{t in b} |qV[t, n] - zV[t]| / l[g].  Three blocks of the
+    default 256 positions, the last one ragged."""
+    Hq, Hkv, L, d = 8, 2, 700, 128
+    q, K, V, kd, vd = _int_query_case(24, Hq, Hkv, L, d)
+    y = o.msd_attention(q, *K, *V, Hkv)
+    y_ref = o.attention_ref(q, kd, vd, Hkv)
+    G = Hq // Hkv
+    for h in range(Hkv):
+        rows = slice(h * G, (h + 1) * G)
+        score = q[rows].astype(np.float64) @ kd[h].T / np.sqrt(d)       # exact keys, exact queries
+        p = np.exp(score - score.max(axis=1, keepdims=True))
+        l = p.sum(axis=1)
+        w = p * V[1][h].astype(np.float64)[None, :]                   # weights with the value scale
+        qv = np.abs(V[0][h].astype(np.int64) - V[2][h].astype(np.float16).astype(np.int64)[:, None])
+        bound = np.zeros((G, d))
+        for c0 in range(0, L, o.ATTN_CHUNK):
+            _, R = o.decompose_activations(w[:, c0:c0 + o.ATTN_CHUNK], 2)
+            bound += (R[1].astype(np.float64) / 2)[:, None] * qv[c0:c0 + o.ATTN_CHUNK].sum(axis=0)[None, :]
+        bound /= l[:, None]
+        err = np.abs(y[rows] - y_ref[rows])
+        assert np.all(err <= bound * (1 + 1e-9) + 1e-13)
+        # the bound is tight enough to mean something: within 0.3 % of the
+        # largest output (a wrong block scale or a dropped slice is far off)
+        assert bound.max() < 3e-3 * np.abs(y_ref[rows]).max()
+        assert np.abs(y[rows] - y_ref[rows]).max() > 0  # the split is not exact here
+    # planted: a weight split that keeps only its first slice breaks the bound
+    import oracle.w4_oracle as ow
+    real = ow.decompose_activations
+
+    def first_slice_only(x, nslices=2):
+        A, S = real(x, nslices)
+        A[1:] = 0
+        return A, S
+    monkeypatch.setattr(ow, "decompose_activations", first_slice_only)
+    y_bad = o.msd_attention(q, *K, *V, Hkv)
+    monkeypatch.setattr(ow, "decompose_activations", real)
+    assert np.abs(y_bad - y_ref).max() > 2 * np.abs(y - y_ref).max()
+    assert o.max_row_rel_l2(y_bad, y_ref) > 1e-3
+
+
 # ------------------------------------------------------- residual compensation
 def test_salient_channels_hand_example():
     x = np.array([[0.5, -3.0, 2.0, 3.0, 0.0, 1.0],
