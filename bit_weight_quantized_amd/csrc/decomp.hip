@@ -218,10 +218,154 @@ __global__ __launch_bounds__(T) void decompose_kernel(
   }
 }
 
+// Lean variant for one or two slices with the row cached in registers (K <=
+// 32 T): the same decisions as decompose_kernel, with fewer instructions.
+//  * The absmax comes from the magnitude bits (an integer maximum: the bit
+//    pattern of |x| orders like the value for finite x).
+//  * r_1 = fl32(x - s_1 A_1) is one fp32 fma: the exact residual rounded once,
+//    which is the fp32 value decide127 starts from when given the exact fp64
+//    residual.  The second slice decides from it (adaptive: rint(r_1 / s_2);
+//    fixed ratio: rint(fl32(254 r_1) / s_1), the estimate the product with the
+//    decomposition in its K loop uses, within 2^-15 of the quotient).
+//  * Each 16-byte chunk's 8 decisions take their fast fp32 form, and the exact
+//    decide127 runs for all 8 only when one of them lies within 2^-14 of a
+//    half-integer (about 1 chunk in 1000): one branch per chunk, not one per
+//    decision.
+//  * fp64 remains for the exact residual maximum (the adaptive second scale)
+//    and inside those fallbacks.
+template <int NS, bool FIXED, int T>
+__global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                           int8_t* __restrict__ slices_op,
+                                                           int8_t* __restrict__ slices_out,
+                                                           float* __restrict__ tok_scale) {
+  static_assert(NS == 1 || NS == 2, "one or two slices");
+  static_assert(!FIXED || NS == 2, "the fixed ratio defines a second slice");
+  constexpr int CH = 4;
+  constexpr int kStep = 8 * T;
+  __shared__ double red[T / kWave];
+  const int rt = (int)threadIdx.x;
+  const int m = (int)blockIdx.x;
+  const uint16_t* xr = x + (size_t)m * K;
+
+  u32x4 xc[CH];
+  uint32_t mag = 0;  // two 15-bit magnitudes per word: the larger of each half
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k = 8 * rt + c * kStep;
+    xc[c] = k < K ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = xc[c][i] & 0x7FFF7FFFu;
+      mag = max(mag, max(w & 0xFFFFu, w >> 16));
+    }
+  }
+  const double amax = block_max<T>((double)half_bits_to_float((uint16_t)mag), red);
+  const double s1 = (double)(float)(amax / 127.0);
+  const float inv1 = s1 != 0.0 ? (float)(1.0 / s1) : 0.f;
+  const float s1f = (float)s1;
+
+  auto store8 = [&](int j, int k, const int (&a)[8]) {
+    const size_t row = ((size_t)j * M + m) * K;
+    if (slices_out)
+      *reinterpret_cast<u32x2*>(slices_out + row + k) = u32x2{pack4(a[0], a[1], a[2], a[3]), pack4(a[4], a[5], a[6], a[7])};
+    const int kk = k % 64, h = kk / 32, kb = (kk % 32) / 8;
+    *reinterpret_cast<u32x2*>(slices_op + row + (k - kk) + 16 * kb + 8 * h) =
+        u32x2{pack4(a[0], a[4], a[1], a[5]), pack4(a[2], a[6], a[3], a[7])};
+  };
+  // rint of the fp32 estimate t and whether t is within 2^-14 of a half-integer
+  auto fast = [&](float t, bool& near) {
+    const float q = (t + kRintMagic) - kRintMagic;
+    near = near || fabsf(fabsf(t - q) - 0.5f) < kNearHalf;
+    return q;
+  };
+
+  float rf[NS > 1 ? CH : 1][8];     // r_1 = fl32(x - s_1 A_1)
+  uint32_t code1[NS > 1 ? CH : 1][2];  // A_1, plain order (for the exact fallbacks of slice 2)
+  double amax2 = 0.0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k = 8 * rt + c * kStep;
+    if (k >= K) continue;
+    float xf[8], q[8];
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xf[2 * i] = half_bits_to_float((uint16_t)(xc[c][i] & 0xFFFFu));
+      xf[2 * i + 1] = half_bits_to_float((uint16_t)(xc[c][i] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = fast(xf[i] * inv1, near);
+    if (near) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = decide127((double)xf[i], s1, inv1);
+    }
+    int a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      q[i] = fminf(fmaxf(q[i], -127.f), 127.f);
+      a[i] = (int)q[i];
+    }
+    store8(0, k, a);
+    if constexpr (NS > 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        rf[c][i] = fmaf(-s1f, q[i], xf[i]);
+        if constexpr (!FIXED) amax2 = fmax(amax2, fabs(fma(-s1, (double)q[i], (double)xf[i])));  // exact
+      }
+      code1[c][0] = pack4(a[0], a[1], a[2], a[3]);
+      code1[c][1] = pack4(a[4], a[5], a[6], a[7]);
+    }
+  }
+  if (rt == 0) tok_scale[m] = (float)s1;
+  if constexpr (NS == 1) return;
+
+  double s2 = s1;
+  float inv2 = inv1;
+  if constexpr (!FIXED) {
+    s2 = (double)(float)(block_max<T>(amax2, red) / 127.0);
+    inv2 = s2 != 0.0 ? (float)(1.0 / s2) : 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int k = 8 * rt + c * kStep;
+    if (k >= K) continue;
+    float q[8];
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float n = FIXED ? (float)kFixedRatio * rf[c][i] : rf[c][i];
+      q[i] = fast(n * inv2, near);
+    }
+    if (near) {  // the exact residual, from x and A_1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double xv = (double)half_bits_to_float((uint16_t)(xc[c][i / 2] >> (16 * (i % 2))));
+        const double r = xv - s1 * (double)code_byte(code1[c], i);
+        q[i] = FIXED ? decide127(kFixedRatio * r, s1, inv1) : decide127(r, s2, inv2);
+      }
+    }
+    int a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (int)fminf(fmaxf(q[i], -127.f), 127.f);
+    store8(1, k, a);
+  }
+  if (rt == 0) tok_scale[(size_t)M + m] = FIXED ? (float)(s1 / kFixedRatio) : (float)s2;
+}
+
 }  // namespace
 
 int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, int8_t* slices_op, int8_t* slices_out,
                      float* tok_scale, hipStream_t s) {
+// rows cached in registers: the lean kernel for one or two slices
+#define W4_DECOMP_CACHED(NS, FX, T)                                                                                 \
+  do {                                                                                                             \
+    if constexpr (NS <= 2)                                                                                         \
+      hipLaunchKernelGGL((decompose_lean_kernel<NS, FX, T>), dim3(M), dim3(T), 0, s, x, M, K, slices_op, slices_out, \
+                         tok_scale);                                                                               \
+    else                                                                                                           \
+      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4, false, T>), dim3(M), dim3(T), 0, s, x, M, K, slices_op,       \
+                         slices_out, tok_scale);                                                                   \
+  } while (0)
 #define W4_DECOMP(NS, FX)                                                                                        \
   do {                                                                                                          \
     constexpr int kRows = kDecompThreads / kWave;                                                               \
@@ -229,11 +373,9 @@ int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, i
       hipLaunchKernelGGL((decompose_kernel<NS, FX, 1, true, kDecompThreads>), dim3((M + kRows - 1) / kRows),    \
                          dim3(kDecompThreads), 0, s, x, M, K, slices_op, slices_out, tok_scale);                \
     else if (M <= kFewRows && K <= 4 * 8 * kDecompWide)                                                         \
-      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4, false, kDecompWide>), dim3(M), dim3(kDecompWide), 0, s, x, \
-                         M, K, slices_op, slices_out, tok_scale);                                               \
+      W4_DECOMP_CACHED(NS, FX, kDecompWide);                                                                    \
     else if (K <= 4 * 8 * kDecompThreads)                                                                       \
-      hipLaunchKernelGGL((decompose_kernel<NS, FX, 4, false, kDecompThreads>), dim3(M), dim3(kDecompThreads), 0, \
-                         s, x, M, K, slices_op, slices_out, tok_scale);                                         \
+      W4_DECOMP_CACHED(NS, FX, kDecompThreads);                                                                 \
     else                                                                                                        \
       hipLaunchKernelGGL((decompose_kernel<NS, FX, 0, false, kDecompThreads>), dim3(M), dim3(kDecompThreads), 0, \
                          s, x, M, K, slices_op, slices_out, tok_scale);                                         \
@@ -247,6 +389,7 @@ int launch_decompose(const uint16_t* x, int M, int K, int nslices, bool fixed, i
   else
     W4_DECOMP(3, false);
 #undef W4_DECOMP
+#undef W4_DECOMP_CACHED
   return check_launch("decompose");
 }
 
