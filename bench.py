@@ -305,6 +305,10 @@ def bench_mlp_gemv(w4, torch, stream, replays=4):
 
 DECODER_LAYER = (("q", 8192, 8192), ("k", 8192, 1024), ("v", 8192, 1024), ("o", 8192, 8192),
                  ("gate", 8192, 28672), ("up", 8192, 28672), ("down", 28672, 8192))
+# The same layer with the products that share an input stored as one matrix
+# (q, k, v and gate, up concatenated along N): four products instead of seven.
+DECODER_LAYER_FUSED = (("qkv", 8192, 10240, ("q", "k", "v")), ("o", 8192, 8192, ("o",)),
+                       ("gate_up", 8192, 57344, ("gate", "up")), ("down", 28672, 8192, ("down",)))
 
 
 def bench_decoder_layer(w4, torch, stream, replays=4):
@@ -318,63 +322,74 @@ def bench_decoder_layer(w4, torch, stream, replays=4):
     for fmt, G in ((w4.INT4_ASYM, 128), (w4.NF4, 64)):
         layer_bytes = sum(weight_stream_bytes(fmt, K, N, G) for _, K, N in DECODER_LAYER)
         n_sets = rotation_sets(layer_bytes)
-        sets = [{name: make_weight_sets(w4, torch, fmt, K, N, G, 1, 60000 + 1000 * s + 10 * i + 100 * fmt)[0]
-                 for i, (name, K, N) in enumerate(DECODER_LAYER)} for s in range(n_sets)]
+        sep = [{name: make_weight_sets(w4, torch, fmt, K, N, G, 1, 60000 + 1000 * s + 10 * i + 100 * fmt)[0]
+                for i, (name, K, N) in enumerate(DECODER_LAYER)} for s in range(n_sets)]
+        # the fused layer holds the same weights: packed rows, scales and zero
+        # points concatenated along N (the packed tiles are stored row block
+        # by row block, so the bytes concatenate)
+        fused = [{name: tuple(None if sep[s][parts[0]][a] is None else
+                              torch.cat([sep[s][pn][a] for pn in parts]) for a in range(3))
+                  for name, _, _, parts in DECODER_LAYER_FUSED} for s in range(n_sets)]
         paths = [("gemv", 1)]
         paths += [("dq_f16", 256), ("postscale", 256)]
         if fmt == w4.INT4_ASYM:
             paths += [("msd2", 256), ("msd2_fixed", 256), ("msd2_fixed_fused", 256)]
-        for path, M in paths:
-            xs = {K: torch.from_numpy(wl.make_activations(5, 0 if K == 8192 else 6, M, K)).cuda()
-                  for K in {K for _, K, _ in DECODER_LAYER}}
-            ys = {name: torch.empty((M, N), dtype=torch.float16, device="cuda") for name, _, N in DECODER_LAYER}
-            calls = []
-            for s in range(n_sets):
-                for name, K, N in DECODER_LAYER:
-                    p, sc, z = sets[s][name]
-                    x, y = xs[K], ys[name]
-                    if path == "gemv":
-                        ws = torch.zeros(max(16, w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)), dtype=torch.uint8,
-                                         device="cuda")
-                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, K=K: w4.gemv(x, p, sc, z, G, fmt, out=y,
-                                                                                         workspace=ws))
-                    elif path in ("dq_f16", "postscale"):
-                        mode = w4.DQ_F16 if path == "dq_f16" else w4.POSTSCALE
-                        ws = torch.empty(max(16, w4.workspace_bytes(w4.OP_GEMM, M, K, N, G, mode)), dtype=torch.uint8,
-                                         device="cuda")
-                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, mode=mode: w4.gemm(
-                            x, p, sc, z, G, fmt, mode, out=y, workspace=ws))
-                    elif path == "msd2_fixed_fused":
-                        ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP_FUSED, M, K, N, G, 0),
-                                         dtype=torch.uint8, device="cuda")
-                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws: w4.gemm_decomp_fixed_fused(
-                            x, p, sc, z, G, out=y, workspace=ws))
-                    else:
-                        ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8,
-                                         device="cuda")
-                        fn = w4.gemm_decomp_fixed if path == "msd2_fixed" else (
-                            lambda *a, **k: w4.gemm_decomp(*a[:5], 2, **k))
-                        calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, fn=fn: fn(x, p, sc, z, G, out=y,
-                                                                                         workspace=ws))
-            g = graph_of(torch, stream, calls)
-            time_replays(torch, stream, g, 1)
-            us = time_replays(torch, stream, g, replays) * 1e3 / (replays * n_sets)
-            row = {"format": "int4_asym_g128" if fmt == w4.INT4_ASYM else "nf4_b64", "path": path, "M": M,
-                   "us_per_layer": round(us, 1), "weight_bytes": layer_bytes}
-            if M == 1:
-                gbs = layer_bytes / (us * 1e-6) / 1e9
-                row.update({"GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-            else:
-                tf = flops_256 / (us * 1e-6) / 1e12
-                mult, peak = (2, INT8_MFMA_PEAK_TOPS) if path.startswith("msd") else (1, FP16_MFMA_PEAK_TFLOPS)
-                row.update({"tflops_useful": round(tf, 1), "mfma_frac": round(tf * mult / peak, 4)})
-            out.append(row)
-            del g, calls
-        del sets
+        for layout, mats, sets in (("separate", DECODER_LAYER, sep),
+                                   ("fused", tuple(m[:3] for m in DECODER_LAYER_FUSED), fused)):
+            for path, M in paths:
+                xs = {K: torch.from_numpy(wl.make_activations(5, 0 if K == 8192 else 6, M, K)).cuda()
+                      for K in {K for _, K, _ in mats}}
+                ys = {name: torch.empty((M, N), dtype=torch.float16, device="cuda") for name, _, N in mats}
+                calls = []
+                for s in range(n_sets):
+                    for name, K, N in mats:
+                        p, sc, z = sets[s][name]
+                        x, y = xs[K], ys[name]
+                        if path == "gemv":
+                            ws = torch.zeros(max(16, w4.workspace_bytes(w4.OP_GEMV, M, K, N, G, fmt)),
+                                             dtype=torch.uint8, device="cuda")
+                            calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, K=K: w4.gemv(
+                                x, p, sc, z, G, fmt, out=y, workspace=ws))
+                        elif path in ("dq_f16", "postscale"):
+                            mode = w4.DQ_F16 if path == "dq_f16" else w4.POSTSCALE
+                            ws = torch.empty(max(16, w4.workspace_bytes(w4.OP_GEMM, M, K, N, G, mode)),
+                                             dtype=torch.uint8, device="cuda")
+                            calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, mode=mode: w4.gemm(
+                                x, p, sc, z, G, fmt, mode, out=y, workspace=ws))
+                        elif path == "msd2_fixed_fused":
+                            ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP_FUSED, M, K, N, G, 0),
+                                             dtype=torch.uint8, device="cuda")
+                            calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws: w4.gemm_decomp_fixed_fused(
+                                x, p, sc, z, G, out=y, workspace=ws))
+                        else:
+                            ws = torch.empty(w4.workspace_bytes(w4.OP_GEMM_DECOMP, M, K, N, G, 2), dtype=torch.uint8,
+                                             device="cuda")
+                            fn = w4.gemm_decomp_fixed if path == "msd2_fixed" else (
+                                lambda *a, **k: w4.gemm_decomp(*a[:5], 2, **k))
+                            calls.append(lambda p=p, sc=sc, z=z, x=x, y=y, ws=ws, fn=fn: fn(x, p, sc, z, G, out=y,
+                                                                                             workspace=ws))
+                g = graph_of(torch, stream, calls)
+                time_replays(torch, stream, g, 1)
+                us = time_replays(torch, stream, g, replays) * 1e3 / (replays * n_sets)
+                row = {"format": "int4_asym_g128" if fmt == w4.INT4_ASYM else "nf4_b64", "layout": layout,
+                       "path": path, "M": M, "us_per_layer": round(us, 1), "weight_bytes": layer_bytes}
+                if M == 1:
+                    gbs = layer_bytes / (us * 1e-6) / 1e9
+                    row.update({"GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+                else:
+                    tf = flops_256 / (us * 1e-6) / 1e12
+                    mult, peak = (2, INT8_MFMA_PEAK_TOPS) if path.startswith("msd") else (1, FP16_MFMA_PEAK_TFLOPS)
+                    row.update({"tflops_useful": round(tf, 1), "mfma_frac": round(tf * mult / peak, 4)})
+                out.append(row)
+                del g, calls
+        del sep, fused, sets
         torch.cuda.empty_cache()
     return {"workload": "decoder_layer_hidden8192_inter28672_q64_kv8", "matrices": [list(m) for m in DECODER_LAYER],
+            "fused_matrices": [[m[0], m[1], m[2]] for m in DECODER_LAYER_FUSED],
             "note": "M=256 msd paths include the activation decomposition of every product and are measured "
-                    "against the dense int8 peak with two int8 products per useful multiply-add",
+                    "against the dense int8 peak with two int8 products per useful multiply-add; layout "
+                    "'separate' runs the seven products, 'fused' the same weights as four (q|k|v and gate|up "
+                    "concatenated along N, as inference engines store them)",
             "rows": out}
 
 
