@@ -52,16 +52,24 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return min(max(e, -127), 127);
 }
 
+// E2M1 code of t (round to nearest, ties to even, |t| saturated at 6),
+// without branches: below 1 the code is rint(2 |t|) (0, 0.5 or 1.0); from 1
+// on, |t| rounded to one mantissa bit on its fp32 bit pattern is (1 + m/2) 2^E
+// and the code is 2 E + 2 + m.
 __device__ __forceinline__ int e2m1_code(float t) {
   const float a = fminf(fabsf(t), 6.f);
-  const int c = a <= 0.25f ? 0 : a < 0.75f ? 1 : a <= 1.25f ? 2 : a < 1.75f ? 3
-              : a <= 2.5f ? 4 : a < 3.5f ? 5 : a <= 5.f ? 6 : 7;
+  const int lo = (int)__builtin_rintf(2.f * a);
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t r = b + 0x1FFFFFu + ((b >> 22) & 1u);  // carry into the exponent allowed
+  const int hi = (int)(r >> 22) - 2 * 127 + 2;             // 2 (E + 127) + m - 254 + 2
+  const int c = a < 1.f ? lo : hi;
   return (t < 0.f && c != 0) ? (c | 8) : c;
 }
 
+// magnitude of code c (0..7): 0.5 c below 2, else (1 + m/2) 2^(c/2 - 1)
 __device__ __forceinline__ float e2m1_mag(int c) {
-  const int e = (c >> 1) & 3, m = c & 1;
-  return e == 0 ? 0.5f * m : ldexpf(1.f + 0.5f * m, e - 1);
+  const float big = __uint_as_float(((uint32_t)((c >> 1) + 126) << 23) | ((uint32_t)(c & 1) << 22));
+  return c < 2 ? 0.5f * (float)c : big;
 }
 
 // one 32-element block: codes and exponent of v (v is left as the residual)
