@@ -395,18 +395,6 @@ __device__ __forceinline__ int operand_byte(int t) {
   return 64 * bb + 16 * kk + 8 * hh + (e < 4 ? 2 * e : 2 * (e - 4) + 1);
 }
 
-// clamp(rint(fl64(n / s)), -127, 127) as the decomposition kernel decides
-// it: inv = 1 / s correctly rounded, |n / s| < 2^8, so fl64(n * inv) and the
-// quotient round alike unless the quotient lies within 2^-44 of a
-// half-integer; a product within 2^-30 of one takes the division itself.
-__device__ __forceinline__ double quant127_q(double n, double s, double inv) {
-  if (s == 0.0) return 0.0;
-  const double t = n * inv;
-  double q = rint(t);
-  if (fabs(fabs(t - q) - 0.5) < 0x1p-30) q = rint(n / s);
-  return fmin(fmax(q, -127.0), 127.0);
-}
-
 __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
     const uint16_t* __restrict__ qh, int MQ, int Hq, int Hkv, int L,
     const uint8_t* __restrict__ kp, const uint16_t* __restrict__ ks, const uint16_t* __restrict__ kz,
@@ -451,8 +439,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
       zk[pp] = kz[tok0 + 16 * (2 * pp + hi) + ln];
       sk[pp] = ks[tok0 + 16 * (2 * pp + hi) + ln];
     }
-    // ---- the group's queries split into two int8 slices, in fp64 with the
-    // decisions of the decomposition kernel (per head: s_1 = fp32(max|q| /
+    // ---- the group's queries split into two int8 slices with the decisions
+    // of the decomposition kernel, taken in fp32 (per head: s_1 = fp32(max|q| /
     // 127), A_1 = rint(q / s_1), r = q - s_1 A_1, s_2 = fp32(max|r| / 127),
     // A_2 = rint(r / s_2)), while the cache loads are in flight.  Lane l takes
     // head l / 8, dimensions 16 (l mod 8) .. + 15; the codes go to this wave's
@@ -469,37 +457,74 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
         xq[0] = src[0];
         xq[1] = src[1];
       }
-      auto xval = [&](int e) {  // dimension 16 p8 + e
-        return (double)half_bits_to_float((uint16_t)(xq[e / 8][(e % 8) / 2] >> (16 * (e % 2))));
-      };
-      auto max8 = [](double v) {  // over the 8 lanes of a head
+      // dimension 16 p8 + e, and the largest magnitude of the head's 128 (as
+      // bits: for finite values they order like the magnitudes)
+      float xf[16];
+      uint32_t mag = 0;
 #pragma unroll
-        for (int off = 1; off < 8; off <<= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t v = xq[i / 4][i % 4];
+        xf[2 * i] = half_bits_to_float((uint16_t)(v & 0xFFFFu));
+        xf[2 * i + 1] = half_bits_to_float((uint16_t)(v >> 16));
+        const uint32_t m2 = v & 0x7FFF7FFFu;
+        mag = max(mag, max(m2 & 0xFFFFu, m2 >> 16));
+      }
+      auto max8 = [](uint32_t v) {  // over the 8 lanes of a head
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
         return v;
       };
-      double amax = 0.0;
+      // two 8-byte groups per slice: dimensions 16 p8 + 8 u + (0..7) sit at
+      // operand_byte(16 p8 + 8 u) + p(e)
+      auto store16 = [&](int row, const float (&q)[16]) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) amax = fmax(amax, fabs(xval(e)));
-      amax = max8(amax);
-      const double s1 = (double)(float)(amax / 127.0);
-      const double inv1 = s1 != 0.0 ? 1.0 / s1 : 0.0;
-      double amax2 = 0.0;
+        for (int u = 0; u < 2; ++u) {
+          int c[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) c[e] = (int)fminf(fmaxf(q[8 * u + e], -127.f), 127.f);
+          auto b4 = [](int a0, int a1, int a2, int a3) {
+            return (uint32_t)(a0 & 0xFF) | ((uint32_t)(a1 & 0xFF) << 8) | ((uint32_t)(a2 & 0xFF) << 16) |
+                   ((uint32_t)(a3 & 0xFF) << 24);
+          };
+          *reinterpret_cast<u32x2*>(my + row * kChunk + operand_byte(16 * p8 + 8 * u)) =
+              u32x2{b4(c[0], c[4], c[1], c[5]), b4(c[2], c[6], c[3], c[7])};
+        }
+      };
+      mag = max8(mag);
+      const double s1 = (double)(float)((double)half_bits_to_float((uint16_t)mag) / 127.0);
+      const float s1f = (float)s1, inv1 = s1 != 0.0 ? (float)(1.0 / s1) : 0.f;
+      // slice 1: the fast fp32 decisions, all 16 exact (decide127) when one
+      // is near a half-integer
+      float q[16];
+      bool near = false;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) q[e] = rint127_fast(xf[e], inv1, near);
+      if (near) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) q[e] = decide127((double)xf[e], s1, inv1);
+      }
+      store16(gq, q);
+      // r = x - s_1 A_1 is exact in fp32.  For A_1 = 0 it is x.  Otherwise
+      // |x| >= s_1 / 2, so x is a multiple of s_1's ulp (the fp16 grid at |x|
+      // is at least 2^12 of them), and |r| <= s_1 / 2 is at most 2^23 of them.
+      float rf[16];
+      uint32_t mag2 = 0;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const double x = xval(e);
-        const double a = quant127_q(x, s1, inv1);
-        my[gq * kChunk + operand_byte(16 * p8 + e)] = (int8_t)(int)a;
-        amax2 = fmax(amax2, fabs(x - s1 * a));
+        rf[e] = fmaf(-s1f, fminf(fmaxf(q[e], -127.f), 127.f), xf[e]);
+        mag2 = max(mag2, __float_as_uint(fabsf(rf[e])));
       }
-      amax2 = max8(amax2);
-      const double s2 = (double)(float)(amax2 / 127.0);
-      const double inv2 = s2 != 0.0 ? 1.0 / s2 : 0.0;
+      mag2 = max8(mag2);
+      const double s2 = (double)(float)((double)__uint_as_float(mag2) / 127.0);
+      const float inv2 = s2 != 0.0 ? (float)(1.0 / s2) : 0.f;
+      near = false;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const double x = xval(e);
-        const double r = x - s1 * quant127_q(x, s1, inv1);
-        my[(8 + gq) * kChunk + operand_byte(16 * p8 + e)] = (int8_t)(int)quant127_q(r, s2, inv2);
+      for (int e = 0; e < 16; ++e) q[e] = rint127_fast(rf[e], inv2, near);
+      if (near) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) q[e] = decide127((double)rf[e], s2, inv2);
       }
+      store16(8 + gq, q);
       if (p8 == 0) {
         qscale[w][0][gq] = (float)s1;
         qscale[w][1][gq] = (float)s2;

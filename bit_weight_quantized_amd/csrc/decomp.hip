@@ -47,37 +47,6 @@ __device__ __forceinline__ double block_max(double v, double* red) {
   return r;
 }
 
-// clamp(rint(fl64(n / s)), -127, 127) for an exactly known fp64 numerator n
-// (x itself, a residual, or 254 times one) and a scale s that is an fp32
-// value, decided in fp32.  inv = fl32(1 / s) (the quotient in fp64, so its
-// relative error is at most 2^-24 + 2^-53); with nf = fl32(n) the estimate
-// t = fl32(nf * inv) is within 3 * 2^-24 * 127.0001 < 2^-15.4 of n / s, since
-// every quotient here has |n / s| <= 127.0001.  Where t is at least 2^-14 from
-// every half-integer, rint(t) is the decision.  Nearer (about 1 in 8000), the
-// sign of n - h s (h the half-integer next to rint(t) on t's side, the only
-// one that can lie between t and the quotient), from one fp64 fma of exact
-// operands rounded once, says which side the quotient lies on (on h: to
-// even).  That decides rint of the exact quotient; rint(fl64(n / s)) is the
-// same integer because no quotient here comes within 2^-25 of a half-integer
-// without being one (n - h s is a multiple of the finer of the grids of n and
-// s / 2, and that grid is at least 2^-25 s wherever the quotient is near a
-// half-integer of magnitude 1/2 or more), while fl64 moves a quotient by at
-// most 2^-46.  rint is the fp32 addition of 1.5 * 2^23 (ties to even).
-constexpr float kRintMagic = 12582912.0f;  // 1.5 * 2^23
-constexpr float kNearHalf = 0x1p-14f;
-
-__device__ __forceinline__ float decide127(double n, double s, float inv) {
-#pragma clang fp contract(off)
-  const float t = (float)n * inv;
-  float q = (t + kRintMagic) - kRintMagic;
-  if (fabsf(fabsf(t - q) - 0.5f) < kNearHalf) {
-    const float sg = t >= q ? 1.f : -1.f;
-    const double d = fma(-(double)(q + 0.5f * sg), s, n);
-    if (d * (double)sg > 0.0 || (d == 0.0 && ((int)q & 1) != 0)) q += sg;
-  }
-  return fminf(fmaxf(q, -127.f), 127.f);
-}
-
 __device__ __forceinline__ int code_byte(const uint32_t (&w)[2], int i) {
   return (int)(int8_t)(uint8_t)(w[i / 4] >> (8 * (i % 4)));
 }
@@ -222,17 +191,18 @@ __global__ __launch_bounds__(T) void decompose_kernel(
 // 32 T): the same decisions as decompose_kernel, with fewer instructions.
 //  * The absmax comes from the magnitude bits (an integer maximum: the bit
 //    pattern of |x| orders like the value for finite x).
-//  * r_1 = fl32(x - s_1 A_1) is one fp32 fma: the exact residual rounded once,
-//    which is the fp32 value decide127 starts from when given the exact fp64
-//    residual.  The second slice decides from it (adaptive: rint(r_1 / s_2);
-//    fixed ratio: rint(fl32(254 r_1) / s_1), the estimate the product with the
+//  * r_1 = x - s_1 A_1 is one fp32 fma, and exact: for A_1 = 0 it is x;
+//    otherwise |x| >= s_1 / 2, so x is a multiple of s_1's ulp (the fp16 grid
+//    at |x| is at least 2^12 of them) and |r_1| <= s_1 / 2 is at most 2^23 of
+//    them.  So the residual maximum is an fp32 maximum, and the second slice
+//    decides from r_1 (adaptive: rint(r_1 / s_2); fixed ratio:
+//    rint(fl32(254 r_1) / s_1), the estimate the product with the
 //    decomposition in its K loop uses, within 2^-15 of the quotient).
 //  * Each 16-byte chunk's 8 decisions take their fast fp32 form, and the exact
 //    decide127 runs for all 8 only when one of them lies within 2^-14 of a
 //    half-integer (about 1 chunk in 1000): one branch per chunk, not one per
 //    decision.
-//  * fp64 remains for the exact residual maximum (the adaptive second scale)
-//    and inside those fallbacks.
+//  * fp64 remains for the scales and inside those fallbacks.
 template <int NS, bool FIXED, int T>
 __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                            int8_t* __restrict__ slices_op,
@@ -272,16 +242,8 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
     *reinterpret_cast<u32x2*>(slices_op + row + (k - kk) + 16 * kb + 8 * h) =
         u32x2{pack4(a[0], a[4], a[1], a[5]), pack4(a[2], a[6], a[3], a[7])};
   };
-  // rint of the fp32 estimate t and whether t is within 2^-14 of a half-integer
-  auto fast = [&](float t, bool& near) {
-    const float q = (t + kRintMagic) - kRintMagic;
-    near = near || fabsf(fabsf(t - q) - 0.5f) < kNearHalf;
-    return q;
-  };
-
-  float rf[NS > 1 ? CH : 1][8];     // r_1 = fl32(x - s_1 A_1)
-  uint32_t code1[NS > 1 ? CH : 1][2];  // A_1, plain order (for the exact fallbacks of slice 2)
-  double amax2 = 0.0;
+  float rf[NS > 1 ? CH : 1][8];  // r_1 = x - s_1 A_1 (exact)
+  uint32_t mag2 = 0;             // bits of max |r_1|
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int k = 8 * rt + c * kStep;
@@ -294,7 +256,7 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
       xf[2 * i + 1] = half_bits_to_float((uint16_t)(xc[c][i] >> 16));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = fast(xf[i] * inv1, near);
+    for (int i = 0; i < 8; ++i) q[i] = rint127_fast(xf[i], inv1, near);
     if (near) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = decide127((double)xf[i], s1, inv1);
@@ -310,10 +272,8 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         rf[c][i] = fmaf(-s1f, q[i], xf[i]);
-        if constexpr (!FIXED) amax2 = fmax(amax2, fabs(fma(-s1, (double)q[i], (double)xf[i])));  // exact
+        mag2 = max(mag2, __float_as_uint(fabsf(rf[c][i])));
       }
-      code1[c][0] = pack4(a[0], a[1], a[2], a[3]);
-      code1[c][1] = pack4(a[4], a[5], a[6], a[7]);
     }
   }
   if (rt == 0) tok_scale[m] = (float)s1;
@@ -322,7 +282,7 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
   double s2 = s1;
   float inv2 = inv1;
   if constexpr (!FIXED) {
-    s2 = (double)(float)(block_max<T>(amax2, red) / 127.0);
+    s2 = (double)(float)(block_max<T>((double)__uint_as_float(mag2), red) / 127.0);
     inv2 = s2 != 0.0 ? (float)(1.0 / s2) : 0.f;
   }
 #pragma unroll
@@ -334,13 +294,12 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float n = FIXED ? (float)kFixedRatio * rf[c][i] : rf[c][i];
-      q[i] = fast(n * inv2, near);
+      q[i] = rint127_fast(n, inv2, near);
     }
-    if (near) {  // the exact residual, from x and A_1
+    if (near) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const double xv = (double)half_bits_to_float((uint16_t)(xc[c][i / 2] >> (16 * (i % 2))));
-        const double r = xv - s1 * (double)code_byte(code1[c], i);
+        const double r = (double)rf[c][i];
         q[i] = FIXED ? decide127(kFixedRatio * r, s1, inv1) : decide127(r, s2, inv2);
       }
     }

@@ -135,4 +135,48 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __half_as_ushort(__float2half_rn(f));
 }
 
+// clamp(rint(fl64(n / s)), -127, 127) for an exactly known fp64 numerator n
+// (x itself, a residual, or 254 times one) and a scale s that is an fp32
+// value, decided in fp32.  inv = fl32(1 / s) (the quotient in fp64, so its
+// relative error is at most 2^-24 + 2^-53); with nf = fl32(n) the estimate
+// t = fl32(nf * inv) is within 3 * 2^-24 * 127.0001 < 2^-15.4 of n / s, since
+// every quotient here has |n / s| <= 127.0001.  Where t is at least 2^-14 from
+// every half-integer, rint(t) is the decision.  Nearer (about 1 in 8000), the
+// sign of n - h s (h the half-integer next to rint(t) on t's side, the only
+// one that can lie between t and the quotient), from one fp64 fma of exact
+// operands rounded once, says which side the quotient lies on (on h: to
+// even).  That decides rint of the exact quotient; rint(fl64(n / s)) is the
+// same integer because no quotient here comes within 2^-25 of a half-integer
+// without being one (n - h s is a multiple of the finer of the grids of n and
+// s / 2, and that grid is at least 2^-25 s wherever the quotient is near a
+// half-integer of magnitude 1/2 or more), while fl64 moves a quotient by at
+// most 2^-46.  rint is the fp32 addition of 1.5 * 2^23 (ties to even).
+constexpr float kRintMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kNearHalf = 0x1p-14f;
+
+__device__ __forceinline__ float decide127(double n, double s, float inv) {
+#pragma clang fp contract(off)
+  const float t = (float)n * inv;
+  float q = (t + kRintMagic) - kRintMagic;
+  if (fabsf(fabsf(t - q) - 0.5f) < kNearHalf) {
+    const float sg = t >= q ? 1.f : -1.f;
+    const double d = fma(-(double)(q + 0.5f * sg), s, n);
+    if (d * (double)sg > 0.0 || (d == 0.0 && ((int)q & 1) != 0)) q += sg;
+  }
+  return fminf(fmaxf(q, -127.f), 127.f);
+}
+
+// The fast form of decide127's estimate: rint(fl32(n * inv)), and near set
+// when that estimate lies within 2^-14 of a half-integer (then decide127 must
+// decide).  Branch-free, for callers that decide a group of values this way
+// and take decide127 for the whole group only when one of them is near.
+__device__ __forceinline__ float rint127_fast(float n, float inv, bool& near) {
+#pragma clang fp contract(off)
+  const float t = n * inv;
+  const float q = (t + kRintMagic) - kRintMagic;
+  near = near || fabsf(fabsf(t - q) - 0.5f) < kNearHalf;
+  return q;
+}
+
+
 }  // namespace w4

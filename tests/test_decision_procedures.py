@@ -157,3 +157,26 @@ def test_emulation_rejects_a_plain_fp32_rounding():
         t = (r.astype(F32) * inv32(s)).astype(F32)
         wrong += int(np.sum(np.clip(rint32(t), -127, 127) != A[0, m]))
     assert wrong > 0
+
+
+def test_first_residual_is_exact_in_fp32():
+    """x - s_1 A_1 (A_1 the oracle's first slice) is an fp32 value: for A_1 = 0
+    it is x, otherwise x sits on a grid coarser than s_1's ulp and |r| <= s_1
+    / 2.  Rows: those above, plus rows spanning 10 decades with fp16
+    subnormals."""
+    rng = np.random.default_rng(77)
+    wide = (rng.standard_normal((64, 512)) * 10.0 ** rng.uniform(-7, 4, (64, 512))).astype(np.float16)
+    for x in (rows_under_test(), wide):
+        A, S = o.decompose_activations(x, 2)
+        r = x.astype(np.float64) - S[0][:, None].astype(np.float64) * A[0].astype(np.float64)  # exact in fp64
+        assert np.array_equal(r.astype(F32).astype(np.float64), r)
+        # the fp32 fma the kernels use gives it: fl32 of the exact value
+        assert np.array_equal(np.abs(r).max(axis=1).astype(F32).view(np.uint32),
+                              np.abs(r.astype(F32)).max(axis=1).view(np.uint32))
+    # the single rounding matters: the product rounded to fp32 first, then
+    # the difference, misses the exact residual on some elements
+    x = rows_under_test()
+    A, S = o.decompose_activations(x, 2)
+    r = x.astype(np.float64) - S[0][:, None].astype(np.float64) * A[0].astype(np.float64)
+    two = (x.astype(F32) - (S[0][:, None] * A[0].astype(F32)).astype(F32)).astype(F32)
+    assert not np.array_equal(two.astype(np.float64), r)
