@@ -90,3 +90,42 @@ def test_attention_msd_argument_errors():
     with pytest.raises(w4.W4Error) as e:
         w4.attn_decode_msd(dev(q), dev(kp), dev(K[1]), dev(K[2]), dev(vp), dev(V[1]), dev(V[2]), 3)  # 8 % 3
     assert e.value.status == -1
+
+
+def _call(qd, kd, vd, Hkv, out, ws, stream=None):
+    return w4.attn_decode_msd(qd, kd[0], kd[1], kd[2], vd[0], vd[1], vd[2], Hkv, out=out, workspace=ws,
+                              stream=stream)
+
+
+def test_attention_graph_replays_between_eager_calls():
+    """Replays of a captured call and eager calls (other queries, same
+    workspace, same stream) alternate; every replay's output equals the eager
+    output of the same query, and so does every eager call's."""
+    require_gpu()
+    B, Hq, Hkv, L = 2, 16, 2, 2048
+    q, K, V, kp, vp = make_cache(990, B, Hq, Hkv, L)
+    q2 = np.random.default_rng(991).standard_normal(q.shape).astype(np.float16)
+    qd, q2d = dev(q), dev(q2)
+    kd, vd = (dev(kp), dev(K[1]), dev(K[2])), (dev(vp), dev(V[1]), dev(V[2]))
+    ws = torch.empty(w4.workspace_bytes(w4.OP_ATTN_MSD, B, Hq, L, 0, 0), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    ref1, ref2, og, o2 = (torch.empty_like(qd) for _ in range(4))
+    announce("attn graph replays")
+    with torch.cuda.stream(s):
+        _call(qd, kd, vd, Hkv, ref1, ws, s)
+        _call(q2d, kd, vd, Hkv, ref2, ws, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _call(qd, kd, vd, Hkv, og, ws, s)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        og.zero_()
+        o2.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+            _call(q2d, kd, vd, Hkv, o2, ws, s)
+        s.synchronize()
+        assert torch.equal(og, ref1)
+        assert torch.equal(o2, ref2)
