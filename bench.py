@@ -446,9 +446,39 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
             gemv_launch(i)
             cur.wait_stream(side)
             w4.residual_correct(x, r_host, idx, y)
+        # the selection and the fp32 correction (which does not read y) on a
+        # second stream beside the GEMV; the correction is added to y after both
+        c = torch.empty((1, N), dtype=torch.float32, device="cuda")
+
+        def overlapped(i):
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                w4.salient_select(x, k, out=idx)
+                w4.residual_correct_f32(x, r_host, idx, c)
+            gemv_launch(i)
+            cur.wait_stream(side)
+            w4.residual_apply(c, y)
         g = graph_of(torch, stream, [lambda i=i: chain(i) for i in range(n_sets)])
         time_replays(torch, stream, g, 1)
         serial_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
+        del g
+        g = graph_of(torch, stream, [lambda i=i: overlapped(i) for i in range(n_sets)])
+        time_replays(torch, stream, g, 1)
+        overlapped_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
+        del g
+
+        def overlapped_one(i):  # the same with selection and correction in one launch
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                w4.salient_correct_f32(x, r_host, k, c, idx=idx)
+            gemv_launch(i)
+            cur.wait_stream(side)
+            w4.residual_apply(c, y)
+        g = graph_of(torch, stream, [lambda i=i: overlapped_one(i) for i in range(n_sets)])
+        time_replays(torch, stream, g, 1)
+        overlapped_one_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
         del g
         g = graph_of(torch, stream, [lambda i=i: forked(i) for i in range(n_sets)])
         time_replays(torch, stream, g, 1)
@@ -458,12 +488,15 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
         time_replays(torch, stream, g, 1)
         fused_us = time_replays(torch, stream, g, 4) * 1e3 / (4 * n_sets)
         del g
-        steps = {"serial": serial_us, "forked": forked_us, "fused": fused_us}
+        steps = {"serial": serial_us, "forked": forked_us, "fused": fused_us, "overlapped": overlapped_us,
+                 "overlapped_one_launch": overlapped_one_us}
         schedule = min(steps, key=steps.get)
         step_us = steps[schedule]
         link = k * N * 2 / (timed["correct_host_us"] * 1e-6) / 1e9
         res.append({"k": k, **timed, "gemv_us": round(gemv_us, 2), "step_serial_us": round(serial_us, 2),
                     "step_forked_us": round(forked_us, 2), "step_fused_us": round(fused_us, 2),
+                    "step_overlapped_us": round(overlapped_us, 2),
+                    "step_overlapped_one_launch_us": round(overlapped_one_us, 2),
                     "step_us": round(step_us, 2), "schedule": schedule,
                     "overhead_frac": round((step_us - gemv_us) / gemv_us, 3),
                     "residual_bytes": k * N * 2, "host_link_GBps": round(link, 2),
@@ -473,7 +506,10 @@ def bench_residual(w4, torch, stream, gemv_launch, n_sets, gemv_us, K, N, ks, re
             "step": "step_serial_us: GEMV, selection and correction one after the other on one stream; "
                     "step_forked_us: the selection on a second stream beside the GEMV, the correction after "
                     "both; step_fused_us: GEMV, then selection and correction in one launch "
-                    "(w4_salient_correct); step_us: the fastest (schedule names it)",
+                    "(w4_salient_correct); step_overlapped_us: the selection and the fp32 correction "
+                    "(w4_residual_correct_f32) on a second stream beside the GEMV, then w4_residual_apply; "
+                    "step_overlapped_one_launch_us: the same with w4_salient_correct_f32 on the second stream; "
+                    "step_us: the fastest (schedule names it)",
             "host_link_peak_GBps": HOST_LINK_PEAK_GBS, "per_k": res}
 
 

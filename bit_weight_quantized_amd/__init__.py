@@ -21,7 +21,8 @@ __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
     "lib", "lib_path", "quantize", "pack", "gemv", "gemv_noalloc", "gemv_plan", "gemm", "gemm_decomp", "gemm_decomp_fixed",
     "gemm_decomp_fixed_fused", "stream_read",
-    "salient_select", "residual_correct", "salient_correct", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
+    "salient_select", "residual_correct", "salient_correct", "residual_correct_f32", "residual_apply",
+    "salient_correct_f32", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
     "workspace_bytes", "nf4_levels", "version",
 ]
 
@@ -77,6 +78,9 @@ def lib():
         L.w4_attn_decode_msd.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_residual_correct.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p]
         L.w4_salient_correct.argtypes = [_p, _i, _i, _i, _p, _i, _p, _p, _p]
+        L.w4_residual_correct_f32.argtypes = [_p, _i, _i, _i, _p, _p, _i, _p, _p]
+        L.w4_residual_apply.argtypes = [_p, _i, _i, _p, _p]
+        L.w4_salient_correct_f32.argtypes = [_p, _i, _i, _i, _p, _i, _p, _p, _p]
         L.w4_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
         L.w4_workspace_bytes.restype = _sz
         L.w4_nf4_levels.argtypes = [_p]
@@ -86,7 +90,8 @@ def lib():
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
         for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemv_noalloc", "w4_gemv_plan", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
-                   "w4_gemm_decomp_fixed_fused", "w4_stream_read", "w4_salient_select", "w4_residual_correct", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
+                   "w4_gemm_decomp_fixed_fused", "w4_stream_read", "w4_salient_select", "w4_residual_correct", "w4_salient_correct",
+                   "w4_residual_correct_f32", "w4_residual_apply", "w4_salient_correct_f32", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
                    "w4_attn_decode_msd",
                    "w4_nf4_levels"):
             getattr(L, fn).restype = _i
@@ -315,6 +320,54 @@ def residual_correct(x, resid, idx, y, *, stream=None):
     k = idx.numel()
     _check("w4_residual_correct", lib().w4_residual_correct(_ptr(x), M, K, N, _ptr(resid), _ptr(idx), k, _ptr(y),
                                                             _stream(stream)))
+    return y
+
+
+def residual_correct_f32(x, resid, idx, c=None, *, N=None, stream=None):
+    """c = x[:, idx] . resid[idx, :] in fp32 (stored, not added; c fp32
+    [M][N], allocated when None); returns c.  With w4.residual_apply(c, y)
+    afterwards, y ends as residual_correct would leave it."""
+    _dev(x, torch.float16, "x")
+    if resid.dtype != torch.float16 or resid.dim() != 2 or not resid.is_contiguous():
+        raise ValueError("resid must be a contiguous fp16 [K][N] tensor")
+    if resid.device.type == "cpu" and not resid.is_pinned():
+        raise ValueError("a host-resident resid must be pinned (pin_memory=True)")
+    M, K = x.shape
+    N = resid.shape[1] if N is None else N
+    c = torch.empty((M, N), dtype=torch.float32, device=x.device) if c is None else c
+    _dev(c, torch.float32, "c")
+    k = idx.numel()
+    _check("w4_residual_correct_f32", lib().w4_residual_correct_f32(_ptr(x), M, K, N, _ptr(resid), _ptr(idx), k,
+                                                                    _ptr(c), _stream(stream)))
+    return c
+
+
+def salient_correct_f32(x, resid, k, c=None, *, idx=None, N=None, stream=None):
+    """salient_select then residual_correct_f32 in one launch; returns (idx,
+    c) with c fp32 [M][N] (allocated when None)."""
+    _dev(x, torch.float16, "x")
+    if resid.dtype != torch.float16 or resid.dim() != 2 or not resid.is_contiguous():
+        raise ValueError("resid must be a contiguous fp16 [K][N] tensor")
+    if resid.device.type == "cpu" and not resid.is_pinned():
+        raise ValueError("a host-resident resid must be pinned (pin_memory=True)")
+    M, K = x.shape
+    N = resid.shape[1] if N is None else N
+    c = torch.empty((M, N), dtype=torch.float32, device=x.device) if c is None else c
+    _dev(c, torch.float32, "c")
+    idx = torch.empty((k,), dtype=torch.int32, device=x.device) if idx is None else idx
+    _check("w4_salient_correct_f32", lib().w4_salient_correct_f32(_ptr(x), M, K, N, _ptr(resid), k, _ptr(idx),
+                                                                  _ptr(c), _stream(stream)))
+    return idx, c
+
+
+def residual_apply(c, y, *, stream=None):
+    """y = fp16(y + c) in place (c from residual_correct_f32)."""
+    _dev(c, torch.float32, "c")
+    _dev(y, torch.float16, "y")
+    if c.shape != y.shape or y.dim() != 2:
+        raise ValueError("c and y must both be [M][N]")
+    M, N = y.shape
+    _check("w4_residual_apply", lib().w4_residual_apply(_ptr(c), M, N, _ptr(y), _stream(stream)))
     return y
 
 

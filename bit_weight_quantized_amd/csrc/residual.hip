@@ -146,9 +146,11 @@ __global__ __launch_bounds__(kSelThreads) void salient_select_kernel(const uint1
 constexpr int kCorrWaves = 8;
 constexpr int kCorrBatch = 4;
 
-template <int CPT, int MMAX>
+// F32: the correction is stored to c (fp32 [M][N]) instead of added to y.
+template <int CPT, int MMAX, bool F32>
 __device__ void correct_columns(const uint16_t* __restrict__ x, int M, int K, int N, const uint16_t* __restrict__ resid,
-                                const int32_t* idx, int k, uint16_t* __restrict__ y, float* part) {
+                                const int32_t* idx, int k, uint16_t* __restrict__ y, float* __restrict__ c,
+                                float* part) {
   // part: LDS [kCorrWaves][MMAX][64 * CPT]
   constexpr int kCols = 64 * CPT;
   const int lane = threadIdx.x % kWave;
@@ -209,26 +211,46 @@ __device__ void correct_columns(const uint16_t* __restrict__ x, int M, int K, in
     float s = 0.f;
     for (int ww = 0; ww < kCorrWaves; ++ww) s += part[(ww * MMAX + m) * kCols + col];
     const size_t at = (size_t)m * N + nn;
-    y[at] = float_to_half_bits(half_bits_to_float(y[at]) + s);
+    if constexpr (F32) c[at] = s;
+    else y[at] = float_to_half_bits(half_bits_to_float(y[at]) + s);
   }
 }
 
-template <int CPT, int MMAX>
+template <int CPT, int MMAX, bool F32>
 __global__ __launch_bounds__(kCorrWaves * kWave) void residual_correct_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint16_t* __restrict__ resid,
-    const int32_t* __restrict__ idx, int k, uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ idx, int k, uint16_t* __restrict__ y, float* __restrict__ c) {
   extern __shared__ float part[];  // [kCorrWaves][MMAX][64 * CPT]
-  correct_columns<CPT, MMAX>(x, M, K, N, resid, idx, k, y, part);
+  correct_columns<CPT, MMAX, F32>(x, M, K, N, resid, idx, k, y, c, part);
+}
+
+// y[i] = fp16(y[i] + c[i]) for i < n (n % 8 == 0), eight elements per thread:
+// the same rounding as the correction that adds to y itself.
+__global__ __launch_bounds__(256) void residual_apply_kernel(const float* __restrict__ c, size_t n,
+                                                             uint16_t* __restrict__ y) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const u32x4 yv = *reinterpret_cast<const u32x4*>(y + i);
+  const float4 c0 = *reinterpret_cast<const float4*>(c + i), c1 = *reinterpret_cast<const float4*>(c + i + 4);
+  const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint16_t lo = float_to_half_bits(half_bits_to_float((uint16_t)(yv[j] & 0xFFFFu)) + cv[2 * j]);
+    const uint16_t hi = float_to_half_bits(half_bits_to_float((uint16_t)(yv[j] >> 16)) + cv[2 * j + 1]);
+    out[j] = (uint32_t)lo | ((uint32_t)hi << 16);
+  }
+  *reinterpret_cast<u32x4*>(y + i) = out;
 }
 
 // Selection and correction in one launch: every workgroup picks the channels
 // itself (the same ones: the selection is deterministic) into LDS, workgroup 0
 // also writes them to idx, and each then corrects its columns.  The dynamic
 // LDS holds the selection keys first and the correction's partial sums after.
-template <int CPT, int MMAX>
+template <int CPT, int MMAX, bool F32>
 __global__ __launch_bounds__(kCorrWaves * kWave) void salient_correct_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint16_t* __restrict__ resid, int k,
-    int32_t* __restrict__ idx, uint16_t* __restrict__ y) {
+    int32_t* __restrict__ idx, uint16_t* __restrict__ y, float* __restrict__ c) {
   extern __shared__ uint32_t dyn[];  // keys[K], then part[kCorrWaves][MMAX][64 * CPT]
   __shared__ SelLds sl;
   __shared__ int32_t picked[kSelMaxTop];
@@ -236,20 +258,20 @@ __global__ __launch_bounds__(kCorrWaves * kWave) void salient_correct_kernel(
   __syncthreads();
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < k; i += kCorrWaves * kWave) idx[i] = picked[i];
-  correct_columns<CPT, MMAX>(x, M, K, N, resid, picked, k, y, reinterpret_cast<float*>(dyn));
+  correct_columns<CPT, MMAX, F32>(x, M, K, N, resid, picked, k, y, c, reinterpret_cast<float*>(dyn));
 }
 
-template <int CPT, int MMAX>
+template <int CPT, int MMAX, bool F32>
 int launch_correct_t(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx, int k,
-                     uint16_t* y, hipStream_t s) {
+                     uint16_t* y, float* c, hipStream_t s) {
   const int lds = kCorrWaves * MMAX * 64 * CPT * (int)sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(&residual_correct_kernel<CPT, MMAX>);
-  const int st = allow_dynamic_lds(fn, lds, "w4_residual_correct");
+  const void* fn = reinterpret_cast<const void*>(&residual_correct_kernel<CPT, MMAX, F32>);
+  const int st = allow_dynamic_lds(fn, lds, F32 ? "w4_residual_correct_f32" : "w4_residual_correct");
   if (st != 0) return st;
   const int blocks = (N + 64 * CPT - 1) / (64 * CPT);
-  hipLaunchKernelGGL((residual_correct_kernel<CPT, MMAX>), dim3(blocks), dim3(kCorrWaves * kWave), lds, s, x, M, K,
-                     N, resid, idx, k, y);
-  return check_launch("residual_correct");
+  hipLaunchKernelGGL((residual_correct_kernel<CPT, MMAX, F32>), dim3(blocks), dim3(kCorrWaves * kWave), lds, s, x, M,
+                     K, N, resid, idx, k, y, c);
+  return check_launch(F32 ? "residual_correct_f32" : "residual_correct");
 }
 
 }  // namespace
@@ -265,27 +287,46 @@ int launch_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, 
 
 int launch_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
                             int k, uint16_t* y, hipStream_t s) {
-  if (M <= 8) return launch_correct_t<8, 8>(x, M, K, N, resid, idx, k, y, s);
-  return launch_correct_t<2, 32>(x, M, K, N, resid, idx, k, y, s);
+  if (M <= 8) return launch_correct_t<8, 8, false>(x, M, K, N, resid, idx, k, y, nullptr, s);
+  return launch_correct_t<2, 32, false>(x, M, K, N, resid, idx, k, y, nullptr, s);
 }
 
-template <int CPT, int MMAX>
+int launch_residual_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
+                                int k, float* c, hipStream_t s) {
+  if (M <= 8) return launch_correct_t<8, 8, true>(x, M, K, N, resid, idx, k, nullptr, c, s);
+  return launch_correct_t<2, 32, true>(x, M, K, N, resid, idx, k, nullptr, c, s);
+}
+
+int launch_residual_apply(const float* c, int M, int N, uint16_t* y, hipStream_t s) {
+  const size_t n = (size_t)M * N;
+  const unsigned blocks = (unsigned)((n / 8 + 255) / 256);
+  hipLaunchKernelGGL(residual_apply_kernel, dim3(blocks), dim3(256), 0, s, c, n, y);
+  return check_launch("residual_apply");
+}
+
+template <int CPT, int MMAX, bool F32>
 int launch_salient_correct_t(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
-                             uint16_t* y, hipStream_t s) {
+                             uint16_t* y, float* c, hipStream_t s) {
   const int lds = std::max(K * (int)sizeof(uint32_t), kCorrWaves * MMAX * 64 * CPT * (int)sizeof(float));
-  const void* fn = reinterpret_cast<const void*>(&salient_correct_kernel<CPT, MMAX>);
-  const int st = allow_dynamic_lds(fn, lds, "w4_salient_correct");
+  const void* fn = reinterpret_cast<const void*>(&salient_correct_kernel<CPT, MMAX, F32>);
+  const int st = allow_dynamic_lds(fn, lds, F32 ? "w4_salient_correct_f32" : "w4_salient_correct");
   if (st != 0) return st;
   const int blocks = (N + 64 * CPT - 1) / (64 * CPT);
-  hipLaunchKernelGGL((salient_correct_kernel<CPT, MMAX>), dim3(blocks), dim3(kCorrWaves * kWave), lds, s, x, M, K, N,
-                     resid, k, idx, y);
-  return check_launch("salient_correct");
+  hipLaunchKernelGGL((salient_correct_kernel<CPT, MMAX, F32>), dim3(blocks), dim3(kCorrWaves * kWave), lds, s, x, M,
+                     K, N, resid, k, idx, y, c);
+  return check_launch(F32 ? "salient_correct_f32" : "salient_correct");
 }
 
 int launch_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
                            uint16_t* y, hipStream_t s) {
-  if (M <= 8) return launch_salient_correct_t<8, 8>(x, M, K, N, resid, k, idx, y, s);
-  return launch_salient_correct_t<2, 32>(x, M, K, N, resid, k, idx, y, s);
+  if (M <= 8) return launch_salient_correct_t<8, 8, false>(x, M, K, N, resid, k, idx, y, nullptr, s);
+  return launch_salient_correct_t<2, 32, false>(x, M, K, N, resid, k, idx, y, nullptr, s);
+}
+
+int launch_salient_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
+                               float* c, hipStream_t s) {
+  if (M <= 8) return launch_salient_correct_t<8, 8, true>(x, M, K, N, resid, k, idx, nullptr, c, s);
+  return launch_salient_correct_t<2, 32, true>(x, M, K, N, resid, k, idx, nullptr, c, s);
 }
 
 }  // namespace w4

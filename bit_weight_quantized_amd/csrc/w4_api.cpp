@@ -321,6 +321,34 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
   return launch_residual_correct(x, M, K, N, static_cast<const uint16_t*>(dev), idx, k, y, (hipStream_t)stream);
 }
 
+int w4_residual_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
+                            int k, float* c, void* stream) {
+  g_last_error[0] = '\0';
+  if (M < 1 || M > 32 || K < 1 || N < 1 || N % 8)
+    return fail(W4_EINVAL,
+                "w4_residual_correct_f32: need 1 <= M <= 32, K >= 1, N >= 1 with N %% 8 == 0 (got M=%d K=%d N=%d)", M,
+                K, N);
+  if (k < 0) return fail(W4_EINVAL, "w4_residual_correct_f32: k must be >= 0 (got %d)", k);
+  if (!x || !c || !resid || (k > 0 && !idx)) return fail(W4_EINVAL, "w4_residual_correct_f32: null operand");
+  if (!aligned16(resid) || !aligned16(c) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
+      (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return fail(W4_EINVAL, "w4_residual_correct_f32: resid and c must be 16-byte aligned, x 2-byte, idx 4-byte");
+  const void* dev = residual_device_address(resid);
+  if (!dev)
+    return fail(W4_EINVAL,
+                "w4_residual_correct_f32: resid must be pinned host memory (hipHostMalloc) or device memory");
+  return launch_residual_correct_f32(x, M, K, N, static_cast<const uint16_t*>(dev), idx, k, c, (hipStream_t)stream);
+}
+
+int w4_residual_apply(const float* c, int M, int N, uint16_t* y, void* stream) {
+  g_last_error[0] = '\0';
+  if (M < 1 || N < 1 || N % 8)
+    return fail(W4_EINVAL, "w4_residual_apply: need M >= 1, N >= 1 with N %% 8 == 0 (got M=%d N=%d)", M, N);
+  if (!c || !y) return fail(W4_EINVAL, "w4_residual_apply: null operand");
+  if (!aligned16(c) || !aligned16(y)) return fail(W4_EINVAL, "w4_residual_apply: c and y must be 16-byte aligned");
+  return launch_residual_apply(c, M, N, y, (hipStream_t)stream);
+}
+
 int w4_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
                        uint16_t* y, void* stream) {
   g_last_error[0] = '\0';
@@ -339,6 +367,31 @@ int w4_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* r
     return fail(W4_EINVAL, "w4_salient_correct: resid must be pinned host memory (hipHostMalloc) or device memory");
   if (k == 0) return W4_OK;
   return launch_salient_correct(x, M, K, N, static_cast<const uint16_t*>(dev), k, idx, y, (hipStream_t)stream);
+}
+
+int w4_salient_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
+                           float* c, void* stream) {
+  g_last_error[0] = '\0';
+  if (M < 1 || M > 32 || K < 1 || K > kSelMaxK || N < 1 || N % 8)
+    return fail(W4_EINVAL,
+                "w4_salient_correct_f32: need 1 <= M <= 32, 1 <= K <= %d, N >= 1 with N %% 8 == 0 (got M=%d K=%d "
+                "N=%d)",
+                kSelMaxK, M, K, N);
+  if (k < 0 || k > K || k > kSelMaxTop)
+    return fail(W4_EINVAL, "w4_salient_correct_f32: k must be in [0, min(K, %d)] (got %d)", kSelMaxTop, k);
+  if (!x || !c || !resid || (k > 0 && !idx)) return fail(W4_EINVAL, "w4_salient_correct_f32: null operand");
+  if (!aligned16(resid) || !aligned16(c) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
+      (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return fail(W4_EINVAL, "w4_salient_correct_f32: resid and c must be 16-byte aligned, x 2-byte, idx 4-byte");
+  const void* dev = residual_device_address(resid);
+  if (!dev)
+    return fail(W4_EINVAL,
+                "w4_salient_correct_f32: resid must be pinned host memory (hipHostMalloc) or device memory");
+  // k = 0: no selection (it needs k >= 1), the correction kernel writes the zeros
+  if (k == 0)
+    return launch_residual_correct_f32(x, M, K, N, static_cast<const uint16_t*>(dev), nullptr, 0, c,
+                                       (hipStream_t)stream);
+  return launch_salient_correct_f32(x, M, K, N, static_cast<const uint16_t*>(dev), k, idx, c, (hipStream_t)stream);
 }
 
 int w4_quantize_mx(const float* wt, int K, int N, uint8_t* codes, uint8_t* scale, void* stream) {

@@ -129,6 +129,11 @@ constexpr int kSelMaxTop = 1024;
 int launch_salient_select(const uint16_t* x, int M, int K, int k, int32_t* idx, hipStream_t s);
 int launch_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
                             int k, uint16_t* y, hipStream_t s);
+int launch_residual_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid, const int32_t* idx,
+                                int k, float* c, hipStream_t s);
+int launch_residual_apply(const float* c, int M, int N, uint16_t* y, hipStream_t s);
+int launch_salient_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
+                               float* c, hipStream_t s);
 int launch_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k, int32_t* idx,
                            uint16_t* y, hipStream_t s);
 

@@ -397,6 +397,28 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
                         const int32_t* idx, int k, uint16_t* y, void* stream);
 
 /*
+ * w4_residual_correct_f32 -- the correction of w4_residual_correct, stored
+ * instead of added: c[m,n] = sum_j x[m,idx[j]] * R[idx[j],n] in fp32 (every
+ * element of c is written; k = 0 writes zeros).  It does not read the
+ * product, so it can run on a second stream beside the GEMV that writes y
+ * ([DecDEC] Abstract: the residual fetch is meant to add little to the
+ * step's time); w4_residual_apply then adds c to y.  The two calls leave y
+ * bit-identical to w4_residual_correct on the same y.
+ *
+ * x, resid, idx, M, K, N, k: as for w4_residual_correct (k = 0 still
+ * launches).  c: fp32 [M][N] device, 16-byte aligned, written.
+ */
+int w4_residual_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid,
+                            const int32_t* idx, int k, float* c, void* stream);
+
+/*
+ * w4_residual_apply -- y[m,n] = fp16(y[m,n] + c[m,n]) for a correction from
+ * w4_residual_correct_f32.  c: fp32 [M][N], y: fp16 [M][N], both device and
+ * 16-byte aligned; N % 8 == 0.
+ */
+int w4_residual_apply(const float* c, int M, int N, uint16_t* y, void* stream);
+
+/*
  * w4_salient_correct -- w4_salient_select followed by w4_residual_correct in
  * one launch ([DecDEC] Abstract: salient channels chosen anew at every step,
  * their residual rows fetched from host memory).  The picks and y are
@@ -411,6 +433,17 @@ int w4_residual_correct(const uint16_t* x, int M, int K, int N, const uint16_t* 
  */
 int w4_salient_correct(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k,
                        int32_t* idx, uint16_t* y, void* stream);
+
+/*
+ * w4_salient_correct_f32 -- w4_salient_select followed by
+ * w4_residual_correct_f32 in one launch: the picks go to idx and the
+ * correction is stored to c (fp32 [M][N], every element written; k = 0
+ * writes zeros and still launches), for w4_residual_apply.  Arguments and
+ * limits as for w4_salient_correct, with c (device, 16-byte aligned) in place
+ * of y.
+ */
+int w4_salient_correct_f32(const uint16_t* x, int M, int K, int N, const uint16_t* resid, int k,
+                           int32_t* idx, float* c, void* stream);
 
 /*
  * w4_workspace_bytes -- bytes of workspace an entry point needs for the given

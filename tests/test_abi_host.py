@@ -194,6 +194,38 @@ def test_residual_argument_errors(L):
     assert sc(idx=None) == W4_EINVAL
     assert sc(y=MISALIGNED) == W4_EINVAL
     assert b"w4_salient_correct" in L.w4_last_error()
+    # the correction stored in fp32, and its application to y
+
+    def c32(**kw):
+        a = {**args, **kw}
+        return L.w4_residual_correct_f32(a["x"], a["M"], a["K"], a["N"], a["r"], a["idx"], a["k"], a["y"], None)
+    assert c32(M=0) == W4_EINVAL
+    assert c32(M=33) == W4_EINVAL
+    assert c32(N=12) == W4_EINVAL
+    assert c32(k=-1) == W4_EINVAL
+    assert c32(y=None) == W4_EINVAL
+    assert c32(idx=None) == W4_EINVAL
+    assert c32(y=MISALIGNED) == W4_EINVAL
+    assert b"w4_residual_correct_f32" in L.w4_last_error()
+    assert L.w4_residual_apply(FAKE, 0, 64, FAKE, None) == W4_EINVAL
+    assert L.w4_residual_apply(FAKE, 1, 12, FAKE, None) == W4_EINVAL
+    assert L.w4_residual_apply(None, 1, 64, FAKE, None) == W4_EINVAL
+    assert L.w4_residual_apply(FAKE, 1, 64, MISALIGNED, None) == W4_EINVAL
+    assert b"w4_residual_apply" in L.w4_last_error()
+
+    def sc32(**kw):
+        a = {**args, **kw}
+        return L.w4_salient_correct_f32(a["x"], a["M"], a["K"], a["N"], a["r"], a["k"], a["idx"], a["y"], None)
+    assert sc32(M=33) == W4_EINVAL
+    assert sc32(K=32769) == W4_EINVAL
+    assert sc32(N=12) == W4_EINVAL
+    assert sc32(k=65) == W4_EINVAL  # k > K
+    assert sc32(K=4096, k=1025) == W4_EINVAL
+    assert sc32(k=-1) == W4_EINVAL
+    assert sc32(y=None) == W4_EINVAL
+    assert sc32(idx=None) == W4_EINVAL
+    assert sc32(y=MISALIGNED) == W4_EINVAL
+    assert b"w4_salient_correct_f32" in L.w4_last_error()
 
 
 def test_mx_argument_errors(L):

@@ -174,3 +174,115 @@ def test_salient_correct_equals_select_then_correct(where, M, K, N, k):
     assert np.array_equal(host(idx_one), idx_ref)
     ref = host(y0).astype(np.float64) + o.residual_correction(x, R, idx_ref)
     assert row_rel_l2(host(y_one), ref) <= TOL_ROW_REL_L2
+
+
+@pytest.mark.parametrize("where", ["pinned", "device"])
+@pytest.mark.parametrize("M,K,N,k", [(1, 1024, 256, 11), (5, 2048, 1040, 40), (9, 1024, 520, 33),
+                                     (32, 2048, 2048, 100), (1, 8192, 8192, 82), (2, 256, 64, 0)])
+def test_correction_f32_then_apply_equals_correction(where, M, K, N, k):
+    """The correction stored in fp32 matches the oracle (every element
+    written: c starts as NaN; k = 0 gives zeros), and adding it to y leaves
+    the same bits as the correction that adds to y itself."""
+    require_gpu()
+    x, _, _, _, _, R = residual_case(660 + M, M, K, N)
+    idx = o.salient_channels(x, k)
+    r = pinned(R) if where == "pinned" else dev(R)
+    xd, idxd = dev(x), dev(idx)
+    y0 = torch.randn((M, N), device="cuda").half()
+    y_one, y_two = y0.clone(), y0.clone()
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    announce("residual correct f32 + apply", dict(where=where, M=M, K=K, N=N, k=k))
+    w4.residual_correct(xd, r, idxd, y_one)
+    w4.residual_correct_f32(xd, r, idxd, c)
+    w4.residual_apply(c, y_two)
+    torch.cuda.synchronize()
+    ref = o.residual_correction(x, R, idx)
+    if k == 0:
+        assert torch.count_nonzero(c).item() == 0
+    else:
+        assert row_rel_l2(host(c), ref) <= TOL_ROW_REL_L2
+    assert torch.equal(y_two, y_one)
+
+
+@pytest.mark.parametrize("where", ["pinned", "device"])
+@pytest.mark.parametrize("M,K,N,k", [(1, 1024, 256, 11), (9, 1024, 520, 33), (32, 2048, 2048, 100),
+                                     (1, 8192, 8192, 82), (2, 32768, 1024, 1024), (3, 128, 8, 1), (4, 128, 64, 0)])
+def test_salient_correct_f32_equals_select_then_correct_f32(where, M, K, N, k):
+    """The one-launch selection with the fp32 correction picks the same
+    channels and stores the same c bits as the two calls (k = 0: zeros)."""
+    require_gpu()
+    x, _, _, _, _, R = residual_case(680 + M, M, K, N)
+    r = pinned(R) if where == "pinned" else dev(R)
+    xd = dev(x)
+    announce("salient correct f32", dict(where=where, M=M, K=K, N=N, k=k))
+    idx_two = w4.salient_select(xd, k)
+    c_two = w4.residual_correct_f32(xd, r, idx_two, N=N)
+    idx_one = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+    c_one = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    w4.salient_correct_f32(xd, r, k, c_one, idx=idx_one)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_one, idx_two)
+    assert torch.equal(c_one, c_two)
+    assert np.array_equal(host(idx_one), o.salient_channels(x, k))
+    if k == 0:
+        assert torch.count_nonzero(c_one).item() == 0
+
+
+@pytest.mark.parametrize("side_launches", [2, 1])
+def test_overlapped_step_equals_serial_step(side_launches):
+    """The decode step with the residual work beside the GEMV (selection and
+    fp32 correction on a second stream, as two launches or one, then the
+    apply after both) gives the serial step's picks and output bits: eagerly,
+    and over graph replays of the forked schedule."""
+    require_gpu()
+    M, K, N, k, G = 1, 8192, 8192, 82, 128
+    w = wl.make_weight(670, 0, N, K)
+    x = wl.make_activations(670, 0, M, K, outliers=True)
+    R = (np.random.default_rng(671).standard_normal((K, N), dtype=np.float32) * 1e-3).astype(np.float16)
+    announce("overlapped residual step", dict(M=M, K=K, N=N, k=k, side_launches=side_launches))
+    codes, scale, zero = w4.quantize(dev(w), G, w4.INT4_ASYM)
+    packed = w4.pack(codes)
+    xd, r = dev(x), pinned(R)
+    y_ser = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    idx_ser = torch.empty((k,), dtype=torch.int32, device="cuda")
+    w4.gemv(xd, packed, scale, zero, G, w4.INT4_ASYM, out=y_ser)
+    w4.salient_select(xd, k, out=idx_ser)
+    w4.residual_correct(xd, r, idx_ser, y_ser)
+    torch.cuda.synchronize()
+
+    y_ovl = torch.empty_like(y_ser)
+    idx_ovl = torch.empty_like(idx_ser)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def step():
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            if side_launches == 2:
+                w4.salient_select(xd, k, out=idx_ovl, stream=side)
+                w4.residual_correct_f32(xd, r, idx_ovl, c, stream=side)
+            else:
+                w4.salient_correct_f32(xd, r, k, c, idx=idx_ovl, stream=side)
+        w4.gemv(xd, packed, scale, zero, G, w4.INT4_ASYM, out=y_ovl, stream=main)
+        main.wait_stream(side)
+        w4.residual_apply(c, y_ovl, stream=main)
+
+    with torch.cuda.stream(main):
+        step()
+    torch.cuda.synchronize()
+    assert torch.equal(idx_ovl, idx_ser)
+    assert torch.equal(y_ovl, y_ser)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=main):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y_ovl.zero_()
+        idx_ovl.zero_()
+        c.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(main):
+            g.replay()
+        main.synchronize()
+        assert torch.equal(idx_ovl, idx_ser)
+        assert torch.equal(y_ovl, y_ser)
