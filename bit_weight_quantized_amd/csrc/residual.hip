@@ -36,7 +36,7 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // and four scalars; idx (LDS or device memory) receives the k channels.
 struct SelLds {
   uint32_t hist[256];
-  uint32_t top[kSelMaxTop];
+  __align__(16) uint32_t top[kSelMaxTop];
   uint32_t prefix, remaining, count, done;
 };
 
@@ -52,10 +52,54 @@ __device__ void select_salient(const uint16_t* __restrict__ x, int M, int K, int
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
 
-  for (int c = tid; c < K; c += NT) {
-    uint32_t s = 0;
-    for (int m = 0; m < M; ++m) s = max(s, (uint32_t)(x[(size_t)m * K + c] & 0x7FFFu));
-    keys[c] = (s << kIdxBits) | (uint32_t)((1 << kIdxBits) - 1 - c);
+  // keys: thread t scores channels 8 t .. 8 t + 7 of each chunk of 8 NT,
+  // with the loads of four rows in flight at a time (16-byte loads when x
+  // and K allow them; otherwise eight 2-byte loads, the index clamped to the
+  // row so that none is conditional)
+  auto store_keys = [&](int c0, const uint32_t (&mx)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c0 + e < K) keys[c0 + e] = (mx[e] << kIdxBits) | (uint32_t)((1 << kIdxBits) - 1 - (c0 + e));
+  };
+  auto fold = [](uint32_t (&mx)[8], const u32x4& v) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx[e] = max(mx[e], (v[e / 2] >> (16 * (e % 2))) & 0x7FFFu);
+  };
+  if ((reinterpret_cast<uintptr_t>(x) & 15u) == 0 && K % 8 == 0) {
+    for (int c0 = 8 * tid; c0 < K; c0 += 8 * NT) {
+      uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int m0 = 0; m0 < M; m0 += 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = m0 + u < M ? *reinterpret_cast<const u32x4*>(x + (size_t)(m0 + u) * K + c0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fold(mx, v[u]);
+      }
+      store_keys(c0, mx);
+    }
+  } else {
+    for (int c0 = 8 * tid; c0 < K; c0 += 8 * NT) {
+      uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int m0 = 0; m0 < M; m0 += 4) {
+        uint16_t h[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint16_t* row = x + (size_t)min(m0 + u, M - 1) * K;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[u][e] = row[min(c0 + e, K - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          u32x4 v{0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (m0 + u < M && c0 + e < K) v[e / 2] |= (uint32_t)h[u][e] << (16 * (e % 2));
+          fold(mx, v);
+        }
+      }
+      store_keys(c0, mx);
+    }
   }
   if (tid == 0) {
     s_prefix = 0;
@@ -119,12 +163,24 @@ __device__ void select_salient(const uint16_t* __restrict__ x, int M, int K, int
       if (sel) top[base + lanes_below(b)] = key;
     }
   }
+  // zeros after the k keys up to a multiple of 8 (every key is at least 1:
+  // its low bits are 2^17 - 1 - c with c < 2^17), so the rank loop below
+  // reads whole 16-byte pieces
+  const int k8 = (k + 7) & ~7;  // <= kSelMaxTop
+  if (tid < k8 - k) top[k + tid] = 0u;
   __syncthreads();
-  // rank of each gathered key = number of larger ones (keys are distinct)
+  // rank of each gathered key = number of larger ones (keys are distinct);
+  // the reads are the same for every lane (broadcast), eight keys per step
   for (int i = tid; i < k; i += NT) {
     const uint32_t key = top[i];
     int r = 0;
-    for (int j = 0; j < k; ++j) r += top[j] > key ? 1 : 0;
+#pragma unroll 4
+    for (int j = 0; j < k8; j += 8) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(top + j);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(top + j + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r += (a[e] > key ? 1 : 0) + (b[e] > key ? 1 : 0);
+    }
     idx[r] = (1 << kIdxBits) - 1 - (int)(key & ((1u << kIdxBits) - 1));
   }
 }
