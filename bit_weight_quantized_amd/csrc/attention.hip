@@ -37,32 +37,41 @@ __device__ __forceinline__ i32x4 mfma_i8_16x16x64(u32x4 a, u32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
 }
 
+// How a row reduction combines: a float maximum, a sum, or the maximum of
+// non-negative floats taken on their bits (an integer maximum orders them
+// like the values and, unlike the float one, needs no NaN canonicalisation,
+// so the DPP move folds into it as it does into the sum).
+enum RowOp { kRowMax, kRowSum, kRowMaxNonNeg };
+
 // all-reduce over the 16 lanes of a DPP row (the lanes holding one row group
 // of a matrix-core output): swap within pairs and quads, then the row's
-// half-mirror (lane i with 7 - i) and mirror (lane i with 15 - i)
-template <bool MAX>
+// half-mirror (lane i with 7 - i) and mirror (lane i with 15 - i).  Every
+// lane's source is in its row, so bound_ctrl changes nothing; it lets the
+// compiler fold the move into the add or integer max (one instruction a
+// step).
+template <RowOp OP>
 __device__ __forceinline__ float row16(float v) {
-  auto step = [](float x, int ctrl) {
-    int y;
+  auto step = [](int x, int ctrl) {
     switch (ctrl) {  // the control must be a constant
       case 0:
-        y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
-        break;
+        return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
       case 1:
-        y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
-        break;
+        return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
       case 2:
-        y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false);  // half mirror
-        break;
+        return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);  // half mirror
       default:
-        y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false);  // mirror
+        return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);  // mirror
     }
-    return __builtin_bit_cast(float, y);
   };
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const float o = step(v, c);
-    v = MAX ? fmaxf(v, o) : v + o;
+    const int o = step(__builtin_bit_cast(int, v), c);
+    if constexpr (OP == kRowMaxNonNeg)
+      v = __builtin_bit_cast(float, max(__builtin_bit_cast(uint32_t, v), (uint32_t)o));
+    else if constexpr (OP == kRowSum)
+      v = v + __builtin_bit_cast(float, o);
+    else
+      v = fmaxf(v, __builtin_bit_cast(float, o));
   }
   return v;
 }
@@ -79,7 +88,7 @@ __device__ __forceinline__ void reduce_rows(float (&v)[NV][4], float* red, int w
 #pragma unroll
   for (int a = 0; a < NV; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[a][i] = ((MAXMASK >> a) & 1) ? row16<true>(v[a][i]) : row16<false>(v[a][i]);
+    for (int i = 0; i < 4; ++i) v[a][i] = ((MAXMASK >> a) & 1) ? row16<kRowMax>(v[a][i]) : row16<kRowSum>(v[a][i]);
   if (lane % 16 == 0)
 #pragma unroll
     for (int a = 0; a < NV; ++a)
@@ -378,13 +387,14 @@ __device__ __forceinline__ void swap_halves(int& a, int& b) {
 
 // reduction over the 32 lanes that hold the same heads: the 16 lanes of a
 // row group, then lane l with lane l ^ 32
-template <bool MAX>
+template <RowOp OP>
 __device__ __forceinline__ float row32(float v) {
-  v = row16<MAX>(v);
+  v = row16<OP>(v);
   int a = __builtin_bit_cast(int, v), b = a;
   swap_halves(a, b);  // a: lanes 0-31 of v on both halves, b: lanes 32-63
+  if constexpr (OP == kRowMaxNonNeg) return __builtin_bit_cast(float, max((uint32_t)a, (uint32_t)b));
   const float x = __builtin_bit_cast(float, a), y = __builtin_bit_cast(float, b);
-  return MAX ? fmaxf(x, y) : x + y;
+  return OP == kRowMax ? fmaxf(x, y) : x + y;
 }
 
 // byte offset of chunk position t in the int8 operand order: per 64
@@ -425,115 +435,118 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
     for (int np = 0; np < 4; ++np) O[np][i] = 0.f;
   }
 
-  if (chunk < L / kChunk) {  // wave-uniform
-    const size_t tok0 = bh * L + (size_t)chunk * kChunk;
-    // ---- this chunk's 16 key tiles, and the scales and zero points of the
-    // tokens the lane holds after the swaps (token ln of tile 2 p + hi)
-    u32x4 T[16];
-    const uint8_t* kbase = kp + (bh * (size_t)(L / 16) + (size_t)chunk * 16) * 1024 + 16 * lane;
+  const bool has_chunk = chunk < L / kChunk;  // wave-uniform
+  const size_t tok0 = bh * L + (size_t)chunk * kChunk;
+  // Vector loads return in the order they were issued (per wave, and
+  // through the CU's memory pipeline), so a wait also waits for the loads
+  // issued before: the loads go out in the order of first use.  First the
+  // queries the split below needs, then the key scales and zero points and
+  // the chunk's 16 key tiles (the scores need both); the value side below
+  // likewise.
+  const int gh = 2 * w + lane / 32, d0 = 4 * (lane % 32);  // this lane's head and dimensions in the split
+  u32x2 xq = {0, 0};
+  if (gh < G) xq = *reinterpret_cast<const u32x2*>(qh + (size_t)(qrow0 + gh) * kHeadDim + d0);
+  // the scales and zero points of the tokens the lane holds after the swaps
+  // (token ln of tile 2 p + hi), each in a register of its own (two in one
+  // register would make the wave wait for them here), and the 16 key tiles.
+  // A wave without a chunk (at the end of a row whose chunk count is not a
+  // multiple of 4) loads chunk 0 instead and ignores it: no branch between
+  // these loads and the split, which would make the split wait for them all.
+  const size_t ktok0 = has_chunk ? tok0 : bh * L;
+  uint32_t zk[8], sk[8];
+  u32x4 T[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) T[t] = *reinterpret_cast<const u32x4*>(kbase + (size_t)t * 1024);
-    uint16_t zk[8], sk[8];
+  for (int pp = 0; pp < 8; ++pp) {
+    zk[pp] = kz[ktok0 + 16 * (2 * pp + hi) + ln];
+    sk[pp] = ks[ktok0 + 16 * (2 * pp + hi) + ln];
+  }
+  const uint8_t* kbase = kp + (bh * (size_t)(L / 16) + (size_t)(has_chunk ? chunk : 0) * 16) * 1024 + 16 * lane;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) T[t] = *reinterpret_cast<const u32x4*>(kbase + (size_t)t * 1024);
+  __builtin_amdgcn_sched_barrier(0);  // the key loads go out before the split
+
+  // ---- the group's queries split into two int8 slices with the decisions
+  // of the decomposition kernel, taken in fp32 (per head: s_1 = fp32(max|q| /
+  // 127), A_1 = rint(q / s_1), r = q - s_1 A_1, s_2 = fp32(max|r| / 127),
+  // A_2 = rint(r / s_2)), while the key loads are in flight.  The workgroup's
+  // four waves share one split: wave w takes heads 2 w and 2 w + 1, 32 lanes
+  // per head and 4 dimensions per lane, and the codes go to qop (slice 1 of
+  // head g in row g, slice 2 in row 8 + g, operand order), from which every
+  // wave reads its stacked A operands: row ln = slice ln / 8 of head ln mod 8.
+  __shared__ __align__(16) int8_t qop[16][kHeadDim];
+  __shared__ float qscale[2][8];
+  {
+    float xf[4];
+    uint32_t mag = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      xf[2 * i] = half_bits_to_float((uint16_t)(xq[i] & 0xFFFFu));
+      xf[2 * i + 1] = half_bits_to_float((uint16_t)(xq[i] >> 16));
+      const uint32_t m2 = xq[i] & 0x7FFF7FFFu;  // magnitude bits order like the magnitudes
+      mag = max(mag, max(m2 & 0xFFFFu, m2 >> 16));
+    }
+    auto max32 = [](uint32_t v) {  // over the 32 lanes of a head
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
+      return v;
+    };
+    auto store4 = [&](int row, const float (&q)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qop[row][operand_byte(d0 + e)] = (int8_t)(int)fminf(fmaxf(q[e], -127.f), 127.f);
+    };
+    mag = max32(mag);
+    const double s1 = (double)(float)((double)half_bits_to_float((uint16_t)mag) / 127.0);
+    const float s1f = (float)s1, inv1 = s1 != 0.0 ? (float)(1.0 / s1) : 0.f;
+    float q[4];
+    bool near = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = rint127_fast(xf[e], inv1, near);
+    if (near) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = decide127((double)xf[e], s1, inv1);
+    }
+    store4(gh, q);  // a head beyond G has x = 0: zero codes and scales
+    // r = x - s_1 A_1 is exact in fp32.  For A_1 = 0 it is x.  Otherwise
+    // |x| >= s_1 / 2, so x is a multiple of s_1's ulp (the fp16 grid at |x|
+    // is at least 2^12 of them), and |r| <= s_1 / 2 is at most 2^23 of them.
+    float rf[4];
+    uint32_t mag2 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rf[e] = fmaf(-s1f, fminf(fmaxf(q[e], -127.f), 127.f), xf[e]);
+      mag2 = max(mag2, __float_as_uint(fabsf(rf[e])));
+    }
+    mag2 = max32(mag2);
+    const double s2 = (double)(float)((double)__uint_as_float(mag2) / 127.0);
+    const float inv2 = s2 != 0.0 ? (float)(1.0 / s2) : 0.f;
+    near = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = rint127_fast(rf[e], inv2, near);
+    if (near) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = decide127((double)rf[e], s2, inv2);
+    }
+    store4(8 + gh, q);
+    if (lane % 32 == 0) {
+      qscale[0][gh] = (float)s1;
+      qscale[1][gh] = (float)s2;
+    }
+  }
+  __syncthreads();
+
+  int8_t* my = &psl[w][0][0];
+  if (has_chunk) {
+    // ---- the chunk's 16 value tiles (V^T: 8 tiles of 16 dimensions by 2 of
+    // 128 positions), issued once the decomposition's registers are free;
+    // they fly during the scores and the softmax.  Their scales and zero
+    // points go first: the softmax and the weight slicing need them.
+    uint16_t sv16[8], zv16[8];
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      zk[pp] = kz[tok0 + 16 * (2 * pp + hi) + ln];
-      sk[pp] = ks[tok0 + 16 * (2 * pp + hi) + ln];
+      sv16[pp] = vs[tok0 + 16 * (2 * pp + hi) + ln];
+      zv16[pp] = vz[tok0 + 16 * (2 * pp + hi) + ln];
     }
-    // ---- the group's queries split into two int8 slices with the decisions
-    // of the decomposition kernel, taken in fp32 (per head: s_1 = fp32(max|q| /
-    // 127), A_1 = rint(q / s_1), r = q - s_1 A_1, s_2 = fp32(max|r| / 127),
-    // A_2 = rint(r / s_2)), while the cache loads are in flight.  Lane l takes
-    // head l / 8, dimensions 16 (l mod 8) .. + 15; the codes go to this wave's
-    // LDS rows (slice 1 of head g in row g, slice 2 in row 8 + g, operand
-    // order), from which the stacked A operands are read: row ln = slice
-    // ln / 8 of head ln mod 8.
-    __shared__ float qscale[kAttnWaves][2][8];
-    int8_t* my = &psl[w][0][0];
-    {
-      const int gq = lane / 8, p8 = lane % 8;
-      u32x4 xq[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
-      if (gq < G) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(qh + (size_t)(qrow0 + gq) * kHeadDim + 16 * p8);
-        xq[0] = src[0];
-        xq[1] = src[1];
-      }
-      // dimension 16 p8 + e, and the largest magnitude of the head's 128 (as
-      // bits: for finite values they order like the magnitudes)
-      float xf[16];
-      uint32_t mag = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t v = xq[i / 4][i % 4];
-        xf[2 * i] = half_bits_to_float((uint16_t)(v & 0xFFFFu));
-        xf[2 * i + 1] = half_bits_to_float((uint16_t)(v >> 16));
-        const uint32_t m2 = v & 0x7FFF7FFFu;
-        mag = max(mag, max(m2 & 0xFFFFu, m2 >> 16));
-      }
-      auto max8 = [](uint32_t v) {  // over the 8 lanes of a head
-#pragma unroll
-        for (int off = 1; off < 8; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
-        return v;
-      };
-      // two 8-byte groups per slice: dimensions 16 p8 + 8 u + (0..7) sit at
-      // operand_byte(16 p8 + 8 u) + p(e)
-      auto store16 = [&](int row, const float (&q)[16]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          int c[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) c[e] = (int)fminf(fmaxf(q[8 * u + e], -127.f), 127.f);
-          auto b4 = [](int a0, int a1, int a2, int a3) {
-            return (uint32_t)(a0 & 0xFF) | ((uint32_t)(a1 & 0xFF) << 8) | ((uint32_t)(a2 & 0xFF) << 16) |
-                   ((uint32_t)(a3 & 0xFF) << 24);
-          };
-          *reinterpret_cast<u32x2*>(my + row * kChunk + operand_byte(16 * p8 + 8 * u)) =
-              u32x2{b4(c[0], c[4], c[1], c[5]), b4(c[2], c[6], c[3], c[7])};
-        }
-      };
-      mag = max8(mag);
-      const double s1 = (double)(float)((double)half_bits_to_float((uint16_t)mag) / 127.0);
-      const float s1f = (float)s1, inv1 = s1 != 0.0 ? (float)(1.0 / s1) : 0.f;
-      // slice 1: the fast fp32 decisions, all 16 exact (decide127) when one
-      // is near a half-integer
-      float q[16];
-      bool near = false;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = rint127_fast(xf[e], inv1, near);
-      if (near) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) q[e] = decide127((double)xf[e], s1, inv1);
-      }
-      store16(gq, q);
-      // r = x - s_1 A_1 is exact in fp32.  For A_1 = 0 it is x.  Otherwise
-      // |x| >= s_1 / 2, so x is a multiple of s_1's ulp (the fp16 grid at |x|
-      // is at least 2^12 of them), and |r| <= s_1 / 2 is at most 2^23 of them.
-      float rf[16];
-      uint32_t mag2 = 0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        rf[e] = fmaf(-s1f, fminf(fmaxf(q[e], -127.f), 127.f), xf[e]);
-        mag2 = max(mag2, __float_as_uint(fabsf(rf[e])));
-      }
-      mag2 = max8(mag2);
-      const double s2 = (double)(float)((double)__uint_as_float(mag2) / 127.0);
-      const float inv2 = s2 != 0.0 ? (float)(1.0 / s2) : 0.f;
-      near = false;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = rint127_fast(rf[e], inv2, near);
-      if (near) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) q[e] = decide127((double)rf[e], s2, inv2);
-      }
-      store16(8 + gq, q);
-      if (p8 == 0) {
-        qscale[w][0][gq] = (float)s1;
-        qscale[w][1][gq] = (float)s2;
-      }
-    }
-    // ---- the chunk's 16 value tiles (V^T: 8 tiles of 16 dimensions by 2 of
-    // 128 positions) with their scales and zero points, issued once the
-    // decomposition's registers are free; they fly during the scores and the
-    // softmax
     u32x4 V[16];
     const uint8_t* vbase = vtp + bh * (size_t)L * (kHeadDim / 2) + 16 * lane;
 #pragma unroll
@@ -541,21 +554,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         V[2 * nd + q] = *reinterpret_cast<const u32x4*>(vbase + ((size_t)nd * ltiles + chunk * 2 + q) * 1024);
-    uint16_t sv16[8], zv16[8];
-#pragma unroll
-    for (int pp = 0; pp < 8; ++pp) {
-      sv16[pp] = vs[tok0 + 16 * (2 * pp + hi) + ln];
-      zv16[pp] = vz[tok0 + 16 * (2 * pp + hi) + ln];
-    }
+    __builtin_amdgcn_sched_barrier(0);  // all value loads go out before the first wait for the keys
 
     u32x4 Aq[2];
 #pragma unroll
-    for (int pu = 0; pu < 2; ++pu) Aq[pu] = *reinterpret_cast<const u32x4*>(my + ln * kChunk + 64 * pu + 16 * kb);
+    for (int pu = 0; pu < 2; ++pu) Aq[pu] = *reinterpret_cast<const u32x4*>(&qop[ln][64 * pu + 16 * kb]);
     float s1q[4], s2q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s1q[i] = qscale[w][0][4 * hq + i];
-      s2q[i] = qscale[w][1][4 * hq + i];
+      s1q[i] = qscale[0][4 * hq + i];
+      s2q[i] = qscale[1][4 * hq + i];
     }
     // the key zero point enters after the product: D_j = sum_d A_j q - zK
     // sum_d A_j, with the row sums of the query slices from one product
@@ -592,8 +600,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
         D[hh] = mfma_i8_16x16x64(Aq[0], Bk[0], i32x4{0, 0, 0, 0});
         D[hh] = mfma_i8_16x16x64(Aq[1], Bk[1], D[hh]);
       }
-      const float skf = half_bits_to_float(sk[pp]) * inv_sqrt_d;
-      const float zkf = half_bits_to_float(zk[pp]);
+      const float skf = half_bits_to_float((uint16_t)sk[pp]) * inv_sqrt_d;
+      const float zkf = half_bits_to_float((uint16_t)zk[pp]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int x = D[0][i], y = D[1][i];
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
       m[i] = sc[0][i];
 #pragma unroll
       for (int pp = 1; pp < 8; ++pp) m[i] = fmaxf(m[i], sc[pp][i]);
-      m[i] = row32<true>(m[i]);
+      m[i] = row32<kRowMax>(m[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -623,14 +631,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
         sc[pp][i] = e * half_bits_to_float(sv16[pp]);
         am[i] = fmaxf(am[i], sc[pp][i]);
       }
-      l[i] = row32<false>(l[i]);
-      am[i] = row32<true>(am[i]);
+      l[i] = row32<kRowSum>(l[i]);
+      am[i] = row32<kRowMaxNonNeg>(am[i]);  // w = p sV >= 0
     }
-    float r1[4], r2[4], zt1[4], zt2[4];  // the weight slices go to the same LDS rows (Aq is in registers)
+    float r1[4], r2[4], zt1[4], zt2[4];  // the weight slices go to this wave's LDS rows
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       r1[i] = am[i] * (1.f / 127.f);
-      const float inv1 = r1[i] > 0.f ? 1.f / r1[i] : 0.f;
+      const float inv1 = r1[i] > 0.f ? __builtin_amdgcn_rcpf(r1[i]) : 0.f;  // 1 ulp: the codes are compared within a tolerance
       float am2 = 0.f, z1 = 0.f;  // integer sums below 2^24: exact in fp32
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
@@ -641,8 +649,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
         sc[pp][i] = sc[pp][i] - r1[i] * a;
         am2 = fmaxf(am2, fabsf(sc[pp][i]));
       }
-      r2[i] = row32<true>(am2) * (1.f / 127.f);
-      const float inv2 = r2[i] > 0.f ? 1.f / r2[i] : 0.f;
+      r2[i] = row32<kRowMaxNonNeg>(am2) * (1.f / 127.f);
+      const float inv2 = r2[i] > 0.f ? __builtin_amdgcn_rcpf(r2[i]) : 0.f;
       float z2 = 0.f;
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
@@ -651,8 +659,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
         my[(8 + 4 * hq + i) * kChunk + operand_byte(t)] = (int8_t)(int)a;
         z2 = fmaf(a, half_bits_to_float(zv16[pp]), z2);
       }
-      zt1[i] = row32<false>(z1);  // |sum| <= 256 * 127 * 15 < 2^24: exact
-      zt2[i] = row32<false>(z2);
+      zt1[i] = row32<kRowSum>(z1);  // |sum| <= 256 * 127 * 15 < 2^24: exact
+      zt2[i] = row32<kRowSum>(z2);
     }
 
     // ---- values: E (rows 0-7 slice 1, 8-15 slice 2) per dim tile, pairs of
