@@ -115,6 +115,10 @@ __device__ __forceinline__ float quant_i8(float v, float inv) {
   return fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
 }
 
+// rint(v / s) where |v| <= 127 s by construction (s = max |v| / 127 rounded
+// to fp32, inv within an ulp of 1 / s, so |v inv| < 127.5): no clamp
+__device__ __forceinline__ float quant_i8_inrange(float v, float inv) { return rintf(v * inv); }
+
 // Everything one chunk of 256 positions needs from the caches: per lane, its
 // wave's 4 key tiles and 2 x 2 value tiles, and the per-token scales and
 // zero points of its 4 positions.
@@ -642,7 +646,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
       float am2 = 0.f, z1 = 0.f;  // integer sums below 2^24: exact in fp32
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
-        const float a = quant_i8(sc[pp][i], inv1);
+        const float a = quant_i8_inrange(sc[pp][i], inv1);
         const int t = 16 * (2 * pp + hi) + ln;
         my[(4 * hq + i) * kChunk + operand_byte(t)] = (int8_t)(int)a;
         z1 = fmaf(a, half_bits_to_float(zv16[pp]), z1);
@@ -654,7 +658,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
       float z2 = 0.f;
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
-        const float a = quant_i8(sc[pp][i], inv2);
+        const float a = quant_i8_inrange(sc[pp][i], inv2);
         const int t = 16 * (2 * pp + hi) + ln;
         my[(8 + 4 * hq + i) * kChunk + operand_byte(t)] = (int8_t)(int)a;
         z2 = fmaf(a, half_bits_to_float(zv16[pp]), z2);
