@@ -32,6 +32,10 @@ constexpr int kHeadDim = 128;
 constexpr int kChunk = 256;
 constexpr int kAttnThreads = 256;  // 4 waves
 constexpr int kAttnWaves = kAttnThreads / kWave;
+// Scores are kept in base-2 units, scaled by log2(e) / sqrt(128), so that
+// every exponential of the softmax and of the combination is one exp2 (e^x
+// = 2^(x log2 e)); the maxima stored with the partials are in the same units.
+constexpr float kScoreScale = 0x1.0527dbd87e24dp-3f;  // 0.12751743082459868
 
 __device__ __forceinline__ i32x4 mfma_i8_16x16x64(u32x4 a, u32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
@@ -201,7 +205,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
     }
   };
 
-  const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
   float Mrun[4], Lrun[4], Orun[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sc[tt][i] = s * fmaf(sq[0][i], (float)D[0][i], sq[1][i] * (float)D[1][i]) * inv_sqrt_d;
+        sc[tt][i] = s * fmaf(sq[0][i], (float)D[0][i], sq[1][i] * (float)D[1][i]) * kScoreScale;
     }
 
     if (more) load_keys(c0 + ci + 1, cur);  // in flight during the rest of this chunk
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
       la[1][i] = 0.f;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const float e = __expf(sc[tt][i] - m[0][i]);
+        const float e = __builtin_amdgcn_exp2f(sc[tt][i] - m[0][i]);
         la[0][i] += e;
         p[tt][i] = e * sv[tt];
         la[1][i] = fmaxf(la[1][i], p[tt][i]);
@@ -324,8 +327,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float mn = fmaxf(Mrun[i], m[0][i]);
-      fa[i] = __expf(Mrun[i] - mn);
-      fb[i] = __expf(m[0][i] - mn);
+      fa[i] = __builtin_amdgcn_exp2f(Mrun[i] - mn);
+      fb[i] = __builtin_amdgcn_exp2f(m[0][i] - mn);
       Lrun[i] = fmaf(fa[i], Lrun[i], fb[i] * l[i]);
       Mrun[i] = mn;
     }
@@ -587,8 +590,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
     }
 
     // ---- scores: tile pairs (2 p, 2 p + 1)
-    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
-    float sc[8][4];
+      float sc[8][4];
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
       i32x4 D[2];
@@ -604,7 +606,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
         D[hh] = mfma_i8_16x16x64(Aq[0], Bk[0], i32x4{0, 0, 0, 0});
         D[hh] = mfma_i8_16x16x64(Aq[1], Bk[1], D[hh]);
       }
-      const float skf = half_bits_to_float((uint16_t)sk[pp]) * inv_sqrt_d;
+      const float skf = half_bits_to_float((uint16_t)sk[pp]) * kScoreScale;
       const float zkf = half_bits_to_float((uint16_t)zk[pp]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
       am[i] = 0.f;
 #pragma unroll
       for (int pp = 0; pp < 8; ++pp) {
-        const float e = __expf(sc[pp][i] - m[i]);
+        const float e = __builtin_amdgcn_exp2f(sc[pp][i] - m[i]);
         l[i] += e;
         sc[pp][i] = e * half_bits_to_float(sv16[pp]);
         am[i] = fmaxf(am[i], sc[pp][i]);
@@ -724,7 +726,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kAttnWaves; ++ww) {
-      const float f = __expf(mml[ww][g][0] - mx);  // 0 for a wave without a chunk
+      const float f = __builtin_amdgcn_exp2f(mml[ww][g][0] - mx);  // 0 for a wave without a chunk
       num = fmaf(f, mo[ww][g][n], num);
       den = fmaf(f, mml[ww][g][1], den);
     }
@@ -761,12 +763,12 @@ __global__ __launch_bounds__(kHeadDim) void attn_combine_kernel(const float* __r
     float mb = m;
 #pragma unroll
     for (int i = 0; i < 8; ++i) mb = fmaxf(mb, v[i].x);
-    const float f0 = m == -INFINITY ? 0.f : expf(m - mb);  // rescale what came before
+    const float f0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mb);  // rescale what came before
     num *= f0;
     den *= f0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float f = v[i].x == -INFINITY ? 0.f : expf(v[i].x - mb);
+      const float f = v[i].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[i].x - mb);
       num = fmaf(f, o[i], num);
       den = fmaf(f, v[i].y, den);
     }
