@@ -500,16 +500,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
     auto store4 = [&](int row, const float (&q)[4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        qop[row][operand_byte(d0 + e)] = (int8_t)(int)fminf(fmaxf(q[e], -127.f), 127.f);
+        qop[row][operand_byte(d0 + e)] = (int8_t)(int)q[e];  // in [-127, 127] without a clamp
     };
     mag = max32(mag);
     const double s1 = (double)(float)((double)half_bits_to_float((uint16_t)mag) / 127.0);
     const float s1f = (float)s1, inv1 = s1 != 0.0 ? (float)(1.0 / s1) : 0.f;
     float q[4];
-    bool near = false;
+    float dmax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) q[e] = rint127_fast(xf[e], inv1, near);
-    if (near) {
+    for (int e = 0; e < 4; ++e) q[e] = rint127_fast(xf[e], inv1, dmax);
+    if (near127(dmax)) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) q[e] = decide127((double)xf[e], s1, inv1);
     }
@@ -521,16 +521,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_msd_wave_kernel(
     uint32_t mag2 = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      rf[e] = fmaf(-s1f, fminf(fmaxf(q[e], -127.f), 127.f), xf[e]);
+      rf[e] = fmaf(-s1f, q[e], xf[e]);
       mag2 = max(mag2, __float_as_uint(fabsf(rf[e])));
     }
     mag2 = max32(mag2);
     const double s2 = (double)(float)((double)__uint_as_float(mag2) / 127.0);
     const float inv2 = s2 != 0.0 ? (float)(1.0 / s2) : 0.f;
-    near = false;
+    dmax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) q[e] = rint127_fast(rf[e], inv2, near);
-    if (near) {
+    for (int e = 0; e < 4; ++e) q[e] = rint127_fast(rf[e], inv2, dmax);
+    if (near127(dmax)) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) q[e] = decide127((double)rf[e], s2, inv2);
     }

@@ -249,24 +249,21 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
     const int k = 8 * rt + c * kStep;
     if (k >= K) continue;
     float xf[8], q[8];
-    bool near = false;
+    float dmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       xf[2 * i] = half_bits_to_float((uint16_t)(xc[c][i] & 0xFFFFu));
       xf[2 * i + 1] = half_bits_to_float((uint16_t)(xc[c][i] >> 16));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = rint127_fast(xf[i], inv1, near);
-    if (near) {
+    for (int i = 0; i < 8; ++i) q[i] = rint127_fast(xf[i], inv1, dmax);
+    if (near127(dmax)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = decide127((double)xf[i], s1, inv1);
     }
     int a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      q[i] = fminf(fmaxf(q[i], -127.f), 127.f);
-      a[i] = (int)q[i];
-    }
+    for (int i = 0; i < 8; ++i) a[i] = (int)q[i];  // in [-127, 127]: |x / s_1| <= 127.0001
     store8(0, k, a);
     if constexpr (NS > 1) {
 #pragma unroll
@@ -290,13 +287,13 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
     const int k = 8 * rt + c * kStep;
     if (k >= K) continue;
     float q[8];
-    bool near = false;
+    float dmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float n = FIXED ? (float)kFixedRatio * rf[c][i] : rf[c][i];
-      q[i] = rint127_fast(n, inv2, near);
+      q[i] = rint127_fast(n, inv2, dmax);
     }
-    if (near) {
+    if (near127(dmax)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const double r = (double)rf[c][i];
@@ -305,7 +302,7 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
     }
     int a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (int)fminf(fmaxf(q[i], -127.f), 127.f);
+    for (int i = 0; i < 8; ++i) a[i] = (int)q[i];  // |r_1 / s_2|, |254 r_1 / s_1| <= 127.0001
     store8(1, k, a);
   }
   if (rt == 0) tok_scale[(size_t)M + m] = FIXED ? (float)(s1 / kFixedRatio) : (float)s2;

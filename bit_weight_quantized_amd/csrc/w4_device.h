@@ -166,17 +166,21 @@ __device__ __forceinline__ float decide127(double n, double s, float inv) {
   return fminf(fmaxf(q, -127.f), 127.f);
 }
 
-// The fast form of decide127's estimate: rint(fl32(n * inv)), and near set
-// when that estimate lies within 2^-14 of a half-integer (then decide127 must
-// decide).  Branch-free, for callers that decide a group of values this way
-// and take decide127 for the whole group only when one of them is near.
-__device__ __forceinline__ float rint127_fast(float n, float inv, bool& near) {
+// The fast form of decide127's estimate: rint(fl32(n * inv)) (v_rndne: the
+// same integer as the 1.5 * 2^23 addition), with |t - rint(t)| folded into
+// dmax.  Since |t - rint(t)| <= 1/2, t lies within 2^-14 of a half-integer
+// exactly when that distance exceeds 1/2 - 2^-14 (both sides exact in fp32):
+// callers decide a group of values this way and take decide127 for the whole
+// group when near127(dmax).  Branch-free.  For |n / s| <= 127.0001 the
+// result is in [-127, 127] without a clamp.
+__device__ __forceinline__ float rint127_fast(float n, float inv, float& dmax) {
 #pragma clang fp contract(off)
   const float t = n * inv;
-  const float q = (t + kRintMagic) - kRintMagic;
-  near = near || fabsf(fabsf(t - q) - 0.5f) < kNearHalf;
+  const float q = __builtin_rintf(t);
+  dmax = fmaxf(dmax, fabsf(t - q));
   return q;
 }
+__device__ __forceinline__ bool near127(float dmax) { return dmax > 0.5f - kNearHalf; }
 
 
 }  // namespace w4

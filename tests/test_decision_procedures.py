@@ -41,7 +41,11 @@ def decide127(n, s, inv, window):
     float), inv: fl32(1 / s)."""
     t = (n.astype(F32) * inv).astype(F32)
     q = rint32(t)
-    near = np.abs(np.abs((t - q).astype(F32)) - F32(0.5)) < F32(window)
+    assert np.all(np.abs(q) <= 127)  # the kernels take the fast estimate without a clamp
+    # near a half-integer: |t - q| > 1/2 - window (the kernels' form; the
+    # same set as ||t - q| - 1/2| < window, since |t - q| <= 1/2)
+    near = np.abs((t - q).astype(F32)) > F32(0.5) - F32(window)
+    assert np.array_equal(near, np.abs(np.abs((t - q).astype(F32)) - F32(0.5)) < F32(window))
     for i in np.nonzero(near)[0]:
         sg = 1.0 if t[i] >= q[i] else -1.0
         h = Fraction(float(q[i])) + Fraction(sg) / 2
@@ -77,13 +81,15 @@ def fused_fixed_emulated(x, s1, window):
     s1f, inv = F32(s1), inv32(s1)
     t1 = (xf * inv).astype(F32)
     q1 = rint32(t1)
-    near = np.abs(np.abs((t1 - q1).astype(F32)) - F32(0.5)) < F32(window)
+    assert np.all(np.abs(q1) <= 127)
+    near = np.abs((t1 - q1).astype(F32)) > F32(0.5) - F32(window)
     q1 = np.clip(q1, -127, 127).astype(F32)
     # fma(-s1, q1, x) rounded once: the fp64 sum is exact here
     r1 = (xf.astype(np.float64) - float(s1f) * q1.astype(np.float64)).astype(F32)
     t2 = ((F32(254.0) * r1).astype(F32) * inv).astype(F32)
     q2 = rint32(t2)
-    near |= np.abs(np.abs((t2 - q2).astype(F32)) - F32(0.5)) < F32(window)
+    assert np.all(np.abs(q2) <= 127)
+    near |= np.abs((t2 - q2).astype(F32)) > F32(0.5) - F32(window)
     q2 = np.clip(q2, -127, 127).astype(F32)
     for i in np.nonzero(near)[0]:
         def exact_rint(v, c, t):
