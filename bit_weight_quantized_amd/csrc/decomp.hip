@@ -187,6 +187,28 @@ __global__ __launch_bounds__(T) void decompose_kernel(
   }
 }
 
+// The largest of a block's non-negative values given as bits whose unsigned
+// order is the values' order (fp16 or fp32 magnitudes): within each DPP row
+// of 16 lanes (pairs, quads, half-mirror, mirror; the moves fold into the
+// integer maximum), over the wave's four rows (lane reads), then over the
+// waves through LDS.
+template <int T>
+__device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t* red) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true));
+  const uint32_t w = max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+                         max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+  __syncthreads();  // the previous maximum's reads of red are done
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = w;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < T / kWave; ++i) r = max(r, red[i]);
+  return r;
+}
+
 // Lean variant for one or two slices with the row cached in registers (K <=
 // 32 T): the same decisions as decompose_kernel, with fewer instructions.
 //  * The absmax comes from the magnitude bits (an integer maximum: the bit
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
   static_assert(!FIXED || NS == 2, "the fixed ratio defines a second slice");
   constexpr int CH = 4;
   constexpr int kStep = 8 * T;
-  __shared__ double red[T / kWave];
+  __shared__ uint32_t red[T / kWave];
   const int rt = (int)threadIdx.x;
   const int m = (int)blockIdx.x;
   const uint16_t* xr = x + (size_t)m * K;
@@ -229,7 +251,7 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
       mag = max(mag, max(w & 0xFFFFu, w >> 16));
     }
   }
-  const double amax = block_max<T>((double)half_bits_to_float((uint16_t)mag), red);
+  const double amax = (double)half_bits_to_float((uint16_t)block_max_bits<T>(mag, red));
   const double s1 = (double)(float)(amax / 127.0);
   const float inv1 = s1 != 0.0 ? (float)(1.0 / s1) : 0.f;
   const float s1f = (float)s1;
@@ -279,7 +301,7 @@ __global__ __launch_bounds__(T) void decompose_lean_kernel(const uint16_t* __res
   double s2 = s1;
   float inv2 = inv1;
   if constexpr (!FIXED) {
-    s2 = (double)(float)(block_max<T>((double)__uint_as_float(mag2), red) / 127.0);
+    s2 = (double)(float)((double)__uint_as_float(block_max_bits<T>(mag2, red)) / 127.0);
     inv2 = s2 != 0.0 ? (float)(1.0 / s2) : 0.f;
   }
 #pragma unroll
