@@ -174,6 +174,72 @@ def bench_gemm_prefill(w4, torch, reps):
             "paths": res}
 
 
+def bench_mfma_ceiling(w4, torch, iters=8192):
+    """The matrix-core ceiling on this part, measured (w4_mfma_rate): one
+    workgroup of 8 waves per CU, each wave issuing iters x 8 independent
+    16 x 16 products, fp16 (16x16x32) and int8 (16x16x64); the clock comes
+    from the waves' shader-clock and 100 MHz ticks.  The same launch with V
+    independent fp32 FMAs per product shows how many VALU instructions run
+    beside a product without slowing it (the last V within 3 % of V = 0)."""
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+    ticks = torch.zeros(wgs * 16, dtype=torch.int64, device="cuda")
+    st = torch.cuda.Stream()
+    res = {}
+    for kind, name, ops, peak in ((0, "fp16_16x16x32", 16384, FP16_MFMA_PEAK_TFLOPS),
+                                  (1, "int8_16x16x64", 32768, INT8_MFMA_PEAK_TOPS)):
+        sweep = {}
+        clock = None
+        with torch.cuda.stream(st):
+            for valu in (0, 1, 2, 3, 4, 6, 8):
+                w4.mfma_rate(kind, valu, wgs, iters, sink, ticks, stream=st)
+                st.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                for _ in range(3):
+                    w4.mfma_rate(kind, valu, wgs, iters, sink, ticks, stream=st)
+                b.record(st)
+                st.synchronize()
+                sweep[valu] = a.elapsed_time(b) * 1e3 / 3
+                if valu == 0:
+                    t = ticks.cpu().double().reshape(-1, 2)
+                    clock = float((t[:, 0] / (t[:, 1] / 100e6)).mean() / 1e9)
+        rate = wgs * 8 * iters * 8 * ops / (sweep[0] * 1e-6) / 1e12
+        free = max(v for v in sweep if sweep[v] <= 1.03 * sweep[0])
+        res[name] = {"us_per_launch": round(sweep[0], 1), "rate": round(rate, 1), "peak": peak,
+                     "frac_of_peak": round(rate / peak, 4), "clock_ghz": round(clock, 3),
+                     "free_valu_per_product": free,
+                     "us_by_valu_per_product": {str(v): round(us, 1) for v, us in sweep.items()}}
+    return {"workload": "independent matrix-core products, 8 waves per CU", "iters_per_wave": iters * 8,
+            "unit": "TFLOP/s (fp16), TOP/s (int8)", "kinds": res}
+
+
+def bench_library_f16_gemm(torch, reps=10):
+    """hipBLASLt's fp16 GEMM (torch.matmul) at the prefill shape, on fp16
+    weights: no unpacking, the library's own tiling; a comparison point."""
+    M, K, N = 2048, 5120, 25600
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(41000)
+    x = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32).half()
+    w = (torch.randn((K, N), generator=gen, device="cuda", dtype=torch.float32) * 0.02).half()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for _ in range(3):
+            y = torch.matmul(x, w)
+        st.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            y = torch.matmul(x, w)
+        b.record(st)
+        st.synchronize()
+    del y
+    us = a.elapsed_time(b) * 1e3 / reps
+    tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    return {"workload": "fp16 GEMM M=2048 K=5120 N=25600 (torch.matmul, hipBLASLt)", "us_per_call": round(us, 1),
+            "tflops": round(tf, 1), "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+
+
 def prefill_paths(w4, torch):
     """The prefill product M = 2048, K = 5120, N = 25600 (INT4 g128; MXFP4 for
     the mxfp4 paths): a dict of name -> (thunk, MFMA products per useful
@@ -950,6 +1016,13 @@ def main():
     except Exception as e:  # reported, never fatal to the headline line
         plain = {"error": f"{type(e).__name__}: {e}"}
     gemm = bench_gemm_prefill(w4, torch, args.gemm_reps) if args.gemm_reps > 0 else None
+    if gemm is not None:
+        for key, fn in (("mfma_ceiling", lambda: bench_mfma_ceiling(w4, torch)),
+                        ("library_f16_gemm", lambda: bench_library_f16_gemm(torch))):
+            try:
+                gemm[key] = fn()
+            except Exception as e:  # reported, never fatal to the headline line
+                gemm[key] = {"error": f"{type(e).__name__}: {e}"}
     single = None
     try:
         single = bench_single_gemv(w4, torch, stream)

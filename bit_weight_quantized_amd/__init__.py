@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "INT4_ASYM", "NF4", "DQ_F16", "POSTSCALE", "W4Error", "W4LibraryMissing",
     "lib", "lib_path", "quantize", "pack", "gemv", "gemv_noalloc", "gemv_plan", "gemm", "gemm_decomp", "gemm_decomp_fixed",
-    "gemm_decomp_fixed_fused", "stream_read",
+    "gemm_decomp_fixed_fused", "stream_read", "mfma_rate",
     "salient_select", "residual_correct", "salient_correct", "residual_correct_f32", "residual_apply",
     "salient_correct_f32", "quantize_mx", "pack_mx", "gemm_mx", "attn_decode_msd",
     "workspace_bytes", "nf4_levels", "version",
@@ -71,6 +71,7 @@ def lib():
         L.w4_gemm_decomp_fixed.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p]
         L.w4_gemm_decomp_fixed_fused.argtypes = [_p, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _sz, _p]
         L.w4_stream_read.argtypes = [_p, _sz, _p, _p]
+        L.w4_mfma_rate.argtypes = [_i, _i, _i, _i, _p, _p, _p]
         L.w4_salient_select.argtypes = [_p, _i, _i, _i, _p, _p]
         L.w4_quantize_mx.argtypes = [_p, _i, _i, _p, _p, _p]
         L.w4_pack_mx.argtypes = [_p, _i, _i, _p, _p]
@@ -90,7 +91,7 @@ def lib():
         L.w4_last_error.restype = ctypes.c_char_p
         L.w4_version.restype = ctypes.c_char_p
         for fn in ("w4_quantize", "w4_pack", "w4_gemv", "w4_gemv_noalloc", "w4_gemv_plan", "w4_gemm", "w4_gemm_decomp", "w4_gemm_decomp_fixed",
-                   "w4_gemm_decomp_fixed_fused", "w4_stream_read", "w4_salient_select", "w4_residual_correct", "w4_salient_correct",
+                   "w4_gemm_decomp_fixed_fused", "w4_stream_read", "w4_mfma_rate", "w4_salient_select", "w4_residual_correct", "w4_salient_correct",
                    "w4_residual_correct_f32", "w4_residual_apply", "w4_salient_correct_f32", "w4_quantize_mx", "w4_pack_mx", "w4_gemm_mx",
                    "w4_attn_decode_msd",
                    "w4_nf4_levels"):
@@ -295,6 +296,23 @@ def stream_read(buf, xor_acc, *, stream=None):
     nbytes = buf.numel() * buf.element_size()
     _check("w4_stream_read", lib().w4_stream_read(_ptr(buf), nbytes, _ptr(xor_acc), _stream(stream)))
     return xor_acc
+
+
+def mfma_rate(kind: int, valu: int, workgroups: int, iters: int, sink, ticks=None, *, stream=None):
+    """Independent matrix-core products (kind 0 fp16 16x16x32, 1 int8
+    16x16x64), iters x 8 per wave with `valu` fp32 FMAs each; sink: float32
+    device tensor of workgroups x 512, ticks: int64 device tensor of
+    2 x (workgroups x 8) (shader-clock and 100 MHz ticks per wave) or None."""
+    _dev(sink, torch.float32, "sink")
+    if sink.numel() < workgroups * 512:
+        raise ValueError("sink needs workgroups x 512 elements")
+    if ticks is not None:
+        _dev(ticks, torch.int64, "ticks")
+        if ticks.numel() < workgroups * 16:
+            raise ValueError("ticks needs workgroups x 16 elements")
+    _check("w4_mfma_rate", lib().w4_mfma_rate(kind, valu, workgroups, iters, _ptr(sink), _ptr(ticks),
+                                              _stream(stream)))
+    return sink
 
 
 def salient_select(x, k: int, *, out=None, stream=None):

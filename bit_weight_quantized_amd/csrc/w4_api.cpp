@@ -496,6 +496,20 @@ int w4_stream_read(const void* buf, size_t bytes, uint32_t* xor_acc, void* strea
   return launch_stream_read(buf, bytes, xor_acc, (hipStream_t)stream);
 }
 
+int w4_mfma_rate(int kind, int valu, int workgroups, int iters, float* sink, unsigned long long* ticks,
+                 void* stream) {
+  g_last_error[0] = '\0';
+  if (kind != 0 && kind != 1) return fail(W4_EINVAL, "w4_mfma_rate: kind must be 0 (fp16) or 1 (int8) (got %d)", kind);
+  if (valu < 0 || valu > 8 || valu == 5 || valu == 7)
+    return fail(W4_EINVAL, "w4_mfma_rate: valu must be 0, 1, 2, 3, 4, 6 or 8 (got %d)", valu);
+  if (workgroups < 1 || iters < 1)
+    return fail(W4_EINVAL, "w4_mfma_rate: workgroups and iters must be positive (got %d, %d)", workgroups, iters);
+  if (!sink) return fail(W4_EINVAL, "w4_mfma_rate: sink must be non-null");
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u) || (reinterpret_cast<uintptr_t>(ticks) & 7u))
+    return fail(W4_EINVAL, "w4_mfma_rate: sink must be 4-byte and ticks 8-byte aligned");
+  return launch_mfma_rate(kind, valu, workgroups, iters, sink, ticks, (hipStream_t)stream);
+}
+
 int w4_nf4_levels(float* out16) {
   if (!out16) return fail(W4_EINVAL, "w4_nf4_levels: out16 must be non-null");
   std::memcpy(out16, kNf4LevelBits, sizeof(kNf4LevelBits));

@@ -162,4 +162,9 @@ extern const uint32_t kNf4LevelBits[16];
 // Plain read of bytes / 16 16-byte pieces, XOR-folded into *acc.
 int launch_stream_read(const void* buf, size_t bytes, uint32_t* acc, hipStream_t s);
 
+// Independent matrix-core products (kind 0 fp16, 1 int8) with valu fp32 FMAs
+// each, iters rounds of 8 per wave, 512 threads per workgroup.
+int launch_mfma_rate(int kind, int valu, int workgroups, int iters, float* sink, unsigned long long* ticks,
+                     hipStream_t s);
+
 }  // namespace w4

@@ -472,6 +472,26 @@ size_t w4_workspace_bytes(int op, int M, int K, int N, int G, int fmt_or_mode);
 #define W4_STREAM_READ_ACC_WORDS 449
 int w4_stream_read(const void* buf, size_t bytes, uint32_t* xor_acc, void* stream);
 
+/*
+ * w4_mfma_rate -- the matrix-core issue rate, the measured ceiling the
+ * prefill products are compared with beside the nominal dense peak (not part
+ * of the method).  Launches `workgroups` workgroups of 512 threads (8 waves,
+ * two per SIMD, as the prefill products run); every wave issues iters x 8
+ * independent 16 x 16 products -- kind 0: v_mfma_f32_16x16x32_f16 (16384
+ * flops each), kind 1: v_mfma_i32_16x16x64_i8 (32768 ops each) -- and, with
+ * each product, `valu` independent fp32 FMAs (0, 1, 2, 3, 4, 6 or 8).  No
+ * memory traffic besides the results: sink (device, workgroups x 512 floats)
+ * receives a per-thread sum of the accumulators, and ticks (device, 2 words
+ * per wave, or null) receives each wave's elapsed shader-clock ticks
+ * (s_memtime) and 100 MHz real-time ticks (s_memrealtime) around its loop,
+ * whose ratio is the clock the part ran at.  96 KB of LDS are reserved per
+ * workgroup (and not used), so one workgroup runs per CU.  Errors: W4_EINVAL for another
+ * kind or valu, workgroups or iters below 1, a null sink, or a misaligned
+ * pointer.
+ */
+int w4_mfma_rate(int kind, int valu, int workgroups, int iters, float* sink, unsigned long long* ticks,
+                 void* stream);
+
 /* Host-only: copies the library's 16 fp32 NF4 levels into out16 (host). */
 int w4_nf4_levels(float* out16);
 

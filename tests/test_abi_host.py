@@ -281,3 +281,14 @@ def test_workspace_bytes(L):
         assert L.w4_workspace_bytes(4, 100, 1024, 64, 128, ns) == want
     assert L.w4_workspace_bytes(4, 100, 1024, 64, 128, 4) == 0
     assert L.w4_workspace_bytes(99, 1, 1, 1, 1, 0) == ctypes.c_size_t(-1).value
+
+
+def test_mfma_rate_argument_errors(L):
+    assert L.w4_mfma_rate(2, 0, 1, 1, FAKE, None, None) == W4_EINVAL  # kind
+    assert L.w4_mfma_rate(0, 5, 1, 1, FAKE, None, None) == W4_EINVAL  # valu not instantiated
+    assert L.w4_mfma_rate(0, 9, 1, 1, FAKE, None, None) == W4_EINVAL
+    assert L.w4_mfma_rate(1, 0, 0, 1, FAKE, None, None) == W4_EINVAL  # no workgroups
+    assert L.w4_mfma_rate(1, 0, 1, 0, FAKE, None, None) == W4_EINVAL  # no iterations
+    assert L.w4_mfma_rate(0, 0, 1, 1, None, None, None) == W4_EINVAL  # sink
+    assert L.w4_mfma_rate(0, 0, 1, 1, MISALIGNED, None, None) == W4_EINVAL
+    assert b"w4_mfma_rate" in L.w4_last_error()
