@@ -219,6 +219,12 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   __syncthreads();
 
+  // DQ, INT4: the nibble mask held in a VGPR (opaque to the compiler), so that
+  // (v >> 4j) & mask | 0x64006400 is one v_and_or_b32 with the constant in an
+  // SGPR (one constant-bus operand) instead of a separate and and or
+  uint32_t nib_mask = 0x000F000Fu;
+  if constexpr (PATH == 0 && FMT == 0) asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(nib_mask));
+
   // per-step state: raw weight words, per-column scales / zero points
   u32x4 Bq[NT];
   float sfv[GPT][NT];      // PS: per-column scale (x 2^24 for INT4)
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(kF16Threads) __attribute__((amdgpu_waves_per_eu(2, 
         uint32_t d[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t q = (v >> (4 * j)) & 0x000F000Fu;  // (c_2j, c_2j+1) * 2^-24
+          const uint32_t q = (v >> (4 * j)) & nib_mask;  // (c_2j, c_2j+1) * 2^-24
           d[j] = PATH == 1 ? pk_sub_f16(q, zzv[gi][nt]) : pk_mul_f16(pk_sub_f16(q | 0x64006400u, zzv[gi][nt]), spv[gi][nt]);
         }
         Bu[nt] = u32x4{d[0], d[1], d[2], d[3]};

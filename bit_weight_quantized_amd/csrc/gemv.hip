@@ -394,7 +394,13 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   for (int t = 0; t < MT; ++t) mrow[t] = ONE ? 0 : min(t * 16 + ln, M - 1);
   // INT4: the group's activation sum per token, as a product with constant B
   // (1 for the even pairs, 16 for the pre-scaled odd pairs)
-  const u32x4 kSumB{0x3C003C00u, 0x4C004C00u, 0x3C003C00u, 0x4C004C00u};
+  // (held in VGPRs for the whole run: opaque to the compiler, which would
+  // otherwise rebuild the operand from scalar registers for every tile)
+  u32x4 kSumB;
+  asm volatile("v_mov_b32 %0, 0x3C003C00" : "=v"(kSumB[0]));
+  asm volatile("v_mov_b32 %0, 0x4C004C00" : "=v"(kSumB[1]));
+  kSumB[2] = kSumB[0];
+  kSumB[3] = kSumB[1];
   // the lane's row of the scale block, at the wave's first tile
   const uint32_t* sc_row = VS ? sc + (size_t)(wr * 16 + ln) * sc_pitch + (size_t)t0 * EW
                               : sc + (size_t)ln * sc_pitch * EW;
