@@ -592,14 +592,17 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)((size_t)N * (K / 2)));
   const uint32_t voff = (uint32_t)lane * 16;
   // operand order: lane (ln, kb) reads row ln, chunk 4 w + kb of word w;
-  // XL: load j gives lane (ln, kb) row 4 j + kb, chunk ln
-  const u32x4* xrow[XL ? 4 : 1][MT];
+  // XL: load j gives lane (ln, kb) row 4 j + kb, chunk ln.  Buffer loads:
+  // the lane's byte offset in a VGPR, the tile's (tt * 256) in an SGPR, so
+  // no per-load 64-bit address arithmetic.
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+  uint32_t xoff[XL ? 4 : 1][MT];
 #pragma unroll
   for (int j = 0; j < (XL ? 4 : 1); ++j)
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-      xrow[j][m] = XL ? reinterpret_cast<const u32x4*>(x + (size_t)min(m * 16 + 4 * j + kb, M - 1) * K) + ln
-                      : reinterpret_cast<const u32x4*>(x + (size_t)min(m * 16 + ln, M - 1) * K) + kb;
+      xoff[j][m] = XL ? (uint32_t)min(m * 16 + 4 * j + kb, M - 1) * (uint32_t)K * 2u + (uint32_t)ln * 16u
+                      : (uint32_t)min(m * 16 + ln, M - 1) * (uint32_t)K * 2u + (uint32_t)kb * 16u;
   auto load_slot = [&](Slot& sl, int t) {
     const int tt = __builtin_amdgcn_readfirstlane(min(min(t, t_last), KT - 1));
 #pragma unroll
@@ -608,7 +611,9 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) sl.a[w][m] = XL ? xrow[w][m][tt * 16] : xrow[0][m][tt * 16 + 4 * w];
+      for (int m = 0; m < MT; ++m)
+        sl.a[w][m] = XL ? buffer_load16_cached(xrs, xoff[w][m], (uint32_t)tt * 256u)
+                        : buffer_load16_cached(xrs, xoff[0][m] + 64u * (uint32_t)w, (uint32_t)tt * 256u);
   };
   unsigned char* const xs = smem + xl_off + (size_t)wave * MT * 4096;  // XL: this wave's area
 
@@ -680,7 +685,11 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
   for (int c = 0; c < C; ++c)
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc_c[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 kOnes{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  // held in VGPRs for the whole run (opaque to the compiler, which would
+  // otherwise rebuild the operand from scalar registers for every step)
+  u32x4 kOnes;
+  asm volatile("v_mov_b32 %0, 0x3C003C00" : "=v"(kOnes[0]));
+  kOnes[1] = kOnes[2] = kOnes[3] = kOnes[0];
   const uint32_t* lut_c = lut + lane % kLutCopies;
 
   auto compute = [&](Slot& sl, int ci) {

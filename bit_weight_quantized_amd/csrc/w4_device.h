@@ -55,6 +55,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
 }
+// The same with the default cache policy (data that other waves read again).
+__device__ __forceinline__ u32x4 buffer_load16_cached(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
