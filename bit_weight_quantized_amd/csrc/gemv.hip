@@ -96,14 +96,32 @@ __device__ __forceinline__ void div_small(int u, int d, float inv_d, int& q, int
 // NWK x MT x 256 floats of LDS, free when called after a barrier), then the
 // fp16 store, or with S > 1 the fp32 partial of this K slice (summed over the
 // slices by gemv_reduce_kernel, launched right after on the same stream).
-template <int MT, bool ONE = false>
+template <int MT, int TM = 0>
 __device__ __forceinline__ void gemv_finish(const f32x4 (&C)[MT], float* red, int wave, int lane, int nwr, int nwk,
                                             int row_wg0, int M, int N, uint16_t* __restrict__ y,
                                             float* __restrict__ partial) {
   constexpr int kTile = MT * 256;
   const int S = gridDim.y;
   const int ks = blockIdx.y;
-  if constexpr (ONE) {
+  if constexpr (TM == 2) {
+    // 2 <= M <= 4: token j sits in product row 4 j, so lane l holds token
+    // l / 16 of column l % 16 in its first accumulator element
+    red[wave * 64 + lane] = C[0][0];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * nwr; e += blockDim.x) {
+      const int w_r = e / 64, l = e % 64;
+      const int m = l / 16, n = row_wg0 + 16 * w_r + l % 16;
+      if (m >= M || n >= N) continue;
+      float sum = 0.f;
+      for (int k2 = 0; k2 < nwk; ++k2) sum += red[(k2 * nwr + w_r) * 64 + l];
+      if (S == 1)
+        y[(size_t)m * N + n] = float_to_half_bits(sum);
+      else
+        partial[((size_t)ks * M + m) * N + n] = sum;
+    }
+    return;
+  }
+  if constexpr (TM == 1) {
     // M = 1: only token 0 is live, in lanes 0..15 (row l) of each wave
     if (lane < 16) red[wave * 16 + lane] = C[0][0];
     __syncthreads();
@@ -172,11 +190,15 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
   }
 }
 
-// Staged kernel.  ONE: M == 1 (only the accumulator of token 0 is updated).
+// Staged kernel.  TM (token mode), with one token tile: 1 for M == 1 (only
+// the accumulator of token 0 is updated); 2 for 2 <= M <= 4, where token j
+// is placed in product row 4 j (rows 4 j + 1 .. 4 j + 3 repeat it), so each
+// lane's first accumulator element holds one token and the per-tile
+// epilogue updates one element, not four.
 // VS: the workgroup stages its rows' scale block for all of K with 16-byte
 // loads (K not split, K / G a multiple of 8); otherwise each wave stages the
 // block of its own run.
-template <int FMT, int LB, int MT, int XU, int R, bool ONE, bool VS>
+template <int FMT, int LB, int MT, int XU, int R, int TM, bool VS>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
@@ -185,7 +207,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   constexpr int GPT = kTileK / G;  // groups per tile: 1 (G=128) or 2 (G=64)
   constexpr int WPG = 4 / GPT;     // 4-byte words (one product each) per group
   constexpr int RG = G / 8;        // 8-position activation units per group
-  static_assert(!ONE || MT == 1, "M == 1 has one token tile");
+  static_assert(TM == 0 || MT == 1, "M <= 4 has one token tile");
+  constexpr bool ONE = TM == 1;
   extern __shared__ __align__(16) unsigned char smem[];
   // NF4 pair table, kLutCopies interleaved copies: entry e of copy c at word
   // e * kLutCopies + c, and lane l reads copy l % kLutCopies, so random
@@ -391,7 +414,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   for (int t = 0; t < MT; ++t) C[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   int mrow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) mrow[t] = ONE ? 0 : min(t * 16 + ln, M - 1);
+  for (int t = 0; t < MT; ++t) mrow[t] = ONE ? 0 : TM == 2 ? min(ln >> 2, M - 1) : min(t * 16 + ln, M - 1);
   // INT4: the group's activation sum per token, as a product with constant B
   // (1 for the even pairs, 16 for the pre-scaled odd pairs)
   // (held in VGPRs for the whole run: opaque to the compiler, which would
@@ -435,7 +458,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = gi * WPG; w < (gi + 1) * WPG; ++w) acc = mfma_f16(xa[(4 * w) * xstride + mrow[t]], B[w], acc);
-        constexpr int NI = ONE ? 1 : 4;  // accumulators that hold tokens
+        constexpr int NI = TM != 0 ? 1 : 4;  // accumulator elements that hold tokens
         if constexpr (FMT == 0) {
           // y += (s 2^24) sum x q 2^-24 - (s z) sum x
           f32x4 sx = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -478,7 +501,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   __syncthreads();
 
   // ---- cross-wave reduction (over wk) through LDS, reusing the staging area
-  gemv_finish<MT, ONE>(C, reinterpret_cast<float*>(smem), wave, lane, nwr, nwk, row_wg0, M, N, y, partial);
+  gemv_finish<MT, TM>(C, reinterpret_cast<float*>(smem), wave, lane, nwr, nwk, row_wg0, M, N, y, partial);
 }
 
 // Direct variant.  Each wave owns C tile columns (16 C weight rows) and a run
@@ -1018,7 +1041,7 @@ int check_gemv_plan(const GemvPlan& c, int fmt) {
 
 namespace {
 
-template <int FMT, int LB, int MT, int XU, int R, bool ONE, bool VS>
+template <int FMT, int LB, int MT, int XU, int R, int TM, bool VS>
 int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
               const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   if (const int bad = check_gemv_plan(c, FMT)) return bad;
@@ -1026,10 +1049,10 @@ int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const u
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   // the plan's one-workgroup budget; the NF4 table is static LDS on top
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R, ONE, VS>),
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R, TM, VS>),
                                    kGemvLdsOne - (FMT == 1 ? kLutBytes : 0), "w4_gemv");
   if (st != 0) return st;
-  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R, ONE, VS>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
+  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R, TM, VS>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
                      y, partial, c.nwr, c.nwk, c.sc_pitch, c.x_bytes);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
@@ -1040,12 +1063,16 @@ int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const ui
              const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   if constexpr (MT == 1) {
     if (M == 1) {
-      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, true, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-      return launch_t1<FMT, LB, 1, XU, R, true, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, 1, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+      return launch_t1<FMT, LB, 1, XU, R, 1, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+    }
+    if (M <= 4) {
+      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, 2, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+      return launch_t1<FMT, LB, 1, XU, R, 2, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
     }
   }
-  if (c.vs) return launch_t1<FMT, LB, MT, XU, R, false, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-  return launch_t1<FMT, LB, MT, XU, R, false, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  if (c.vs) return launch_t1<FMT, LB, MT, XU, R, 0, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_t1<FMT, LB, MT, XU, R, 0, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
 template <int FMT, int LB, int MT, int C, bool VS, bool XL>
