@@ -58,6 +58,24 @@ constexpr int kXUSmall = 4;    // the smaller staging batch (fewer redundant loa
 constexpr int kSE = 8;         // scale entries per lane, at most: 16 rows x 32 tiles per wave
 constexpr int kMaxRun = kSE * kWave / 16;  // tiles per wave, at most
 constexpr int kLutCopies = 16;  // copies of the NF4 pair table (16 KB of LDS)
+// With one workgroup per CU and LDS to spare, 64 copies (64 KB): entry e of
+// copy c at byte 256 e + 4 c, lane l reads copy l, so no lookup shares a
+// bank and one v_perm_b32 forms a lookup's whole address (the code byte over
+// the lane's copy offset).
+constexpr int kLutCopiesWide = 64;
+
+// NF4 level pair of code byte I (0..3) of word a from a table of LC copies
+// (LC = 16: lut_c = lut + lane % 16; LC = 64: lane4 = 4 lane, the byte
+// offset of the lane's copy)
+template <int LC, int I>
+__device__ __forceinline__ uint32_t lut_pair(const uint32_t* lut, const uint32_t* lut_c, uint32_t lane4, uint32_t a) {
+  if constexpr (LC == kLutCopiesWide) {
+    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) +
+                                              __builtin_amdgcn_perm(a, lane4, 0x0C0C0400u + 0x100u * I));
+  } else {
+    return lut_c[((a >> (8 * I)) & 0xFFu) * LC];
+  }
+}
 constexpr int kSEDirect = 8;    // scale entries per lane in the direct variant
 constexpr int kDirectFromM = 4; // the direct variant serves M > 4
 constexpr int kTileK = 128;      // K positions per weight tile
@@ -198,7 +216,7 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
 // VS: the workgroup stages its rows' scale block for all of K with 16-byte
 // loads (K not split, K / G a multiple of 8); otherwise each wave stages the
 // block of its own run.
-template <int FMT, int LB, int MT, int XU, int R, int TM, bool VS>
+template <int FMT, int LB, int MT, int XU, int R, int TM, bool VS, int LC>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   // e * kLutCopies + c, and lane l reads copy l % kLutCopies, so random
   // indices from the lanes of a copy group spread over the banks instead of
   // colliding (one copy costs several conflict cycles per lookup).
-  __shared__ uint32_t lut[FMT == 1 ? 256 * kLutCopies : 1];
+  __shared__ uint32_t lut[FMT == 1 ? 256 * LC : 1];
 
   const int lane = threadIdx.x % kWave;
   // wave-uniform by construction; readfirstlane lets the compiler keep it (and
@@ -402,8 +420,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
       const int e = tid + i * nthr;
       if (e < 256) {
 #pragma unroll
-        for (int c = 0; c < kLutCopies; c += 4)
-          *reinterpret_cast<u32x4*>(&lut[e * kLutCopies + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
+        for (int c = 0; c < LC; c += 4)
+          *reinterpret_cast<u32x4*>(&lut[e * LC + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
       }
     }
   }
@@ -427,7 +445,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
   // the lane's row of the scale block, at the wave's first tile
   const uint32_t* sc_row = VS ? sc + (size_t)(wr * 16 + ln) * sc_pitch + (size_t)t0 * EW
                               : sc + (size_t)ln * sc_pitch * EW;
-  const uint32_t* lut_c = lut + lane % kLutCopies;
+  const uint32_t* lut_c = lut + lane % LC;
+  const uint32_t lane4 = (uint32_t)lane * 4u;
   const int xstride = ONE ? 1 : M;
 
   // products of tile ci of the wave's run
@@ -445,8 +464,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
         const uint32_t as = a >> 8;
         B[w] = u32x4{a & 0x000F000Fu, a & 0x00F000F0u, as & 0x000F000Fu, as & 0x00F000F0u};
       } else {
-        B[w] = u32x4{lut_c[(a & 0xFFu) * kLutCopies], lut_c[((a >> 8) & 0xFFu) * kLutCopies],
-                     lut_c[((a >> 16) & 0xFFu) * kLutCopies], lut_c[(a >> 24) * kLutCopies]};
+        B[w] = u32x4{lut_pair<LC, 0>(lut, lut_c, lane4, a), lut_pair<LC, 1>(lut, lut_c, lane4, a),
+                     lut_pair<LC, 2>(lut, lut_c, lane4, a), lut_pair<LC, 3>(lut, lut_c, lane4, a)};
       }
     }
     const int tl = t0 - ts0 + ci;  // tile index within the slice
@@ -523,7 +542,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
 // order and read back in the operand order (chunk c of row r at slot
 // c ^ r: both sides free of bank conflicts).  The wave's LDS accesses
 // complete in order, so no barrier is involved.
-template <int FMT, int LB, int MT, int C, int R, bool VS, bool XL>
+template <int FMT, int LB, int MT, int C, int R, bool VS, bool XL, int LC>
 __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
     const uint16_t* __restrict__ x, int M, int K, int N, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scale, const uint16_t* __restrict__ zero, uint16_t* __restrict__ y,
@@ -533,7 +552,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
   constexpr int WPG = 4 / GPT;
   constexpr int EW = (FMT == 0 && GPT == 2) ? 2 : 1;
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ uint32_t lut[FMT == 1 ? 256 * kLutCopies : 1];
+  __shared__ uint32_t lut[FMT == 1 ? 256 * LC : 1];
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // = the K wave
@@ -695,8 +714,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
       const int e = tid + i * nthr;
       if (e < 256) {
 #pragma unroll
-        for (int c = 0; c < kLutCopies; c += 4)
-          *reinterpret_cast<u32x4*>(&lut[e * kLutCopies + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
+        for (int c = 0; c < LC; c += 4)
+          *reinterpret_cast<u32x4*>(&lut[e * LC + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
       }
     }
     if constexpr (!VS) __syncthreads();  // the table is shared; the scale block is the wave's own
@@ -713,7 +732,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
   u32x4 kOnes;
   asm volatile("v_mov_b32 %0, 0x3C003C00" : "=v"(kOnes[0]));
   kOnes[1] = kOnes[2] = kOnes[3] = kOnes[0];
-  const uint32_t* lut_c = lut + lane % kLutCopies;
+  const uint32_t* lut_c = lut + lane % LC;
+  const uint32_t lane4 = (uint32_t)lane * 4u;
 
   auto compute = [&](Slot& sl, int ci) {
     if constexpr (XL) {
@@ -765,8 +785,8 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
           if constexpr (FMT == 0) {
             B[wi] = u32x4{a & 0x000F000Fu, (a >> 4) & 0x000F000Fu, (a >> 8) & 0x000F000Fu, (a >> 12) & 0x000F000Fu};
           } else {
-            B[wi] = u32x4{lut_c[(a & 0xFFu) * kLutCopies], lut_c[((a >> 8) & 0xFFu) * kLutCopies],
-                          lut_c[((a >> 16) & 0xFFu) * kLutCopies], lut_c[(a >> 24) * kLutCopies]};
+            B[wi] = u32x4{lut_pair<LC, 0>(lut, lut_c, lane4, a), lut_pair<LC, 1>(lut, lut_c, lane4, a),
+                          lut_pair<LC, 2>(lut, lut_c, lane4, a), lut_pair<LC, 3>(lut, lut_c, lane4, a)};
           }
         }
 #pragma unroll
@@ -847,6 +867,7 @@ constexpr int kGemvLdsTarget = 78 * 1024;   // two workgroups per CU (160 KB of 
 constexpr int kGemvLdsOne = 150 * 1024;     // one workgroup per CU (static LDS included)
 constexpr int kCUs = 256;
 constexpr int kLutBytes = 256 * kLutCopies * 4;
+constexpr int kLutBytesWide = 256 * kLutCopiesWide * 4;
 
 }  // namespace
 
@@ -1022,26 +1043,37 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
   const int kind = env_int("W4_GEMV_KIND", -1);
   if (kind == 1 || (kind != 0 && M > kDirectFromM)) plan_direct(c, M, K, N, G, fmt);
   c.ws_bytes = c.s > 1 ? (size_t)c.s * M * N * sizeof(float) : 0;
+  // NF4: the 64-copy table where the plan runs one workgroup per CU (one
+  // token tile, the default ring) and its LDS leaves room for it; the plan
+  // itself is the one chosen for the 16-copy table
+  c.lut = kLutCopies;
+  if (fmt == 1 && c.mt == 1 && c.ring == kRing && (long)c.row_blocks * c.s <= kCUs &&
+      c.lds_bytes + kLutBytesWide <= (size_t)kGemvLdsOne && env_int("W4_GEMV_LUT", kLutCopiesWide) == kLutCopiesWide)
+    c.lut = kLutCopiesWide;
   return c;
 }
 
 size_t gemv_lds_budget(int fmt) { return (size_t)(kGemvLdsOne - (fmt == 1 ? kLutBytes : 0)); }
 size_t gemv_static_lds(int fmt) { return fmt == 1 ? (size_t)kLutBytes : 4; }
+size_t gemv_plan_static_lds(const GemvPlan& c, int fmt) { return fmt == 1 ? (size_t)256 * c.lut * 4 : 4; }
+size_t gemv_plan_lds_budget(const GemvPlan& c, int fmt) {
+  return (size_t)kGemvLdsOne - (fmt == 1 ? (size_t)256 * c.lut * 4 : 0);
+}
 int gemv_plan_threads(const GemvPlan& c) { return (c.kind == 1 ? 1 : c.nwr) * c.nwk * kWave; }
 
 int check_gemv_plan(const GemvPlan& c, int fmt) {
   if (gemv_plan_threads(c) > kGemvMaxThreads)  // the kernels are built for at most this many threads
     return fail(-1 /* W4_EINVAL */, "w4_gemv: plan with %d x %d waves exceeds the kernel's %d threads",
                 c.kind == 1 ? 1 : c.nwr, c.nwk, kGemvMaxThreads);
-  if (c.lds_bytes > gemv_lds_budget(fmt))
+  if (c.lds_bytes > gemv_plan_lds_budget(c, fmt))
     return fail(-2 /* W4_EUNSUPPORTED */, "w4_gemv: plan needs %zu bytes of LDS (at most %zu)", c.lds_bytes,
-                gemv_lds_budget(fmt));
+                gemv_plan_lds_budget(c, fmt));
   return 0;
 }
 
 namespace {
 
-template <int FMT, int LB, int MT, int XU, int R, int TM, bool VS>
+template <int FMT, int LB, int MT, int XU, int R, int TM, bool VS, int LC>
 int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
               const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   if (const int bad = check_gemv_plan(c, FMT)) return bad;
@@ -1049,34 +1081,43 @@ int launch_t1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const u
   const dim3 grid((unsigned)c.row_blocks, (unsigned)c.s);
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   // the plan's one-workgroup budget; the NF4 table is static LDS on top
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R, TM, VS>),
-                                   kGemvLdsOne - (FMT == 1 ? kLutBytes : 0), "w4_gemv");
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, LB, MT, XU, R, TM, VS, LC>),
+                                   kGemvLdsOne - (FMT == 1 ? 256 * LC * 4 : 0), "w4_gemv");
   if (st != 0) return st;
-  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R, TM, VS>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
+  hipLaunchKernelGGL((gemv_kernel<FMT, LB, MT, XU, R, TM, VS, LC>), grid, block, c.lds_bytes, s, x, M, K, N, packed, scale, zero,
                      y, partial, c.nwr, c.nwk, c.sc_pitch, c.x_bytes);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
 }
 
+template <int FMT, int LB, int MT, int XU, int R, int LC>
+int launch_t_lc(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+  if constexpr (MT == 1) {
+    if (M == 1) {
+      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, 1, true, LC>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+      return launch_t1<FMT, LB, 1, XU, R, 1, false, LC>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+    }
+    if (M <= 4) {
+      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, 2, true, LC>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+      return launch_t1<FMT, LB, 1, XU, R, 2, false, LC>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+    }
+  }
+  if (c.vs) return launch_t1<FMT, LB, MT, XU, R, 0, true, LC>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_t1<FMT, LB, MT, XU, R, 0, false, LC>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+}
+
 template <int FMT, int LB, int MT, int XU, int R>
 int launch_t(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
              const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
-  if constexpr (MT == 1) {
-    if (M == 1) {
-      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, 1, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-      return launch_t1<FMT, LB, 1, XU, R, 1, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-    }
-    if (M <= 4) {
-      if (c.vs) return launch_t1<FMT, LB, 1, XU, R, 2, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-      return launch_t1<FMT, LB, 1, XU, R, 2, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-    }
-  }
-  if (c.vs) return launch_t1<FMT, LB, MT, XU, R, 0, true>(c, x, M, K, N, packed, scale, zero, y, ws, s);
-  return launch_t1<FMT, LB, MT, XU, R, 0, false>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  if constexpr (FMT == 1 && MT == 1 && R == kRing)
+    if (c.lut == kLutCopiesWide)
+      return launch_t_lc<FMT, LB, MT, XU, R, kLutCopiesWide>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_t_lc<FMT, LB, MT, XU, R, kLutCopies>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
-template <int FMT, int LB, int MT, int C, bool VS, bool XL>
-int launch_direct1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+template <int FMT, int LB, int MT, int C, bool VS, bool XL, int LC>
+int launch_direct1_lc(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
                    const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
   constexpr int R = MT == 1 ? 4 : 2;
   const dim3 block(c.nwk * kWave);
@@ -1084,15 +1125,24 @@ int launch_direct1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, co
   float* partial = c.s > 1 ? static_cast<float*>(ws) : nullptr;
   // the one-workgroup budget (the NF4 table is static LDS on top), reserved
   // once per instantiation: beyond 64 KB of dynamic LDS a launch needs it
-  const int budget = (int)gemv_lds_budget(FMT);
+  const int budget = kGemvLdsOne - (FMT == 1 ? 256 * LC * 4 : 0);
   if (const int bad = check_gemv_plan(c, FMT)) return bad;
-  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_direct_kernel<FMT, LB, MT, C, R, VS, XL>),
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(&gemv_direct_kernel<FMT, LB, MT, C, R, VS, XL, LC>),
                                    budget, "w4_gemv");
   if (st != 0) return st;
-  hipLaunchKernelGGL((gemv_direct_kernel<FMT, LB, MT, C, R, VS, XL>), grid, block, c.lds_bytes, s, x, M, K, N, packed,
+  hipLaunchKernelGGL((gemv_direct_kernel<FMT, LB, MT, C, R, VS, XL, LC>), grid, block, c.lds_bytes, s, x, M, K, N, packed,
                      scale, zero, y, partial, c.sc_pitch, c.xl_off);
   if (c.s > 1) return launch_reduce_partials(partial, c.s, (long)M * N, y, s);
   return check_launch("gemv");
+}
+
+template <int FMT, int LB, int MT, int C, bool VS, bool XL>
+int launch_direct1(const GemvPlan& c, const uint16_t* x, int M, int K, int N, const uint8_t* packed,
+                   const uint16_t* scale, const uint16_t* zero, uint16_t* y, void* ws, hipStream_t s) {
+  if constexpr (FMT == 1 && MT == 1)
+    if (c.lut == kLutCopiesWide)
+      return launch_direct1_lc<FMT, LB, MT, C, VS, XL, kLutCopiesWide>(c, x, M, K, N, packed, scale, zero, y, ws, s);
+  return launch_direct1_lc<FMT, LB, MT, C, VS, XL, kLutCopies>(c, x, M, K, N, packed, scale, zero, y, ws, s);
 }
 
 template <int FMT, int LB, int MT, int C>

@@ -208,8 +208,8 @@ int w4_gemv_plan(int M, int K, int N, int G, int fmt, int64_t* out, int n_out) {
                                           c.row_blocks,
                                           gemv_plan_threads(c),
                                           (int64_t)c.lds_bytes,
-                                          (int64_t)gemv_lds_budget(fmt),
-                                          (int64_t)gemv_static_lds(fmt),
+                                          (int64_t)gemv_plan_lds_budget(c, fmt),
+                                          (int64_t)gemv_plan_static_lds(c, fmt),
                                           (int64_t)c.ws_bytes,
                                           check_gemv_plan(c, fmt) == 0 ? 1 : 0,
                                           c.ring,

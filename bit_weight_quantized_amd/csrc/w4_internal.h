@@ -48,6 +48,7 @@ int launch_pack(const uint8_t* codes, int K, int N, uint8_t* packed, hipStream_t
 // vs: the staged kernel fetches its workgroup's scale block with 16-byte loads.
 struct GemvPlan {
   int kind, cols, mt, nwr, nwk, s, xu, row_blocks, sc_pitch, x_bytes, ring, vs, xl, xl_off;
+  int lut;  // NF4 table copies in LDS (16 or 64)
   size_t lds_bytes, ws_bytes;
 };
 GemvPlan plan_gemv(int M, int K, int N, int G, int fmt);
@@ -57,6 +58,9 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt);
 // negative w4_status with the error text recorded.
 size_t gemv_lds_budget(int fmt);
 size_t gemv_static_lds(int fmt);
+// the same for a given plan (its NF4 table size)
+size_t gemv_plan_lds_budget(const GemvPlan& c, int fmt);
+size_t gemv_plan_static_lds(const GemvPlan& c, int fmt);
 int gemv_plan_threads(const GemvPlan& c);
 int check_gemv_plan(const GemvPlan& c, int fmt);
 int launch_gemv(const GemvPlan& plan, const uint16_t* x, int M, int K, int N,

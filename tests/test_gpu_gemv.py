@@ -259,3 +259,28 @@ def test_gemv_decoder_layer_kv_m1(fmt, G):
     y, y_ref = full_size_case(fmt, G, 1, 8192, 1024, cfg=5, mat=1, n_sample=128)
     assert row_rel_l2(y, y_ref) <= TOL_ROW_REL_L2
     assert_elementwise(y, y_ref)
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("M", [1, 3, 4, 16])
+def test_nf4_table_copies_agree(monkeypatch, G, M):
+    """NF4 with the 64-copy level table (addresses formed by v_perm_b32,
+    chosen where the plan runs one workgroup per CU) and with the 16-copy
+    table (W4_GEMV_LUT=16): bit-identical outputs (the same levels, products
+    and order), within tolerance of the oracle."""
+    require_gpu()
+    K, N = 2048, 1024
+    assert w4.gemv_plan(M, K, N, G, w4.NF4)["static_lds"] == 256 * 64 * 4  # the wide table is the default here
+    w = wl.make_weight(11, 0, N, K)
+    x = wl.make_activations(11, 0, M, K)
+    codes, scale, zero = oracle_weights(o.FMT_NF4, w, G)
+    packed, sc, zc = upload_weights(codes, scale, zero)
+    announce("gemv nf4 table", dict(G=G, M=M, K=K, N=N))
+    y64 = host(w4.gemv(dev(x), packed, sc, zc, G, w4.NF4))
+    monkeypatch.setenv("W4_GEMV_LUT", "16")
+    assert w4.gemv_plan(M, K, N, G, w4.NF4)["static_lds"] == 256 * 16 * 4
+    y16 = host(w4.gemv(dev(x), packed, sc, zc, G, w4.NF4))
+    y_ref = o.matmul_ref(x, o.dequant(o.FMT_NF4, codes, scale, zero, G))
+    assert row_rel_l2(y64, y_ref) <= TOL_ROW_REL_L2
+    assert_elementwise(y64, y_ref)
+    assert np.array_equal(y64.view(np.uint16), y16.view(np.uint16))
