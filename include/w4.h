@@ -165,7 +165,9 @@ int w4_gemv_noalloc(const uint16_t* x, int M, int K, int N,
  *   1 tile columns per wave, 2 token tiles of 16, 3 row waves,
  *   4 K waves, 5 K slices over workgroups, 6 staged units per thread,
  *   7 workgroups along N, 8 threads per workgroup, 9 dynamic LDS bytes,
- *   10 dynamic LDS budget, 11 static LDS bytes, 12 workspace bytes,
+ *   10 dynamic LDS budget, 11 static LDS bytes (for NF4 the level table:
+ *      16 KB, or 64 KB where the plan runs one workgroup per CU and the
+ *      LDS allows; W4_GEMV_LUT=16 keeps 16 KB), 12 workspace bytes,
  *   13 1 when the plan meets the kernels' bounds (threads <= 512, dynamic
  *      LDS within budget), else 0 -- w4_gemv refuses such a plan,
  *   14 weight tiles (staged kernel) or operand slots (direct kernel) each
