@@ -1044,10 +1044,11 @@ GemvPlan plan_gemv(int M, int K, int N, int G, int fmt) {
   if (kind == 1 || (kind != 0 && M > kDirectFromM)) plan_direct(c, M, K, N, G, fmt);
   c.ws_bytes = c.s > 1 ? (size_t)c.s * M * N * sizeof(float) : 0;
   // NF4: the 64-copy table where the plan runs one workgroup per CU (one
-  // token tile, the default ring) and its LDS leaves room for it; the plan
-  // itself is the one chosen for the 16-copy table
+  // token tile, the default ring), its LDS leaves room for it and the layer
+  // is large enough (2^25 weights or more) to repay filling 64 KB per
+  // workgroup; the plan itself is the one chosen for the 16-copy table
   c.lut = kLutCopies;
-  if (fmt == 1 && c.mt == 1 && c.ring == kRing && (long)c.row_blocks * c.s <= kCUs &&
+  if (fmt == 1 && c.mt == 1 && c.ring == kRing && (long)c.row_blocks * c.s <= kCUs && (long)N * K >= (1L << 25) &&
       c.lds_bytes + kLutBytesWide <= (size_t)kGemvLdsOne && env_int("W4_GEMV_LUT", kLutCopiesWide) == kLutCopiesWide)
     c.lut = kLutCopiesWide;
   return c;

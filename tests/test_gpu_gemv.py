@@ -269,7 +269,7 @@ def test_nf4_table_copies_agree(monkeypatch, G, M):
     table (W4_GEMV_LUT=16): bit-identical outputs (the same levels, products
     and order), within tolerance of the oracle."""
     require_gpu()
-    K, N = 2048, 1024
+    K, N = 8192, 4096
     assert w4.gemv_plan(M, K, N, G, w4.NF4)["static_lds"] == 256 * 64 * 4  # the wide table is the default here
     w = wl.make_weight(11, 0, N, K)
     x = wl.make_activations(11, 0, M, K)
