@@ -420,8 +420,12 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(
       const int e = tid + i * nthr;
       if (e < 256) {
 #pragma unroll
-        for (int c = 0; c < LC; c += 4)
+        for (int j = 0; j < LC; j += 4) {
+          // copies in a lane-rotated order: consecutive entries at one copy
+          // would all fall on the same banks
+          const int c = (j + 4 * (e % (LC / 4))) % LC;
           *reinterpret_cast<u32x4*>(&lut[e * LC + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
+        }
       }
     }
   }
@@ -714,8 +718,12 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_direct_kernel(
       const int e = tid + i * nthr;
       if (e < 256) {
 #pragma unroll
-        for (int c = 0; c < LC; c += 4)
+        for (int j = 0; j < LC; j += 4) {
+          // copies in a lane-rotated order: consecutive entries at one copy
+          // would all fall on the same banks
+          const int c = (j + 4 * (e % (LC / 4))) % LC;
           *reinterpret_cast<u32x4*>(&lut[e * LC + c]) = u32x4{lutv[i], lutv[i], lutv[i], lutv[i]};
+        }
       }
     }
     if constexpr (!VS) __syncthreads();  // the table is shared; the scale block is the wave's own
